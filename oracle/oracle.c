@@ -1,0 +1,376 @@
+/*
+ * oracle.c - plain CPU oracle of the sparsely-gated MoE layer forward.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the
+ * benchmark's CPU-baseline leg may load this library.  It shares no code,
+ * header or table with the HIP library, and it never receives a value that
+ * the HIP library produced.
+ *
+ * What it computes (page names are the titles of the source web pages):
+ *
+ *   y(x) = sum_i G(x)_i * E_i(x),  G(x) = softmax(KeepTopK(x W_g, k))
+ *     - "Sparsely-Gated MoE" paper summary (Qiita), sections "Sparsely-Gated
+ *       MoE layer formula" and "Gating: Noisy Top-k Softmax" (the
+ *       inference-time, noise-free form).
+ *   Router scores in float32, one term at a time, then a stable descending
+ *   sort (ties keep the lower expert index), the first k kept, and a
+ *   softmax over those k only, with the maximum subtracted
+ *     - Go book chapter "MoE (Mixture of Experts)", section 2 "Routing:
+ *       pick the top k and re-softmax" (Route).
+ *   Token loop: count each chosen expert, run its FFN, add weight * output
+ *     - same chapter and section (Forward, Stats).
+ *   Expert FFN: Linear -> GELU -> Linear (4x wider hidden layer)
+ *     - "Extending Raschka's GPT-2: an MoE ..." summary (techfeed), section
+ *       "How MoE works: split the FFN"; Go chapter, "What was simplified"
+ *       (GELU experts; real ones such as Mixtral use SwiGLU).
+ *   SwiGLU expert with gate and up projections packed into one
+ *   [E, 2h, d] tensor (rows 0..h-1 gate/w1, rows h..2h-1 up/w3)
+ *     - "Understanding MoE in Transformers", section "Weight Loading
+ *       Refactor" (MergeModulelist over experts, Concatenate on dim 1).
+ *   Load-balance loss N * sum_e f_e^2, 0 when no token was routed
+ *     - Go chapter, section 3 "Load balancing".
+ *   Importance(X)_i = sum_x G(x)_i, CV(.)^2 of Importance and Load
+ *     - Qiita summary, section "Load-balancing losses".
+ *   Parameter accounting Total = d*E + E*P_e, Active = d*E + k*P_e
+ *     - Go chapter, section 1 "Parameter accounting".
+ *
+ * Readings where the pages are silent (each is listed with its reason in
+ * the design notes of the repository):
+ *   - router dot product: fmaf per term, i ascending, starting from +0.0f,
+ *     bias (if any) added after the last term, all in float32;
+ *   - softmax weights evaluated in double from the float32 scores;
+ *   - GELU is the exact x * Phi(x) (erf form);
+ *   - expert arithmetic in double from the exact values of the stored
+ *     float32 / bfloat16 numbers; no rounding of intermediates;
+ *   - Load(X) = hard per-expert counts (no noise at inference);
+ *   - CV^2 uses the population variance; 0 when the mean is 0;
+ *   - SwiGLU experts count P_e = 3*d*h weights, GELU experts 2*d*h; a
+ *     shared always-on expert adds P_e to both totals;
+ *   - within an expert's group, rows keep the order of the flat assignment
+ *     index t*k + j.
+ *
+ * Build: gcc -O2 -fopenmp -ffp-contract=off -mfma (no other contraction).
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#include <omp.h>
+
+#define ORACLE_GELU 0
+#define ORACLE_SWIGLU 1
+#define ORACLE_F32 0
+#define ORACLE_BF16 1
+
+typedef struct {
+  int64_t T;
+  int32_t d, h, E, k, S, act, dtype;
+} oracle_cfg;
+
+typedef struct {
+  const float *w_gate; /* [E, d] float32 */
+  const float *b_gate; /* [E] float32 or NULL */
+  const void *w_up;    /* GELU [E, h, d]; SwiGLU [E, 2h, d] */
+  const void *w_down;  /* [E, d, h] */
+  const void *b_up;    /* GELU [E, h] or NULL */
+  const void *b_down;  /* GELU [E, d] or NULL */
+  const void *w_up_shared;   /* [S, 2h, d] or NULL */
+  const void *w_down_shared; /* [S, d, h] or NULL */
+} oracle_weights;
+
+/* ---- element access: the exact value of a stored float32 / bfloat16 ---- */
+
+static float bf16_value(uint16_t bits) {
+  uint32_t u = (uint32_t)bits << 16; /* bfloat16 is the top half of a float32 */
+  float f;
+  memcpy(&f, &u, sizeof f);
+  return f;
+}
+
+static float elem_f(const void *base, int dtype, int64_t i) {
+  if (dtype == ORACLE_F32) return ((const float *)base)[i];
+  return bf16_value(((const uint16_t *)base)[i]);
+}
+
+static double elem(const void *base, int dtype, int64_t i) {
+  return (double)elem_f(base, dtype, i);
+}
+
+static int cfg_ok(const oracle_cfg *c) {
+  return c && c->T >= 0 && c->d > 0 && c->h > 0 && c->E > 0 && c->k >= 1 &&
+         c->k <= c->E && (c->S == 0 || c->S == 1) &&
+         (c->act == ORACLE_GELU || c->act == ORACLE_SWIGLU) &&
+         (c->dtype == ORACLE_F32 || c->dtype == ORACLE_BF16) &&
+         !(c->S && c->act != ORACLE_SWIGLU);
+}
+
+/* ---- step 1: router scores of one token (float32, sequential) ---- */
+
+static void router_scores(const oracle_cfg *c, const void *x, const float *wg,
+                          const float *bg, int64_t t, float *score) {
+  const int d = c->d;
+  for (int e = 0; e < c->E; ++e) {
+    float s = 0.0f;
+    for (int i = 0; i < d; ++i)
+      s = fmaf(elem_f(x, c->dtype, t * d + i), wg[(int64_t)e * d + i], s);
+    if (bg) s = s + bg[e];
+    score[e] = s;
+  }
+}
+
+/* ---- step 2: KeepTopK as the first k entries of a stable descending sort.
+ * A selection sort that only moves on a strictly larger score keeps equal
+ * scores in ascending expert order, which is exactly what a stable sort on
+ * "greater" does.  IEEE '>' treats +0 and -0 as equal. ---- */
+
+static void keep_top_k(const float *score, int E, int k, int32_t *idx,
+                       unsigned char *taken) {
+  memset(taken, 0, (size_t)E);
+  for (int j = 0; j < k; ++j) {
+    int best = -1;
+    for (int e = 0; e < E; ++e) {
+      if (taken[e]) continue;
+      if (best < 0 || score[e] > score[best]) best = e;
+    }
+    taken[best] = 1;
+    idx[j] = best;
+  }
+}
+
+/* ---- step 3: softmax over the k kept scores (the rest are -inf and get
+ * weight exactly 0), maximum subtracted, evaluated in double. ---- */
+
+static void kept_softmax(const float *score, const int32_t *idx, int k,
+                         double *w) {
+  const double m = (double)score[idx[0]];
+  double z = 0.0;
+  for (int j = 0; j < k; ++j) {
+    w[j] = exp((double)score[idx[j]] - m);
+    z += w[j];
+  }
+  for (int j = 0; j < k; ++j) w[j] = w[j] / z;
+}
+
+/* ---- step 4: one expert FFN on one token row, in double.
+ * e in [0, E) is a routed expert; e == E is the shared expert. ---- */
+
+static double gelu(double a) { return 0.5 * a * (1.0 + erf(a * M_SQRT1_2)); }
+
+static double silu(double g) { return g / (1.0 + exp(-g)); }
+
+static void expert_ffn(const oracle_cfg *c, const oracle_weights *W, int e,
+                       const double *xr, double *hid, double *yr) {
+  const int64_t d = c->d, h = c->h;
+  const int dt = c->dtype;
+  const int shared = (e == c->E);
+  const void *wu = shared ? W->w_up_shared : W->w_up;
+  const void *wd = shared ? W->w_down_shared : W->w_down;
+  const int64_t eo = shared ? 0 : e;
+
+  if (c->act == ORACLE_GELU) {
+    const int64_t ub = eo * h * d; /* W1[e] is [h, d] */
+    for (int64_t n = 0; n < h; ++n) {
+      double a = 0.0;
+      for (int64_t i = 0; i < d; ++i) a += elem(wu, dt, ub + n * d + i) * xr[i];
+      if (W->b_up) a += elem(W->b_up, dt, eo * h + n);
+      hid[n] = gelu(a);
+    }
+  } else {
+    const int64_t ub = eo * 2 * h * d; /* [2h, d]: gate rows, then up rows */
+    for (int64_t n = 0; n < h; ++n) {
+      double g = 0.0, u = 0.0;
+      for (int64_t i = 0; i < d; ++i) {
+        g += elem(wu, dt, ub + n * d + i) * xr[i];
+        u += elem(wu, dt, ub + (h + n) * d + i) * xr[i];
+      }
+      hid[n] = silu(g) * u;
+    }
+  }
+  const int64_t db = eo * d * h; /* W2[e] is [d, h] */
+  for (int64_t o = 0; o < d; ++o) {
+    double s = 0.0;
+    for (int64_t n = 0; n < h; ++n) s += elem(wd, dt, db + o * h + n) * hid[n];
+    if (c->act == ORACLE_GELU && W->b_down) s += elem(W->b_down, dt, eo * d + o);
+    yr[o] = s;
+  }
+}
+
+/* ======================= exported entry points ======================= */
+
+int oracle_max_threads(void) { return omp_get_max_threads(); }
+void oracle_set_threads(int n) {
+  if (n > 0) omp_set_num_threads(n);
+}
+
+/* Routing of tokens t0 .. t0+nt-1: float32 scores (optional), kept expert
+ * indices in descending score order, and their double softmax weights. */
+int oracle_route(const oracle_cfg *c, const void *x, const float *wg,
+                 const float *bg, int64_t t0, int64_t nt, float *scores,
+                 int32_t *idx, double *w) {
+  if (!cfg_ok(c) || !x || !wg || !idx || !w || t0 < 0 || nt < 0 ||
+      t0 + nt > c->T)
+    return -1;
+  int bad = 0;
+#pragma omp parallel reduction(| : bad)
+  {
+    float *s = (float *)malloc(sizeof(float) * (size_t)c->E);
+    unsigned char *tk = (unsigned char *)malloc((size_t)c->E);
+#pragma omp for schedule(static)
+    for (int64_t r = 0; r < nt; ++r) {
+      router_scores(c, x, wg, bg, t0 + r, s);
+      for (int e = 0; e < c->E; ++e)
+        if (!isfinite(s[e])) bad = 1;
+      if (scores) memcpy(scores + r * c->E, s, sizeof(float) * (size_t)c->E);
+      keep_top_k(s, c->E, c->k, idx + r * c->k, tk);
+      kept_softmax(s, idx + r * c->k, c->k, w + r * c->k);
+    }
+    free(s);
+    free(tk);
+  }
+  return bad ? -2 : 0;
+}
+
+/* Per-expert counts (Stats.TokensPerExpert) and Importance, token order. */
+int oracle_counts(const oracle_cfg *c, const int32_t *idx, const double *w,
+                  int32_t *counts, double *importance) {
+  if (!cfg_ok(c) || !idx || !counts) return -1;
+  for (int e = 0; e < c->E; ++e) {
+    counts[e] = 0;
+    if (importance) importance[e] = 0.0;
+  }
+  for (int64_t f = 0; f < c->T * c->k; ++f) {
+    const int e = idx[f];
+    if (e < 0 || e >= c->E) return -1;
+    counts[e] += 1;
+    if (importance && w) importance[e] += w[f];
+  }
+  return 0;
+}
+
+/* Grouping of the T*k assignments by expert: offsets[E+1] (exclusive scan of
+ * the counts), perm_src[p] = source token of row p, pos[t*k+j] = row of
+ * assignment (t, j).  Rows of one expert keep flat-index order. */
+int oracle_permute(const oracle_cfg *c, const int32_t *idx, int32_t *offsets,
+                   int32_t *perm_src, int32_t *pos) {
+  if (!cfg_ok(c) || !idx || !offsets || !perm_src || !pos) return -1;
+  const int64_t n = c->T * c->k;
+  int64_t p = 0;
+  for (int e = 0; e < c->E; ++e) {
+    offsets[e] = (int32_t)p;
+    for (int64_t f = 0; f < n; ++f) {
+      if (idx[f] != e) continue;
+      perm_src[p] = (int32_t)(f / c->k);
+      pos[f] = (int32_t)p;
+      ++p;
+    }
+  }
+  offsets[c->E] = (int32_t)p;
+  return p == n ? 0 : -1;
+}
+
+/* One expert (e < E routed, e == E shared) applied to one row, in double. */
+int oracle_expert(const oracle_cfg *c, const oracle_weights *W, int e,
+                  const double *xr, double *yr) {
+  if (!cfg_ok(c) || !W || !xr || !yr || e < 0 || e > c->E) return -1;
+  if (e == c->E && !c->S) return -1;
+  double *hid = (double *)malloc(sizeof(double) * (size_t)c->h);
+  expert_ffn(c, W, e, xr, hid, yr);
+  free(hid);
+  return 0;
+}
+
+/* The whole layer on the listed tokens: y[r] = sum_j w_j * E_{idx_j}(x_t)
+ * (+ the shared expert with weight 1), accumulated in slot order. */
+int oracle_forward_tokens(const oracle_cfg *c, const oracle_weights *W,
+                          const void *x, const int64_t *tokens, int64_t nt,
+                          double *y, int32_t *idx, double *w) {
+  if (!cfg_ok(c) || !W || !W->w_gate || !x || !tokens || !y || !idx || !w ||
+      nt < 0)
+    return -1;
+  if (c->S && (!W->w_up_shared || !W->w_down_shared)) return -1;
+  for (int64_t r = 0; r < nt; ++r)
+    if (tokens[r] < 0 || tokens[r] >= c->T) return -1;
+  const int64_t d = c->d;
+  int bad = 0;
+#pragma omp parallel reduction(| : bad)
+  {
+    float *s = (float *)malloc(sizeof(float) * (size_t)c->E);
+    unsigned char *tk = (unsigned char *)malloc((size_t)c->E);
+    double *xr = (double *)malloc(sizeof(double) * (size_t)d);
+    double *ye = (double *)malloc(sizeof(double) * (size_t)d);
+    double *hid = (double *)malloc(sizeof(double) * (size_t)c->h);
+#pragma omp for schedule(dynamic, 1)
+    for (int64_t r = 0; r < nt; ++r) {
+      const int64_t t = tokens[r];
+      router_scores(c, x, W->w_gate, W->b_gate, t, s);
+      for (int e = 0; e < c->E; ++e)
+        if (!isfinite(s[e])) bad = 1;
+      int32_t *ix = idx + r * c->k;
+      double *wr = w + r * c->k;
+      keep_top_k(s, c->E, c->k, ix, tk);
+      kept_softmax(s, ix, c->k, wr);
+      for (int64_t i = 0; i < d; ++i) xr[i] = elem(x, c->dtype, t * d + i);
+      double *yo = y + r * d;
+      for (int64_t i = 0; i < d; ++i) yo[i] = 0.0;
+      for (int j = 0; j < c->k; ++j) {
+        expert_ffn(c, W, ix[j], xr, hid, ye);
+        for (int64_t i = 0; i < d; ++i) yo[i] += wr[j] * ye[i];
+      }
+      if (c->S) {
+        expert_ffn(c, W, c->E, xr, hid, ye);
+        for (int64_t i = 0; i < d; ++i) yo[i] += ye[i];
+      }
+    }
+    free(s);
+    free(tk);
+    free(xr);
+    free(ye);
+    free(hid);
+  }
+  return bad ? -2 : 0;
+}
+
+/* Side statistics: out[0] = CV^2(Importance), out[1] = CV^2(Load = counts),
+ * out[2] = load-balance loss E * sum_e (counts_e / total)^2 (0 if total 0). */
+static double cv2(const double *v, int n) {
+  double mean = 0.0;
+  for (int i = 0; i < n; ++i) mean += v[i];
+  mean /= n;
+  if (mean == 0.0) return 0.0;
+  double var = 0.0;
+  for (int i = 0; i < n; ++i) var += (v[i] - mean) * (v[i] - mean);
+  var /= n;
+  return var / (mean * mean);
+}
+
+int oracle_load_stats(const int32_t *counts, const double *importance, int E,
+                      double *out) {
+  if (!counts || !out || E <= 0) return -1;
+  double *v = (double *)malloc(sizeof(double) * (size_t)E);
+  double total = 0.0;
+  for (int e = 0; e < E; ++e) {
+    v[e] = (double)counts[e];
+    total += v[e];
+  }
+  out[0] = importance ? cv2(importance, E) : 0.0;
+  out[1] = cv2(v, E);
+  double lb = 0.0;
+  if (total != 0.0) {
+    for (int e = 0; e < E; ++e) lb += (v[e] / total) * (v[e] / total);
+    lb *= E;
+  }
+  out[2] = lb;
+  free(v);
+  return 0;
+}
+
+/* Parameter accounting: router d*E plus per-expert P_e weights (biases are
+ * not counted); the shared expert, if any, is always active. */
+int oracle_param_counts(const oracle_cfg *c, int64_t *total, int64_t *active) {
+  if (!cfg_ok(c) || !total || !active) return -1;
+  const int64_t pe = (int64_t)(c->act == ORACLE_GELU ? 2 : 3) * c->d * c->h;
+  const int64_t router = (int64_t)c->d * c->E;
+  *total = router + (int64_t)c->E * pe + (int64_t)c->S * pe;
+  *active = router + (int64_t)c->k * pe + (int64_t)c->S * pe;
+  return 0;
+}

@@ -1,0 +1,369 @@
+"""Pins of the CPU oracle to facts other than its own code.
+
+Each test names what fixes the expected value: a number printed on the
+pages (tests/golden/pages_pins.json), a closed form, an invariant, a
+special case that reduces to a library routine (numpy/scipy/torch), or
+brute force on tiny inputs.  Page names are the titles of the source pages.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import scipy.special
+import torch
+
+from helpers import BF16, F32, GELU, SWIGLU, layer, random_layer
+
+GOLD = json.load(open(os.path.join(os.path.dirname(__file__), "golden",
+                                   "pages_pins.json")))
+
+
+def _identity_router(scores, k):
+    """A layer whose router scores are exactly ``scores``: x = scores and
+    W_g = I, so every product is exact and every added term is +-0."""
+    s = np.asarray(scores, np.float32)
+    T, E = s.shape
+    return layer(T, E, 4, E, k, x=s, w_gate=np.eye(E, dtype=np.float32),
+                 w_up=np.zeros((E, 4, E)), w_down=np.zeros((E, E, 4)))
+
+
+# ---------------------------------------------------------------- routing --
+
+def test_router_worked_example(oracle_lib):
+    """The techfeed summary's router example: scores over 6 experts pick
+    indices 4 and 2; the two kept weights are the closed-form 2-way
+    softmax sigma(l4 - l2)."""
+    g = GOLD["router_example"]
+    L = _identity_router([g["scores"]], g["k"])
+    idx, w, sc = oracle_lib.route(L, want_scores=True)
+    assert sc[0].tolist() == np.float32(g["scores"]).tolist()
+    assert idx[0].tolist() == g["expected_indices"]
+    l4, l2 = float(np.float32(0.5106)), float(np.float32(0.4254))
+    assert w[0, 0] == pytest.approx(1.0 / (1.0 + math.exp(l2 - l4)), rel=1e-15)
+    assert w[0, 1] == pytest.approx(1.0 / (1.0 + math.exp(l4 - l2)), rel=1e-15)
+    assert w[0, 0] == pytest.approx(0.5212871, abs=5e-8)
+
+
+@pytest.mark.parametrize("E,k", [(6, 2), (8, 1), (8, 8), (32, 4), (256, 8)])
+def test_keep_topk_is_stable_descending_sort(oracle_lib, E, k):
+    """KeepTopK = first k of a stable descending sort (lower index first on
+    ties): compared with numpy's stable argsort; many forced ties."""
+    rng = np.random.default_rng(E * 31 + k)
+    s = (np.round(rng.standard_normal((200, E)) * 2) / 2).astype(np.float32)
+    s[0] = 0.0
+    s[1, :] = -0.0
+    s[1, ::3] = 0.0          # +0 and -0 compare equal
+    L = _identity_router(s, k)
+    idx, w, _ = oracle_lib.route(L)
+    ref = np.argsort(-s.astype(np.float64), axis=1, kind="stable")[:, :k]
+    assert np.array_equal(idx, ref)
+    assert idx[0].tolist() == list(range(k))
+    assert idx[1].tolist() == list(range(k))
+
+
+def test_ties_zero_input_and_duplicate_rows(oracle_lib):
+    """x = 0 gives equal scores: indices 0..k-1 and weights 1/k.  Two equal
+    router rows (experts 3 and 5) that beat the rest keep the order 3, 5."""
+    E, d, k = 8, 16, 3
+    rng = np.random.default_rng(1)
+    wg = rng.standard_normal((E, d)).astype(np.float32) * 0.1
+    wg[5] = wg[3]
+    x = np.zeros((2, d), np.float32)
+    x[1] = wg[3] * 50
+    L = layer(2, d, 4, E, k, x=x, w_gate=wg, w_up=np.zeros((E, 4, d)),
+              w_down=np.zeros((E, d, 4)))
+    idx, w, sc = oracle_lib.route(L, want_scores=True)
+    assert idx[0].tolist() == [0, 1, 2]
+    assert np.all(w[0] == 1.0 / 3.0)
+    assert sc[1, 3] == sc[1, 5]
+    assert idx[1, :2].tolist() == [3, 5]
+
+
+def test_softmax_closed_forms(oracle_lib):
+    """k = 1 gives weight exactly 1; k = 2 is sigma(l0 - l1); k = E is the
+    dense softmax gate softmax(x W_g) of the Qiita summary (scipy)."""
+    rng = np.random.default_rng(2)
+    s = rng.standard_normal((50, 6)).astype(np.float32) * 3
+    idx1, w1, _ = oracle_lib.route(_identity_router(s, 1))
+    assert np.all(w1 == 1.0)
+    idx2, w2, _ = oracle_lib.route(_identity_router(s, 2))
+    l0 = np.take_along_axis(s, idx2[:, :1], 1)[:, 0].astype(np.float64)
+    l1 = np.take_along_axis(s, idx2[:, 1:], 1)[:, 0].astype(np.float64)
+    np.testing.assert_allclose(w2[:, 0], 1 / (1 + np.exp(l1 - l0)), rtol=1e-14)
+    idx6, w6, _ = oracle_lib.route(_identity_router(s, 6))
+    dense = scipy.special.softmax(s.astype(np.float64), axis=1)
+    np.testing.assert_allclose(w6, np.take_along_axis(dense, idx6, 1), rtol=1e-13)
+
+
+@pytest.mark.parametrize("k", [1, 2, 4, 8])
+def test_kept_weights_sum_to_one_and_descend(oracle_lib, k):
+    L = random_layer(3, T=300, d=40, h=8, E=16, k=k, bias=True)
+    idx, w, _ = oracle_lib.route(L)
+    assert np.all(np.abs(w.sum(1) - 1.0) <= k * 2.0 ** -52 * 4)
+    assert np.all(w > 0) and np.all(np.diff(w, axis=1) <= 0)
+    assert all(len(set(r)) == k for r in idx.tolist())
+
+
+def test_router_scores_exact_integer_products(oracle_lib):
+    """Small integers: every partial sum is exact in float32, so the scores
+    equal the integer matrix product (numpy int64) plus the bias."""
+    rng = np.random.default_rng(4)
+    T, d, E = 20, 24, 7
+    x = rng.integers(-8, 9, (T, d))
+    wg = rng.integers(-8, 9, (E, d))
+    b = rng.integers(-50, 50, E)
+    L = layer(T, d, 4, E, 2, x=x, w_gate=wg, b_gate=b,
+              w_up=np.zeros((E, 4, d)), w_down=np.zeros((E, d, 4)))
+    _, _, sc = oracle_lib.route(L, want_scores=True)
+    assert np.array_equal(sc, (x @ wg.T + b).astype(np.float32))
+
+
+def test_router_scores_fused_multiply_add_per_term(oracle_lib):
+    """Reading of the Go Route loop: one fused multiply-add per term.  With
+    s = -1 after term 0, term 1 adds (1 + 2^-12)^2 = 1 + 2^-11 + 2^-24
+    without rounding the product first: the score is 2^-11 + 2^-24 (an
+    unfused multiply-add would give 2^-11)."""
+    a = 1.0 + 2.0 ** -12
+    L = layer(1, 2, 4, 2, 1, x=[[1.0, a]], w_gate=[[-1.0, a], [0.0, 0.0]],
+              w_up=np.zeros((2, 4, 2)), w_down=np.zeros((2, 2, 4)))
+    _, _, sc = oracle_lib.route(L, want_scores=True)
+    assert float(sc[0, 0]) == 2.0 ** -11 + 2.0 ** -24
+
+
+def test_router_scores_ascending_order(oracle_lib):
+    """Terms are added in ascending i: 2^24 + 1 rounds back to 2^24 and the
+    last term cancels it, so the score is 0 (descending order would give 1)."""
+    L = layer(1, 3, 4, 2, 1, x=[[2.0 ** 24, 1.0, -(2.0 ** 24)]],
+              w_gate=[[1.0, 1.0, 1.0], [0.0, 0.0, 0.0]],
+              w_up=np.zeros((2, 4, 3)), w_down=np.zeros((2, 3, 4)))
+    _, _, sc = oracle_lib.route(L, want_scores=True)
+    assert float(sc[0, 0]) == 0.0
+
+
+def test_router_scores_within_float32_error_bound(oracle_lib):
+    """|score - exact dot| <= gamma_d * sum|x_i w_i| + |bias| u (standard
+    error bound of a length-d float32 recursive sum)."""
+    L = random_layer(5, T=64, d=512, h=8, E=12, k=2, dtype=BF16, bias=True)
+    _, _, sc = oracle_lib.route(L, want_scores=True)
+    xf = (L.x.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    wg = L.w_gate.astype(np.float64)
+    exact = xf @ wg.T + L.b_gate.astype(np.float64)
+    u = 2.0 ** -24
+    gam = (513 * u) / (1 - 513 * u)
+    bound = gam * (np.abs(xf) @ np.abs(wg).T + np.abs(L.b_gate))
+    assert np.all(np.abs(sc - exact) <= bound)
+
+
+def test_non_finite_input_rejected(oracle_lib):
+    L = random_layer(6, T=4, d=8, h=8, E=4, k=2)
+    L.x[2, 3] = np.nan
+    with pytest.raises(FloatingPointError):
+        oracle_lib.route(L)
+
+
+# -------------------------------------------------- counts / permutation --
+
+def test_counts_importance_and_permutation(oracle_lib):
+    """Counts = histogram of the kept indices (np.bincount), summing to T*k;
+    Importance = per-expert sum of the kept weights (sums to T); the
+    grouping is numpy's stable argsort of the flat index array."""
+    L = random_layer(7, T=333, d=32, h=8, E=12, k=3, bias=True)
+    c = L.cfg
+    idx, w, _ = oracle_lib.route(L)
+    cnt, imp = oracle_lib.counts(c, idx, w)
+    assert np.array_equal(cnt, np.bincount(idx.ravel(), minlength=c.E))
+    assert cnt.sum() == c.T * c.k
+    np.testing.assert_allclose(
+        imp, np.bincount(idx.ravel(), weights=w.ravel(), minlength=c.E), rtol=1e-13)
+    assert imp.sum() == pytest.approx(c.T, rel=1e-13)
+    off, src, pos = oracle_lib.permute(c, idx)
+    order = np.argsort(idx.ravel(), kind="stable")
+    assert np.array_equal(off, np.concatenate([[0], np.cumsum(cnt)]))
+    assert np.array_equal(src, order // c.k)
+    assert np.array_equal(pos[order], np.arange(c.T * c.k))
+
+
+def test_permutation_with_empty_experts(oracle_lib):
+    L = _identity_router(np.tile(np.float32([5, 4, 0, 0, 3, 0]), (9, 1)), 2)
+    idx, w, _ = oracle_lib.route(L)
+    off, src, pos = oracle_lib.permute(L.cfg, idx)
+    assert off.tolist() == [0, 9, 18, 18, 18, 18, 18]
+    assert src.tolist() == list(range(9)) * 2
+
+
+# ----------------------------------------------------------- expert FFNs --
+
+def _int_gelu_layer(dtype, seed):
+    """GELU experts whose pre-activations are all multiples of 64: in double,
+    erf(+-45.25) is exactly +-1, so GELU(a) = max(a, 0) exactly and the FFN
+    reduces to integer matrix products (numpy int64)."""
+    rng = np.random.default_rng(seed)
+    E, d, h, T = 3, 6, 10, 5
+    x = rng.integers(-1, 2, (T, d))
+    w1 = rng.integers(-2, 3, (E, h, d)) * 64
+    b1 = rng.integers(-2, 3, (E, h)) * 64
+    w2 = rng.integers(-3, 4, (E, d, h))
+    b2 = rng.integers(-9, 10, (E, d))
+    L = layer(T, d, h, E, 2, GELU, dtype, x=x, w_gate=np.ones((E, d)),
+              w_up=w1, w_down=w2, b_up=b1, b_down=b2)
+    return L, x, w1, b1, w2, b2
+
+
+@pytest.mark.parametrize("dtype", [F32, BF16])
+def test_gelu_expert_reduces_to_integer_matmul(oracle_lib, dtype):
+    L, x, w1, b1, w2, b2 = _int_gelu_layer(dtype, 8)
+    for e in range(3):
+        for t in range(5):
+            ref = w2[e] @ np.maximum(w1[e] @ x[t] + b1[e], 0) + b2[e]
+            got = oracle_lib.expert(L, e, x[t].astype(np.float64))
+            assert np.array_equal(got, ref.astype(np.float64)), (e, t)
+
+
+@pytest.mark.parametrize("dtype", [F32, BF16])
+def test_swiglu_expert_reduces_to_integer_matmul(oracle_lib, dtype):
+    """SwiGLU with packed [2h, d] gate/up rows.  x in {0, 1}, gate weights in
+    {0, 64, -2048} with d = 6: every gate pre-activation is 0, >= 64 or
+    <= -1728, where silu(g) is exactly g, g, or -0 in double, so
+    H = max(gate, 0) * up and y = W2 H are integer matrix products."""
+    rng = np.random.default_rng(9)
+    E, d, h, T = 2, 6, 5, 7
+    x = rng.integers(0, 2, (T, d))
+    gate = rng.choice([0, 64, -2048], size=(E, h, d), p=[0.4, 0.45, 0.15])
+    up = rng.integers(-3, 4, (E, h, d))
+    w2 = rng.integers(-3, 4, (E, d, h))
+    L = layer(T, d, h, E, 1, SWIGLU, dtype, x=x, w_gate=np.ones((E, d)),
+              w_up=np.concatenate([gate, up], axis=1), w_down=w2)
+    for e in range(E):
+        for t in range(T):
+            hid = np.maximum(gate[e] @ x[t], 0) * (up[e] @ x[t])
+            got = oracle_lib.expert(L, e, x[t].astype(np.float64))
+            assert np.array_equal(got, (w2[e] @ hid).astype(np.float64)), (e, t)
+
+
+def test_activation_values(oracle_lib):
+    """GELU(1) = Phi(1); SwiGLU(1) = sigmoid(1); SwiGLU(ln 3) = (3/4) (ln 3)^2,
+    all through 1x1 experts."""
+    Lg = layer(1, 1, 1, 1, 1, GELU, x=[[1.0]], w_gate=[[1.0]],
+               w_up=[[[1.0]]], w_down=[[[1.0]]])
+    phi1 = 0.5 * (1 + math.erf(1 / math.sqrt(2)))
+    assert oracle_lib.expert(Lg, 0, np.array([1.0]))[0] == pytest.approx(phi1, rel=1e-15)
+    assert phi1 == pytest.approx(0.8413447460685429, rel=1e-15)
+    Ls = layer(1, 1, 1, 1, 1, SWIGLU, x=[[1.0]], w_gate=[[1.0]],
+               w_up=[[[1.0]], [[1.0]]], w_down=[[[1.0]]])
+    ln3 = math.log(3.0)
+    assert oracle_lib.expert(Ls, 0, np.array([1.0]))[0] == pytest.approx(1 / (1 + math.exp(-1)), rel=1e-15)
+    assert oracle_lib.expert(Ls, 0, np.array([ln3]))[0] == pytest.approx(0.75 * ln3 * ln3, rel=1e-14)
+
+
+@pytest.mark.parametrize("act", [GELU, SWIGLU])
+def test_single_expert_top1_is_plain_ffn(oracle_lib, act):
+    """The Go chapter's boundary check: 1 expert, top-1 equals a plain FFN.
+    The plain FFN here is torch's Linear/GELU/SiLU in float64."""
+    g = GOLD["single_expert_is_ffn"]
+    L = random_layer(10, T=9, d=12, h=20, E=g["E"], k=g["k"], act=act,
+                     expert_bias=(act == GELU))
+    y, idx, w = oracle_lib.forward_tokens(L, range(9))
+    assert np.all(idx == 0) and np.all(w == 1.0)
+    X = torch.tensor(L.x, dtype=torch.float64)
+    W1 = torch.tensor(L.w_up[0], dtype=torch.float64)
+    W2 = torch.tensor(L.w_down[0], dtype=torch.float64)
+    if act == GELU:
+        hid = torch.nn.functional.gelu(
+            torch.nn.functional.linear(X, W1, torch.tensor(L.b_up[0], dtype=torch.float64)))
+        ref = torch.nn.functional.linear(hid, W2, torch.tensor(L.b_down[0], dtype=torch.float64))
+    else:
+        hdim = L.cfg.h
+        hid = torch.nn.functional.silu(X @ W1[:hdim].T) * (X @ W1[hdim:].T)
+        ref = hid @ W2.T
+    np.testing.assert_allclose(y, ref.numpy(), rtol=1e-12, atol=1e-13)
+
+
+@pytest.mark.parametrize("act,S", [(GELU, 0), (SWIGLU, 0), (SWIGLU, 1)])
+def test_sparse_forward_equals_dense_gated_sum(oracle_lib, act, S):
+    """y = sum over ALL experts of G_i * E_i(x), with G = softmax(KeepTopK)
+    built densely (-inf outside the top k, scipy softmax): the sparse token
+    loop that skips zero gates gives the same result (Qiita summary,
+    'Sparsely-Gated MoE layer formula')."""
+    L = random_layer(11, T=6, d=10, h=14, E=5, k=2, act=act, S=S, bias=True)
+    c = L.cfg
+    y, idx, w = oracle_lib.forward_tokens(L, range(c.T))
+    _, _, sc = oracle_lib.route(L, want_scores=True)
+    for t in range(c.T):
+        keep = np.full(c.E, -np.inf)
+        top = np.argsort(-sc[t].astype(np.float64), kind="stable")[:c.k]
+        keep[top] = sc[t, top]
+        G = scipy.special.softmax(keep)
+        xr = L.x[t].astype(np.float64)
+        dense = sum(G[i] * oracle_lib.expert(L, i, xr) for i in range(c.E))
+        if S:
+            dense = dense + oracle_lib.expert(L, c.E, xr)
+        np.testing.assert_allclose(y[t], dense, rtol=1e-12, atol=1e-14)
+        assert np.count_nonzero(G) == c.k
+
+
+def test_output_scales_exactly_with_down_projection(oracle_lib):
+    L = random_layer(12, T=7, d=16, h=24, E=4, k=2, act=SWIGLU)
+    y1, _, _ = oracle_lib.forward_tokens(L, range(7))
+    L.w_down = np.ascontiguousarray(L.w_down * np.float32(8.0))
+    y8, _, _ = oracle_lib.forward_tokens(L, range(7))
+    assert np.array_equal(y8, 8.0 * y1)
+
+
+def test_zero_down_projection_gives_bias(oracle_lib):
+    """W2 = 0: every expert outputs b2, and the kept weights sum to 1."""
+    L = random_layer(13, T=5, d=8, h=16, E=4, k=2, expert_bias=True)
+    L.w_down = np.zeros_like(L.w_down)
+    L.b_down = np.ascontiguousarray(np.tile(np.float32([1, 2, 3, 4, 5, 6, 7, 8]), (4, 1)))
+    y, _, _ = oracle_lib.forward_tokens(L, range(5))
+    np.testing.assert_allclose(y, np.tile(np.arange(1, 9.0), (5, 1)), rtol=1e-15)
+
+
+# ------------------------------------------------------------ statistics --
+
+def test_load_balance_loss_ends_and_cv(oracle_lib):
+    """Go chapter: loss 1 when uniform, N when concentrated, 0 when empty.
+    With population variance, loss = 1 + CV^2(Load) for any counts."""
+    g = GOLD["load_balance_ends"]
+    for N in (2, 6, 8, 256):
+        assert oracle_lib.load_stats(np.full(N, 5))[2] == g["uniform"]
+        one = np.zeros(N, np.int32)
+        one[N // 3] = 17
+        assert oracle_lib.load_stats(one)[2] == pytest.approx(N, rel=1e-15)
+        assert oracle_lib.load_stats(np.zeros(N, np.int32))[2] == 0.0
+    rng = np.random.default_rng(14)
+    for _ in range(20):
+        cnt = rng.integers(0, 100, 16)
+        cv_imp, cv_load, lb = oracle_lib.load_stats(cnt, cnt * 0.5)
+        assert lb == pytest.approx(1.0 + cv_load, rel=1e-13)
+        m = cnt.mean()
+        assert cv_load == pytest.approx(cnt.var() / m / m, rel=1e-12)
+        assert cv_imp == pytest.approx(cv_load, rel=1e-12)
+    assert oracle_lib.load_stats(np.int32([1, 0, 0, 0]))[1] == pytest.approx(3.0)
+
+
+def test_parameter_accounting(oracle_lib):
+    """Go chapter, 'Parameter accounting': at 8 experts / top-2 the experts'
+    total is 4x the active count; Total = d*E + E*P_e, Active = d*E + k*P_e."""
+    from synthetic import MIXTRAL, TINY
+    g = GOLD["expert_total_over_active"]
+    for cfg in (TINY, MIXTRAL):
+        assert (cfg.E, cfg.k) == (g["E"], g["k"])
+        tot, act = oracle_lib.param_counts(cfg)
+        router = cfg.d * cfg.E
+        assert (tot - router) == g["ratio"] * (act - router)
+    tot, act = oracle_lib.param_counts(TINY)
+    assert (tot - 512, act - 512) == (262144, 65536)
+    tot, act = oracle_lib.param_counts(MIXTRAL)
+    assert (tot - 4096 * 8, act - 4096 * 8) == (1409286144, 352321536)
+
+
+def test_invalid_configs_rejected(oracle_lib):
+    L = random_layer(15, T=4, d=8, h=8, E=4, k=2)
+    L.cfg = L.cfg.with_(k=5)
+    with pytest.raises(ValueError):
+        oracle_lib.route(L)
+    L.cfg = L.cfg.with_(k=0)
+    with pytest.raises(ValueError):
+        oracle_lib.route(L)
