@@ -1,0 +1,194 @@
+"""Benchmark of the MoE layer forward on one MI355X.
+
+One step = one pass of the whole hot path over one batch of synthetic
+tokens already resident in HBM: router + KeepTopK + softmax, grouping by
+expert, expert up projection + activation, down projection, gate-weighted
+combine, and the side statistics (counts, Importance, CV^2, load-balance
+loss).  The step issues the same kernels as moe_forward, through the stage
+entry points, so that the dominant kernel (the expert up projection) can
+be bracketed with HIP events on the stream it runs on.
+
+Prints one JSON line.  Default workload: the Mixtral-8x7B-shape layer
+(T=4096, d=4096, h=14336, 8 experts, top-2, SwiGLU, bf16).
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+METRIC = "MoE layer tokens/s + grouped-GEMM TFLOP/s (% MFMA peak); decode HBM GB/s"
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--workload", default="mixtral-8x7b")
+    p.add_argument("--cpu-seconds", type=float, default=15.0,
+                   help="target CPU time of the oracle baseline sample")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--traffic", default=None,
+                   help="JSON file with measured FETCH/WRITE bytes of the dominant kernel")
+    return p.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on one GPU only: this build has no multi-GPU path "
+              "(expert parallelism is a design note, not code)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import synthetic
+    from sparse_mixture_experts_07_amd import binding as B
+    from sparse_mixture_experts_07_amd.device import DeviceLayer, Forward
+
+    cfg = synthetic.BY_NAME[args.workload]
+    t_gen = time.time()
+    L = synthetic.make_inputs(cfg)
+    dl = DeviceLayer.upload(L)
+    gen_s = time.time() - t_gen
+    c, W = dl.cfg, dl.weights()
+    T, k, E, d, h = cfg.T, cfg.k, cfg.E, cfg.d, cfg.h
+    dev = dl.x.device
+    dt = dl.act_dtype
+    R = B.moe_grouped_rows(c)
+
+    idx = torch.empty((T, k), dtype=torch.int32, device=dev)
+    tw = torch.empty((T, k), dtype=torch.float32, device=dev)
+    counts = torch.empty(E, dtype=torch.int32, device=dev)
+    offsets = torch.empty(E + 1, dtype=torch.int32, device=dev)
+    perm_src = torch.empty(T * k, dtype=torch.int32, device=dev)
+    pos = torch.empty(T * k, dtype=torch.int32, device=dev)
+    imp = torch.empty(E, dtype=torch.float32, device=dev)
+    stats = torch.empty(3, dtype=torch.float64, device=dev)
+    x_perm = torch.empty((T * k, d), dtype=dt, device=dev)
+    hidden = torch.empty((R, h), dtype=dt, device=dev)
+    y_perm = torch.empty((R, d), dtype=dt, device=dev)
+    y = torch.empty((T, d), dtype=dt, device=dev)
+    ws = torch.empty(B.moe_workspace_bytes(c), dtype=torch.uint8, device=dev)
+
+    def step(ev=None):
+        B.moe_route(c, dl.x, dl.w_gate, dl.b_gate, idx, tw, counts)
+        B.moe_permute(c, idx, tw, dl.x, offsets, perm_src, pos, imp, stats, x_perm, ws)
+        if ev is not None:
+            ev[0].record()
+        B.moe_expert_up(c, W, x_perm, dl.x, offsets, hidden)
+        if ev is not None:
+            ev[1].record()
+        B.moe_expert_down(c, W, hidden, offsets, y_perm)
+        B.moe_combine(c, y_perm, pos, tw, y)
+
+    # the stage sequence is the moe_forward sequence: check once, bitwise
+    fw = Forward(dl)
+    fw()
+    step()
+    torch.cuda.synchronize()
+    same = torch.equal(fw.y.view(torch.int16 if dt == torch.bfloat16 else torch.int32),
+                       y.view(torch.int16 if dt == torch.bfloat16 else torch.int32))
+    del fw
+
+    for _ in range(args.warmup):
+        step()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    loop0 = torch.cuda.Event(enable_timing=True)
+    loop1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    loop0.record()
+    for i in range(args.steps):
+        step(evs[i])
+    loop1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = loop0.elapsed_time(loop1) / args.steps
+    up_ms = [a.elapsed_time(b) for a, b in evs]
+    up_avg = float(np.mean(up_ms))
+
+    cnt = counts.cpu().numpy()
+    touched = int((cnt > 0).sum())
+    n_up = cfg.n_up
+    rows = T * k + cfg.S * T
+    up_flops = 2.0 * rows * d * n_up
+    layer_flops = float(cfg.expert_flops())
+    es = 2 if cfg.dtype == synthetic.BF16 else 4
+    up_w_bytes = (touched + cfg.S) * n_up * d * es
+    down_w_bytes = (touched + cfg.S) * d * h * es
+    up_bytes = up_w_bytes + (T * k + cfg.S * T) * (d + h) * es   # weights + A read + H write
+    decode = (T * k) / E < 32
+
+    tokens_per_s = T / (ms_step / 1e3)
+    if decode:
+        roof = {"bound": "hbm", "achieved": up_bytes / (up_avg / 1e3) / 1e9,
+                "peak": PEAK_HBM_GBS, "unit": "GB/s"}
+    else:
+        roof = {"bound": "mfma", "achieved": up_flops / (up_avg / 1e3) / 1e12,
+                "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s"}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof["kernel"] = "gemm_bf16_kernel (expert up projection + activation)"
+    roof["avg_ms"] = up_avg
+    roof["traffic"] = None
+    if args.traffic and os.path.exists(args.traffic):
+        roof["traffic"] = json.load(open(args.traffic)).get(args.workload)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        nthr = oracle.max_threads()
+        probe = list(range(min(T, max(2, nthr))))
+        t1 = time.perf_counter()
+        oracle.forward_tokens(L, probe)
+        per_tok = (time.perf_counter() - t1) / len(probe)
+        n = int(min(T, max(len(probe), args.cpu_seconds / max(per_tok, 1e-9))))
+        sample = np.linspace(0, T - 1, n).astype(np.int64)
+        t1 = time.perf_counter()
+        oracle.forward_tokens(L, sample)
+        el = time.perf_counter() - t1
+        cpu = {"value": n / el, "unit": "tokens/s", "cores": nthr, "kind": "oracle",
+               "sample": f"{n} of {T} tokens (evenly spaced), full routing + "
+                         f"expert FFNs + combine per token, {el:.1f} s"}
+
+    out = {
+        "metric": METRIC,
+        "value": tokens_per_s,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if cfg.dtype == synthetic.BF16 else "f32",
+        "data": "synthetic (seeded numpy PCG64, seed 0; random-init weights)",
+        "config": {"workload": cfg.name, "T": T, "d_model": d, "d_hidden": h,
+                   "experts": E, "top_k": k, "shared": cfg.S,
+                   "act": "swiglu" if cfg.act == synthetic.SWIGLU else "gelu",
+                   "router_bias": cfg.router_bias},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "layer_tflops": layer_flops / (ms_step / 1e3) / 1e12,
+        "layer_frac_mfma_peak": layer_flops / (ms_step / 1e3) / 1e12 / PEAK_BF16_TFLOPS,
+        "expert_weight_gbs": (up_w_bytes + down_w_bytes) / (ms_step / 1e3) / 1e9,
+        "experts_touched": touched,
+        "wall_s_timed": wall,
+        "input_gen_upload_s": gen_s,
+        "stage_sequence_equals_moe_forward": bool(same),
+    }
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,200 @@
+/*
+ * moe.h - C ABI of the MI355X (gfx950) sparsely-gated MoE layer forward.
+ *
+ * The layer computes y = sum_i G(x)_i * E_i(x) with
+ * G(x) = softmax(KeepTopK(x W_g, k)): a linear router, the k largest scores
+ * kept (ties to the lower expert index), a softmax over those k only, the k
+ * selected expert FFNs, and their gate-weighted sum ("Sparsely-Gated MoE"
+ * paper summary on Qiita, sections "Sparsely-Gated MoE layer formula" and
+ * "Gating: Noisy Top-k Softmax", inference form without noise).  The
+ * dispatch -> compute -> collect split of the calls below follows the
+ * "Expert Backend" section of "Understanding MoE in Transformers"; the
+ * per-token loop it replaces is Route/Forward in section 2 "Routing" of the
+ * Go book chapter "MoE (Mixture of Experts)".
+ *
+ * Conventions shared by every call:
+ *  - Device buffers are plain device pointers, dense row-major, 16-byte
+ *    aligned, owned by the caller.  The library allocates no device memory
+ *    and keeps no state between calls; scratch space comes from a caller
+ *    workspace of at least moe_workspace_bytes() bytes.
+ *  - Each call validates its arguments on the host, then only enqueues
+ *    kernels on `stream`; it never synchronises or reads device memory, so
+ *    the calls can be captured in a HIP graph.  On any error status nothing
+ *    has been enqueued, except MOE_ERR_HIP (a launch failed).
+ *  - T = num_tokens may be 0: counts, importance and stats are then zeroed
+ *    and no other buffer is touched.
+ *  - dtype (x, expert weights, hidden rows, y) is bf16 or fp32; the router
+ *    weights W_g and b_g are always fp32 and the router scores are fp32.
+ *  - Results are deterministic: no floating-point atomics anywhere.
+ *  - Non-finite inputs give undefined (but memory-safe) results.
+ *
+ * Sizes: 1 <= E <= 256, 1 <= k <= E, S (shared always-on experts) is 0 or 1
+ * and needs SwiGLU, d and h are multiples of 64, T*k + S*T < 2^31.
+ */
+#ifndef MOE_MI355X_H
+#define MOE_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOE_ABI_VERSION 1
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARGUMENT = 1,    /* NULL/misaligned pointer, k > E, ... */
+  MOE_ERR_UNSUPPORTED = 2,         /* valid but outside the sizes above */
+  MOE_ERR_WORKSPACE_TOO_SMALL = 3,
+  MOE_ERR_HIP = 4                  /* a kernel launch failed */
+} moe_status_t;
+
+typedef enum { MOE_DTYPE_F32 = 0, MOE_DTYPE_BF16 = 1 } moe_dtype_t;
+
+/* Expert FFN.  GELU: Linear(d->h) + bias -> exact GELU (x*Phi(x)) ->
+ * Linear(h->d) + bias, the GPT-2 style expert of the techfeed summary
+ * ("How MoE works: split the FFN") and the Go chapter.  SwiGLU: silu(x W1^T)
+ * * (x W3^T) -> W2, no biases, the Mixtral-style expert the Go chapter's
+ * "What was simplified" names. */
+typedef enum { MOE_ACT_GELU = 0, MOE_ACT_SWIGLU = 1 } moe_act_t;
+
+typedef struct {
+  int64_t num_tokens;  /* T */
+  int32_t d_model;     /* d */
+  int32_t d_hidden;    /* h */
+  int32_t num_experts; /* E, routed experts */
+  int32_t top_k;       /* k */
+  int32_t num_shared;  /* S, 0 or 1: always-on expert with weight 1 */
+  int32_t act;         /* moe_act_t */
+  int32_t dtype;       /* moe_dtype_t */
+} moe_config_t;
+
+/* Expert weights, all packed over experts into single tensors ("Weight
+ * Loading Refactor" section of "Understanding MoE in Transformers").
+ * Every matrix is [out_features, in_features] with in_features contiguous. */
+typedef struct {
+  const float *w_gate;   /* router W_g [E, d] fp32 (required) */
+  const float *b_gate;   /* router bias [E] fp32, or NULL (added to the score) */
+  const void *w_up;      /* GELU: W1 [E, h, d]; SwiGLU: [E, 2h, d] with rows
+                            0..h-1 the gate (w1) and rows h..2h-1 the up (w3) */
+  const void *b_up;      /* GELU only: [E, h] or NULL; must be NULL for SwiGLU */
+  const void *w_down;    /* W2 [E, d, h] */
+  const void *b_down;    /* GELU only: [E, d] or NULL; must be NULL for SwiGLU */
+  const void *w_up_shared;   /* S = 1: [1, 2h, d], else NULL */
+  const void *w_down_shared; /* S = 1: [1, d, h], else NULL */
+} moe_weights_t;
+
+int moe_abi_version(void);
+const char *moe_status_string(moe_status_t status);
+
+/* Workspace bytes needed by moe_forward (also enough for moe_permute and
+ * moe_expert_ffn).  Pure host; *bytes is 0 when T == 0. */
+moe_status_t moe_workspace_bytes(const moe_config_t *cfg, size_t *bytes);
+
+/* Rows of the grouped (expert-sorted) buffers: R = T*k + S*T.  Rows
+ * [0, T*k) hold the routed assignments grouped by expert; rows
+ * [T*k, T*k + T) hold the shared expert's rows in token order. */
+moe_status_t moe_grouped_rows(const moe_config_t *cfg, int64_t *rows);
+
+/* Router + KeepTopK + softmax over the kept scores (Go chapter section 2,
+ * Route; Qiita summary, "Gating: Noisy Top-k Softmax", inference form).
+ *   x        [T, d] dtype            (device, in)
+ *   w_gate   [E, d] fp32, b_gate [E] fp32 or NULL (device, in)
+ *   topk_idx [T, k] int32  (out) expert indices in descending score order;
+ *            equal scores keep the lower index first (a stable sort)
+ *   topk_w   [T, k] fp32   (out) exp(s_j - s_0) / sum_i exp(s_i - s_0)
+ *   counts   [E] int32     (out) tokens routed to each expert (Stats)
+ *   logits   [T, E] fp32 or NULL (out) router scores: for each (t, e)
+ *            s = +0; s = fma(x[t,i], W_g[e,i], s) for i = 0..d-1 in order;
+ *            s = s + b_g[e]; all in fp32 */
+moe_status_t moe_route(const moe_config_t *cfg, const void *x,
+                       const float *w_gate, const float *b_gate,
+                       int32_t *topk_idx, float *topk_w, int32_t *counts,
+                       float *logits, hipStream_t stream);
+
+/* Dispatch: stable grouping of the T*k assignments by expert (ties by the
+ * flat index t*k + j) and the row move x -> x_perm ("Expert Backend":
+ * sort and group tokens by expert id before the grouped GEMM).
+ *   topk_idx, topk_w [T, k]   (device, in) as written by moe_route
+ *   x          [T, d] dtype   (device, in)
+ *   offsets    [E + 1] int32  (out) group starts; offsets[E] = T*k
+ *   perm_src   [T*k] int32    (out) source token of grouped row p
+ *   pos        [T*k] int32    (out) grouped row of assignment (t, j)
+ *   importance [E] fp32       (out) Importance(X)_e = sum of the kept
+ *              weights routed to e (Qiita summary, "Load-balancing losses"),
+ *              summed in group order
+ *   stats      [3] double or NULL (out) CV^2(Importance), CV^2(Load) with
+ *              Load = counts, and the load-balance loss E*sum_e f_e^2 of the
+ *              Go chapter's section 3 (population variance; 0 if empty)
+ *   x_perm     [T*k, d] dtype (out) x_perm[p] = x[perm_src[p]]
+ *   ws         workspace >= moe_workspace_bytes() */
+moe_status_t moe_permute(const moe_config_t *cfg, const int32_t *topk_idx,
+                         const float *topk_w, const void *x, int32_t *offsets,
+                         int32_t *perm_src, int32_t *pos, float *importance,
+                         double *stats, void *x_perm, void *ws,
+                         size_t ws_bytes, hipStream_t stream);
+
+/* Up projection + activation of every expert group (grouped GEMM on bf16
+ * MFMA, fp32 accumulation; fp32 SIMT for dtype fp32).  Experts with no rows
+ * are skipped (conditional computation: Qiita summary, "Sparsely-Gated MoE
+ * layer formula").
+ *   x_perm [T*k, d], x [T, d] (shared expert input; may be NULL if S = 0)
+ *   offsets [E + 1] int32
+ *   hidden [R, h] dtype (out) activation rows, R = T*k + S*T */
+moe_status_t moe_expert_up(const moe_config_t *cfg, const moe_weights_t *w,
+                           const void *x_perm, const void *x,
+                           const int32_t *offsets, void *hidden,
+                           hipStream_t stream);
+
+/* Down projection of every group: y_perm[r] = W2[e] hidden[r] (+ b2[e]).
+ *   hidden [R, h] dtype (in), y_perm [R, d] dtype (out) */
+moe_status_t moe_expert_down(const moe_config_t *cfg, const moe_weights_t *w,
+                             const void *hidden, const int32_t *offsets,
+                             void *y_perm, hipStream_t stream);
+
+/* moe_expert_up then moe_expert_down, hidden rows in the workspace. */
+moe_status_t moe_expert_ffn(const moe_config_t *cfg, const moe_weights_t *w,
+                            const void *x_perm, const void *x,
+                            const int32_t *offsets, void *y_perm, void *ws,
+                            size_t ws_bytes, hipStream_t stream);
+
+/* Collect: y[t] = sum_{j<k} topk_w[t,j] * y_perm[pos[t*k+j]] (+ the shared
+ * row y_perm[T*k + t] with weight 1), accumulated in fp32 in slot order and
+ * rounded once to dtype (Go chapter section 2, Forward: out += w * y).
+ *   y_perm [R, d], pos [T*k], topk_w [T, k] (in); y [T, d] dtype (out) */
+moe_status_t moe_combine(const moe_config_t *cfg, const void *y_perm,
+                         const int32_t *pos, const float *topk_w, void *y,
+                         hipStream_t stream);
+
+/* The whole layer: route, permute, expert up/down, combine.
+ *   x [T, d] (in); y [T, d] (out); topk_idx, topk_w, counts, importance as
+ *   above (out, required); stats [3] double or NULL (out). */
+moe_status_t moe_forward(const moe_config_t *cfg, const moe_weights_t *w,
+                         const void *x, void *y, int32_t *topk_idx,
+                         float *topk_w, int32_t *counts, float *importance,
+                         double *stats, void *ws, size_t ws_bytes,
+                         hipStream_t stream);
+
+/* Host-only helpers. */
+
+/* Parameter accounting of the Go chapter's section 1: Total = d*E + E*P_e,
+ * Active = d*E + k*P_e, with P_e = 2*d*h (GELU) or 3*d*h (SwiGLU); a shared
+ * expert adds P_e to both; biases are not counted. */
+moe_status_t moe_param_counts(const moe_config_t *cfg, int64_t *total,
+                              int64_t *active);
+
+/* Side statistics from host arrays: CV^2(importance), CV^2(counts) and the
+ * load-balance loss E * sum_e (counts_e / sum counts)^2 (0 when the sum is
+ * 0); population variance, CV^2 = 0 when the mean is 0.  importance may be
+ * NULL (then *cv2_importance = 0). */
+moe_status_t moe_load_stats(const int32_t *counts, const float *importance,
+                            int32_t num_experts, double *cv2_importance,
+                            double *cv2_load, double *load_balance);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_MI355X_H */

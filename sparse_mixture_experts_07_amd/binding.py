@@ -1,0 +1,241 @@
+"""ctypes binding of libmoe.so (the C ABI declared in include/moe.h).
+
+Argument marshalling only: every function has the name of its C entry
+point, turns torch device tensors into raw device pointers and the current
+torch stream into a hipStream_t, calls the library, and raises MoeError on
+a non-OK status.  No step of the layer runs in Python; if libmoe.so is
+missing, loading fails loudly (there is no fallback path).
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+from typing import Optional
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmoe.so")
+
+MOE_OK = 0
+MOE_ERR_INVALID_ARGUMENT = 1
+MOE_ERR_UNSUPPORTED = 2
+MOE_ERR_WORKSPACE_TOO_SMALL = 3
+MOE_ERR_HIP = 4
+
+MOE_DTYPE_F32 = 0
+MOE_DTYPE_BF16 = 1
+MOE_ACT_GELU = 0
+MOE_ACT_SWIGLU = 1
+
+EXPORTS = (
+    "moe_abi_version", "moe_status_string", "moe_workspace_bytes",
+    "moe_grouped_rows", "moe_route", "moe_permute", "moe_expert_up",
+    "moe_expert_down", "moe_expert_ffn", "moe_combine", "moe_forward",
+    "moe_param_counts", "moe_load_stats",
+)
+
+
+class MoeError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        self.status = status
+        super().__init__(f"{fn}: {status_string(status)} (status {status})")
+
+
+class MoeConfig(C.Structure):
+    _fields_ = [("num_tokens", C.c_int64), ("d_model", C.c_int32),
+                ("d_hidden", C.c_int32), ("num_experts", C.c_int32),
+                ("top_k", C.c_int32), ("num_shared", C.c_int32),
+                ("act", C.c_int32), ("dtype", C.c_int32)]
+
+
+class MoeWeights(C.Structure):
+    _fields_ = [("w_gate", C.c_void_p), ("b_gate", C.c_void_p),
+                ("w_up", C.c_void_p), ("b_up", C.c_void_p),
+                ("w_down", C.c_void_p), ("b_down", C.c_void_p),
+                ("w_up_shared", C.c_void_p), ("w_down_shared", C.c_void_p)]
+
+
+_lib = None
+
+
+def lib():
+    """Load libmoe.so once; raise if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is missing: build it with __graft_entry__.build() "
+                "(hipcc --offload-arch=gfx950); there is no fallback path")
+        L = C.CDLL(LIB_PATH)
+        P, S = C.c_void_p, C.c_int
+        L.moe_abi_version.restype = C.c_int
+        L.moe_status_string.restype = C.c_char_p
+        L.moe_status_string.argtypes = [S]
+        sig = {
+            "moe_workspace_bytes": [P, P],
+            "moe_grouped_rows": [P, P],
+            "moe_route": [P, P, P, P, P, P, P, P, P],
+            "moe_permute": [P, P, P, P, P, P, P, P, P, P, P, C.c_size_t, P],
+            "moe_expert_up": [P, P, P, P, P, P, P],
+            "moe_expert_down": [P, P, P, P, P, P],
+            "moe_expert_ffn": [P, P, P, P, P, P, P, C.c_size_t, P],
+            "moe_combine": [P, P, P, P, P, P],
+            "moe_forward": [P, P, P, P, P, P, P, P, P, P, C.c_size_t, P],
+            "moe_param_counts": [P, P, P],
+            "moe_load_stats": [P, P, C.c_int32, P, P, P],
+        }
+        for name, args in sig.items():
+            fn = getattr(L, name)
+            fn.argtypes = args
+            fn.restype = C.c_int
+        _lib = L
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return lib().moe_status_string(int(status)).decode()
+
+
+def moe_abi_version() -> int:
+    return lib().moe_abi_version()
+
+
+def moe_status_string(status: int) -> str:
+    return status_string(status)
+
+
+# ------------------------------------------------------------ marshalling --
+
+def _ptr(t) -> Optional[int]:
+    """Device pointer of a tensor (or a raw int / None passed through)."""
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    if not t.is_cuda:
+        raise ValueError("expected a device tensor")
+    if not t.is_contiguous():
+        raise ValueError("expected a contiguous tensor")
+    return t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _nbytes(t) -> int:
+    return t.numel() * t.element_size()
+
+
+def _check(fn: str, st: int) -> None:
+    if st != MOE_OK:
+        raise MoeError(fn, st)
+
+
+def config(T: int, d: int, h: int, E: int, k: int, act: int, dtype: int,
+           S: int = 0) -> MoeConfig:
+    return MoeConfig(int(T), int(d), int(h), int(E), int(k), int(S), int(act),
+                     int(dtype))
+
+
+def config_of(c) -> MoeConfig:
+    """From any object with T, d, h, E, k, S, act, dtype attributes."""
+    return config(c.T, c.d, c.h, c.E, c.k, c.act, c.dtype, c.S)
+
+
+def weights(w_gate, w_up, w_down, b_gate=None, b_up=None, b_down=None,
+            w_up_shared=None, w_down_shared=None) -> MoeWeights:
+    """Pointer struct; the caller keeps the tensors alive while it is used."""
+    return MoeWeights(_ptr(w_gate), _ptr(b_gate), _ptr(w_up), _ptr(b_up),
+                      _ptr(w_down), _ptr(b_down), _ptr(w_up_shared),
+                      _ptr(w_down_shared))
+
+
+# ------------------------------------------------------------ entry points --
+
+def moe_workspace_bytes(cfg: MoeConfig) -> int:
+    n = C.c_size_t()
+    _check("moe_workspace_bytes", lib().moe_workspace_bytes(C.byref(cfg), C.byref(n)))
+    return n.value
+
+
+def moe_grouped_rows(cfg: MoeConfig) -> int:
+    n = C.c_int64()
+    _check("moe_grouped_rows", lib().moe_grouped_rows(C.byref(cfg), C.byref(n)))
+    return n.value
+
+
+def moe_route(cfg, x, w_gate, b_gate, topk_idx, topk_w, counts, logits=None,
+              stream=None) -> None:
+    _check("moe_route", lib().moe_route(
+        C.byref(cfg), _ptr(x), _ptr(w_gate), _ptr(b_gate), _ptr(topk_idx),
+        _ptr(topk_w), _ptr(counts), _ptr(logits), _stream(stream)))
+
+
+def moe_permute(cfg, topk_idx, topk_w, x, offsets, perm_src, pos, importance,
+                stats, x_perm, ws, ws_bytes=None, stream=None) -> None:
+    nb = _nbytes(ws) if ws_bytes is None and ws is not None else (ws_bytes or 0)
+    _check("moe_permute", lib().moe_permute(
+        C.byref(cfg), _ptr(topk_idx), _ptr(topk_w), _ptr(x), _ptr(offsets),
+        _ptr(perm_src), _ptr(pos), _ptr(importance), _ptr(stats), _ptr(x_perm),
+        _ptr(ws), nb, _stream(stream)))
+
+
+def moe_expert_up(cfg, w: MoeWeights, x_perm, x, offsets, hidden,
+                  stream=None) -> None:
+    _check("moe_expert_up", lib().moe_expert_up(
+        C.byref(cfg), C.byref(w), _ptr(x_perm), _ptr(x), _ptr(offsets),
+        _ptr(hidden), _stream(stream)))
+
+
+def moe_expert_down(cfg, w: MoeWeights, hidden, offsets, y_perm,
+                    stream=None) -> None:
+    _check("moe_expert_down", lib().moe_expert_down(
+        C.byref(cfg), C.byref(w), _ptr(hidden), _ptr(offsets), _ptr(y_perm),
+        _stream(stream)))
+
+
+def moe_expert_ffn(cfg, w: MoeWeights, x_perm, x, offsets, y_perm, ws,
+                   ws_bytes=None, stream=None) -> None:
+    nb = _nbytes(ws) if ws_bytes is None and ws is not None else (ws_bytes or 0)
+    _check("moe_expert_ffn", lib().moe_expert_ffn(
+        C.byref(cfg), C.byref(w), _ptr(x_perm), _ptr(x), _ptr(offsets),
+        _ptr(y_perm), _ptr(ws), nb, _stream(stream)))
+
+
+def moe_combine(cfg, y_perm, pos, topk_w, y, stream=None) -> None:
+    _check("moe_combine", lib().moe_combine(
+        C.byref(cfg), _ptr(y_perm), _ptr(pos), _ptr(topk_w), _ptr(y),
+        _stream(stream)))
+
+
+def moe_forward(cfg, w: MoeWeights, x, y, topk_idx, topk_w, counts,
+                importance, stats, ws, ws_bytes=None, stream=None) -> None:
+    nb = _nbytes(ws) if ws_bytes is None and ws is not None else (ws_bytes or 0)
+    _check("moe_forward", lib().moe_forward(
+        C.byref(cfg), C.byref(w), _ptr(x), _ptr(y), _ptr(topk_idx),
+        _ptr(topk_w), _ptr(counts), _ptr(importance), _ptr(stats), _ptr(ws),
+        nb, _stream(stream)))
+
+
+def moe_param_counts(cfg: MoeConfig):
+    tot, act = C.c_int64(), C.c_int64()
+    _check("moe_param_counts",
+           lib().moe_param_counts(C.byref(cfg), C.byref(tot), C.byref(act)))
+    return tot.value, act.value
+
+
+def moe_load_stats(counts, importance=None):
+    """Host arrays (numpy int32 counts, float32 importance or None)."""
+    import numpy as np
+    cnt = np.ascontiguousarray(counts, dtype=np.int32)
+    imp = None if importance is None else np.ascontiguousarray(importance, dtype=np.float32)
+    a, b, c = C.c_double(), C.c_double(), C.c_double()
+    _check("moe_load_stats", lib().moe_load_stats(
+        cnt.ctypes.data, None if imp is None else imp.ctypes.data, int(cnt.size),
+        C.byref(a), C.byref(b), C.byref(c)))
+    return a.value, b.value, c.value

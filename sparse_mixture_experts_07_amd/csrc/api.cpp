@@ -1,0 +1,358 @@
+// api.cpp - the C ABI (include/moe.h): argument checks, workspace carving and
+// kernel launches.  Host code only; every kernel lives in the .hip files.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+
+#include "moe.h"
+
+namespace moe {
+hipError_t launch_fill_i32(int32_t *p, int n, int32_t v, hipStream_t s);
+hipError_t launch_route(bool bf16, const void *x, const float *wg, const float *bg,
+                        int T, int d, int E, int k, int32_t *idx, float *w,
+                        int32_t *counts, float *logits, hipStream_t s);
+int perm_num_segments(int64_t n);
+hipError_t launch_permute(const int32_t *idx, const float *w, const void *x, int T,
+                          int k, int E, int row_bytes, int32_t *offsets,
+                          int32_t *perm_src, int32_t *pos, float *importance,
+                          double *stats, void *x_perm, int32_t *hist,
+                          float *perm_w, hipStream_t s);
+hipError_t launch_expert_up_bf16(bool swiglu, const int32_t *offsets, int E, int S,
+                                 int T, int k, int d, int h, const void *x_perm,
+                                 const void *x, const void *w_up,
+                                 const void *w_up_shared, const void *b_up,
+                                 void *hidden, hipStream_t s);
+hipError_t launch_expert_down_bf16(const int32_t *offsets, int E, int S, int T, int k,
+                                   int d, int h, const void *hidden,
+                                   const void *w_down, const void *w_down_shared,
+                                   const void *b_down, void *y_perm, hipStream_t s);
+hipError_t launch_expert_up_f32(bool swiglu, const int32_t *offsets, int E, int S,
+                                int T, int k, int d, int h, const void *x_perm,
+                                const void *x, const void *w_up,
+                                const void *w_up_shared, const void *b_up,
+                                void *hidden, hipStream_t s);
+hipError_t launch_expert_down_f32(const int32_t *offsets, int E, int S, int T, int k,
+                                  int d, int h, const void *hidden,
+                                  const void *w_down, const void *w_down_shared,
+                                  const void *b_down, void *y_perm, hipStream_t s);
+hipError_t launch_combine(bool bf16, const void *y_perm, const int32_t *pos,
+                          const float *w, int T, int k, int d, int S, void *y,
+                          hipStream_t s);
+hipError_t launch_zero_stats(float *importance, int E, double *stats, hipStream_t s);
+}  // namespace moe
+
+namespace {
+
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool dev_ok(const void *p) { return p != nullptr && aligned16(p); }
+bool opt_ok(const void *p) { return p == nullptr || aligned16(p); }
+
+moe_status_t check_cfg(const moe_config_t *c) {
+  if (!c) return MOE_ERR_INVALID_ARGUMENT;
+  if (c->num_tokens < 0 || c->d_model <= 0 || c->d_hidden <= 0 ||
+      c->num_experts < 1 || c->top_k < 1 || c->top_k > c->num_experts ||
+      c->num_shared < 0)
+    return MOE_ERR_INVALID_ARGUMENT;
+  if ((c->act != MOE_ACT_GELU && c->act != MOE_ACT_SWIGLU) ||
+      (c->dtype != MOE_DTYPE_F32 && c->dtype != MOE_DTYPE_BF16))
+    return MOE_ERR_INVALID_ARGUMENT;
+  if (c->num_experts > 256 || c->num_shared > 1) return MOE_ERR_UNSUPPORTED;
+  if (c->num_shared == 1 && c->act != MOE_ACT_SWIGLU) return MOE_ERR_UNSUPPORTED;
+  if (c->d_model % 64 != 0 || c->d_hidden % 64 != 0) return MOE_ERR_UNSUPPORTED;
+  const int64_t rows = c->num_tokens * (c->top_k + c->num_shared);
+  if (rows >= (int64_t(1) << 31)) return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+moe_status_t check_weights(const moe_config_t *c, const moe_weights_t *w, bool up,
+                           bool down, bool router) {
+  if (!w) return MOE_ERR_INVALID_ARGUMENT;
+  if (router && !dev_ok(w->w_gate)) return MOE_ERR_INVALID_ARGUMENT;
+  if (router && !opt_ok(w->b_gate)) return MOE_ERR_INVALID_ARGUMENT;
+  const bool swi = c->act == MOE_ACT_SWIGLU;
+  if (up) {
+    if (!dev_ok(w->w_up) || !opt_ok(w->b_up)) return MOE_ERR_INVALID_ARGUMENT;
+    if (swi && w->b_up) return MOE_ERR_INVALID_ARGUMENT;
+    if (c->num_shared ? !dev_ok(w->w_up_shared) : w->w_up_shared != nullptr)
+      return MOE_ERR_INVALID_ARGUMENT;
+  }
+  if (down) {
+    if (!dev_ok(w->w_down) || !opt_ok(w->b_down)) return MOE_ERR_INVALID_ARGUMENT;
+    if (swi && w->b_down) return MOE_ERR_INVALID_ARGUMENT;
+    if (c->num_shared ? !dev_ok(w->w_down_shared) : w->w_down_shared != nullptr)
+      return MOE_ERR_INVALID_ARGUMENT;
+  }
+  return MOE_OK;
+}
+
+size_t elem_bytes(const moe_config_t *c) { return c->dtype == MOE_DTYPE_BF16 ? 2 : 4; }
+
+// Workspace regions, each 256-byte aligned, in this order.
+struct Layout {
+  size_t hist, perm_w, permute_end;   // moe_permute scratch
+  size_t offsets, perm_src, pos, x_perm, hidden, y_perm, total;  // moe_forward
+};
+
+Layout layout(const moe_config_t *c) {
+  const int64_t T = c->num_tokens, n = T * c->top_k;
+  const int64_t R = n + (int64_t)c->num_shared * T;
+  const size_t es = elem_bytes(c);
+  const int E = c->num_experts;
+  Layout L{};
+  size_t o = 0;
+  L.hist = o;      o += align_up(sizeof(int32_t) * (size_t)moe::perm_num_segments(n) * E);
+  L.perm_w = o;    o += align_up(sizeof(float) * (size_t)n);
+  L.permute_end = o;
+  L.offsets = o;   o += align_up(sizeof(int32_t) * (size_t)(E + 1));
+  L.perm_src = o;  o += align_up(sizeof(int32_t) * (size_t)n);
+  L.pos = o;       o += align_up(sizeof(int32_t) * (size_t)n);
+  L.x_perm = o;    o += align_up(es * (size_t)n * c->d_model);
+  L.hidden = o;    o += align_up(es * (size_t)R * c->d_hidden);
+  L.y_perm = o;    o += align_up(es * (size_t)R * c->d_model);
+  L.total = o;
+  return L;
+}
+
+size_t hidden_bytes(const moe_config_t *c) {
+  const int64_t R = c->num_tokens * (c->top_k + c->num_shared);
+  return align_up(elem_bytes(c) * (size_t)R * c->d_hidden);
+}
+
+template <typename T>
+T *at(void *ws, size_t off) {
+  return reinterpret_cast<T *>(static_cast<char *>(ws) + off);
+}
+
+moe_status_t hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
+
+// Pending errors of earlier, unrelated HIP calls are cleared so that a
+// launch status reflects this call only.
+void clear_pending_error() { (void)hipGetLastError(); }
+
+}  // namespace
+
+extern "C" {
+
+int moe_abi_version(void) { return MOE_ABI_VERSION; }
+
+const char *moe_status_string(moe_status_t s) {
+  switch (s) {
+    case MOE_OK: return "ok";
+    case MOE_ERR_INVALID_ARGUMENT: return "invalid argument";
+    case MOE_ERR_UNSUPPORTED: return "unsupported configuration";
+    case MOE_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
+    case MOE_ERR_HIP: return "HIP launch failed";
+  }
+  return "unknown status";
+}
+
+moe_status_t moe_workspace_bytes(const moe_config_t *cfg, size_t *bytes) {
+  moe_status_t st = check_cfg(cfg);
+  if (st != MOE_OK) return st;
+  if (!bytes) return MOE_ERR_INVALID_ARGUMENT;
+  *bytes = cfg->num_tokens == 0 ? 0 : layout(cfg).total;
+  return MOE_OK;
+}
+
+moe_status_t moe_grouped_rows(const moe_config_t *cfg, int64_t *rows) {
+  moe_status_t st = check_cfg(cfg);
+  if (st != MOE_OK) return st;
+  if (!rows) return MOE_ERR_INVALID_ARGUMENT;
+  *rows = cfg->num_tokens * (cfg->top_k + cfg->num_shared);
+  return MOE_OK;
+}
+
+moe_status_t moe_route(const moe_config_t *cfg, const void *x, const float *w_gate,
+                       const float *b_gate, int32_t *topk_idx, float *topk_w,
+                       int32_t *counts, float *logits, hipStream_t stream) {
+  moe_status_t st = check_cfg(cfg);
+  if (st != MOE_OK) return st;
+  if (!dev_ok(counts)) return MOE_ERR_INVALID_ARGUMENT;
+  const int T = (int)cfg->num_tokens;
+  if (T > 0 && (!dev_ok(x) || !dev_ok(w_gate) || !opt_ok(b_gate) ||
+                !dev_ok(topk_idx) || !dev_ok(topk_w) || !opt_ok(logits)))
+    return MOE_ERR_INVALID_ARGUMENT;
+  clear_pending_error();
+  return hip_status(moe::launch_route(cfg->dtype == MOE_DTYPE_BF16, x, w_gate, b_gate, T,
+                                      cfg->d_model, cfg->num_experts, cfg->top_k,
+                                      topk_idx, topk_w, counts, logits, stream));
+}
+
+moe_status_t moe_permute(const moe_config_t *cfg, const int32_t *topk_idx,
+                         const float *topk_w, const void *x, int32_t *offsets,
+                         int32_t *perm_src, int32_t *pos, float *importance,
+                         double *stats, void *x_perm, void *ws, size_t ws_bytes,
+                         hipStream_t stream) {
+  moe_status_t st = check_cfg(cfg);
+  if (st != MOE_OK) return st;
+  const int T = (int)cfg->num_tokens;
+  if (!dev_ok(offsets) || !dev_ok(importance) || !opt_ok(stats))
+    return MOE_ERR_INVALID_ARGUMENT;
+  if (T > 0 && (!dev_ok(topk_idx) || !dev_ok(topk_w) || !dev_ok(x) ||
+                !dev_ok(perm_src) || !dev_ok(pos) || !dev_ok(x_perm) || !dev_ok(ws)))
+    return MOE_ERR_INVALID_ARGUMENT;
+  const Layout L = layout(cfg);
+  if (T > 0 && ws_bytes < L.permute_end) return MOE_ERR_WORKSPACE_TOO_SMALL;
+  clear_pending_error();
+  if (T == 0) {
+    hipError_t e = moe::launch_fill_i32(offsets, cfg->num_experts + 1, 0, stream);
+    if (e != hipSuccess) return MOE_ERR_HIP;
+  }
+  return hip_status(moe::launch_permute(
+      topk_idx, topk_w, x, T, cfg->top_k, cfg->num_experts,
+      (int)(cfg->d_model * elem_bytes(cfg)), offsets, perm_src, pos, importance, stats,
+      x_perm, T ? at<int32_t>(ws, L.hist) : nullptr, T ? at<float>(ws, L.perm_w) : nullptr,
+      stream));
+}
+
+moe_status_t moe_expert_up(const moe_config_t *cfg, const moe_weights_t *w,
+                           const void *x_perm, const void *x, const int32_t *offsets,
+                           void *hidden, hipStream_t stream) {
+  moe_status_t st = check_cfg(cfg);
+  if (st != MOE_OK) return st;
+  if ((st = check_weights(cfg, w, true, false, false)) != MOE_OK) return st;
+  const int T = (int)cfg->num_tokens;
+  if (T == 0) return MOE_OK;
+  if (!dev_ok(x_perm) || !dev_ok(offsets) || !dev_ok(hidden) ||
+      (cfg->num_shared && !dev_ok(x)))
+    return MOE_ERR_INVALID_ARGUMENT;
+  clear_pending_error();
+  const bool swi = cfg->act == MOE_ACT_SWIGLU;
+  if (cfg->dtype == MOE_DTYPE_BF16)
+    return hip_status(moe::launch_expert_up_bf16(
+        swi, offsets, cfg->num_experts, cfg->num_shared, T, cfg->top_k, cfg->d_model,
+        cfg->d_hidden, x_perm, x, w->w_up, w->w_up_shared, w->b_up, hidden, stream));
+  return hip_status(moe::launch_expert_up_f32(
+      swi, offsets, cfg->num_experts, cfg->num_shared, T, cfg->top_k, cfg->d_model,
+      cfg->d_hidden, x_perm, x, w->w_up, w->w_up_shared, w->b_up, hidden, stream));
+}
+
+moe_status_t moe_expert_down(const moe_config_t *cfg, const moe_weights_t *w,
+                             const void *hidden, const int32_t *offsets, void *y_perm,
+                             hipStream_t stream) {
+  moe_status_t st = check_cfg(cfg);
+  if (st != MOE_OK) return st;
+  if ((st = check_weights(cfg, w, false, true, false)) != MOE_OK) return st;
+  const int T = (int)cfg->num_tokens;
+  if (T == 0) return MOE_OK;
+  if (!dev_ok(hidden) || !dev_ok(offsets) || !dev_ok(y_perm))
+    return MOE_ERR_INVALID_ARGUMENT;
+  clear_pending_error();
+  if (cfg->dtype == MOE_DTYPE_BF16)
+    return hip_status(moe::launch_expert_down_bf16(
+        offsets, cfg->num_experts, cfg->num_shared, T, cfg->top_k, cfg->d_model,
+        cfg->d_hidden, hidden, w->w_down, w->w_down_shared, w->b_down, y_perm, stream));
+  return hip_status(moe::launch_expert_down_f32(
+      offsets, cfg->num_experts, cfg->num_shared, T, cfg->top_k, cfg->d_model,
+      cfg->d_hidden, hidden, w->w_down, w->w_down_shared, w->b_down, y_perm, stream));
+}
+
+moe_status_t moe_expert_ffn(const moe_config_t *cfg, const moe_weights_t *w,
+                            const void *x_perm, const void *x, const int32_t *offsets,
+                            void *y_perm, void *ws, size_t ws_bytes, hipStream_t stream) {
+  moe_status_t st = check_cfg(cfg);
+  if (st != MOE_OK) return st;
+  if ((st = check_weights(cfg, w, true, true, false)) != MOE_OK) return st;
+  if (cfg->num_tokens == 0) return MOE_OK;
+  if (!dev_ok(ws)) return MOE_ERR_INVALID_ARGUMENT;
+  if (ws_bytes < hidden_bytes(cfg)) return MOE_ERR_WORKSPACE_TOO_SMALL;
+  if (!dev_ok(x_perm) || !dev_ok(offsets) || !dev_ok(y_perm) ||
+      (cfg->num_shared && !dev_ok(x)))
+    return MOE_ERR_INVALID_ARGUMENT;
+  if ((st = moe_expert_up(cfg, w, x_perm, x, offsets, ws, stream)) != MOE_OK) return st;
+  return moe_expert_down(cfg, w, ws, offsets, y_perm, stream);
+}
+
+moe_status_t moe_combine(const moe_config_t *cfg, const void *y_perm, const int32_t *pos,
+                         const float *topk_w, void *y, hipStream_t stream) {
+  moe_status_t st = check_cfg(cfg);
+  if (st != MOE_OK) return st;
+  const int T = (int)cfg->num_tokens;
+  if (T == 0) return MOE_OK;
+  if (!dev_ok(y_perm) || !dev_ok(pos) || !dev_ok(topk_w) || !dev_ok(y))
+    return MOE_ERR_INVALID_ARGUMENT;
+  clear_pending_error();
+  return hip_status(moe::launch_combine(cfg->dtype == MOE_DTYPE_BF16, y_perm, pos,
+                                            topk_w, T, cfg->top_k, cfg->d_model,
+                                            cfg->num_shared, y, stream));
+}
+
+moe_status_t moe_forward(const moe_config_t *cfg, const moe_weights_t *w, const void *x,
+                         void *y, int32_t *topk_idx, float *topk_w, int32_t *counts,
+                         float *importance, double *stats, void *ws, size_t ws_bytes,
+                         hipStream_t stream) {
+  moe_status_t st = check_cfg(cfg);
+  if (st != MOE_OK) return st;
+  if ((st = check_weights(cfg, w, true, true, true)) != MOE_OK) return st;
+  const int T = (int)cfg->num_tokens;
+  if (!dev_ok(counts) || !dev_ok(importance) || !opt_ok(stats))
+    return MOE_ERR_INVALID_ARGUMENT;
+  if (T > 0 && (!dev_ok(x) || !dev_ok(y) || !dev_ok(topk_idx) || !dev_ok(topk_w) ||
+                !dev_ok(ws)))
+    return MOE_ERR_INVALID_ARGUMENT;
+  const Layout L = layout(cfg);
+  if (T > 0 && ws_bytes < L.total) return MOE_ERR_WORKSPACE_TOO_SMALL;
+  if (T == 0) {
+    if ((st = moe_route(cfg, x, w->w_gate, w->b_gate, topk_idx, topk_w, counts, nullptr,
+                        stream)) != MOE_OK)
+      return st;
+    clear_pending_error();
+    return hip_status(moe::launch_zero_stats(importance, cfg->num_experts, stats, stream));
+  }
+  int32_t *offsets = at<int32_t>(ws, L.offsets);
+  int32_t *perm_src = at<int32_t>(ws, L.perm_src);
+  int32_t *pos = at<int32_t>(ws, L.pos);
+  void *x_perm = at<char>(ws, L.x_perm);
+  void *hidden = at<char>(ws, L.hidden);
+  void *y_perm = at<char>(ws, L.y_perm);
+  if ((st = moe_route(cfg, x, w->w_gate, w->b_gate, topk_idx, topk_w, counts, nullptr,
+                      stream)) != MOE_OK)
+    return st;
+  if ((st = moe_permute(cfg, topk_idx, topk_w, x, offsets, perm_src, pos, importance, stats,
+                        x_perm, ws, L.permute_end, stream)) != MOE_OK)
+    return st;
+  if ((st = moe_expert_up(cfg, w, x_perm, x, offsets, hidden, stream)) != MOE_OK) return st;
+  if ((st = moe_expert_down(cfg, w, hidden, offsets, y_perm, stream)) != MOE_OK) return st;
+  return moe_combine(cfg, y_perm, pos, topk_w, y, stream);
+}
+
+moe_status_t moe_param_counts(const moe_config_t *cfg, int64_t *total, int64_t *active) {
+  moe_status_t st = check_cfg(cfg);
+  if (st != MOE_OK) return st;
+  if (!total || !active) return MOE_ERR_INVALID_ARGUMENT;
+  const int64_t pe = (int64_t)(cfg->act == MOE_ACT_GELU ? 2 : 3) * cfg->d_model * cfg->d_hidden;
+  const int64_t router = (int64_t)cfg->d_model * cfg->num_experts;
+  *total = router + (cfg->num_experts + cfg->num_shared) * pe;
+  *active = router + (cfg->top_k + cfg->num_shared) * pe;
+  return MOE_OK;
+}
+
+moe_status_t moe_load_stats(const int32_t *counts, const float *importance, int32_t E,
+                            double *cv2_importance, double *cv2_load, double *load_balance) {
+  if (!counts || E < 1 || !cv2_importance || !cv2_load || !load_balance)
+    return MOE_ERR_INVALID_ARGUMENT;
+  double sc = 0.0, si = 0.0;
+  for (int e = 0; e < E; ++e) {
+    sc += counts[e];
+    if (importance) si += importance[e];
+  }
+  const double mc = sc / E, mi = si / E;
+  double vc = 0.0, vi = 0.0, f2 = 0.0;
+  for (int e = 0; e < E; ++e) {
+    vc += (counts[e] - mc) * (counts[e] - mc);
+    if (importance) vi += (importance[e] - mi) * (importance[e] - mi);
+    if (sc != 0.0) f2 += (counts[e] / sc) * (counts[e] / sc);
+  }
+  *cv2_load = mc == 0.0 ? 0.0 : (vc / E) / (mc * mc);
+  *cv2_importance = (!importance || mi == 0.0) ? 0.0 : (vi / E) / (mi * mi);
+  *load_balance = sc == 0.0 ? 0.0 : E * f2;
+  return MOE_OK;
+}
+
+}  // extern "C"

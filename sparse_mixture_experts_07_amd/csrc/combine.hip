@@ -1,0 +1,102 @@
+// combine.hip - collect: y[t] = sum_j w[t,j] * y_perm[pos[t*k+j]] (+ shared).
+//
+// Go book chapter "MoE (Mixture of Experts)", section 2 (Forward): the
+// output row accumulates weight * expert output for each kept expert in
+// slot order.  A gather (every token reads its k grouped rows) instead of a
+// scatter-add keeps the sum deterministic without floating-point atomics.
+// The shared always-on expert's row sits at grouped row T*k + t and enters
+// with weight 1.  fp32 accumulation, one rounding to the output dtype.
+#include "common.h"
+
+#pragma clang fp contract(off)
+
+namespace moe {
+
+constexpr int kCombineThreads = 256;
+
+template <bool BF16>
+__global__ __launch_bounds__(kCombineThreads) void combine_kernel(
+    const void *__restrict__ y_perm, const int32_t *__restrict__ pos,
+    const float *__restrict__ w, int T, int k, int d, int rows, int shared,
+    void *__restrict__ y) {
+  constexpr int VEC = BF16 ? 8 : 4;   // elements per 16-byte vector
+  __shared__ int ps[kMaxExperts];
+  __shared__ float wsh[kMaxExperts];
+  const int nvec = d / VEC;
+  const int routed = T * k;
+  for (int t = blockIdx.x; t < T; t += gridDim.x) {
+    __syncthreads();
+    for (int j = threadIdx.x; j < k; j += kCombineThreads) {
+      ps[j] = min(max(pos[(int64_t)t * k + j], 0), rows - 1);
+      wsh[j] = w[(int64_t)t * k + j];
+    }
+    __syncthreads();
+    for (int i = threadIdx.x; i < nvec; i += kCombineThreads) {
+      float acc[VEC];
+#pragma unroll
+      for (int q = 0; q < VEC; ++q) acc[q] = 0.0f;
+      for (int j = 0; j <= k; ++j) {
+        int row;
+        float wj;
+        if (j < k) {
+          row = ps[j];
+          wj = wsh[j];
+        } else {
+          if (!shared) break;
+          row = routed + t;
+          wj = 1.0f;
+        }
+        const uint4 v = reinterpret_cast<const uint4 *>(y_perm)[(int64_t)row * nvec + i];
+        float f[VEC];
+        if constexpr (BF16) {
+          const uint32_t u[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            f[2 * q] = __uint_as_float(u[q] << 16);
+            f[2 * q + 1] = __uint_as_float(u[q] & 0xffff0000u);
+          }
+        } else {
+          f[0] = __uint_as_float(v.x);
+          f[1] = __uint_as_float(v.y);
+          f[2] = __uint_as_float(v.z);
+          f[3] = __uint_as_float(v.w);
+        }
+        if (j < k) {
+#pragma unroll
+          for (int q = 0; q < VEC; ++q) acc[q] = __builtin_fmaf(wj, f[q], acc[q]);
+        } else {
+#pragma unroll
+          for (int q = 0; q < VEC; ++q) acc[q] = acc[q] + f[q];
+        }
+      }
+      uint4 o;
+      if constexpr (BF16) {
+        o.x = pack_bf16x2(acc[0], acc[1]);
+        o.y = pack_bf16x2(acc[2], acc[3]);
+        o.z = pack_bf16x2(acc[4], acc[5]);
+        o.w = pack_bf16x2(acc[6], acc[7]);
+      } else {
+        o.x = __float_as_uint(acc[0]);
+        o.y = __float_as_uint(acc[1]);
+        o.z = __float_as_uint(acc[2]);
+        o.w = __float_as_uint(acc[3]);
+      }
+      reinterpret_cast<uint4 *>(y)[(int64_t)t * nvec + i] = o;
+    }
+  }
+}
+
+hipError_t launch_combine(bool bf16, const void *y_perm, const int32_t *pos,
+                          const float *w, int T, int k, int d, int S, void *y,
+                          hipStream_t s) {
+  if (T == 0) return hipSuccess;
+  const int rows = T * k + S * T;
+  const int blocks = T < 16384 ? T : 16384;
+  if (bf16)
+    combine_kernel<true><<<blocks, kCombineThreads, 0, s>>>(y_perm, pos, w, T, k, d, rows, S, y);
+  else
+    combine_kernel<false><<<blocks, kCombineThreads, 0, s>>>(y_perm, pos, w, T, k, d, rows, S, y);
+  return hipGetLastError();
+}
+
+}  // namespace moe

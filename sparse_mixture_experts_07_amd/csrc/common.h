@@ -1,0 +1,97 @@
+// common.h - types and small device helpers shared by the HIP kernels of the
+// MoE layer forward (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+constexpr int kMaxExperts = 256;   // routed experts per layer
+constexpr int kWave = 64;          // CDNA wavefront width
+
+// bfloat16 storage is the upper 16 bits of an IEEE float32.
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+  return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+
+// float32 -> bfloat16, round to nearest, ties to even; NaN stays NaN.
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return static_cast<uint16_t>(u >> 16);
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return static_cast<uint32_t>(f32_to_bf16(lo)) |
+         (static_cast<uint32_t>(f32_to_bf16(hi)) << 16);
+}
+
+// Exact GELU x * Phi(x) and SiLU x * sigmoid(x) in fp32.
+__device__ __forceinline__ float gelu_f32(float a) {
+  return 0.5f * a * (1.0f + erff(a * 0.70710678118654752440f));
+}
+__device__ __forceinline__ float silu_f32(float g) {
+  return g / (1.0f + __expf(-g));
+}
+
+__device__ __forceinline__ int ceil_div(int a, int b) { return (a + b - 1) / b; }
+
+// Inclusive prefix sum across the 64 lanes of a wavefront.
+__device__ __forceinline__ int wave_inclusive_scan(int v) {
+  const int lane = threadIdx.x % kWave;
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) {
+    const int n = __shfl_up(v, off);
+    if (lane >= off) v += n;
+  }
+  return v;
+}
+
+// Exclusive prefix sum over a workgroup of NT threads (NT/64 <= 64 waves);
+// `tmp` is LDS scratch of NT/64 ints.  Returns the exclusive prefix of the
+// calling thread and the block total through *total.
+template <int NT>
+__device__ __forceinline__ int block_exclusive_scan(int v, int *tmp, int *total) {
+  constexpr int NW = NT / kWave;
+  const int lane = threadIdx.x % kWave;
+  const int wave = threadIdx.x / kWave;
+  const int inc = wave_inclusive_scan(v);
+  if (lane == kWave - 1) tmp[wave] = inc;
+  __syncthreads();
+  int before = 0, all = 0;
+  for (int w = 0; w < NW; ++w) {
+    const int t = tmp[w];
+    if (w < wave) before += t;
+    all += t;
+  }
+  __syncthreads();
+  *total = all;
+  return before + inc - v;
+}
+
+// Number of expert groups that take part in the expert GEMMs: E routed
+// groups, plus the shared always-on expert as group E when present.
+struct GroupTable {
+  const int32_t *offsets;  // [E + 1] group starts in the grouped rows
+  int32_t E;
+  int32_t S;
+  int32_t T;               // tokens (rows of the shared group)
+  int32_t routed_rows;     // T * k
+
+  __device__ __forceinline__ int num_groups() const { return E + S; }
+  __device__ __forceinline__ int rows(int g) const {
+    return g < E ? offsets[g + 1] - offsets[g] : T;
+  }
+  // first grouped row (of hidden / y_perm) of group g
+  __device__ __forceinline__ int row0(int g) const {
+    return g < E ? offsets[g] : routed_rows;
+  }
+};
+
+}  // namespace moe

@@ -1,0 +1,234 @@
+// permute.hip - dispatch: stable grouping of the T*k assignments by expert.
+//
+// The "Expert Backend" section of "Understanding MoE in Transformers"
+// describes the grouped backend as: sort and group the tokens by expert id,
+// run one grouped GEMM, then collect and reorder.  Here the sort is a
+// counting sort, stable in the flat assignment index f = t*k + j:
+//   1. hist    - one workgroup per segment of kSeg assignments builds an LDS
+//                histogram of expert ids (integer atomics: order-free).
+//   2. scan    - one workgroup: per expert, exclusive prefix over segments,
+//                counts, exclusive prefix over experts = group offsets, and
+//                the first grouped row of every (segment, expert).
+//   3. scatter - one workgroup per segment, one wavefront per quarter of
+//                it; inside a wavefront, lanes holding the same expert are
+//                matched with 8 ballots (expert ids < 256) and ranked by
+//                lane order, so rows keep flat-index order.
+//   4. stats   - one workgroup: Importance(X)_e = sum of the kept weights of
+//                group e in group order (Qiita summary "Load-balancing
+//                losses"), then CV^2(Importance), CV^2(Load) and the load-
+//                balance loss of the Go chapter's section 3, in fp64.
+//   5. move    - x_perm[p] = x[perm_src[p]], 16-byte vectors, one row per
+//                workgroup iteration (coalesced reads and writes).
+#include "common.h"
+
+namespace moe {
+
+constexpr int kSeg = 1024;          // assignments per segment
+constexpr int kPermThreads = 256;   // 4 wavefronts x 256 assignments
+
+__global__ __launch_bounds__(kPermThreads) void perm_hist_kernel(
+    const int32_t *__restrict__ idx, int n, int E, int32_t *__restrict__ hist) {
+  __shared__ int h[kMaxExperts];
+  for (int e = threadIdx.x; e < E; e += kPermThreads) h[e] = 0;
+  __syncthreads();
+  const int f0 = blockIdx.x * kSeg;
+  const int f1 = min(n, f0 + kSeg);
+  for (int f = f0 + threadIdx.x; f < f1; f += kPermThreads) {
+    const int e = idx[f];
+    if (static_cast<unsigned>(e) < static_cast<unsigned>(E)) atomicAdd(&h[e], 1);
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < E; e += kPermThreads)
+    hist[(int64_t)blockIdx.x * E + e] = h[e];
+}
+
+// One workgroup of 256 threads; thread e owns expert e.
+__global__ __launch_bounds__(kPermThreads) void perm_scan_kernel(
+    int32_t *__restrict__ hist, int nseg, int E, int n,
+    int32_t *__restrict__ offsets) {
+  __shared__ int sc[kPermThreads];
+  const int e = threadIdx.x;
+  int total = 0;
+  if (e < E) {
+    for (int s = 0; s < nseg; ++s) {
+      const int c = hist[(int64_t)s * E + e];
+      hist[(int64_t)s * E + e] = total;
+      total += c;
+    }
+  }
+  sc[e] = total;
+  __syncthreads();
+  // inclusive Hillis-Steele scan over the 256 expert totals
+  for (int off = 1; off < kPermThreads; off <<= 1) {
+    const int v = e >= off ? sc[e - off] : 0;
+    __syncthreads();
+    sc[e] += v;
+    __syncthreads();
+  }
+  const int start = sc[e] - total;  // exclusive
+  if (e < E) {
+    offsets[e] = start;
+    for (int s = 0; s < nseg; ++s) hist[(int64_t)s * E + e] += start;
+  }
+  if (e == 0) offsets[E] = n;
+}
+
+__global__ __launch_bounds__(kPermThreads) void perm_scatter_kernel(
+    const int32_t *__restrict__ idx, const float *__restrict__ w, int n, int k,
+    int E, const int32_t *__restrict__ base, int32_t *__restrict__ pos,
+    int32_t *__restrict__ perm_src, float *__restrict__ perm_w) {
+  constexpr int NW = kPermThreads / kWave;
+  constexpr int SUB = kSeg / NW;    // assignments per wavefront
+  __shared__ int run[NW][kMaxExperts];
+  const int lane = threadIdx.x % kWave;
+  const int wv = threadIdx.x / kWave;
+  const int f0 = blockIdx.x * kSeg + wv * SUB;
+
+  for (int i = threadIdx.x; i < NW * kMaxExperts; i += kPermThreads) (&run[0][0])[i] = 0;
+  __syncthreads();
+  for (int c = 0; c < SUB; c += kWave) {
+    const int f = f0 + c + lane;
+    if (f < n) {
+      const int e = idx[f];
+      if (static_cast<unsigned>(e) < static_cast<unsigned>(E)) atomicAdd(&run[wv][e], 1);
+    }
+  }
+  __syncthreads();
+  // per-wavefront first grouped row of every expert
+  for (int e = threadIdx.x; e < E; e += kPermThreads) {
+    int r = base[(int64_t)blockIdx.x * E + e];
+    for (int v = 0; v < NW; ++v) {
+      const int c = run[v][e];
+      run[v][e] = r;
+      r += c;
+    }
+  }
+  __syncthreads();
+  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  for (int c = 0; c < SUB; c += kWave) {
+    const int f = f0 + c + lane;
+    int e = f < n ? idx[f] : -1;
+    const bool valid = static_cast<unsigned>(e) < static_cast<unsigned>(E);
+    if (!valid) e = 0;
+    uint64_t peers = __ballot(valid);
+#pragma unroll
+    for (int b = 0; b < 8; ++b) {
+      const bool bit = (e >> b) & 1;
+      const uint64_t m = __ballot(valid && bit);
+      peers &= bit ? m : ~m;
+    }
+    if (valid) {
+      const int rank = __popcll(peers & below);
+      const int p = run[wv][e] + rank;
+      pos[f] = p;
+      perm_src[p] = f / k;
+      perm_w[p] = w[f];
+      // the lowest lane of each peer group advances the group's next row;
+      // every lane read run[] above, before this store (in-order LDS)
+      if (rank == 0) run[wv][e] = p + __popcll(peers);
+    }
+  }
+}
+
+// One workgroup: importance[e] and the three side statistics.
+__global__ __launch_bounds__(kPermThreads) void perm_stats_kernel(
+    const int32_t *__restrict__ offsets, const float *__restrict__ perm_w,
+    int E, float *__restrict__ importance, double *__restrict__ stats) {
+  constexpr int NW = kPermThreads / kWave;
+  __shared__ float imp[kMaxExperts];
+  const int lane = threadIdx.x % kWave;
+  const int wv = threadIdx.x / kWave;
+  for (int e = wv; e < E; e += NW) {
+    const int r0 = offsets[e], r1 = offsets[e + 1];
+    float s = 0.0f;
+    for (int r = r0 + lane; r < r1; r += kWave) s += perm_w[r];
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) s += __shfl_xor(s, off);
+    if (lane == 0) {
+      imp[e] = s;
+      importance[e] = s;
+    }
+  }
+  __syncthreads();
+  if (!stats || wv != 0) return;
+  double si = 0.0, sc = 0.0;
+  for (int e = lane; e < E; e += kWave) {
+    si += imp[e];
+    sc += offsets[e + 1] - offsets[e];
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    si += __shfl_xor(si, off);
+    sc += __shfl_xor(sc, off);
+  }
+  const double mi = si / E, mc = sc / E;
+  double vi = 0.0, vc = 0.0, f2 = 0.0;
+  for (int e = lane; e < E; e += kWave) {
+    const double c = offsets[e + 1] - offsets[e];
+    vi += (imp[e] - mi) * (imp[e] - mi);
+    vc += (c - mc) * (c - mc);
+    if (sc != 0.0) f2 += (c / sc) * (c / sc);
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    vi += __shfl_xor(vi, off);
+    vc += __shfl_xor(vc, off);
+    f2 += __shfl_xor(f2, off);
+  }
+  if (lane == 0) {
+    stats[0] = mi == 0.0 ? 0.0 : (vi / E) / (mi * mi);
+    stats[1] = mc == 0.0 ? 0.0 : (vc / E) / (mc * mc);
+    stats[2] = sc == 0.0 ? 0.0 : E * f2;
+  }
+}
+
+// x_perm[p] = x[perm_src[p]]; row_vec16 = bytes per row / 16.  The source
+// index is clamped to [0, T) so that a corrupt index cannot read outside x.
+__global__ __launch_bounds__(kPermThreads) void perm_move_kernel(
+    const uint4 *__restrict__ x, const int32_t *__restrict__ perm_src, int n,
+    int T, int row_vec16, uint4 *__restrict__ x_perm) {
+  for (int p = blockIdx.x; p < n; p += gridDim.x) {
+    const int t = min(max(perm_src[p], 0), T - 1);
+    const uint4 *src = x + (int64_t)t * row_vec16;
+    uint4 *dst = x_perm + (int64_t)p * row_vec16;
+    for (int i = threadIdx.x; i < row_vec16; i += kPermThreads) dst[i] = src[i];
+  }
+}
+
+__global__ void zero_f32_kernel(float *p, int n) {
+  for (int i = threadIdx.x; i < n; i += blockDim.x) p[i] = 0.0f;
+}
+__global__ void zero_stats_kernel(double *p) {
+  if (threadIdx.x < 3) p[threadIdx.x] = 0.0;
+}
+
+hipError_t launch_zero_stats(float *importance, int E, double *stats, hipStream_t s) {
+  zero_f32_kernel<<<1, 256, 0, s>>>(importance, E);
+  if (stats) zero_stats_kernel<<<1, 64, 0, s>>>(stats);
+  return hipGetLastError();
+}
+
+int perm_num_segments(int64_t n) { return static_cast<int>((n + kSeg - 1) / kSeg); }
+
+// Workspace: hist [nseg * E] int32, perm_w [n] fp32.
+hipError_t launch_permute(const int32_t *idx, const float *w, const void *x,
+                          int T, int k, int E, int row_bytes, int32_t *offsets,
+                          int32_t *perm_src, int32_t *pos, float *importance,
+                          double *stats, void *x_perm, int32_t *hist,
+                          float *perm_w, hipStream_t s) {
+  const int n = T * k;
+  if (n == 0) return launch_zero_stats(importance, E, stats, s);
+  const int nseg = perm_num_segments(n);
+  perm_hist_kernel<<<nseg, kPermThreads, 0, s>>>(idx, n, E, hist);
+  perm_scan_kernel<<<1, kPermThreads, 0, s>>>(hist, nseg, E, n, offsets);
+  perm_scatter_kernel<<<nseg, kPermThreads, 0, s>>>(idx, w, n, k, E, hist, pos,
+                                                    perm_src, perm_w);
+  perm_stats_kernel<<<1, kPermThreads, 0, s>>>(offsets, perm_w, E, importance, stats);
+  const int blocks = n < 8192 ? n : 8192;
+  perm_move_kernel<<<blocks, kPermThreads, 0, s>>>(
+      static_cast<const uint4 *>(x), perm_src, n, T, row_bytes / 16,
+      static_cast<uint4 *>(x_perm));
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,279 @@
+// route.hip - router scores, KeepTopK and the softmax over the kept scores.
+//
+// One workgroup owns BT = 32 tokens and every expert.  The score of (t, e) is
+// one fp32 fused multiply-add chain over i = 0..d-1 in ascending order,
+// starting from +0, with the router bias added after the last term: the Go
+// book chapter "MoE (Mixture of Experts)", section 2 (Route) accumulates
+// score += x_i * W_g[i, e] one term at a time in float32.  Tokens and
+// experts are spread over the threads; every thread keeps its chains in
+// registers, so no chain is ever split or reordered.
+//
+// Selection: the first k entries of a stable descending sort, i.e. the k
+// largest scores with equal scores ordered by the lower expert index (same
+// section, sort.SliceStable; KeepTopK of the "Sparsely-Gated MoE" Qiita
+// summary, "Gating: Noisy Top-k Softmax").  One wavefront per token runs k
+// rounds of a 64-lane arg-max whose order is (score desc, index asc).
+// Weights: exp(s_j - s_0) / sum_i exp(s_i - s_0) over the kept scores only.
+// Counts: an LDS histogram per workgroup, then one integer atomic per
+// (workgroup, expert), so counts are exact and order-independent.
+#include "common.h"
+
+#pragma clang fp contract(off)
+
+namespace moe {
+
+constexpr int kRouteThreads = 256;
+constexpr int kRouteBK = 32;
+
+template <typename XT>
+struct XLoad;
+
+template <>
+struct XLoad<uint16_t> {  // bf16 rows: 8 values (16 B) per load
+  static constexpr int kVec = 8;
+  __device__ static void load(const uint16_t *p, float *out) {
+    uint4 v = *reinterpret_cast<const uint4 *>(p);
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      out[2 * i] = __uint_as_float(w[i] << 16);
+      out[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+    }
+  }
+};
+
+template <>
+struct XLoad<float> {  // fp32 rows: 4 values (16 B) per load
+  static constexpr int kVec = 4;
+  __device__ static void load(const float *p, float *out) {
+    float4 v = *reinterpret_cast<const float4 *>(p);
+    out[0] = v.x; out[1] = v.y; out[2] = v.z; out[3] = v.w;
+  }
+};
+
+// TX threads across experts (each owns EPT experts strided by TX), TY =
+// 256/TX threads across tokens (each owns TPT consecutive tokens).
+template <typename XT, int TX, int EPT, int TPT>
+__global__ __launch_bounds__(kRouteThreads) void route_kernel(
+    const XT *__restrict__ x, const float *__restrict__ wg,
+    const float *__restrict__ bg, int T, int d, int E, int k,
+    int32_t *__restrict__ topk_idx, float *__restrict__ topk_w,
+    int32_t *__restrict__ counts, float *__restrict__ logits) {
+  constexpr int TY = kRouteThreads / TX;
+  constexpr int BT = TY * TPT;
+  constexpr int EP = TX * EPT;      // padded expert count
+  constexpr int EPS = EP + 1;       // LDS row stride (bank spread)
+  constexpr int BK = kRouteBK;
+  constexpr int NQ = (EP + 63) / 64;  // score slots per lane in the top-k
+  constexpr int VEC = XLoad<XT>::kVec;
+  static_assert(BT == 32, "one workgroup owns 32 tokens");
+
+  // the staged x / W_g chunks and, after the K loop, the scores share LDS
+  __shared__ float lds[BK * BT + BK * EPS];
+  __shared__ int cnt[EP];
+  float(*xs)[BT] = reinterpret_cast<float(*)[BT]>(lds);
+  float(*ws)[EPS] = reinterpret_cast<float(*)[EPS]>(lds + BK * BT);
+  float(*ls)[EPS] = reinterpret_cast<float(*)[EPS]>(lds);
+  static_assert(BT * EPS <= BK * BT + BK * EPS, "scores fit the staging space");
+
+  const int tid = threadIdx.x;
+  const int tx = tid % TX;
+  const int ty = tid / TX;
+  const int t0 = blockIdx.x * BT;
+
+  for (int e = tid; e < EP; e += kRouteThreads) cnt[e] = 0;
+
+  float acc[TPT][EPT];
+#pragma unroll
+  for (int r = 0; r < TPT; ++r)
+#pragma unroll
+    for (int j = 0; j < EPT; ++j) acc[r][j] = 0.0f;
+
+  for (int k0 = 0; k0 < d; k0 += BK) {
+    // stage x[t0 .. t0+BT, k0 .. k0+BK) transposed to xs[kk][row]
+    for (int q = tid; q < BT * (BK / VEC); q += kRouteThreads) {
+      const int row = q / (BK / VEC);
+      const int c = (q % (BK / VEC)) * VEC;
+      float v[VEC];
+      if (t0 + row < T) {
+        XLoad<XT>::load(x + (int64_t)(t0 + row) * d + k0 + c, v);
+      } else {
+#pragma unroll
+        for (int i = 0; i < VEC; ++i) v[i] = 0.0f;
+      }
+#pragma unroll
+      for (int i = 0; i < VEC; ++i) xs[c + i][row] = v[i];
+    }
+    // stage W_g[0 .. E, k0 .. k0+BK) transposed to ws[kk][e]
+    for (int q = tid; q < EP * (BK / 4); q += kRouteThreads) {
+      const int e = q / (BK / 4);
+      const int c = (q % (BK / 4)) * 4;
+      float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (e < E) v = *reinterpret_cast<const float4 *>(wg + (int64_t)e * d + k0 + c);
+      ws[c + 0][e] = v.x;
+      ws[c + 1][e] = v.y;
+      ws[c + 2][e] = v.z;
+      ws[c + 3][e] = v.w;
+    }
+    __syncthreads();
+#pragma unroll 4
+    for (int kk = 0; kk < BK; ++kk) {
+      float xv[TPT], wv[EPT];
+#pragma unroll
+      for (int r = 0; r < TPT; ++r) xv[r] = xs[kk][ty * TPT + r];
+#pragma unroll
+      for (int j = 0; j < EPT; ++j) wv[j] = ws[kk][tx + TX * j];
+#pragma unroll
+      for (int r = 0; r < TPT; ++r)
+#pragma unroll
+        for (int j = 0; j < EPT; ++j) acc[r][j] = __builtin_fmaf(xv[r], wv[j], acc[r][j]);
+    }
+    __syncthreads();
+  }
+
+#pragma unroll
+  for (int j = 0; j < EPT; ++j) {
+    const int e = tx + TX * j;
+    if (e >= E) continue;
+    const float b = bg ? bg[e] : 0.0f;
+#pragma unroll
+    for (int r = 0; r < TPT; ++r) {
+      const int row = ty * TPT + r;
+      const float s = bg ? acc[r][j] + b : acc[r][j];
+      ls[row][e] = s;
+      if (logits && t0 + row < T) logits[(int64_t)(t0 + row) * E + e] = s;
+    }
+  }
+  __syncthreads();
+
+  // ---- KeepTopK + softmax: one wavefront per token ----
+  const int lane = tid % kWave;
+  const int wave = tid / kWave;
+  constexpr int NW = kRouteThreads / kWave;
+  for (int row = wave; row < BT; row += NW) {
+    const int t = t0 + row;
+    if (t >= T) break;
+    float v[NQ];
+    uint32_t avail = 0;
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) {
+      const int e = lane + 64 * q;
+      v[q] = 0.0f;
+      if (e < E) {
+        v[q] = ls[row][e];
+        avail |= 1u << q;
+      }
+    }
+    int my_e[NQ];
+    float my_v[NQ];
+    float s0 = 0.0f;
+    for (int j = 0; j < k; ++j) {
+      // lane-local best: strictly greater wins, so the lower index (lower q)
+      // keeps a tie
+      float bv = 0.0f;
+      int be = 0x7fffffff;
+#pragma unroll
+      for (int q = 0; q < NQ; ++q)
+        if ((avail >> q) & 1u)
+          if (be == 0x7fffffff || v[q] > bv) {
+            bv = v[q];
+            be = lane + 64 * q;
+          }
+      // wave arg-max under (score desc, index asc); a total order, so every
+      // lane ends with the same winner
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) {
+        const float ov = __shfl_xor(bv, off);
+        const int oe = __shfl_xor(be, off);
+        const bool take = oe != 0x7fffffff &&
+                          (be == 0x7fffffff || ov > bv || (ov == bv && oe < be));
+        if (take) {
+          bv = ov;
+          be = oe;
+        }
+      }
+      if ((be & 63) == lane) avail &= ~(1u << (be >> 6));
+      if (j == 0) s0 = bv;
+#pragma unroll
+      for (int q = 0; q < NQ; ++q)
+        if (j == lane + 64 * q) {
+          my_e[q] = be;
+          my_v[q] = bv;
+        }
+    }
+    float z[NQ];
+    float part = 0.0f;
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) {
+      z[q] = 0.0f;
+      if (lane + 64 * q < k) {
+        z[q] = expf(my_v[q] - s0);
+        part += z[q];
+      }
+    }
+    // butterfly sum: fp32 addition is commutative, so all lanes agree
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) part += __shfl_xor(part, off);
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) {
+      const int j = lane + 64 * q;
+      if (j < k) {
+        topk_idx[(int64_t)t * k + j] = my_e[q];
+        topk_w[(int64_t)t * k + j] = z[q] / part;
+        atomicAdd(&cnt[my_e[q]], 1);
+      }
+    }
+  }
+  __syncthreads();
+  for (int e = tid; e < E; e += kRouteThreads)
+    if (cnt[e]) atomicAdd(counts + e, cnt[e]);
+}
+
+__global__ void fill_i32_kernel(int32_t *p, int n, int32_t v) {
+  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x)
+    p[i] = v;
+}
+
+template <typename XT, int TX, int EPT, int TPT>
+static hipError_t launch_route_t(const void *x, const float *wg, const float *bg,
+                                 int T, int d, int E, int k, int32_t *idx,
+                                 float *w, int32_t *counts, float *logits,
+                                 hipStream_t s) {
+  const int blocks = (T + 31) / 32;
+  route_kernel<XT, TX, EPT, TPT><<<blocks, kRouteThreads, 0, s>>>(
+      static_cast<const XT *>(x), wg, bg, T, d, E, k, idx, w, counts, logits);
+  return hipGetLastError();
+}
+
+template <typename XT>
+static hipError_t launch_route_dt(const void *x, const float *wg, const float *bg,
+                                  int T, int d, int E, int k, int32_t *idx,
+                                  float *w, int32_t *counts, float *logits,
+                                  hipStream_t s) {
+  if (E <= 8) return launch_route_t<XT, 8, 1, 1>(x, wg, bg, T, d, E, k, idx, w, counts, logits, s);
+  if (E <= 16) return launch_route_t<XT, 16, 1, 2>(x, wg, bg, T, d, E, k, idx, w, counts, logits, s);
+  if (E <= 32) return launch_route_t<XT, 32, 1, 4>(x, wg, bg, T, d, E, k, idx, w, counts, logits, s);
+  if (E <= 64) return launch_route_t<XT, 32, 2, 4>(x, wg, bg, T, d, E, k, idx, w, counts, logits, s);
+  if (E <= 128) return launch_route_t<XT, 32, 4, 4>(x, wg, bg, T, d, E, k, idx, w, counts, logits, s);
+  return launch_route_t<XT, 32, 8, 4>(x, wg, bg, T, d, E, k, idx, w, counts, logits, s);
+}
+
+hipError_t launch_fill_i32(int32_t *p, int n, int32_t v, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  const int blocks = (n + 255) / 256 < 1024 ? (n + 255) / 256 : 1024;
+  fill_i32_kernel<<<blocks, 256, 0, s>>>(p, n, v);
+  return hipGetLastError();
+}
+
+// counts are zeroed here, then accumulated by the route kernel
+hipError_t launch_route(bool bf16, const void *x, const float *wg,
+                        const float *bg, int T, int d, int E, int k,
+                        int32_t *idx, float *w, int32_t *counts, float *logits,
+                        hipStream_t s) {
+  hipError_t err = launch_fill_i32(counts, E, 0, s);
+  if (err != hipSuccess || T == 0) return err;
+  return bf16 ? launch_route_dt<uint16_t>(x, wg, bg, T, d, E, k, idx, w, counts, logits, s)
+              : launch_route_dt<float>(x, wg, bg, T, d, E, k, idx, w, counts, logits, s);
+}
+
+}  // namespace moe

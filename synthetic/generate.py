@@ -99,8 +99,11 @@ def zipf_log_bias(E: int, s: float = 1.1) -> np.ndarray:
     return np.log(p).astype(np.float32)
 
 
-def make_inputs(cfg: LayerConfig, workers: Optional[int] = None) -> LayerInputs:
-    """Draw every input array of ``cfg`` from its seed (see module docstring)."""
+def make_inputs(cfg: LayerConfig, workers: Optional[int] = None,
+                experts: bool = True) -> LayerInputs:
+    """Draw every input array of ``cfg`` from its seed (see module docstring).
+    ``experts=False`` draws only x and the router (expert arrays are then
+    zero-size placeholders); the drawn values do not change."""
     T, d, h, E = cfg.T, cfg.d, cfg.h, cfg.E
     children = np.random.SeedSequence(cfg.seed).spawn(3 + E + max(cfg.S, 1))
 
@@ -126,6 +129,10 @@ def make_inputs(cfg: LayerConfig, workers: Optional[int] = None) -> LayerInputs:
         raise ValueError(cfg.router_bias)
 
     sd = _store_dtype(cfg)
+    if not experts:
+        empty = np.empty((0,), dtype=sd)
+        return LayerInputs(cfg, x, w_gate, b_gate, empty, empty, None, None,
+                           None, None)
     w_up = np.empty((E, cfg.n_up, d), dtype=sd)
     w_down = np.empty((E, d, h), dtype=sd)
     jobs = [(children[3 + e], w_up[e], w_down[e]) for e in range(E)]
