@@ -46,6 +46,10 @@ struct GemmArgs {
   int n_tiles;              // ceil(n_out / BN_out)
 };
 
+// Word 3 of a raw buffer resource on gfx9-family parts (32-bit data format,
+// no swizzle, no index stride).
+constexpr int kBufferWord3 = 0x00020000;
+
 __device__ __forceinline__ int swz(int chunk, int row) {
   return chunk ^ ((row & 7) ^ ((row >> 3) & 1));
 }
@@ -117,9 +121,12 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_bf16_kernel(GemmArgs a) {
       const int mid = (lo + hi + 1) / 2;
       if (tprefix[mid] * a.n_tiles <= L) lo = mid; else hi = mid - 1;
     }
-    const int g = lo;
-    const int tg = tprefix[g + 1] - tprefix[g];
-    const int local = L - tprefix[g] * a.n_tiles;
+    // tile coordinates are workgroup-uniform: make that explicit so group
+    // bases and buffer descriptors live in scalar registers
+    const int g = __builtin_amdgcn_readfirstlane(lo);
+    const int tpg = __builtin_amdgcn_readfirstlane(tprefix[g]);
+    const int tg = __builtin_amdgcn_readfirstlane(tprefix[g + 1]) - tpg;
+    const int local = L - tpg * a.n_tiles;
     const int nt = local / tg;
     const int mt = local % tg;
 
@@ -142,29 +149,32 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_bf16_kernel(GemmArgs a) {
     const int m0 = mt * BM;
     const int n0 = nt * BN_OUT;
 
-    // global source rows of this thread's 16-byte loads
-    const uint16_t *asrc[A_LD];
-    const uint16_t *wsrc[W_LD];
-#pragma unroll
-    for (int i = 0; i < A_LD; ++i) {
-      const int q = tid + i * NT;
-      const int r = q / CH;
-      const int row = min(m0 + r, rows - 1);
-      asrc[i] = abase + (int64_t)row * a.K + (q % CH) * 8;
+    // Buffer descriptors over this tile's rows: loads past the last valid
+    // row (group tail, N tail) are out of range and return zeros, so no
+    // clamping is needed and one 32-bit offset per thread addresses all
+    // of its 16-byte loads.
+    const uint32_t row_bytes = (uint32_t)a.K * 2u;
+    const int arows = min(BM, rows - m0);
+    const __amdgpu_buffer_rsrc_t rs_a = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t *>(abase + (int64_t)m0 * a.K), 0, arows * row_bytes, kBufferWord3);
+    __amdgpu_buffer_rsrc_t rs_w0, rs_w1;
+    if constexpr (SWI) {
+      const int h = a.n_out;
+      const int wv = min(BNW / 2, h - n0);
+      rs_w0 = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<uint16_t *>(wbase + (int64_t)n0 * a.K), 0, wv * row_bytes, kBufferWord3);
+      rs_w1 = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<uint16_t *>(wbase + (int64_t)(h + n0) * a.K), 0, wv * row_bytes, kBufferWord3);
+    } else {
+      const int wv = min(BNW, a.w_rows - n0);
+      rs_w0 = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<uint16_t *>(wbase + (int64_t)n0 * a.K), 0, wv * row_bytes, kBufferWord3);
+      rs_w1 = rs_w0;
     }
-#pragma unroll
-    for (int i = 0; i < W_LD; ++i) {
-      const int q = tid + i * NT;
-      const int r = q / CH;
-      int wr;
-      if constexpr (SWI) {
-        const int h = a.n_out;
-        wr = r < BNW / 2 ? min(n0 + r, h - 1) : h + min(n0 + r - BNW / 2, h - 1);
-      } else {
-        wr = min(n0 + r, a.w_rows - 1);
-      }
-      wsrc[i] = wbase + (int64_t)wr * a.K + (q % CH) * 8;
-    }
+    // thread's first row (tid / CH) and 16-byte chunk (tid % CH); load i
+    // covers row tid / CH + i * (NT / CH)
+    const uint32_t voff0 = (uint32_t)(tid / CH) * row_bytes + (uint32_t)(tid % CH) * 16u;
+    const uint32_t istride = (uint32_t)(NT / CH) * row_bytes;
 
     f32x4_t acc[FW][FM];
 #pragma unroll
@@ -172,44 +182,53 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_bf16_kernel(GemmArgs a) {
 #pragma unroll
       for (int j = 0; j < FM; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
+    // One register stage (prefetch distance 1) feeding two LDS buffers.
     u32x4_t ra[A_LD], rw[W_LD];
+    auto gload = [&](int kt) {
+      const uint32_t ko = (uint32_t)kt * (BK * 2);
 #pragma unroll
-    for (int i = 0; i < A_LD; ++i) ra[i] = *reinterpret_cast<const u32x4_t *>(asrc[i]);
+      for (int i = 0; i < A_LD; ++i)
+        ra[i] = __builtin_amdgcn_raw_buffer_load_b128(rs_a, voff0 + i * istride + ko, 0, 0);
 #pragma unroll
-    for (int i = 0; i < W_LD; ++i) rw[i] = *reinterpret_cast<const u32x4_t *>(wsrc[i]);
+      for (int i = 0; i < W_LD; ++i) {
+        if (!SWI || i < W_LD / 2) {
+          rw[i] = __builtin_amdgcn_raw_buffer_load_b128(rs_w0, voff0 + i * istride + ko, 0, 0);
+        } else {
+          rw[i] = __builtin_amdgcn_raw_buffer_load_b128(
+              rs_w1, voff0 + (i - W_LD / 2) * istride + ko, 0, 0);
+        }
+      }
+    };
+    auto lstore = [&](int buf) {
 #pragma unroll
-    for (int i = 0; i < A_LD; ++i) {
-      const int q = tid + i * NT;
-      As[0][(q / CH) * CH + swz(q % CH, q / CH)] = ra[i];
-    }
+      for (int i = 0; i < A_LD; ++i) {
+        const int q = tid + i * NT;
+        As[buf][(q / CH) * CH + swz(q % CH, q / CH)] = ra[i];
+      }
 #pragma unroll
-    for (int i = 0; i < W_LD; ++i) {
-      const int q = tid + i * NT;
-      Ws[0][(q / CH) * CH + swz(q % CH, q / CH)] = rw[i];
-    }
-    __syncthreads();
-
+      for (int i = 0; i < W_LD; ++i) {
+        const int q = tid + i * NT;
+        Ws[buf][(q / CH) * CH + swz(q % CH, q / CH)] = rw[i];
+      }
+    };
     const int lrow = lane % 16;
     const int lch = lane / 16;
-    for (int kt = 0; kt < nk; ++kt) {
-      const int buf = kt & 1;
-      const bool more = kt + 1 < nk;
-      if (more) {
-        const int ko = (kt + 1) * BK;
+    // fragments of both k32 halves are read before the MFMAs are issued, so
+    // the second half's LDS latency hides behind the first half's MFMAs
+    auto compute = [&](int buf) {
+      bf16x8_t fa[2][FM], fw[2][FW];
 #pragma unroll
-        for (int i = 0; i < A_LD; ++i) ra[i] = *reinterpret_cast<const u32x4_t *>(asrc[i] + ko);
+      for (int s = 0; s < 2; ++s) {
+        const int ch = 4 * s + lch;
 #pragma unroll
-        for (int i = 0; i < W_LD; ++i) rw[i] = *reinterpret_cast<const u32x4_t *>(wsrc[i] + ko);
+        for (int j = 0; j < FM; ++j) {
+          const int r = wm * WTM + j * 16 + lrow;
+          fa[s][j] = __builtin_bit_cast(bf16x8_t, As[buf][r * CH + swz(ch, r)]);
+        }
       }
 #pragma unroll
       for (int s = 0; s < 2; ++s) {
         const int ch = 4 * s + lch;
-        bf16x8_t fa[FM], fw[FW];
-#pragma unroll
-        for (int j = 0; j < FM; ++j) {
-          const int r = wm * WTM + j * 16 + lrow;
-          fa[j] = __builtin_bit_cast(bf16x8_t, As[buf][r * CH + swz(ch, r)]);
-        }
 #pragma unroll
         for (int i = 0; i < FW; ++i) {
           int r;
@@ -219,26 +238,39 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_bf16_kernel(GemmArgs a) {
           } else {
             r = wn * WTW + i * 16 + lrow;
           }
-          fw[i] = __builtin_bit_cast(bf16x8_t, Ws[buf][r * CH + swz(ch, r)]);
+          fw[s][i] = __builtin_bit_cast(bf16x8_t, Ws[buf][r * CH + swz(ch, r)]);
         }
+      }
+#pragma unroll
+      for (int s = 0; s < 2; ++s)
 #pragma unroll
         for (int i = 0; i < FW; ++i)
 #pragma unroll
           for (int j = 0; j < FM; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fw[i], fa[j], acc[i][j], 0, 0, 0);
-      }
-      if (more) {
+            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fw[s][i], fa[s][j], acc[i][j], 0, 0, 0);
+      // schedule: the token fragments and the first PD weight fragments,
+      // then per weight fragment its FM MFMAs with the read of the fragment
+      // PD ahead in flight, so no MFMA waits on an LDS read issued just
+      // before it (PD * FM MFMAs >= ~8 cover the LDS latency)
+      constexpr int NWF = 2 * FW;
+      constexpr int PD = (8 + FM - 1) / FM < NWF ? (8 + FM - 1) / FM : NWF;
+      __builtin_amdgcn_sched_group_barrier(0x100, 2 * FM + PD, 0);
 #pragma unroll
-        for (int i = 0; i < A_LD; ++i) {
-          const int q = tid + i * NT;
-          As[buf ^ 1][(q / CH) * CH + swz(q % CH, q / CH)] = ra[i];
-        }
-#pragma unroll
-        for (int i = 0; i < W_LD; ++i) {
-          const int q = tid + i * NT;
-          Ws[buf ^ 1][(q / CH) * CH + swz(q % CH, q / CH)] = rw[i];
-        }
+      for (int n = 0; n < NWF; ++n) {
+        __builtin_amdgcn_sched_group_barrier(0x008, FM, 0);
+        if (n + PD < NWF) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
       }
+    };
+
+    gload(0);
+    lstore(0);
+    __syncthreads();
+    for (int kt = 0; kt < nk; ++kt) {
+      const int buf = kt & 1;
+      const bool more = kt + 1 < nk;
+      if (more) gload(kt + 1);
+      compute(buf);
+      if (more) lstore(buf ^ 1);
       __syncthreads();
     }
 
@@ -296,8 +328,9 @@ static int num_cus() {
   return cached;
 }
 
-template <int BM, int BNW, int MODE>
+template <int BM, int BNW, int WM, int WN, int MODE>
 static hipError_t launch_bm(const GemmArgs &a0, hipStream_t s) {
+  constexpr int NT = WM * WN * 64;
   GemmArgs a = a0;
   constexpr int BN_OUT = MODE == kUpSwiglu ? BNW / 2 : BNW;
   a.n_tiles = (a.n_out + BN_OUT - 1) / BN_OUT;
@@ -308,27 +341,29 @@ static hipError_t launch_bm(const GemmArgs &a0, hipStream_t s) {
   if (!per_cu) {
     int nb = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-            &nb, gemm_bf16_kernel<BM, BNW, 2, 2, MODE>, 256, 0) != hipSuccess || nb <= 0)
+            &nb, gemm_bf16_kernel<BM, BNW, WM, WN, MODE>, NT, 0) != hipSuccess || nb <= 0)
       nb = 1;
     per_cu = nb;
   }
   int64_t grid = (int64_t)num_cus() * per_cu;   // persistent grid
   if (tiles < grid) grid = tiles;
   grid = ((grid + 7) / 8) * 8;     // the slice order needs a multiple of 8
-  gemm_bf16_kernel<BM, BNW, 2, 2, MODE><<<(int)grid, 256, 0, s>>>(a);
+  gemm_bf16_kernel<BM, BNW, WM, WN, MODE><<<(int)grid, NT, 0, s>>>(a);
   return hipGetLastError();
 }
 
 template <int MODE>
 static hipError_t launch_mode(const GemmArgs &a, int bm, hipStream_t s) {
-  if (bm >= 128) return launch_bm<128, 256, MODE>(a, s);
-  if (bm >= 64) return launch_bm<64, 256, MODE>(a, s);
-  return launch_bm<32, 256, MODE>(a, s);
+  if (bm >= 256) return launch_bm<256, 256, 4, 2, MODE>(a, s);
+  if (bm >= 128) return launch_bm<128, 256, 2, 4, MODE>(a, s);
+  if (bm >= 64) return launch_bm<64, 256, 2, 2, MODE>(a, s);
+  return launch_bm<32, 256, 2, 2, MODE>(a, s);
 }
 
 // Token-row tile: large for prefill-sized groups, small for decode-sized.
 static int pick_bm(int routed_rows, int E) {
   const int avg = E > 0 ? routed_rows / E : 0;
+  if (avg >= 512) return 256;
   if (avg >= 256) return 128;
   if (avg >= 48) return 64;
   return 32;
