@@ -44,21 +44,29 @@ struct GemmArgs {
   uint16_t *c;              // [routed_rows + S*T, n_out]
   int n_out;                // h (up) or d (down)
   int n_tiles;              // ceil(n_out / BN_out)
+  int min_rows, max_rows;   // this launch takes the groups whose row count
+                            // lies in [min_rows, max_rows]
 };
 
 // Word 3 of a raw buffer resource on gfx9-family parts (32-bit data format,
 // no swizzle, no index stride).
 constexpr int kBufferWord3 = 0x00020000;
 
+// LDS placement of 16-byte chunk `chunk` of tile row `row`.  With 32-wide
+// k stages a row is 64 B and a fragment read (16 rows x 4 chunks) is one
+// contiguous 1 KB block: no swizzle.  With 64-wide stages the 128-B rows are
+// XOR-swizzled (pattern chosen by measuring fragment-read throughput).
+template <int BK>
 __device__ __forceinline__ int swz(int chunk, int row) {
-  return chunk ^ ((row & 7) ^ ((row >> 3) & 1));
+  if constexpr (BK == 32) return chunk;
+  return chunk ^ ((((row >> 2) & 3) << 1) ^ ((row >> 1) & 1));
 }
 
-template <int BM, int BNW, int WM, int WN, int MODE>
+template <int BM, int BNW, int WM, int WN, int BK, int PFD, int MODE>
 __global__ __launch_bounds__(WM *WN * 64) void gemm_bf16_kernel(GemmArgs a) {
   constexpr int NT = WM * WN * 64;
-  constexpr int BK = 64;
   constexpr int CH = BK / 8;             // 16-byte chunks per row
+  constexpr int KS = BK / 32;            // k32 MFMA steps per stage
   constexpr int WTM = BM / WM;           // token rows per wave
   constexpr int WTW = BNW / WN;          // weight rows per wave
   constexpr int FM = WTM / 16;
@@ -67,8 +75,10 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_bf16_kernel(GemmArgs a) {
   constexpr int BN_OUT = SWI ? BNW / 2 : BNW;
   constexpr int A_LD = BM * CH / NT;     // 16-byte loads per thread per stage
   constexpr int W_LD = BNW * CH / NT;
+  static_assert(BK == 32 || BK == 64, "stage depth");
   static_assert(FM >= 1 && FW >= 1 && (!SWI || FW % 2 == 0), "wave tile");
   static_assert(A_LD * NT == BM * CH && W_LD * NT == BNW * CH, "load split");
+  static_assert(!SWI || (W_LD % 2 == 0), "gate and up rows split the loads evenly");
 
   __shared__ u32x4_t As[2][BM * CH];
   __shared__ u32x4_t Ws[2][BNW * CH];
@@ -98,6 +108,7 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_bf16_kernel(GemmArgs a) {
       } else if (g < G) {
         rows = a.T;
       }
+      if (rows < a.min_rows || rows > a.max_rows) rows = 0;
       c2[q] = (rows + BM - 1) / BM;
     }
     int total;
@@ -109,13 +120,15 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_bf16_kernel(GemmArgs a) {
   __syncthreads();
   const int total_tiles = tprefix[G] * a.n_tiles;
   const int nk = a.K / BK;
+  const int lrow = lane % 16;
+  const int lch = lane / 16;
 
   const int nblk = gridDim.x;
   for (int it = 0;; ++it) {
     // slice order: XCD x (= blockIdx % 8) takes a contiguous run of tiles
     const int L = it * nblk + (blockIdx.x % 8) * (nblk / 8) + blockIdx.x / 8;
     if (L >= total_tiles) break;
-    // group g: tiles [tprefix[g] * n_tiles, tprefix[g+1] * n_tiles)
+    // group g owns tiles [tprefix[g] * n_tiles, tprefix[g+1] * n_tiles)
     int lo = 0, hi = G - 1;
     while (lo < hi) {
       const int mid = (lo + hi + 1) / 2;
@@ -182,9 +195,12 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_bf16_kernel(GemmArgs a) {
 #pragma unroll
       for (int j = 0; j < FM; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-    // One register stage (prefetch distance 1) feeding two LDS buffers.
-    u32x4_t ra[A_LD], rw[W_LD];
-    auto gload = [&](int kt) {
+    // Two register stages (prefetch distance 2) feed two LDS buffers: the
+    // loads of stage k+2 are issued while stage k is computed and stored to
+    // LDS only after stage k+1 is computed.
+    u32x4_t ra0[A_LD], rw0[W_LD];
+    u32x4_t ra1[PFD == 2 ? A_LD : 1], rw1[PFD == 2 ? W_LD : 1];
+    auto gload = [&](u32x4_t(&ra)[A_LD], u32x4_t(&rw)[W_LD], int kt) {
       const uint32_t ko = (uint32_t)kt * (BK * 2);
 #pragma unroll
       for (int i = 0; i < A_LD; ++i)
@@ -199,62 +215,58 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_bf16_kernel(GemmArgs a) {
         }
       }
     };
-    auto lstore = [&](int buf) {
+    auto lstore = [&](const u32x4_t(&ra)[A_LD], const u32x4_t(&rw)[W_LD], int buf) {
 #pragma unroll
       for (int i = 0; i < A_LD; ++i) {
         const int q = tid + i * NT;
-        As[buf][(q / CH) * CH + swz(q % CH, q / CH)] = ra[i];
+        As[buf][(q / CH) * CH + swz<BK>(q % CH, q / CH)] = ra[i];
       }
 #pragma unroll
       for (int i = 0; i < W_LD; ++i) {
         const int q = tid + i * NT;
-        Ws[buf][(q / CH) * CH + swz(q % CH, q / CH)] = rw[i];
+        Ws[buf][(q / CH) * CH + swz<BK>(q % CH, q / CH)] = rw[i];
       }
     };
-    const int lrow = lane % 16;
-    const int lch = lane / 16;
-    // fragments of both k32 halves are read before the MFMAs are issued, so
-    // the second half's LDS latency hides behind the first half's MFMAs
+    auto wrow = [&](int i) {
+      if constexpr (SWI) {
+        return (i < FW / 2) ? wn * (WTW / 2) + i * 16 + lrow
+                            : BNW / 2 + wn * (WTW / 2) + (i - FW / 2) * 16 + lrow;
+      } else {
+        return wn * WTW + i * 16 + lrow;
+      }
+    };
+    // Token fragments of every k32 step are read first, then weight
+    // fragments are streamed PD ahead of the MFMAs that use them.
     auto compute = [&](int buf) {
-      bf16x8_t fa[2][FM], fw[2][FW];
+      bf16x8_t fa[KS][FM], fw[KS][FW];
 #pragma unroll
-      for (int s = 0; s < 2; ++s) {
+      for (int s = 0; s < KS; ++s) {
         const int ch = 4 * s + lch;
 #pragma unroll
         for (int j = 0; j < FM; ++j) {
           const int r = wm * WTM + j * 16 + lrow;
-          fa[s][j] = __builtin_bit_cast(bf16x8_t, As[buf][r * CH + swz(ch, r)]);
+          fa[s][j] = __builtin_bit_cast(bf16x8_t, As[buf][r * CH + swz<BK>(ch, r)]);
         }
       }
 #pragma unroll
-      for (int s = 0; s < 2; ++s) {
+      for (int s = 0; s < KS; ++s) {
         const int ch = 4 * s + lch;
 #pragma unroll
         for (int i = 0; i < FW; ++i) {
-          int r;
-          if constexpr (SWI) {
-            r = (i < FW / 2) ? wn * (WTW / 2) + i * 16 + lrow
-                             : BNW / 2 + wn * (WTW / 2) + (i - FW / 2) * 16 + lrow;
-          } else {
-            r = wn * WTW + i * 16 + lrow;
-          }
-          fw[s][i] = __builtin_bit_cast(bf16x8_t, Ws[buf][r * CH + swz(ch, r)]);
+          const int r = wrow(i);
+          fw[s][i] = __builtin_bit_cast(bf16x8_t, Ws[buf][r * CH + swz<BK>(ch, r)]);
         }
       }
 #pragma unroll
-      for (int s = 0; s < 2; ++s)
+      for (int s = 0; s < KS; ++s)
 #pragma unroll
         for (int i = 0; i < FW; ++i)
 #pragma unroll
           for (int j = 0; j < FM; ++j)
             acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fw[s][i], fa[s][j], acc[i][j], 0, 0, 0);
-      // schedule: the token fragments and the first PD weight fragments,
-      // then per weight fragment its FM MFMAs with the read of the fragment
-      // PD ahead in flight, so no MFMA waits on an LDS read issued just
-      // before it (PD * FM MFMAs >= ~8 cover the LDS latency)
-      constexpr int NWF = 2 * FW;
+      constexpr int NWF = KS * FW;
       constexpr int PD = (8 + FM - 1) / FM < NWF ? (8 + FM - 1) / FM : NWF;
-      __builtin_amdgcn_sched_group_barrier(0x100, 2 * FM + PD, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, KS * FM + PD, 0);
 #pragma unroll
       for (int n = 0; n < NWF; ++n) {
         __builtin_amdgcn_sched_group_barrier(0x008, FM, 0);
@@ -262,16 +274,38 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_bf16_kernel(GemmArgs a) {
       }
     };
 
-    gload(0);
-    lstore(0);
-    __syncthreads();
-    for (int kt = 0; kt < nk; ++kt) {
-      const int buf = kt & 1;
-      const bool more = kt + 1 < nk;
-      if (more) gload(kt + 1);
-      compute(buf);
-      if (more) lstore(buf ^ 1);
+    if constexpr (PFD == 2) {
+      gload(ra0, rw0, 0);
+      lstore(ra0, rw0, 0);
+      if (nk > 1) gload(ra1, rw1, 1);
       __syncthreads();
+      int kt = 0;
+      for (; kt + 2 <= nk; kt += 2) {
+        // even step: LDS buffer 0 holds stage kt, registers 1 hold stage kt+1
+        if (kt + 2 < nk) gload(ra0, rw0, kt + 2);
+        compute(0);
+        lstore(ra1, rw1, 1);
+        __syncthreads();
+        // odd step: LDS buffer 1 holds stage kt+1, registers 0 hold stage kt+2
+        if (kt + 3 < nk) gload(ra1, rw1, kt + 3);
+        compute(1);
+        if (kt + 2 < nk) lstore(ra0, rw0, 0);
+        __syncthreads();
+      }
+      if (kt < nk) compute(0);   // odd stage count: the last stage is in buffer 0
+    } else {
+      // one register stage: the loads of stage k+1 fly while stage k computes
+      gload(ra0, rw0, 0);
+      lstore(ra0, rw0, 0);
+      __syncthreads();
+      for (int kt = 0; kt < nk; ++kt) {
+        const int buf = kt & 1;
+        const bool more = kt + 1 < nk;
+        if (more) gload(ra0, rw0, kt + 1);
+        compute(buf);
+        if (more) lstore(ra0, rw0, buf ^ 1);
+        __syncthreads();
+      }
     }
 
     // ---- epilogue: lane owns columns 4*(lane/16)+0..3 of token row lane%16 ----
@@ -328,7 +362,9 @@ static int num_cus() {
   return cached;
 }
 
-template <int BM, int BNW, int WM, int WN, int MODE>
+// persistent: one resident wave of workgroups walks all tiles; otherwise one
+// workgroup per tile (the hardware dispatcher balances short streaming tiles)
+template <int BM, int BNW, int WM, int WN, int BK, int PFD, int MODE, bool PERSIST = true>
 static hipError_t launch_bm(const GemmArgs &a0, hipStream_t s) {
   constexpr int NT = WM * WN * 64;
   GemmArgs a = a0;
@@ -341,32 +377,33 @@ static hipError_t launch_bm(const GemmArgs &a0, hipStream_t s) {
   if (!per_cu) {
     int nb = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-            &nb, gemm_bf16_kernel<BM, BNW, WM, WN, MODE>, NT, 0) != hipSuccess || nb <= 0)
+            &nb, gemm_bf16_kernel<BM, BNW, WM, WN, BK, PFD, MODE>, NT, 0) != hipSuccess || nb <= 0)
       nb = 1;
     per_cu = nb;
   }
   int64_t grid = (int64_t)num_cus() * per_cu;   // persistent grid
-  if (tiles < grid) grid = tiles;
+  if (!PERSIST || tiles < grid) grid = tiles;
   grid = ((grid + 7) / 8) * 8;     // the slice order needs a multiple of 8
-  gemm_bf16_kernel<BM, BNW, WM, WN, MODE><<<(int)grid, NT, 0, s>>>(a);
+  gemm_bf16_kernel<BM, BNW, WM, WN, BK, PFD, MODE><<<(int)grid, NT, 0, s>>>(a);
   return hipGetLastError();
 }
 
+// Groups are split by row count into two tile classes, one launch each:
+// small groups (<= 64 rows: decode batches, cold experts) stream their
+// weights through 32-row tiles; larger groups use 256 x 256 tiles.  The
+// large class is skipped when no group can exceed 64 rows (every group has
+// at most T rows).
 template <int MODE>
-static hipError_t launch_mode(const GemmArgs &a, int bm, hipStream_t s) {
-  if (bm >= 256) return launch_bm<256, 256, 4, 2, MODE>(a, s);
-  if (bm >= 128) return launch_bm<128, 256, 2, 4, MODE>(a, s);
-  if (bm >= 64) return launch_bm<64, 256, 2, 2, MODE>(a, s);
-  return launch_bm<32, 256, 2, 2, MODE>(a, s);
-}
-
-// Token-row tile: large for prefill-sized groups, small for decode-sized.
-static int pick_bm(int routed_rows, int E) {
-  const int avg = E > 0 ? routed_rows / E : 0;
-  if (avg >= 512) return 256;
-  if (avg >= 256) return 128;
-  if (avg >= 48) return 64;
-  return 32;
+static hipError_t launch_classes(GemmArgs a, hipStream_t s) {
+  hipError_t err = hipSuccess;
+  if (a.T > 64) {
+    a.min_rows = 65;
+    a.max_rows = 1 << 30;
+    if ((err = launch_bm<256, 256, 4, 2, 64, 1, MODE>(a, s)) != hipSuccess) return err;
+  }
+  a.min_rows = 1;
+  a.max_rows = 64;
+  return launch_bm<32, 128, 2, 2, 64, 2, MODE>(a, s);
 }
 
 hipError_t launch_expert_up_bf16(bool swiglu, const int32_t *offsets, int E, int S,
@@ -389,8 +426,7 @@ hipError_t launch_expert_up_bf16(bool swiglu, const int32_t *offsets, int E, int
   a.bias = static_cast<const uint16_t *>(b_up);
   a.c = static_cast<uint16_t *>(hidden);
   a.n_out = h;
-  const int bm = pick_bm(a.routed_rows, E);
-  return swiglu ? launch_mode<kUpSwiglu>(a, bm, s) : launch_mode<kUpGelu>(a, bm, s);
+  return swiglu ? launch_classes<kUpSwiglu>(a, s) : launch_classes<kUpGelu>(a, s);
 }
 
 hipError_t launch_expert_down_bf16(const int32_t *offsets, int E, int S, int T,
@@ -413,8 +449,7 @@ hipError_t launch_expert_down_bf16(const int32_t *offsets, int E, int S, int T,
   a.bias = static_cast<const uint16_t *>(b_down);
   a.c = static_cast<uint16_t *>(y_perm);
   a.n_out = d;
-  const int bm = pick_bm(a.routed_rows, E);
-  return launch_mode<kDown>(a, bm, s);
+  return launch_classes<kDown>(a, s);
 }
 
 }  // namespace moe

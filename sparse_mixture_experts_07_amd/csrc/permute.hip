@@ -13,10 +13,11 @@
 //                it; inside a wavefront, lanes holding the same expert are
 //                matched with 8 ballots (expert ids < 256) and ranked by
 //                lane order, so rows keep flat-index order.
-//   4. stats   - one workgroup: Importance(X)_e = sum of the kept weights of
-//                group e in group order (Qiita summary "Load-balancing
-//                losses"), then CV^2(Importance), CV^2(Load) and the load-
-//                balance loss of the Go chapter's section 3, in fp64.
+//   4. stats   - Importance(X)_e = sum of the kept weights of group e in
+//                group order, one wavefront per expert (Qiita summary
+//                "Load-balancing losses"); then one wavefront computes
+//                CV^2(Importance), CV^2(Load) and the load-balance loss of
+//                the Go chapter's section 3, in fp64.
 //   5. move    - x_perm[p] = x[perm_src[p]], 16-byte vectors, one row per
 //                workgroup iteration (coalesced reads and writes).
 #include "common.h"
@@ -130,30 +131,31 @@ __global__ __launch_bounds__(kPermThreads) void perm_scatter_kernel(
   }
 }
 
-// One workgroup: importance[e] and the three side statistics.
-__global__ __launch_bounds__(kPermThreads) void perm_stats_kernel(
+// importance[e]: one wavefront per expert sums the kept weights of its
+// group (lane-strided partial sums, then a fixed butterfly: deterministic).
+__global__ __launch_bounds__(kPermThreads) void perm_importance_kernel(
     const int32_t *__restrict__ offsets, const float *__restrict__ perm_w,
-    int E, float *__restrict__ importance, double *__restrict__ stats) {
-  constexpr int NW = kPermThreads / kWave;
-  __shared__ float imp[kMaxExperts];
+    int E, float *__restrict__ importance) {
   const int lane = threadIdx.x % kWave;
-  const int wv = threadIdx.x / kWave;
-  for (int e = wv; e < E; e += NW) {
-    const int r0 = offsets[e], r1 = offsets[e + 1];
-    float s = 0.0f;
-    for (int r = r0 + lane; r < r1; r += kWave) s += perm_w[r];
+  const int e = blockIdx.x * (kPermThreads / kWave) + threadIdx.x / kWave;
+  if (e >= E) return;
+  const int r0 = offsets[e], r1 = offsets[e + 1];
+  float s = 0.0f;
+  for (int r = r0 + lane; r < r1; r += kWave) s += perm_w[r];
 #pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) s += __shfl_xor(s, off);
-    if (lane == 0) {
-      imp[e] = s;
-      importance[e] = s;
-    }
-  }
-  __syncthreads();
-  if (!stats || wv != 0) return;
+  for (int off = 32; off >= 1; off >>= 1) s += __shfl_xor(s, off);
+  if (lane == 0) importance[e] = s;
+}
+
+// One wavefront: CV^2(Importance), CV^2(Load) and the load-balance loss, in
+// fp64 with a fixed reduction order.
+__global__ __launch_bounds__(kWave) void perm_stats_kernel(
+    const int32_t *__restrict__ offsets, const float *__restrict__ importance,
+    int E, double *__restrict__ stats) {
+  const int lane = threadIdx.x;
   double si = 0.0, sc = 0.0;
   for (int e = lane; e < E; e += kWave) {
-    si += imp[e];
+    si += importance[e];
     sc += offsets[e + 1] - offsets[e];
   }
 #pragma unroll
@@ -165,7 +167,8 @@ __global__ __launch_bounds__(kPermThreads) void perm_stats_kernel(
   double vi = 0.0, vc = 0.0, f2 = 0.0;
   for (int e = lane; e < E; e += kWave) {
     const double c = offsets[e + 1] - offsets[e];
-    vi += (imp[e] - mi) * (imp[e] - mi);
+    const double im = importance[e];
+    vi += (im - mi) * (im - mi);
     vc += (c - mc) * (c - mc);
     if (sc != 0.0) f2 += (c / sc) * (c / sc);
   }
@@ -223,7 +226,8 @@ hipError_t launch_permute(const int32_t *idx, const float *w, const void *x,
   perm_scan_kernel<<<1, kPermThreads, 0, s>>>(hist, nseg, E, n, offsets);
   perm_scatter_kernel<<<nseg, kPermThreads, 0, s>>>(idx, w, n, k, E, hist, pos,
                                                     perm_src, perm_w);
-  perm_stats_kernel<<<1, kPermThreads, 0, s>>>(offsets, perm_w, E, importance, stats);
+  perm_importance_kernel<<<(E + 3) / 4, kPermThreads, 0, s>>>(offsets, perm_w, E, importance);
+  if (stats) perm_stats_kernel<<<1, kWave, 0, s>>>(offsets, importance, E, stats);
   const int blocks = n < 8192 ? n : 8192;
   perm_move_kernel<<<blocks, kPermThreads, 0, s>>>(
       static_cast<const uint4 *>(x), perm_src, n, T, row_bytes / 16,

@@ -52,29 +52,35 @@ struct XLoad<float> {  // fp32 rows: 4 values (16 B) per load
 };
 
 // TX threads across experts (each owns EPT experts strided by TX), TY =
-// 256/TX threads across tokens (each owns TPT consecutive tokens).
-template <typename XT, int TX, int EPT, int TPT>
+// 256/TX threads across tokens (each owns TPT consecutive tokens).  The K
+// loop stages "super-chunks" of G x 32 columns of x and W_g in LDS (k
+// contiguous, rows padded by 16 B against bank conflicts), double-buffered:
+// the global loads of super-chunk c+1 fly while super-chunk c is consumed,
+// so one load latency is paid per G x 32 columns.  Each thread walks k in
+// ascending order for every one of its TPT x EPT chains.
+template <typename XT, int TX, int EPT, int TPT, int GMAX>
 __global__ __launch_bounds__(kRouteThreads) void route_kernel(
     const XT *__restrict__ x, const float *__restrict__ wg,
-    const float *__restrict__ bg, int T, int d, int E, int k,
+    const float *__restrict__ bg, int T, int d, int E, int k, int G,
     int32_t *__restrict__ topk_idx, float *__restrict__ topk_w,
     int32_t *__restrict__ counts, float *__restrict__ logits) {
   constexpr int TY = kRouteThreads / TX;
   constexpr int BT = TY * TPT;
   constexpr int EP = TX * EPT;      // padded expert count
-  constexpr int EPS = EP + 1;       // LDS row stride (bank spread)
+  constexpr int EPS = EP + 1;       // score row stride
   constexpr int BK = kRouteBK;
+  constexpr int KS = BK + 4;        // staged row stride (floats)
   constexpr int NQ = (EP + 63) / 64;  // score slots per lane in the top-k
   constexpr int VEC = XLoad<XT>::kVec;
-  static_assert(BT == 32, "one workgroup owns 32 tokens");
+  constexpr int XQ = BT * (BK / VEC);              // x vector loads per chunk
+  constexpr int XL = (XQ + kRouteThreads - 1) / kRouteThreads;
+  constexpr int WQ = EP * (BK / 4);                // W_g float4 loads per chunk
+  constexpr int WL = (WQ + kRouteThreads - 1) / kRouteThreads;
+  constexpr int CHUNK = (BT + EP) * KS;            // floats per staged chunk
 
-  // the staged x / W_g chunks and, after the K loop, the scores share LDS
-  __shared__ float lds[BK * BT + BK * EPS];
+  extern __shared__ float lds[];                   // 2 * G * CHUNK floats
   __shared__ int cnt[EP];
-  float(*xs)[BT] = reinterpret_cast<float(*)[BT]>(lds);
-  float(*ws)[EPS] = reinterpret_cast<float(*)[EPS]>(lds + BK * BT);
-  float(*ls)[EPS] = reinterpret_cast<float(*)[EPS]>(lds);
-  static_assert(BT * EPS <= BK * BT + BK * EPS, "scores fit the staging space");
+  const int stage = G * CHUNK;
 
   const int tid = threadIdx.x;
   const int tx = tid % TX;
@@ -89,47 +95,101 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(
 #pragma unroll
     for (int j = 0; j < EPT; ++j) acc[r][j] = 0.0f;
 
-  for (int k0 = 0; k0 < d; k0 += BK) {
-    // stage x[t0 .. t0+BT, k0 .. k0+BK) transposed to xs[kk][row]
-    for (int q = tid; q < BT * (BK / VEC); q += kRouteThreads) {
-      const int row = q / (BK / VEC);
-      const int c = (q % (BK / VEC)) * VEC;
-      float v[VEC];
-      if (t0 + row < T) {
-        XLoad<XT>::load(x + (int64_t)(t0 + row) * d + k0 + c, v);
-      } else {
+  float xr[GMAX][XL][VEC];
+  float4 wr[GMAX][WL];
+  auto gload = [&](int k0) {   // super-chunk starting at column k0
 #pragma unroll
-        for (int i = 0; i < VEC; ++i) v[i] = 0.0f;
+    for (int g = 0; g < GMAX; ++g) {
+      if (g >= G) break;
+      const int kg = k0 + g * BK;
+#pragma unroll
+      for (int i = 0; i < XL; ++i) {
+        const int q = tid + i * kRouteThreads;
+        const int row = q / (BK / VEC);
+        const int c = (q % (BK / VEC)) * VEC;
+        if (q < XQ && t0 + row < T) {
+          XLoad<XT>::load(x + (int64_t)(t0 + row) * d + kg + c, xr[g][i]);
+        } else {
+#pragma unroll
+          for (int v = 0; v < VEC; ++v) xr[g][i][v] = 0.0f;
+        }
       }
 #pragma unroll
-      for (int i = 0; i < VEC; ++i) xs[c + i][row] = v[i];
+      for (int i = 0; i < WL; ++i) {
+        const int q = tid + i * kRouteThreads;
+        const int e = q / (BK / 4);
+        const int c = (q % (BK / 4)) * 4;
+        wr[g][i] = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (q < WQ && e < E) wr[g][i] = *reinterpret_cast<const float4 *>(wg + (int64_t)e * d + kg + c);
+      }
     }
-    // stage W_g[0 .. E, k0 .. k0+BK) transposed to ws[kk][e]
-    for (int q = tid; q < EP * (BK / 4); q += kRouteThreads) {
-      const int e = q / (BK / 4);
-      const int c = (q % (BK / 4)) * 4;
-      float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (e < E) v = *reinterpret_cast<const float4 *>(wg + (int64_t)e * d + k0 + c);
-      ws[c + 0][e] = v.x;
-      ws[c + 1][e] = v.y;
-      ws[c + 2][e] = v.z;
-      ws[c + 3][e] = v.w;
+  };
+  auto lstore = [&](int buf) {
+#pragma unroll
+    for (int g = 0; g < GMAX; ++g) {
+      if (g >= G) break;
+      float *xs = lds + buf * stage + g * CHUNK;
+      float *ws = xs + BT * KS;
+#pragma unroll
+      for (int i = 0; i < XL; ++i) {
+        const int q = tid + i * kRouteThreads;
+        if (q < XQ) {
+          const int row = q / (BK / VEC);
+          const int c = (q % (BK / VEC)) * VEC;
+#pragma unroll
+          for (int v = 0; v < VEC; v += 4)
+            *reinterpret_cast<float4 *>(xs + row * KS + c + v) =
+                make_float4(xr[g][i][v], xr[g][i][v + 1], xr[g][i][v + 2], xr[g][i][v + 3]);
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < WL; ++i) {
+        const int q = tid + i * kRouteThreads;
+        if (q < WQ) *reinterpret_cast<float4 *>(ws + (q / (BK / 4)) * KS + (q % (BK / 4)) * 4) = wr[g][i];
+      }
     }
-    __syncthreads();
-#pragma unroll 4
-    for (int kk = 0; kk < BK; ++kk) {
-      float xv[TPT], wv[EPT];
+  };
+  auto consume = [&](int buf) {
+    for (int g = 0; g < G; ++g) {
+      const float *xs = lds + buf * stage + g * CHUNK;
+      const float *ws = xs + BT * KS;
 #pragma unroll
-      for (int r = 0; r < TPT; ++r) xv[r] = xs[kk][ty * TPT + r];
+      for (int kk = 0; kk < BK; kk += 4) {
+        float4 xv[TPT], wv[EPT];
 #pragma unroll
-      for (int j = 0; j < EPT; ++j) wv[j] = ws[kk][tx + TX * j];
+        for (int r = 0; r < TPT; ++r)
+          xv[r] = *reinterpret_cast<const float4 *>(xs + (ty * TPT + r) * KS + kk);
 #pragma unroll
-      for (int r = 0; r < TPT; ++r)
+        for (int j = 0; j < EPT; ++j)
+          wv[j] = *reinterpret_cast<const float4 *>(ws + (tx + TX * j) * KS + kk);
 #pragma unroll
-        for (int j = 0; j < EPT; ++j) acc[r][j] = __builtin_fmaf(xv[r], wv[j], acc[r][j]);
+        for (int r = 0; r < TPT; ++r)
+#pragma unroll
+          for (int j = 0; j < EPT; ++j) {
+            float a = acc[r][j];
+            a = __builtin_fmaf(xv[r].x, wv[j].x, a);
+            a = __builtin_fmaf(xv[r].y, wv[j].y, a);
+            a = __builtin_fmaf(xv[r].z, wv[j].z, a);
+            a = __builtin_fmaf(xv[r].w, wv[j].w, a);
+            acc[r][j] = a;
+          }
+      }
     }
+  };
+
+  const int nsc = d / (BK * G);
+  gload(0);
+  lstore(0);
+  __syncthreads();
+  for (int sc = 0; sc < nsc; ++sc) {
+    const int buf = sc & 1;
+    const bool more = sc + 1 < nsc;
+    if (more) gload((sc + 1) * BK * G);
+    consume(buf);
+    if (more) lstore(buf ^ 1);
     __syncthreads();
   }
+  float(*ls)[EPS] = reinterpret_cast<float(*)[EPS]>(lds);
 
 #pragma unroll
   for (int j = 0; j < EPT; ++j) {
@@ -234,28 +294,52 @@ __global__ void fill_i32_kernel(int32_t *p, int n, int32_t v) {
     p[i] = v;
 }
 
-template <typename XT, int TX, int EPT, int TPT>
+template <typename XT, int TX, int EPT, int TPT, int GMAX>
 static hipError_t launch_route_t(const void *x, const float *wg, const float *bg,
                                  int T, int d, int E, int k, int32_t *idx,
                                  float *w, int32_t *counts, float *logits,
                                  hipStream_t s) {
-  const int blocks = (T + 31) / 32;
-  route_kernel<XT, TX, EPT, TPT><<<blocks, kRouteThreads, 0, s>>>(
-      static_cast<const XT *>(x), wg, bg, T, d, E, k, idx, w, counts, logits);
+  constexpr int BT = (kRouteThreads / TX) * TPT;
+  constexpr int CHUNK = (BT + TX * EPT) * (kRouteBK + 4);
+  constexpr int EPS = TX * EPT + 1;
+  // chunks per super-chunk: the most that divide d and keep the two LDS
+  // buffers within 128 KB
+  int G = 1;
+  for (int g = GMAX; g >= 1; --g)
+    if (d % (kRouteBK * g) == 0 && 2 * g * CHUNK * 4 <= 128 * 1024) {
+      G = g;
+      break;
+    }
+  size_t lds = sizeof(float) * 2 * (size_t)G * CHUNK;
+  if (lds < sizeof(float) * (size_t)BT * EPS) lds = sizeof(float) * (size_t)BT * EPS;
+  auto kern = route_kernel<XT, TX, EPT, TPT, GMAX>;
+  hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (err != hipSuccess) return err;
+  const int blocks = (T + BT - 1) / BT;
+  kern<<<blocks, kRouteThreads, lds, s>>>(static_cast<const XT *>(x), wg, bg, T, d, E, k, G,
+                                          idx, w, counts, logits);
   return hipGetLastError();
 }
 
+// Small batches (decode): one chain per thread and a few tokens per
+// workgroup, so the sequential chains spread over as many SIMDs as there
+// are (token, expert) pairs; large batches: register tiles of 4 tokens.
 template <typename XT>
 static hipError_t launch_route_dt(const void *x, const float *wg, const float *bg,
                                   int T, int d, int E, int k, int32_t *idx,
                                   float *w, int32_t *counts, float *logits,
                                   hipStream_t s) {
-  if (E <= 8) return launch_route_t<XT, 8, 1, 1>(x, wg, bg, T, d, E, k, idx, w, counts, logits, s);
-  if (E <= 16) return launch_route_t<XT, 16, 1, 2>(x, wg, bg, T, d, E, k, idx, w, counts, logits, s);
-  if (E <= 32) return launch_route_t<XT, 32, 1, 4>(x, wg, bg, T, d, E, k, idx, w, counts, logits, s);
-  if (E <= 64) return launch_route_t<XT, 32, 2, 4>(x, wg, bg, T, d, E, k, idx, w, counts, logits, s);
-  if (E <= 128) return launch_route_t<XT, 32, 4, 4>(x, wg, bg, T, d, E, k, idx, w, counts, logits, s);
-  return launch_route_t<XT, 32, 8, 4>(x, wg, bg, T, d, E, k, idx, w, counts, logits, s);
+  const bool small = T <= 1024;
+#define MOE_ROUTE(TX, EPT, TPT, GM) \
+  return launch_route_t<XT, TX, EPT, TPT, GM>(x, wg, bg, T, d, E, k, idx, w, counts, logits, s)
+  if (E <= 8) { if (small) MOE_ROUTE(8, 1, 1, 8); MOE_ROUTE(8, 1, 1, 4); }
+  if (E <= 16) { if (small) MOE_ROUTE(16, 1, 1, 8); MOE_ROUTE(16, 1, 2, 4); }
+  if (E <= 32) { if (small) MOE_ROUTE(32, 1, 1, 8); MOE_ROUTE(32, 1, 4, 2); }
+  if (E <= 64) { if (small) MOE_ROUTE(32, 2, 1, 4); MOE_ROUTE(32, 2, 4, 2); }
+  if (E <= 128) MOE_ROUTE(32, 4, 4, 1);
+  MOE_ROUTE(32, 8, 4, 1);
+#undef MOE_ROUTE
 }
 
 hipError_t launch_fill_i32(int32_t *p, int n, int32_t v, hipStream_t s) {

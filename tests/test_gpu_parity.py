@@ -32,6 +32,8 @@ SMALL = {
     "big-groups-swiglu-bf16": dict(T=1000, d=256, h=512, E=3, k=2, act=SWIGLU, dtype=BF16),
     "e256-swiglu-bf16": dict(T=600, d=64, h=64, E=256, k=8, act=SWIGLU, dtype=BF16, bias=True),
     "gelu-f32-bias": dict(T=200, d=128, h=256, E=6, k=2, act=GELU, dtype=F32, expert_bias=True),
+    "mid-groups-gelu-bf16": dict(T=700, d=128, h=192, E=4, k=2, act=GELU, dtype=BF16, expert_bias=True),
+    "mid-groups-swiglu-shared-bf16": dict(T=520, d=192, h=320, E=3, k=2, act=SWIGLU, dtype=BF16, S=1),
 }
 
 
@@ -59,6 +61,20 @@ def test_small_layers_every_element(name):
     np.testing.assert_allclose(res["importance"], rimp, rtol=1e-5)
     cvi, cvl, lb = oracle.load_stats(rc, rimp)
     np.testing.assert_allclose(res["stats"], [cvi, cvl, lb], rtol=1e-4, atol=1e-9)
+
+
+def test_group_size_classes_in_one_layer():
+    """Skewed router biases give groups of <= 64, 65..384 and > 384 rows in
+    the same layer, so every tile class of the grouped GEMM runs; the
+    shared expert (T rows) lands in the largest class."""
+    L = random_layer(21, T=1000, d=128, h=256, E=8, k=2, act=SWIGLU, dtype=BF16,
+                     S=1, bias=True, wstd=0.1)
+    L.b_gate = np.float32([4, 3, 2, 1, 0, -1, -2, -3]) * np.float32(0.6)
+    res, _, _ = run_forward(L)
+    c = res["counts"]
+    assert (c <= 64).any() and ((c > 64) & (c <= 384)).any() and (c > 384).any(), c
+    check_routing(L, res["idx"], res["w"], res["counts"])
+    check_outputs(L, res["y"], range(1000))
 
 
 def test_stage_calls_equal_forward_and_are_deterministic():
