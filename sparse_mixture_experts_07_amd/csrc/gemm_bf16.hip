@@ -62,8 +62,11 @@ __device__ __forceinline__ int swz(int chunk, int row) {
   return chunk ^ ((((row >> 2) & 3) << 1) ^ ((row >> 1) & 1));
 }
 
+// At least two waves per SIMD: 8-wave tiles run one workgroup per CU,
+// 4-wave tiles two (their register budget is capped at 256 per lane).
 template <int BM, int BNW, int WM, int WN, int BK, int PFD, int MODE>
-__global__ __launch_bounds__(WM *WN * 64) void gemm_bf16_kernel(GemmArgs a) {
+__global__ __launch_bounds__(WM *WN * 64) __attribute__((amdgpu_waves_per_eu(2)))
+void gemm_bf16_kernel(GemmArgs a) {
   constexpr int NT = WM * WN * 64;
   constexpr int CH = BK / 8;             // 16-byte chunks per row
   constexpr int KS = BK / 32;            // k32 MFMA steps per stage
@@ -274,22 +277,29 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_bf16_kernel(GemmArgs a) {
       }
     };
 
+    // Scheduling fences keep each stage's global loads ahead of the MFMAs
+    // (the compiler would otherwise sink them next to their LDS stores and
+    // expose the whole load latency).
     if constexpr (PFD == 2) {
       gload(ra0, rw0, 0);
       lstore(ra0, rw0, 0);
-      if (nk > 1) gload(ra1, rw1, 1);
+      gload(ra1, rw1, 1);
       __syncthreads();
       int kt = 0;
       for (; kt + 2 <= nk; kt += 2) {
         // even step: LDS buffer 0 holds stage kt, registers 1 hold stage kt+1
-        if (kt + 2 < nk) gload(ra0, rw0, kt + 2);
+        gload(ra0, rw0, kt + 2);
+        __builtin_amdgcn_sched_barrier(0);
         compute(0);
+        __builtin_amdgcn_sched_barrier(0);
         lstore(ra1, rw1, 1);
         __syncthreads();
         // odd step: LDS buffer 1 holds stage kt+1, registers 0 hold stage kt+2
-        if (kt + 3 < nk) gload(ra1, rw1, kt + 3);
+        gload(ra1, rw1, kt + 3);
+        __builtin_amdgcn_sched_barrier(0);
         compute(1);
-        if (kt + 2 < nk) lstore(ra0, rw0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        lstore(ra0, rw0, 0);
         __syncthreads();
       }
       if (kt < nk) compute(0);   // odd stage count: the last stage is in buffer 0
@@ -300,10 +310,11 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_bf16_kernel(GemmArgs a) {
       __syncthreads();
       for (int kt = 0; kt < nk; ++kt) {
         const int buf = kt & 1;
-        const bool more = kt + 1 < nk;
-        if (more) gload(ra0, rw0, kt + 1);
+        gload(ra0, rw0, kt + 1);
+        __builtin_amdgcn_sched_barrier(0);
         compute(buf);
-        if (more) lstore(ra0, rw0, buf ^ 1);
+        __builtin_amdgcn_sched_barrier(0);
+        lstore(ra0, rw0, buf ^ 1);
         __syncthreads();
       }
     }

@@ -185,7 +185,10 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(
     const int buf = sc & 1;
     const bool more = sc + 1 < nsc;
     if (more) gload((sc + 1) * BK * G);
+    // keep the loads ahead of the arithmetic (not sunk next to their stores)
+    __builtin_amdgcn_sched_barrier(0);
     consume(buf);
+    __builtin_amdgcn_sched_barrier(0);
     if (more) lstore(buf ^ 1);
     __syncthreads();
   }
@@ -294,6 +297,163 @@ __global__ void fill_i32_kernel(int32_t *p, int n, int32_t v) {
     p[i] = v;
 }
 
+// ---------------------------------------------------------------------------
+// Few experts (E <= 64): a wavefront owns 64/EP tokens x EP experts with one
+// (token, expert) chain per lane, and streams its x and W_g rows straight
+// from memory through buffer loads (reads past a row's end or past the last
+// token return zeros).  Four register sets of 32 columns rotate: a set is
+// refilled right after it is consumed, so three sets (96 columns of
+// arithmetic) cover each load's latency.  No LDS staging, no barriers in the
+// K loop.  KeepTopK/softmax run inside each EP-lane group with shuffles.
+template <typename XT>
+struct RowLoad;
+template <>
+struct RowLoad<uint16_t> {   // 32 bf16 columns = 4 x 16 B
+  static constexpr int kLoads = 4;
+  static constexpr int kBytes = 2;
+  __device__ static void expand(const u32x4_t (&v)[kLoads], float *out) {
+#pragma unroll
+    for (int i = 0; i < kLoads; ++i)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        out[8 * i + 2 * q] = __uint_as_float(v[i][q] << 16);
+        out[8 * i + 2 * q + 1] = __uint_as_float(v[i][q] & 0xffff0000u);
+      }
+  }
+};
+template <>
+struct RowLoad<float> {      // 32 fp32 columns = 8 x 16 B
+  static constexpr int kLoads = 8;
+  static constexpr int kBytes = 4;
+  __device__ static void expand(const u32x4_t (&v)[kLoads], float *out) {
+#pragma unroll
+    for (int i = 0; i < kLoads; ++i)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) out[4 * i + q] = __uint_as_float(v[i][q]);
+  }
+};
+
+constexpr int kBufWord3 = 0x00020000;   // raw buffer resource, gfx9 family
+
+template <typename XT, int EP>
+__global__ __launch_bounds__(kRouteThreads) void route_direct_kernel(
+    const XT *__restrict__ x, const float *__restrict__ wg,
+    const float *__restrict__ bg, int T, int d, int E, int k,
+    int32_t *__restrict__ topk_idx, float *__restrict__ topk_w,
+    int32_t *__restrict__ counts, float *__restrict__ logits) {
+  constexpr int TPW = kWave / EP;          // tokens per wavefront
+  constexpr int NS = 4;                    // rotating register sets
+  constexpr int XL = RowLoad<XT>::kLoads;  // x loads per 32 columns
+  __shared__ int cnt[EP];
+  const int lane = threadIdx.x % kWave;
+  const int wave = threadIdx.x / kWave;
+  const int e = lane % EP;
+  const int t = (blockIdx.x * (kRouteThreads / kWave) + wave) * TPW + lane / EP;
+  const bool valid = t < T && e < E;
+  for (int i = threadIdx.x; i < EP; i += kRouteThreads) cnt[i] = 0;
+
+  const uint32_t xrec = (uint32_t)T * (uint32_t)d * RowLoad<XT>::kBytes;
+  const uint32_t wrec = (uint32_t)E * (uint32_t)d * 4u;
+  const __amdgpu_buffer_rsrc_t rx =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<XT *>(x), 0, xrec, kBufWord3);
+  const __amdgpu_buffer_rsrc_t rw =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(wg), 0, wrec, kBufWord3);
+  // a lane without a chain reads only out-of-range zeros
+  const uint32_t xo = t < T ? (uint32_t)t * (uint32_t)d * RowLoad<XT>::kBytes : xrec;
+  const uint32_t wo = e < E ? (uint32_t)e * (uint32_t)d * 4u : wrec;
+
+  u32x4_t xs[NS][XL], ws[NS][8];
+  auto load = [&](int set, int c0) {   // columns c0 .. c0+31
+#pragma unroll
+    for (int i = 0; i < XL; ++i)
+      xs[set][i] = __builtin_amdgcn_raw_buffer_load_b128(
+          rx, xo + (uint32_t)c0 * RowLoad<XT>::kBytes + 16u * i, 0, 0);
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      ws[set][i] = __builtin_amdgcn_raw_buffer_load_b128(rw, wo + (uint32_t)c0 * 4u + 16u * i, 0, 0);
+  };
+  float acc = 0.0f;
+  auto consume = [&](int set) {
+    float xv[32];
+    RowLoad<XT>::expand(xs[set], xv);
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) acc = __builtin_fmaf(xv[4 * i + q], __uint_as_float(ws[set][i][q]), acc);
+  };
+#pragma unroll
+  for (int u = 0; u < NS; ++u) load(u, 32 * u);
+  const int nstep = d / 32;   // d is a multiple of 64
+  int c = 0;
+  for (; c + NS <= nstep; c += NS) {
+#pragma unroll
+    for (int u = 0; u < NS; ++u) {
+      consume(u);
+      __builtin_amdgcn_sched_barrier(0);
+      load(u, 32 * (c + u + NS));   // past the row end: never consumed
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < NS; ++u)
+    if (c + u < nstep) consume(u);
+
+  float sc = acc;
+  if (bg && e < E) sc = acc + bg[e];
+  if (logits && valid) logits[(int64_t)t * E + e] = sc;
+
+  // ---- KeepTopK over the EP lanes of each token (lower index wins ties) ----
+  bool avail = e < E;
+  int my_e = 0;
+  float my_v = 0.0f, s0 = 0.0f;
+  for (int j = 0; j < k; ++j) {
+    float bv = sc;
+    int be = avail ? e : 0x7fffffff;
+#pragma unroll
+    for (int off = EP / 2; off >= 1; off >>= 1) {
+      const float ov = __shfl_xor(bv, off);
+      const int oe = __shfl_xor(be, off);
+      const bool take = oe != 0x7fffffff &&
+                        (be == 0x7fffffff || ov > bv || (ov == bv && oe < be));
+      if (take) {
+        bv = ov;
+        be = oe;
+      }
+    }
+    if (be == e) avail = false;
+    if (j == 0) s0 = bv;
+    if (e == j) {
+      my_e = be;
+      my_v = bv;
+    }
+  }
+  float z = e < k ? expf(my_v - s0) : 0.0f;
+  float sum = z;
+#pragma unroll
+  for (int off = EP / 2; off >= 1; off >>= 1) sum += __shfl_xor(sum, off);
+  __syncthreads();   // cnt[] zeroed
+  if (t < T && e < k) {
+    topk_idx[(int64_t)t * k + e] = my_e;
+    topk_w[(int64_t)t * k + e] = z / sum;
+    atomicAdd(&cnt[my_e], 1);
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < E; i += kRouteThreads)
+    if (cnt[i]) atomicAdd(counts + i, cnt[i]);
+}
+
+template <typename XT, int EP>
+static hipError_t launch_route_direct(const void *x, const float *wg, const float *bg,
+                                      int T, int d, int E, int k, int32_t *idx,
+                                      float *w, int32_t *counts, float *logits,
+                                      hipStream_t s) {
+  constexpr int TPB = (kRouteThreads / kWave) * (kWave / EP);   // tokens per workgroup
+  const int blocks = (T + TPB - 1) / TPB;
+  route_direct_kernel<XT, EP><<<blocks, kRouteThreads, 0, s>>>(
+      static_cast<const XT *>(x), wg, bg, T, d, E, k, idx, w, counts, logits);
+  return hipGetLastError();
+}
+
 template <typename XT, int TX, int EPT, int TPT, int GMAX>
 static hipError_t launch_route_t(const void *x, const float *wg, const float *bg,
                                  int T, int d, int E, int k, int32_t *idx,
@@ -330,11 +490,15 @@ static hipError_t launch_route_dt(const void *x, const float *wg, const float *b
                                   int T, int d, int E, int k, int32_t *idx,
                                   float *w, int32_t *counts, float *logits,
                                   hipStream_t s) {
+  // few experts: direct streaming kernel (buffer offsets must fit 32 bits)
+  const bool fits = (int64_t)T * d * (int64_t)sizeof(XT) < (int64_t(1) << 31);
+  if (fits && E <= 8) return launch_route_direct<XT, 8>(x, wg, bg, T, d, E, k, idx, w, counts, logits, s);
+  if (fits && E <= 16) return launch_route_direct<XT, 16>(x, wg, bg, T, d, E, k, idx, w, counts, logits, s);
   const bool small = T <= 1024;
 #define MOE_ROUTE(TX, EPT, TPT, GM) \
   return launch_route_t<XT, TX, EPT, TPT, GM>(x, wg, bg, T, d, E, k, idx, w, counts, logits, s)
-  if (E <= 8) { if (small) MOE_ROUTE(8, 1, 1, 8); MOE_ROUTE(8, 1, 1, 4); }
-  if (E <= 16) { if (small) MOE_ROUTE(16, 1, 1, 8); MOE_ROUTE(16, 1, 2, 4); }
+  if (E <= 8) MOE_ROUTE(8, 1, 1, 4);
+  if (E <= 16) MOE_ROUTE(16, 1, 2, 4);
   if (E <= 32) { if (small) MOE_ROUTE(32, 1, 1, 8); MOE_ROUTE(32, 1, 4, 2); }
   if (E <= 64) { if (small) MOE_ROUTE(32, 2, 1, 4); MOE_ROUTE(32, 2, 4, 2); }
   if (E <= 128) MOE_ROUTE(32, 4, 4, 1);
