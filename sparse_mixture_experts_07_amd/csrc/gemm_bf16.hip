@@ -10,21 +10,29 @@
 //          SwiGLU: act = silu(gate row n) * (up row h + n) of W = [2h, d]
 //   down : y_perm[r, c] = sum_n hidden[r, n] * W2[e][c, n]     (+ bias)
 //
-// Both operands are K-contiguous, so tiles of either are rows of 128 B
-// (BK = 64 bf16).  The MFMA is v_mfma_f32_16x16x32_bf16 with the weight rows
-// as its A operand (M side) and the token rows as its B operand (N side):
-// a lane then owns 4 consecutive output columns of one token row, and the
-// epilogue stores 8-byte runs.  fp32 accumulation in registers.
+// Both operands are K-contiguous, so tiles of either are runs of rows along
+// K.  The MFMA is v_mfma_f32_16x16x32_bf16 with the weight rows as its A
+// operand (M side) and the token rows as its B operand (N side): a lane then
+// owns 4 consecutive output columns of one token row, and the epilogue
+// stores 8-byte runs.  fp32 accumulation in registers.
 //
-// Tiles: BM token rows x BNW weight rows x BK.  Global -> registers -> LDS,
-// double-buffered (one barrier per K step); 16-byte LDS chunks are XOR-
-// swizzled per row so the fragment reads of 16 consecutive rows hit
-// distinct banks.  A persistent grid walks the ragged tile space: every
-// workgroup computes the per-group tile prefix from the group offsets, then
+// A persistent grid walks the ragged tile space: every workgroup computes
+// the per-group tile prefix from the group offsets (no host sync), then
 // takes tiles in a slice order that keeps each XCD (workgroups are dealt to
 // the 8 XCDs round-robin) on a contiguous run of tiles, i.e. the m-tiles of
 // a few neighbouring weight tiles, so weight tiles are fetched from HBM once
-// per XCD and reused from its L2.
+// per XCD and reused from its L2.  Three kernels share the tile arithmetic:
+//
+//   gemm_dma_kernel   large groups, K <= 8192: operands DMA'd from global
+//                     memory into four rotating LDS buffers, 8 waves
+//   gemm_pp_kernel    large groups, longer K: register-staged loads, two
+//                     wave groups alternating compute and memory slots
+//   gemm_bf16_kernel  small groups (<= 64 rows, e.g. decode): 32-row tiles
+//                     streaming the weights, registers -> LDS, lock-step
+//
+// Measured on MI355X the large-group kernels are bound by the L2 -> CU
+// operand stream (about 21-26 B/clk per CU in this access pattern, against
+// 32 B/clk that full MFMA rate on 256 x 256 tiles would need), not by LDS.
 #include "common.h"
 
 namespace moe {
@@ -55,280 +63,286 @@ constexpr int kBufferWord3 = 0x00020000;
 // LDS placement of 16-byte chunk `chunk` of tile row `row`.  With 32-wide
 // k stages a row is 64 B and a fragment read (16 rows x 4 chunks) is one
 // contiguous 1 KB block: no swizzle.  With 64-wide stages the 128-B rows are
-// XOR-swizzled (pattern chosen by measuring fragment-read throughput).
+// XOR-swizzled (pattern chosen by measuring fragment-read throughput and
+// whole-kernel time against a k32-plane layout).
 template <int BK>
 __device__ __forceinline__ int swz(int chunk, int row) {
   if constexpr (BK == 32) return chunk;
   return chunk ^ ((((row >> 2) & 3) << 1) ^ ((row >> 1) & 1));
 }
 
-// At least two waves per SIMD: 8-wave tiles run one workgroup per CU,
-// 4-wave tiles two (their register budget is capped at 256 per lane).
-template <int BM, int BNW, int WM, int WN, int BK, int PFD, int MODE>
-__global__ __launch_bounds__(WM *WN * 64) __attribute__((amdgpu_waves_per_eu(2)))
-void gemm_bf16_kernel(GemmArgs a) {
-  constexpr int NT = WM * WN * 64;
-  constexpr int CH = BK / 8;             // 16-byte chunks per row
-  constexpr int KS = BK / 32;            // k32 MFMA steps per stage
-  constexpr int WTM = BM / WM;           // token rows per wave
-  constexpr int WTW = BNW / WN;          // weight rows per wave
-  constexpr int FM = WTM / 16;
-  constexpr int FW = WTW / 16;
-  constexpr bool SWI = MODE == kUpSwiglu;
-  constexpr int BN_OUT = SWI ? BNW / 2 : BNW;
-  constexpr int A_LD = BM * CH / NT;     // 16-byte loads per thread per stage
-  constexpr int W_LD = BNW * CH / NT;
+// Workgroup barrier that orders LDS only: the wave waits for its own LDS
+// operations, not for its global loads, which stay in flight across it.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// Per-group m-tile prefix (exclusive) of the groups this launch takes, into
+// tprefix[0..G]; robust against out-of-range offsets.  Thread t owns groups
+// 2t and 2t+1 (G <= 257 <= 2 * NT).
+template <int NT, int BM>
+__device__ __forceinline__ void tile_prefix(const GemmArgs &a, int *tprefix, int *scan_tmp) {
+  static_assert(2 * NT >= kMaxExperts + 1, "two groups per thread cover E + S");
+  const int tid = threadIdx.x;
+  const int G = a.E + a.S;
+  int c2[2];
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const int g = 2 * tid + q;
+    int rows = 0;
+    if (g < a.E) {
+      const int r0 = min(max(a.offsets[g], 0), a.routed_rows);
+      const int r1 = min(max(a.offsets[g + 1], r0), a.routed_rows);
+      rows = r1 - r0;
+    } else if (g < G) {
+      rows = a.T;
+    }
+    if (rows < a.min_rows || rows > a.max_rows) rows = 0;
+    c2[q] = (rows + BM - 1) / BM;
+  }
+  int total;
+  const int ex = block_exclusive_scan<NT>(c2[0] + c2[1], scan_tmp, &total);
+  if (2 * tid < G + 1) tprefix[2 * tid] = ex;
+  if (2 * tid + 1 < G + 1) tprefix[2 * tid + 1] = ex + c2[0];
+  if (tid == 0) tprefix[G] = total;
+}
+
+// One output tile: group, row range and the buffer descriptors of its
+// operands.  Loads past the last valid row (group tail, N tail) are out of
+// the descriptor's range and return zeros, so no clamping is needed and one
+// 32-bit offset per thread addresses all of its 16-byte loads.
+struct Tile {
+  int g, grow0, rows, m0, n0;
+  __amdgpu_buffer_rsrc_t rs_a, rs_w0, rs_w1;
+};
+
+// Tile L of the launch's ragged tile space: group g owns tiles
+// [tprefix[g] * n_tiles, tprefix[g+1] * n_tiles), m-tile fastest.
+template <int BM, int BNW, bool SWI>
+__device__ __forceinline__ Tile decode_tile(const GemmArgs &a, const int *tprefix, int L) {
+  const int G = a.E + a.S;
+  int lo = 0, hi = G - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) / 2;
+    if (tprefix[mid] * a.n_tiles <= L) lo = mid; else hi = mid - 1;
+  }
+  // tile coordinates are workgroup-uniform: make that explicit so group
+  // bases and buffer descriptors live in scalar registers
+  Tile t;
+  t.g = __builtin_amdgcn_readfirstlane(lo);
+  const int tpg = __builtin_amdgcn_readfirstlane(tprefix[t.g]);
+  const int tg = __builtin_amdgcn_readfirstlane(tprefix[t.g + 1]) - tpg;
+  const int local = L - tpg * a.n_tiles;
+  const int nt = local / tg;
+  const int mt = local % tg;
+  const uint16_t *abase;
+  const uint16_t *wbase;
+  if (t.g < a.E) {
+    const int r0 = min(max(a.offsets[t.g], 0), a.routed_rows);
+    const int r1 = min(max(a.offsets[t.g + 1], r0), a.routed_rows);
+    t.grow0 = r0;
+    t.rows = r1 - r0;
+    abase = a.a_routed + (int64_t)r0 * a.K;
+    wbase = a.w + (int64_t)t.g * a.w_rows * a.K;
+  } else {
+    t.grow0 = a.routed_rows;
+    t.rows = a.T;
+    abase = a.a_shared;
+    wbase = a.w_shared;
+  }
+  t.m0 = mt * BM;
+  t.n0 = nt * (SWI ? BNW / 2 : BNW);
+  const uint32_t row_bytes = (uint32_t)a.K * 2u;
+  const int arows = min(BM, t.rows - t.m0);
+  t.rs_a = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t *>(abase + (int64_t)t.m0 * a.K), 0, arows * row_bytes, kBufferWord3);
+  if constexpr (SWI) {
+    const int h = a.n_out;
+    const int wv = min(BNW / 2, h - t.n0);
+    t.rs_w0 = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t *>(wbase + (int64_t)t.n0 * a.K), 0, wv * row_bytes, kBufferWord3);
+    t.rs_w1 = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t *>(wbase + (int64_t)(h + t.n0) * a.K), 0, wv * row_bytes, kBufferWord3);
+  } else {
+    const int wv = min(BNW, a.w_rows - t.n0);
+    t.rs_w0 = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t *>(wbase + (int64_t)t.n0 * a.K), 0, wv * row_bytes, kBufferWord3);
+    t.rs_w1 = t.rs_w0;
+  }
+  return t;
+}
+
+// Tile arithmetic shared by the kernels: BM token rows x BNW weight rows per
+// tile, k stages of BK, WM x WN waves each owning (BM/WM) x (BNW/WN).
+// LDS layout of a stage: XOR-swizzled 128-byte rows, or (PLANES) BK/32
+// planes of 64-byte rows, where every 16-row fragment read and every
+// 16-row x 64-byte store is one contiguous 1 KB block.
+template <int BM, int BNW, int WM, int WN, int BK, int MODE, bool PLANES = false>
+struct TileMath {
+  static constexpr int NT = WM * WN * 64;
+  static constexpr int CH = BK / 8;            // 16-byte chunks per row
+  static constexpr int KS = BK / 32;           // k32 MFMA steps per stage
+  static constexpr int WTM = BM / WM;          // token rows per wave
+  static constexpr int WTW = BNW / WN;         // weight rows per wave
+  static constexpr int FM = WTM / 16;
+  static constexpr int FW = WTW / 16;
+  static constexpr bool SWI = MODE == kUpSwiglu;
+  static constexpr int BN_OUT = SWI ? BNW / 2 : BNW;
+  static constexpr int A_LD = BM * CH / NT;    // 16-byte loads per thread per stage
+  static constexpr int W_LD = BNW * CH / NT;
   static_assert(BK == 32 || BK == 64, "stage depth");
   static_assert(FM >= 1 && FW >= 1 && (!SWI || FW % 2 == 0), "wave tile");
   static_assert(A_LD * NT == BM * CH && W_LD * NT == BNW * CH, "load split");
   static_assert(!SWI || (W_LD % 2 == 0), "gate and up rows split the loads evenly");
 
-  __shared__ u32x4_t As[2][BM * CH];
-  __shared__ u32x4_t Ws[2][BNW * CH];
-  __shared__ int tprefix[2 * NT + 2];
-  __shared__ int scan_tmp[NT / 64];
-  static_assert(2 * NT >= kMaxExperts + 1, "two groups per thread cover E + S");
-
-  const int tid = threadIdx.x;
-  const int lane = tid % 64;
-  const int wave = tid / 64;
-  const int wm = wave / WN;
-  const int wn = wave % WN;
-  const int G = a.E + a.S;
-
-  // ---- per-group m-tile prefix (exclusive), safe against bad offsets.
-  // Thread t owns groups 2t and 2t+1 (G <= 257 <= 2 * NT). ----
-  {
-    int c2[2];
-#pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      const int g = 2 * tid + q;
-      int rows = 0;
-      if (g < a.E) {
-        const int r0 = min(max(a.offsets[g], 0), a.routed_rows);
-        const int r1 = min(max(a.offsets[g + 1], r0), a.routed_rows);
-        rows = r1 - r0;
-      } else if (g < G) {
-        rows = a.T;
-      }
-      if (rows < a.min_rows || rows > a.max_rows) rows = 0;
-      c2[q] = (rows + BM - 1) / BM;
-    }
-    int total;
-    const int ex = block_exclusive_scan<NT>(c2[0] + c2[1], scan_tmp, &total);
-    if (2 * tid < G + 1) tprefix[2 * tid] = ex;
-    if (2 * tid + 1 < G + 1) tprefix[2 * tid + 1] = ex + c2[0];
-    if (tid == 0) tprefix[G] = total;
+  // thread's first row (tid / CH) and 16-byte chunk (tid % CH); load i
+  // covers row tid / CH + i * (NT / CH)
+  static __device__ __forceinline__ uint32_t voff0(uint32_t row_bytes) {
+    return (uint32_t)(threadIdx.x / CH) * row_bytes + (uint32_t)(threadIdx.x % CH) * 16u;
   }
-  __syncthreads();
-  const int total_tiles = tprefix[G] * a.n_tiles;
-  const int nk = a.K / BK;
-  const int lrow = lane % 16;
-  const int lch = lane / 16;
 
-  const int nblk = gridDim.x;
-  for (int it = 0;; ++it) {
-    // slice order: XCD x (= blockIdx % 8) takes a contiguous run of tiles
-    const int L = it * nblk + (blockIdx.x % 8) * (nblk / 8) + blockIdx.x / 8;
-    if (L >= total_tiles) break;
-    // group g owns tiles [tprefix[g] * n_tiles, tprefix[g+1] * n_tiles)
-    int lo = 0, hi = G - 1;
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) / 2;
-      if (tprefix[mid] * a.n_tiles <= L) lo = mid; else hi = mid - 1;
-    }
-    // tile coordinates are workgroup-uniform: make that explicit so group
-    // bases and buffer descriptors live in scalar registers
-    const int g = __builtin_amdgcn_readfirstlane(lo);
-    const int tpg = __builtin_amdgcn_readfirstlane(tprefix[g]);
-    const int tg = __builtin_amdgcn_readfirstlane(tprefix[g + 1]) - tpg;
-    const int local = L - tpg * a.n_tiles;
-    const int nt = local / tg;
-    const int mt = local % tg;
-
-    int grow0, rows;   // first grouped row (of c) and row count of group g
-    const uint16_t *abase;
-    const uint16_t *wbase;
-    if (g < a.E) {
-      const int r0 = min(max(a.offsets[g], 0), a.routed_rows);
-      const int r1 = min(max(a.offsets[g + 1], r0), a.routed_rows);
-      grow0 = r0;
-      rows = r1 - r0;
-      abase = a.a_routed + (int64_t)r0 * a.K;
-      wbase = a.w + (int64_t)g * a.w_rows * a.K;
-    } else {
-      grow0 = a.routed_rows;
-      rows = a.T;
-      abase = a.a_shared;
-      wbase = a.w_shared;
-    }
-    const int m0 = mt * BM;
-    const int n0 = nt * BN_OUT;
-
-    // Buffer descriptors over this tile's rows: loads past the last valid
-    // row (group tail, N tail) are out of range and return zeros, so no
-    // clamping is needed and one 32-bit offset per thread addresses all
-    // of its 16-byte loads.
-    const uint32_t row_bytes = (uint32_t)a.K * 2u;
-    const int arows = min(BM, rows - m0);
-    const __amdgpu_buffer_rsrc_t rs_a = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint16_t *>(abase + (int64_t)m0 * a.K), 0, arows * row_bytes, kBufferWord3);
-    __amdgpu_buffer_rsrc_t rs_w0, rs_w1;
-    if constexpr (SWI) {
-      const int h = a.n_out;
-      const int wv = min(BNW / 2, h - n0);
-      rs_w0 = __builtin_amdgcn_make_buffer_rsrc(
-          const_cast<uint16_t *>(wbase + (int64_t)n0 * a.K), 0, wv * row_bytes, kBufferWord3);
-      rs_w1 = __builtin_amdgcn_make_buffer_rsrc(
-          const_cast<uint16_t *>(wbase + (int64_t)(h + n0) * a.K), 0, wv * row_bytes, kBufferWord3);
-    } else {
-      const int wv = min(BNW, a.w_rows - n0);
-      rs_w0 = __builtin_amdgcn_make_buffer_rsrc(
-          const_cast<uint16_t *>(wbase + (int64_t)n0 * a.K), 0, wv * row_bytes, kBufferWord3);
-      rs_w1 = rs_w0;
-    }
-    // thread's first row (tid / CH) and 16-byte chunk (tid % CH); load i
-    // covers row tid / CH + i * (NT / CH)
-    const uint32_t voff0 = (uint32_t)(tid / CH) * row_bytes + (uint32_t)(tid % CH) * 16u;
+  static __device__ __forceinline__ void gload(const Tile &t, uint32_t v0, uint32_t row_bytes,
+                                               u32x4_t (&ra)[A_LD], u32x4_t (&rw)[W_LD], int kt) {
     const uint32_t istride = (uint32_t)(NT / CH) * row_bytes;
-
-    f32x4_t acc[FW][FM];
+    // the k offset is uniform: it goes in the scalar offset, so the vector
+    // offsets stay loop-invariant (row validity is decided by them alone)
+    const int ko = kt * (BK * 2);
 #pragma unroll
-    for (int i = 0; i < FW; ++i)
+    for (int i = 0; i < A_LD; ++i)
+      ra[i] = __builtin_amdgcn_raw_buffer_load_b128(t.rs_a, v0 + i * istride, ko, 0);
 #pragma unroll
-      for (int j = 0; j < FM; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-
-    // Two register stages (prefetch distance 2) feed two LDS buffers: the
-    // loads of stage k+2 are issued while stage k is computed and stored to
-    // LDS only after stage k+1 is computed.
-    u32x4_t ra0[A_LD], rw0[W_LD];
-    u32x4_t ra1[PFD == 2 ? A_LD : 1], rw1[PFD == 2 ? W_LD : 1];
-    auto gload = [&](u32x4_t(&ra)[A_LD], u32x4_t(&rw)[W_LD], int kt) {
-      const uint32_t ko = (uint32_t)kt * (BK * 2);
-#pragma unroll
-      for (int i = 0; i < A_LD; ++i)
-        ra[i] = __builtin_amdgcn_raw_buffer_load_b128(rs_a, voff0 + i * istride + ko, 0, 0);
-#pragma unroll
-      for (int i = 0; i < W_LD; ++i) {
-        if (!SWI || i < W_LD / 2) {
-          rw[i] = __builtin_amdgcn_raw_buffer_load_b128(rs_w0, voff0 + i * istride + ko, 0, 0);
-        } else {
-          rw[i] = __builtin_amdgcn_raw_buffer_load_b128(
-              rs_w1, voff0 + (i - W_LD / 2) * istride + ko, 0, 0);
-        }
-      }
-    };
-    auto lstore = [&](const u32x4_t(&ra)[A_LD], const u32x4_t(&rw)[W_LD], int buf) {
-#pragma unroll
-      for (int i = 0; i < A_LD; ++i) {
-        const int q = tid + i * NT;
-        As[buf][(q / CH) * CH + swz<BK>(q % CH, q / CH)] = ra[i];
-      }
-#pragma unroll
-      for (int i = 0; i < W_LD; ++i) {
-        const int q = tid + i * NT;
-        Ws[buf][(q / CH) * CH + swz<BK>(q % CH, q / CH)] = rw[i];
-      }
-    };
-    auto wrow = [&](int i) {
-      if constexpr (SWI) {
-        return (i < FW / 2) ? wn * (WTW / 2) + i * 16 + lrow
-                            : BNW / 2 + wn * (WTW / 2) + (i - FW / 2) * 16 + lrow;
+    for (int i = 0; i < W_LD; ++i) {
+      if (!SWI || i < W_LD / 2) {
+        rw[i] = __builtin_amdgcn_raw_buffer_load_b128(t.rs_w0, v0 + i * istride, ko, 0);
       } else {
-        return wn * WTW + i * 16 + lrow;
-      }
-    };
-    // Token fragments of every k32 step are read first, then weight
-    // fragments are streamed PD ahead of the MFMAs that use them.
-    auto compute = [&](int buf) {
-      bf16x8_t fa[KS][FM], fw[KS][FW];
-#pragma unroll
-      for (int s = 0; s < KS; ++s) {
-        const int ch = 4 * s + lch;
-#pragma unroll
-        for (int j = 0; j < FM; ++j) {
-          const int r = wm * WTM + j * 16 + lrow;
-          fa[s][j] = __builtin_bit_cast(bf16x8_t, As[buf][r * CH + swz<BK>(ch, r)]);
-        }
-      }
-#pragma unroll
-      for (int s = 0; s < KS; ++s) {
-        const int ch = 4 * s + lch;
-#pragma unroll
-        for (int i = 0; i < FW; ++i) {
-          const int r = wrow(i);
-          fw[s][i] = __builtin_bit_cast(bf16x8_t, Ws[buf][r * CH + swz<BK>(ch, r)]);
-        }
-      }
-#pragma unroll
-      for (int s = 0; s < KS; ++s)
-#pragma unroll
-        for (int i = 0; i < FW; ++i)
-#pragma unroll
-          for (int j = 0; j < FM; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fw[s][i], fa[s][j], acc[i][j], 0, 0, 0);
-      constexpr int NWF = KS * FW;
-      constexpr int PD = (8 + FM - 1) / FM < NWF ? (8 + FM - 1) / FM : NWF;
-      __builtin_amdgcn_sched_group_barrier(0x100, KS * FM + PD, 0);
-#pragma unroll
-      for (int n = 0; n < NWF; ++n) {
-        __builtin_amdgcn_sched_group_barrier(0x008, FM, 0);
-        if (n + PD < NWF) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      }
-    };
-
-    // Scheduling fences keep each stage's global loads ahead of the MFMAs
-    // (the compiler would otherwise sink them next to their LDS stores and
-    // expose the whole load latency).
-    if constexpr (PFD == 2) {
-      gload(ra0, rw0, 0);
-      lstore(ra0, rw0, 0);
-      gload(ra1, rw1, 1);
-      __syncthreads();
-      int kt = 0;
-      for (; kt + 2 <= nk; kt += 2) {
-        // even step: LDS buffer 0 holds stage kt, registers 1 hold stage kt+1
-        gload(ra0, rw0, kt + 2);
-        __builtin_amdgcn_sched_barrier(0);
-        compute(0);
-        __builtin_amdgcn_sched_barrier(0);
-        lstore(ra1, rw1, 1);
-        __syncthreads();
-        // odd step: LDS buffer 1 holds stage kt+1, registers 0 hold stage kt+2
-        gload(ra1, rw1, kt + 3);
-        __builtin_amdgcn_sched_barrier(0);
-        compute(1);
-        __builtin_amdgcn_sched_barrier(0);
-        lstore(ra0, rw0, 0);
-        __syncthreads();
-      }
-      if (kt < nk) compute(0);   // odd stage count: the last stage is in buffer 0
-    } else {
-      // one register stage: the loads of stage k+1 fly while stage k computes
-      gload(ra0, rw0, 0);
-      lstore(ra0, rw0, 0);
-      __syncthreads();
-      for (int kt = 0; kt < nk; ++kt) {
-        const int buf = kt & 1;
-        gload(ra0, rw0, kt + 1);
-        __builtin_amdgcn_sched_barrier(0);
-        compute(buf);
-        __builtin_amdgcn_sched_barrier(0);
-        lstore(ra0, rw0, buf ^ 1);
-        __syncthreads();
+        rw[i] = __builtin_amdgcn_raw_buffer_load_b128(
+            t.rs_w1, v0 + (i - W_LD / 2) * istride, ko, 0);
       }
     }
+  }
 
-    // ---- epilogue: lane owns columns 4*(lane/16)+0..3 of token row lane%16 ----
+  static __device__ __forceinline__ void lstore(u32x4_t *As, u32x4_t *Ws,
+                                                const u32x4_t (&ra)[A_LD],
+                                                const u32x4_t (&rw)[W_LD]) {
+    const int tid = threadIdx.x;
+#pragma unroll
+    for (int i = 0; i < A_LD; ++i) {
+      const int q = tid + i * NT;
+      As[(q / CH) * CH + swz<BK>(q % CH, q / CH)] = ra[i];
+    }
+#pragma unroll
+    for (int i = 0; i < W_LD; ++i) {
+      const int q = tid + i * NT;
+      Ws[(q / CH) * CH + swz<BK>(q % CH, q / CH)] = rw[i];
+    }
+  }
+
+  // LDS row of weight fragment i of wave column wn (SwiGLU: gate fragments
+  // first, then the matching up fragments from the second half of the tile)
+  static __device__ __forceinline__ int wrow(int wn, int i, int lrow) {
+    if constexpr (SWI) {
+      return (i < FW / 2) ? wn * (WTW / 2) + i * 16 + lrow
+                          : BNW / 2 + wn * (WTW / 2) + (i - FW / 2) * 16 + lrow;
+    } else {
+      return wn * WTW + i * 16 + lrow;
+    }
+  }
+
+  static constexpr int NWF = KS * FW;   // weight fragments per stage
+  // weight fragments read ahead of the MFMAs that use them
+  static constexpr int PD = (8 + FM - 1) / FM < NWF ? (8 + FM - 1) / FM : NWF;
+
+  // MFMA operands of one stage: token fragment (k32 step s, row block j)
+  // and weight fragment n = s * FW + i
+  struct Frags {
+    bf16x8_t a[KS][FM];
+    bf16x8_t w[NWF];
+  };
+
+  // LDS slot (16-byte units) of chunk ch of row r of the token / weight tile
+  static __device__ __forceinline__ int a_idx(int r, int ch) {
+    if constexpr (PLANES) return ((ch >> 2) * BM + r) * 4 + (ch & 3);
+    return r * CH + swz<BK>(ch, r);
+  }
+  static __device__ __forceinline__ int w_idx(int r, int ch) {
+    if constexpr (PLANES) return ((ch >> 2) * BNW + r) * 4 + (ch & 3);
+    return r * CH + swz<BK>(ch, r);
+  }
+
+  static __device__ __forceinline__ bf16x8_t read_a(const u32x4_t *As, int s, int j, int wm) {
+    const int lane = threadIdx.x % 64;
+    const int ch = 4 * s + lane / 16;
+    const int r = wm * WTM + j * 16 + lane % 16;
+    return __builtin_bit_cast(bf16x8_t, As[a_idx(r, ch)]);
+  }
+  static __device__ __forceinline__ bf16x8_t read_w(const u32x4_t *Ws, int n, int wn) {
+    const int lane = threadIdx.x % 64;
+    const int ch = 4 * (n / FW) + lane / 16;
+    const int r = wrow(wn, n % FW, lane % 16);
+    return __builtin_bit_cast(bf16x8_t, Ws[w_idx(r, ch)]);
+  }
+
+  // Token fragments of every k32 step and the first PD weight fragments.
+  static __device__ __forceinline__ void head(const u32x4_t *As, const u32x4_t *Ws, Frags &f,
+                                              int wm, int wn) {
+#pragma unroll
+    for (int s = 0; s < KS; ++s)
+#pragma unroll
+      for (int j = 0; j < FM; ++j) f.a[s][j] = read_a(As, s, j, wm);
+#pragma unroll
+    for (int n = 0; n < PD; ++n) f.w[n] = read_w(Ws, n, wn);
+  }
+
+  // The stage's MFMAs; the remaining weight fragments are streamed PD ahead
+  // of their first use.  LEAD: the head's reads are in the same scheduling
+  // region and go first.
+  template <bool LEAD>
+  static __device__ __forceinline__ void body(const u32x4_t *Ws, Frags &f,
+                                              f32x4_t (&acc)[FW][FM], int wn) {
+#pragma unroll
+    for (int n = PD; n < NWF; ++n) f.w[n] = read_w(Ws, n, wn);
+#pragma unroll
+    for (int n = 0; n < NWF; ++n)
+#pragma unroll
+      for (int j = 0; j < FM; ++j)
+        acc[n % FW][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f.w[n], f.a[n / FW][j],
+                                                                 acc[n % FW][j], 0, 0, 0);
+    if constexpr (LEAD) __builtin_amdgcn_sched_group_barrier(0x100, KS * FM + PD, 0);
+#pragma unroll
+    for (int n = 0; n < NWF; ++n) {
+      __builtin_amdgcn_sched_group_barrier(0x008, FM, 0);
+      if (n + PD < NWF) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+  }
+
+  // One whole stage: head and body in one scheduling region.
+  static __device__ __forceinline__ void compute(const u32x4_t *As, const u32x4_t *Ws,
+                                                 f32x4_t (&acc)[FW][FM], int wm, int wn) {
+    Frags f;
+    head(As, Ws, f, wm, wn);
+    body<true>(Ws, f, acc, wn);
+  }
+
+  // lane owns columns 4*(lane/16)+0..3 of token row lane%16 of each fragment;
+  // values are computed unconditionally and only the stores are predicated,
+  // which keeps the epilogue one basic block
+  static __device__ __forceinline__ void epilogue(const GemmArgs &a, const Tile &t,
+                                                  const f32x4_t (&acc)[FW][FM], int wm, int wn) {
+    const int lane = threadIdx.x % 64;
+    const int lrow = lane % 16;
+    const int lch = lane / 16;
     constexpr int FO = SWI ? FW / 2 : FW;
     const int wcol0 = SWI ? wn * (WTW / 2) : wn * WTW;
+    const bool has_bias = MODE != kUpSwiglu && a.bias && t.g < a.E;
 #pragma unroll
     for (int i = 0; i < FO; ++i) {
-      const int col = n0 + wcol0 + i * 16 + 4 * lch;
-      if (col >= a.n_out) continue;
+      const int col = t.n0 + wcol0 + i * 16 + 4 * lch;
+      const bool col_ok = col < a.n_out;
       float bias[4] = {0.f, 0.f, 0.f, 0.f};
-      if (MODE != kUpSwiglu && a.bias && g < a.E) {
-        const uint2 b = *reinterpret_cast<const uint2 *>(a.bias + (int64_t)g * a.n_out + col);
+      if (has_bias && col_ok) {
+        const uint2 b = *reinterpret_cast<const uint2 *>(a.bias + (int64_t)t.g * a.n_out + col);
         bias[0] = __uint_as_float(b.x << 16);
         bias[1] = __uint_as_float(b.x & 0xffff0000u);
         bias[2] = __uint_as_float(b.y << 16);
@@ -336,8 +350,7 @@ void gemm_bf16_kernel(GemmArgs a) {
       }
 #pragma unroll
       for (int j = 0; j < FM; ++j) {
-        const int m = m0 + wm * WTM + j * 16 + lrow;
-        if (m >= rows) continue;
+        const int m = t.m0 + wm * WTM + j * 16 + lrow;
         float v[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
@@ -352,9 +365,328 @@ void gemm_bf16_kernel(GemmArgs a) {
         uint2 o;
         o.x = pack_bf16x2(v[0], v[1]);
         o.y = pack_bf16x2(v[2], v[3]);
-        *reinterpret_cast<uint2 *>(a.c + (int64_t)(grow0 + m) * a.n_out + col) = o;
+        if (col_ok && m < t.rows)
+          *reinterpret_cast<uint2 *>(a.c + (int64_t)(t.grow0 + m) * a.n_out + col) = o;
+        // one output fragment at a time: keeps the scheduler from pulling
+        // every accumulator into VGPRs at once
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
+  }
+};
+
+// slice order: XCD x (= blockIdx % 8, workgroups are dealt to the XCDs
+// round-robin) takes a contiguous run of tiles
+__device__ __forceinline__ int slice_tile(int it) {
+  const int nblk = gridDim.x;
+  return it * nblk + (blockIdx.x % 8) * (nblk / 8) + blockIdx.x / 8;
+}
+
+// Lock-step kernel: every wave loads, stores and computes each stage; the
+// loads of stage k+1 (PFD 1) or k+2 (PFD 2, register double buffer) fly
+// while stage k is computed.  At least two waves per SIMD: 8-wave tiles run
+// one workgroup per CU, 4-wave tiles two (their register budget is capped
+// at 256 per lane).
+template <int BM, int BNW, int WM, int WN, int BK, int PFD, int MODE>
+__global__ __launch_bounds__(WM *WN * 64) __attribute__((amdgpu_waves_per_eu(2)))
+void gemm_bf16_kernel(GemmArgs a) {
+  using TM = TileMath<BM, BNW, WM, WN, BK, MODE>;
+  constexpr int NT = TM::NT, CH = TM::CH, A_LD = TM::A_LD, W_LD = TM::W_LD;
+  constexpr int FM = TM::FM, FW = TM::FW;
+
+  __shared__ u32x4_t As[2][BM * CH];
+  __shared__ u32x4_t Ws[2][BNW * CH];
+  __shared__ int tprefix[2 * NT + 2];
+  __shared__ int scan_tmp[NT / 64];
+
+  const int wave = threadIdx.x / 64;
+  const int wm = wave / WN;
+  const int wn = wave % WN;
+  tile_prefix<NT, BM>(a, tprefix, scan_tmp);
+  __syncthreads();
+  const int total_tiles = tprefix[a.E + a.S] * a.n_tiles;
+  const int nk = a.K / BK;
+  const uint32_t row_bytes = (uint32_t)a.K * 2u;
+  const uint32_t v0 = TM::voff0(row_bytes);
+
+  for (int it = 0;; ++it) {
+    const int L = slice_tile(it);
+    if (L >= total_tiles) break;
+    const Tile t = decode_tile<BM, BNW, TM::SWI>(a, tprefix, L);
+
+    f32x4_t acc[FW][FM];
+#pragma unroll
+    for (int i = 0; i < FW; ++i)
+#pragma unroll
+      for (int j = 0; j < FM; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+    u32x4_t ra0[A_LD], rw0[W_LD];
+    u32x4_t ra1[PFD == 2 ? A_LD : 1], rw1[PFD == 2 ? W_LD : 1];
+
+    // Scheduling fences keep each stage's global loads ahead of the MFMAs
+    // (the compiler would otherwise sink them next to their LDS stores and
+    // expose the whole load latency).
+    if constexpr (PFD == 2) {
+      TM::gload(t, v0, row_bytes, ra0, rw0, 0);
+      TM::lstore(As[0], Ws[0], ra0, rw0);
+      TM::gload(t, v0, row_bytes, ra1, rw1, 1);
+      __syncthreads();
+      int kt = 0;
+      for (; kt + 2 <= nk; kt += 2) {
+        // even step: LDS buffer 0 holds stage kt, registers 1 hold stage kt+1
+        TM::gload(t, v0, row_bytes, ra0, rw0, kt + 2);
+        __builtin_amdgcn_sched_barrier(0);
+        TM::compute(As[0], Ws[0], acc, wm, wn);
+        __builtin_amdgcn_sched_barrier(0);
+        TM::lstore(As[1], Ws[1], ra1, rw1);
+        __syncthreads();
+        // odd step: LDS buffer 1 holds stage kt+1, registers 0 hold stage kt+2
+        TM::gload(t, v0, row_bytes, ra1, rw1, kt + 3);
+        __builtin_amdgcn_sched_barrier(0);
+        TM::compute(As[1], Ws[1], acc, wm, wn);
+        __builtin_amdgcn_sched_barrier(0);
+        TM::lstore(As[0], Ws[0], ra0, rw0);
+        __syncthreads();
+      }
+      if (kt < nk) TM::compute(As[0], Ws[0], acc, wm, wn);   // odd stage count
+    } else {
+      TM::gload(t, v0, row_bytes, ra0, rw0, 0);
+      TM::lstore(As[0], Ws[0], ra0, rw0);
+      __syncthreads();
+      for (int kt = 0; kt < nk; ++kt) {
+        const int buf = kt & 1;
+        TM::gload(t, v0, row_bytes, ra0, rw0, kt + 1);
+        __builtin_amdgcn_sched_barrier(0);
+        TM::compute(As[buf], Ws[buf], acc, wm, wn);
+        __builtin_amdgcn_sched_barrier(0);
+        TM::lstore(As[buf ^ 1], Ws[buf ^ 1], ra0, rw0);
+        __syncthreads();
+      }
+    }
+    TM::epilogue(a, t, acc, wm, wn);
+  }
+}
+
+// Ping-pong kernel for large groups: 256 x 256 tiles, 8 waves in two groups
+// of four, one wave of each group per SIMD.  The groups alternate between a
+// compute slot (the MFMAs of one whole stage) and a memory slot (store the
+// staged registers of the next stage to LDS, issue the global loads of the
+// stage after it), offset by one slot, so that on every SIMD one wave feeds
+// the matrix core while the other moves data.  Slots end at LDS-only
+// barriers: global loads stay in flight for two slots.
+//
+// Group 0 (token rows 0..127) computes stage k in slot 2k, group 1 (rows
+// 128..255) in slot 2k+1.  Group 1 stores its half of stage k+1 in slot
+// 2k, group 0 in slot 2k+1, so stage k+1 is complete before slot 2k+2 and
+// two LDS buffers suffice: stage k+2 overwrites stage k only from slot
+// 2k+2 on, after both groups have finished it.
+template <int MODE>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2)))
+void gemm_pp_kernel(GemmArgs a) {
+  constexpr int BM = 256, BNW = 256, WM = 4, WN = 2, BK = 64;
+  using TM = TileMath<BM, BNW, WM, WN, BK, MODE>;
+  constexpr int NT = TM::NT, CH = TM::CH, A_LD = TM::A_LD, W_LD = TM::W_LD;
+  constexpr int FM = TM::FM, FW = TM::FW;
+
+  __shared__ u32x4_t As[2][BM * CH];
+  __shared__ u32x4_t Ws[2][BNW * CH];
+  __shared__ int tprefix[2 * NT + 2];
+  __shared__ int scan_tmp[NT / 64];
+
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / 64);
+  const int wm = wave / WN;
+  const int wn = wave % WN;
+  const int grp = wave / 4;
+  tile_prefix<NT, BM>(a, tprefix, scan_tmp);
+  __syncthreads();
+  const int total_tiles = tprefix[a.E + a.S] * a.n_tiles;
+  const int nk = a.K / BK;
+  const uint32_t row_bytes = (uint32_t)a.K * 2u;
+  const uint32_t v0 = TM::voff0(row_bytes);
+
+  for (int it = 0;; ++it) {
+    const int L = slice_tile(it);
+    if (L >= total_tiles) break;
+    const Tile t = decode_tile<BM, BNW, TM::SWI>(a, tprefix, L);
+
+    f32x4_t acc[FW][FM];
+#pragma unroll
+    for (int i = 0; i < FW; ++i)
+#pragma unroll
+      for (int j = 0; j < FM; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+    u32x4_t ra[A_LD], rw[W_LD];
+    TM::gload(t, v0, row_bytes, ra, rw, 0);
+    TM::lstore(As[0], Ws[0], ra, rw);
+    if (nk > 1) TM::gload(t, v0, row_bytes, ra, rw, 1);
+    __syncthreads();
+
+    auto memory_slot = [&](int kt) {
+      if (kt + 1 < nk) TM::lstore(As[(kt + 1) & 1], Ws[(kt + 1) & 1], ra, rw);
+      if (kt + 2 < nk) TM::gload(t, v0, row_bytes, ra, rw, kt + 2);
+    };
+    // group 1 runs its memory slots one stage ahead; one call site each for
+    // compute and memory keeps the register assignment identical for both
+    // groups
+    if (grp == 1) {
+      memory_slot(0);
+      lds_barrier();
+    }
+    for (int kt = 0; kt < nk; ++kt) {
+      TM::compute(As[kt & 1], Ws[kt & 1], acc, wm, wn);
+      lds_barrier();
+      memory_slot(kt + grp);
+      if (kt + grp < nk) lds_barrier();
+    }
+    TM::epilogue(a, t, acc, wm, wn);
+  }
+}
+
+// DMA-fed kernel for large groups: BM x BNW tiles (token rows x weight
+// rows), WM x WN waves.  Operands go from global memory straight into LDS
+// (buffer loads with the LDS flag): stores from registers would compete with
+// the fragment reads for the LDS port, DMA writes barely do, and no staging
+// registers are needed.  Stages are k32 wide (rows of 64 B, so a 16-row
+// fragment read or a 16-row DMA block is one contiguous 1 KB) and rotate
+// through four LDS buffers:
+//
+//   iteration s: read the operands of stage s+1 | MFMAs of stage s |
+//                DMA stage s+4 (into the buffer of stage s, whose operands
+//                are in registers by now) | wait for stage s+2 | barrier
+//
+// so the MFMAs after a barrier never wait for memory and a DMA has more
+// than two iterations to land (L2 misses included).  DMAs and reads past
+// the last stage stay in bounds (buffer descriptors; spare LDS buffers) and
+// are never used; rows past the group's end or the weight matrix only feed
+// outputs that the epilogue drops.
+template <int BM, int BNW, int WM, int WN, int MODE>
+__global__ __launch_bounds__(WM *WN * 64) __attribute__((amdgpu_waves_per_eu(WM * WN / 4)))
+void gemm_dma_kernel(GemmArgs a) {
+  constexpr int BK = 32, NB = 4, NW = WM * WN;
+  using TM = TileMath<BM, BNW, WM, WN, BK, MODE>;
+  constexpr int NT = TM::NT, CH = TM::CH;
+  constexpr int FM = TM::FM, FW = TM::FW;
+  constexpr int ABLK = BM / 16, WBLK = BNW / 16;        // 16-row DMA blocks
+  constexpr int BPW = (ABLK + WBLK) / NW;                // blocks per wave
+  static_assert(BPW * NW == ABLK + WBLK && CH == 4, "blocks split evenly");
+  static_assert(2 * (FM + FW + BPW) <= FW * FM, "operand traffic fits the MFMA stream");
+
+  __shared__ u32x4_t As[NB][BM * CH];
+  __shared__ u32x4_t Ws[NB][BNW * CH];
+  __shared__ int tprefix[2 * NT + 2];
+  __shared__ int scan_tmp[NT / 64];
+
+  const int lane = threadIdx.x % 64;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / 64);
+  const int wm = wave / WN;
+  const int wn = wave % WN;
+  tile_prefix<NT, BM>(a, tprefix, scan_tmp);
+  __syncthreads();
+  const int total_tiles = tprefix[a.E + a.S] * a.n_tiles;
+  const int nk = a.K / BK;
+  const uint32_t row_bytes = (uint32_t)a.K * 2u;
+  // lane -> row lane / 4, 16-byte chunk lane % 4 of a 16-row block
+  const uint32_t voff = (uint32_t)(lane / 4) * row_bytes + (uint32_t)(lane % 4) * 16u;
+
+  for (int it = 0;; ++it) {
+    const int L = slice_tile(it);
+    if (L >= total_tiles) break;
+    const Tile t = decode_tile<BM, BNW, TM::SWI>(a, tprefix, L);
+
+    // wave w moves blocks BPW w .. BPW w + BPW - 1 of the stage: token
+    // blocks first, then weight blocks (SwiGLU: gate rows from one
+    // descriptor, up rows from the other)
+    auto dma = [&](int s) {
+#pragma unroll
+      for (int i = 0; i < BPW; ++i) {
+        const int blk = wave * BPW + i;
+        __amdgpu_buffer_rsrc_t rs;
+        u32x4_t *dst;
+        int row;
+        if (blk < ABLK) {
+          rs = t.rs_a;
+          dst = As[s % NB] + blk * 64;
+          row = blk * 16;
+        } else {
+          const int wb = blk - ABLK;
+          dst = Ws[s % NB] + wb * 64;
+          if (TM::SWI && wb >= WBLK / 2) {
+            rs = t.rs_w1;
+            row = (wb - WBLK / 2) * 16;
+          } else {
+            rs = t.rs_w0;
+            row = wb * 16;
+          }
+        }
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, dst, 16, voff,
+                                                 row * (int)row_bytes + s * (BK * 2), 0, 0);
+      }
+    };
+
+    f32x4_t acc[FW][FM];
+#pragma unroll
+    for (int i = 0; i < FW; ++i)
+#pragma unroll
+      for (int j = 0; j < FM; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+    bf16x8_t fa0[FM], fw0[FW], fa1[FM], fw1[FW];
+    auto read_stage = [&](int buf, bf16x8_t(&fa)[FM], bf16x8_t(&fw)[FW]) {
+#pragma unroll
+      for (int j = 0; j < FM; ++j) fa[j] = TM::read_a(As[buf], 0, j, wm);
+#pragma unroll
+      for (int i = 0; i < FW; ++i) fw[i] = TM::read_w(Ws[buf], i, wn);
+    };
+    auto iteration = [&](int s, bf16x8_t(&fa_cur)[FM], bf16x8_t(&fw_cur)[FW],
+                         bf16x8_t(&fa_nxt)[FM], bf16x8_t(&fw_nxt)[FW]) {
+      read_stage((s + 1) % NB, fa_nxt, fw_nxt);
+#pragma unroll
+      for (int i = 0; i < FW; ++i)
+#pragma unroll
+        for (int j = 0; j < FM; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fw_cur[i], fa_cur[j], acc[i][j],
+                                                               0, 0, 0);
+      dma(s + 4);
+      // operand reads one per two MFMAs, then the DMAs one per two MFMAs
+#pragma unroll
+      for (int q = 0; q < FM + FW; ++q) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+#pragma unroll
+      for (int q = 0; q < BPW; ++q) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, FW * FM - 2 * (FM + FW + BPW), 0);
+      // Stage s+2 has landed (stages s+3 and s+4 may still be in flight) and
+      // this wave's operand reads are done; then a plain barrier (a fence
+      // would also wait for the DMAs still in flight).  The empty asm
+      // statements keep the compiler from moving LDS accesses across it.
+      __builtin_amdgcn_s_waitcnt(0x0070 | (2 * BPW));   // vmcnt(2 BPW) lgkmcnt(0)
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+    };
+
+    dma(0);
+    dma(1);
+    dma(2);
+    dma(3);
+    __builtin_amdgcn_s_waitcnt(0x0070 | (2 * BPW));   // stages 0 and 1
+    __syncthreads();
+    read_stage(0, fa0, fw0);
+
+    // two stages per trip so the register sets are named statically (nk is
+    // even: K is a multiple of 64)
+    for (int s = 0; s < nk; s += 2) {
+      iteration(s, fa0, fw0, fa1, fw1);
+      iteration(s + 1, fa1, fw1, fa0, fw0);
+    }
+    // the next tile's first DMAs go to buffers that the last (unused) DMAs
+    // and reads above may still touch
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+    __syncthreads();
+    TM::epilogue(a, t, acc, wm, wn);
   }
 }
 
@@ -373,30 +705,49 @@ static int num_cus() {
   return cached;
 }
 
-// persistent: one resident wave of workgroups walks all tiles; otherwise one
-// workgroup per tile (the hardware dispatcher balances short streaming tiles)
-template <int BM, int BNW, int WM, int WN, int BK, int PFD, int MODE, bool PERSIST = true>
-static hipError_t launch_bm(const GemmArgs &a0, hipStream_t s) {
-  constexpr int NT = WM * WN * 64;
-  GemmArgs a = a0;
-  constexpr int BN_OUT = MODE == kUpSwiglu ? BNW / 2 : BNW;
+// Persistent launch: one resident wave of workgroups walks all tiles (fewer
+// when there are fewer tiles), rounded to a multiple of 8 for the slice
+// order.  `per_cu` caches the occupancy of the instantiation.
+template <int BM, int BN_OUT, int NT>
+static hipError_t launch_persistent(const void *kernel, int &per_cu, GemmArgs a,
+                                    hipStream_t s) {
   a.n_tiles = (a.n_out + BN_OUT - 1) / BN_OUT;
   // upper bound of the ragged m-tile count: every group wastes < 1 tile
   const int64_t mt_bound = (int64_t)(a.routed_rows + BM - 1) / BM + a.E + a.S;
   const int64_t tiles = mt_bound * a.n_tiles;
-  static int per_cu = 0;   // resident workgroups per CU for this instantiation
   if (!per_cu) {
     int nb = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-            &nb, gemm_bf16_kernel<BM, BNW, WM, WN, BK, PFD, MODE>, NT, 0) != hipSuccess || nb <= 0)
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, kernel, NT, 0) != hipSuccess || nb <= 0)
       nb = 1;
     per_cu = nb;
   }
-  int64_t grid = (int64_t)num_cus() * per_cu;   // persistent grid
-  if (!PERSIST || tiles < grid) grid = tiles;
-  grid = ((grid + 7) / 8) * 8;     // the slice order needs a multiple of 8
-  gemm_bf16_kernel<BM, BNW, WM, WN, BK, PFD, MODE><<<(int)grid, NT, 0, s>>>(a);
-  return hipGetLastError();
+  int64_t grid = (int64_t)num_cus() * per_cu;
+  if (tiles < grid) grid = tiles;
+  grid = ((grid + 7) / 8) * 8;
+  void *args[] = {&a};
+  return hipLaunchKernel(kernel, dim3((unsigned)grid), dim3(NT), args, 0, s);
+}
+
+template <int BM, int BNW, int WM, int WN, int BK, int PFD, int MODE>
+static hipError_t launch_bm(const GemmArgs &a, hipStream_t s) {
+  static int per_cu = 0;
+  return launch_persistent<BM, MODE == kUpSwiglu ? BNW / 2 : BNW, WM * WN * 64>(
+      reinterpret_cast<const void *>(&gemm_bf16_kernel<BM, BNW, WM, WN, BK, PFD, MODE>),
+      per_cu, a, s);
+}
+
+template <int MODE>
+static hipError_t launch_pp(const GemmArgs &a, hipStream_t s) {
+  static int per_cu = 0;
+  return launch_persistent<256, MODE == kUpSwiglu ? 128 : 256, 512>(
+      reinterpret_cast<const void *>(&gemm_pp_kernel<MODE>), per_cu, a, s);
+}
+
+template <int BM, int BNW, int WM, int WN, int MODE>
+static hipError_t launch_dma(const GemmArgs &a, hipStream_t s) {
+  static int per_cu = 0;
+  return launch_persistent<BM, MODE == kUpSwiglu ? BNW / 2 : BNW, WM * WN * 64>(
+      reinterpret_cast<const void *>(&gemm_dma_kernel<BM, BNW, WM, WN, MODE>), per_cu, a, s);
 }
 
 // Groups are split by row count into two tile classes, one launch each:
@@ -410,7 +761,10 @@ static hipError_t launch_classes(GemmArgs a, hipStream_t s) {
   if (a.T > 64) {
     a.min_rows = 65;
     a.max_rows = 1 << 30;
-    if ((err = launch_bm<256, 256, 4, 2, 64, 1, MODE>(a, s)) != hipSuccess) return err;
+    // measured on MI355X: the DMA-fed kernel is ahead up to K = 8192, the
+    // ping-pong kernel on the long-K down projections
+    err = a.K <= 8192 ? launch_dma<256, 256, 4, 2, MODE>(a, s) : launch_pp<MODE>(a, s);
+    if (err != hipSuccess) return err;
   }
   a.min_rows = 1;
   a.max_rows = 64;
