@@ -35,6 +35,8 @@
 // 32 B/clk that full MFMA rate on 256 x 256 tiles would need), not by LDS.
 #include "common.h"
 
+#include <cmath>
+
 namespace moe {
 
 enum GemmMode { kUpGelu = 0, kUpSwiglu = 1, kDown = 2 };
@@ -194,8 +196,6 @@ struct TileMath {
   static constexpr int W_LD = BNW * CH / NT;
   static_assert(BK == 32 || BK == 64, "stage depth");
   static_assert(FM >= 1 && FW >= 1 && (!SWI || FW % 2 == 0), "wave tile");
-  static_assert(A_LD * NT == BM * CH && W_LD * NT == BNW * CH, "load split");
-  static_assert(!SWI || (W_LD % 2 == 0), "gate and up rows split the loads evenly");
 
   // thread's first row (tid / CH) and 16-byte chunk (tid % CH); load i
   // covers row tid / CH + i * (NT / CH)
@@ -203,8 +203,14 @@ struct TileMath {
     return (uint32_t)(threadIdx.x / CH) * row_bytes + (uint32_t)(threadIdx.x % CH) * 16u;
   }
 
+  // register-staged stage loads: every thread moves A_LD + W_LD chunks
+  static constexpr void check_load_split() {
+    static_assert(A_LD * NT == BM * CH && W_LD * NT == BNW * CH, "load split");
+    static_assert(!SWI || (W_LD % 2 == 0), "gate and up rows split the loads evenly");
+  }
   static __device__ __forceinline__ void gload(const Tile &t, uint32_t v0, uint32_t row_bytes,
                                                u32x4_t (&ra)[A_LD], u32x4_t (&rw)[W_LD], int kt) {
+    check_load_split();
     const uint32_t istride = (uint32_t)(NT / CH) * row_bytes;
     // the k offset is uniform: it goes in the scalar offset, so the vector
     // offsets stay loop-invariant (row validity is decided by them alone)
@@ -467,23 +473,23 @@ void gemm_bf16_kernel(GemmArgs a) {
   }
 }
 
-// Ping-pong kernel for large groups: 256 x 256 tiles, 8 waves in two groups
-// of four, one wave of each group per SIMD.  The groups alternate between a
+// Ping-pong kernel for large groups: BM x 256 tiles (BM = 256 or 192), 8
+// waves in two groups of four, one wave of each group per SIMD.  The groups alternate between a
 // compute slot (the MFMAs of one whole stage) and a memory slot (store the
 // staged registers of the next stage to LDS, issue the global loads of the
 // stage after it), offset by one slot, so that on every SIMD one wave feeds
 // the matrix core while the other moves data.  Slots end at LDS-only
 // barriers: global loads stay in flight for two slots.
 //
-// Group 0 (token rows 0..127) computes stage k in slot 2k, group 1 (rows
-// 128..255) in slot 2k+1.  Group 1 stores its half of stage k+1 in slot
+// Group 0 (the first BM/2 token rows) computes stage k in slot 2k, group 1
+// (the others) in slot 2k+1.  Group 1 stores its half of stage k+1 in slot
 // 2k, group 0 in slot 2k+1, so stage k+1 is complete before slot 2k+2 and
 // two LDS buffers suffice: stage k+2 overwrites stage k only from slot
 // 2k+2 on, after both groups have finished it.
-template <int MODE>
+template <int BM, int MODE>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2)))
 void gemm_pp_kernel(GemmArgs a) {
-  constexpr int BM = 256, BNW = 256, WM = 4, WN = 2, BK = 64;
+  constexpr int BNW = 256, WM = 4, WN = 2, BK = 64;
   using TM = TileMath<BM, BNW, WM, WN, BK, MODE>;
   constexpr int NT = TM::NT, CH = TM::CH, A_LD = TM::A_LD, W_LD = TM::W_LD;
   constexpr int FM = TM::FM, FW = TM::FW;
@@ -567,9 +573,16 @@ void gemm_dma_kernel(GemmArgs a) {
   constexpr int NT = TM::NT, CH = TM::CH;
   constexpr int FM = TM::FM, FW = TM::FW;
   constexpr int ABLK = BM / 16, WBLK = BNW / 16;        // 16-row DMA blocks
-  constexpr int BPW = (ABLK + WBLK) / NW;                // blocks per wave
-  static_assert(BPW * NW == ABLK + WBLK && CH == 4, "blocks split evenly");
-  static_assert(2 * (FM + FW + BPW) <= FW * FM, "operand traffic fits the MFMA stream");
+  constexpr int NBLK = ABLK + WBLK;
+  // blocks per wave; when they do not split evenly the last waves repeat
+  // the stage's last block (same data to the same place), so that every
+  // wave issues the same number of DMAs and one vmcnt fits all
+  constexpr int BPW = (NBLK + NW - 1) / NW;
+  static_assert(CH == 4, "k32 stages");
+  // interleave: QM MFMAs per operand read or DMA, then the rest
+  constexpr int NMEM = FM + FW + BPW;
+  constexpr int QM = (FW * FM) / NMEM >= 2 ? 2 : 1;
+  static_assert(QM * NMEM <= FW * FM, "operand traffic fits the MFMA stream");
 
   __shared__ u32x4_t As[NB][BM * CH];
   __shared__ u32x4_t Ws[NB][BNW * CH];
@@ -599,7 +612,7 @@ void gemm_dma_kernel(GemmArgs a) {
     auto dma = [&](int s) {
 #pragma unroll
       for (int i = 0; i < BPW; ++i) {
-        const int blk = wave * BPW + i;
+        const int blk = min(wave * BPW + i, NBLK - 1);
         __amdgpu_buffer_rsrc_t rs;
         u32x4_t *dst;
         int row;
@@ -646,18 +659,19 @@ void gemm_dma_kernel(GemmArgs a) {
           acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fw_cur[i], fa_cur[j], acc[i][j],
                                                                0, 0, 0);
       dma(s + 4);
-      // operand reads one per two MFMAs, then the DMAs one per two MFMAs
+      // operand reads one per QM MFMAs, then the DMAs one per QM MFMAs
 #pragma unroll
       for (int q = 0; q < FM + FW; ++q) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, QM, 0);
         __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
       }
 #pragma unroll
       for (int q = 0; q < BPW; ++q) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, QM, 0);
         __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
       }
-      __builtin_amdgcn_sched_group_barrier(0x008, FW * FM - 2 * (FM + FW + BPW), 0);
+      if constexpr (FW * FM > QM * NMEM)
+        __builtin_amdgcn_sched_group_barrier(0x008, FW * FM - QM * NMEM, 0);
       // Stage s+2 has landed (stages s+3 and s+4 may still be in flight) and
       // this wave's operand reads are done; then a plain barrier (a fence
       // would also wait for the DMAs still in flight).  The empty asm
@@ -736,11 +750,11 @@ static hipError_t launch_bm(const GemmArgs &a, hipStream_t s) {
       per_cu, a, s);
 }
 
-template <int MODE>
+template <int BM, int MODE>
 static hipError_t launch_pp(const GemmArgs &a, hipStream_t s) {
   static int per_cu = 0;
-  return launch_persistent<256, MODE == kUpSwiglu ? 128 : 256, 512>(
-      reinterpret_cast<const void *>(&gemm_pp_kernel<MODE>), per_cu, a, s);
+  return launch_persistent<BM, MODE == kUpSwiglu ? 128 : 256, 512>(
+      reinterpret_cast<const void *>(&gemm_pp_kernel<BM, MODE>), per_cu, a, s);
 }
 
 template <int BM, int BNW, int WM, int WN, int MODE>
@@ -750,9 +764,33 @@ static hipError_t launch_dma(const GemmArgs &a, hipStream_t s) {
       reinterpret_cast<const void *>(&gemm_dma_kernel<BM, BNW, WM, WN, MODE>), per_cu, a, s);
 }
 
+// Large groups.  Row tile: 256 or 192 token rows, whichever needs fewer
+// tile rounds over the persistent grid (one workgroup per CU) once the
+// smaller tile's lower operand reuse is priced in (measured: about 12 %
+// more time per row); group sizes are device-side, so the count of m-tiles
+// is estimated as rows / BM plus half a tile per group.  Kernel: the
+// DMA-fed one up to K = 8192, the ping-pong one on longer K (measured on
+// MI355X).
+template <int MODE>
+static hipError_t launch_big(const GemmArgs &a, hipStream_t s) {
+  const double nblk = num_cus();
+  const int bn_out = MODE == kUpSwiglu ? 128 : 256;
+  const double n_tiles = (a.n_out + bn_out - 1) / bn_out;
+  const double rows = (double)a.routed_rows + (double)a.S * a.T;
+  const double groups = a.E + a.S;
+  auto cost = [&](double bm, double per_row) {
+    const double mt = rows / bm + 0.5 * groups;
+    return std::ceil(mt * n_tiles / nblk) * bm * per_row;
+  };
+  const bool bm192 = cost(192, 1.12) < cost(256, 1.0);
+  if (a.K <= 8192)
+    return bm192 ? launch_dma<192, 256, 4, 2, MODE>(a, s) : launch_dma<256, 256, 4, 2, MODE>(a, s);
+  return bm192 ? launch_pp<192, MODE>(a, s) : launch_pp<256, MODE>(a, s);
+}
+
 // Groups are split by row count into two tile classes, one launch each:
 // small groups (<= 64 rows: decode batches, cold experts) stream their
-// weights through 32-row tiles; larger groups use 256 x 256 tiles.  The
+// weights through 32-row tiles; larger groups use 256- or 192-row tiles.  The
 // large class is skipped when no group can exceed 64 rows (every group has
 // at most T rows).
 template <int MODE>
@@ -761,10 +799,7 @@ static hipError_t launch_classes(GemmArgs a, hipStream_t s) {
   if (a.T > 64) {
     a.min_rows = 65;
     a.max_rows = 1 << 30;
-    // measured on MI355X: the DMA-fed kernel is ahead up to K = 8192, the
-    // ping-pong kernel on the long-K down projections
-    err = a.K <= 8192 ? launch_dma<256, 256, 4, 2, MODE>(a, s) : launch_pp<MODE>(a, s);
-    if (err != hipSuccess) return err;
+    if ((err = launch_big<MODE>(a, s)) != hipSuccess) return err;
   }
   a.min_rows = 1;
   a.max_rows = 64;

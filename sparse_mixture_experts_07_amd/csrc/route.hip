@@ -335,8 +335,8 @@ struct RowLoad<float> {      // 32 fp32 columns = 8 x 16 B
 
 constexpr int kBufWord3 = 0x00020000;   // raw buffer resource, gfx9 family
 
-template <typename XT, int EP>
-__global__ __launch_bounds__(kRouteThreads) void route_direct_kernel(
+template <typename XT, int EP, int NTH>
+__global__ __launch_bounds__(NTH) void route_direct_kernel(
     const XT *__restrict__ x, const float *__restrict__ wg,
     const float *__restrict__ bg, int T, int d, int E, int k,
     int32_t *__restrict__ topk_idx, float *__restrict__ topk_w,
@@ -348,9 +348,9 @@ __global__ __launch_bounds__(kRouteThreads) void route_direct_kernel(
   const int lane = threadIdx.x % kWave;
   const int wave = threadIdx.x / kWave;
   const int e = lane % EP;
-  const int t = (blockIdx.x * (kRouteThreads / kWave) + wave) * TPW + lane / EP;
+  const int t = (blockIdx.x * (NTH / kWave) + wave) * TPW + lane / EP;
   const bool valid = t < T && e < E;
-  for (int i = threadIdx.x; i < EP; i += kRouteThreads) cnt[i] = 0;
+  for (int i = threadIdx.x; i < EP; i += NTH) cnt[i] = 0;
 
   const uint32_t xrec = (uint32_t)T * (uint32_t)d * RowLoad<XT>::kBytes;
   const uint32_t wrec = (uint32_t)E * (uint32_t)d * 4u;
@@ -438,19 +438,30 @@ __global__ __launch_bounds__(kRouteThreads) void route_direct_kernel(
     atomicAdd(&cnt[my_e], 1);
   }
   __syncthreads();
-  for (int i = threadIdx.x; i < E; i += kRouteThreads)
+  for (int i = threadIdx.x; i < E; i += NTH)
     if (cnt[i]) atomicAdd(counts + i, cnt[i]);
 }
 
+// Workgroups of four wavefronts; one wavefront each when there are fewer
+// wavefronts than CUs (decode batches), so that the chains and their operand
+// streams spread over as many CUs as possible.
 template <typename XT, int EP>
 static hipError_t launch_route_direct(const void *x, const float *wg, const float *bg,
                                       int T, int d, int E, int k, int32_t *idx,
                                       float *w, int32_t *counts, float *logits,
                                       hipStream_t s) {
-  constexpr int TPB = (kRouteThreads / kWave) * (kWave / EP);   // tokens per workgroup
-  const int blocks = (T + TPB - 1) / TPB;
-  route_direct_kernel<XT, EP><<<blocks, kRouteThreads, 0, s>>>(
-      static_cast<const XT *>(x), wg, bg, T, d, E, k, idx, w, counts, logits);
+  const int64_t waves = ((int64_t)T * EP + kWave - 1) / kWave;
+  if (waves < 256) {
+    constexpr int TPB = kWave / EP;   // tokens per one-wave workgroup
+    const int blocks = (T + TPB - 1) / TPB;
+    route_direct_kernel<XT, EP, kWave><<<blocks, kWave, 0, s>>>(
+        static_cast<const XT *>(x), wg, bg, T, d, E, k, idx, w, counts, logits);
+  } else {
+    constexpr int TPB = (kRouteThreads / kWave) * (kWave / EP);
+    const int blocks = (T + TPB - 1) / TPB;
+    route_direct_kernel<XT, EP, kRouteThreads><<<blocks, kRouteThreads, 0, s>>>(
+        static_cast<const XT *>(x), wg, bg, T, d, E, k, idx, w, counts, logits);
+  }
   return hipGetLastError();
 }
 
@@ -495,6 +506,11 @@ static hipError_t launch_route_dt(const void *x, const float *wg, const float *b
   if (fits && E <= 8) return launch_route_direct<XT, 8>(x, wg, bg, T, d, E, k, idx, w, counts, logits, s);
   if (fits && E <= 16) return launch_route_direct<XT, 16>(x, wg, bg, T, d, E, k, idx, w, counts, logits, s);
   const bool small = T <= 1024;
+  // decode batches with up to 64 experts: one chain per lane as well
+  if (fits && small && E <= 32)
+    return launch_route_direct<XT, 32>(x, wg, bg, T, d, E, k, idx, w, counts, logits, s);
+  if (fits && small && E <= 64)
+    return launch_route_direct<XT, 64>(x, wg, bg, T, d, E, k, idx, w, counts, logits, s);
 #define MOE_ROUTE(TX, EPT, TPT, GM) \
   return launch_route_t<XT, TX, EPT, TPT, GM>(x, wg, bg, T, d, E, k, idx, w, counts, logits, s)
   if (E <= 8) MOE_ROUTE(8, 1, 1, 4);

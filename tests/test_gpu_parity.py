@@ -34,6 +34,14 @@ SMALL = {
     "gelu-f32-bias": dict(T=200, d=128, h=256, E=6, k=2, act=GELU, dtype=F32, expert_bias=True),
     "mid-groups-gelu-bf16": dict(T=700, d=128, h=192, E=4, k=2, act=GELU, dtype=BF16, expert_bias=True),
     "mid-groups-swiglu-shared-bf16": dict(T=520, d=192, h=320, E=3, k=2, act=SWIGLU, dtype=BF16, S=1),
+    # router kernel selection: one chain per lane for decode-size batches
+    # (32 and 64 expert lanes), four-wave workgroups for large batches, the
+    # staged kernel for more experts on large batches
+    "e48-decode-swiglu-bf16": dict(T=40, d=192, h=128, E=48, k=6, act=SWIGLU, dtype=BF16),
+    "e32-decode-swiglu-f32": dict(T=64, d=128, h=128, E=32, k=4, act=SWIGLU, dtype=F32),
+    "e24-bias-bf16": dict(T=900, d=128, h=128, E=24, k=3, act=SWIGLU, dtype=BF16, bias=True),
+    "e16-bigT-bf16": dict(T=4200, d=64, h=64, E=16, k=2, act=GELU, dtype=BF16),
+    "e20-bigT-bf16": dict(T=1500, d=64, h=64, E=20, k=2, act=SWIGLU, dtype=BF16),
 }
 
 
@@ -75,6 +83,26 @@ def test_group_size_classes_in_one_layer():
     assert (c <= 64).any() and ((c > 64) & (c <= 384)).any() and (c > 384).any(), c
     check_routing(L, res["idx"], res["w"], res["counts"])
     check_outputs(L, res["y"], range(1000))
+
+
+# Shapes that steer the large-group GEMM to each of its kernels and row
+# tiles: the DMA-fed kernel (K <= 8192) and the ping-pong kernel (longer K),
+# each with 256- and 192-row tiles (the 256-row tile wins when the 192-row
+# tiling needs an extra round over the CUs).
+LARGE_TILES = {
+    "dma-bm256-down": dict(T=3200, d=2048, h=128, E=2, k=2, act=SWIGLU, dtype=BF16),
+    "pp-bm192-down": dict(T=300, d=128, h=8256, E=4, k=2, act=SWIGLU, dtype=BF16),
+    "pp-bm256-down": dict(T=3200, d=2048, h=8256, E=2, k=2, act=SWIGLU, dtype=BF16),
+}
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("name", list(LARGE_TILES))
+def test_large_group_kernels(name):
+    L = random_layer(zlib.crc32(name.encode()) % 1000, wstd=0.05, **LARGE_TILES[name])
+    res, _, _ = run_forward(L)
+    check_routing(L, res["idx"], res["w"], res["counts"])
+    check_outputs(L, res["y"], sample_tokens(L.cfg.T, 40))
 
 
 def test_stage_calls_equal_forward_and_are_deterministic():
