@@ -792,10 +792,17 @@ static hipError_t launch_big(const GemmArgs &a, hipStream_t s) {
 // small groups (<= 64 rows: decode batches, cold experts) stream their
 // weights through 32-row tiles; larger groups use 256- or 192-row tiles.  The
 // large class is skipped when no group can exceed 64 rows (every group has
-// at most T rows).
+// at most T rows); the small class when groups are large on average.
 template <int MODE>
 static hipError_t launch_classes(GemmArgs a, hipStream_t s) {
   hipError_t err = hipSuccess;
+  // Groups average 512 rows or more: small groups are rare enough that the
+  // large-tile launch takes every group and the second launch is saved.
+  if ((int64_t)a.routed_rows >= 512ll * a.E) {
+    a.min_rows = 1;
+    a.max_rows = 1 << 30;
+    return launch_big<MODE>(a, s);
+  }
   if (a.T > 64) {
     a.min_rows = 65;
     a.max_rows = 1 << 30;

@@ -198,6 +198,138 @@ __global__ __launch_bounds__(kPermThreads) void perm_move_kernel(
   }
 }
 
+// Steps 1-4 in one workgroup for up to kFusedMax assignments (decode and
+// small prefill batches), where launch latency outweighs the work (measured:
+// 7 us for 256 assignments against about 22 us for the five launches, break
+// even near 6000).  Same arithmetic as the multi-workgroup kernels: the stable
+// order (flat index, ballot ranks within a wavefront, wavefront order within
+// a chunk, chunk order), the Importance sums and the statistics are
+// computed in the same order, so both paths give identical results.
+constexpr int kFusedThreads = 1024;
+constexpr int kFusedMax = 4096;
+
+__global__ __launch_bounds__(kFusedThreads) void perm_fused_kernel(
+    const int32_t *__restrict__ idx, const float *__restrict__ w, int n, int k,
+    int E, int32_t *__restrict__ offsets, int32_t *__restrict__ pos,
+    int32_t *__restrict__ perm_src, float *__restrict__ perm_w,
+    float *__restrict__ importance, double *__restrict__ stats) {
+  constexpr int NW = kFusedThreads / kWave;
+  __shared__ int h[kMaxExperts];
+  __shared__ int off[kMaxExperts + 1];
+  __shared__ int run[NW][kMaxExperts];
+  __shared__ int scan_tmp[NW];
+  const int tid = threadIdx.x;
+  const int lane = tid % kWave;
+  const int wv = tid / kWave;
+
+  // 1. histogram
+  for (int e = tid; e < kMaxExperts; e += kFusedThreads) h[e] = 0;
+  __syncthreads();
+  for (int f = tid; f < n; f += kFusedThreads) {
+    const int e = idx[f];
+    if (static_cast<unsigned>(e) < static_cast<unsigned>(E)) atomicAdd(&h[e], 1);
+  }
+  __syncthreads();
+  // 2. group offsets: exclusive scan over the experts
+  {
+    const int c = tid < E ? h[tid] : 0;
+    int total;
+    const int ex = block_exclusive_scan<kFusedThreads>(c, scan_tmp, &total);
+    if (tid < E) {
+      off[tid] = ex;
+      offsets[tid] = ex;
+      h[tid] = ex;          // running first row of each expert
+    }
+    if (tid == 0) {
+      off[E] = n;
+      offsets[E] = n;
+    }
+  }
+  __syncthreads();
+  // 3. stable scatter, one chunk of kFusedThreads assignments at a time
+  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  for (int c0 = 0; c0 < n; c0 += kFusedThreads) {
+    const int f = c0 + tid;
+    int e = f < n ? idx[f] : -1;
+    const bool valid = static_cast<unsigned>(e) < static_cast<unsigned>(E);
+    if (!valid) e = 0;
+    uint64_t peers = __ballot(valid);
+#pragma unroll
+    for (int b = 0; b < 8; ++b) {
+      const bool bit = (e >> b) & 1;
+      const uint64_t m = __ballot(valid && bit);
+      peers &= bit ? m : ~m;
+    }
+    const int rank = __popcll(peers & below);
+    for (int i = tid; i < NW * kMaxExperts; i += kFusedThreads) (&run[0][0])[i] = 0;
+    __syncthreads();
+    if (valid && rank == 0) run[wv][e] = __popcll(peers);
+    __syncthreads();
+    for (int x = tid; x < E; x += kFusedThreads) {
+      int r = h[x];
+      for (int v = 0; v < NW; ++v) {
+        const int cnt = run[v][x];
+        run[v][x] = r;
+        r += cnt;
+      }
+      h[x] = r;
+    }
+    __syncthreads();
+    if (valid) {
+      const int p = run[wv][e] + rank;
+      pos[f] = p;
+      perm_src[p] = f / k;
+      perm_w[p] = w[f];
+    }
+    __syncthreads();
+  }
+  // 4. Importance, one wavefront per expert (lane-strided sums, butterfly)
+  __shared__ float imp[kMaxExperts];
+  for (int x = wv; x < E; x += NW) {
+    float sum = 0.0f;
+    for (int r = off[x] + lane; r < off[x + 1]; r += kWave) sum += perm_w[r];
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) sum += __shfl_xor(sum, o);
+    if (lane == 0) {
+      importance[x] = sum;
+      imp[x] = sum;
+    }
+  }
+  __syncthreads();
+  if (!stats || wv != 0) return;
+  // statistics: the fp64 reductions of perm_stats_kernel
+  double si = 0.0, sc = 0.0;
+  for (int x = lane; x < E; x += kWave) {
+    si += imp[x];
+    sc += off[x + 1] - off[x];
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    si += __shfl_xor(si, o);
+    sc += __shfl_xor(sc, o);
+  }
+  const double mi = si / E, mc = sc / E;
+  double vi = 0.0, vc = 0.0, f2 = 0.0;
+  for (int x = lane; x < E; x += kWave) {
+    const double cnt = off[x + 1] - off[x];
+    const double im = imp[x];
+    vi += (im - mi) * (im - mi);
+    vc += (cnt - mc) * (cnt - mc);
+    if (sc != 0.0) f2 += (cnt / sc) * (cnt / sc);
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    vi += __shfl_xor(vi, o);
+    vc += __shfl_xor(vc, o);
+    f2 += __shfl_xor(f2, o);
+  }
+  if (lane == 0) {
+    stats[0] = mi == 0.0 ? 0.0 : (vi / E) / (mi * mi);
+    stats[1] = mc == 0.0 ? 0.0 : (vc / E) / (mc * mc);
+    stats[2] = sc == 0.0 ? 0.0 : E * f2;
+  }
+}
+
 __global__ void zero_f32_kernel(float *p, int n) {
   for (int i = threadIdx.x; i < n; i += blockDim.x) p[i] = 0.0f;
 }
@@ -221,6 +353,15 @@ hipError_t launch_permute(const int32_t *idx, const float *w, const void *x,
                           float *perm_w, hipStream_t s) {
   const int n = T * k;
   if (n == 0) return launch_zero_stats(importance, E, stats, s);
+  const int blocks = n < 8192 ? n : 8192;
+  if (n <= kFusedMax) {
+    perm_fused_kernel<<<1, kFusedThreads, 0, s>>>(idx, w, n, k, E, offsets, pos, perm_src,
+                                                  perm_w, importance, stats);
+    perm_move_kernel<<<blocks, kPermThreads, 0, s>>>(
+        static_cast<const uint4 *>(x), perm_src, n, T, row_bytes / 16,
+        static_cast<uint4 *>(x_perm));
+    return hipGetLastError();
+  }
   const int nseg = perm_num_segments(n);
   perm_hist_kernel<<<nseg, kPermThreads, 0, s>>>(idx, n, E, hist);
   perm_scan_kernel<<<1, kPermThreads, 0, s>>>(hist, nseg, E, n, offsets);
@@ -228,7 +369,6 @@ hipError_t launch_permute(const int32_t *idx, const float *w, const void *x,
                                                     perm_src, perm_w);
   perm_importance_kernel<<<(E + 3) / 4, kPermThreads, 0, s>>>(offsets, perm_w, E, importance);
   if (stats) perm_stats_kernel<<<1, kWave, 0, s>>>(offsets, importance, E, stats);
-  const int blocks = n < 8192 ? n : 8192;
   perm_move_kernel<<<blocks, kPermThreads, 0, s>>>(
       static_cast<const uint4 *>(x), perm_src, n, T, row_bytes / 16,
       static_cast<uint4 *>(x_perm));

@@ -42,6 +42,8 @@ SMALL = {
     "e24-bias-bf16": dict(T=900, d=128, h=128, E=24, k=3, act=SWIGLU, dtype=BF16, bias=True),
     "e16-bigT-bf16": dict(T=4200, d=64, h=64, E=16, k=2, act=GELU, dtype=BF16),
     "e20-bigT-bf16": dict(T=1500, d=64, h=64, E=20, k=2, act=SWIGLU, dtype=BF16),
+    # more than 16384 assignments: the multi-workgroup grouping kernels
+    "many-assignments-bf16": dict(T=3000, d=64, h=64, E=64, k=6, act=SWIGLU, dtype=BF16),
 }
 
 
@@ -103,6 +105,19 @@ def test_large_group_kernels(name):
     res, _, _ = run_forward(L)
     check_routing(L, res["idx"], res["w"], res["counts"])
     check_outputs(L, res["y"], sample_tokens(L.cfg.T, 40))
+
+
+def test_single_class_with_a_small_group():
+    """Groups averaging 512 rows or more all go to the large-tile kernel,
+    including a group of a few rows (skewed router bias)."""
+    L = random_layer(33, T=3000, d=64, h=128, E=4, k=2, act=SWIGLU, dtype=BF16,
+                     bias=True, wstd=0.1)
+    L.b_gate = np.float32([1.5, 1.0, 0.0, -1.2])
+    res, _, _ = run_forward(L)
+    c = res["counts"]
+    assert c.sum() >= 512 * 4 and (c <= 64).any(), c
+    check_routing(L, res["idx"], res["w"], res["counts"])
+    check_outputs(L, res["y"], range(3000))
 
 
 def test_stage_calls_equal_forward_and_are_deterministic():
