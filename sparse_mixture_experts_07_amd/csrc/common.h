@@ -42,6 +42,11 @@ __device__ __forceinline__ float silu_f32(float g) {
 
 __device__ __forceinline__ int ceil_div(int a, int b) { return (a + b - 1) / b; }
 
+// s_waitcnt immediates (gfx9 family encoding): vmcnt n (6 bits: [3:0] and
+// [15:14]), expcnt not waited for (7), lgkmcnt 0 or not waited for (15).
+constexpr int waitcnt_vm_lgkm0(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4); }
+constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
+
 // Inclusive prefix sum across the 64 lanes of a wavefront.
 __device__ __forceinline__ int wave_inclusive_scan(int v) {
   const int lane = threadIdx.x % kWave;

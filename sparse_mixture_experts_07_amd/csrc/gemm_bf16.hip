@@ -676,7 +676,7 @@ void gemm_dma_kernel(GemmArgs a) {
       // this wave's operand reads are done; then a plain barrier (a fence
       // would also wait for the DMAs still in flight).  The empty asm
       // statements keep the compiler from moving LDS accesses across it.
-      __builtin_amdgcn_s_waitcnt(0x0070 | (2 * BPW));   // vmcnt(2 BPW) lgkmcnt(0)
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(2 * BPW));
       asm volatile("" ::: "memory");
       __builtin_amdgcn_s_barrier();
       asm volatile("" ::: "memory");
@@ -686,7 +686,7 @@ void gemm_dma_kernel(GemmArgs a) {
     dma(1);
     dma(2);
     dma(3);
-    __builtin_amdgcn_s_waitcnt(0x0070 | (2 * BPW));   // stages 0 and 1
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(2 * BPW));   // stages 0 and 1
     __syncthreads();
     read_stage(0, fa0, fw0);
 
@@ -698,7 +698,7 @@ void gemm_dma_kernel(GemmArgs a) {
     }
     // the next tile's first DMAs go to buffers that the last (unused) DMAs
     // and reads above may still touch
-    __builtin_amdgcn_s_waitcnt(0x0F70);
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
     __syncthreads();
     TM::epilogue(a, t, acc, wm, wn);
   }

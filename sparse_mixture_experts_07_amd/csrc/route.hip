@@ -445,6 +445,195 @@ __global__ __launch_bounds__(NTH) void route_direct_kernel(
 // Workgroups of four wavefronts; one wavefront each when there are fewer
 // wavefronts than CUs (decode batches), so that the chains and their operand
 // streams spread over as many CUs as possible.
+// ---------------------------------------------------------------------------
+// The same chains (one (token, expert) chain per lane, EP-lane groups per
+// token), with the operands staged in LDS: each workgroup of NWV wavefronts
+// (TPB tokens x EP experts) brings chunks of CC columns of its x rows and of
+// W_g into four rotating LDS buffers with buffer loads that write LDS
+// directly, three chunks ahead of the chains, so load latency is hidden
+// without holding prefetched operands in registers, and every x or W_g
+// element crosses the memory pipeline once per workgroup instead of once
+// per lane that uses it.  A chain reads its 32-column slices from LDS; the
+// 16-byte slots of each row are XOR-swizzled so that the lanes of a
+// wavefront, reading the same column of up to 16 rows, hit distinct banks.
+template <typename XT, int EP, int NWV>
+struct LaneGeom {
+  static constexpr int NTH = NWV * kWave;
+  static constexpr int TPB = NWV * (kWave / EP);         // tokens per workgroup
+  static constexpr int BPC = TPB * (int)sizeof(XT) + EP * 4;   // bytes per column
+  static constexpr int CC0 = 24576 / BPC;
+  static constexpr int CC = CC0 >= 256 ? 256 : CC0 >= 128 ? 128 : CC0 >= 64 ? 64 : 32;
+  static constexpr int XS = CC * (int)sizeof(XT) / 16;   // 16-byte slots of an x row segment
+  static constexpr int WS = CC * 4 / 16;                 // ... of a W_g row segment
+  static constexpr int XM = XS < 16 ? XS : 16;           // swizzle ranges
+  static constexpr int WM = WS < 16 ? WS : 16;
+  static constexpr int XBLK = (TPB * XS + 63) / 64;      // 1 KB DMA blocks per chunk
+  static constexpr int WBLK = (EP * WS + 63) / 64;
+  static constexpr int NBLK = XBLK + WBLK;
+  static constexpr int BPW = (NBLK + NWV - 1) / NWV;     // per wavefront (last repeats)
+  static constexpr int CHUNK = NBLK * 1024;              // LDS bytes per buffer
+  static constexpr int NB = 4;
+  static_assert(2 * BPW < 64, "vmcnt range");
+  static __device__ __forceinline__ int xslot(int r, int j) { return r * XS + (j ^ (r % XM)); }
+  static __device__ __forceinline__ int wslot(int r, int j) { return r * WS + (j ^ (r % WM)); }
+};
+
+template <typename XT, int EP, int NWV>
+__global__ __launch_bounds__(NWV * kWave) void route_lane_kernel(
+    const XT *__restrict__ x, const float *__restrict__ wg,
+    const float *__restrict__ bg, int T, int d, int E, int k,
+    int32_t *__restrict__ topk_idx, float *__restrict__ topk_w,
+    int32_t *__restrict__ counts, float *__restrict__ logits) {
+  using G = LaneGeom<XT, EP, NWV>;
+  constexpr int TPW = kWave / EP;          // tokens per wavefront
+  constexpr int CC = G::CC;
+  __shared__ u32x4_t lds[G::NB][G::CHUNK / 16];
+  __shared__ int cnt[EP];
+  const int lane = threadIdx.x % kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int e = lane % EP;
+  const int tl = wave * TPW + lane / EP;   // token within the workgroup
+  const int tb = blockIdx.x * G::TPB;      // first token of the workgroup
+  const int t = tb + tl;
+  const bool valid = t < T && e < E;
+  for (int i = threadIdx.x; i < EP; i += G::NTH) cnt[i] = 0;
+
+  // buffer descriptors: x rows of this workgroup's tokens, all of W_g; reads
+  // past either end return zeros
+  const uint32_t row_x = (uint32_t)d * sizeof(XT);
+  const uint32_t row_w = (uint32_t)d * 4u;
+  const int64_t xrows = min(T - tb, G::TPB);
+  const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<XT *>(x) + (int64_t)tb * d, 0, (uint32_t)(xrows * row_x), kBufWord3);
+  const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<float *>(wg), 0, (uint32_t)E * row_w, kBufWord3);
+  // DMA block b of a chunk: x blocks first, then W_g blocks; lane l fills
+  // LDS slot 64 b + l, the swizzled slot of some (row, column) of the
+  // chunk, with that element's 16 bytes
+  auto dma = [&](int ch) {
+    u32x4_t *buf = lds[ch % G::NB];
+    const int c0 = ch * CC;
+#pragma unroll
+    for (int i = 0; i < G::BPW; ++i) {
+      const int b = min(wave * G::BPW + i, G::NBLK - 1);
+      if (b < G::XBLK) {
+        const int p = b * 64 + lane;
+        const int r = p / G::XS;
+        const int j = (p % G::XS) ^ (r % G::XM);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, buf + b * 64, 16,
+                                                 (uint32_t)r * row_x + (uint32_t)j * 16u,
+                                                 c0 * (int)sizeof(XT), 0, 0);
+      } else {
+        const int p = (b - G::XBLK) * 64 + lane;
+        const int r = p / G::WS;
+        const int j = (p % G::WS) ^ (r % G::WM);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, buf + b * 64, 16,
+                                                 (uint32_t)r * row_w + (uint32_t)j * 16u,
+                                                 c0 * 4, 0, 0);
+      }
+    }
+  };
+
+  float acc = 0.0f;
+  const int nch = (d + CC - 1) / CC;
+#pragma unroll
+  for (int c = 0; c < G::NB - 1; ++c)
+    if (c < nch) dma(c);
+  for (int ch = 0; ch < nch; ++ch) {
+    // chunk ch has landed (later chunks may be in flight), this wavefront's
+    // reads of chunk ch-1 are done; then the workgroup barrier makes chunk
+    // ch complete and frees the buffer of chunk ch-1 for chunk ch+3.  The
+    // empty asm statements keep the compiler from moving LDS accesses
+    // across the barrier (a fence would also wait for the DMAs in flight).
+    const int ahead = min(nch - 1 - ch, G::NB - 2);
+    if (ahead >= 2) __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(2 * G::BPW));
+    else if (ahead == 1) __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(G::BPW));
+    else __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    if (ch + G::NB - 1 < nch) dma(ch + G::NB - 1);
+    const u32x4_t *xb = lds[ch % G::NB];
+    const u32x4_t *wb = xb + G::XBLK * 64;
+    const int ncol = min(CC, d - ch * CC);
+    for (int c = 0; c < ncol; c += 32) {
+      float xv[32];
+      if constexpr (sizeof(XT) == 2) {
+        u32x4_t xs[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) xs[i] = xb[G::xslot(tl, c / 8 + i)];
+        RowLoad<uint16_t>::expand(xs, xv);
+      } else {
+        u32x4_t xs[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) xs[i] = xb[G::xslot(tl, c / 4 + i)];
+        RowLoad<float>::expand(xs, xv);
+      }
+      u32x4_t ws[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) ws[i] = wb[G::wslot(e, c / 4 + i)];
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) acc = __builtin_fmaf(xv[4 * i + q], __uint_as_float(ws[i][q]), acc);
+    }
+  }
+
+  float sc = acc;
+  if (bg && e < E) sc = acc + bg[e];
+  if (logits && valid) logits[(int64_t)t * E + e] = sc;
+
+  // ---- KeepTopK over the EP lanes of each token (lower index wins ties) ----
+  bool avail = e < E;
+  int my_e = 0;
+  float my_v = 0.0f, s0 = 0.0f;
+  for (int j = 0; j < k; ++j) {
+    float bv = sc;
+    int be = avail ? e : 0x7fffffff;
+#pragma unroll
+    for (int off = EP / 2; off >= 1; off >>= 1) {
+      const float ov = __shfl_xor(bv, off);
+      const int oe = __shfl_xor(be, off);
+      const bool take = oe != 0x7fffffff &&
+                        (be == 0x7fffffff || ov > bv || (ov == bv && oe < be));
+      if (take) {
+        bv = ov;
+        be = oe;
+      }
+    }
+    if (be == e) avail = false;
+    if (j == 0) s0 = bv;
+    if (e == j) {
+      my_e = be;
+      my_v = bv;
+    }
+  }
+  float z = e < k ? expf(my_v - s0) : 0.0f;
+  float sum = z;
+#pragma unroll
+  for (int off = EP / 2; off >= 1; off >>= 1) sum += __shfl_xor(sum, off);
+  __syncthreads();   // cnt[] zeroed
+  if (t < T && e < k) {
+    topk_idx[(int64_t)t * k + e] = my_e;
+    topk_w[(int64_t)t * k + e] = z / sum;
+    atomicAdd(&cnt[my_e], 1);
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < E; i += G::NTH)
+    if (cnt[i]) atomicAdd(counts + i, cnt[i]);
+}
+
+template <typename XT, int EP, int NWV>
+static hipError_t launch_route_lane(const void *x, const float *wg, const float *bg, int T,
+                                    int d, int E, int k, int32_t *idx, float *w,
+                                    int32_t *counts, float *logits, hipStream_t s) {
+  using G = LaneGeom<XT, EP, NWV>;
+  const int blocks = (T + G::TPB - 1) / G::TPB;
+  route_lane_kernel<XT, EP, NWV><<<blocks, G::NTH, 0, s>>>(
+      static_cast<const XT *>(x), wg, bg, T, d, E, k, idx, w, counts, logits);
+  return hipGetLastError();
+}
+
 template <typename XT, int EP>
 static hipError_t launch_route_direct(const void *x, const float *wg, const float *bg,
                                       int T, int d, int E, int k, int32_t *idx,
@@ -501,22 +690,25 @@ static hipError_t launch_route_dt(const void *x, const float *wg, const float *b
                                   int T, int d, int E, int k, int32_t *idx,
                                   float *w, int32_t *counts, float *logits,
                                   hipStream_t s) {
-  // few experts: direct streaming kernel (buffer offsets must fit 32 bits)
+  // Up to 64 experts, one chain per lane.  Batches that give at least 64
+  // workgroups: operands staged in LDS (route_lane_kernel); smaller batches
+  // (decode): operands streamed straight into registers by few-wavefront
+  // workgroups spread over the CUs (route_direct_kernel, whose 32-bit
+  // buffer offsets cover the whole of x).  Measured on MI355X.
   const bool fits = (int64_t)T * d * (int64_t)sizeof(XT) < (int64_t(1) << 31);
-  if (fits && E <= 8) return launch_route_direct<XT, 8>(x, wg, bg, T, d, E, k, idx, w, counts, logits, s);
-  if (fits && E <= 16) return launch_route_direct<XT, 16>(x, wg, bg, T, d, E, k, idx, w, counts, logits, s);
-  const bool small = T <= 1024;
-  // decode batches with up to 64 experts: one chain per lane as well
-  if (fits && small && E <= 32)
-    return launch_route_direct<XT, 32>(x, wg, bg, T, d, E, k, idx, w, counts, logits, s);
-  if (fits && small && E <= 64)
-    return launch_route_direct<XT, 64>(x, wg, bg, T, d, E, k, idx, w, counts, logits, s);
+#define MOE_LANE(EP)                                                                 \
+  do {                                                                               \
+    if (T >= 64 * LaneGeom<XT, EP, 4>::TPB || !fits)                                 \
+      return launch_route_lane<XT, EP, 4>(x, wg, bg, T, d, E, k, idx, w, counts, logits, s); \
+    return launch_route_direct<XT, EP>(x, wg, bg, T, d, E, k, idx, w, counts, logits, s);   \
+  } while (0)
+  if (E <= 8) MOE_LANE(8);
+  if (E <= 16) MOE_LANE(16);
+  if (E <= 32) MOE_LANE(32);
+  if (E <= 64) MOE_LANE(64);
+#undef MOE_LANE
 #define MOE_ROUTE(TX, EPT, TPT, GM) \
   return launch_route_t<XT, TX, EPT, TPT, GM>(x, wg, bg, T, d, E, k, idx, w, counts, logits, s)
-  if (E <= 8) MOE_ROUTE(8, 1, 1, 4);
-  if (E <= 16) MOE_ROUTE(16, 1, 2, 4);
-  if (E <= 32) { if (small) MOE_ROUTE(32, 1, 1, 8); MOE_ROUTE(32, 1, 4, 2); }
-  if (E <= 64) { if (small) MOE_ROUTE(32, 2, 1, 4); MOE_ROUTE(32, 2, 4, 2); }
   if (E <= 128) MOE_ROUTE(32, 4, 4, 1);
   MOE_ROUTE(32, 8, 4, 1);
 #undef MOE_ROUTE

@@ -42,6 +42,7 @@ SMALL = {
     "e24-bias-bf16": dict(T=900, d=128, h=128, E=24, k=3, act=SWIGLU, dtype=BF16, bias=True),
     "e16-bigT-bf16": dict(T=4200, d=64, h=64, E=16, k=2, act=GELU, dtype=BF16),
     "e20-bigT-bf16": dict(T=1500, d=64, h=64, E=20, k=2, act=SWIGLU, dtype=BF16),
+    "f32-lane-router": dict(T=2100, d=64, h=64, E=8, k=2, act=GELU, dtype=F32),
     # more than 16384 assignments: the multi-workgroup grouping kernels
     "many-assignments-bf16": dict(T=3000, d=64, h=64, E=64, k=6, act=SWIGLU, dtype=BF16),
 }
