@@ -35,9 +35,23 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=15.0,
                    help="target CPU time of the oracle baseline sample")
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--traffic", default=None,
-                   help="JSON file with measured FETCH/WRITE bytes of the dominant kernel")
+    p.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "traffic.txt"),
+                   help="measured HBM bytes of the dominant kernel per workload (JSON text)")
+    p.add_argument("--copy-calibration", action="store_true",
+                   help="first copy 1 GiB device to device three times, so that a PMC "
+                        "run sees a plain copy of known size beside the layer's kernels")
     return p.parse_args()
+
+
+def source_digest() -> str:
+    """sha256 over the sources of the grouped-GEMM kernels: measured traffic
+    is reported only while they are unchanged."""
+    import hashlib
+    h = hashlib.sha256()
+    for f in ("gemm_bf16.hip", "common.h"):
+        with open(os.path.join(ROOT, "sparse_mixture_experts_07_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
 
 
 def main():
@@ -53,6 +67,14 @@ def main():
     import synthetic
     from sparse_mixture_experts_07_amd import binding as B
     from sparse_mixture_experts_07_amd.device import DeviceLayer, Forward
+
+    if args.copy_calibration:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     cfg = synthetic.BY_NAME[args.workload]
     t_gen = time.time()
@@ -137,11 +159,17 @@ def main():
         roof = {"bound": "mfma", "achieved": up_flops / (up_avg / 1e3) / 1e12,
                 "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
-    roof["kernel"] = "gemm_bf16_kernel (expert up projection + activation)"
+    roof["kernel"] = "expert up projection + activation (moe_expert_up: gemm_dma_kernel / gemm_pp_kernel / gemm_bf16_kernel by group size and K)"
     roof["avg_ms"] = up_avg
+    # HBM bytes per launch of the dominant kernel from the FETCH_SIZE and
+    # WRITE_SIZE counters, scaled by the counters of a plain 1 GiB copy;
+    # null when not measured for these kernel sources
     roof["traffic"] = None
     if args.traffic and os.path.exists(args.traffic):
-        roof["traffic"] = json.load(open(args.traffic)).get(args.workload)
+        rec = json.load(open(args.traffic)).get(args.workload)
+        if rec and rec.get("gemm_source_sha256") == source_digest():
+            roof["traffic"] = rec["traffic_bytes"]
+            roof["traffic_over_algorithmic_bytes"] = rec["traffic_bytes"] / up_bytes
 
     cpu = None
     if not args.no_cpu_baseline:
