@@ -66,12 +66,17 @@ def lib():
         L.oracle_permute.argtypes = [P, P, P, P, P]
         L.oracle_expert.argtypes = [P, P, C.c_int, P, P]
         L.oracle_forward_tokens.argtypes = [P, P, P, P, C.c_int64, P, P, P]
+        L.oracle_forward_tokens_keep.argtypes = [P, P, P, P, C.c_int64, P, P, P, P]
+        L.oracle_capacity_keep.argtypes = [P, P, C.c_int32, P]
+        L.oracle_permute_keep.argtypes = [P, P, P, P, P, P]
         L.oracle_load_stats.argtypes = [P, P, C.c_int, P]
         L.oracle_param_counts.argtypes = [P, P, P]
         L.oracle_set_threads.argtypes = [C.c_int]
         for f in ("oracle_route", "oracle_counts", "oracle_permute",
                   "oracle_expert", "oracle_forward_tokens", "oracle_load_stats",
-                  "oracle_param_counts", "oracle_max_threads"):
+                  "oracle_param_counts", "oracle_max_threads",
+                  "oracle_forward_tokens_keep", "oracle_capacity_keep",
+                  "oracle_permute_keep"):
             getattr(L, f).restype = C.c_int
         _lib = L
     return _lib
@@ -150,6 +155,31 @@ def permute(c, idx: np.ndarray):
     return off, src, pos
 
 
+def capacity_keep(c, idx: np.ndarray, capacity: int) -> np.ndarray:
+    """uint8 [T*k]: 1 where an assignment is within its expert's first
+    `capacity` assignments in flat order (capacity 0: no limit)."""
+    idx = np.ascontiguousarray(idx, np.int32)
+    keep = np.empty(c.T * c.k, np.uint8)
+    cfg = _cfg(c)
+    _check(lib().oracle_capacity_keep(C.byref(cfg), _ptr(idx), int(capacity),
+                                      _ptr(keep)), "oracle_capacity_keep")
+    return keep
+
+
+def permute_keep(c, idx: np.ndarray, keep: np.ndarray):
+    """(offsets [E+1], perm_src [offsets[E]], pos [T*k] with -1 = dropped)
+    of the grouping of the kept assignments."""
+    idx = np.ascontiguousarray(idx, np.int32)
+    keep = np.ascontiguousarray(keep, np.uint8)
+    off = np.empty(c.E + 1, np.int32)
+    src = np.empty(c.T * c.k, np.int32)
+    pos = np.empty(c.T * c.k, np.int32)
+    cfg = _cfg(c)
+    _check(lib().oracle_permute_keep(C.byref(cfg), _ptr(idx), _ptr(keep), _ptr(off),
+                                     _ptr(src), _ptr(pos)), "oracle_permute_keep")
+    return off, src[: off[-1]], pos
+
+
 def expert(layer, e: int, xrow: np.ndarray) -> np.ndarray:
     """Expert e (e == E: the shared expert) on one row, float64 [d]."""
     c = layer.cfg
@@ -162,8 +192,9 @@ def expert(layer, e: int, xrow: np.ndarray) -> np.ndarray:
     return y
 
 
-def forward_tokens(layer, tokens: Sequence[int]):
-    """The layer on the listed tokens: (y float64 [n,d], idx [n,k], w [n,k])."""
+def forward_tokens(layer, tokens: Sequence[int], keep: Optional[np.ndarray] = None):
+    """The layer on the listed tokens: (y float64 [n,d], idx [n,k], w [n,k]).
+    keep: uint8 [T*k] from capacity_keep (dropped slots add nothing)."""
     c = layer.cfg
     tok = np.ascontiguousarray(np.asarray(tokens, np.int64))
     n = tok.size
@@ -172,10 +203,23 @@ def forward_tokens(layer, tokens: Sequence[int]):
     w = np.empty((n, c.k), np.float64)
     cfg = _cfg(c)
     W = _weights(layer)
-    rc = lib().oracle_forward_tokens(C.byref(cfg), C.byref(W), _ptr(layer.x),
-                                     _ptr(tok), n, _ptr(y), _ptr(idx), _ptr(w))
+    if keep is None:
+        rc = lib().oracle_forward_tokens(C.byref(cfg), C.byref(W), _ptr(layer.x),
+                                         _ptr(tok), n, _ptr(y), _ptr(idx), _ptr(w))
+    else:
+        keep = np.ascontiguousarray(keep, np.uint8)
+        assert keep.size == c.T * c.k
+        rc = lib().oracle_forward_tokens_keep(C.byref(cfg), C.byref(W), _ptr(layer.x),
+                                              _ptr(tok), n, _ptr(keep), _ptr(y),
+                                              _ptr(idx), _ptr(w))
     _check(rc, "oracle_forward_tokens")
     return y, idx, w
+
+
+def expert_capacity(T: int, k: int, E: int, factor: float) -> int:
+    """C = ceil(factor * T * k / E), at least 1 (factor > 0)."""
+    import math
+    return max(1, math.ceil(factor * T * k / E))
 
 
 def load_stats(cnt: np.ndarray, importance: Optional[np.ndarray] = None):

@@ -47,7 +47,10 @@
  *   - SwiGLU experts count P_e = 3*d*h weights, GELU experts 2*d*h; a
  *     shared always-on expert adds P_e to both totals;
  *   - within an expert's group, rows keep the order of the flat assignment
- *     index t*k + j.
+ *     index t*k + j;
+ *   - expert capacity: an expert accepts its first C assignments in that
+ *     flat order, the rest are dropped, the surviving weights are not
+ *     renormalised (Go chapter, "What was simplified").
  *
  * Build: gcc -O2 -fopenmp -ffp-contract=off -mfma (no other contraction).
  */
@@ -268,6 +271,51 @@ int oracle_permute(const oracle_cfg *c, const int32_t *idx, int32_t *offsets,
   return p == n ? 0 : -1;
 }
 
+/* Expert capacity (Go chapter, "What was simplified": real implementations
+ * cap the tokens an expert accepts and drop the overflow).  Reading: expert
+ * e accepts its first `capacity` assignments in flat order f = t*k + j
+ * (token order, and a token's higher-scored slot first); keep[f] = 1 for
+ * those, 0 for the dropped ones.  capacity = 0 means no limit. */
+int oracle_capacity_keep(const oracle_cfg *c, const int32_t *idx, int32_t capacity,
+                         unsigned char *keep) {
+  if (!cfg_ok(c) || !idx || !keep || capacity < 0) return -1;
+  int64_t *taken = (int64_t *)calloc((size_t)c->E, sizeof(int64_t));
+  for (int64_t f = 0; f < c->T * c->k; ++f) {
+    const int e = idx[f];
+    if (e < 0 || e >= c->E) {
+      free(taken);
+      return -1;
+    }
+    keep[f] = (capacity == 0 || taken[e] < capacity) ? 1 : 0;
+    taken[e] += 1;
+  }
+  free(taken);
+  return 0;
+}
+
+/* Grouping with a capacity: only kept assignments get rows; offsets[E+1]
+ * over the kept rows, perm_src[p] for p < offsets[E], pos[f] = -1 for a
+ * dropped assignment. */
+int oracle_permute_keep(const oracle_cfg *c, const int32_t *idx,
+                        const unsigned char *keep, int32_t *offsets,
+                        int32_t *perm_src, int32_t *pos) {
+  if (!cfg_ok(c) || !idx || !keep || !offsets || !perm_src || !pos) return -1;
+  const int64_t n = c->T * c->k;
+  int64_t p = 0;
+  for (int64_t f = 0; f < n; ++f) pos[f] = -1;
+  for (int e = 0; e < c->E; ++e) {
+    offsets[e] = (int32_t)p;
+    for (int64_t f = 0; f < n; ++f) {
+      if (idx[f] != e || !keep[f]) continue;
+      perm_src[p] = (int32_t)(f / c->k);
+      pos[f] = (int32_t)p;
+      ++p;
+    }
+  }
+  offsets[c->E] = (int32_t)p;
+  return 0;
+}
+
 /* One expert (e < E routed, e == E shared) applied to one row, in double. */
 int oracle_expert(const oracle_cfg *c, const oracle_weights *W, int e,
                   const double *xr, double *yr) {
@@ -280,10 +328,13 @@ int oracle_expert(const oracle_cfg *c, const oracle_weights *W, int e,
 }
 
 /* The whole layer on the listed tokens: y[r] = sum_j w_j * E_{idx_j}(x_t)
- * (+ the shared expert with weight 1), accumulated in slot order. */
-int oracle_forward_tokens(const oracle_cfg *c, const oracle_weights *W,
-                          const void *x, const int64_t *tokens, int64_t nt,
-                          double *y, int32_t *idx, double *w) {
+ * (+ the shared expert with weight 1), accumulated in slot order.  keep
+ * (T*k flags from oracle_capacity_keep, or NULL = keep all): a dropped slot
+ * adds nothing and the other weights are not renormalised. */
+int oracle_forward_tokens_keep(const oracle_cfg *c, const oracle_weights *W,
+                               const void *x, const int64_t *tokens, int64_t nt,
+                               const unsigned char *keep, double *y, int32_t *idx,
+                               double *w) {
   if (!cfg_ok(c) || !W || !W->w_gate || !x || !tokens || !y || !idx || !w ||
       nt < 0)
     return -1;
@@ -313,6 +364,7 @@ int oracle_forward_tokens(const oracle_cfg *c, const oracle_weights *W,
       double *yo = y + r * d;
       for (int64_t i = 0; i < d; ++i) yo[i] = 0.0;
       for (int j = 0; j < c->k; ++j) {
+        if (keep && !keep[t * c->k + j]) continue;
         expert_ffn(c, W, ix[j], xr, hid, ye);
         for (int64_t i = 0; i < d; ++i) yo[i] += wr[j] * ye[i];
       }
@@ -373,4 +425,11 @@ int oracle_param_counts(const oracle_cfg *c, int64_t *total, int64_t *active) {
   *total = router + (int64_t)c->E * pe + (int64_t)c->S * pe;
   *active = router + (int64_t)c->k * pe + (int64_t)c->S * pe;
   return 0;
+}
+
+/* Without a capacity: every slot kept. */
+int oracle_forward_tokens(const oracle_cfg *c, const oracle_weights *W,
+                          const void *x, const int64_t *tokens, int64_t nt,
+                          double *y, int32_t *idx, double *w) {
+  return oracle_forward_tokens_keep(c, W, x, tokens, nt, NULL, y, idx, w);
 }

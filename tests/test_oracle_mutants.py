@@ -32,13 +32,21 @@ MUTANTS = {
     "combine_unweighted": ("yo[i] += wr[j] * ye[i];", "yo[i] += ye[i];"),
     "shared_dropped": ("for (int64_t i = 0; i < d; ++i) yo[i] += ye[i];\n      }",
                        "}"),
-    "perm_src_modulo": ("perm_src[p] = (int32_t)(f / c->k);",
-                        "perm_src[p] = (int32_t)(f % c->k);"),
+    "perm_src_modulo": ("if (idx[f] != e) continue;\n      perm_src[p] = (int32_t)(f / c->k);",
+                        "if (idx[f] != e) continue;\n      perm_src[p] = (int32_t)(f % c->k);"),
+    "kept_perm_src_modulo": (
+        "if (idx[f] != e || !keep[f]) continue;\n      perm_src[p] = (int32_t)(f / c->k);",
+        "if (idx[f] != e || !keep[f]) continue;\n      perm_src[p] = (int32_t)(f % c->k);"),
     "count_from_one": ("counts[e] = 0;", "counts[e] = (e == 0);"),
     "sample_variance": ("var /= n;", "var /= (n - 1);"),
     "lb_missing_E": ("lb *= E;", ""),
     "swiglu_params_2dh": ("(c->act == ORACLE_GELU ? 2 : 3)", "2"),
     "bf16_low_half": ("(uint32_t)bits << 16", "(uint32_t)bits << 15"),
+    "capacity_off_by_one": ("keep[f] = (capacity == 0 || taken[e] < capacity) ? 1 : 0;",
+                            "keep[f] = (capacity == 0 || taken[e] <= capacity) ? 1 : 0;"),
+    "capacity_ignored_in_forward": ("if (keep && !keep[t * c->k + j]) continue;", ""),
+    "grouping_ignores_drops": ("if (idx[f] != e || !keep[f]) continue;",
+                               "if (idx[f] != e) continue;"),
 }
 
 

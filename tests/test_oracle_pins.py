@@ -14,6 +14,7 @@ import pytest
 import scipy.special
 import torch
 
+import synthetic
 from helpers import BF16, F32, GELU, SWIGLU, layer, random_layer
 
 GOLD = json.load(open(os.path.join(os.path.dirname(__file__), "golden",
@@ -367,3 +368,105 @@ def test_invalid_configs_rejected(oracle_lib):
     L.cfg = L.cfg.with_(k=0)
     with pytest.raises(ValueError):
         oracle_lib.route(L)
+
+
+# ---- expert capacity (Go chapter, "What was simplified": an expert accepts
+# at most C tokens, the overflow is dropped) ----
+
+def _routing(seed, T, E, k):
+    rng = np.random.default_rng(seed)
+    # k distinct experts per token, skewed towards low indices
+    p = np.exp(-0.3 * np.arange(E))
+    p /= p.sum()
+    return np.stack([rng.choice(E, size=k, replace=False, p=p) for _ in range(T)]).astype(np.int32)
+
+
+@pytest.mark.parametrize("C", [1, 3, 7, 40])
+def test_capacity_keeps_first_C_assignments_in_flat_order(oracle_lib, C):
+    """keep = the first C flat indices t*k+j of each expert (numpy nonzero
+    order), and an expert keeps min(n_e, C) assignments."""
+    T, E, k = 60, 6, 2
+    idx = _routing(C, T, E, k)
+    c = synthetic.TINY.with_(T=T, E=E, k=k)
+    keep = oracle_lib.capacity_keep(c, idx, C)
+    ref = np.zeros(T * k, np.uint8)
+    flat = idx.ravel()
+    for e in range(E):
+        ref[np.flatnonzero(flat == e)[:C]] = 1
+    np.testing.assert_array_equal(keep, ref)
+    n = np.bincount(flat, minlength=E)
+    kept = np.bincount(flat[keep == 1], minlength=E)
+    np.testing.assert_array_equal(kept, np.minimum(n, C))
+
+
+def test_capacity_zero_or_large_keeps_everything(oracle_lib):
+    L = random_layer(3, T=9, d=8, h=12, E=4, k=2, act=SWIGLU, S=1, bias=True)
+    c = L.cfg
+    idx, _, _ = oracle_lib.route(L)
+    for C in (0, c.T * c.k):
+        assert oracle_lib.capacity_keep(c, idx, C).all()
+    y0, _, _ = oracle_lib.forward_tokens(L, range(c.T))
+    y1, _, _ = oracle_lib.forward_tokens(L, range(c.T), keep=np.ones(c.T * c.k, np.uint8))
+    np.testing.assert_array_equal(y0, y1)
+
+
+def test_capacity_grouping_of_kept_rows(oracle_lib):
+    """Kept rows grouped by expert in flat order (numpy lexsort), offsets =
+    exclusive scan of min(n_e, C), pos = -1 exactly for dropped slots."""
+    T, E, k, C = 50, 5, 3, 9
+    idx = _routing(7, T, E, k)
+    c = synthetic.TINY.with_(T=T, E=E, k=k)
+    keep = oracle_lib.capacity_keep(c, idx, C)
+    off, src, pos = oracle_lib.permute_keep(c, idx, keep)
+    flat = idx.ravel()
+    n = np.minimum(np.bincount(flat, minlength=E), C)
+    np.testing.assert_array_equal(off, np.concatenate([[0], np.cumsum(n)]))
+    kept_f = np.flatnonzero(keep)
+    order = kept_f[np.lexsort((kept_f, flat[kept_f]))]
+    np.testing.assert_array_equal(src, order // k)
+    ref_pos = np.full(T * k, -1, np.int32)
+    ref_pos[order] = np.arange(order.size)
+    np.testing.assert_array_equal(pos, ref_pos)
+
+
+@pytest.mark.parametrize("S", [0, 1])
+def test_dropped_slots_are_zeroed_gates_without_renormalisation(oracle_lib, S):
+    """With a capacity the layer equals the dense gated sum in which the
+    dropped experts' gates are set to 0 and the others keep their softmax
+    values (scipy softmax over the kept k)."""
+    L = random_layer(12, T=24, d=10, h=14, E=5, k=2, act=SWIGLU, S=S, bias=True)
+    c = L.cfg
+    idx, _, sc = oracle_lib.route(L, want_scores=True)
+    keep = oracle_lib.capacity_keep(c, idx, 4)
+    assert 0 < keep.sum() < c.T * c.k
+    y, _, _ = oracle_lib.forward_tokens(L, range(c.T), keep=keep)
+    for t in range(c.T):
+        g = np.full(c.E, -np.inf)
+        top = np.argsort(-sc[t].astype(np.float64), kind="stable")[:c.k]
+        g[top] = sc[t, top]
+        G = scipy.special.softmax(g)
+        for j in range(c.k):
+            if not keep[t * c.k + j]:
+                G[top[j]] = 0.0
+        xr = L.x[t].astype(np.float64)
+        dense = sum(G[i] * oracle_lib.expert(L, i, xr) for i in range(c.E))
+        if S:
+            dense = dense + oracle_lib.expert(L, c.E, xr)
+        np.testing.assert_allclose(y[t], dense, rtol=1e-12, atol=1e-14)
+
+
+def test_token_with_every_slot_dropped(oracle_lib):
+    """A token whose experts are all full adds no routed term: y = 0 without
+    a shared expert (exactly), y = the shared expert with one."""
+    for S in (0, 1):
+        L = random_layer(5, T=6, d=8, h=8, E=2, k=2, act=SWIGLU, S=S)
+        c = L.cfg
+        idx, _, _ = oracle_lib.route(L)
+        keep = oracle_lib.capacity_keep(c, idx, 1)   # E = k = 2: token 0 fills both
+        assert keep[:2].all() and not keep[2:].any()
+        y, _, _ = oracle_lib.forward_tokens(L, [4], keep=keep)
+        if S:
+            ref = oracle_lib.expert(L, c.E, L.x[4].astype(np.float64))
+            np.testing.assert_array_equal(y[0], ref)
+        else:
+            np.testing.assert_array_equal(y[0], np.zeros(c.d))
