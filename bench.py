@@ -35,6 +35,8 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=15.0,
                    help="target CPU time of the oracle baseline sample")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--capacity-factor", type=float, default=0.0,
+                   help="per-expert capacity ceil(f*T*k/E) with drops (0: none)")
     p.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "traffic.txt"),
                    help="measured HBM bytes of the dominant kernel per workload (JSON text)")
     p.add_argument("--copy-calibration", action="store_true",
@@ -79,7 +81,10 @@ def main():
     cfg = synthetic.BY_NAME[args.workload]
     t_gen = time.time()
     L = synthetic.make_inputs(cfg)
-    dl = DeviceLayer.upload(L)
+    cap = 0
+    if args.capacity_factor > 0:
+        cap = B.moe_expert_capacity(cfg.T, cfg.k, cfg.E, args.capacity_factor)
+    dl = DeviceLayer.upload(L, capacity=cap)
     gen_s = time.time() - t_gen
     c, W = dl.cfg, dl.weights()
     T, k, E, d, h = cfg.T, cfg.k, cfg.E, cfg.d, cfg.h
@@ -140,15 +145,17 @@ def main():
     up_avg = float(np.mean(up_ms))
 
     cnt = counts.cpu().numpy()
-    touched = int((cnt > 0).sum())
+    kept_cnt = np.diff(offsets.cpu().numpy())
+    kept = int(kept_cnt.sum())
+    touched = int((kept_cnt > 0).sum())
     n_up = cfg.n_up
-    rows = T * k + cfg.S * T
+    rows = kept + cfg.S * T
     up_flops = 2.0 * rows * d * n_up
-    layer_flops = float(cfg.expert_flops())
+    layer_flops = float(cfg.expert_flops()) * rows / (T * k + cfg.S * T)
     es = 2 if cfg.dtype == synthetic.BF16 else 4
     up_w_bytes = (touched + cfg.S) * n_up * d * es
     down_w_bytes = (touched + cfg.S) * d * h * es
-    up_bytes = up_w_bytes + (T * k + cfg.S * T) * (d + h) * es   # weights + A read + H write
+    up_bytes = up_w_bytes + rows * (d + h) * es   # weights + A read + H write
     decode = (T * k) / E < 32
 
     tokens_per_s = T / (ms_step / 1e3)
@@ -181,8 +188,12 @@ def main():
         per_tok = (time.perf_counter() - t1) / len(probe)
         n = int(min(T, max(len(probe), args.cpu_seconds / max(per_tok, 1e-9))))
         sample = np.linspace(0, T - 1, n).astype(np.int64)
+        keep = None
+        if cap:
+            ridx, _, _ = oracle.route(L)
+            keep = oracle.capacity_keep(cfg, ridx, cap)
         t1 = time.perf_counter()
-        oracle.forward_tokens(L, sample)
+        oracle.forward_tokens(L, sample, keep=keep)
         el = time.perf_counter() - t1
         cpu = {"value": n / el, "unit": "tokens/s", "cores": nthr, "kind": "oracle",
                "sample": f"{n} of {T} tokens (evenly spaced), full routing + "
@@ -204,13 +215,16 @@ def main():
         "config": {"workload": cfg.name, "T": T, "d_model": d, "d_hidden": h,
                    "experts": E, "top_k": k, "shared": cfg.S,
                    "act": "swiglu" if cfg.act == synthetic.SWIGLU else "gelu",
-                   "router_bias": cfg.router_bias},
+                   "router_bias": cfg.router_bias,
+                   **({"capacity_factor": args.capacity_factor, "capacity": cap}
+                      if cap else {})},
         "roofline": roof,
         "cpu_baseline": cpu,
         "layer_tflops": layer_flops / (ms_step / 1e3) / 1e12,
         "layer_frac_mfma_peak": layer_flops / (ms_step / 1e3) / 1e12 / PEAK_BF16_TFLOPS,
         "expert_weight_gbs": (up_w_bytes + down_w_bytes) / (ms_step / 1e3) / 1e9,
         "experts_touched": touched,
+        "dropped_fraction": 1.0 - kept / (T * k) if T else 0.0,
         "wall_s_timed": wall,
         "input_gen_upload_s": gen_s,
         "stage_sequence_equals_moe_forward": bool(same),

@@ -42,7 +42,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 1
+#define MOE_ABI_VERSION 2
 
 typedef enum {
   MOE_OK = 0,
@@ -70,6 +70,14 @@ typedef struct {
   int32_t num_shared;  /* S, 0 or 1: always-on expert with weight 1 */
   int32_t act;         /* moe_act_t */
   int32_t dtype;       /* moe_dtype_t */
+  int32_t capacity;    /* expert capacity C: 0 = no limit; C >= 1: each expert
+                          accepts its first C assignments in flat order
+                          t*k + j (token order, then slot order) and the rest
+                          are dropped: they add nothing to y and the other
+                          weights are not renormalised (the Go chapter's
+                          "What was simplified": real implementations cap
+                          what an expert accepts and drop the overflow).
+                          See moe_expert_capacity for C from a factor. */
 } moe_config_t;
 
 /* Expert weights, all packed over experts into single tensors ("Weight
@@ -120,16 +128,21 @@ moe_status_t moe_route(const moe_config_t *cfg, const void *x,
  * sort and group tokens by expert id before the grouped GEMM).
  *   topk_idx, topk_w [T, k]   (device, in) as written by moe_route
  *   x          [T, d] dtype   (device, in)
- *   offsets    [E + 1] int32  (out) group starts; offsets[E] = T*k
- *   perm_src   [T*k] int32    (out) source token of grouped row p
- *   pos        [T*k] int32    (out) grouped row of assignment (t, j)
- *   importance [E] fp32       (out) Importance(X)_e = sum of the kept
+ *   offsets    [E + 1] int32  (out) group starts of the kept assignments;
+ *              offsets[E] = T*k without a capacity, else sum_e min(n_e, C)
+ *   perm_src   [T*k] int32    (out) source token of grouped row p, for
+ *              p < offsets[E]
+ *   pos        [T*k] int32    (out) grouped row of assignment (t, j), or -1
+ *              if the expert capacity dropped it
+ *   importance [E] fp32       (out) Importance(X)_e = sum of the router
  *              weights routed to e (Qiita summary, "Load-balancing losses"),
- *              summed in group order
+ *              summed in group order; dropped assignments included (they
+ *              are the router's output)
  *   stats      [3] double or NULL (out) CV^2(Importance), CV^2(Load) with
  *              Load = counts, and the load-balance loss E*sum_e f_e^2 of the
  *              Go chapter's section 3 (population variance; 0 if empty)
- *   x_perm     [T*k, d] dtype (out) x_perm[p] = x[perm_src[p]]
+ *   x_perm     [T*k, d] dtype (out) x_perm[p] = x[perm_src[p]] for
+ *              p < offsets[E]
  *   ws         workspace >= moe_workspace_bytes() */
 moe_status_t moe_permute(const moe_config_t *cfg, const int32_t *topk_idx,
                          const float *topk_w, const void *x, int32_t *offsets,
@@ -163,7 +176,8 @@ moe_status_t moe_expert_ffn(const moe_config_t *cfg, const moe_weights_t *w,
 
 /* Collect: y[t] = sum_{j<k} topk_w[t,j] * y_perm[pos[t*k+j]] (+ the shared
  * row y_perm[T*k + t] with weight 1), accumulated in fp32 in slot order and
- * rounded once to dtype (Go chapter section 2, Forward: out += w * y).
+ * rounded once to dtype (Go chapter section 2, Forward: out += w * y);
+ * slots with pos = -1 (dropped by the capacity) are skipped.
  *   y_perm [R, d], pos [T*k], topk_w [T, k] (in); y [T, d] dtype (out) */
 moe_status_t moe_combine(const moe_config_t *cfg, const void *y_perm,
                          const int32_t *pos, const float *topk_w, void *y,
@@ -185,6 +199,11 @@ moe_status_t moe_forward(const moe_config_t *cfg, const moe_weights_t *w,
  * expert adds P_e to both; biases are not counted. */
 moe_status_t moe_param_counts(const moe_config_t *cfg, int64_t *total,
                               int64_t *active);
+
+/* Expert capacity from a capacity factor: C = ceil(factor * T * k / E), at
+ * least 1 (factor > 0; MOE_ERR_UNSUPPORTED if C would not fit int32). */
+moe_status_t moe_expert_capacity(int64_t num_tokens, int32_t top_k, int32_t num_experts,
+                                 double factor, int32_t *capacity);
 
 /* Side statistics from host arrays: CV^2(importance), CV^2(counts) and the
  * load-balance loss E * sum_e (counts_e / sum counts)^2 (0 when the sum is

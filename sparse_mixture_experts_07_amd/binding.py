@@ -30,7 +30,7 @@ EXPORTS = (
     "moe_abi_version", "moe_status_string", "moe_workspace_bytes",
     "moe_grouped_rows", "moe_route", "moe_permute", "moe_expert_up",
     "moe_expert_down", "moe_expert_ffn", "moe_combine", "moe_forward",
-    "moe_param_counts", "moe_load_stats",
+    "moe_param_counts", "moe_load_stats", "moe_expert_capacity",
 )
 
 
@@ -44,7 +44,8 @@ class MoeConfig(C.Structure):
     _fields_ = [("num_tokens", C.c_int64), ("d_model", C.c_int32),
                 ("d_hidden", C.c_int32), ("num_experts", C.c_int32),
                 ("top_k", C.c_int32), ("num_shared", C.c_int32),
-                ("act", C.c_int32), ("dtype", C.c_int32)]
+                ("act", C.c_int32), ("dtype", C.c_int32),
+                ("capacity", C.c_int32)]
 
 
 class MoeWeights(C.Structure):
@@ -82,6 +83,7 @@ def lib():
             "moe_forward": [P, P, P, P, P, P, P, P, P, P, C.c_size_t, P],
             "moe_param_counts": [P, P, P],
             "moe_load_stats": [P, P, C.c_int32, P, P, P],
+            "moe_expert_capacity": [C.c_int64, C.c_int32, C.c_int32, C.c_double, P],
         }
         for name, args in sig.items():
             fn = getattr(L, name)
@@ -137,14 +139,14 @@ def _check(fn: str, st: int) -> None:
 
 
 def config(T: int, d: int, h: int, E: int, k: int, act: int, dtype: int,
-           S: int = 0) -> MoeConfig:
+           S: int = 0, capacity: int = 0) -> MoeConfig:
     return MoeConfig(int(T), int(d), int(h), int(E), int(k), int(S), int(act),
-                     int(dtype))
+                     int(dtype), int(capacity))
 
 
-def config_of(c) -> MoeConfig:
+def config_of(c, capacity: int = 0) -> MoeConfig:
     """From any object with T, d, h, E, k, S, act, dtype attributes."""
-    return config(c.T, c.d, c.h, c.E, c.k, c.act, c.dtype, c.S)
+    return config(c.T, c.d, c.h, c.E, c.k, c.act, c.dtype, c.S, capacity)
 
 
 def weights(w_gate, w_up, w_down, b_gate=None, b_up=None, b_down=None,
@@ -227,6 +229,13 @@ def moe_param_counts(cfg: MoeConfig):
     _check("moe_param_counts",
            lib().moe_param_counts(C.byref(cfg), C.byref(tot), C.byref(act)))
     return tot.value, act.value
+
+
+def moe_expert_capacity(T: int, k: int, E: int, factor: float) -> int:
+    cap = C.c_int32()
+    _check("moe_expert_capacity",
+           lib().moe_expert_capacity(int(T), int(k), int(E), float(factor), C.byref(cap)))
+    return cap.value
 
 
 def moe_load_stats(counts, importance=None):

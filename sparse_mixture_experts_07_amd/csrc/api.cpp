@@ -15,9 +15,9 @@ hipError_t launch_route(bool bf16, const void *x, const float *wg, const float *
                         int32_t *counts, float *logits, hipStream_t s);
 int perm_num_segments(int64_t n);
 hipError_t launch_permute(const int32_t *idx, const float *w, const void *x, int T,
-                          int k, int E, int row_bytes, int32_t *offsets,
+                          int k, int E, int capacity, int row_bytes, int32_t *offsets,
                           int32_t *perm_src, int32_t *pos, float *importance,
-                          double *stats, void *x_perm, int32_t *hist,
+                          double *stats, void *x_perm, int32_t *hist, int32_t *full_off,
                           float *perm_w, hipStream_t s);
 hipError_t launch_expert_up_bf16(bool swiglu, const int32_t *offsets, int E, int S,
                                  int T, int k, int d, int h, const void *x_perm,
@@ -57,7 +57,7 @@ moe_status_t check_cfg(const moe_config_t *c) {
   if (!c) return MOE_ERR_INVALID_ARGUMENT;
   if (c->num_tokens < 0 || c->d_model <= 0 || c->d_hidden <= 0 ||
       c->num_experts < 1 || c->top_k < 1 || c->top_k > c->num_experts ||
-      c->num_shared < 0)
+      c->num_shared < 0 || c->capacity < 0)
     return MOE_ERR_INVALID_ARGUMENT;
   if ((c->act != MOE_ACT_GELU && c->act != MOE_ACT_SWIGLU) ||
       (c->dtype != MOE_DTYPE_F32 && c->dtype != MOE_DTYPE_BF16))
@@ -95,7 +95,7 @@ size_t elem_bytes(const moe_config_t *c) { return c->dtype == MOE_DTYPE_BF16 ? 2
 
 // Workspace regions, each 256-byte aligned, in this order.
 struct Layout {
-  size_t hist, perm_w, permute_end;   // moe_permute scratch
+  size_t hist, full_off, perm_w, permute_end;   // moe_permute scratch
   size_t offsets, perm_src, pos, x_perm, hidden, y_perm, total;  // moe_forward
 };
 
@@ -107,6 +107,7 @@ Layout layout(const moe_config_t *c) {
   Layout L{};
   size_t o = 0;
   L.hist = o;      o += align_up(sizeof(int32_t) * (size_t)moe::perm_num_segments(n) * E);
+  L.full_off = o;  o += align_up(sizeof(int32_t) * (size_t)(E + 1));
   L.perm_w = o;    o += align_up(sizeof(float) * (size_t)n);
   L.permute_end = o;
   L.offsets = o;   o += align_up(sizeof(int32_t) * (size_t)(E + 1));
@@ -205,10 +206,10 @@ moe_status_t moe_permute(const moe_config_t *cfg, const int32_t *topk_idx,
     if (e != hipSuccess) return MOE_ERR_HIP;
   }
   return hip_status(moe::launch_permute(
-      topk_idx, topk_w, x, T, cfg->top_k, cfg->num_experts,
+      topk_idx, topk_w, x, T, cfg->top_k, cfg->num_experts, cfg->capacity,
       (int)(cfg->d_model * elem_bytes(cfg)), offsets, perm_src, pos, importance, stats,
-      x_perm, T ? at<int32_t>(ws, L.hist) : nullptr, T ? at<float>(ws, L.perm_w) : nullptr,
-      stream));
+      x_perm, T ? at<int32_t>(ws, L.hist) : nullptr, T ? at<int32_t>(ws, L.full_off) : nullptr,
+      T ? at<float>(ws, L.perm_w) : nullptr, stream));
 }
 
 moe_status_t moe_expert_up(const moe_config_t *cfg, const moe_weights_t *w,
@@ -330,6 +331,16 @@ moe_status_t moe_param_counts(const moe_config_t *cfg, int64_t *total, int64_t *
   const int64_t router = (int64_t)cfg->d_model * cfg->num_experts;
   *total = router + (cfg->num_experts + cfg->num_shared) * pe;
   *active = router + (cfg->top_k + cfg->num_shared) * pe;
+  return MOE_OK;
+}
+
+moe_status_t moe_expert_capacity(int64_t num_tokens, int32_t top_k, int32_t num_experts,
+                                 double factor, int32_t *capacity) {
+  if (!capacity || num_tokens < 0 || top_k < 1 || num_experts < 1 || !(factor > 0.0))
+    return MOE_ERR_INVALID_ARGUMENT;
+  const double c = std::ceil(factor * (double)num_tokens * top_k / num_experts);
+  if (!(c < 2147483647.0)) return MOE_ERR_UNSUPPORTED;
+  *capacity = c < 1.0 ? 1 : (int32_t)c;
   return MOE_OK;
 }
 

@@ -5,7 +5,8 @@
 // slot order.  A gather (every token reads its k grouped rows) instead of a
 // scatter-add keeps the sum deterministic without floating-point atomics.
 // The shared always-on expert's row sits at grouped row T*k + t and enters
-// with weight 1.  fp32 accumulation, one rounding to the output dtype.
+// with weight 1; a slot dropped by the expert capacity (pos = -1) adds
+// nothing.  fp32 accumulation, one rounding to the output dtype.
 #include "common.h"
 
 #pragma clang fp contract(off)
@@ -27,7 +28,8 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(
   for (int t = blockIdx.x; t < T; t += gridDim.x) {
     __syncthreads();
     for (int j = threadIdx.x; j < k; j += kCombineThreads) {
-      ps[j] = min(max(pos[(int64_t)t * k + j], 0), rows - 1);
+      const int pj = pos[(int64_t)t * k + j];
+      ps[j] = pj < 0 ? -1 : min(pj, rows - 1);   // -1: dropped (expert capacity)
       wsh[j] = w[(int64_t)t * k + j];
     }
     __syncthreads();
@@ -40,6 +42,7 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(
         float wj;
         if (j < k) {
           row = ps[j];
+          if (row < 0) continue;
           wj = wsh[j];
         } else {
           if (!shared) break;

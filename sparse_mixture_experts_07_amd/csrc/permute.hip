@@ -20,6 +20,13 @@
 //                the Go chapter's section 3, in fp64.
 //   5. move    - x_perm[p] = x[perm_src[p]], 16-byte vectors, one row per
 //                workgroup iteration (coalesced reads and writes).
+//
+// Expert capacity C (the Go chapter's "What was simplified": an expert
+// accepts a bounded number of tokens and the overflow is dropped): an
+// assignment whose rank within its expert's group (flat order) is C or more
+// is dropped.  Kept assignments get compacted rows (offsets over the kept
+// rows, pos = -1 for a dropped one); Importance and the statistics keep the
+// router's view (every assignment), through the full group starts.
 #include "common.h"
 
 namespace moe {
@@ -43,11 +50,12 @@ __global__ __launch_bounds__(kPermThreads) void perm_hist_kernel(
     hist[(int64_t)blockIdx.x * E + e] = h[e];
 }
 
-// One workgroup of 256 threads; thread e owns expert e.
+// One workgroup of 256 threads; thread e owns expert e.  full_off: group
+// starts over every assignment; offsets: over the kept ones (capacity cap).
 __global__ __launch_bounds__(kPermThreads) void perm_scan_kernel(
-    int32_t *__restrict__ hist, int nseg, int E, int n,
-    int32_t *__restrict__ offsets) {
-  __shared__ int sc[kPermThreads];
+    int32_t *__restrict__ hist, int nseg, int E, int n, int cap,
+    int32_t *__restrict__ full_off, int32_t *__restrict__ offsets) {
+  __shared__ int sc[kPermThreads], kc[kPermThreads];
   const int e = threadIdx.x;
   int total = 0;
   if (e < E) {
@@ -58,26 +66,35 @@ __global__ __launch_bounds__(kPermThreads) void perm_scan_kernel(
     }
   }
   sc[e] = total;
+  kc[e] = min(total, cap);
   __syncthreads();
-  // inclusive Hillis-Steele scan over the 256 expert totals
+  // inclusive Hillis-Steele scans over the 256 expert totals
   for (int off = 1; off < kPermThreads; off <<= 1) {
     const int v = e >= off ? sc[e - off] : 0;
+    const int u = e >= off ? kc[e - off] : 0;
     __syncthreads();
     sc[e] += v;
+    kc[e] += u;
     __syncthreads();
   }
   const int start = sc[e] - total;  // exclusive
   if (e < E) {
-    offsets[e] = start;
+    full_off[e] = start;
+    offsets[e] = kc[e] - min(total, cap);
     for (int s = 0; s < nseg; ++s) hist[(int64_t)s * E + e] += start;
   }
-  if (e == 0) offsets[E] = n;
+  if (e == 0) {
+    full_off[E] = n;
+    offsets[E] = kc[kPermThreads - 1];
+  }
 }
 
 __global__ __launch_bounds__(kPermThreads) void perm_scatter_kernel(
     const int32_t *__restrict__ idx, const float *__restrict__ w, int n, int k,
-    int E, const int32_t *__restrict__ base, int32_t *__restrict__ pos,
-    int32_t *__restrict__ perm_src, float *__restrict__ perm_w) {
+    int E, int cap, const int32_t *__restrict__ base,
+    const int32_t *__restrict__ full_off, const int32_t *__restrict__ offsets,
+    int32_t *__restrict__ pos, int32_t *__restrict__ perm_src,
+    float *__restrict__ perm_w) {
   constexpr int NW = kPermThreads / kWave;
   constexpr int SUB = kSeg / NW;    // assignments per wavefront
   __shared__ int run[NW][kMaxExperts];
@@ -121,9 +138,15 @@ __global__ __launch_bounds__(kPermThreads) void perm_scatter_kernel(
     if (valid) {
       const int rank = __popcll(peers & below);
       const int p = run[wv][e] + rank;
-      pos[f] = p;
-      perm_src[p] = f / k;
+      const int r = p - full_off[e];   // rank within the expert's group
       perm_w[p] = w[f];
+      if (r < cap) {
+        const int q = offsets[e] + r;
+        pos[f] = q;
+        perm_src[q] = f / k;
+      } else {
+        pos[f] = -1;
+      }
       // the lowest lane of each peer group advances the group's next row;
       // every lane read run[] above, before this store (in-order LDS)
       if (rank == 0) run[wv][e] = p + __popcll(peers);
@@ -131,8 +154,9 @@ __global__ __launch_bounds__(kPermThreads) void perm_scatter_kernel(
   }
 }
 
-// importance[e]: one wavefront per expert sums the kept weights of its
-// group (lane-strided partial sums, then a fixed butterfly: deterministic).
+// importance[e]: one wavefront per expert sums the router weights of its
+// group (every assignment, starts `full_off`; lane-strided partial sums,
+// then a fixed butterfly: deterministic).
 __global__ __launch_bounds__(kPermThreads) void perm_importance_kernel(
     const int32_t *__restrict__ offsets, const float *__restrict__ perm_w,
     int E, float *__restrict__ importance) {
@@ -185,12 +209,15 @@ __global__ __launch_bounds__(kWave) void perm_stats_kernel(
   }
 }
 
-// x_perm[p] = x[perm_src[p]]; row_vec16 = bytes per row / 16.  The source
-// index is clamped to [0, T) so that a corrupt index cannot read outside x.
+// x_perm[p] = x[perm_src[p]] for the kept rows p < *kept_rows; row_vec16 =
+// bytes per row / 16.  The source index is clamped to [0, T) so that a
+// corrupt index cannot read outside x.
 __global__ __launch_bounds__(kPermThreads) void perm_move_kernel(
-    const uint4 *__restrict__ x, const int32_t *__restrict__ perm_src, int n,
-    int T, int row_vec16, uint4 *__restrict__ x_perm) {
-  for (int p = blockIdx.x; p < n; p += gridDim.x) {
+    const uint4 *__restrict__ x, const int32_t *__restrict__ perm_src,
+    const int32_t *__restrict__ kept_rows, int n, int T, int row_vec16,
+    uint4 *__restrict__ x_perm) {
+  const int rows = min(max(*kept_rows, 0), n);
+  for (int p = blockIdx.x; p < rows; p += gridDim.x) {
     const int t = min(max(perm_src[p], 0), T - 1);
     const uint4 *src = x + (int64_t)t * row_vec16;
     uint4 *dst = x_perm + (int64_t)p * row_vec16;
@@ -210,12 +237,13 @@ constexpr int kFusedMax = 4096;
 
 __global__ __launch_bounds__(kFusedThreads) void perm_fused_kernel(
     const int32_t *__restrict__ idx, const float *__restrict__ w, int n, int k,
-    int E, int32_t *__restrict__ offsets, int32_t *__restrict__ pos,
+    int E, int cap, int32_t *__restrict__ offsets, int32_t *__restrict__ pos,
     int32_t *__restrict__ perm_src, float *__restrict__ perm_w,
     float *__restrict__ importance, double *__restrict__ stats) {
   constexpr int NW = kFusedThreads / kWave;
   __shared__ int h[kMaxExperts];
-  __shared__ int off[kMaxExperts + 1];
+  __shared__ int off[kMaxExperts + 1];    // full group starts
+  __shared__ int koff[kMaxExperts];       // kept group starts
   __shared__ int run[NW][kMaxExperts];
   __shared__ int scan_tmp[NW];
   const int tid = threadIdx.x;
@@ -230,19 +258,22 @@ __global__ __launch_bounds__(kFusedThreads) void perm_fused_kernel(
     if (static_cast<unsigned>(e) < static_cast<unsigned>(E)) atomicAdd(&h[e], 1);
   }
   __syncthreads();
-  // 2. group offsets: exclusive scan over the experts
+  // 2. group offsets: exclusive scans over the experts, of every assignment
+  //    (full) and of the kept ones (capacity)
   {
     const int c = tid < E ? h[tid] : 0;
-    int total;
+    int total, ktotal;
     const int ex = block_exclusive_scan<kFusedThreads>(c, scan_tmp, &total);
+    const int kex = block_exclusive_scan<kFusedThreads>(min(c, cap), scan_tmp, &ktotal);
     if (tid < E) {
       off[tid] = ex;
-      offsets[tid] = ex;
-      h[tid] = ex;          // running first row of each expert
+      koff[tid] = kex;
+      offsets[tid] = kex;
+      h[tid] = ex;          // running first full row of each expert
     }
     if (tid == 0) {
       off[E] = n;
-      offsets[E] = n;
+      offsets[E] = ktotal;
     }
   }
   __syncthreads();
@@ -277,9 +308,15 @@ __global__ __launch_bounds__(kFusedThreads) void perm_fused_kernel(
     __syncthreads();
     if (valid) {
       const int p = run[wv][e] + rank;
-      pos[f] = p;
-      perm_src[p] = f / k;
+      const int r = p - off[e];
       perm_w[p] = w[f];
+      if (r < cap) {
+        const int q = koff[e] + r;
+        pos[f] = q;
+        perm_src[q] = f / k;
+      } else {
+        pos[f] = -1;
+      }
     }
     __syncthreads();
   }
@@ -345,32 +382,32 @@ hipError_t launch_zero_stats(float *importance, int E, double *stats, hipStream_
 
 int perm_num_segments(int64_t n) { return static_cast<int>((n + kSeg - 1) / kSeg); }
 
-// Workspace: hist [nseg * E] int32, perm_w [n] fp32.
+// Workspace: hist [nseg * E] int32, full_off [E + 1] int32, perm_w [n] fp32.
 hipError_t launch_permute(const int32_t *idx, const float *w, const void *x,
-                          int T, int k, int E, int row_bytes, int32_t *offsets,
-                          int32_t *perm_src, int32_t *pos, float *importance,
-                          double *stats, void *x_perm, int32_t *hist,
-                          float *perm_w, hipStream_t s) {
+                          int T, int k, int E, int capacity, int row_bytes,
+                          int32_t *offsets, int32_t *perm_src, int32_t *pos,
+                          float *importance, double *stats, void *x_perm,
+                          int32_t *hist, int32_t *full_off, float *perm_w,
+                          hipStream_t s) {
   const int n = T * k;
   if (n == 0) return launch_zero_stats(importance, E, stats, s);
+  const int cap = capacity > 0 ? capacity : n;
   const int blocks = n < 8192 ? n : 8192;
   if (n <= kFusedMax) {
-    perm_fused_kernel<<<1, kFusedThreads, 0, s>>>(idx, w, n, k, E, offsets, pos, perm_src,
-                                                  perm_w, importance, stats);
-    perm_move_kernel<<<blocks, kPermThreads, 0, s>>>(
-        static_cast<const uint4 *>(x), perm_src, n, T, row_bytes / 16,
-        static_cast<uint4 *>(x_perm));
-    return hipGetLastError();
+    perm_fused_kernel<<<1, kFusedThreads, 0, s>>>(idx, w, n, k, E, cap, offsets, pos,
+                                                  perm_src, perm_w, importance, stats);
+  } else {
+    const int nseg = perm_num_segments(n);
+    perm_hist_kernel<<<nseg, kPermThreads, 0, s>>>(idx, n, E, hist);
+    perm_scan_kernel<<<1, kPermThreads, 0, s>>>(hist, nseg, E, n, cap, full_off, offsets);
+    perm_scatter_kernel<<<nseg, kPermThreads, 0, s>>>(idx, w, n, k, E, cap, hist, full_off,
+                                                      offsets, pos, perm_src, perm_w);
+    perm_importance_kernel<<<(E + 3) / 4, kPermThreads, 0, s>>>(full_off, perm_w, E,
+                                                                importance);
+    if (stats) perm_stats_kernel<<<1, kWave, 0, s>>>(full_off, importance, E, stats);
   }
-  const int nseg = perm_num_segments(n);
-  perm_hist_kernel<<<nseg, kPermThreads, 0, s>>>(idx, n, E, hist);
-  perm_scan_kernel<<<1, kPermThreads, 0, s>>>(hist, nseg, E, n, offsets);
-  perm_scatter_kernel<<<nseg, kPermThreads, 0, s>>>(idx, w, n, k, E, hist, pos,
-                                                    perm_src, perm_w);
-  perm_importance_kernel<<<(E + 3) / 4, kPermThreads, 0, s>>>(offsets, perm_w, E, importance);
-  if (stats) perm_stats_kernel<<<1, kWave, 0, s>>>(offsets, importance, E, stats);
   perm_move_kernel<<<blocks, kPermThreads, 0, s>>>(
-      static_cast<const uint4 *>(x), perm_src, n, T, row_bytes / 16,
+      static_cast<const uint4 *>(x), perm_src, offsets + E, n, T, row_bytes / 16,
       static_cast<uint4 *>(x_perm));
   return hipGetLastError();
 }

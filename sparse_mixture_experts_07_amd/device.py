@@ -45,8 +45,9 @@ class DeviceLayer:
     w_down_shared: Optional[torch.Tensor]
 
     @classmethod
-    def upload(cls, layer, device="cuda") -> "DeviceLayer":
-        return cls(B.config_of(layer.cfg), to_device(layer.x, device),
+    def upload(cls, layer, device="cuda", capacity: int = 0) -> "DeviceLayer":
+        """capacity: per-expert limit on kept assignments (0: no limit)."""
+        return cls(B.config_of(layer.cfg, capacity), to_device(layer.x, device),
                    to_device(layer.w_gate, device), to_device(layer.b_gate, device),
                    to_device(layer.w_up, device), to_device(layer.w_down, device),
                    to_device(layer.b_up, device), to_device(layer.b_down, device),

@@ -28,9 +28,9 @@ def to_f64(t: torch.Tensor) -> np.ndarray:
     return t.detach().cpu().numpy().astype(np.float64)
 
 
-def run_forward(layer):
+def run_forward(layer, capacity: int = 0):
     """moe_forward on the layer; host copies of every output."""
-    dl = DeviceLayer.upload(layer)
+    dl = DeviceLayer.upload(layer, capacity=capacity)
     fw = Forward(dl)
     fw()
     torch.cuda.synchronize()
@@ -57,9 +57,10 @@ def check_routing(layer, idx, w, counts, t0=0):
     return ridx, rw
 
 
-def check_outputs(layer, y, tokens, tol=None):
+def check_outputs(layer, y, tokens, tol=None, keep=None):
+    """keep: the oracle's capacity mask (dropped slots add nothing)."""
     tokens = np.asarray(tokens, np.int64)
-    ref, _, _ = oracle.forward_tokens(layer, tokens)
+    ref, _, _ = oracle.forward_tokens(layer, tokens, keep=keep)
     got = y[tokens]
     assert np.all(np.isfinite(got))
     tol = tol or (BF16_TOL if layer.cfg.dtype == 1 else F32_TOL)

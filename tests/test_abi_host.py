@@ -27,7 +27,7 @@ def test_library_exports_every_declared_entry_point():
     assert set(B.EXPORTS) == set(names), names
     for n in names:
         assert hasattr(lib, n), f"libmoe.so does not export {n}"
-    assert B.moe_abi_version() == 1
+    assert B.moe_abi_version() == 2
 
 
 def test_status_strings():
@@ -77,16 +77,17 @@ BAD_CFGS = {
     "bad_act": (dict(act=7), B.MOE_ERR_INVALID_ARGUMENT),
     "bad_dtype": (dict(dtype=5), B.MOE_ERR_INVALID_ARGUMENT),
     "too_many_rows": (dict(T=2 ** 30, k=2), B.MOE_ERR_UNSUPPORTED),
+    "capacity_negative": (dict(capacity=-1), B.MOE_ERR_INVALID_ARGUMENT),
 }
 
 FAKE = 1 << 20   # aligned non-null stand-in pointer; never dereferenced
 
 
 def _cfg(**kw):
-    base = dict(T=64, d=64, h=256, E=8, k=2, act=0, dtype=0, S=0)
+    base = dict(T=64, d=64, h=256, E=8, k=2, act=0, dtype=0, S=0, capacity=0)
     base.update(kw)
     return B.config(base["T"], base["d"], base["h"], base["E"], base["k"],
-                    base["act"], base["dtype"], base["S"])
+                    base["act"], base["dtype"], base["S"], base["capacity"])
 
 
 @pytest.mark.parametrize("name", list(BAD_CFGS))
@@ -133,3 +134,19 @@ def test_pointer_and_workspace_checks():
     assert L.moe_permute(r, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, 16, None) == small
     assert L.moe_expert_ffn(r, C.byref(w), FAKE, FAKE, FAKE, FAKE, FAKE, 16, None) == small
     assert L.moe_load_stats(None, None, 4, None, None, None) == inv
+
+
+def test_expert_capacity_matches_oracle():
+    for T, k, E, f in [(1, 1, 8, 1.0), (4096, 2, 8, 1.0), (4096, 2, 8, 1.25),
+                       (4096, 8, 256, 1.0), (7, 2, 64, 0.5), (12288, 2, 8, 2.0),
+                       (3, 1, 4, 1e-9), (100, 4, 6, 1.5)]:
+        assert B.moe_expert_capacity(T, k, E, f) == oracle.expert_capacity(T, k, E, f)
+    L = B.lib()
+    out = C.c_int32()
+    inv = B.MOE_ERR_INVALID_ARGUMENT
+    assert L.moe_expert_capacity(16, 2, 8, 0.0, C.byref(out)) == inv
+    assert L.moe_expert_capacity(16, 2, 8, -1.0, C.byref(out)) == inv
+    assert L.moe_expert_capacity(16, 2, 8, float("nan"), C.byref(out)) == inv
+    assert L.moe_expert_capacity(16, 2, 0, 1.0, C.byref(out)) == inv
+    assert L.moe_expert_capacity(16, 2, 8, 1.0, None) == inv
+    assert L.moe_expert_capacity(2 ** 40, 8, 1, 1.0, C.byref(out)) == B.MOE_ERR_UNSUPPORTED
