@@ -38,7 +38,7 @@ def build(force: bool = True) -> str:
 class _Cfg(C.Structure):
     _fields_ = [("T", C.c_int64), ("d", C.c_int32), ("h", C.c_int32),
                 ("E", C.c_int32), ("k", C.c_int32), ("S", C.c_int32),
-                ("act", C.c_int32), ("dtype", C.c_int32)]
+                ("act", C.c_int32), ("dtype", C.c_int32), ("gate", C.c_int32)]
 
 
 class _Weights(C.Structure):
@@ -91,7 +91,7 @@ def _ptr(a: Optional[np.ndarray]):
 
 def _cfg(c) -> _Cfg:
     return _Cfg(int(c.T), int(c.d), int(c.h), int(c.E), int(c.k), int(c.S),
-                int(c.act), int(c.dtype))
+                int(c.act), int(c.dtype), int(getattr(c, "gate", 0)))
 
 
 def _weights(L) -> _Weights:

@@ -50,7 +50,18 @@
  *     index t*k + j;
  *   - expert capacity: an expert accepts its first C assignments in that
  *     flat order, the rest are dropped, the surviving weights are not
- *     renormalised (Go chapter, "What was simplified").
+ *     renormalised (Go chapter, "What was simplified");
+ *   - gate modes other than the default (cfg.gate):
+ *     bias-selects: the router bias steers the selection only, the kept
+ *     weights are the softmax of the unbiased kept scores (Go chapter,
+ *     section 3 "Load balancing" and "Pros, cons and real examples":
+ *     DeepSeek-V3 balances load by adjusting a bias instead of a loss);
+ *     softmax-all: the softmax runs over all E scores and the kept values
+ *     are used as they are, not renormalised (techfeed summary, "The
+ *     hardest part: making the router trainable": the softmaxed router
+ *     output weights the chosen experts; with k = 1 this is the Switch
+ *     Transformer top-1 gate).  Selection is the same stable top-k on the
+ *     (biased) float32 scores in every mode.
  *
  * Build: gcc -O2 -fopenmp -ffp-contract=off -mfma (no other contraction).
  */
@@ -65,9 +76,13 @@
 #define ORACLE_F32 0
 #define ORACLE_BF16 1
 
+#define ORACLE_GATE_TOPK 0
+#define ORACLE_GATE_BIAS_SELECTS 1
+#define ORACLE_GATE_SOFTMAX_ALL 2
+
 typedef struct {
   int64_t T;
-  int32_t d, h, E, k, S, act, dtype;
+  int32_t d, h, E, k, S, act, dtype, gate;
 } oracle_cfg;
 
 typedef struct {
@@ -104,18 +119,21 @@ static int cfg_ok(const oracle_cfg *c) {
          c->k <= c->E && (c->S == 0 || c->S == 1) &&
          (c->act == ORACLE_GELU || c->act == ORACLE_SWIGLU) &&
          (c->dtype == ORACLE_F32 || c->dtype == ORACLE_BF16) &&
-         !(c->S && c->act != ORACLE_SWIGLU);
+         !(c->S && c->act != ORACLE_SWIGLU) &&
+         c->gate >= ORACLE_GATE_TOPK && c->gate <= ORACLE_GATE_SOFTMAX_ALL;
 }
 
-/* ---- step 1: router scores of one token (float32, sequential) ---- */
+/* ---- step 1: router scores of one token (float32, sequential).  score[e]
+ * includes the bias; raw[e] is the same chain without it. ---- */
 
 static void router_scores(const oracle_cfg *c, const void *x, const float *wg,
-                          const float *bg, int64_t t, float *score) {
+                          const float *bg, int64_t t, float *score, float *raw) {
   const int d = c->d;
   for (int e = 0; e < c->E; ++e) {
     float s = 0.0f;
     for (int i = 0; i < d; ++i)
       s = fmaf(elem_f(x, c->dtype, t * d + i), wg[(int64_t)e * d + i], s);
+    raw[e] = s;
     if (bg) s = s + bg[e];
     score[e] = s;
   }
@@ -145,13 +163,38 @@ static void keep_top_k(const float *score, int E, int k, int32_t *idx,
 
 static void kept_softmax(const float *score, const int32_t *idx, int k,
                          double *w) {
-  const double m = (double)score[idx[0]];
+  double m = (double)score[idx[0]];
+  for (int j = 1; j < k; ++j)
+    if ((double)score[idx[j]] > m) m = (double)score[idx[j]];
   double z = 0.0;
   for (int j = 0; j < k; ++j) {
     w[j] = exp((double)score[idx[j]] - m);
     z += w[j];
   }
   for (int j = 0; j < k; ++j) w[j] = w[j] / z;
+}
+
+/* softmax over all E scores, read at the kept indices (no renormalisation
+ * over the kept ones). */
+static void full_softmax_at(const float *score, int E, const int32_t *idx,
+                            int k, double *w) {
+  double m = (double)score[0];
+  for (int e = 1; e < E; ++e)
+    if ((double)score[e] > m) m = (double)score[e];
+  double z = 0.0;
+  for (int e = 0; e < E; ++e) z += exp((double)score[e] - m);
+  for (int j = 0; j < k; ++j) w[j] = exp((double)score[idx[j]] - m) / z;
+}
+
+/* The gate values of the kept experts for the configured gate mode. */
+static void gate_weights(const oracle_cfg *c, const float *score,
+                         const float *raw, const int32_t *idx, double *w) {
+  if (c->gate == ORACLE_GATE_BIAS_SELECTS)
+    kept_softmax(raw, idx, c->k, w);
+  else if (c->gate == ORACLE_GATE_SOFTMAX_ALL)
+    full_softmax_at(score, c->E, idx, c->k, w);
+  else
+    kept_softmax(score, idx, c->k, w);
 }
 
 /* ---- step 4: one expert FFN on one token row, in double.
@@ -217,17 +260,19 @@ int oracle_route(const oracle_cfg *c, const void *x, const float *wg,
 #pragma omp parallel reduction(| : bad)
   {
     float *s = (float *)malloc(sizeof(float) * (size_t)c->E);
+    float *raw = (float *)malloc(sizeof(float) * (size_t)c->E);
     unsigned char *tk = (unsigned char *)malloc((size_t)c->E);
 #pragma omp for schedule(static)
     for (int64_t r = 0; r < nt; ++r) {
-      router_scores(c, x, wg, bg, t0 + r, s);
+      router_scores(c, x, wg, bg, t0 + r, s, raw);
       for (int e = 0; e < c->E; ++e)
-        if (!isfinite(s[e])) bad = 1;
+        if (!isfinite(s[e]) || !isfinite(raw[e])) bad = 1;
       if (scores) memcpy(scores + r * c->E, s, sizeof(float) * (size_t)c->E);
       keep_top_k(s, c->E, c->k, idx + r * c->k, tk);
-      kept_softmax(s, idx + r * c->k, c->k, w + r * c->k);
+      gate_weights(c, s, raw, idx + r * c->k, w + r * c->k);
     }
     free(s);
+    free(raw);
     free(tk);
   }
   return bad ? -2 : 0;
@@ -346,6 +391,7 @@ int oracle_forward_tokens_keep(const oracle_cfg *c, const oracle_weights *W,
 #pragma omp parallel reduction(| : bad)
   {
     float *s = (float *)malloc(sizeof(float) * (size_t)c->E);
+    float *raw = (float *)malloc(sizeof(float) * (size_t)c->E);
     unsigned char *tk = (unsigned char *)malloc((size_t)c->E);
     double *xr = (double *)malloc(sizeof(double) * (size_t)d);
     double *ye = (double *)malloc(sizeof(double) * (size_t)d);
@@ -353,13 +399,13 @@ int oracle_forward_tokens_keep(const oracle_cfg *c, const oracle_weights *W,
 #pragma omp for schedule(dynamic, 1)
     for (int64_t r = 0; r < nt; ++r) {
       const int64_t t = tokens[r];
-      router_scores(c, x, W->w_gate, W->b_gate, t, s);
+      router_scores(c, x, W->w_gate, W->b_gate, t, s, raw);
       for (int e = 0; e < c->E; ++e)
-        if (!isfinite(s[e])) bad = 1;
+        if (!isfinite(s[e]) || !isfinite(raw[e])) bad = 1;
       int32_t *ix = idx + r * c->k;
       double *wr = w + r * c->k;
       keep_top_k(s, c->E, c->k, ix, tk);
-      kept_softmax(s, ix, c->k, wr);
+      gate_weights(c, s, raw, ix, wr);
       for (int64_t i = 0; i < d; ++i) xr[i] = elem(x, c->dtype, t * d + i);
       double *yo = y + r * d;
       for (int64_t i = 0; i < d; ++i) yo[i] = 0.0;
@@ -374,6 +420,7 @@ int oracle_forward_tokens_keep(const oracle_cfg *c, const oracle_weights *W,
       }
     }
     free(s);
+    free(raw);
     free(tk);
     free(xr);
     free(ye);

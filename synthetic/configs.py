@@ -15,6 +15,10 @@ GELU = 0
 SWIGLU = 1
 F32 = 0
 BF16 = 1
+# how the kept gate values are formed from the router scores
+GATE_TOPK_SOFTMAX = 0    # softmax over the k kept scores (bias in both)
+GATE_BIAS_SELECTS = 1    # bias steers the selection only; softmax of unbiased kept scores
+GATE_SOFTMAX_ALL = 2     # softmax over all E scores, kept values not renormalised
 
 
 @dataclass(frozen=True)
@@ -32,6 +36,7 @@ class LayerConfig:
     layernorm_x: bool = False   # x drawn N(0,1) then LayerNorm'd per row
     expert_bias: bool = False   # GELU experts carry b1/b2 (zero-filled)
     seed: int = 0
+    gate: int = GATE_TOPK_SOFTMAX
 
     @property
     def n_up(self) -> int:

@@ -10,9 +10,10 @@ from synthetic import BF16, F32, GELU, SWIGLU, LayerConfig, f32_to_bf16_bits
 
 def layer(T, d, h, E, k, act=GELU, dtype=F32, S=0, *, x, w_gate, b_gate=None,
           w_up, w_down, b_up=None, b_down=None, w_up_shared=None,
-          w_down_shared=None):
+          w_down_shared=None, gate=0):
     """Wrap hand-made float arrays as a layer; bf16 layers round them (RNE)."""
-    cfg = LayerConfig("hand", T=T, d=d, h=h, E=E, k=k, act=act, dtype=dtype, S=S)
+    cfg = LayerConfig("hand", T=T, d=d, h=h, E=E, k=k, act=act, dtype=dtype, S=S,
+                      gate=gate)
 
     def q(a):
         if a is None:
@@ -29,7 +30,7 @@ def layer(T, d, h, E, k, act=GELU, dtype=F32, S=0, *, x, w_gate, b_gate=None,
 
 
 def random_layer(seed, T, d, h, E, k, act=GELU, dtype=F32, S=0, bias=False,
-                 expert_bias=False, wstd=0.3):
+                 expert_bias=False, wstd=0.3, gate=0):
     rng = np.random.default_rng(seed)
     n_up = h if act == GELU else 2 * h
     return layer(
@@ -42,7 +43,8 @@ def random_layer(seed, T, d, h, E, k, act=GELU, dtype=F32, S=0, bias=False,
         b_up=rng.standard_normal((E, h)) * 0.1 if expert_bias else None,
         b_down=rng.standard_normal((E, d)) * 0.1 if expert_bias else None,
         w_up_shared=rng.standard_normal((1, 2 * h, d)) * wstd if S else None,
-        w_down_shared=rng.standard_normal((1, d, h)) * wstd if S else None)
+        w_down_shared=rng.standard_normal((1, d, h)) * wstd if S else None,
+        gate=gate)
 
 
 __all__ = ["layer", "random_layer", "BF16", "F32", "GELU", "SWIGLU"]

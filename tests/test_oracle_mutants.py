@@ -47,6 +47,17 @@ MUTANTS = {
     "capacity_ignored_in_forward": ("if (keep && !keep[t * c->k + j]) continue;", ""),
     "grouping_ignores_drops": ("if (idx[f] != e || !keep[f]) continue;",
                                "if (idx[f] != e) continue;"),
+    "bias_selects_uses_biased_scores": ("kept_softmax(raw, idx, c->k, w);",
+                                        "kept_softmax(score, idx, c->k, w);"),
+    "raw_scores_include_bias": ("    raw[e] = s;\n    if (bg) s = s + bg[e];",
+                                "    if (bg) s = s + bg[e];\n    raw[e] = s;"),
+    "softmax_all_renormalised": (
+        "for (int e = 0; e < E; ++e) z += exp((double)score[e] - m);",
+        "for (int j = 0; j < k; ++j) z += exp((double)score[idx[j]] - m);"),
+    "softmax_all_off_by_one_sum": (
+        "for (int e = 0; e < E; ++e) z += exp((double)score[e] - m);",
+        "for (int e = 1; e < E; ++e) z += exp((double)score[e] - m);"),
+    "gate_mode_ignored": ("if (c->gate == ORACLE_GATE_BIAS_SELECTS)", "if (0)"),
 }
 
 

@@ -470,3 +470,118 @@ def test_token_with_every_slot_dropped(oracle_lib):
             np.testing.assert_array_equal(y[0], ref)
         else:
             np.testing.assert_array_equal(y[0], np.zeros(c.d))
+
+
+# ---- gate modes.  bias-selects: the bias steers the selection only (Go
+# chapter, section 3 and "Pros, cons and real examples": DeepSeek-V3 balances
+# load through a bias instead of a loss); softmax-all: the softmax over all E
+# scores weights the chosen experts as it is (techfeed summary, "The hardest
+# part: making the router trainable"; k = 1 is the Switch Transformer gate) ----
+
+def _with_gate(L, gate, b_gate="keep"):
+    L.cfg = L.cfg.with_(gate=gate)
+    if not isinstance(b_gate, str):
+        L.b_gate = None if b_gate is None else np.asarray(b_gate, np.float32)
+    return L
+
+
+def test_bias_selects_worked_example(oracle_lib):
+    """The techfeed scores with a bias lifting experts 0 (+2) and 1 (+1):
+    both modes select [0, 1]; the default weights are sigma of the biased
+    gap, bias-selects weights sigma of the unbiased gap."""
+    g = GOLD["router_example"]
+    s = np.float32(g["scores"])
+    b = np.float32([2, 1, 0, 0, 0, 0])
+    l0, l1 = float(s[0]), float(s[1])
+    for gate, gap in ((synthetic.GATE_TOPK_SOFTMAX, float(np.float32(l0 + 2)) - float(np.float32(l1 + 1))),
+                      (synthetic.GATE_BIAS_SELECTS, l0 - l1)):
+        L = _with_gate(_identity_router([s], 2), gate, b)
+        idx, w, sc = oracle_lib.route(L, want_scores=True)
+        assert idx[0].tolist() == [0, 1]
+        assert sc[0].tolist() == (s + b).tolist()
+        assert w[0, 0] == pytest.approx(1.0 / (1.0 + math.exp(-gap)), rel=1e-15)
+        assert w[0, 1] == pytest.approx(1.0 / (1.0 + math.exp(gap)), rel=1e-15)
+
+
+@pytest.mark.parametrize("k", [1, 2, 4, 8])
+def test_bias_selects_weights_are_unbiased_softmax(oracle_lib, k):
+    """Same selection as the default mode; weights = scipy softmax of the
+    scores the same router gives without its bias, at the kept experts.
+    Without a bias the two modes agree exactly."""
+    L = random_layer(21, T=40, d=24, h=8, E=8, k=k, act=SWIGLU, bias=True)
+    idx0, _, sc = oracle_lib.route(L, want_scores=True)
+    b = L.b_gate
+    _with_gate(L, synthetic.GATE_BIAS_SELECTS)
+    idx1, w1, sc1 = oracle_lib.route(L, want_scores=True)
+    np.testing.assert_array_equal(idx1, idx0)
+    np.testing.assert_array_equal(sc1, sc)
+    _with_gate(L, synthetic.GATE_TOPK_SOFTMAX, None)
+    _, _, raw = oracle_lib.route(L, want_scores=True)
+    assert not np.array_equal(raw, sc)
+    ref = scipy.special.softmax(np.take_along_axis(raw, idx1, 1).astype(np.float64), axis=1)
+    np.testing.assert_allclose(w1, ref, rtol=1e-13, atol=0)
+    # no bias: the modes coincide
+    idx_a, w_a, _ = oracle_lib.route(L)
+    _with_gate(L, synthetic.GATE_BIAS_SELECTS, None)
+    idx_b, w_b, _ = oracle_lib.route(L)
+    np.testing.assert_array_equal(idx_a, idx_b)
+    np.testing.assert_array_equal(w_a, w_b)
+    del b
+
+
+def test_softmax_all_closed_forms(oracle_lib):
+    """Techfeed scores: k = 1 gives p_max = 1 / sum_e exp(s_e - s_max) (the
+    Switch gate), k = 2 gives p_4 and p_2 from the full softmax (their sum
+    below 1), k = E gives the whole softmax in descending order (sum 1)."""
+    s = np.float64(np.float32(GOLD["router_example"]["scores"]))
+    z = sum(math.exp(v - s.max()) for v in s)
+    for k in (1, 2, 6):
+        L = _with_gate(_identity_router([np.float32(s)], k), synthetic.GATE_SOFTMAX_ALL)
+        idx, w, _ = oracle_lib.route(L)
+        assert idx[0, :2].tolist() == [4, 2][:k]
+        for j in range(k):
+            assert w[0, j] == pytest.approx(math.exp(s[idx[0, j]] - s.max()) / z, rel=1e-15)
+        if k == 6:
+            assert w[0].sum() == pytest.approx(1.0, rel=1e-15)
+        else:
+            assert w[0].sum() < 1.0
+
+
+@pytest.mark.parametrize("k", [1, 3, 8])
+def test_softmax_all_against_scipy_and_kept_ratios(oracle_lib, k):
+    """Weights = scipy softmax over all E (biased) scores read at the kept
+    experts; their ratios equal those of the default (renormalised) mode."""
+    L = random_layer(22, T=50, d=16, h=8, E=8, k=k, act=GELU, bias=True)
+    idx0, w0, sc = oracle_lib.route(L, want_scores=True)
+    _with_gate(L, synthetic.GATE_SOFTMAX_ALL)
+    idx2, w2, _ = oracle_lib.route(L)
+    np.testing.assert_array_equal(idx2, idx0)
+    p = scipy.special.softmax(sc.astype(np.float64), axis=1)
+    np.testing.assert_allclose(w2, np.take_along_axis(p, idx2, 1), rtol=1e-13, atol=0)
+    np.testing.assert_allclose(w2 / w2.sum(1, keepdims=True), w0, rtol=1e-13, atol=0)
+
+
+@pytest.mark.parametrize("S", [0, 1])
+def test_softmax_all_with_every_expert_is_dense_softmax_gate(oracle_lib, S):
+    """k = E: the layer is the dense softmax-gated mixture sum_e softmax(s)_e
+    E_e(x) (Qiita summary, "Sparsely-Gated MoE layer formula" with the
+    plain softmax gate); k < E: the same sum over the kept experts only."""
+    for k in (5, 2):
+        L = random_layer(23, T=5, d=10, h=12, E=5, k=k, act=SWIGLU, S=S, bias=True,
+                         gate=synthetic.GATE_SOFTMAX_ALL)
+        c = L.cfg
+        y, idx, _ = oracle_lib.forward_tokens(L, range(c.T))
+        _, _, sc = oracle_lib.route(L, want_scores=True)
+        for t in range(c.T):
+            G = scipy.special.softmax(sc[t].astype(np.float64))
+            xr = L.x[t].astype(np.float64)
+            dense = sum(G[i] * oracle_lib.expert(L, i, xr) for i in idx[t])
+            if S:
+                dense = dense + oracle_lib.expert(L, c.E, xr)
+            np.testing.assert_allclose(y[t], dense, rtol=1e-12, atol=1e-14)
+
+
+def test_unknown_gate_mode_rejected(oracle_lib):
+    L = _with_gate(random_layer(24, T=3, d=8, h=8, E=4, k=2), 3)
+    with pytest.raises(ValueError):
+        oracle_lib.route(L)
