@@ -42,7 +42,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 2
+#define MOE_ABI_VERSION 3
 
 typedef enum {
   MOE_OK = 0,
@@ -61,6 +61,24 @@ typedef enum { MOE_DTYPE_F32 = 0, MOE_DTYPE_BF16 = 1 } moe_dtype_t;
  * "What was simplified" names. */
 typedef enum { MOE_ACT_GELU = 0, MOE_ACT_SWIGLU = 1 } moe_act_t;
 
+/* How the kept gate values come from the router scores s = x W_g^T + b.
+ * The selection is the same in every mode: the stable top-k of s.
+ *   MOE_GATE_TOPK_SOFTMAX: softmax over the k kept s (Go chapter section 2,
+ *     Route: pick the top k and re-softmax).
+ *   MOE_GATE_BIAS_SELECTS: the bias steers the selection only; the weights
+ *     are the softmax over the kept experts of the unbiased scores x W_g^T
+ *     (Go chapter, section 3 and "Pros, cons and real examples": DeepSeek-V3
+ *     balances expert load by adjusting a bias rather than with a loss).
+ *   MOE_GATE_SOFTMAX_ALL: softmax over all E scores, read at the kept
+ *     experts and not renormalised (techfeed summary, "The hardest part:
+ *     making the router trainable": the softmaxed router output weights the
+ *     chosen experts; with k = 1 this is the Switch Transformer gate). */
+typedef enum {
+  MOE_GATE_TOPK_SOFTMAX = 0,
+  MOE_GATE_BIAS_SELECTS = 1,
+  MOE_GATE_SOFTMAX_ALL = 2
+} moe_gate_t;
+
 typedef struct {
   int64_t num_tokens;  /* T */
   int32_t d_model;     /* d */
@@ -78,6 +96,7 @@ typedef struct {
                           "What was simplified": real implementations cap
                           what an expert accepts and drop the overflow).
                           See moe_expert_capacity for C from a factor. */
+  int32_t gate;        /* moe_gate_t (0 = softmax over the kept k) */
 } moe_config_t;
 
 /* Expert weights, all packed over experts into single tensors ("Weight
@@ -113,11 +132,13 @@ moe_status_t moe_grouped_rows(const moe_config_t *cfg, int64_t *rows);
  *   w_gate   [E, d] fp32, b_gate [E] fp32 or NULL (device, in)
  *   topk_idx [T, k] int32  (out) expert indices in descending score order;
  *            equal scores keep the lower index first (a stable sort)
- *   topk_w   [T, k] fp32   (out) exp(s_j - s_0) / sum_i exp(s_i - s_0)
+ *   topk_w   [T, k] fp32   (out) the gate values of cfg->gate; default
+ *            exp(s_j - s_0) / sum_i exp(s_i - s_0) over the kept i
  *   counts   [E] int32     (out) tokens routed to each expert (Stats)
  *   logits   [T, E] fp32 or NULL (out) router scores: for each (t, e)
  *            s = +0; s = fma(x[t,i], W_g[e,i], s) for i = 0..d-1 in order;
- *            s = s + b_g[e]; all in fp32 */
+ *            s = s + b_g[e]; all in fp32 (the biased score, in every
+ *            gate mode) */
 moe_status_t moe_route(const moe_config_t *cfg, const void *x,
                        const float *w_gate, const float *b_gate,
                        int32_t *topk_idx, float *topk_w, int32_t *counts,

@@ -25,6 +25,9 @@ MOE_DTYPE_F32 = 0
 MOE_DTYPE_BF16 = 1
 MOE_ACT_GELU = 0
 MOE_ACT_SWIGLU = 1
+MOE_GATE_TOPK_SOFTMAX = 0
+MOE_GATE_BIAS_SELECTS = 1
+MOE_GATE_SOFTMAX_ALL = 2
 
 EXPORTS = (
     "moe_abi_version", "moe_status_string", "moe_workspace_bytes",
@@ -45,7 +48,7 @@ class MoeConfig(C.Structure):
                 ("d_hidden", C.c_int32), ("num_experts", C.c_int32),
                 ("top_k", C.c_int32), ("num_shared", C.c_int32),
                 ("act", C.c_int32), ("dtype", C.c_int32),
-                ("capacity", C.c_int32)]
+                ("capacity", C.c_int32), ("gate", C.c_int32)]
 
 
 class MoeWeights(C.Structure):
@@ -139,14 +142,16 @@ def _check(fn: str, st: int) -> None:
 
 
 def config(T: int, d: int, h: int, E: int, k: int, act: int, dtype: int,
-           S: int = 0, capacity: int = 0) -> MoeConfig:
+           S: int = 0, capacity: int = 0, gate: int = 0) -> MoeConfig:
     return MoeConfig(int(T), int(d), int(h), int(E), int(k), int(S), int(act),
-                     int(dtype), int(capacity))
+                     int(dtype), int(capacity), int(gate))
 
 
 def config_of(c, capacity: int = 0) -> MoeConfig:
-    """From any object with T, d, h, E, k, S, act, dtype attributes."""
-    return config(c.T, c.d, c.h, c.E, c.k, c.act, c.dtype, c.S, capacity)
+    """From any object with T, d, h, E, k, S, act, dtype (and optionally
+    gate) attributes."""
+    return config(c.T, c.d, c.h, c.E, c.k, c.act, c.dtype, c.S, capacity,
+                  getattr(c, "gate", 0))
 
 
 def weights(w_gate, w_up, w_down, b_gate=None, b_up=None, b_down=None,

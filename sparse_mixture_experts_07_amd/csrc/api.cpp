@@ -10,7 +10,7 @@
 
 namespace moe {
 hipError_t launch_fill_i32(int32_t *p, int n, int32_t v, hipStream_t s);
-hipError_t launch_route(bool bf16, const void *x, const float *wg, const float *bg,
+hipError_t launch_route(bool bf16, int gate, const void *x, const float *wg, const float *bg,
                         int T, int d, int E, int k, int32_t *idx, float *w,
                         int32_t *counts, float *logits, hipStream_t s);
 int perm_num_segments(int64_t n);
@@ -57,7 +57,8 @@ moe_status_t check_cfg(const moe_config_t *c) {
   if (!c) return MOE_ERR_INVALID_ARGUMENT;
   if (c->num_tokens < 0 || c->d_model <= 0 || c->d_hidden <= 0 ||
       c->num_experts < 1 || c->top_k < 1 || c->top_k > c->num_experts ||
-      c->num_shared < 0 || c->capacity < 0)
+      c->num_shared < 0 || c->capacity < 0 || c->gate < MOE_GATE_TOPK_SOFTMAX ||
+      c->gate > MOE_GATE_SOFTMAX_ALL)
     return MOE_ERR_INVALID_ARGUMENT;
   if ((c->act != MOE_ACT_GELU && c->act != MOE_ACT_SWIGLU) ||
       (c->dtype != MOE_DTYPE_F32 && c->dtype != MOE_DTYPE_BF16))
@@ -180,7 +181,8 @@ moe_status_t moe_route(const moe_config_t *cfg, const void *x, const float *w_ga
                 !dev_ok(topk_idx) || !dev_ok(topk_w) || !opt_ok(logits)))
     return MOE_ERR_INVALID_ARGUMENT;
   clear_pending_error();
-  return hip_status(moe::launch_route(cfg->dtype == MOE_DTYPE_BF16, x, w_gate, b_gate, T,
+  return hip_status(moe::launch_route(cfg->dtype == MOE_DTYPE_BF16, cfg->gate, x, w_gate,
+                                      b_gate, T,
                                       cfg->d_model, cfg->num_experts, cfg->top_k,
                                       topk_idx, topk_w, counts, logits, stream));
 }

@@ -13,7 +13,13 @@
 // section, sort.SliceStable; KeepTopK of the "Sparsely-Gated MoE" Qiita
 // summary, "Gating: Noisy Top-k Softmax").  One wavefront per token runs k
 // rounds of a 64-lane arg-max whose order is (score desc, index asc).
-// Weights: exp(s_j - s_0) / sum_i exp(s_i - s_0) over the kept scores only.
+// Weights: exp(s_j - s_0) / sum_i exp(s_i - s_0) over the kept scores only
+// (default gate mode).  Two more gate modes take the same selection: the
+// bias steers the selection only and the weights are the softmax of the
+// unbiased kept scores (the Go chapter on DeepSeek-V3's bias balancing,
+// section 3 and "Pros, cons and real examples"), or the softmax runs over
+// all E scores and is read at the kept experts without renormalisation
+// (techfeed summary, "The hardest part: making the router trainable").
 // Counts: an LDS histogram per workgroup, then one integer atomic per
 // (workgroup, expert), so counts are exact and order-independent.
 #include "common.h"
@@ -24,6 +30,39 @@ namespace moe {
 
 constexpr int kRouteThreads = 256;
 constexpr int kRouteBK = 32;
+constexpr int kGateTopK = 0;         // softmax over the kept scores
+constexpr int kGateBiasSelects = 1;  // softmax over the kept unbiased scores
+constexpr int kGateSoftmaxAll = 2;   // softmax over all scores, not renormalised
+
+// Gate value of lane e's kept slot inside one EP-lane group that holds one
+// token: lane e carries expert e's biased score sc and unbiased chain acc;
+// after KeepTopK, lanes j < k carry the j-th kept expert my_e and its
+// biased score my_v, and s0 is the largest score.  Every lane of the group
+// takes part in the shuffles; lanes j >= k return an unused value.
+template <int EP>
+__device__ __forceinline__ float group_gate(int gate, int e, int E, int k, float sc,
+                                            float acc, int my_e, float my_v, float s0) {
+  if (gate == kGateSoftmaxAll) {
+    float all = e < E ? expf(sc - s0) : 0.0f;
+#pragma unroll
+    for (int off = EP / 2; off >= 1; off >>= 1) all += __shfl_xor(all, off);
+    return (e < k ? expf(my_v - s0) : 0.0f) / all;
+  }
+  float z;
+  if (gate == kGateBiasSelects) {
+    const float r = __shfl(acc, my_e, EP);   // unbiased score of the kept expert
+    float m = e < k ? r : -INFINITY;
+#pragma unroll
+    for (int off = EP / 2; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+    z = e < k ? expf(r - m) : 0.0f;
+  } else {
+    z = e < k ? expf(my_v - s0) : 0.0f;
+  }
+  float sum = z;
+#pragma unroll
+  for (int off = EP / 2; off >= 1; off >>= 1) sum += __shfl_xor(sum, off);
+  return z / sum;
+}
 
 template <typename XT>
 struct XLoad;
@@ -61,7 +100,7 @@ struct XLoad<float> {  // fp32 rows: 4 values (16 B) per load
 template <typename XT, int TX, int EPT, int TPT, int GMAX>
 __global__ __launch_bounds__(kRouteThreads) void route_kernel(
     const XT *__restrict__ x, const float *__restrict__ wg,
-    const float *__restrict__ bg, int T, int d, int E, int k, int G,
+    const float *__restrict__ bg, int T, int d, int E, int k, int gate, int G,
     int32_t *__restrict__ topk_idx, float *__restrict__ topk_w,
     int32_t *__restrict__ counts, float *__restrict__ logits) {
   constexpr int TY = kRouteThreads / TX;
@@ -193,6 +232,7 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(
     __syncthreads();
   }
   float(*ls)[EPS] = reinterpret_cast<float(*)[EPS]>(lds);
+  float(*lr)[EPS] = reinterpret_cast<float(*)[EPS]>(lds + BT * EPS);  // unbiased
 
 #pragma unroll
   for (int j = 0; j < EPT; ++j) {
@@ -204,6 +244,7 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(
       const int row = ty * TPT + r;
       const float s = bg ? acc[r][j] + b : acc[r][j];
       ls[row][e] = s;
+      if (gate == kGateBiasSelects) lr[row][e] = acc[r][j];
       if (logits && t0 + row < T) logits[(int64_t)(t0 + row) * E + e] = s;
     }
   }
@@ -266,13 +307,32 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(
     }
     float z[NQ];
     float part = 0.0f;
+    if (gate == kGateBiasSelects) {
+      // softmax of the unbiased scores of the kept experts
+      float m = -INFINITY;
+#pragma unroll
+      for (int q = 0; q < NQ; ++q)
+        if (lane + 64 * q < k) {
+          my_v[q] = lr[row][my_e[q]];
+          m = fmaxf(m, my_v[q]);
+        }
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+      s0 = m;
+    }
 #pragma unroll
     for (int q = 0; q < NQ; ++q) {
       z[q] = 0.0f;
       if (lane + 64 * q < k) {
         z[q] = expf(my_v[q] - s0);
-        part += z[q];
+        if (gate != kGateSoftmaxAll) part += z[q];
       }
+    }
+    if (gate == kGateSoftmaxAll) {
+      // denominator over all E scores
+#pragma unroll
+      for (int q = 0; q < NQ; ++q)
+        if (lane + 64 * q < E) part += expf(ls[row][lane + 64 * q] - s0);
     }
     // butterfly sum: fp32 addition is commutative, so all lanes agree
 #pragma unroll
@@ -338,7 +398,7 @@ constexpr int kBufWord3 = 0x00020000;   // raw buffer resource, gfx9 family
 template <typename XT, int EP, int NTH>
 __global__ __launch_bounds__(NTH) void route_direct_kernel(
     const XT *__restrict__ x, const float *__restrict__ wg,
-    const float *__restrict__ bg, int T, int d, int E, int k,
+    const float *__restrict__ bg, int T, int d, int E, int k, int gate,
     int32_t *__restrict__ topk_idx, float *__restrict__ topk_w,
     int32_t *__restrict__ counts, float *__restrict__ logits) {
   constexpr int TPW = kWave / EP;          // tokens per wavefront
@@ -427,14 +487,11 @@ __global__ __launch_bounds__(NTH) void route_direct_kernel(
       my_v = bv;
     }
   }
-  float z = e < k ? expf(my_v - s0) : 0.0f;
-  float sum = z;
-#pragma unroll
-  for (int off = EP / 2; off >= 1; off >>= 1) sum += __shfl_xor(sum, off);
+  const float gw = group_gate<EP>(gate, e, E, k, sc, acc, my_e, my_v, s0);
   __syncthreads();   // cnt[] zeroed
   if (t < T && e < k) {
     topk_idx[(int64_t)t * k + e] = my_e;
-    topk_w[(int64_t)t * k + e] = z / sum;
+    topk_w[(int64_t)t * k + e] = gw;
     atomicAdd(&cnt[my_e], 1);
   }
   __syncthreads();
@@ -481,7 +538,7 @@ struct LaneGeom {
 template <typename XT, int EP, int NWV>
 __global__ __launch_bounds__(NWV * kWave) void route_lane_kernel(
     const XT *__restrict__ x, const float *__restrict__ wg,
-    const float *__restrict__ bg, int T, int d, int E, int k,
+    const float *__restrict__ bg, int T, int d, int E, int k, int gate,
     int32_t *__restrict__ topk_idx, float *__restrict__ topk_w,
     int32_t *__restrict__ counts, float *__restrict__ logits) {
   using G = LaneGeom<XT, EP, NWV>;
@@ -608,14 +665,11 @@ __global__ __launch_bounds__(NWV * kWave) void route_lane_kernel(
       my_v = bv;
     }
   }
-  float z = e < k ? expf(my_v - s0) : 0.0f;
-  float sum = z;
-#pragma unroll
-  for (int off = EP / 2; off >= 1; off >>= 1) sum += __shfl_xor(sum, off);
+  const float gw = group_gate<EP>(gate, e, E, k, sc, acc, my_e, my_v, s0);
   __syncthreads();   // cnt[] zeroed
   if (t < T && e < k) {
     topk_idx[(int64_t)t * k + e] = my_e;
-    topk_w[(int64_t)t * k + e] = z / sum;
+    topk_w[(int64_t)t * k + e] = gw;
     atomicAdd(&cnt[my_e], 1);
   }
   __syncthreads();
@@ -625,18 +679,18 @@ __global__ __launch_bounds__(NWV * kWave) void route_lane_kernel(
 
 template <typename XT, int EP, int NWV>
 static hipError_t launch_route_lane(const void *x, const float *wg, const float *bg, int T,
-                                    int d, int E, int k, int32_t *idx, float *w,
+                                    int d, int E, int k, int gate, int32_t *idx, float *w,
                                     int32_t *counts, float *logits, hipStream_t s) {
   using G = LaneGeom<XT, EP, NWV>;
   const int blocks = (T + G::TPB - 1) / G::TPB;
   route_lane_kernel<XT, EP, NWV><<<blocks, G::NTH, 0, s>>>(
-      static_cast<const XT *>(x), wg, bg, T, d, E, k, idx, w, counts, logits);
+      static_cast<const XT *>(x), wg, bg, T, d, E, k, gate, idx, w, counts, logits);
   return hipGetLastError();
 }
 
 template <typename XT, int EP>
 static hipError_t launch_route_direct(const void *x, const float *wg, const float *bg,
-                                      int T, int d, int E, int k, int32_t *idx,
+                                      int T, int d, int E, int k, int gate, int32_t *idx,
                                       float *w, int32_t *counts, float *logits,
                                       hipStream_t s) {
   const int64_t waves = ((int64_t)T * EP + kWave - 1) / kWave;
@@ -644,19 +698,19 @@ static hipError_t launch_route_direct(const void *x, const float *wg, const floa
     constexpr int TPB = kWave / EP;   // tokens per one-wave workgroup
     const int blocks = (T + TPB - 1) / TPB;
     route_direct_kernel<XT, EP, kWave><<<blocks, kWave, 0, s>>>(
-        static_cast<const XT *>(x), wg, bg, T, d, E, k, idx, w, counts, logits);
+        static_cast<const XT *>(x), wg, bg, T, d, E, k, gate, idx, w, counts, logits);
   } else {
     constexpr int TPB = (kRouteThreads / kWave) * (kWave / EP);
     const int blocks = (T + TPB - 1) / TPB;
     route_direct_kernel<XT, EP, kRouteThreads><<<blocks, kRouteThreads, 0, s>>>(
-        static_cast<const XT *>(x), wg, bg, T, d, E, k, idx, w, counts, logits);
+        static_cast<const XT *>(x), wg, bg, T, d, E, k, gate, idx, w, counts, logits);
   }
   return hipGetLastError();
 }
 
 template <typename XT, int TX, int EPT, int TPT, int GMAX>
 static hipError_t launch_route_t(const void *x, const float *wg, const float *bg,
-                                 int T, int d, int E, int k, int32_t *idx,
+                                 int T, int d, int E, int k, int gate, int32_t *idx,
                                  float *w, int32_t *counts, float *logits,
                                  hipStream_t s) {
   constexpr int BT = (kRouteThreads / TX) * TPT;
@@ -671,13 +725,15 @@ static hipError_t launch_route_t(const void *x, const float *wg, const float *bg
       break;
     }
   size_t lds = sizeof(float) * 2 * (size_t)G * CHUNK;
-  if (lds < sizeof(float) * (size_t)BT * EPS) lds = sizeof(float) * (size_t)BT * EPS;
+  // scores (and the unbiased ones for the bias-selects gate) reuse the space
+  const size_t score_lds = sizeof(float) * (size_t)BT * EPS * (gate == kGateBiasSelects ? 2 : 1);
+  if (lds < score_lds) lds = score_lds;
   auto kern = route_kernel<XT, TX, EPT, TPT, GMAX>;
   hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (err != hipSuccess) return err;
   const int blocks = (T + BT - 1) / BT;
-  kern<<<blocks, kRouteThreads, lds, s>>>(static_cast<const XT *>(x), wg, bg, T, d, E, k, G,
+  kern<<<blocks, kRouteThreads, lds, s>>>(static_cast<const XT *>(x), wg, bg, T, d, E, k, gate, G,
                                           idx, w, counts, logits);
   return hipGetLastError();
 }
@@ -687,7 +743,7 @@ static hipError_t launch_route_t(const void *x, const float *wg, const float *bg
 // are (token, expert) pairs; large batches: register tiles of 4 tokens.
 template <typename XT>
 static hipError_t launch_route_dt(const void *x, const float *wg, const float *bg,
-                                  int T, int d, int E, int k, int32_t *idx,
+                                  int T, int d, int E, int k, int gate, int32_t *idx,
                                   float *w, int32_t *counts, float *logits,
                                   hipStream_t s) {
   // Up to 64 experts, one chain per lane.  Batches that give at least 64
@@ -699,8 +755,8 @@ static hipError_t launch_route_dt(const void *x, const float *wg, const float *b
 #define MOE_LANE(EP)                                                                 \
   do {                                                                               \
     if (T >= 64 * LaneGeom<XT, EP, 4>::TPB || !fits)                                 \
-      return launch_route_lane<XT, EP, 4>(x, wg, bg, T, d, E, k, idx, w, counts, logits, s); \
-    return launch_route_direct<XT, EP>(x, wg, bg, T, d, E, k, idx, w, counts, logits, s);   \
+      return launch_route_lane<XT, EP, 4>(x, wg, bg, T, d, E, k, gate, idx, w, counts, logits, s); \
+    return launch_route_direct<XT, EP>(x, wg, bg, T, d, E, k, gate, idx, w, counts, logits, s);   \
   } while (0)
   if (E <= 8) MOE_LANE(8);
   if (E <= 16) MOE_LANE(16);
@@ -708,7 +764,7 @@ static hipError_t launch_route_dt(const void *x, const float *wg, const float *b
   if (E <= 64) MOE_LANE(64);
 #undef MOE_LANE
 #define MOE_ROUTE(TX, EPT, TPT, GM) \
-  return launch_route_t<XT, TX, EPT, TPT, GM>(x, wg, bg, T, d, E, k, idx, w, counts, logits, s)
+  return launch_route_t<XT, TX, EPT, TPT, GM>(x, wg, bg, T, d, E, k, gate, idx, w, counts, logits, s)
   if (E <= 128) MOE_ROUTE(32, 4, 4, 1);
   MOE_ROUTE(32, 8, 4, 1);
 #undef MOE_ROUTE
@@ -722,14 +778,14 @@ hipError_t launch_fill_i32(int32_t *p, int n, int32_t v, hipStream_t s) {
 }
 
 // counts are zeroed here, then accumulated by the route kernel
-hipError_t launch_route(bool bf16, const void *x, const float *wg,
+hipError_t launch_route(bool bf16, int gate, const void *x, const float *wg,
                         const float *bg, int T, int d, int E, int k,
                         int32_t *idx, float *w, int32_t *counts, float *logits,
                         hipStream_t s) {
   hipError_t err = launch_fill_i32(counts, E, 0, s);
   if (err != hipSuccess || T == 0) return err;
-  return bf16 ? launch_route_dt<uint16_t>(x, wg, bg, T, d, E, k, idx, w, counts, logits, s)
-              : launch_route_dt<float>(x, wg, bg, T, d, E, k, idx, w, counts, logits, s);
+  return bf16 ? launch_route_dt<uint16_t>(x, wg, bg, T, d, E, k, gate, idx, w, counts, logits, s)
+              : launch_route_dt<float>(x, wg, bg, T, d, E, k, gate, idx, w, counts, logits, s);
 }
 
 }  // namespace moe

@@ -27,7 +27,7 @@ def test_library_exports_every_declared_entry_point():
     assert set(B.EXPORTS) == set(names), names
     for n in names:
         assert hasattr(lib, n), f"libmoe.so does not export {n}"
-    assert B.moe_abi_version() == 2
+    assert B.moe_abi_version() == 3
 
 
 def test_status_strings():
@@ -78,16 +78,19 @@ BAD_CFGS = {
     "bad_dtype": (dict(dtype=5), B.MOE_ERR_INVALID_ARGUMENT),
     "too_many_rows": (dict(T=2 ** 30, k=2), B.MOE_ERR_UNSUPPORTED),
     "capacity_negative": (dict(capacity=-1), B.MOE_ERR_INVALID_ARGUMENT),
+    "gate_negative": (dict(gate=-1), B.MOE_ERR_INVALID_ARGUMENT),
+    "gate_3": (dict(gate=3), B.MOE_ERR_INVALID_ARGUMENT),
 }
 
 FAKE = 1 << 20   # aligned non-null stand-in pointer; never dereferenced
 
 
 def _cfg(**kw):
-    base = dict(T=64, d=64, h=256, E=8, k=2, act=0, dtype=0, S=0, capacity=0)
+    base = dict(T=64, d=64, h=256, E=8, k=2, act=0, dtype=0, S=0, capacity=0, gate=0)
     base.update(kw)
     return B.config(base["T"], base["d"], base["h"], base["E"], base["k"],
-                    base["act"], base["dtype"], base["S"], base["capacity"])
+                    base["act"], base["dtype"], base["S"], base["capacity"],
+                    base["gate"])
 
 
 @pytest.mark.parametrize("name", list(BAD_CFGS))
