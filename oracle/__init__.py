@@ -72,11 +72,14 @@ def lib():
         L.oracle_load_stats.argtypes = [P, P, C.c_int, P]
         L.oracle_param_counts.argtypes = [P, P, P]
         L.oracle_set_threads.argtypes = [C.c_int]
+        L.oracle_cv2.argtypes = [P, C.c_int, P]
+        L.oracle_route_noisy.argtypes = [P, P, P, P, P, P, C.c_int64, C.c_int64,
+                                         P, P, P, P, P, P]
         for f in ("oracle_route", "oracle_counts", "oracle_permute",
                   "oracle_expert", "oracle_forward_tokens", "oracle_load_stats",
                   "oracle_param_counts", "oracle_max_threads",
                   "oracle_forward_tokens_keep", "oracle_capacity_keep",
-                  "oracle_permute_keep"):
+                  "oracle_permute_keep", "oracle_route_noisy", "oracle_cv2"):
             getattr(L, f).restype = C.c_int
         _lib = L
     return _lib
@@ -129,6 +132,28 @@ def route(layer, t0: int = 0, nt: Optional[int] = None, want_scores=False):
                             _ptr(w))
     _check(rc, "oracle_route")
     return idx, w, sc
+
+
+def route_noisy(layer, noise: np.ndarray, t0: int = 0, nt: Optional[int] = None):
+    """Noisy top-k routing of tokens [t0, t0+nt) with the given N(0,1) draws
+    noise [T, E] float32 and the layer's ``w_noise`` [E, d] float32.
+    Returns a dict: clean, scale, h (float32 [nt, E]), idx (int32 [nt, k]),
+    w (float64 [nt, k]) and p (float64 [nt, E], the smooth-load terms)."""
+    c = layer.cfg
+    nt = c.T - t0 if nt is None else nt
+    noise = np.ascontiguousarray(noise, np.float32)
+    wn = np.ascontiguousarray(layer.w_noise, np.float32)
+    assert noise.shape == (c.T, c.E) and wn.shape == (c.E, c.d)
+    out = dict(clean=np.empty((nt, c.E), np.float32), scale=np.empty((nt, c.E), np.float32),
+               h=np.empty((nt, c.E), np.float32), idx=np.empty((nt, c.k), np.int32),
+               w=np.empty((nt, c.k), np.float64), p=np.empty((nt, c.E), np.float64))
+    cfg = _cfg(c)
+    rc = lib().oracle_route_noisy(C.byref(cfg), _ptr(layer.x), _ptr(layer.w_gate),
+                                  _ptr(layer.b_gate), _ptr(wn), _ptr(noise), t0, nt,
+                                  _ptr(out["clean"]), _ptr(out["scale"]), _ptr(out["h"]),
+                                  _ptr(out["idx"]), _ptr(out["w"]), _ptr(out["p"]))
+    _check(rc, "oracle_route_noisy")
+    return out
 
 
 def counts(c, idx: np.ndarray, w: Optional[np.ndarray] = None):
@@ -230,6 +255,14 @@ def load_stats(cnt: np.ndarray, importance: Optional[np.ndarray] = None):
     _check(lib().oracle_load_stats(_ptr(cnt), _ptr(imp), int(cnt.size),
                                    _ptr(out)), "oracle_load_stats")
     return float(out[0]), float(out[1]), float(out[2])
+
+
+def cv2(v: np.ndarray) -> float:
+    """CV^2 of a per-expert vector (population variance / mean^2)."""
+    v = np.ascontiguousarray(v, np.float64)
+    out = C.c_double()
+    _check(lib().oracle_cv2(_ptr(v), int(v.size), C.byref(out)), "oracle_cv2")
+    return out.value
 
 
 def param_counts(c):

@@ -463,6 +463,14 @@ int oracle_load_stats(const int32_t *counts, const double *importance, int E,
   return 0;
 }
 
+/* CV^2 (population variance over the squared mean, 0 when the mean is 0) of
+ * any per-expert vector, e.g. the smooth Load(X). */
+int oracle_cv2(const double *v, int n, double *out) {
+  if (!v || !out || n <= 0) return -1;
+  *out = cv2(v, n);
+  return 0;
+}
+
 /* Parameter accounting: router d*E plus per-expert P_e weights (biases are
  * not counted); the shared expert, if any, is always active. */
 int oracle_param_counts(const oracle_cfg *c, int64_t *total, int64_t *active) {
@@ -479,4 +487,90 @@ int oracle_forward_tokens(const oracle_cfg *c, const oracle_weights *W,
                           const void *x, const int64_t *tokens, int64_t nt,
                           double *y, int32_t *idx, double *w) {
   return oracle_forward_tokens_keep(c, W, x, tokens, nt, NULL, y, idx, w);
+}
+
+/* ---- noisy top-k gating, the training-time form of the Qiita summary's
+ * "Gating: Noisy Top-k Softmax":
+ *   H_i = (x W_g)_i (+ b_i) + n_i * Softplus((x W_noise)_i),
+ *   G = softmax(KeepTopK(H, k)),
+ * with n_i ~ N(0, 1) given as input (the caller draws it).  Softplus is
+ * evaluated in double from the float32 noise score and rounded to float32;
+ * H is one float32 fused multiply-add, so the top-k decision is taken in
+ * float32 as for the clean scores.
+ *
+ * Smooth load (the Qiita summary's "Load-balancing losses" names Load(X) as
+ * a smooth estimate of the per-expert sample count; the estimator is that
+ * of Shazeer et al. 2017, appendix A): P(x, i) is the probability that
+ * expert i stays in the top k when only its own noise is drawn again,
+ *   P(x, i) = Phi(((x W_g)_i - kth_excluding(H, k, i)) / Softplus(...)_i),
+ * where kth_excluding is the k-th largest entry of H without entry i, and
+ * Load(X)_i = sum_x P(x, i).  With k = E every expert always stays: P = 1.
+ * A zero noise scale makes P the indicator of clean score > threshold. ---- */
+
+static double softplus_d(double v) {
+  return v > 0.0 ? v + log1p(exp(-v)) : log1p(exp(v));
+}
+
+static double normal_cdf(double z) { return 0.5 * erfc(-z * M_SQRT1_2); }
+
+/* Tokens t0 .. t0+nt-1.  Outputs (all [nt, ...]): clean float32 scores
+ * [E], noise scale Softplus(x W_noise) float32 [E], H float32 [E], kept
+ * indices [k] (stable descending order of H), their softmax weights over the
+ * kept H in double [k], and P(x, i) in double [E]. */
+int oracle_route_noisy(const oracle_cfg *c, const void *x, const float *wg,
+                       const float *bg, const float *wn, const float *noise,
+                       int64_t t0, int64_t nt, float *clean, float *scale,
+                       float *h, int32_t *idx, double *w, double *p) {
+  if (!cfg_ok(c) || !x || !wg || !wn || !noise || !clean || !scale || !h ||
+      !idx || !w || !p || t0 < 0 || nt < 0 || t0 + nt > c->T)
+    return -1;
+  if (c->gate != ORACLE_GATE_TOPK) return -1;
+  const int E = c->E, k = c->k;
+  int bad = 0;
+#pragma omp parallel reduction(| : bad)
+  {
+    float *raw = (float *)malloc(sizeof(float) * (size_t)E);
+    float *nr = (float *)malloc(sizeof(float) * (size_t)E);
+    float *nraw = (float *)malloc(sizeof(float) * (size_t)E);
+    unsigned char *tk = (unsigned char *)malloc((size_t)E);
+    int32_t *order = (int32_t *)malloc(sizeof(int32_t) * (size_t)E);
+#pragma omp for schedule(static)
+    for (int64_t r = 0; r < nt; ++r) {
+      const int64_t t = t0 + r;
+      float *cs = clean + r * E, *sc = scale + r * E, *hs = h + r * E;
+      router_scores(c, x, wg, bg, t, cs, raw);
+      router_scores(c, x, wn, NULL, t, nr, nraw);
+      for (int e = 0; e < E; ++e) {
+        sc[e] = (float)softplus_d((double)nr[e]);
+        hs[e] = fmaf(noise[t * E + e], sc[e], cs[e]);
+        if (!isfinite(cs[e]) || !isfinite(hs[e])) bad = 1;
+      }
+      /* the full stable descending order of H; the first k are kept */
+      keep_top_k(hs, E, E, order, tk);
+      memcpy(idx + r * k, order, sizeof(int32_t) * (size_t)k);
+      kept_softmax(hs, idx + r * k, k, w + r * k);
+      for (int e = 0; e < E; ++e) tk[e] = 0;
+      for (int j = 0; j < k; ++j) tk[order[j]] = 1;
+      double *pr = p + r * E;
+      for (int e = 0; e < E; ++e) {
+        if (k == E) {
+          pr[e] = 1.0;
+          continue;
+        }
+        /* k-th largest of H without entry e */
+        const double thr = (double)hs[order[tk[e] ? k : k - 1]];
+        const double diff = (double)cs[e] - thr;
+        if (sc[e] == 0.0f)
+          pr[e] = diff > 0.0 ? 1.0 : 0.0;
+        else
+          pr[e] = normal_cdf(diff / (double)sc[e]);
+      }
+    }
+    free(raw);
+    free(nr);
+    free(nraw);
+    free(tk);
+    free(order);
+  }
+  return bad ? -2 : 0;
 }

@@ -14,6 +14,10 @@ so any expert can be regenerated alone and experts are drawn in parallel):
   child 3 + e   expert e: W_up[e] [N_up, d] then W_down[e] [d, h] ~ N(0, 0.02)
   child 3 + E   shared expert: W_up_s [2h, d] then W_down_s [d, h]
 
+Noisy gating (training-time routing) draws from SeedSequence([seed, 1]),
+spawned into two streams: W_noise [E, d] ~ N(0, 0.02) float32, then the
+standard-normal noise [T, E] float32 (``make_noisy_gate``).
+
 Every draw is float32; bf16 layers round each value to bfloat16 with
 round-to-nearest-even and store the 16-bit patterns as ``uint16``.
 GELU experts of the tiny layer carry zero-filled biases b1 [E, h], b2 [E, d].
@@ -157,3 +161,14 @@ def make_inputs(cfg: LayerConfig, workers: Optional[int] = None,
 
     return LayerInputs(cfg, x, w_gate, b_gate, w_up, w_down, b_up, b_down,
                        w_up_s, w_down_s)
+
+
+def make_noisy_gate(cfg: LayerConfig):
+    """(w_noise [E, d] float32, noise [T, E] float32) for noisy top-k gating
+    of ``cfg``: the noise-scale router ~ N(0, 0.02) and the N(0, 1) draws."""
+    a, b = np.random.SeedSequence([cfg.seed, 1]).spawn(2)
+    w_noise = (np.random.Generator(np.random.PCG64(a))
+               .standard_normal((cfg.E, cfg.d), dtype=np.float32) * np.float32(WEIGHT_STD))
+    noise = np.random.Generator(np.random.PCG64(b)).standard_normal((cfg.T, cfg.E),
+                                                                   dtype=np.float32)
+    return w_noise, noise

@@ -58,6 +58,17 @@ MUTANTS = {
         "for (int e = 0; e < E; ++e) z += exp((double)score[e] - m);",
         "for (int e = 1; e < E; ++e) z += exp((double)score[e] - m);"),
     "gate_mode_ignored": ("if (c->gate == ORACLE_GATE_BIAS_SELECTS)", "if (0)"),
+    "noisy_h_unfused": ("hs[e] = fmaf(noise[t * E + e], sc[e], cs[e]);",
+                        "hs[e] = cs[e] + noise[t * E + e] * sc[e];"),
+    "noise_transposed": ("hs[e] = fmaf(noise[t * E + e], sc[e], cs[e]);",
+                         "hs[e] = fmaf(noise[e * c->T + t], sc[e], cs[e]);"),
+    "softplus_missing_log": ("v > 0.0 ? v + log1p(exp(-v)) : log1p(exp(v));",
+                             "v > 0.0 ? v + log1p(exp(-v)) : exp(v);"),
+    "noisy_threshold_not_excluding": ("order[tk[e] ? k : k - 1]", "order[k - 1]"),
+    "smooth_load_uses_noisy_score": ("const double diff = (double)cs[e] - thr;",
+                                     "const double diff = (double)hs[e] - thr;"),
+    "smooth_load_cdf_sign": ("return 0.5 * erfc(-z * M_SQRT1_2);",
+                             "return 0.5 * erfc(z * M_SQRT1_2);"),
 }
 
 

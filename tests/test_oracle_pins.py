@@ -12,6 +12,7 @@ import os
 import numpy as np
 import pytest
 import scipy.special
+import scipy.stats
 import torch
 
 import synthetic
@@ -585,3 +586,156 @@ def test_unknown_gate_mode_rejected(oracle_lib):
     L = _with_gate(random_layer(24, T=3, d=8, h=8, E=4, k=2), 3)
     with pytest.raises(ValueError):
         oracle_lib.route(L)
+
+
+# ---- noisy top-k gating, training form (Qiita summary, "Gating: Noisy Top-k
+# Softmax"): H = clean + n * Softplus(x W_noise), G = softmax(KeepTopK(H, k)),
+# and the smooth Load(X) ("Load-balancing losses"; estimator of Shazeer et
+# al. 2017, appendix A) ----
+
+def _noisy_identity(clean, nraw, noise, k, bias=None):
+    """x = [clean | nraw], W_g = [I | 0], W_noise = [0 | I]: the clean and
+    noise scores are exactly the given values."""
+    clean = np.asarray(clean, np.float32)
+    T, E = clean.shape
+    x = np.concatenate([clean, np.asarray(nraw, np.float32)], 1)
+    wg = np.concatenate([np.eye(E), np.zeros((E, E))], 1).astype(np.float32)
+    L = layer(T, 2 * E, 4, E, k, x=x, w_gate=wg, b_gate=bias,
+              w_up=np.zeros((E, 4, 2 * E)), w_down=np.zeros((E, 2 * E, 4)))
+    L.w_noise = np.concatenate([np.zeros((E, E)), np.eye(E)], 1).astype(np.float32)
+    return L, np.ascontiguousarray(noise, np.float32)
+
+
+def _noisy_random(seed, T, E, k, d=24, bias=True):
+    L = random_layer(seed, T=T, d=d, h=8, E=E, k=k, act=SWIGLU, bias=bias)
+    rng = np.random.default_rng(seed + 100)
+    L.w_noise = (rng.standard_normal((E, d)) * 0.3).astype(np.float32)
+    return L, rng.standard_normal((T, E)).astype(np.float32)
+
+
+def test_noisy_gate_with_zero_noise_is_the_inference_gate(oracle_lib):
+    """n = 0 removes the noise term: the clean scores, kept experts and
+    weights are exactly those of the deterministic router."""
+    L, n = _noisy_random(41, T=30, E=8, k=2)
+    r = oracle_lib.route_noisy(L, np.zeros_like(n))
+    idx, w, sc = oracle_lib.route(L, want_scores=True)
+    np.testing.assert_array_equal(r["clean"], sc)
+    np.testing.assert_array_equal(r["h"], sc)
+    np.testing.assert_array_equal(r["idx"], idx)
+    np.testing.assert_array_equal(r["w"], w)
+
+
+def test_noise_scale_is_softplus(oracle_lib):
+    """Scale = Softplus(x W_noise) = log(1 + e^v) (numpy logaddexp) rounded
+    to float32; W_noise = 0 gives ln 2; a very negative v gives 0."""
+    L, n = _noisy_random(42, T=40, E=6, k=2)
+    r = oracle_lib.route_noisy(L, n)
+    Ln = random_layer(42, T=40, d=24, h=8, E=6, k=2, act=SWIGLU)
+    Ln.w_gate = L.w_noise
+    _, _, nraw = oracle_lib.route(Ln, want_scores=True)
+    ref = np.logaddexp(0.0, nraw.astype(np.float64)).astype(np.float32)
+    np.testing.assert_allclose(r["scale"], ref, rtol=1.2e-7, atol=0)
+    L0, n0 = _noisy_identity([[1.0, 2.0, -3.0]], [[0.0, -200.0, 50.0]], [[1.0, 1.0, 1.0]], 1)
+    s = oracle_lib.route_noisy(L0, n0)["scale"][0]
+    assert s[0] == np.float32(math.log(2.0)) and s[1] == 0.0 and s[2] == np.float32(50.0)
+
+
+def _round_f32(q):
+    """The float32 nearest to the rational q (ties to even)."""
+    from fractions import Fraction
+    c = np.float32(float(q))
+    best = None
+    for v in (np.nextafter(c, np.float32(-np.inf)), c, np.nextafter(c, np.float32(np.inf))):
+        dist = abs(Fraction(float(v)) - q)
+        if best is None or dist < best[0] or (dist == best[0] and int(v.view(np.uint32)) % 2 == 0):
+            best = (dist, v)
+    return best[1]
+
+
+def test_noisy_scores_are_one_fused_multiply_add(oracle_lib):
+    """H = clean + n * scale with a single rounding (exact rational sum
+    rounded to the nearest float32)."""
+    from fractions import Fraction
+    L, n = _noisy_random(43, T=50, E=8, k=2)
+    r = oracle_lib.route_noisy(L, n)
+    for t in range(50):
+        for e in range(8):
+            q = Fraction(float(r["clean"][t, e])) + Fraction(float(n[t, e])) * Fraction(float(r["scale"][t, e]))
+            assert r["h"][t, e] == _round_f32(q), (t, e)
+
+
+@pytest.mark.parametrize("k", [1, 2, 5])
+def test_noisy_topk_and_kept_softmax(oracle_lib, k):
+    """Kept experts = stable descending order of H (numpy), weights = scipy
+    softmax over the kept H."""
+    L, n = _noisy_random(44 + k, T=60, E=8, k=k)
+    r = oracle_lib.route_noisy(L, n)
+    order = np.argsort(-r["h"].astype(np.float64), axis=1, kind="stable")[:, :k]
+    np.testing.assert_array_equal(r["idx"], order)
+    ref = scipy.special.softmax(np.take_along_axis(r["h"], order, 1).astype(np.float64), axis=1)
+    np.testing.assert_allclose(r["w"], ref, rtol=1e-13, atol=0)
+
+
+def test_smooth_load_two_experts_closed_form(oracle_lib):
+    """E = 2, k = 1: expert 0 stays chosen while its noisy score beats H_1,
+    so P(x, 0) = Phi((clean_0 - H_1) / scale_0), and symmetrically."""
+    rng = np.random.default_rng(45)
+    clean = rng.standard_normal((20, 2)).astype(np.float32)
+    nraw = rng.standard_normal((20, 2)).astype(np.float32)
+    noise = rng.standard_normal((20, 2)).astype(np.float32)
+    L, n = _noisy_identity(clean, nraw, noise, 1)
+    r = oracle_lib.route_noisy(L, n)
+    h, s = r["h"].astype(np.float64), r["scale"].astype(np.float64)
+    c = clean.astype(np.float64)
+    np.testing.assert_allclose(r["p"][:, 0], scipy.stats.norm.cdf((c[:, 0] - h[:, 1]) / s[:, 0]),
+                               rtol=1e-12, atol=1e-300)
+    np.testing.assert_allclose(r["p"][:, 1], scipy.stats.norm.cdf((c[:, 1] - h[:, 0]) / s[:, 1]),
+                               rtol=1e-12, atol=1e-300)
+
+
+def test_smooth_load_is_the_probability_of_staying_in_the_top_k(oracle_lib):
+    """Brute force: redraw expert i's noise 200000 times with the other
+    noisy scores fixed and count how often i is among the first k of a
+    stable descending order; P(x, i) agrees within the Monte Carlo error."""
+    L, n = _noisy_random(46, T=4, E=6, k=2)
+    r = oracle_lib.route_noisy(L, n)
+    rng = np.random.default_rng(47)
+    draws = rng.standard_normal(200000)
+    for t in range(4):
+        h = r["h"][t].astype(np.float64)
+        for i in range(6):
+            hi = r["clean"][t, i] + draws * float(r["scale"][t, i])
+            others = np.delete(np.arange(6), i)
+            ahead = np.zeros(draws.size, np.int64)
+            for j in others:
+                ahead += (h[j] > hi) | ((h[j] == hi) & (j < i))
+            p_mc = float(np.mean(ahead < 2))
+            p = float(r["p"][t, i])
+            assert abs(p - p_mc) <= 5 * math.sqrt(max(p * (1 - p), 1e-6) / draws.size) + 1e-4, (t, i, p, p_mc)
+
+
+def test_smooth_load_edge_cases(oracle_lib):
+    """k = E: every expert always stays (P = 1).  A zero noise scale makes P
+    the indicator of clean score > threshold."""
+    L, n = _noisy_random(48, T=10, E=4, k=4)
+    assert np.all(oracle_lib.route_noisy(L, n)["p"] == 1.0)
+    clean = [[3.0, 2.0, 1.0, 0.0]]
+    L, n = _noisy_identity(clean, [[-200.0] * 4], [[1.0] * 4], 2)
+    r = oracle_lib.route_noisy(L, n)
+    assert r["scale"].max() == 0.0 and r["idx"][0].tolist() == [0, 1]
+    # kept 0, 1: thresholds H_2 = 1 (excluding a kept one); unkept: H_1 = 2
+    assert r["p"][0].tolist() == [1.0, 1.0, 0.0, 0.0]
+
+
+def test_smooth_load_and_importance_sums(oracle_lib):
+    """Load = column sums of P, Importance = sums of the kept weights; with
+    k = E Load is T for every expert (CV^2 0)."""
+    L, n = _noisy_random(49, T=64, E=8, k=2)
+    r = oracle_lib.route_noisy(L, n)
+    cnt, imp = oracle_lib.counts(L.cfg, r["idx"], r["w"])
+    assert cnt.sum() == 128 and imp.sum() == pytest.approx(64.0, rel=1e-12)
+    load = r["p"].sum(0)
+    assert np.all(load > 0) and np.all(load < 64)
+    assert oracle_lib.cv2(np.full(8, 64.0)) == 0.0
+    v = np.array([1.0, 3.0])
+    assert oracle_lib.cv2(v) == pytest.approx(0.25, rel=1e-15)   # var 1, mean 2
