@@ -117,8 +117,8 @@ typedef struct {
 int moe_abi_version(void);
 const char *moe_status_string(moe_status_t status);
 
-/* Workspace bytes needed by moe_forward (also enough for moe_permute and
- * moe_expert_ffn).  Pure host; *bytes is 0 when T == 0. */
+/* Workspace bytes needed by moe_forward (also enough for moe_permute,
+ * moe_expert_ffn and moe_route_noisy).  Pure host; *bytes is 0 when T == 0. */
 moe_status_t moe_workspace_bytes(const moe_config_t *cfg, size_t *bytes);
 
 /* Rows of the grouped (expert-sorted) buffers: R = T*k + S*T.  Rows
@@ -143,6 +143,38 @@ moe_status_t moe_route(const moe_config_t *cfg, const void *x,
                        const float *w_gate, const float *b_gate,
                        int32_t *topk_idx, float *topk_w, int32_t *counts,
                        float *logits, hipStream_t stream);
+
+/* Noisy top-k gating, the training-time gate of the Qiita summary ("Gating:
+ * Noisy Top-k Softmax"): H_i = s_i + n_i * Softplus((x W_noise)_i), where s
+ * is the router score of moe_route (bias included) and n ~ N(0, 1) is drawn
+ * by the caller; G = softmax(KeepTopK(H, k)).  Softplus is evaluated in
+ * double from the fp32 noise score and rounded to fp32; H is one fp32 fused
+ * multiply-add.  Also the smooth Load of the same summary ("Load-balancing
+ * losses": a smooth estimate of each expert's sample count), with the
+ * estimator of Shazeer et al.: P(x, i) = Phi((s_i - t_i) / Softplus_i), t_i
+ * the k-th largest H without entry i (P = 1 when k = E; a zero scale gives
+ * the indicator of s_i > t_i); Load_i = sum over tokens of P(x, i).
+ * cfg->gate must be MOE_GATE_TOPK_SOFTMAX (else MOE_ERR_UNSUPPORTED).
+ *   x, w_gate, b_gate   as for moe_route     (device, in)
+ *   w_noise      [E, d] fp32                 (device, in)
+ *   noise        [T, E] fp32 N(0,1) draws    (device, in)
+ *   clean_logits [T, E] fp32 (out) s, the moe_route scores
+ *   noise_scale  [T, E] fp32 (out) Softplus(x W_noise^T)
+ *   topk_idx, topk_w [T, k] (out) kept experts in descending H order (ties
+ *                to the lower index) and their softmax over the kept H
+ *   counts [E] int32 (out); importance [E] fp32 (out) sum of the kept
+ *                weights; load [E] fp32 (out) the smooth Load
+ *   cv2    [2] fp64 or NULL (out) CV^2(Importance), CV^2(Load)
+ *   workspace    >= moe_workspace_bytes(cfg) bytes (device, scratch)
+ * Sums are taken in a fixed order: results are deterministic. */
+moe_status_t moe_route_noisy(const moe_config_t *cfg, const void *x,
+                             const float *w_gate, const float *b_gate,
+                             const float *w_noise, const float *noise,
+                             float *clean_logits, float *noise_scale,
+                             int32_t *topk_idx, float *topk_w, int32_t *counts,
+                             float *importance, float *load, double *cv2,
+                             void *workspace, size_t workspace_bytes,
+                             hipStream_t stream);
 
 /* Dispatch: stable grouping of the T*k assignments by expert (ties by the
  * flat index t*k + j) and the row move x -> x_perm ("Expert Backend":

@@ -34,6 +34,7 @@ EXPORTS = (
     "moe_grouped_rows", "moe_route", "moe_permute", "moe_expert_up",
     "moe_expert_down", "moe_expert_ffn", "moe_combine", "moe_forward",
     "moe_param_counts", "moe_load_stats", "moe_expert_capacity",
+    "moe_route_noisy",
 )
 
 
@@ -78,6 +79,8 @@ def lib():
             "moe_workspace_bytes": [P, P],
             "moe_grouped_rows": [P, P],
             "moe_route": [P, P, P, P, P, P, P, P, P],
+            "moe_route_noisy": [P, P, P, P, P, P, P, P, P, P, P, P, P, P, P,
+                                C.c_size_t, P],
             "moe_permute": [P, P, P, P, P, P, P, P, P, P, P, C.c_size_t, P],
             "moe_expert_up": [P, P, P, P, P, P, P],
             "moe_expert_down": [P, P, P, P, P, P],
@@ -181,6 +184,17 @@ def moe_route(cfg, x, w_gate, b_gate, topk_idx, topk_w, counts, logits=None,
     _check("moe_route", lib().moe_route(
         C.byref(cfg), _ptr(x), _ptr(w_gate), _ptr(b_gate), _ptr(topk_idx),
         _ptr(topk_w), _ptr(counts), _ptr(logits), _stream(stream)))
+
+
+def moe_route_noisy(cfg, x, w_gate, b_gate, w_noise, noise, clean_logits, noise_scale,
+                    topk_idx, topk_w, counts, importance, load, cv2, ws, ws_bytes=None,
+                    stream=None) -> None:
+    nb = _nbytes(ws) if ws_bytes is None and ws is not None else (ws_bytes or 0)
+    _check("moe_route_noisy", lib().moe_route_noisy(
+        C.byref(cfg), _ptr(x), _ptr(w_gate), _ptr(b_gate), _ptr(w_noise), _ptr(noise),
+        _ptr(clean_logits), _ptr(noise_scale), _ptr(topk_idx), _ptr(topk_w),
+        _ptr(counts), _ptr(importance), _ptr(load), _ptr(cv2), _ptr(ws), nb,
+        _stream(stream)))
 
 
 def moe_permute(cfg, topk_idx, topk_w, x, offsets, perm_src, pos, importance,

@@ -14,6 +14,11 @@ hipError_t launch_route(bool bf16, int gate, const void *x, const float *wg, con
                         int T, int d, int E, int k, int32_t *idx, float *w,
                         int32_t *counts, float *logits, hipStream_t s);
 int perm_num_segments(int64_t n);
+int64_t noisy_workspace_bytes(int64_t T, int E);
+hipError_t launch_noisy_gate(const float *noise, int T, int E, int k, const float *clean,
+                             float *scale, int32_t *idx, float *w, int32_t *counts,
+                             float *importance, float *load, double *cv2, float *part,
+                             hipStream_t s);
 hipError_t launch_permute(const int32_t *idx, const float *w, const void *x, int T,
                           int k, int E, int capacity, int row_bytes, int32_t *offsets,
                           int32_t *perm_src, int32_t *pos, float *importance,
@@ -118,6 +123,9 @@ Layout layout(const moe_config_t *c) {
   L.hidden = o;    o += align_up(es * (size_t)R * c->d_hidden);
   L.y_perm = o;    o += align_up(es * (size_t)R * c->d_model);
   L.total = o;
+  // moe_route_noisy uses the front of the workspace for its partial sums
+  const size_t noisy = align_up((size_t)moe::noisy_workspace_bytes(T, E));
+  if (L.total < noisy) L.total = noisy;
   return L;
 }
 
@@ -185,6 +193,45 @@ moe_status_t moe_route(const moe_config_t *cfg, const void *x, const float *w_ga
                                       b_gate, T,
                                       cfg->d_model, cfg->num_experts, cfg->top_k,
                                       topk_idx, topk_w, counts, logits, stream));
+}
+
+moe_status_t moe_route_noisy(const moe_config_t *cfg, const void *x, const float *w_gate,
+                             const float *b_gate, const float *w_noise, const float *noise,
+                             float *clean_logits, float *noise_scale, int32_t *topk_idx,
+                             float *topk_w, int32_t *counts, float *importance, float *load,
+                             double *cv2, void *workspace, size_t workspace_bytes,
+                             hipStream_t stream) {
+  moe_status_t st = check_cfg(cfg);
+  if (st != MOE_OK) return st;
+  if (cfg->gate != MOE_GATE_TOPK_SOFTMAX) return MOE_ERR_UNSUPPORTED;
+  if (!dev_ok(counts) || !dev_ok(importance) || !dev_ok(load) || !opt_ok(cv2))
+    return MOE_ERR_INVALID_ARGUMENT;
+  const int T = (int)cfg->num_tokens, E = cfg->num_experts;
+  if (T > 0 && (!dev_ok(x) || !dev_ok(w_gate) || !opt_ok(b_gate) || !dev_ok(w_noise) ||
+                !dev_ok(noise) || !dev_ok(clean_logits) || !dev_ok(noise_scale) ||
+                !dev_ok(topk_idx) || !dev_ok(topk_w)))
+    return MOE_ERR_INVALID_ARGUMENT;
+  const size_t need = (size_t)moe::noisy_workspace_bytes(T, E);
+  if (T > 0 && !dev_ok(workspace)) return MOE_ERR_INVALID_ARGUMENT;
+  if (T > 0 && workspace_bytes < need) return MOE_ERR_WORKSPACE_TOO_SMALL;
+  clear_pending_error();
+  const bool bf16 = cfg->dtype == MOE_DTYPE_BF16;
+  hipError_t e = hipSuccess;
+  if (T > 0) {
+    // the router chains: raw noise scores into noise_scale, clean scores
+    // (with the bias) into clean_logits; the indices, weights and counts
+    // they also write are replaced by the noisy gate below
+    e = moe::launch_route(bf16, MOE_GATE_TOPK_SOFTMAX, x, w_noise, nullptr, T, cfg->d_model,
+                          E, cfg->top_k, topk_idx, topk_w, counts, noise_scale, stream);
+    if (e == hipSuccess)
+      e = moe::launch_route(bf16, MOE_GATE_TOPK_SOFTMAX, x, w_gate, b_gate, T, cfg->d_model,
+                            E, cfg->top_k, topk_idx, topk_w, counts, clean_logits, stream);
+  }
+  if (e == hipSuccess)
+    e = moe::launch_noisy_gate(noise, T, E, cfg->top_k, clean_logits, noise_scale, topk_idx,
+                               topk_w, counts, importance, load, cv2,
+                               T > 0 ? static_cast<float *>(workspace) : nullptr, stream);
+  return hip_status(e);
 }
 
 moe_status_t moe_permute(const moe_config_t *cfg, const int32_t *topk_idx,

@@ -110,6 +110,8 @@ def test_every_entry_point_rejects_bad_config(name):
         L.moe_combine(r, FAKE, FAKE, FAKE, FAKE, None),
         L.moe_forward(r, C.byref(w), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, 1 << 40, None),
         L.moe_param_counts(r, C.byref(C.c_int64()), C.byref(C.c_int64())),
+        L.moe_route_noisy(r, FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                          FAKE, FAKE, None, FAKE, 1 << 40, None),
     ]
     assert calls == [status] * len(calls)
 
@@ -153,3 +155,25 @@ def test_expert_capacity_matches_oracle():
     assert L.moe_expert_capacity(16, 2, 0, 1.0, C.byref(out)) == inv
     assert L.moe_expert_capacity(16, 2, 8, 1.0, None) == inv
     assert L.moe_expert_capacity(2 ** 40, 8, 1, 1.0, C.byref(out)) == B.MOE_ERR_UNSUPPORTED
+
+
+def test_noisy_route_checks():
+    L = B.lib()
+    inv, small = B.MOE_ERR_INVALID_ARGUMENT, B.MOE_ERR_WORKSPACE_TOO_SMALL
+    cfg = _cfg()
+    r = C.byref(cfg)
+    args = [FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None]
+    # only the default gate takes noise
+    sel = _cfg(gate=1)
+    assert L.moe_route_noisy(C.byref(sel), *args, FAKE, 1 << 40, None) == B.MOE_ERR_UNSUPPORTED
+    # W_noise and the noise draws are required
+    bad = list(args)
+    bad[3] = None
+    assert L.moe_route_noisy(r, *bad, FAKE, 1 << 40, None) == inv
+    bad = list(args)
+    bad[4] = FAKE + 4
+    assert L.moe_route_noisy(r, *bad, FAKE, 1 << 40, None) == inv
+    # workspace: partial sums of 2 x E floats per 16 tokens
+    assert L.moe_route_noisy(r, *args, FAKE, 4 * 2 * 8 * 4 - 1, None) == small
+    assert L.moe_route_noisy(r, *args, None, 1 << 40, None) == inv
+    assert B.moe_workspace_bytes(cfg) >= 4 * 2 * 8 * 4
