@@ -26,6 +26,9 @@ PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 METRIC = "MoE layer tokens/s + grouped-GEMM TFLOP/s (% MFMA peak); decode HBM GB/s"
 
 
+GATES = {"topk-softmax": 0, "bias-selects": 1, "softmax-all": 2}
+
+
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
@@ -35,6 +38,11 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=15.0,
                    help="target CPU time of the oracle baseline sample")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--gate", choices=list(GATES), default="topk-softmax",
+                   help="gate mode: softmax over the kept k, bias that selects only, "
+                        "or softmax over all experts")
+    p.add_argument("--noisy", action="store_true",
+                   help="training-time noisy top-k gate (moe_route_noisy) in the step")
     p.add_argument("--capacity-factor", type=float, default=0.0,
                    help="per-expert capacity ceil(f*T*k/E) with drops (0: none)")
     p.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "traffic.txt"),
@@ -78,9 +86,13 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
-    cfg = synthetic.BY_NAME[args.workload]
+    cfg = synthetic.BY_NAME[args.workload].with_(gate=GATES[args.gate])
+    if args.noisy and cfg.gate != 0:
+        sys.exit("--noisy takes the default gate only")
     t_gen = time.time()
     L = synthetic.make_inputs(cfg)
+    if args.noisy:
+        L.w_noise, noise_np = synthetic.make_noisy_gate(cfg)
     cap = 0
     if args.capacity_factor > 0:
         cap = B.moe_expert_capacity(cfg.T, cfg.k, cfg.E, args.capacity_factor)
@@ -105,9 +117,24 @@ def main():
     y_perm = torch.empty((R, d), dtype=dt, device=dev)
     y = torch.empty((T, d), dtype=dt, device=dev)
     ws = torch.empty(B.moe_workspace_bytes(c), dtype=torch.uint8, device=dev)
+    if args.noisy:
+        from sparse_mixture_experts_07_amd.device import to_device
+        w_noise, noise = to_device(L.w_noise, dev), to_device(noise_np, dev)
+        clean = torch.empty((T, E), dtype=torch.float32, device=dev)
+        nscale = torch.empty((T, E), dtype=torch.float32, device=dev)
+        nimp = torch.empty(E, dtype=torch.float32, device=dev)
+        nload = torch.empty(E, dtype=torch.float32, device=dev)
+        ncv2 = torch.empty(2, dtype=torch.float64, device=dev)
+
+    def route():
+        if args.noisy:
+            B.moe_route_noisy(c, dl.x, dl.w_gate, dl.b_gate, w_noise, noise, clean, nscale,
+                              idx, tw, counts, nimp, nload, ncv2, ws)
+        else:
+            B.moe_route(c, dl.x, dl.w_gate, dl.b_gate, idx, tw, counts)
 
     def step(ev=None):
-        B.moe_route(c, dl.x, dl.w_gate, dl.b_gate, idx, tw, counts)
+        route()
         B.moe_permute(c, idx, tw, dl.x, offsets, perm_src, pos, imp, stats, x_perm, ws)
         if ev is not None:
             ev[0].record()
@@ -118,13 +145,16 @@ def main():
         B.moe_combine(c, y_perm, pos, tw, y)
 
     # the stage sequence is the moe_forward sequence: check once, bitwise
-    fw = Forward(dl)
-    fw()
-    step()
-    torch.cuda.synchronize()
-    same = torch.equal(fw.y.view(torch.int16 if dt == torch.bfloat16 else torch.int32),
-                       y.view(torch.int16 if dt == torch.bfloat16 else torch.int32))
-    del fw
+    # (the noisy gate routes differently from moe_forward: not compared)
+    same = None
+    if not args.noisy:
+        fw = Forward(dl)
+        fw()
+        step()
+        torch.cuda.synchronize()
+        same = torch.equal(fw.y.view(torch.int16 if dt == torch.bfloat16 else torch.int32),
+                           y.view(torch.int16 if dt == torch.bfloat16 else torch.int32))
+        del fw
 
     for _ in range(args.warmup):
         step()
@@ -179,7 +209,8 @@ def main():
             roof["traffic_over_algorithmic_bytes"] = rec["traffic_bytes"] / up_bytes
 
     cpu = None
-    if not args.no_cpu_baseline:
+    # the oracle's token loop has no noisy gate: no CPU baseline for --noisy
+    if not args.no_cpu_baseline and not args.noisy:
         import oracle
         nthr = oracle.max_threads()
         probe = list(range(min(T, max(2, nthr))))
@@ -216,6 +247,8 @@ def main():
                    "experts": E, "top_k": k, "shared": cfg.S,
                    "act": "swiglu" if cfg.act == synthetic.SWIGLU else "gelu",
                    "router_bias": cfg.router_bias,
+                   **({"gate": args.gate} if cfg.gate else {}),
+                   **({"noisy_gate": True} if args.noisy else {}),
                    **({"capacity_factor": args.capacity_factor, "capacity": cap}
                       if cap else {})},
         "roofline": roof,

@@ -17,7 +17,7 @@ int perm_num_segments(int64_t n);
 int64_t noisy_workspace_bytes(int64_t T, int E);
 hipError_t launch_noisy_gate(const float *noise, int T, int E, int k, const float *clean,
                              float *scale, int32_t *idx, float *w, int32_t *counts,
-                             float *importance, float *load, double *cv2, float *part,
+                             float *importance, float *load, double *cv2, void *ws,
                              hipStream_t s);
 hipError_t launch_permute(const int32_t *idx, const float *w, const void *x, int T,
                           int k, int E, int capacity, int row_bytes, int32_t *offsets,
@@ -230,7 +230,7 @@ moe_status_t moe_route_noisy(const moe_config_t *cfg, const void *x, const float
   if (e == hipSuccess)
     e = moe::launch_noisy_gate(noise, T, E, cfg->top_k, clean_logits, noise_scale, topk_idx,
                                topk_w, counts, importance, load, cv2,
-                               T > 0 ? static_cast<float *>(workspace) : nullptr, stream);
+                               T > 0 ? workspace : nullptr, stream);
   return hip_status(e);
 }
 

@@ -17,7 +17,7 @@
 //   Softplus_i), t_i the k-th largest H without entry i, which is the
 //   (k+1)-th largest H when i is kept and the k-th largest otherwise.
 // Importance and Load are summed per workgroup in a fixed order, then over
-// workgroups in a fixed order by one reduction workgroup: deterministic.
+// workgroups in a fixed order by one wavefront per expert: deterministic.
 #include "common.h"
 
 #pragma clang fp contract(off)
@@ -172,44 +172,52 @@ __global__ __launch_bounds__(kNoisyThreads) void noisy_topk_kernel(
   }
 }
 
-// One workgroup: thread e sums expert e's partials over the workgroups in
-// order (fp64), then thread 0 forms CV^2 of Importance and of Load
-// (population variance / mean^2, 0 when the mean is 0).
-__global__ __launch_bounds__(kMaxExperts) void noisy_reduce_kernel(
+// One wavefront per expert: lane l sums the partials of workgroups l, l+64,
+// ... in order (fp64), then a fixed butterfly; sums[e] and sums[E+e] keep
+// the fp64 totals for the CV^2 kernel.
+__global__ __launch_bounds__(kWave) void noisy_reduce_kernel(
     const float *__restrict__ part, int nblk, int E, float *__restrict__ importance,
-    float *__restrict__ load, double *__restrict__ cv2) {
-  __shared__ double si[kMaxExperts], sl[kMaxExperts];
-  const int e = threadIdx.x;
-  if (e < E) {
-    double a = 0.0, b = 0.0;
-    for (int blk = 0; blk < nblk; ++blk) {
-      a += part[(int64_t)blk * 2 * E + e];
-      b += part[(int64_t)blk * 2 * E + E + e];
-    }
+    float *__restrict__ load, double *__restrict__ sums) {
+  const int e = blockIdx.x;
+  const int lane = threadIdx.x;
+  double a = 0.0, b = 0.0;
+  for (int blk = lane; blk < nblk; blk += kWave) {
+    a += part[(int64_t)blk * 2 * E + e];
+    b += part[(int64_t)blk * 2 * E + E + e];
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    a += __shfl_xor(a, off);
+    b += __shfl_xor(b, off);
+  }
+  if (lane == 0) {
     importance[e] = (float)a;
     load[e] = (float)b;
-    si[e] = a;
-    sl[e] = b;
+    sums[e] = a;
+    sums[E + e] = b;
   }
-  __syncthreads();
-  if (e == 0 && cv2) {
-    double ma = 0.0, mb = 0.0;
-    for (int i = 0; i < E; ++i) {
-      ma += si[i];
-      mb += sl[i];
-    }
-    ma /= E;
-    mb /= E;
-    double va = 0.0, vb = 0.0;
-    for (int i = 0; i < E; ++i) {
-      va += (si[i] - ma) * (si[i] - ma);
-      vb += (sl[i] - mb) * (sl[i] - mb);
-    }
-    va /= E;
-    vb /= E;
-    cv2[0] = ma == 0.0 ? 0.0 : va / (ma * ma);
-    cv2[1] = mb == 0.0 ? 0.0 : vb / (mb * mb);
+}
+
+// CV^2 of Importance and of Load (population variance / mean^2, 0 when the
+// mean is 0) from the fp64 totals, in expert order.
+__global__ void noisy_cv2_kernel(const double *__restrict__ sums, int E, double *__restrict__ cv2) {
+  if (threadIdx.x != 0) return;
+  double ma = 0.0, mb = 0.0;
+  for (int i = 0; i < E; ++i) {
+    ma += sums[i];
+    mb += sums[E + i];
   }
+  ma /= E;
+  mb /= E;
+  double va = 0.0, vb = 0.0;
+  for (int i = 0; i < E; ++i) {
+    va += (sums[i] - ma) * (sums[i] - ma);
+    vb += (sums[E + i] - mb) * (sums[E + i] - mb);
+  }
+  va /= E;
+  vb /= E;
+  cv2[0] = ma == 0.0 ? 0.0 : va / (ma * ma);
+  cv2[1] = mb == 0.0 ? 0.0 : vb / (mb * mb);
 }
 
 __global__ void noisy_zero_kernel(float *importance, float *load, int E, double *cv2) {
@@ -223,9 +231,10 @@ __global__ void noisy_zero_kernel(float *importance, float *load, int E, double 
   }
 }
 
+// Workspace: the fp64 totals [2E], then the partials [nblk][2][E] fp32.
 int64_t noisy_workspace_bytes(int64_t T, int E) {
   const int64_t nblk = (T + kNoisyTPB - 1) / kNoisyTPB;
-  return nblk * 2 * E * (int64_t)sizeof(float);
+  return 2 * E * (int64_t)sizeof(double) + nblk * 2 * E * (int64_t)sizeof(float);
 }
 
 hipError_t launch_fill_i32(int32_t *p, int n, int32_t v, hipStream_t s);
@@ -234,7 +243,7 @@ hipError_t launch_fill_i32(int32_t *p, int n, int32_t v, hipStream_t s);
 // written: zero the counts, then the gate and the reduction.
 hipError_t launch_noisy_gate(const float *noise, int T, int E, int k, const float *clean,
                              float *scale, int32_t *idx, float *w, int32_t *counts,
-                             float *importance, float *load, double *cv2, float *part,
+                             float *importance, float *load, double *cv2, void *ws,
                              hipStream_t s) {
   hipError_t err = launch_fill_i32(counts, E, 0, s);
   if (err != hipSuccess) return err;
@@ -243,6 +252,8 @@ hipError_t launch_noisy_gate(const float *noise, int T, int E, int k, const floa
     return hipGetLastError();
   }
   const int nblk = (T + kNoisyTPB - 1) / kNoisyTPB;
+  double *sums = static_cast<double *>(ws);
+  float *part = reinterpret_cast<float *>(sums + 2 * E);
   if (E <= 64)
     noisy_topk_kernel<1><<<nblk, kNoisyThreads, 0, s>>>(noise, T, E, k, clean, scale, idx, w,
                                                         counts, part);
@@ -252,7 +263,8 @@ hipError_t launch_noisy_gate(const float *noise, int T, int E, int k, const floa
   else
     noisy_topk_kernel<4><<<nblk, kNoisyThreads, 0, s>>>(noise, T, E, k, clean, scale, idx, w,
                                                         counts, part);
-  noisy_reduce_kernel<<<1, kMaxExperts, 0, s>>>(part, nblk, E, importance, load, cv2);
+  noisy_reduce_kernel<<<E, kWave, 0, s>>>(part, nblk, E, importance, load, sums);
+  if (cv2) noisy_cv2_kernel<<<1, kWave, 0, s>>>(sums, E, cv2);
   return hipGetLastError();
 }
 

@@ -173,7 +173,8 @@ def test_noisy_route_checks():
     bad = list(args)
     bad[4] = FAKE + 4
     assert L.moe_route_noisy(r, *bad, FAKE, 1 << 40, None) == inv
-    # workspace: partial sums of 2 x E floats per 16 tokens
-    assert L.moe_route_noisy(r, *args, FAKE, 4 * 2 * 8 * 4 - 1, None) == small
+    # workspace: 2E fp64 totals, then 2E fp32 partial sums per 16 tokens
+    need = 2 * 8 * 8 + 4 * 2 * 8 * 4
+    assert L.moe_route_noisy(r, *args, FAKE, need - 1, None) == small
     assert L.moe_route_noisy(r, *args, None, 1 << 40, None) == inv
-    assert B.moe_workspace_bytes(cfg) >= 4 * 2 * 8 * 4
+    assert B.moe_workspace_bytes(cfg) >= need
