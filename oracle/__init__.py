@@ -273,3 +273,6 @@ def param_counts(c):
     _check(lib().oracle_param_counts(C.byref(cfg), C.byref(tot), C.byref(act)),
            "oracle_param_counts")
     return tot.value, act.value
+
+
+from . import backward  # noqa: E402  (float64 autograd backward, imports route)

@@ -1,0 +1,94 @@
+"""Pins of the float64 autograd backward in oracle/backward.py (CPU only).
+
+The differentiated function is the layer forward with the oracle's float32
+selection held fixed; it is pinned to the C oracle's forward, and its
+gradients to finite differences (torch.autograd.gradcheck) and to exact
+invariances of the gate."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from helpers import GELU, SWIGLU, random_layer
+
+B = oracle.backward
+
+
+def _layer(seed, act, S=0, bias=True, expert_bias=False, T=7, d=6, h=5, E=4, k=2):
+    return random_layer(seed, T=T, d=d, h=h, E=E, k=k, act=act, S=S, bias=bias,
+                        expert_bias=expert_bias)
+
+
+@pytest.mark.parametrize("act,S,eb", [(GELU, 0, True), (SWIGLU, 0, False), (SWIGLU, 1, False)])
+def test_forward_matches_the_c_oracle(act, S, eb):
+    """The float64 torch forward is the C oracle's forward (up to the fp32
+    vs fp64 router scores), with and without an expert capacity."""
+    L = _layer(1, act, S, expert_bias=eb, T=30, d=16, h=12, E=5, k=2)
+    idx, _, _ = oracle.route(L)
+    p = B.params(L)
+    y, g, imp = B.forward(L, p, idx)
+    yc, _, wc = oracle.forward_tokens(L, range(30))
+    np.testing.assert_allclose(y.detach().numpy(), yc, rtol=1e-6, atol=1e-7 * np.abs(yc).max())
+    np.testing.assert_allclose(g.detach().numpy(), wc, rtol=1e-6)
+    _, rimp = oracle.counts(L.cfg, idx, wc)
+    np.testing.assert_allclose(imp.detach().numpy(), rimp, rtol=1e-6)
+    keep = oracle.capacity_keep(L.cfg, idx, 8)
+    assert 0 < keep.sum() < keep.size
+    yk, _, _ = B.forward(L, p, idx, keep)
+    yck, _, _ = oracle.forward_tokens(L, range(30), keep=keep)
+    np.testing.assert_allclose(yk.detach().numpy(), yck, rtol=1e-6, atol=1e-7 * np.abs(yck).max())
+
+
+@pytest.mark.parametrize("act,S,eb,imp_w,cap", [
+    (GELU, 0, True, 0.0, 0), (SWIGLU, 0, False, 0.0, 0), (SWIGLU, 1, False, 0.0, 0),
+    (SWIGLU, 0, False, 0.7, 0), (GELU, 0, True, 0.3, 3), (SWIGLU, 1, False, 0.5, 4)])
+def test_gradients_match_finite_differences(act, S, eb, imp_w, cap):
+    """torch.autograd.gradcheck of <dy, y> + w * CV^2(Importance) in every
+    input, with the selection fixed (and an expert capacity)."""
+    L = _layer(2, act, S, expert_bias=eb)
+    idx, _, _ = oracle.route(L)
+    keep = oracle.capacity_keep(L.cfg, idx, cap) if cap else None
+    if cap:
+        assert 0 < keep.sum() < keep.size
+    dy = torch.from_numpy(np.random.default_rng(3).standard_normal((L.cfg.T, L.cfg.d)))
+    p = B.params(L)
+    names = list(p)
+
+    def f(*ts):
+        return B.loss(L, dict(zip(names, ts)), idx, dy, keep, imp_w)
+
+    assert torch.autograd.gradcheck(f, tuple(p[n] for n in names), eps=1e-6, atol=1e-6, rtol=1e-5)
+    g = B.backward(L, dy.numpy(), keep, imp_w, idx=idx)
+    assert set(g) == set(names)
+
+
+def test_bias_gradient_sums_to_zero_and_top1_router_gets_none():
+    """Adding one constant to every router bias changes no kept softmax, so
+    the bias gradients sum to 0; with k = 1 the gate is 1 whatever the
+    scores, so the router gets no gradient at all."""
+    L = _layer(4, SWIGLU, 1, T=20, d=8, h=6, E=6, k=3)
+    dy = np.random.default_rng(5).standard_normal((20, 8))
+    g = B.backward(L, dy, importance_weight=0.4)
+    assert abs(g["b_gate"].sum()) <= 1e-12 * np.abs(g["b_gate"]).sum()
+    assert np.abs(g["w_gate"]).max() > 0
+    L1 = _layer(6, GELU, 0, expert_bias=True, T=10, d=8, h=6, E=4, k=1)
+    g1 = B.backward(L1, np.random.default_rng(7).standard_normal((10, 8)), importance_weight=0.0)
+    assert np.all(g1["w_gate"] == 0) and np.all(g1["b_gate"] == 0)
+
+
+def test_gradients_are_linear_in_dy_and_dropped_slots_get_none():
+    """Gradients of <dy, y> are linear in dy; an expert whose every slot is
+    dropped by the capacity gets no weight gradient."""
+    L = _layer(8, SWIGLU, 0, T=12, d=6, h=4, E=3, k=2)
+    rng = np.random.default_rng(9)
+    d1, d2 = rng.standard_normal((12, 6)), rng.standard_normal((12, 6))
+    g1, g2 = B.backward(L, d1), B.backward(L, d2)
+    g12 = B.backward(L, 2.0 * d1 - d2)
+    for n in g1:
+        np.testing.assert_allclose(g12[n], 2.0 * g1[n] - g2[n], rtol=1e-10, atol=1e-12)
+    idx, _, _ = oracle.route(L)
+    keep = np.ones(12 * 2, np.uint8)
+    keep[(idx == 1).reshape(-1)] = 0
+    gk = B.backward(L, d1, keep=keep, idx=idx)
+    assert np.all(gk["w_up"][1] == 0) and np.all(gk["w_down"][1] == 0)
+    assert np.abs(gk["w_up"][0]).max() > 0
