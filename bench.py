@@ -43,6 +43,8 @@ def parse():
                         "or softmax over all experts")
     p.add_argument("--noisy", action="store_true",
                    help="training-time noisy top-k gate (moe_route_noisy) in the step")
+    p.add_argument("--backward", action="store_true",
+                   help="training step: the forward stages, then moe_backward")
     p.add_argument("--capacity-factor", type=float, default=0.0,
                    help="per-expert capacity ceil(f*T*k/E) with drops (0: none)")
     p.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "traffic.txt"),
@@ -133,6 +135,24 @@ def main():
         else:
             B.moe_route(c, dl.x, dl.w_gate, dl.b_gate, idx, tw, counts)
 
+    if args.backward:
+        if cfg.dtype != synthetic.BF16:
+            sys.exit("--backward: bf16 layers only")
+        f32 = dict(dtype=torch.float32, device=dev)
+        n_up = cfg.n_up
+        g_t = dict(dx=torch.empty((T, d), dtype=dt, device=dev),
+                   w_gate=torch.empty((E, d), **f32), w_up=torch.empty((E, n_up, d), **f32),
+                   w_down=torch.empty((E, d, h), **f32),
+                   b_gate=torch.empty(E, **f32) if L.b_gate is not None else None,
+                   w_up_shared=torch.empty((1, n_up, d), **f32) if cfg.S else None,
+                   w_down_shared=torch.empty((1, d, h), **f32) if cfg.S else None)
+        grads = B.grads(g_t["dx"], g_t["w_gate"], g_t["w_up"], g_t["w_down"], g_t["b_gate"],
+                        dw_up_shared=g_t["w_up_shared"], dw_down_shared=g_t["w_down_shared"])
+        ws_b = torch.empty(B.moe_backward_workspace_bytes(c), dtype=torch.uint8, device=dev)
+        dy = torch.randn((T, d), generator=torch.Generator(device="cpu").manual_seed(1)).to(
+            device=dev, dtype=dt)
+        bwd_evs = []
+
     def step(ev=None):
         route()
         B.moe_permute(c, idx, tw, dl.x, offsets, perm_src, pos, imp, stats, x_perm, ws)
@@ -143,6 +163,15 @@ def main():
             ev[1].record()
         B.moe_expert_down(c, W, hidden, offsets, y_perm)
         B.moe_combine(c, y_perm, pos, tw, y)
+        if args.backward:
+            if ev is not None:
+                bwd_evs.append((torch.cuda.Event(enable_timing=True),
+                                torch.cuda.Event(enable_timing=True)))
+                bwd_evs[-1][0].record()
+            B.moe_backward(c, W, dl.x, dy, idx, tw, offsets, pos, x_perm, y_perm, imp, 0.01,
+                           grads, ws_b)
+            if ev is not None:
+                bwd_evs[-1][1].record()
 
     # the stage sequence is the moe_forward sequence: check once, bitwise
     # (the noisy gate routes differently from moe_forward: not compared)
@@ -260,8 +289,18 @@ def main():
         "dropped_fraction": 1.0 - kept / (T * k) if T else 0.0,
         "wall_s_timed": wall,
         "input_gen_upload_s": gen_s,
-        "stage_sequence_equals_moe_forward": bool(same),
+        "stage_sequence_equals_moe_forward": same,
     }
+    if args.backward:
+        bwd_ms = float(np.mean([a.elapsed_time(b) for a, b in bwd_evs]))
+        # algorithmic backward work: dX and dW of both projections, twice
+        # the forward's expert FLOPs (the pre-activation recomputation and
+        # the transposes are overhead, not counted)
+        bflops = 2.0 * layer_flops
+        out["config"]["training_step"] = True
+        out["backward"] = {"ms": bwd_ms, "tflops": bflops / (bwd_ms / 1e3) / 1e12,
+                           "frac_mfma_peak": bflops / (bwd_ms / 1e3) / 1e12 / PEAK_BF16_TFLOPS,
+                           "importance_loss_weight": 0.01}
     print(json.dumps(out))
 
 

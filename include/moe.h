@@ -245,6 +245,50 @@ moe_status_t moe_forward(const moe_config_t *cfg, const moe_weights_t *w,
                          double *stats, void *ws, size_t ws_bytes,
                          hipStream_t stream);
 
+/* Backward pass: gradients of <dy, y> + importance_weight * CV^2(Importance)
+ * with the top-k selection of the forward held fixed (the selection has no
+ * derivative, so the router learns through the softmax weights only:
+ * techfeed summary, "The hardest part: making the router trainable";
+ * Importance and its CV^2: Qiita summary, "Load-balancing losses").  The
+ * expert pre-activations are recomputed from x_perm (no activation storage
+ * in the forward).  bf16 layers and MOE_GATE_TOPK_SOFTMAX only (else
+ * MOE_ERR_UNSUPPORTED); an expert capacity is honoured through pos (a
+ * dropped slot passes no gradient to its expert; its gate still counts in
+ * Importance).  Gradients are fp32 except dx (the layer dtype).
+ *   x [T, d], dy [T, d]                  (device, in)
+ *   saved from the forward (device, in): topk_idx, topk_w [T, k] (moe_route),
+ *     offsets [E+1], pos [T*k], x_perm (moe_permute), y_perm [T*k + S*T, d]
+ *     (the expert outputs, moe_expert_down / moe_expert_ffn)
+ *   importance [E] fp32 or NULL (moe_permute's), importance_weight: the
+ *     weight of the CV^2(Importance) term (ignored when importance is NULL)
+ *   grads: every pointer device memory, written in full:
+ *     dx [T, d] dtype; dw_gate [E, d]; db_gate [E] or NULL; dw_up, dw_down
+ *     with the shapes of w_up, w_down; db_up [E, h], db_down [E, d] or NULL
+ *     (GELU); dw_up_shared [1, 2h, d], dw_down_shared [1, d, h] iff S = 1
+ *   ws >= moe_backward_workspace_bytes(cfg) bytes (device, scratch)
+ * Sums run in a fixed order: results are deterministic. */
+typedef struct {
+  void *dx;
+  float *dw_gate;
+  float *db_gate;
+  float *dw_up;
+  float *dw_down;
+  float *db_up;
+  float *db_down;
+  float *dw_up_shared;
+  float *dw_down_shared;
+} moe_grads_t;
+
+moe_status_t moe_backward_workspace_bytes(const moe_config_t *cfg, size_t *bytes);
+
+moe_status_t moe_backward(const moe_config_t *cfg, const moe_weights_t *w,
+                          const void *x, const void *dy, const int32_t *topk_idx,
+                          const float *topk_w, const int32_t *offsets,
+                          const int32_t *pos, const void *x_perm, const void *y_perm,
+                          const float *importance, float importance_weight,
+                          const moe_grads_t *grads, void *ws, size_t ws_bytes,
+                          hipStream_t stream);
+
 /* Host-only helpers. */
 
 /* Parameter accounting of the Go chapter's section 1: Total = d*E + E*P_e,

@@ -34,7 +34,7 @@ EXPORTS = (
     "moe_grouped_rows", "moe_route", "moe_permute", "moe_expert_up",
     "moe_expert_down", "moe_expert_ffn", "moe_combine", "moe_forward",
     "moe_param_counts", "moe_load_stats", "moe_expert_capacity",
-    "moe_route_noisy",
+    "moe_route_noisy", "moe_backward_workspace_bytes", "moe_backward",
 )
 
 
@@ -79,6 +79,9 @@ def lib():
             "moe_workspace_bytes": [P, P],
             "moe_grouped_rows": [P, P],
             "moe_route": [P, P, P, P, P, P, P, P, P],
+            "moe_backward_workspace_bytes": [P, P],
+            "moe_backward": [P, P, P, P, P, P, P, P, P, P, P, C.c_float, P, P,
+                             C.c_size_t, P],
             "moe_route_noisy": [P, P, P, P, P, P, P, P, P, P, P, P, P, P, P,
                                 C.c_size_t, P],
             "moe_permute": [P, P, P, P, P, P, P, P, P, P, P, C.c_size_t, P],
@@ -184,6 +187,36 @@ def moe_route(cfg, x, w_gate, b_gate, topk_idx, topk_w, counts, logits=None,
     _check("moe_route", lib().moe_route(
         C.byref(cfg), _ptr(x), _ptr(w_gate), _ptr(b_gate), _ptr(topk_idx),
         _ptr(topk_w), _ptr(counts), _ptr(logits), _stream(stream)))
+
+
+class MoeGrads(C.Structure):
+    _fields_ = [("dx", C.c_void_p), ("dw_gate", C.c_void_p), ("db_gate", C.c_void_p),
+                ("dw_up", C.c_void_p), ("dw_down", C.c_void_p), ("db_up", C.c_void_p),
+                ("db_down", C.c_void_p), ("dw_up_shared", C.c_void_p),
+                ("dw_down_shared", C.c_void_p)]
+
+
+def grads(dx, dw_gate, dw_up, dw_down, db_gate=None, db_up=None, db_down=None,
+          dw_up_shared=None, dw_down_shared=None) -> MoeGrads:
+    return MoeGrads(_ptr(dx), _ptr(dw_gate), _ptr(db_gate), _ptr(dw_up), _ptr(dw_down),
+                    _ptr(db_up), _ptr(db_down), _ptr(dw_up_shared), _ptr(dw_down_shared))
+
+
+def moe_backward_workspace_bytes(cfg: MoeConfig) -> int:
+    n = C.c_size_t()
+    _check("moe_backward_workspace_bytes",
+           lib().moe_backward_workspace_bytes(C.byref(cfg), C.byref(n)))
+    return n.value
+
+
+def moe_backward(cfg, w: MoeWeights, x, dy, topk_idx, topk_w, offsets, pos, x_perm, y_perm,
+                 importance, importance_weight: float, g: MoeGrads, ws, ws_bytes=None,
+                 stream=None) -> None:
+    nb = _nbytes(ws) if ws_bytes is None and ws is not None else (ws_bytes or 0)
+    _check("moe_backward", lib().moe_backward(
+        C.byref(cfg), C.byref(w), _ptr(x), _ptr(dy), _ptr(topk_idx), _ptr(topk_w),
+        _ptr(offsets), _ptr(pos), _ptr(x_perm), _ptr(y_perm), _ptr(importance),
+        float(importance_weight), C.byref(g), _ptr(ws), nb, _stream(stream)))
 
 
 def moe_route_noisy(cfg, x, w_gate, b_gate, w_noise, noise, clean_logits, noise_scale,

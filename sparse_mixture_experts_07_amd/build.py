@@ -13,7 +13,7 @@ LIB = os.path.join(HERE, "libmoe.so")
 OBJ = os.path.join(HERE, "_build")
 
 SOURCES = ["route.hip", "permute.hip", "gemm_bf16.hip", "gemm_f32.hip",
-           "combine.hip", "noisy.hip", "api.cpp"]
+           "combine.hip", "noisy.hip", "backward.hip", "api.cpp"]
 
 # packed fp32 instructions are kept out of the device code (-packed-fp32-ops)
 HIPFLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",

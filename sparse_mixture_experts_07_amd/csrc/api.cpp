@@ -7,6 +7,7 @@
 #include <cstring>
 
 #include "moe.h"
+#include "backward.h"
 
 namespace moe {
 hipError_t launch_fill_i32(int32_t *p, int n, int32_t v, hipStream_t s);
@@ -144,6 +145,69 @@ moe_status_t hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ER
 // Pending errors of earlier, unrelated HIP calls are cleared so that a
 // launch status reflects this call only.
 void clear_pending_error() { (void)hipGetLastError(); }
+
+// Backward workspace regions, each 256-byte aligned, in this order.
+struct BwdLayout {
+  size_t gimp, ds, dsp, ds_cols, poff, colsrc;
+  size_t off_all, src_all, pos_all, hist, full_off, perm_w, imp_all;
+  size_t w1t, w2t, w1ts, w2ts, A, H, dyp, dH, dA, dxp, dypT, HT, dAT, xpT, total;
+};
+
+BwdLayout bwd_layout(const moe_config_t *c) {
+  const int64_t T = c->num_tokens, k = c->top_k, E = c->num_experts, S = c->num_shared;
+  const int64_t d = c->d_model, h = c->d_hidden;
+  const int64_t nup = c->act == MOE_ACT_SWIGLU ? 2 * h : h;
+  const int64_t R = T * k + S * T;
+  const int64_t Rp = moe::bwd_padded_cols(T, (int)k, (int)E, (int)S);
+  BwdLayout L{};
+  size_t o = 0;
+  auto take = [&](size_t &f, int64_t bytes) {
+    f = o;
+    o += align_up((size_t)bytes);
+  };
+  take(L.gimp, 4 * E);
+  take(L.ds, 4 * T * k);
+  take(L.dsp, 4 * T * k);
+  take(L.ds_cols, 4 * Rp);
+  take(L.poff, 4 * (E + S + 1));
+  take(L.colsrc, 4 * Rp);
+  const bool cap = c->capacity > 0;   // every assignment regrouped
+  take(L.off_all, cap ? 4 * (E + 1) : 0);
+  take(L.src_all, cap ? 4 * T * k : 0);
+  take(L.pos_all, cap ? 4 * T * k : 0);
+  take(L.hist, cap ? 4 * (int64_t)moe::perm_num_segments(T * k) * E : 0);
+  take(L.full_off, cap ? 4 * (E + 1) : 0);
+  take(L.perm_w, cap ? 4 * T * k : 0);
+  take(L.imp_all, cap ? 4 * E : 0);
+  take(L.w1t, 2 * E * nup * d);
+  take(L.w2t, 2 * E * h * d);
+  take(L.w1ts, 2 * S * nup * d);
+  take(L.w2ts, 2 * S * h * d);
+  take(L.A, 2 * R * nup);
+  take(L.H, 2 * R * h);
+  take(L.dyp, 2 * R * d);
+  take(L.dH, 2 * R * h);
+  take(L.dA, 2 * R * nup);
+  take(L.dxp, 2 * R * d);
+  take(L.dypT, 2 * d * Rp);
+  take(L.HT, 2 * h * Rp);
+  take(L.dAT, 2 * nup * Rp);
+  take(L.xpT, 2 * d * Rp);
+  L.total = o;
+  return L;
+}
+
+moe_status_t check_bwd_cfg(const moe_config_t *cfg) {
+  moe_status_t st = check_cfg(cfg);
+  if (st != MOE_OK) return st;
+  if (cfg->dtype != MOE_DTYPE_BF16 || cfg->gate != MOE_GATE_TOPK_SOFTMAX)
+    return MOE_ERR_UNSUPPORTED;
+  const int64_t Rp = moe::bwd_padded_cols(cfg->num_tokens, cfg->top_k, cfg->num_experts,
+                                          cfg->num_shared);
+  if (Rp >= (int64_t(1) << 31) / 512) return MOE_ERR_UNSUPPORTED;   // 32-bit tile offsets
+  return MOE_OK;
+}
+
 
 }  // namespace
 
@@ -370,6 +434,120 @@ moe_status_t moe_forward(const moe_config_t *cfg, const moe_weights_t *w, const 
   if ((st = moe_expert_up(cfg, w, x_perm, x, offsets, hidden, stream)) != MOE_OK) return st;
   if ((st = moe_expert_down(cfg, w, hidden, offsets, y_perm, stream)) != MOE_OK) return st;
   return moe_combine(cfg, y_perm, pos, topk_w, y, stream);
+}
+
+moe_status_t moe_backward_workspace_bytes(const moe_config_t *cfg, size_t *bytes) {
+  moe_status_t st = check_bwd_cfg(cfg);
+  if (st != MOE_OK) return st;
+  if (!bytes) return MOE_ERR_INVALID_ARGUMENT;
+  *bytes = cfg->num_tokens == 0 ? 0 : bwd_layout(cfg).total;
+  return MOE_OK;
+}
+
+moe_status_t moe_backward(const moe_config_t *cfg, const moe_weights_t *w, const void *x,
+                          const void *dy, const int32_t *topk_idx, const float *topk_w,
+                          const int32_t *offsets, const int32_t *pos, const void *x_perm,
+                          const void *y_perm, const float *importance,
+                          float importance_weight, const moe_grads_t *g, void *ws,
+                          size_t ws_bytes, hipStream_t stream) {
+  moe_status_t st = check_bwd_cfg(cfg);
+  if (st != MOE_OK) return st;
+  if ((st = check_weights(cfg, w, true, true, true)) != MOE_OK) return st;
+  if (!g || !dev_ok(g->dw_gate) || !dev_ok(g->dw_up) || !dev_ok(g->dw_down) ||
+      !opt_ok(g->db_gate) || !opt_ok(g->db_up) || !opt_ok(g->db_down) ||
+      !opt_ok(importance) || !std::isfinite(importance_weight))
+    return MOE_ERR_INVALID_ARGUMENT;
+  const bool swi = cfg->act == MOE_ACT_SWIGLU;
+  if (swi && (g->db_up || g->db_down)) return MOE_ERR_INVALID_ARGUMENT;
+  if (cfg->num_shared ? (!dev_ok(g->dw_up_shared) || !dev_ok(g->dw_down_shared))
+                      : (g->dw_up_shared || g->dw_down_shared))
+    return MOE_ERR_INVALID_ARGUMENT;
+  const int64_t T = cfg->num_tokens;
+  const int E = cfg->num_experts, S = cfg->num_shared;
+  const int64_t d = cfg->d_model, h = cfg->d_hidden, nup = swi ? 2 * h : h;
+  clear_pending_error();
+  if (T == 0) {
+    hipError_t e = moe::launch_fill_f32(g->dw_gate, E * d, stream);
+    if (e == hipSuccess) e = moe::launch_fill_f32(g->db_gate, E, stream);
+    if (e == hipSuccess) e = moe::launch_fill_f32(g->dw_up, E * nup * d, stream);
+    if (e == hipSuccess) e = moe::launch_fill_f32(g->dw_down, E * d * h, stream);
+    if (e == hipSuccess) e = moe::launch_fill_f32(g->db_up, E * h, stream);
+    if (e == hipSuccess) e = moe::launch_fill_f32(g->db_down, E * d, stream);
+    if (e == hipSuccess) e = moe::launch_fill_f32(g->dw_up_shared, S * nup * d, stream);
+    if (e == hipSuccess) e = moe::launch_fill_f32(g->dw_down_shared, S * d * h, stream);
+    return hip_status(e);
+  }
+  if (!dev_ok(x) || !dev_ok(dy) || !dev_ok(topk_idx) || !dev_ok(topk_w) || !dev_ok(offsets) ||
+      !dev_ok(pos) || !dev_ok(x_perm) || !dev_ok(y_perm) || !dev_ok(g->dx))
+    return MOE_ERR_INVALID_ARGUMENT;
+  const BwdLayout L = bwd_layout(cfg);
+  if (!dev_ok(ws)) return MOE_ERR_INVALID_ARGUMENT;
+  if (ws_bytes < L.total) return MOE_ERR_WORKSPACE_TOO_SMALL;
+  moe::BwdArgs a{};
+  a.T = (int)T;
+  a.k = cfg->top_k;
+  a.E = E;
+  a.S = S;
+  a.d = (int)d;
+  a.h = (int)h;
+  a.swiglu = swi;
+  a.capacity = cfg->capacity;
+  a.x = static_cast<const uint16_t *>(x);
+  a.dy = static_cast<const uint16_t *>(dy);
+  a.w_up = static_cast<const uint16_t *>(w->w_up);
+  a.w_down = static_cast<const uint16_t *>(w->w_down);
+  a.b_up = static_cast<const uint16_t *>(w->b_up);
+  a.w_up_s = static_cast<const uint16_t *>(w->w_up_shared);
+  a.w_down_s = static_cast<const uint16_t *>(w->w_down_shared);
+  a.w_gate = w->w_gate;
+  a.idx = topk_idx;
+  a.offsets = offsets;
+  a.pos = pos;
+  a.topk_w = topk_w;
+  a.importance = importance;
+  a.w_imp = importance_weight;
+  a.x_perm = static_cast<const uint16_t *>(x_perm);
+  a.y_perm = static_cast<const uint16_t *>(y_perm);
+  a.dx = static_cast<uint16_t *>(g->dx);
+  a.dw_gate = g->dw_gate;
+  a.db_gate = g->db_gate;
+  a.dw_up = g->dw_up;
+  a.dw_down = g->dw_down;
+  a.db_up = g->db_up;
+  a.db_down = g->db_down;
+  a.dw_up_s = g->dw_up_shared;
+  a.dw_down_s = g->dw_down_shared;
+  moe::BwdBuffers b{};
+  b.gimp = at<float>(ws, L.gimp);
+  b.ds = at<float>(ws, L.ds);
+  b.dsp = at<float>(ws, L.dsp);
+  b.ds_cols = at<float>(ws, L.ds_cols);
+  b.poff = at<int32_t>(ws, L.poff);
+  b.colsrc = at<int32_t>(ws, L.colsrc);
+  if (cfg->capacity > 0) {
+    b.off_all = at<int32_t>(ws, L.off_all);
+    b.src_all = at<int32_t>(ws, L.src_all);
+    b.pos_all = at<int32_t>(ws, L.pos_all);
+    b.hist = at<int32_t>(ws, L.hist);
+    b.full_off = at<int32_t>(ws, L.full_off);
+    b.perm_w = at<float>(ws, L.perm_w);
+    b.imp_all = at<float>(ws, L.imp_all);
+  }
+  b.w1t = at<uint16_t>(ws, L.w1t);
+  b.w2t = at<uint16_t>(ws, L.w2t);
+  b.w1ts = S ? at<uint16_t>(ws, L.w1ts) : nullptr;
+  b.w2ts = S ? at<uint16_t>(ws, L.w2ts) : nullptr;
+  b.A = at<uint16_t>(ws, L.A);
+  b.H = at<uint16_t>(ws, L.H);
+  b.dyp = at<uint16_t>(ws, L.dyp);
+  b.dH = at<uint16_t>(ws, L.dH);
+  b.dA = at<uint16_t>(ws, L.dA);
+  b.dxp = at<uint16_t>(ws, L.dxp);
+  b.dypT = at<uint16_t>(ws, L.dypT);
+  b.HT = at<uint16_t>(ws, L.HT);
+  b.dAT = at<uint16_t>(ws, L.dAT);
+  b.xpT = at<uint16_t>(ws, L.xpT);
+  return hip_status(moe::launch_backward(a, b, stream));
 }
 
 moe_status_t moe_param_counts(const moe_config_t *cfg, int64_t *total, int64_t *active) {

@@ -1,0 +1,38 @@
+// backward.h - host-side interface of backward.hip (shared with api.cpp).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+namespace moe {
+
+int64_t bwd_padded_cols(int64_t T, int k, int E, int S);
+hipError_t launch_fill_f32(float *p, int64_t n, hipStream_t s);
+
+struct BwdBuffers {
+  float *gimp, *ds, *dsp, *ds_cols;
+  int32_t *poff, *colsrc;
+  // regrouping of every assignment (router gradient under a capacity)
+  int32_t *off_all, *src_all, *pos_all, *hist, *full_off;
+  float *perm_w, *imp_all;
+  uint16_t *w1t, *w2t, *w1ts, *w2ts;
+  uint16_t *A, *H, *dyp, *dH, *dA, *dxp;
+  uint16_t *dypT, *HT, *dAT, *xpT;
+};
+
+struct BwdArgs {
+  int T, k, E, S, d, h, swiglu, capacity;
+  const uint16_t *x, *dy, *w_up, *w_down, *b_up, *w_up_s, *w_down_s;
+  const float *w_gate;
+  const int32_t *idx, *offsets, *pos;
+  const float *topk_w, *importance;
+  float w_imp;
+  const uint16_t *x_perm, *y_perm;
+  uint16_t *dx;
+  float *dw_gate, *db_gate, *dw_up, *dw_down, *db_up, *db_down, *dw_up_s, *dw_down_s;
+};
+
+hipError_t launch_backward(const BwdArgs &a, const BwdBuffers &b, hipStream_t s);
+
+}  // namespace moe

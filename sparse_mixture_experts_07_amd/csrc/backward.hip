@@ -1,0 +1,596 @@
+// backward.hip - the backward pass of the layer: the gradient of
+// <dy, y> + w_imp * CV^2(Importance) with the top-k selection held fixed
+// (the selection has no derivative; the router learns through the softmax
+// weights: techfeed summary, "The hardest part: making the router
+// trainable"; Importance and CV^2: Qiita summary, "Load-balancing losses").
+//
+// The grouped GEMMs of the backward pass run in gemm_bf16.hip (dH = dY W2,
+// dX = dA W1 on transposed weight copies, the weight gradients over each
+// group's rows); this file holds the rest, all bf16 storage with fp32
+// arithmetic:
+//   gate     per token: dw_j = <dy, Y_j> (Y_j the expert's output row),
+//            dY_j = w_j dy (the expert's output gradient, kept slots only),
+//            ds_j = w_j (dw'_j - sum_i w_i dw'_i), dw'_j = dw_j + the
+//            Importance term of expert i_j (softmax over the kept scores)
+//   act      H = act(A) from the recomputed pre-activations A; dA = act'(A) dH
+//   layout   group columns padded to 32 for the transposed copies, and the
+//            grouped row behind every column
+//   transpose activations [R, C] -> [C, Rp] (group columns, zero padding),
+//            weights [B, R, C] -> [B, C, R]
+//   sums     per-group weighted row sums (bias and router gradients)
+//   dx       dx = sum_j dX[pos_j] + dX_shared + sum_j ds_j W_g[i_j]
+// Every sum runs in a fixed order: results are deterministic.
+#include "common.h"
+#include "backward.h"
+
+#pragma clang fp contract(off)
+
+namespace moe {
+
+constexpr int kBwdThreads = 256;
+
+__device__ __forceinline__ float bf16_lo(uint32_t v) { return __uint_as_float(v << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t v) { return __uint_as_float(v & 0xffff0000u); }
+
+// Sum over the workgroup in a fixed order (wave butterflies, then the waves
+// in order); every thread gets the total.  red: kBwdThreads / 64 floats.
+__device__ __forceinline__ float block_sum(float v, float *red) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
+  const int wave = threadIdx.x / kWave;
+  __syncthreads();
+  if (threadIdx.x % kWave == 0) red[wave] = v;
+  __syncthreads();
+  float s = 0.0f;
+#pragma unroll
+  for (int w = 0; w < kBwdThreads / kWave; ++w) s += red[w];
+  return s;
+}
+
+// Importance term of the gate gradient: d CV^2 / d I_e scaled by w_imp,
+// CV^2 = V / m^2 with m the mean and V the population variance of I:
+// g_e = w_imp * 2 (I_e - m - V / m) / (E m^2); zero when m = 0.
+__global__ void bwd_importance_grad_kernel(const float *__restrict__ importance, int E,
+                                           float w_imp, float *__restrict__ gimp) {
+  __shared__ double mv[2];
+  if (threadIdx.x == 0) {
+    double m = 0.0;
+    for (int e = 0; e < E; ++e) m += importance[e];
+    m /= E;
+    double v = 0.0;
+    for (int e = 0; e < E; ++e) v += (importance[e] - m) * (importance[e] - m);
+    mv[0] = m;
+    mv[1] = v / E;
+  }
+  __syncthreads();
+  const double m = mv[0], v = mv[1];
+  for (int e = threadIdx.x; e < E; e += blockDim.x)
+    gimp[e] = (m == 0.0 || w_imp == 0.0)
+                  ? 0.0f
+                  : (float)(w_imp * 2.0 * (importance[e] - m - v / m) / (E * m * m));
+}
+
+// One workgroup per token.  dyp: [T*k + S*T, d] expert output gradients
+// (rows of dropped slots are not written); ds: [T, k] score gradients.
+__global__ __launch_bounds__(kBwdThreads) void bwd_gate_kernel(
+    const uint16_t *__restrict__ dy, const uint16_t *__restrict__ y_perm,
+    const int32_t *__restrict__ pos, const int32_t *__restrict__ idx,
+    const float *__restrict__ w, const float *__restrict__ gimp, int T, int k, int d, int E,
+    int S, int rows, uint16_t *__restrict__ dyp, float *__restrict__ ds) {
+  __shared__ float red[kBwdThreads / kWave];
+  __shared__ float dwp[kMaxExperts];
+  const int t = blockIdx.x;
+  const int nv = d / 8;   // 16-byte vectors per row
+  const uint4 *dyr = reinterpret_cast<const uint4 *>(dy + (int64_t)t * d);
+  for (int j = 0; j < k; ++j) {
+    const int p = pos[(int64_t)t * k + j];
+    const float wj = w[(int64_t)t * k + j];
+    float part = 0.0f;
+    if (p >= 0 && p < rows) {
+      const uint4 *yr = reinterpret_cast<const uint4 *>(y_perm + (int64_t)p * d);
+      uint4 *gr = reinterpret_cast<uint4 *>(dyp + (int64_t)p * d);
+      for (int v = threadIdx.x; v < nv; v += kBwdThreads) {
+        const uint4 a = dyr[v], b = yr[v];
+        const uint32_t av[4] = {a.x, a.y, a.z, a.w}, bv[4] = {b.x, b.y, b.z, b.w};
+        uint32_t o[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          part += bf16_lo(av[q]) * bf16_lo(bv[q]);
+          part += bf16_hi(av[q]) * bf16_hi(bv[q]);
+          o[q] = pack_bf16x2(wj * bf16_lo(av[q]), wj * bf16_hi(av[q]));
+        }
+        gr[v] = make_uint4(o[0], o[1], o[2], o[3]);
+      }
+    }
+    const float dw = block_sum(part, red);
+    if (threadIdx.x == 0) {
+      const int e = idx[(int64_t)t * k + j];
+      dwp[j] = dw + (gimp ? gimp[min(max(e, 0), E - 1)] : 0.0f);
+    }
+  }
+  if (S) {
+    uint4 *gr = reinterpret_cast<uint4 *>(dyp + ((int64_t)T * k + t) * d);
+    for (int v = threadIdx.x; v < nv; v += kBwdThreads) gr[v] = dyr[v];
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    float m = 0.0f;
+    for (int j = 0; j < k; ++j) m += w[(int64_t)t * k + j] * dwp[j];
+    for (int j = 0; j < k; ++j) {
+      const float wj = w[(int64_t)t * k + j];
+      ds[(int64_t)t * k + j] = wj * (dwp[j] - m);
+    }
+  }
+}
+
+// H = act(A): GELU H = gelu(A) (A [R, h]); SwiGLU H[:, n] = silu(A[:, n]) *
+// A[:, h + n] (A [R, 2h]).  8 columns per thread.
+__global__ __launch_bounds__(kBwdThreads) void bwd_act_kernel(
+    const uint16_t *__restrict__ A, int64_t R, int h, int swiglu, uint16_t *__restrict__ H) {
+  const int nv = h / 8;
+  const int na = swiglu ? 2 * h : h;
+  for (int64_t i = blockIdx.x * (int64_t)kBwdThreads + threadIdx.x; i < R * nv;
+       i += (int64_t)gridDim.x * kBwdThreads) {
+    const int64_t r = i / nv;
+    const int c = (int)(i % nv) * 8;
+    const uint4 g4 = *reinterpret_cast<const uint4 *>(A + r * na + c);
+    const uint32_t gv[4] = {g4.x, g4.y, g4.z, g4.w};
+    uint32_t o[4];
+    if (swiglu) {
+      const uint4 u4 = *reinterpret_cast<const uint4 *>(A + r * na + h + c);
+      const uint32_t uv[4] = {u4.x, u4.y, u4.z, u4.w};
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        o[q] = pack_bf16x2(silu_f32(bf16_lo(gv[q])) * bf16_lo(uv[q]),
+                           silu_f32(bf16_hi(gv[q])) * bf16_hi(uv[q]));
+    } else {
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        o[q] = pack_bf16x2(gelu_f32(bf16_lo(gv[q])), gelu_f32(bf16_hi(gv[q])));
+    }
+    *reinterpret_cast<uint4 *>(H + r * h + c) = make_uint4(o[0], o[1], o[2], o[3]);
+  }
+}
+
+// dA = act'(A) dH.  GELU: dA = dH (Phi(a) + a phi(a)).  SwiGLU, h = silu(g) u:
+// dg = dH u sigma(g) (1 + g (1 - sigma(g))), du = dH silu(g).
+__device__ __forceinline__ float gelu_grad(float a) {
+  const float cdf = 0.5f * (1.0f + erff(a * 0.70710678118654752f));
+  const float pdf = 0.39894228040143268f * expf(-0.5f * a * a);
+  return cdf + a * pdf;
+}
+
+__global__ __launch_bounds__(kBwdThreads) void bwd_act_grad_kernel(
+    const uint16_t *__restrict__ A, const uint16_t *__restrict__ dH, int64_t R, int h,
+    int swiglu, uint16_t *__restrict__ dA) {
+  const int nv = h / 8;
+  const int na = swiglu ? 2 * h : h;
+  for (int64_t i = blockIdx.x * (int64_t)kBwdThreads + threadIdx.x; i < R * nv;
+       i += (int64_t)gridDim.x * kBwdThreads) {
+    const int64_t r = i / nv;
+    const int c = (int)(i % nv) * 8;
+    const uint4 g4 = *reinterpret_cast<const uint4 *>(A + r * na + c);
+    const uint4 d4 = *reinterpret_cast<const uint4 *>(dH + r * h + c);
+    const uint32_t gv[4] = {g4.x, g4.y, g4.z, g4.w}, dv[4] = {d4.x, d4.y, d4.z, d4.w};
+    uint32_t og[4];
+    if (swiglu) {
+      const uint4 u4 = *reinterpret_cast<const uint4 *>(A + r * na + h + c);
+      const uint32_t uv[4] = {u4.x, u4.y, u4.z, u4.w};
+      uint32_t ou[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        float dg[2], du[2];
+        const float gs[2] = {bf16_lo(gv[q]), bf16_hi(gv[q])};
+        const float us[2] = {bf16_lo(uv[q]), bf16_hi(uv[q])};
+        const float hs[2] = {bf16_lo(dv[q]), bf16_hi(dv[q])};
+#pragma unroll
+        for (int z = 0; z < 2; ++z) {
+          const float sg = 1.0f / (1.0f + expf(-gs[z]));
+          dg[z] = hs[z] * us[z] * sg * (1.0f + gs[z] * (1.0f - sg));
+          du[z] = hs[z] * gs[z] * sg;
+        }
+        og[q] = pack_bf16x2(dg[0], dg[1]);
+        ou[q] = pack_bf16x2(du[0], du[1]);
+      }
+      *reinterpret_cast<uint4 *>(dA + r * na + h + c) = make_uint4(ou[0], ou[1], ou[2], ou[3]);
+    } else {
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        og[q] = pack_bf16x2(bf16_lo(dv[q]) * gelu_grad(bf16_lo(gv[q])),
+                            bf16_hi(dv[q]) * gelu_grad(bf16_hi(gv[q])));
+    }
+    *reinterpret_cast<uint4 *>(dA + r * na + c) = make_uint4(og[0], og[1], og[2], og[3]);
+  }
+}
+
+// Group g's rows: routed groups [offsets[g], offsets[g+1]) (clamped), the
+// shared group (g == E) rows [T*k, T*k + T).  poff: exclusive scan of the
+// row counts rounded up to 32.  One workgroup of kMaxExperts + 1 <= 2 *
+// 256 groups: thread t owns groups 2t and 2t + 1.
+__global__ __launch_bounds__(kBwdThreads) void bwd_layout_kernel(
+    const int32_t *__restrict__ offsets, int E, int S, int T, int routed,
+    int32_t *__restrict__ poff) {
+  __shared__ int sc[kBwdThreads];
+  const int G = E + S;
+  const int tid = threadIdx.x;
+  int c[2];
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const int g = 2 * tid + q;
+    int n = 0;
+    if (g < E) {
+      const int r0 = min(max(offsets[g], 0), routed);
+      const int r1 = min(max(offsets[g + 1], r0), routed);
+      n = r1 - r0;
+    } else if (g < G) {
+      n = T;
+    }
+    c[q] = (n + 31) / 32 * 32;
+  }
+  sc[tid] = c[0] + c[1];
+  __syncthreads();
+  for (int off = 1; off < kBwdThreads; off <<= 1) {
+    const int v = tid >= off ? sc[tid - off] : 0;
+    __syncthreads();
+    sc[tid] += v;
+    __syncthreads();
+  }
+  const int ex = sc[tid] - c[0] - c[1];
+  if (2 * tid <= G) poff[2 * tid] = ex;
+  if (2 * tid + 1 <= G) poff[2 * tid + 1] = ex + c[0];
+}
+
+// colsrc[j]: the grouped row behind padded column j, or -1 (padding).
+__global__ __launch_bounds__(kBwdThreads) void bwd_colsrc_kernel(
+    const int32_t *__restrict__ offsets, const int32_t *__restrict__ poff, int E, int S,
+    int T, int routed, int Rp, int32_t *__restrict__ colsrc) {
+  const int G = E + S;
+  for (int j = blockIdx.x * kBwdThreads + threadIdx.x; j < Rp; j += gridDim.x * kBwdThreads) {
+    int v = -1;
+    if (j < poff[G]) {
+      int lo = 0, hi = G - 1;   // last group with poff[g] <= j
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) / 2;
+        if (poff[mid] <= j) lo = mid; else hi = mid - 1;
+      }
+      int r0, n;
+      if (lo < E) {
+        r0 = min(max(offsets[lo], 0), routed);
+        n = min(max(offsets[lo + 1], r0), routed) - r0;
+      } else {
+        r0 = routed;
+        n = T;
+      }
+      if (j - poff[lo] < n) v = r0 + (j - poff[lo]);
+    }
+    colsrc[j] = v;
+  }
+}
+
+// dst[c][j] = row colsrc[j] of the source (routed rows from src, rows from
+// `routed` on from src_shared), column c; 0 on padding.  64 x 64 tiles
+// through LDS, 16-byte global accesses on both sides.  C % 64 == 0, Rp % 64
+// == 0.
+__global__ __launch_bounds__(kBwdThreads) void bwd_transpose_cols_kernel(
+    const uint16_t *__restrict__ src, const uint16_t *__restrict__ src_shared, int routed,
+    int C, const int32_t *__restrict__ colsrc, int Rp, uint16_t *__restrict__ dst) {
+  __shared__ uint16_t tile[64][64 + 2];
+  const int j0 = blockIdx.x * 64;
+  const int c0 = blockIdx.y * 64;
+  const int tid = threadIdx.x;
+  // load: 64 source rows x 8 vectors of 8 columns
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int q = tid + i * kBwdThreads;
+    const int jj = q / 8, v = q % 8;
+    const int r = colsrc[j0 + jj];
+    uint4 val = make_uint4(0, 0, 0, 0);
+    if (r >= 0) {
+      const uint16_t *row = r < routed ? src + (int64_t)r * C
+                                       : src_shared + (int64_t)(r - routed) * C;
+      val = *reinterpret_cast<const uint4 *>(row + c0 + 8 * v);
+    }
+    const uint32_t w4[4] = {val.x, val.y, val.z, val.w};
+#pragma unroll
+    for (int z = 0; z < 4; ++z) {
+      tile[jj][8 * v + 2 * z] = (uint16_t)(w4[z] & 0xffffu);
+      tile[jj][8 * v + 2 * z + 1] = (uint16_t)(w4[z] >> 16);
+    }
+  }
+  __syncthreads();
+  // store: 64 destination rows (c) x 8 vectors of 8 columns (j)
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int q = tid + i * kBwdThreads;
+    const int cc = q / 8, v = q % 8;
+    uint32_t w4[4];
+#pragma unroll
+    for (int z = 0; z < 4; ++z)
+      w4[z] = (uint32_t)tile[8 * v + 2 * z][cc] | ((uint32_t)tile[8 * v + 2 * z + 1][cc] << 16);
+    *reinterpret_cast<uint4 *>(dst + (int64_t)(c0 + cc) * Rp + j0 + 8 * v) =
+        make_uint4(w4[0], w4[1], w4[2], w4[3]);
+  }
+}
+
+// Batched transpose of [B][R][C] to [B][C][R]; R, C multiples of 64.
+__global__ __launch_bounds__(kBwdThreads) void bwd_transpose_kernel(
+    const uint16_t *__restrict__ src, int R, int C, uint16_t *__restrict__ dst) {
+  __shared__ uint16_t tile[64][64 + 2];
+  const int r0 = blockIdx.x * 64, c0 = blockIdx.y * 64;
+  const int64_t b = blockIdx.z;
+  const uint16_t *s = src + b * R * (int64_t)C;
+  uint16_t *o = dst + b * R * (int64_t)C;
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int q = tid + i * kBwdThreads;
+    const int rr = q / 8, v = q % 8;
+    const uint4 val = *reinterpret_cast<const uint4 *>(s + (int64_t)(r0 + rr) * C + c0 + 8 * v);
+    const uint32_t w4[4] = {val.x, val.y, val.z, val.w};
+#pragma unroll
+    for (int z = 0; z < 4; ++z) {
+      tile[rr][8 * v + 2 * z] = (uint16_t)(w4[z] & 0xffffu);
+      tile[rr][8 * v + 2 * z + 1] = (uint16_t)(w4[z] >> 16);
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int q = tid + i * kBwdThreads;
+    const int cc = q / 8, v = q % 8;
+    uint32_t w4[4];
+#pragma unroll
+    for (int z = 0; z < 4; ++z)
+      w4[z] = (uint32_t)tile[8 * v + 2 * z][cc] | ((uint32_t)tile[8 * v + 2 * z + 1][cc] << 16);
+    *reinterpret_cast<uint4 *>(o + (int64_t)(c0 + cc) * R + r0 + 8 * v) =
+        make_uint4(w4[0], w4[1], w4[2], w4[3]);
+  }
+}
+
+// dsp[pos[f]] = ds[f] (grouped-row order), then ds_cols[j] = dsp[colsrc[j]]
+// for routed rows, 0 otherwise.
+__global__ void bwd_scatter_ds_kernel(const float *__restrict__ ds, const int32_t *__restrict__ pos,
+                                      int n, int routed, float *__restrict__ dsp) {
+  for (int f = blockIdx.x * blockDim.x + threadIdx.x; f < n; f += gridDim.x * blockDim.x) {
+    const int p = pos[f];
+    if (p >= 0 && p < routed) dsp[p] = ds[f];
+  }
+}
+
+__global__ void bwd_ds_cols_kernel(const float *__restrict__ dsp, const int32_t *__restrict__ colsrc,
+                                   int Rp, int routed, float *__restrict__ ds_cols) {
+  for (int j = blockIdx.x * blockDim.x + threadIdx.x; j < Rp; j += gridDim.x * blockDim.x) {
+    const int r = colsrc[j];
+    ds_cols[j] = (r >= 0 && r < routed) ? dsp[r] : 0.0f;
+  }
+}
+
+// out[g][c] = sum over group g's columns j of wcol[j] * at[c][j] (wcol NULL:
+// 1), for groups g < G; one wavefront per (g, c): lanes take columns
+// j = lane, lane + 64, ... in order, then a fixed butterfly.
+__global__ __launch_bounds__(kWave) void bwd_rowsum_kernel(
+    const uint16_t *__restrict__ at, int C, int Rp, const int32_t *__restrict__ poff,
+    const float *__restrict__ wcol, float *__restrict__ out) {
+  const int c = blockIdx.x;
+  const int g = blockIdx.y;
+  const int lane = threadIdx.x;
+  const int j0 = poff[g], j1 = poff[g + 1];
+  const uint16_t *row = at + (int64_t)c * Rp;
+  float s = 0.0f;
+  for (int j = j0 + lane; j < j1; j += kWave) {
+    const float v = __uint_as_float((uint32_t)row[j] << 16);
+    s += wcol ? wcol[j] * v : v;
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) s += __shfl_xor(s, off);
+  if (lane == 0) out[(int64_t)g * C + c] = s;
+}
+
+// out[g] = sum over group g's columns of vals[j]; one wavefront per group.
+__global__ __launch_bounds__(kWave) void bwd_group_sum_kernel(
+    const float *__restrict__ vals, const int32_t *__restrict__ poff, float *__restrict__ out) {
+  const int g = blockIdx.x;
+  const int lane = threadIdx.x;
+  float s = 0.0f;
+  for (int j = poff[g] + lane; j < poff[g + 1]; j += kWave) s += vals[j];
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) s += __shfl_xor(s, off);
+  if (lane == 0) out[g] = s;
+}
+
+// dx[t] = sum_j dX[pos_j] + dX[T*k + t] (shared) + sum_j ds_j W_g[i_j], fp32
+// accumulation in that order, one rounding to bf16.  One workgroup per
+// token, 4 columns per thread.
+__global__ __launch_bounds__(kBwdThreads) void bwd_dx_kernel(
+    const uint16_t *__restrict__ dxp, const int32_t *__restrict__ pos,
+    const float *__restrict__ ds, const int32_t *__restrict__ idx,
+    const float *__restrict__ wg, int T, int k, int d, int E, int S, int rows,
+    uint16_t *__restrict__ dx) {
+  const int t = blockIdx.x;
+  for (int c = 4 * threadIdx.x; c < d; c += 4 * kBwdThreads) {
+    float acc[4] = {0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < k; ++j) {
+      const int p = pos[(int64_t)t * k + j];
+      if (p < 0 || p >= rows) continue;
+      const uint2 v = *reinterpret_cast<const uint2 *>(dxp + (int64_t)p * d + c);
+      acc[0] += bf16_lo(v.x);
+      acc[1] += bf16_hi(v.x);
+      acc[2] += bf16_lo(v.y);
+      acc[3] += bf16_hi(v.y);
+    }
+    if (S) {
+      const uint2 v = *reinterpret_cast<const uint2 *>(dxp + ((int64_t)T * k + t) * d + c);
+      acc[0] += bf16_lo(v.x);
+      acc[1] += bf16_hi(v.x);
+      acc[2] += bf16_lo(v.y);
+      acc[3] += bf16_hi(v.y);
+    }
+    for (int j = 0; j < k; ++j) {
+      const int e = min(max(idx[(int64_t)t * k + j], 0), E - 1);
+      const float sj = ds[(int64_t)t * k + j];
+      const float4 wv = *reinterpret_cast<const float4 *>(wg + (int64_t)e * d + c);
+      acc[0] += sj * wv.x;
+      acc[1] += sj * wv.y;
+      acc[2] += sj * wv.z;
+      acc[3] += sj * wv.w;
+    }
+    uint2 o;
+    o.x = pack_bf16x2(acc[0], acc[1]);
+    o.y = pack_bf16x2(acc[2], acc[3]);
+    *reinterpret_cast<uint2 *>(dx + (int64_t)t * d + c) = o;
+  }
+}
+
+// colsrc_tok[j]: the token behind column j of a grouping (perm_src of the
+// grouped row colsrc[j]), or -1.
+__global__ void bwd_col_token_kernel(const int32_t *__restrict__ colsrc,
+                                     const int32_t *__restrict__ perm_src, int Rp, int n, int T,
+                                     int32_t *__restrict__ colsrc_tok) {
+  for (int j = blockIdx.x * blockDim.x + threadIdx.x; j < Rp; j += gridDim.x * blockDim.x) {
+    const int r = colsrc[j];
+    colsrc_tok[j] = (r >= 0 && r < n) ? min(max(perm_src[r], 0), T - 1) : -1;
+  }
+}
+
+__global__ void bwd_fill_f32_kernel(float *p, int64_t n, float v) {
+  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n;
+       i += (int64_t)gridDim.x * blockDim.x)
+    p[i] = v;
+}
+
+// ------------------------------------------------------------------ host --
+
+hipError_t launch_grouped_linear_bf16(const int32_t *offsets, int E, int S, int T, int k,
+                                      int K, int n_out, const void *a_routed,
+                                      const void *a_shared, const void *w,
+                                      const void *w_shared, const void *bias, void *c,
+                                      hipStream_t s);
+hipError_t launch_permute(const int32_t *idx, const float *w, const void *x, int T, int k,
+                          int E, int capacity, int row_bytes, int32_t *offsets,
+                          int32_t *perm_src, int32_t *pos, float *importance, double *stats,
+                          void *x_perm, int32_t *hist, int32_t *full_off, float *perm_w,
+                          hipStream_t s);
+hipError_t launch_wgrad_bf16(const int32_t *poff, int G, int Rp, int M, int N, const void *at,
+                             const void *bt, float *out, float *out_last, hipStream_t s);
+
+static unsigned grid_for(int64_t work, int64_t per_block) {
+  int64_t b = (work + per_block - 1) / per_block;
+  if (b > 4096) b = 4096;
+  return (unsigned)(b < 1 ? 1 : b);
+}
+
+hipError_t launch_fill_f32(float *p, int64_t n, hipStream_t s) {
+  if (!p || n <= 0) return hipSuccess;
+  bwd_fill_f32_kernel<<<grid_for(n, 256), 256, 0, s>>>(p, n, 0.0f);
+  return hipGetLastError();
+}
+
+int64_t bwd_padded_cols(int64_t T, int k, int E, int S) {
+  const int64_t R = T * k + (int64_t)S * T;
+  return (R + 32 * (int64_t)(E + S) + 63) / 64 * 64;
+}
+
+hipError_t launch_backward(const BwdArgs &a, const BwdBuffers &b, hipStream_t s) {
+  const int T = a.T, k = a.k, E = a.E, S = a.S, d = a.d, h = a.h;
+  const int G = E + S;
+  const int routed = T * k;
+  const int R = routed + S * T;
+  const int nup = a.swiglu ? 2 * h : h;
+  const int Rp = (int)bwd_padded_cols(T, k, E, S);
+  hipError_t err;
+#define MOE_TRY(x)                         \
+  do {                                     \
+    if ((err = (x)) != hipSuccess) return err; \
+  } while (0)
+
+  // gate: Importance term, expert output gradients, score gradients
+  const float *gimp = nullptr;
+  if (a.importance && a.w_imp != 0.0f) {
+    bwd_importance_grad_kernel<<<1, kBwdThreads, 0, s>>>(a.importance, E, a.w_imp, b.gimp);
+    gimp = b.gimp;
+  }
+  bwd_gate_kernel<<<T, kBwdThreads, 0, s>>>(a.dy, a.y_perm, a.pos, a.idx, a.topk_w, gimp, T,
+                                            k, d, E, S, R, b.dyp, b.ds);
+  MOE_TRY(hipGetLastError());
+
+  // padded group columns
+  bwd_layout_kernel<<<1, kBwdThreads, 0, s>>>(a.offsets, E, S, T, routed, b.poff);
+  bwd_colsrc_kernel<<<grid_for(Rp, kBwdThreads), kBwdThreads, 0, s>>>(a.offsets, b.poff, E, S, T,
+                                                                       routed, Rp, b.colsrc);
+  // transposed weights: W1^T [E, d, nup], W2^T [E, h, d]
+  bwd_transpose_kernel<<<dim3(nup / 64, d / 64, E), kBwdThreads, 0, s>>>(a.w_up, nup, d, b.w1t);
+  bwd_transpose_kernel<<<dim3(d / 64, h / 64, E), kBwdThreads, 0, s>>>(a.w_down, d, h, b.w2t);
+  if (S) {
+    bwd_transpose_kernel<<<dim3(nup / 64, d / 64, 1), kBwdThreads, 0, s>>>(a.w_up_s, nup, d, b.w1ts);
+    bwd_transpose_kernel<<<dim3(d / 64, h / 64, 1), kBwdThreads, 0, s>>>(a.w_down_s, d, h, b.w2ts);
+  }
+  MOE_TRY(hipGetLastError());
+
+  // pre-activations recomputed, activations, then the chain back to dX
+  MOE_TRY(launch_grouped_linear_bf16(a.offsets, E, S, T, k, d, nup, a.x_perm, a.x, a.w_up,
+                                     a.w_up_s, a.swiglu ? nullptr : a.b_up, b.A, s));
+  bwd_act_kernel<<<grid_for((int64_t)R * (h / 8), kBwdThreads), kBwdThreads, 0, s>>>(
+      b.A, R, h, a.swiglu, b.H);
+  MOE_TRY(launch_grouped_linear_bf16(a.offsets, E, S, T, k, d, h, b.dyp,
+                                     b.dyp + (int64_t)routed * d, b.w2t, b.w2ts, nullptr, b.dH,
+                                     s));
+  bwd_act_grad_kernel<<<grid_for((int64_t)R * (h / 8), kBwdThreads), kBwdThreads, 0, s>>>(
+      b.A, b.dH, R, h, a.swiglu, b.dA);
+  MOE_TRY(launch_grouped_linear_bf16(a.offsets, E, S, T, k, nup, d, b.dA,
+                                     b.dA + (int64_t)routed * nup, b.w1t, b.w1ts, nullptr,
+                                     b.dxp, s));
+  bwd_dx_kernel<<<T, kBwdThreads, 0, s>>>(b.dxp, a.pos, b.ds, a.idx, a.w_gate, T, k, d, E, S, R,
+                                         a.dx);
+  MOE_TRY(hipGetLastError());
+
+  // weight gradients over each group's rows
+  bwd_transpose_cols_kernel<<<dim3(Rp / 64, d / 64), kBwdThreads, 0, s>>>(
+      b.dyp, b.dyp + (int64_t)routed * d, routed, d, b.colsrc, Rp, b.dypT);
+  bwd_transpose_cols_kernel<<<dim3(Rp / 64, h / 64), kBwdThreads, 0, s>>>(
+      b.H, b.H + (int64_t)routed * h, routed, h, b.colsrc, Rp, b.HT);
+  bwd_transpose_cols_kernel<<<dim3(Rp / 64, nup / 64), kBwdThreads, 0, s>>>(
+      b.dA, b.dA + (int64_t)routed * nup, routed, nup, b.colsrc, Rp, b.dAT);
+  bwd_transpose_cols_kernel<<<dim3(Rp / 64, d / 64), kBwdThreads, 0, s>>>(
+      a.x_perm, a.x, routed, d, b.colsrc, Rp, b.xpT);
+  MOE_TRY(hipGetLastError());
+  MOE_TRY(launch_wgrad_bf16(b.poff, G, Rp, d, h, b.dypT, b.HT, a.dw_down,
+                            S ? a.dw_down_s : nullptr, s));
+  MOE_TRY(launch_wgrad_bf16(b.poff, G, Rp, nup, d, b.dAT, b.xpT, a.dw_up,
+                            S ? a.dw_up_s : nullptr, s));
+  if (a.db_down) bwd_rowsum_kernel<<<dim3(d, E), kWave, 0, s>>>(b.dypT, d, Rp, b.poff, nullptr,
+                                                               a.db_down);
+  if (a.db_up) bwd_rowsum_kernel<<<dim3(h, E), kWave, 0, s>>>(b.dAT, h, Rp, b.poff, nullptr,
+                                                             a.db_up);
+  // router: dW_g[e] = sum over every assignment to e of ds * x, db_g[e] =
+  // sum of ds.  A dropped slot has a score gradient too (its gate shapes the
+  // kept softmax and Importance), so under a capacity every assignment is
+  // grouped again (no row move) and x is transposed in that order into the
+  // space of dY^T, which is no longer needed; otherwise the kept grouping
+  // is the full one and X^T serves.
+  const uint16_t *xT = b.xpT;
+  const int32_t *pos_r = a.pos, *poff_r = b.poff, *colsrc_r = b.colsrc;
+  if (a.capacity > 0) {
+    MOE_TRY(launch_permute(a.idx, a.topk_w, a.x, T, k, E, 0, d * 2, b.off_all, b.src_all,
+                           b.pos_all, b.imp_all, nullptr, nullptr, b.hist, b.full_off,
+                           b.perm_w, s));
+    bwd_layout_kernel<<<1, kBwdThreads, 0, s>>>(b.off_all, E, 0, T, routed, b.poff);
+    bwd_colsrc_kernel<<<grid_for(Rp, kBwdThreads), kBwdThreads, 0, s>>>(
+        b.off_all, b.poff, E, 0, T, routed, Rp, b.colsrc);
+    // the token behind each column, into the (now free) column-source space
+    // of the kept grouping's gradient pass: reuse dsp's neighbour ds_cols
+    bwd_col_token_kernel<<<grid_for(Rp, 256), 256, 0, s>>>(b.colsrc, b.src_all, Rp, routed, T,
+                                                           reinterpret_cast<int32_t *>(b.ds_cols));
+    bwd_transpose_cols_kernel<<<dim3(Rp / 64, d / 64), kBwdThreads, 0, s>>>(
+        a.x, a.x, T, d, reinterpret_cast<const int32_t *>(b.ds_cols), Rp, b.dypT);
+    xT = b.dypT;
+    pos_r = b.pos_all;
+  }
+  bwd_scatter_ds_kernel<<<grid_for(routed, 256), 256, 0, s>>>(b.ds, pos_r, routed, routed, b.dsp);
+  bwd_ds_cols_kernel<<<grid_for(Rp, 256), 256, 0, s>>>(b.dsp, colsrc_r, Rp, routed, b.ds_cols);
+  bwd_rowsum_kernel<<<dim3(d, E), kWave, 0, s>>>(xT, d, Rp, poff_r, b.ds_cols, a.dw_gate);
+  if (a.db_gate) bwd_group_sum_kernel<<<E, kWave, 0, s>>>(b.ds_cols, poff_r, a.db_gate);
+  return hipGetLastError();
+#undef MOE_TRY
+}
+
+}  // namespace moe

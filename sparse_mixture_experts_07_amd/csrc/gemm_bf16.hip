@@ -704,6 +704,93 @@ void gemm_dma_kernel(GemmArgs a) {
   }
 }
 
+// ------------------------------------------------------ weight gradients --
+// dW[g] = A_g^T B_g summed over the rows of group g (the backward pass of
+// the grouped GEMMs), from K-contiguous transposed copies At [M, Rp] and Bt
+// [N, Rp] whose group column ranges [poff[g], poff[g+1]) are zero-padded to
+// multiples of 32:  out[g][m][n] = sum_j At[m][j] * Bt[n][j], fp32.  The
+// same tile arithmetic as the forward kernels with the group's rows as the
+// contraction: one workgroup per (group, m-tile, n-tile), k loop over the
+// group's columns (none for an empty group: its tiles store zeros).
+struct WgradArgs {
+  const int32_t *poff;   // [G + 1], multiples of 32
+  int G, Rp, M, N;
+  const uint16_t *at;    // [M, Rp]
+  const uint16_t *bt;    // [N, Rp]
+  float *out;            // [G][M][N] (or [G - 1] when out_last is set)
+  float *out_last;       // the last group's [M][N] stored apart, or NULL
+  int m_tiles, n_tiles;
+};
+
+template <int BM, int BNW, int WM, int WN>
+__global__ __launch_bounds__(WM *WN * 64) __attribute__((amdgpu_waves_per_eu(2)))
+void gemm_wgrad_kernel(WgradArgs a) {
+  using TM = TileMath<BM, BNW, WM, WN, 32, kDown>;
+  constexpr int CH = TM::CH, A_LD = TM::A_LD, W_LD = TM::W_LD;
+  constexpr int FM = TM::FM, FW = TM::FW, WTM = TM::WTM, WTW = TM::WTW;
+  __shared__ u32x4_t As[2][BM * CH];
+  __shared__ u32x4_t Ws[2][BNW * CH];
+  const int wave = threadIdx.x / 64;
+  const int wm = wave / WN;
+  const int wn = wave % WN;
+  const int per_g = a.m_tiles * a.n_tiles;
+  const int g = blockIdx.x / per_g;
+  const int local = blockIdx.x % per_g;
+  Tile t;
+  t.g = g;
+  t.grow0 = 0;
+  t.rows = a.M;
+  t.m0 = (local % a.m_tiles) * BM;
+  t.n0 = (local / a.m_tiles) * BNW;
+  const int c0 = __builtin_amdgcn_readfirstlane(a.poff[g]);
+  const int c1 = __builtin_amdgcn_readfirstlane(a.poff[g + 1]);
+  const int nk = c1 > c0 ? (c1 - c0) / 32 : 0;
+  const uint32_t row_bytes = (uint32_t)a.Rp * 2u;
+  const int arows = min(BM, a.M - t.m0);
+  const int wrows = min(BNW, a.N - t.n0);
+  t.rs_a = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t *>(a.at + (int64_t)t.m0 * a.Rp + c0), 0, arows * row_bytes, kBufferWord3);
+  t.rs_w0 = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t *>(a.bt + (int64_t)t.n0 * a.Rp + c0), 0, wrows * row_bytes, kBufferWord3);
+  t.rs_w1 = t.rs_w0;
+  const uint32_t v0 = TM::voff0(row_bytes);
+
+  f32x4_t acc[FW][FM];
+#pragma unroll
+  for (int i = 0; i < FW; ++i)
+#pragma unroll
+    for (int j = 0; j < FM; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  if (nk > 0) {
+    u32x4_t ra[A_LD], rw[W_LD];
+    TM::gload(t, v0, row_bytes, ra, rw, 0);
+    TM::lstore(As[0], Ws[0], ra, rw);
+    __syncthreads();
+    for (int kt = 0; kt < nk; ++kt) {
+      const int buf = kt & 1;
+      const bool more = kt + 1 < nk;
+      if (more) TM::gload(t, v0, row_bytes, ra, rw, kt + 1);
+      __builtin_amdgcn_sched_barrier(0);
+      TM::compute(As[buf], Ws[buf], acc, wm, wn);
+      __builtin_amdgcn_sched_barrier(0);
+      if (more) TM::lstore(As[buf ^ 1], Ws[buf ^ 1], ra, rw);
+      __syncthreads();
+    }
+  }
+  // lane owns columns 4*(lane/16)+0..3 of row lane%16 of each fragment
+  float *o = (a.out_last && g == a.G - 1) ? a.out_last : a.out + (int64_t)g * a.M * a.N;
+  const int lane = threadIdx.x % 64;
+#pragma unroll
+  for (int i = 0; i < FW; ++i) {
+    const int col = t.n0 + wn * WTW + i * 16 + 4 * (lane / 16);
+#pragma unroll
+    for (int j = 0; j < FM; ++j) {
+      const int m = t.m0 + wm * WTM + j * 16 + lane % 16;
+      if (col < a.N && m < a.M)
+        *reinterpret_cast<f32x4_t *>(o + (int64_t)m * a.N + col) = acc[i][j];
+    }
+  }
+}
+
 // ---------------------------------------------------------------- launch --
 
 static int num_cus() {
@@ -811,6 +898,53 @@ static hipError_t launch_classes(GemmArgs a, hipStream_t s) {
   a.min_rows = 1;
   a.max_rows = 64;
   return launch_bm<32, 128, 2, 2, 64, 2, MODE>(a, s);
+}
+
+// Plain grouped linear map c[r] = a[r] W[g]^T (+ bias[g]) over the groups of
+// `offsets` and the shared group (rows T*k.., operand a_shared, weights
+// w_shared): the backward pass's dH = dY W2 and dX = dA W1 on transposed
+// weight copies, and the pre-activation recomputation A = X W1^T.
+hipError_t launch_grouped_linear_bf16(const int32_t *offsets, int E, int S, int T, int k,
+                                      int K, int n_out, const void *a_routed,
+                                      const void *a_shared, const void *w,
+                                      const void *w_shared, const void *bias, void *c,
+                                      hipStream_t s) {
+  GemmArgs a{};
+  a.offsets = offsets;
+  a.E = E;
+  a.S = S;
+  a.T = T;
+  a.routed_rows = T * k;
+  a.a_routed = static_cast<const uint16_t *>(a_routed);
+  a.a_shared = static_cast<const uint16_t *>(a_shared);
+  a.K = K;
+  a.w = static_cast<const uint16_t *>(w);
+  a.w_shared = static_cast<const uint16_t *>(w_shared);
+  a.w_rows = n_out;
+  a.bias = static_cast<const uint16_t *>(bias);
+  a.c = static_cast<uint16_t *>(c);
+  a.n_out = n_out;
+  return launch_classes<kDown>(a, s);
+}
+
+hipError_t launch_wgrad_bf16(const int32_t *poff, int G, int Rp, int M, int N, const void *at,
+                             const void *bt, float *out, float *out_last, hipStream_t s) {
+  constexpr int BM = 128, BNW = 128;
+  WgradArgs a{};
+  a.poff = poff;
+  a.G = G;
+  a.Rp = Rp;
+  a.M = M;
+  a.N = N;
+  a.at = static_cast<const uint16_t *>(at);
+  a.bt = static_cast<const uint16_t *>(bt);
+  a.out = out;
+  a.out_last = out_last;
+  a.m_tiles = (M + BM - 1) / BM;
+  a.n_tiles = (N + BNW - 1) / BNW;
+  const int64_t blocks = (int64_t)G * a.m_tiles * a.n_tiles;
+  gemm_wgrad_kernel<BM, BNW, 2, 2><<<dim3((unsigned)blocks), dim3(256), 0, s>>>(a);
+  return hipGetLastError();
 }
 
 hipError_t launch_expert_up_bf16(bool swiglu, const int32_t *offsets, int E, int S,

@@ -406,9 +406,10 @@ hipError_t launch_permute(const int32_t *idx, const float *w, const void *x,
                                                                 importance);
     if (stats) perm_stats_kernel<<<1, kWave, 0, s>>>(full_off, importance, E, stats);
   }
-  perm_move_kernel<<<blocks, kPermThreads, 0, s>>>(
-      static_cast<const uint4 *>(x), perm_src, offsets + E, n, T, row_bytes / 16,
-      static_cast<uint4 *>(x_perm));
+  if (x_perm)   // NULL: grouping only (the backward pass regroups every assignment)
+    perm_move_kernel<<<blocks, kPermThreads, 0, s>>>(
+        static_cast<const uint4 *>(x), perm_src, offsets + E, n, T, row_bytes / 16,
+        static_cast<uint4 *>(x_perm));
   return hipGetLastError();
 }
 

@@ -112,6 +112,10 @@ def test_every_entry_point_rejects_bad_config(name):
         L.moe_param_counts(r, C.byref(C.c_int64()), C.byref(C.c_int64())),
         L.moe_route_noisy(r, FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
                           FAKE, FAKE, None, FAKE, 1 << 40, None),
+        L.moe_backward_workspace_bytes(r, C.byref(C.c_size_t())),
+        L.moe_backward(r, C.byref(w), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None,
+                       C.c_float(0.0), C.byref(B.grads(None, None, None, None)), FAKE,
+                       1 << 40, None),
     ]
     assert calls == [status] * len(calls)
 
@@ -178,3 +182,30 @@ def test_noisy_route_checks():
     assert L.moe_route_noisy(r, *args, FAKE, need - 1, None) == small
     assert L.moe_route_noisy(r, *args, None, 1 << 40, None) == inv
     assert B.moe_workspace_bytes(cfg) >= need
+
+
+def test_backward_checks():
+    L = B.lib()
+    inv, uns = B.MOE_ERR_INVALID_ARGUMENT, B.MOE_ERR_UNSUPPORTED
+    w = B.MoeWeights(FAKE, None, FAKE, None, FAKE, None, None, None)
+    g = B.MoeGrads(FAKE, FAKE, None, FAKE, FAKE, None, None, None, None)
+    args = [FAKE] * 8 + [None, C.c_float(0.0), C.byref(g), FAKE, 1 << 40, None]
+    bf = _cfg(dtype=1)
+    # fp32 layers and the other gate modes have no backward pass here
+    for cfg in (_cfg(dtype=0), _cfg(dtype=1, gate=1), _cfg(dtype=1, gate=2)):
+        assert L.moe_backward(C.byref(cfg), C.byref(w), *args) == uns
+        assert L.moe_backward_workspace_bytes(C.byref(cfg), C.byref(C.c_size_t())) == uns
+    # required gradient outputs; shared-expert gradients iff S = 1
+    g0 = B.MoeGrads(FAKE, None, None, FAKE, FAKE, None, None, None, None)
+    args0 = [FAKE] * 8 + [None, C.c_float(0.0), C.byref(g0), FAKE, 1 << 40, None]
+    assert L.moe_backward(C.byref(bf), C.byref(w), *args0) == inv
+    gs = B.MoeGrads(FAKE, FAKE, None, FAKE, FAKE, None, None, FAKE, FAKE)
+    argss = [FAKE] * 8 + [None, C.c_float(0.0), C.byref(gs), FAKE, 1 << 40, None]
+    assert L.moe_backward(C.byref(bf), C.byref(w), *argss) == inv
+    # workspace
+    n = C.c_size_t()
+    assert L.moe_backward_workspace_bytes(C.byref(bf), C.byref(n)) == 0
+    small = [FAKE] * 8 + [None, C.c_float(0.0), C.byref(g), FAKE, n.value - 1, None]
+    assert L.moe_backward(C.byref(bf), C.byref(w), *small) == B.MOE_ERR_WORKSPACE_TOO_SMALL
+    nan = [FAKE] * 8 + [None, C.c_float(float("nan")), C.byref(g), FAKE, 1 << 40, None]
+    assert L.moe_backward(C.byref(bf), C.byref(w), *nan) == inv

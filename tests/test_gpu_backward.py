@@ -1,0 +1,147 @@
+"""Backward pass through the C ABI against the float64 autograd oracle
+(oracle/backward.py): the gradient of <dy, y> + w * CV^2(Importance) with
+the forward's top-k selection held fixed."""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gpu_common import max_rel, require_gpu, to_f64
+from helpers import BF16, GELU, SWIGLU, random_layer
+from sparse_mixture_experts_07_amd import binding as B
+from sparse_mixture_experts_07_amd.device import DeviceLayer, bf16_bits, to_device
+from synthetic import bf16_bits_to_f32, f32_to_bf16_bits
+
+pytestmark = pytest.mark.gpu
+
+GRAD_TOL = 2e-2   # max |g - g_ref| / max |g_ref| per gradient, bf16 chains
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    require_gpu()
+
+
+def forward_saved(L, capacity=0):
+    """The stage entry points; every tensor the backward pass takes."""
+    dl = DeviceLayer.upload(L, capacity=capacity)
+    c, dev = dl.cfg, dl.x.device
+    T, k, E, d = L.cfg.T, L.cfg.k, L.cfg.E, L.cfg.d
+    R = B.moe_grouped_rows(c)
+    s = dict(idx=torch.empty((T, k), dtype=torch.int32, device=dev),
+             w=torch.empty((T, k), dtype=torch.float32, device=dev),
+             counts=torch.empty(E, dtype=torch.int32, device=dev),
+             offsets=torch.empty(E + 1, dtype=torch.int32, device=dev),
+             perm_src=torch.empty(T * k, dtype=torch.int32, device=dev),
+             pos=torch.empty(T * k, dtype=torch.int32, device=dev),
+             imp=torch.empty(E, dtype=torch.float32, device=dev),
+             x_perm=torch.empty((T * k, d), dtype=torch.bfloat16, device=dev),
+             y_perm=torch.empty((R, d), dtype=torch.bfloat16, device=dev),
+             y=torch.empty((T, d), dtype=torch.bfloat16, device=dev))
+    ws = torch.empty(max(B.moe_workspace_bytes(c), 256), dtype=torch.uint8, device=dev)
+    B.moe_route(c, dl.x, dl.w_gate, dl.b_gate, s["idx"], s["w"], s["counts"])
+    B.moe_permute(c, s["idx"], s["w"], dl.x, s["offsets"], s["perm_src"], s["pos"], s["imp"],
+                  None, s["x_perm"], ws)
+    B.moe_expert_ffn(c, dl.weights(), s["x_perm"], dl.x, s["offsets"], s["y_perm"], ws)
+    B.moe_combine(c, s["y_perm"], s["pos"], s["w"], s["y"])
+    return dl, s
+
+
+def run_backward(L, dy_bits, capacity=0, imp_w=0.0):
+    dl, s = forward_saved(L, capacity)
+    c, dev = dl.cfg, dl.x.device
+    cfg = L.cfg
+    E, d, h, S = cfg.E, cfg.d, cfg.h, cfg.S
+    nup = 2 * h if cfg.act == SWIGLU else h
+    f32 = dict(dtype=torch.float32, device=dev)
+    g = dict(dx=torch.empty((cfg.T, d), dtype=torch.bfloat16, device=dev),
+             w_gate=torch.empty((E, d), **f32), w_up=torch.empty((E, nup, d), **f32),
+             w_down=torch.empty((E, d, h), **f32),
+             b_gate=torch.empty(E, **f32) if L.b_gate is not None else None,
+             b_up=torch.empty((E, h), **f32) if L.b_up is not None else None,
+             b_down=torch.empty((E, d), **f32) if L.b_down is not None else None,
+             w_up_shared=torch.empty((1, nup, d), **f32) if S else None,
+             w_down_shared=torch.empty((1, d, h), **f32) if S else None)
+    mg = B.grads(g["dx"], g["w_gate"], g["w_up"], g["w_down"], g["b_gate"], g["b_up"],
+                 g["b_down"], g["w_up_shared"], g["w_down_shared"])
+    ws = torch.empty(max(B.moe_backward_workspace_bytes(c), 256), dtype=torch.uint8, device=dev)
+    dy = to_device(dy_bits, dev)
+    B.moe_backward(c, dl.weights(), dl.x, dy, s["idx"], s["w"], s["offsets"], s["pos"],
+                   s["x_perm"], s["y_perm"], s["imp"] if imp_w else None, imp_w, mg, ws)
+    torch.cuda.synchronize()
+    out = {("x" if n == "dx" else n): (to_f64(t) if t is not None else None) for n, t in g.items()}
+    return out, s, (dl, mg, ws, dy)
+
+
+def check_backward(L, capacity=0, imp_w=0.0, seed=0):
+    rng = np.random.default_rng(seed)
+    dy_bits = f32_to_bf16_bits(rng.standard_normal((L.cfg.T, L.cfg.d)).astype(np.float32))
+    got, s, _ = run_backward(L, dy_bits, capacity, imp_w)
+    ridx, _, _ = oracle.route(L)
+    assert np.array_equal(s["idx"].cpu().numpy(), ridx)
+    keep = oracle.capacity_keep(L.cfg, ridx, capacity) if capacity else None
+    ref = oracle.backward.backward(L, bf16_bits_to_f32(dy_bits), keep, imp_w, idx=ridx)
+    errs = {}
+    for n, r in ref.items():
+        gv = got.get(n)
+        assert gv is not None, f"no gradient for {n}"
+        assert np.all(np.isfinite(gv)), n
+        errs[n] = max_rel(gv.reshape(r.shape), r)
+        assert errs[n] <= GRAD_TOL, f"{n}: max-relative error {errs[n]:.3e}"
+    return errs
+
+
+CASES = {
+    "swiglu-bias": (dict(T=300, d=128, h=256, E=8, k=2, act=SWIGLU, dtype=BF16, bias=True), 0, 0.0),
+    "gelu-expert-bias": (dict(T=200, d=64, h=192, E=6, k=2, act=GELU, dtype=BF16, bias=True,
+                              expert_bias=True), 0, 0.0),
+    "shared-swiglu": (dict(T=129, d=128, h=128, E=16, k=4, act=SWIGLU, dtype=BF16, S=1), 0, 0.0),
+    "importance-loss": (dict(T=257, d=64, h=128, E=8, k=2, act=SWIGLU, dtype=BF16, bias=True), 0, 0.5),
+    "capacity-drops": (dict(T=400, d=64, h=128, E=6, k=2, act=SWIGLU, dtype=BF16, bias=True), 120, 0.2),
+    "e64-small-groups": (dict(T=100, d=64, h=64, E=64, k=6, act=SWIGLU, dtype=BF16, bias=True), 0, 0.0),
+    "large-groups": (dict(T=1200, d=256, h=512, E=3, k=2, act=SWIGLU, dtype=BF16, S=1), 0, 0.1),
+    "long-k-gelu": (dict(T=600, d=64, h=8256, E=2, k=1, act=GELU, dtype=BF16, expert_bias=True), 0, 0.0),
+}
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_backward_against_autograd(name):
+    kw, cap, imp_w = CASES[name]
+    L = random_layer(61, wstd=0.15, **kw)
+    if cap:
+        cfg = L.cfg
+        idx, _, _ = oracle.route(L)
+        assert oracle.capacity_keep(cfg, idx, cap).sum() < cfg.T * cfg.k
+    errs = check_backward(L, cap, imp_w)
+    print(name, {n: f"{e:.2e}" for n, e in errs.items()})
+
+
+def test_backward_is_deterministic():
+    L = random_layer(62, T=300, d=128, h=256, E=8, k=2, act=SWIGLU, dtype=BF16, bias=True, S=1)
+    dy = f32_to_bf16_bits(np.random.default_rng(1).standard_normal((300, 128)).astype(np.float32))
+    a, _, _ = run_backward(L, dy, imp_w=0.3)
+    b, _, _ = run_backward(L, dy, imp_w=0.3)
+    for n in a:
+        if a[n] is not None:
+            assert np.array_equal(a[n], b[n]), n
+
+
+def test_backward_zero_tokens():
+    L = random_layer(63, T=1, d=64, h=64, E=4, k=2, act=SWIGLU, dtype=BF16, bias=True)
+    L.cfg = L.cfg.with_(T=0)
+    L.x = np.zeros((0, 64), np.uint16)
+    dl = DeviceLayer.upload(L)
+    dev = dl.x.device
+    f32 = dict(dtype=torch.float32, device=dev)
+    gw = torch.full((4, 64), 7.0, **f32)
+    gb = torch.full((4,), 7.0, **f32)
+    gu = torch.full((4, 128, 64), 7.0, **f32)
+    gd = torch.full((4, 64, 64), 7.0, **f32)
+    mg = B.grads(None, gw, gu, gd, gb)
+    B.moe_backward(dl.cfg, dl.weights(), None, None, None, None, None, None, None, None,
+                   None, 0.0, mg, None)
+    torch.cuda.synchronize()
+    for t in (gw, gb, gu, gd):
+        assert t.eq(0).all()
