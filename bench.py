@@ -140,12 +140,13 @@ def main():
             sys.exit("--backward: bf16 layers only")
         f32 = dict(dtype=torch.float32, device=dev)
         n_up = cfg.n_up
-        g_t = dict(dx=torch.empty((T, d), dtype=dt, device=dev),
-                   w_gate=torch.empty((E, d), **f32), w_up=torch.empty((E, n_up, d), **f32),
-                   w_down=torch.empty((E, d, h), **f32),
+        b16 = dict(dtype=dt, device=dev)   # gradients of bf16 parameters
+        g_t = dict(dx=torch.empty((T, d), **b16),
+                   w_gate=torch.empty((E, d), **f32), w_up=torch.empty((E, n_up, d), **b16),
+                   w_down=torch.empty((E, d, h), **b16),
                    b_gate=torch.empty(E, **f32) if L.b_gate is not None else None,
-                   w_up_shared=torch.empty((1, n_up, d), **f32) if cfg.S else None,
-                   w_down_shared=torch.empty((1, d, h), **f32) if cfg.S else None)
+                   w_up_shared=torch.empty((1, n_up, d), **b16) if cfg.S else None,
+                   w_down_shared=torch.empty((1, d, h), **b16) if cfg.S else None)
         grads = B.grads(g_t["dx"], g_t["w_gate"], g_t["w_up"], g_t["w_down"], g_t["b_gate"],
                         dw_up_shared=g_t["w_up_shared"], dw_down_shared=g_t["w_down_shared"])
         ws_b = torch.empty(B.moe_backward_workspace_bytes(c), dtype=torch.uint8, device=dev)

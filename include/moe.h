@@ -254,7 +254,9 @@ moe_status_t moe_forward(const moe_config_t *cfg, const moe_weights_t *w,
  * in the forward).  bf16 layers and MOE_GATE_TOPK_SOFTMAX only (else
  * MOE_ERR_UNSUPPORTED); an expert capacity is honoured through pos (a
  * dropped slot passes no gradient to its expert; its gate still counts in
- * Importance).  Gradients are fp32 except dx (the layer dtype).
+ * Importance).  Every gradient has the dtype of its parameter: dx and the
+ * expert weight and bias gradients bf16, the router's fp32 (accumulation is
+ * fp32 throughout, one rounding at the end).
  *   x [T, d], dy [T, d]                  (device, in)
  *   saved from the forward (device, in): topk_idx, topk_w [T, k] (moe_route),
  *     offsets [E+1], pos [T*k], x_perm (moe_permute), y_perm [T*k + S*T, d]
@@ -262,21 +264,22 @@ moe_status_t moe_forward(const moe_config_t *cfg, const moe_weights_t *w,
  *   importance [E] fp32 or NULL (moe_permute's), importance_weight: the
  *     weight of the CV^2(Importance) term (ignored when importance is NULL)
  *   grads: every pointer device memory, written in full:
- *     dx [T, d] dtype; dw_gate [E, d]; db_gate [E] or NULL; dw_up, dw_down
- *     with the shapes of w_up, w_down; db_up [E, h], db_down [E, d] or NULL
- *     (GELU); dw_up_shared [1, 2h, d], dw_down_shared [1, d, h] iff S = 1
+ *     dx [T, d] bf16; dw_gate [E, d] fp32; db_gate [E] fp32 or NULL; dw_up,
+ *     dw_down bf16 with the shapes of w_up, w_down; db_up [E, h], db_down
+ *     [E, d] bf16 or NULL (GELU); dw_up_shared [1, 2h, d], dw_down_shared
+ *     [1, d, h] bf16 iff S = 1
  *   ws >= moe_backward_workspace_bytes(cfg) bytes (device, scratch)
  * Sums run in a fixed order: results are deterministic. */
 typedef struct {
   void *dx;
   float *dw_gate;
   float *db_gate;
-  float *dw_up;
-  float *dw_down;
-  float *db_up;
-  float *db_down;
-  float *dw_up_shared;
-  float *dw_down_shared;
+  void *dw_up;
+  void *dw_down;
+  void *db_up;
+  void *db_down;
+  void *dw_up_shared;
+  void *dw_down_shared;
 } moe_grads_t;
 
 moe_status_t moe_backward_workspace_bytes(const moe_config_t *cfg, size_t *bytes);

@@ -469,12 +469,16 @@ moe_status_t moe_backward(const moe_config_t *cfg, const moe_weights_t *w, const
   if (T == 0) {
     hipError_t e = moe::launch_fill_f32(g->dw_gate, E * d, stream);
     if (e == hipSuccess) e = moe::launch_fill_f32(g->db_gate, E, stream);
-    if (e == hipSuccess) e = moe::launch_fill_f32(g->dw_up, E * nup * d, stream);
-    if (e == hipSuccess) e = moe::launch_fill_f32(g->dw_down, E * d * h, stream);
-    if (e == hipSuccess) e = moe::launch_fill_f32(g->db_up, E * h, stream);
-    if (e == hipSuccess) e = moe::launch_fill_f32(g->db_down, E * d, stream);
-    if (e == hipSuccess) e = moe::launch_fill_f32(g->dw_up_shared, S * nup * d, stream);
-    if (e == hipSuccess) e = moe::launch_fill_f32(g->dw_down_shared, S * d * h, stream);
+    // bf16 gradients: a zero bf16 is two zero bytes; every count is even
+    auto zero16 = [&](void *p, int64_t n) {
+      return moe::launch_fill_f32(static_cast<float *>(p), n / 2, stream);
+    };
+    if (e == hipSuccess) e = zero16(g->dw_up, E * nup * d);
+    if (e == hipSuccess) e = zero16(g->dw_down, E * d * h);
+    if (e == hipSuccess) e = zero16(g->db_up, E * h);
+    if (e == hipSuccess) e = zero16(g->db_down, E * d);
+    if (e == hipSuccess) e = zero16(g->dw_up_shared, S * nup * d);
+    if (e == hipSuccess) e = zero16(g->dw_down_shared, S * d * h);
     return hip_status(e);
   }
   if (!dev_ok(x) || !dev_ok(dy) || !dev_ok(topk_idx) || !dev_ok(topk_w) || !dev_ok(offsets) ||
@@ -511,12 +515,12 @@ moe_status_t moe_backward(const moe_config_t *cfg, const moe_weights_t *w, const
   a.dx = static_cast<uint16_t *>(g->dx);
   a.dw_gate = g->dw_gate;
   a.db_gate = g->db_gate;
-  a.dw_up = g->dw_up;
-  a.dw_down = g->dw_down;
-  a.db_up = g->db_up;
-  a.db_down = g->db_down;
-  a.dw_up_s = g->dw_up_shared;
-  a.dw_down_s = g->dw_down_shared;
+  a.dw_up = static_cast<uint16_t *>(g->dw_up);
+  a.dw_down = static_cast<uint16_t *>(g->dw_down);
+  a.db_up = static_cast<uint16_t *>(g->db_up);
+  a.db_down = static_cast<uint16_t *>(g->db_down);
+  a.dw_up_s = static_cast<uint16_t *>(g->dw_up_shared);
+  a.dw_down_s = static_cast<uint16_t *>(g->dw_down_shared);
   moe::BwdBuffers b{};
   b.gimp = at<float>(ws, L.gimp);
   b.ds = at<float>(ws, L.ds);

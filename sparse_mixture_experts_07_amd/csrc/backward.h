@@ -30,7 +30,8 @@ struct BwdArgs {
   float w_imp;
   const uint16_t *x_perm, *y_perm;
   uint16_t *dx;
-  float *dw_gate, *db_gate, *dw_up, *dw_down, *db_up, *db_down, *dw_up_s, *dw_down_s;
+  float *dw_gate, *db_gate;   // fp32, the router's dtype
+  uint16_t *dw_up, *dw_down, *db_up, *db_down, *dw_up_s, *dw_down_s;   // bf16
 };
 
 hipError_t launch_backward(const BwdArgs &a, const BwdBuffers &b, hipStream_t s);

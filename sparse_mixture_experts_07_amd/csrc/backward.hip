@@ -13,7 +13,7 @@
 //            ds_j = w_j (dw'_j - sum_i w_i dw'_i), dw'_j = dw_j + the
 //            Importance term of expert i_j (softmax over the kept scores)
 //   act      H = act(A) from the recomputed pre-activations A; dA = act'(A) dH
-//   layout   group columns padded to 32 for the transposed copies, and the
+//   layout   group columns padded to 64 for the transposed copies, and the
 //            grouped row behind every column
 //   transpose activations [R, C] -> [C, Rp] (group columns, zero padding),
 //            weights [B, R, C] -> [B, C, R]
@@ -205,7 +205,7 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_act_grad_kernel(
 
 // Group g's rows: routed groups [offsets[g], offsets[g+1]) (clamped), the
 // shared group (g == E) rows [T*k, T*k + T).  poff: exclusive scan of the
-// row counts rounded up to 32.  One workgroup of kMaxExperts + 1 <= 2 *
+// row counts rounded up to 64.  One workgroup of kMaxExperts + 1 <= 2 *
 // 256 groups: thread t owns groups 2t and 2t + 1.
 __global__ __launch_bounds__(kBwdThreads) void bwd_layout_kernel(
     const int32_t *__restrict__ offsets, int E, int S, int T, int routed,
@@ -225,7 +225,7 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_layout_kernel(
     } else if (g < G) {
       n = T;
     }
-    c[q] = (n + 31) / 32 * 32;
+    c[q] = (n + 63) / 64 * 64;
   }
   sc[tid] = c[0] + c[1];
   __syncthreads();
@@ -367,10 +367,12 @@ __global__ void bwd_ds_cols_kernel(const float *__restrict__ dsp, const int32_t 
 
 // out[g][c] = sum over group g's columns j of wcol[j] * at[c][j] (wcol NULL:
 // 1), for groups g < G; one wavefront per (g, c): lanes take columns
-// j = lane, lane + 64, ... in order, then a fixed butterfly.
+// j = lane, lane + 64, ... in order, then a fixed butterfly.  OUT: float
+// (router gradients) or uint16_t (bf16 bias gradients).
+template <typename OUT>
 __global__ __launch_bounds__(kWave) void bwd_rowsum_kernel(
     const uint16_t *__restrict__ at, int C, int Rp, const int32_t *__restrict__ poff,
-    const float *__restrict__ wcol, float *__restrict__ out) {
+    const float *__restrict__ wcol, OUT *__restrict__ out) {
   const int c = blockIdx.x;
   const int g = blockIdx.y;
   const int lane = threadIdx.x;
@@ -383,7 +385,12 @@ __global__ __launch_bounds__(kWave) void bwd_rowsum_kernel(
   }
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) s += __shfl_xor(s, off);
-  if (lane == 0) out[(int64_t)g * C + c] = s;
+  if (lane == 0) {
+    if constexpr (sizeof(OUT) == 2)
+      out[(int64_t)g * C + c] = (OUT)(pack_bf16x2(s, 0.0f) & 0xffffu);
+    else
+      out[(int64_t)g * C + c] = s;
+  }
 }
 
 // out[g] = sum over group g's columns of vals[j]; one wavefront per group.
@@ -471,7 +478,7 @@ hipError_t launch_permute(const int32_t *idx, const float *w, const void *x, int
                           void *x_perm, int32_t *hist, int32_t *full_off, float *perm_w,
                           hipStream_t s);
 hipError_t launch_wgrad_bf16(const int32_t *poff, int G, int Rp, int M, int N, const void *at,
-                             const void *bt, float *out, float *out_last, hipStream_t s);
+                             const void *bt, void *out, void *out_last, hipStream_t s);
 
 static unsigned grid_for(int64_t work, int64_t per_block) {
   int64_t b = (work + per_block - 1) / per_block;
@@ -485,9 +492,13 @@ hipError_t launch_fill_f32(float *p, int64_t n, hipStream_t s) {
   return hipGetLastError();
 }
 
+// Columns of the transposed copies: every group padded to 64, rounded to an
+// odd multiple of 64 so that the row stride is an odd number of 128-byte
+// lines (rows then spread over the cache sets instead of aliasing).
 int64_t bwd_padded_cols(int64_t T, int k, int E, int S) {
   const int64_t R = T * k + (int64_t)S * T;
-  return (R + 32 * (int64_t)(E + S) + 63) / 64 * 64;
+  const int64_t n64 = (R + 64 * (int64_t)(E + S) + 63) / 64;
+  return 64 * (n64 | 1);
 }
 
 hipError_t launch_backward(const BwdArgs &a, const BwdBuffers &b, hipStream_t s) {
@@ -557,9 +568,11 @@ hipError_t launch_backward(const BwdArgs &a, const BwdBuffers &b, hipStream_t s)
                             S ? a.dw_down_s : nullptr, s));
   MOE_TRY(launch_wgrad_bf16(b.poff, G, Rp, nup, d, b.dAT, b.xpT, a.dw_up,
                             S ? a.dw_up_s : nullptr, s));
-  if (a.db_down) bwd_rowsum_kernel<<<dim3(d, E), kWave, 0, s>>>(b.dypT, d, Rp, b.poff, nullptr,
-                                                               a.db_down);
-  if (a.db_up) bwd_rowsum_kernel<<<dim3(h, E), kWave, 0, s>>>(b.dAT, h, Rp, b.poff, nullptr,
+  if (a.db_down)
+    bwd_rowsum_kernel<uint16_t><<<dim3(d, E), kWave, 0, s>>>(b.dypT, d, Rp, b.poff, nullptr,
+                                                             a.db_down);
+  if (a.db_up)
+    bwd_rowsum_kernel<uint16_t><<<dim3(h, E), kWave, 0, s>>>(b.dAT, h, Rp, b.poff, nullptr,
                                                              a.db_up);
   // router: dW_g[e] = sum over every assignment to e of ds * x, db_g[e] =
   // sum of ds.  A dropped slot has a score gradient too (its gate shapes the
@@ -587,7 +600,7 @@ hipError_t launch_backward(const BwdArgs &a, const BwdBuffers &b, hipStream_t s)
   }
   bwd_scatter_ds_kernel<<<grid_for(routed, 256), 256, 0, s>>>(b.ds, pos_r, routed, routed, b.dsp);
   bwd_ds_cols_kernel<<<grid_for(Rp, 256), 256, 0, s>>>(b.dsp, colsrc_r, Rp, routed, b.ds_cols);
-  bwd_rowsum_kernel<<<dim3(d, E), kWave, 0, s>>>(xT, d, Rp, poff_r, b.ds_cols, a.dw_gate);
+  bwd_rowsum_kernel<float><<<dim3(d, E), kWave, 0, s>>>(xT, d, Rp, poff_r, b.ds_cols, a.dw_gate);
   if (a.db_gate) bwd_group_sum_kernel<<<E, kWave, 0, s>>>(b.ds_cols, poff_r, a.db_gate);
   return hipGetLastError();
 #undef MOE_TRY

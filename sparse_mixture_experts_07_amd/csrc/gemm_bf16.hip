@@ -704,90 +704,229 @@ void gemm_dma_kernel(GemmArgs a) {
   }
 }
 
+// The main loop of gemm_dma_kernel for one tile, taking the tile's stage
+// count: k stages 0 .. nk-1 (nk even) of the operands behind t's
+// descriptors, row stride row_bytes, into acc.  (The forward kernel keeps
+// its own copy of this loop: folded into a function it compiled slower.)
+template <int BM, int BNW, int WM, int WN, int MODE>
+struct DmaLoop {
+  static constexpr int BK = 32, NB = 4, NW = WM * WN;
+  using TM = TileMath<BM, BNW, WM, WN, BK, MODE>;
+  static constexpr int CH = TM::CH, FM = TM::FM, FW = TM::FW;
+  static constexpr int ABLK = BM / 16, WBLK = BNW / 16;   // 16-row DMA blocks
+  static constexpr int NBLK = ABLK + WBLK;
+  // blocks per wave; when they do not split evenly the last waves repeat
+  // the stage's last block (same data to the same place), so that every
+  // wave issues the same number of DMAs and one vmcnt fits all
+  static constexpr int BPW = (NBLK + NW - 1) / NW;
+  static_assert(CH == 4, "k32 stages");
+  // interleave: QM MFMAs per operand read or DMA, then the rest
+  static constexpr int NMEM = FM + FW + BPW;
+  static constexpr int QM = (FW * FM) / NMEM >= 2 ? 2 : 1;
+  static_assert(QM * NMEM <= FW * FM, "operand traffic fits the MFMA stream");
+
+  static __device__ __forceinline__ void run(const Tile &t, int nk, uint32_t row_bytes,
+                                             u32x4_t (*As)[BM * CH], u32x4_t (*Ws)[BNW * CH],
+                                             int wave, int wm, int wn,
+                                             f32x4_t (&acc)[FW][FM]) {
+    const int lane = threadIdx.x % 64;
+    // lane -> row lane / 4, 16-byte chunk lane % 4 of a 16-row block
+    const uint32_t voff = (uint32_t)(lane / 4) * row_bytes + (uint32_t)(lane % 4) * 16u;
+    // wave w moves blocks BPW w .. BPW w + BPW - 1 of the stage: token
+    // blocks first, then weight blocks (SwiGLU: gate rows from one
+    // descriptor, up rows from the other)
+    auto dma = [&](int s) {
+#pragma unroll
+      for (int i = 0; i < BPW; ++i) {
+        const int blk = min(wave * BPW + i, NBLK - 1);
+        __amdgpu_buffer_rsrc_t rs;
+        u32x4_t *dst;
+        int row;
+        if (blk < ABLK) {
+          rs = t.rs_a;
+          dst = As[s % NB] + blk * 64;
+          row = blk * 16;
+        } else {
+          const int wb = blk - ABLK;
+          dst = Ws[s % NB] + wb * 64;
+          if (TM::SWI && wb >= WBLK / 2) {
+            rs = t.rs_w1;
+            row = (wb - WBLK / 2) * 16;
+          } else {
+            rs = t.rs_w0;
+            row = wb * 16;
+          }
+        }
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, dst, 16, voff,
+                                                 row * (int)row_bytes + s * (BK * 2), 0, 0);
+      }
+    };
+
+    bf16x8_t fa0[FM], fw0[FW], fa1[FM], fw1[FW];
+    auto read_stage = [&](int buf, bf16x8_t(&fa)[FM], bf16x8_t(&fw)[FW]) {
+#pragma unroll
+      for (int j = 0; j < FM; ++j) fa[j] = TM::read_a(As[buf], 0, j, wm);
+#pragma unroll
+      for (int i = 0; i < FW; ++i) fw[i] = TM::read_w(Ws[buf], i, wn);
+    };
+    auto iteration = [&](int s, bf16x8_t(&fa_cur)[FM], bf16x8_t(&fw_cur)[FW],
+                         bf16x8_t(&fa_nxt)[FM], bf16x8_t(&fw_nxt)[FW]) {
+      read_stage((s + 1) % NB, fa_nxt, fw_nxt);
+#pragma unroll
+      for (int i = 0; i < FW; ++i)
+#pragma unroll
+        for (int j = 0; j < FM; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fw_cur[i], fa_cur[j], acc[i][j],
+                                                               0, 0, 0);
+      dma(s + 4);
+      // operand reads one per QM MFMAs, then the DMAs one per QM MFMAs
+#pragma unroll
+      for (int q = 0; q < FM + FW; ++q) {
+        __builtin_amdgcn_sched_group_barrier(0x008, QM, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+#pragma unroll
+      for (int q = 0; q < BPW; ++q) {
+        __builtin_amdgcn_sched_group_barrier(0x008, QM, 0);
+        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+      }
+      if constexpr (FW * FM > QM * NMEM)
+        __builtin_amdgcn_sched_group_barrier(0x008, FW * FM - QM * NMEM, 0);
+      // Stage s+2 has landed (stages s+3 and s+4 may still be in flight) and
+      // this wave's operand reads are done; then a plain barrier (a fence
+      // would also wait for the DMAs still in flight).  The empty asm
+      // statements keep the compiler from moving LDS accesses across it.
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(2 * BPW));
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+    };
+
+    dma(0);
+    dma(1);
+    dma(2);
+    dma(3);
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(2 * BPW));   // stages 0 and 1
+    __syncthreads();
+    read_stage(0, fa0, fw0);
+
+    // two stages per trip so the register sets are named statically (nk is
+    // even)
+    for (int s = 0; s < nk; s += 2) {
+      iteration(s, fa0, fw0, fa1, fw1);
+      iteration(s + 1, fa1, fw1, fa0, fw0);
+    }
+    // the next tile's first DMAs go to buffers that the last (unused) DMAs
+    // and reads above may still touch
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+    __syncthreads();
+  }
+};
+
 // ------------------------------------------------------ weight gradients --
 // dW[g] = A_g^T B_g summed over the rows of group g (the backward pass of
 // the grouped GEMMs), from K-contiguous transposed copies At [M, Rp] and Bt
 // [N, Rp] whose group column ranges [poff[g], poff[g+1]) are zero-padded to
-// multiples of 32:  out[g][m][n] = sum_j At[m][j] * Bt[n][j], fp32.  The
+// multiples of 64:  out[g][m][n] = sum_j At[m][j] * Bt[n][j], accumulated in
+// fp32 and rounded once to bf16 (the dtype of the weights).  The
 // same tile arithmetic as the forward kernels with the group's rows as the
-// contraction: one workgroup per (group, m-tile, n-tile), k loop over the
-// group's columns (none for an empty group: its tiles store zeros).
+// contraction, k loop over the group's columns (none for an empty group:
+// its tiles store zeros).
 struct WgradArgs {
-  const int32_t *poff;   // [G + 1], multiples of 32
+  const int32_t *poff;   // [G + 1], multiples of 64
   int G, Rp, M, N;
   const uint16_t *at;    // [M, Rp]
   const uint16_t *bt;    // [N, Rp]
-  float *out;            // [G][M][N] (or [G - 1] when out_last is set)
-  float *out_last;       // the last group's [M][N] stored apart, or NULL
+  uint16_t *out;         // [G][M][N] bf16 (or [G - 1] when out_last is set)
+  uint16_t *out_last;    // the last group's [M][N] stored apart, or NULL
   int m_tiles, n_tiles;
 };
 
+// Persistent grid over the (group, m-tile, n-tile) space in the slice order
+// of the forward kernels; each tile runs the DMA-fed main loop over its
+// group's columns (padded to 64, so the stage count is even) with the
+// descriptors based at the group's first column.
 template <int BM, int BNW, int WM, int WN>
-__global__ __launch_bounds__(WM *WN * 64) __attribute__((amdgpu_waves_per_eu(2)))
+__global__ __launch_bounds__(WM *WN * 64) __attribute__((amdgpu_waves_per_eu(WM * WN / 4)))
 void gemm_wgrad_kernel(WgradArgs a) {
-  using TM = TileMath<BM, BNW, WM, WN, 32, kDown>;
-  constexpr int CH = TM::CH, A_LD = TM::A_LD, W_LD = TM::W_LD;
+  using DL = DmaLoop<BM, BNW, WM, WN, kDown>;
+  using TM = typename DL::TM;
+  constexpr int CH = TM::CH, NB = DL::NB, NT = TM::NT;
   constexpr int FM = TM::FM, FW = TM::FW, WTM = TM::WTM, WTW = TM::WTW;
-  __shared__ u32x4_t As[2][BM * CH];
-  __shared__ u32x4_t Ws[2][BNW * CH];
-  const int wave = threadIdx.x / 64;
+  // the operand buffers, reused after the main loop to stage the output
+  // tile (BM rows of BNW bf16) so that it leaves in whole 16-byte chunks
+  constexpr int LDS_CHUNKS = NB * (BM + BNW) * CH;
+  static_assert(BM * BNW * 2 <= LDS_CHUNKS * 16, "output tile fits the operand buffers");
+  constexpr int OCH = BNW / 8;   // 16-byte chunks per output row
+  __shared__ u32x4_t lds[LDS_CHUNKS];
+  auto As = reinterpret_cast<u32x4_t(*)[BM * CH]>(lds);
+  auto Ws = reinterpret_cast<u32x4_t(*)[BNW * CH]>(lds + NB * BM * CH);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / 64);
   const int wm = wave / WN;
   const int wn = wave % WN;
-  const int per_g = a.m_tiles * a.n_tiles;
-  const int g = blockIdx.x / per_g;
-  const int local = blockIdx.x % per_g;
-  Tile t;
-  t.g = g;
-  t.grow0 = 0;
-  t.rows = a.M;
-  t.m0 = (local % a.m_tiles) * BM;
-  t.n0 = (local / a.m_tiles) * BNW;
-  const int c0 = __builtin_amdgcn_readfirstlane(a.poff[g]);
-  const int c1 = __builtin_amdgcn_readfirstlane(a.poff[g + 1]);
-  const int nk = c1 > c0 ? (c1 - c0) / 32 : 0;
-  const uint32_t row_bytes = (uint32_t)a.Rp * 2u;
-  const int arows = min(BM, a.M - t.m0);
-  const int wrows = min(BNW, a.N - t.n0);
-  t.rs_a = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint16_t *>(a.at + (int64_t)t.m0 * a.Rp + c0), 0, arows * row_bytes, kBufferWord3);
-  t.rs_w0 = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint16_t *>(a.bt + (int64_t)t.n0 * a.Rp + c0), 0, wrows * row_bytes, kBufferWord3);
-  t.rs_w1 = t.rs_w0;
-  const uint32_t v0 = TM::voff0(row_bytes);
-
-  f32x4_t acc[FW][FM];
-#pragma unroll
-  for (int i = 0; i < FW; ++i)
-#pragma unroll
-    for (int j = 0; j < FM; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  if (nk > 0) {
-    u32x4_t ra[A_LD], rw[W_LD];
-    TM::gload(t, v0, row_bytes, ra, rw, 0);
-    TM::lstore(As[0], Ws[0], ra, rw);
-    __syncthreads();
-    for (int kt = 0; kt < nk; ++kt) {
-      const int buf = kt & 1;
-      const bool more = kt + 1 < nk;
-      if (more) TM::gload(t, v0, row_bytes, ra, rw, kt + 1);
-      __builtin_amdgcn_sched_barrier(0);
-      TM::compute(As[buf], Ws[buf], acc, wm, wn);
-      __builtin_amdgcn_sched_barrier(0);
-      if (more) TM::lstore(As[buf ^ 1], Ws[buf ^ 1], ra, rw);
-      __syncthreads();
-    }
-  }
-  // lane owns columns 4*(lane/16)+0..3 of row lane%16 of each fragment
-  float *o = (a.out_last && g == a.G - 1) ? a.out_last : a.out + (int64_t)g * a.M * a.N;
   const int lane = threadIdx.x % 64;
+  const int per_g = a.m_tiles * a.n_tiles;
+  const int total = a.G * per_g;
+  const uint32_t row_bytes = (uint32_t)a.Rp * 2u;
+
+  for (int it = 0;; ++it) {
+    const int L = slice_tile(it);
+    if (L >= total) break;
+    const int g = L / per_g;
+    const int local = L % per_g;
+    Tile t;
+    t.g = g;
+    t.grow0 = 0;
+    t.rows = a.M;
+    t.m0 = (local % a.m_tiles) * BM;
+    t.n0 = (local / a.m_tiles) * BNW;
+    const int c0 = __builtin_amdgcn_readfirstlane(a.poff[g]);
+    const int c1 = __builtin_amdgcn_readfirstlane(a.poff[g + 1]);
+    const int nk = c1 > c0 ? (c1 - c0) / 32 : 0;
+    const int arows = min(BM, a.M - t.m0);
+    const int wrows = min(BNW, a.N - t.n0);
+    t.rs_a = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t *>(a.at + (int64_t)t.m0 * a.Rp + c0), 0, arows * row_bytes, kBufferWord3);
+    t.rs_w0 = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t *>(a.bt + (int64_t)t.n0 * a.Rp + c0), 0, wrows * row_bytes, kBufferWord3);
+    t.rs_w1 = t.rs_w0;
+
+    f32x4_t acc[FW][FM];
 #pragma unroll
-  for (int i = 0; i < FW; ++i) {
-    const int col = t.n0 + wn * WTW + i * 16 + 4 * (lane / 16);
+    for (int i = 0; i < FW; ++i)
 #pragma unroll
-    for (int j = 0; j < FM; ++j) {
-      const int m = t.m0 + wm * WTM + j * 16 + lane % 16;
-      if (col < a.N && m < a.M)
-        *reinterpret_cast<f32x4_t *>(o + (int64_t)m * a.N + col) = acc[i][j];
+      for (int j = 0; j < FM; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    DL::run(t, nk, row_bytes, As, Ws, wave, wm, wn, acc);
+
+    // lane owns columns 4*(lane/16)+0..3 of row lane%16 of each fragment:
+    // 8 bytes into the staged tile, whose 16-byte chunks are XOR-swizzled by
+    // row (chunk c of row r at c ^ (r & 7)) to spread a fragment's 16 rows
+    // over the banks
+    char *st = reinterpret_cast<char *>(lds);
+#pragma unroll
+    for (int i = 0; i < FW; ++i) {
+      const int col = wn * WTW + i * 16 + 4 * (lane / 16);
+#pragma unroll
+      for (int j = 0; j < FM; ++j) {
+        const int r = wm * WTM + j * 16 + lane % 16;
+        uint2 v;
+        v.x = pack_bf16x2(acc[i][j][0], acc[i][j][1]);
+        v.y = pack_bf16x2(acc[i][j][2], acc[i][j][3]);
+        *reinterpret_cast<uint2 *>(st + r * (BNW * 2) + (((col >> 3) ^ (r & 7)) << 4) +
+                                   (col & 7) * 2) = v;
+      }
     }
+    __syncthreads();
+    uint16_t *o = (a.out_last && g == a.G - 1) ? a.out_last : a.out + (int64_t)g * a.M * a.N;
+#pragma unroll
+    for (int q = threadIdx.x; q < BM * OCH; q += NT) {
+      const int r = q / OCH, c = q % OCH;
+      const u32x4_t v = lds[r * OCH + (c ^ (r & 7))];
+      if (t.m0 + r < a.M && t.n0 + 8 * c < a.N)
+        *reinterpret_cast<u32x4_t *>(o + (int64_t)(t.m0 + r) * a.N + t.n0 + 8 * c) = v;
+    }
+    // the next tile's first DMAs overwrite the staged tile
+    __syncthreads();
   }
 }
 
@@ -928,8 +1067,8 @@ hipError_t launch_grouped_linear_bf16(const int32_t *offsets, int E, int S, int 
 }
 
 hipError_t launch_wgrad_bf16(const int32_t *poff, int G, int Rp, int M, int N, const void *at,
-                             const void *bt, float *out, float *out_last, hipStream_t s) {
-  constexpr int BM = 128, BNW = 128;
+                             const void *bt, void *out, void *out_last, hipStream_t s) {
+  constexpr int BM = 256, BNW = 256;
   WgradArgs a{};
   a.poff = poff;
   a.G = G;
@@ -938,13 +1077,24 @@ hipError_t launch_wgrad_bf16(const int32_t *poff, int G, int Rp, int M, int N, c
   a.N = N;
   a.at = static_cast<const uint16_t *>(at);
   a.bt = static_cast<const uint16_t *>(bt);
-  a.out = out;
-  a.out_last = out_last;
+  a.out = static_cast<uint16_t *>(out);
+  a.out_last = static_cast<uint16_t *>(out_last);
   a.m_tiles = (M + BM - 1) / BM;
   a.n_tiles = (N + BNW - 1) / BNW;
-  const int64_t blocks = (int64_t)G * a.m_tiles * a.n_tiles;
-  gemm_wgrad_kernel<BM, BNW, 2, 2><<<dim3((unsigned)blocks), dim3(256), 0, s>>>(a);
-  return hipGetLastError();
+  static int per_cu = 0;
+  const void *kern = reinterpret_cast<const void *>(&gemm_wgrad_kernel<BM, BNW, 4, 2>);
+  if (!per_cu) {
+    int nb = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, kern, 512, 0) != hipSuccess || nb <= 0)
+      nb = 1;
+    per_cu = nb;
+  }
+  int64_t grid = (int64_t)num_cus() * per_cu;
+  const int64_t tiles = (int64_t)G * a.m_tiles * a.n_tiles;
+  if (tiles < grid) grid = tiles;
+  grid = ((grid + 7) / 8) * 8;
+  void *args[] = {&a};
+  return hipLaunchKernel(kern, dim3((unsigned)grid), dim3(512), args, 0, s);
 }
 
 hipError_t launch_expert_up_bf16(bool swiglu, const int32_t *offsets, int E, int S,

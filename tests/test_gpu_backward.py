@@ -56,14 +56,15 @@ def run_backward(L, dy_bits, capacity=0, imp_w=0.0):
     E, d, h, S = cfg.E, cfg.d, cfg.h, cfg.S
     nup = 2 * h if cfg.act == SWIGLU else h
     f32 = dict(dtype=torch.float32, device=dev)
-    g = dict(dx=torch.empty((cfg.T, d), dtype=torch.bfloat16, device=dev),
-             w_gate=torch.empty((E, d), **f32), w_up=torch.empty((E, nup, d), **f32),
-             w_down=torch.empty((E, d, h), **f32),
+    b16 = dict(dtype=torch.bfloat16, device=dev)   # gradients of bf16 parameters
+    g = dict(dx=torch.empty((cfg.T, d), **b16),
+             w_gate=torch.empty((E, d), **f32), w_up=torch.empty((E, nup, d), **b16),
+             w_down=torch.empty((E, d, h), **b16),
              b_gate=torch.empty(E, **f32) if L.b_gate is not None else None,
-             b_up=torch.empty((E, h), **f32) if L.b_up is not None else None,
-             b_down=torch.empty((E, d), **f32) if L.b_down is not None else None,
-             w_up_shared=torch.empty((1, nup, d), **f32) if S else None,
-             w_down_shared=torch.empty((1, d, h), **f32) if S else None)
+             b_up=torch.empty((E, h), **b16) if L.b_up is not None else None,
+             b_down=torch.empty((E, d), **b16) if L.b_down is not None else None,
+             w_up_shared=torch.empty((1, nup, d), **b16) if S else None,
+             w_down_shared=torch.empty((1, d, h), **b16) if S else None)
     mg = B.grads(g["dx"], g["w_gate"], g["w_up"], g["w_down"], g["b_gate"], g["b_up"],
                  g["b_down"], g["w_up_shared"], g["w_down_shared"])
     ws = torch.empty(max(B.moe_backward_workspace_bytes(c), 256), dtype=torch.uint8, device=dev)
@@ -137,8 +138,8 @@ def test_backward_zero_tokens():
     f32 = dict(dtype=torch.float32, device=dev)
     gw = torch.full((4, 64), 7.0, **f32)
     gb = torch.full((4,), 7.0, **f32)
-    gu = torch.full((4, 128, 64), 7.0, **f32)
-    gd = torch.full((4, 64, 64), 7.0, **f32)
+    gu = torch.full((4, 128, 64), 7.0, dtype=torch.bfloat16, device=dev)
+    gd = torch.full((4, 64, 64), 7.0, dtype=torch.bfloat16, device=dev)
     mg = B.grads(None, gw, gu, gd, gb)
     B.moe_backward(dl.cfg, dl.weights(), None, None, None, None, None, None, None, None,
                    None, 0.0, mg, None)
