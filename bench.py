@@ -152,6 +152,7 @@ def main():
         ws_b = torch.empty(B.moe_backward_workspace_bytes(c), dtype=torch.uint8, device=dev)
         dy = torch.randn((T, d), generator=torch.Generator(device="cpu").manual_seed(1)).to(
             device=dev, dtype=dt)
+        preact = torch.empty((R, cfg.n_up), dtype=dt, device=dev)
         bwd_evs = []
 
     def step(ev=None):
@@ -159,7 +160,10 @@ def main():
         B.moe_permute(c, idx, tw, dl.x, offsets, perm_src, pos, imp, stats, x_perm, ws)
         if ev is not None:
             ev[0].record()
-        B.moe_expert_up(c, W, x_perm, dl.x, offsets, hidden)
+        if args.backward:   # the training forward keeps the pre-activations
+            B.moe_expert_up_train(c, W, x_perm, dl.x, offsets, hidden, preact)
+        else:
+            B.moe_expert_up(c, W, x_perm, dl.x, offsets, hidden)
         if ev is not None:
             ev[1].record()
         B.moe_expert_down(c, W, hidden, offsets, y_perm)
@@ -170,7 +174,7 @@ def main():
                                 torch.cuda.Event(enable_timing=True)))
                 bwd_evs[-1][0].record()
             B.moe_backward(c, W, dl.x, dy, idx, tw, offsets, pos, x_perm, y_perm, imp, 0.01,
-                           grads, ws_b)
+                           grads, ws_b, hidden=hidden, preact=preact)
             if ev is not None:
                 bwd_evs[-1][1].record()
 

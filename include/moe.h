@@ -42,7 +42,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 3
+#define MOE_ABI_VERSION 4
 
 typedef enum {
   MOE_OK = 0,
@@ -217,6 +217,17 @@ moe_status_t moe_expert_up(const moe_config_t *cfg, const moe_weights_t *w,
 
 /* Down projection of every group: y_perm[r] = W2[e] hidden[r] (+ b2[e]).
  *   hidden [R, h] dtype (in), y_perm [R, d] dtype (out) */
+/* The up projection of a training step: moe_expert_up, and the expert
+ * pre-activations that the backward pass differentiates through, so that
+ * moe_backward need not recompute them.  bf16 layers only (else
+ * MOE_ERR_UNSUPPORTED).
+ *   hidden [R, h] bf16 (out) as for moe_expert_up
+ *   preact [R, N_up] bf16 (out): SwiGLU x W1^T (gate rows, columns 0..h-1)
+ *          and x W3^T (up rows, columns h..2h-1); GELU x W1^T + b1 */
+moe_status_t moe_expert_up_train(const moe_config_t *cfg, const moe_weights_t *w,
+                                 const void *x_perm, const void *x, const int32_t *offsets,
+                                 void *hidden, void *preact, hipStream_t stream);
+
 moe_status_t moe_expert_down(const moe_config_t *cfg, const moe_weights_t *w,
                              const void *hidden, const int32_t *offsets,
                              void *y_perm, hipStream_t stream);
@@ -249,9 +260,7 @@ moe_status_t moe_forward(const moe_config_t *cfg, const moe_weights_t *w,
  * with the top-k selection of the forward held fixed (the selection has no
  * derivative, so the router learns through the softmax weights only:
  * techfeed summary, "The hardest part: making the router trainable";
- * Importance and its CV^2: Qiita summary, "Load-balancing losses").  The
- * expert pre-activations are recomputed from x_perm (no activation storage
- * in the forward).  bf16 layers and MOE_GATE_TOPK_SOFTMAX only (else
+ * Importance and its CV^2: Qiita summary, "Load-balancing losses").  bf16 layers and MOE_GATE_TOPK_SOFTMAX only (else
  * MOE_ERR_UNSUPPORTED); an expert capacity is honoured through pos (a
  * dropped slot passes no gradient to its expert; its gate still counts in
  * Importance).  Every gradient has the dtype of its parameter: dx and the
@@ -261,6 +270,9 @@ moe_status_t moe_forward(const moe_config_t *cfg, const moe_weights_t *w,
  *   saved from the forward (device, in): topk_idx, topk_w [T, k] (moe_route),
  *     offsets [E+1], pos [T*k], x_perm (moe_permute), y_perm [T*k + S*T, d]
  *     (the expert outputs, moe_expert_down / moe_expert_ffn)
+ *   hidden [R, h], preact [R, N_up] bf16 or NULL (moe_expert_up_train's):
+ *     when preact is NULL the pre-activations are recomputed (one more up
+ *     projection); when hidden is NULL it is formed from the pre-activations
  *   importance [E] fp32 or NULL (moe_permute's), importance_weight: the
  *     weight of the CV^2(Importance) term (ignored when importance is NULL)
  *   grads: every pointer device memory, written in full:
@@ -288,6 +300,7 @@ moe_status_t moe_backward(const moe_config_t *cfg, const moe_weights_t *w,
                           const void *x, const void *dy, const int32_t *topk_idx,
                           const float *topk_w, const int32_t *offsets,
                           const int32_t *pos, const void *x_perm, const void *y_perm,
+                          const void *hidden, const void *preact,
                           const float *importance, float importance_weight,
                           const moe_grads_t *grads, void *ws, size_t ws_bytes,
                           hipStream_t stream);

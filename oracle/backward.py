@@ -79,6 +79,20 @@ def _ffn(cfg, p, e: int, xr: torch.Tensor) -> torch.Tensor:
     return (g * torch.sigmoid(g) * u) @ w2.T
 
 
+def preactivations(layer, e: int, xrows: np.ndarray) -> np.ndarray:
+    """Pre-activations of expert e (e == E: the shared one) on float rows:
+    SwiGLU [x W1^T | x W3^T] (gate rows, then up rows), GELU x W1^T + b1;
+    float64 [n, N_up]."""
+    cfg = layer.cfg
+    p = {n: t.detach() for n, t in params(layer).items()}
+    shared = e == cfg.E
+    w1 = p["w_up_shared"][0] if shared else p["w_up"][e]
+    a = torch.from_numpy(np.asarray(xrows, np.float64)) @ w1.T
+    if cfg.act == 0 and "b_up" in p and not shared:
+        a = a + p["b_up"][e]
+    return a.numpy()
+
+
 def forward(layer, p: dict, idx: np.ndarray, keep: Optional[np.ndarray] = None):
     """(y [T, d], gate values [T, k], Importance [E]) as float64 tensors for
     the fixed selection idx [T, k]."""

@@ -35,6 +35,7 @@ EXPORTS = (
     "moe_expert_down", "moe_expert_ffn", "moe_combine", "moe_forward",
     "moe_param_counts", "moe_load_stats", "moe_expert_capacity",
     "moe_route_noisy", "moe_backward_workspace_bytes", "moe_backward",
+    "moe_expert_up_train",
 )
 
 
@@ -80,8 +81,9 @@ def lib():
             "moe_grouped_rows": [P, P],
             "moe_route": [P, P, P, P, P, P, P, P, P],
             "moe_backward_workspace_bytes": [P, P],
-            "moe_backward": [P, P, P, P, P, P, P, P, P, P, P, C.c_float, P, P,
+            "moe_backward": [P, P, P, P, P, P, P, P, P, P, P, P, P, C.c_float, P, P,
                              C.c_size_t, P],
+            "moe_expert_up_train": [P, P, P, P, P, P, P, P],
             "moe_route_noisy": [P, P, P, P, P, P, P, P, P, P, P, P, P, P, P,
                                 C.c_size_t, P],
             "moe_permute": [P, P, P, P, P, P, P, P, P, P, P, C.c_size_t, P],
@@ -211,12 +213,20 @@ def moe_backward_workspace_bytes(cfg: MoeConfig) -> int:
 
 def moe_backward(cfg, w: MoeWeights, x, dy, topk_idx, topk_w, offsets, pos, x_perm, y_perm,
                  importance, importance_weight: float, g: MoeGrads, ws, ws_bytes=None,
-                 stream=None) -> None:
+                 stream=None, hidden=None, preact=None) -> None:
     nb = _nbytes(ws) if ws_bytes is None and ws is not None else (ws_bytes or 0)
     _check("moe_backward", lib().moe_backward(
         C.byref(cfg), C.byref(w), _ptr(x), _ptr(dy), _ptr(topk_idx), _ptr(topk_w),
-        _ptr(offsets), _ptr(pos), _ptr(x_perm), _ptr(y_perm), _ptr(importance),
-        float(importance_weight), C.byref(g), _ptr(ws), nb, _stream(stream)))
+        _ptr(offsets), _ptr(pos), _ptr(x_perm), _ptr(y_perm), _ptr(hidden), _ptr(preact),
+        _ptr(importance), float(importance_weight), C.byref(g), _ptr(ws), nb,
+        _stream(stream)))
+
+
+def moe_expert_up_train(cfg, w: MoeWeights, x_perm, x, offsets, hidden, preact,
+                        stream=None) -> None:
+    _check("moe_expert_up_train", lib().moe_expert_up_train(
+        C.byref(cfg), C.byref(w), _ptr(x_perm), _ptr(x), _ptr(offsets), _ptr(hidden),
+        _ptr(preact), _stream(stream)))
 
 
 def moe_route_noisy(cfg, x, w_gate, b_gate, w_noise, noise, clean_logits, noise_scale,

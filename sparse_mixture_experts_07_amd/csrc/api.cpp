@@ -30,6 +30,11 @@ hipError_t launch_expert_up_bf16(bool swiglu, const int32_t *offsets, int E, int
                                  const void *x, const void *w_up,
                                  const void *w_up_shared, const void *b_up,
                                  void *hidden, hipStream_t s);
+hipError_t launch_expert_up_train_bf16(bool swiglu, const int32_t *offsets, int E, int S,
+                                       int T, int k, int d, int h, const void *x_perm,
+                                       const void *x, const void *w_up,
+                                       const void *w_up_shared, const void *b_up,
+                                       void *hidden, void *preact, hipStream_t s);
 hipError_t launch_expert_down_bf16(const int32_t *offsets, int E, int S, int T, int k,
                                    int d, int h, const void *hidden,
                                    const void *w_down, const void *w_down_shared,
@@ -347,6 +352,25 @@ moe_status_t moe_expert_up(const moe_config_t *cfg, const moe_weights_t *w,
       cfg->d_hidden, x_perm, x, w->w_up, w->w_up_shared, w->b_up, hidden, stream));
 }
 
+moe_status_t moe_expert_up_train(const moe_config_t *cfg, const moe_weights_t *w,
+                                 const void *x_perm, const void *x, const int32_t *offsets,
+                                 void *hidden, void *preact, hipStream_t stream) {
+  moe_status_t st = check_cfg(cfg);
+  if (st != MOE_OK) return st;
+  if (cfg->dtype != MOE_DTYPE_BF16) return MOE_ERR_UNSUPPORTED;
+  if ((st = check_weights(cfg, w, true, false, false)) != MOE_OK) return st;
+  const int T = (int)cfg->num_tokens;
+  if (T == 0) return MOE_OK;
+  if (!dev_ok(x_perm) || !dev_ok(offsets) || !dev_ok(hidden) || !dev_ok(preact) ||
+      (cfg->num_shared && !dev_ok(x)))
+    return MOE_ERR_INVALID_ARGUMENT;
+  clear_pending_error();
+  return hip_status(moe::launch_expert_up_train_bf16(
+      cfg->act == MOE_ACT_SWIGLU, offsets, cfg->num_experts, cfg->num_shared, T, cfg->top_k,
+      cfg->d_model, cfg->d_hidden, x_perm, x, w->w_up, w->w_up_shared, w->b_up, hidden,
+      preact, stream));
+}
+
 moe_status_t moe_expert_down(const moe_config_t *cfg, const moe_weights_t *w,
                              const void *hidden, const int32_t *offsets, void *y_perm,
                              hipStream_t stream) {
@@ -447,7 +471,8 @@ moe_status_t moe_backward_workspace_bytes(const moe_config_t *cfg, size_t *bytes
 moe_status_t moe_backward(const moe_config_t *cfg, const moe_weights_t *w, const void *x,
                           const void *dy, const int32_t *topk_idx, const float *topk_w,
                           const int32_t *offsets, const int32_t *pos, const void *x_perm,
-                          const void *y_perm, const float *importance,
+                          const void *y_perm, const void *hidden, const void *preact,
+                          const float *importance,
                           float importance_weight, const moe_grads_t *g, void *ws,
                           size_t ws_bytes, hipStream_t stream) {
   moe_status_t st = check_bwd_cfg(cfg);
@@ -455,7 +480,8 @@ moe_status_t moe_backward(const moe_config_t *cfg, const moe_weights_t *w, const
   if ((st = check_weights(cfg, w, true, true, true)) != MOE_OK) return st;
   if (!g || !dev_ok(g->dw_gate) || !dev_ok(g->dw_up) || !dev_ok(g->dw_down) ||
       !opt_ok(g->db_gate) || !opt_ok(g->db_up) || !opt_ok(g->db_down) ||
-      !opt_ok(importance) || !std::isfinite(importance_weight))
+      !opt_ok(importance) || !opt_ok(hidden) || !opt_ok(preact) ||
+      !std::isfinite(importance_weight))
     return MOE_ERR_INVALID_ARGUMENT;
   const bool swi = cfg->act == MOE_ACT_SWIGLU;
   if (swi && (g->db_up || g->db_down)) return MOE_ERR_INVALID_ARGUMENT;
@@ -512,6 +538,8 @@ moe_status_t moe_backward(const moe_config_t *cfg, const moe_weights_t *w, const
   a.w_imp = importance_weight;
   a.x_perm = static_cast<const uint16_t *>(x_perm);
   a.y_perm = static_cast<const uint16_t *>(y_perm);
+  a.hidden = static_cast<const uint16_t *>(hidden);
+  a.preact = static_cast<const uint16_t *>(preact);
   a.dx = static_cast<uint16_t *>(g->dx);
   a.dw_gate = g->dw_gate;
   a.db_gate = g->db_gate;

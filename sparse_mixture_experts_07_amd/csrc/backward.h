@@ -29,6 +29,7 @@ struct BwdArgs {
   const float *topk_w, *importance;
   float w_imp;
   const uint16_t *x_perm, *y_perm;
+  const uint16_t *hidden, *preact;   // from the training forward, or NULL
   uint16_t *dx;
   float *dw_gate, *db_gate;   // fp32, the router's dtype
   uint16_t *dw_up, *dw_down, *db_up, *db_down, *dw_up_s, *dw_down_s;   // bf16

@@ -537,16 +537,21 @@ hipError_t launch_backward(const BwdArgs &a, const BwdBuffers &b, hipStream_t s)
   }
   MOE_TRY(hipGetLastError());
 
-  // pre-activations recomputed, activations, then the chain back to dX
-  MOE_TRY(launch_grouped_linear_bf16(a.offsets, E, S, T, k, d, nup, a.x_perm, a.x, a.w_up,
-                                     a.w_up_s, a.swiglu ? nullptr : a.b_up, b.A, s));
-  bwd_act_kernel<<<grid_for((int64_t)R * (h / 8), kBwdThreads), kBwdThreads, 0, s>>>(
-      b.A, R, h, a.swiglu, b.H);
+  // pre-activations (the training forward's, else recomputed), activations,
+  // then the chain back to dX
+  const uint16_t *A = a.preact ? a.preact : b.A;
+  const uint16_t *H = a.hidden ? a.hidden : b.H;
+  if (!a.preact)
+    MOE_TRY(launch_grouped_linear_bf16(a.offsets, E, S, T, k, d, nup, a.x_perm, a.x, a.w_up,
+                                       a.w_up_s, a.swiglu ? nullptr : a.b_up, b.A, s));
+  if (!a.hidden)
+    bwd_act_kernel<<<grid_for((int64_t)R * (h / 8), kBwdThreads), kBwdThreads, 0, s>>>(
+        A, R, h, a.swiglu, b.H);
   MOE_TRY(launch_grouped_linear_bf16(a.offsets, E, S, T, k, d, h, b.dyp,
                                      b.dyp + (int64_t)routed * d, b.w2t, b.w2ts, nullptr, b.dH,
                                      s));
   bwd_act_grad_kernel<<<grid_for((int64_t)R * (h / 8), kBwdThreads), kBwdThreads, 0, s>>>(
-      b.A, b.dH, R, h, a.swiglu, b.dA);
+      A, b.dH, R, h, a.swiglu, b.dA);
   MOE_TRY(launch_grouped_linear_bf16(a.offsets, E, S, T, k, nup, d, b.dA,
                                      b.dA + (int64_t)routed * nup, b.w1t, b.w1ts, nullptr,
                                      b.dxp, s));
@@ -558,7 +563,7 @@ hipError_t launch_backward(const BwdArgs &a, const BwdBuffers &b, hipStream_t s)
   bwd_transpose_cols_kernel<<<dim3(Rp / 64, d / 64), kBwdThreads, 0, s>>>(
       b.dyp, b.dyp + (int64_t)routed * d, routed, d, b.colsrc, Rp, b.dypT);
   bwd_transpose_cols_kernel<<<dim3(Rp / 64, h / 64), kBwdThreads, 0, s>>>(
-      b.H, b.H + (int64_t)routed * h, routed, h, b.colsrc, Rp, b.HT);
+      H, H + (int64_t)routed * h, routed, h, b.colsrc, Rp, b.HT);
   bwd_transpose_cols_kernel<<<dim3(Rp / 64, nup / 64), kBwdThreads, 0, s>>>(
       b.dA, b.dA + (int64_t)routed * nup, routed, nup, b.colsrc, Rp, b.dAT);
   bwd_transpose_cols_kernel<<<dim3(Rp / 64, d / 64), kBwdThreads, 0, s>>>(

@@ -39,7 +39,12 @@
 
 namespace moe {
 
-enum GemmMode { kUpGelu = 0, kUpSwiglu = 1, kDown = 2 };
+// Up modes with Pre also store the pre-activations (SwiGLU: gate and up
+// rows; GELU: x W1^T + b1) for the backward pass of a training step.
+enum GemmMode { kUpGelu = 0, kUpSwiglu = 1, kDown = 2, kUpGeluPre = 3, kUpSwigluPre = 4 };
+constexpr bool mode_swiglu(int m) { return m == kUpSwiglu || m == kUpSwigluPre; }
+constexpr bool mode_gelu(int m) { return m == kUpGelu || m == kUpGeluPre; }
+constexpr bool mode_pre(int m) { return m == kUpGeluPre || m == kUpSwigluPre; }
 
 struct GemmArgs {
   const int32_t *offsets;   // [E + 1]
@@ -56,6 +61,7 @@ struct GemmArgs {
   int n_tiles;              // ceil(n_out / BN_out)
   int min_rows, max_rows;   // this launch takes the groups whose row count
                             // lies in [min_rows, max_rows]
+  uint16_t *c_pre;          // Pre modes: [routed_rows + S*T, w_rows] pre-activations
 };
 
 // Word 3 of a raw buffer resource on gfx9-family parts (32-bit data format,
@@ -190,7 +196,7 @@ struct TileMath {
   static constexpr int WTW = BNW / WN;         // weight rows per wave
   static constexpr int FM = WTM / 16;
   static constexpr int FW = WTW / 16;
-  static constexpr bool SWI = MODE == kUpSwiglu;
+  static constexpr bool SWI = mode_swiglu(MODE);
   static constexpr int BN_OUT = SWI ? BNW / 2 : BNW;
   static constexpr int A_LD = BM * CH / NT;    // 16-byte loads per thread per stage
   static constexpr int W_LD = BNW * CH / NT;
@@ -341,7 +347,7 @@ struct TileMath {
     const int lch = lane / 16;
     constexpr int FO = SWI ? FW / 2 : FW;
     const int wcol0 = SWI ? wn * (WTW / 2) : wn * WTW;
-    const bool has_bias = MODE != kUpSwiglu && a.bias && t.g < a.E;
+    const bool has_bias = !mode_swiglu(MODE) && a.bias && t.g < a.E;
 #pragma unroll
     for (int i = 0; i < FO; ++i) {
       const int col = t.n0 + wcol0 + i * 16 + 4 * lch;
@@ -360,9 +366,9 @@ struct TileMath {
         float v[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          if constexpr (MODE == kUpSwiglu) {
+          if constexpr (mode_swiglu(MODE)) {
             v[r] = silu_f32(acc[i][j][r]) * acc[i + FW / 2][j][r];
-          } else if constexpr (MODE == kUpGelu) {
+          } else if constexpr (mode_gelu(MODE)) {
             v[r] = gelu_f32(acc[i][j][r] + bias[r]);
           } else {
             v[r] = acc[i][j][r] + bias[r];
@@ -373,6 +379,26 @@ struct TileMath {
         o.y = pack_bf16x2(v[2], v[3]);
         if (col_ok && m < t.rows)
           *reinterpret_cast<uint2 *>(a.c + (int64_t)(t.grow0 + m) * a.n_out + col) = o;
+        if constexpr (mode_pre(MODE)) {
+          // pre-activations: row stride w_rows (2h SwiGLU, h GELU)
+          uint16_t *pre = a.c_pre + (int64_t)(t.grow0 + m) * a.w_rows + col;
+          uint2 p;
+          if constexpr (mode_swiglu(MODE)) {
+            p.x = pack_bf16x2(acc[i][j][0], acc[i][j][1]);
+            p.y = pack_bf16x2(acc[i][j][2], acc[i][j][3]);
+            uint2 u;
+            u.x = pack_bf16x2(acc[i + FW / 2][j][0], acc[i + FW / 2][j][1]);
+            u.y = pack_bf16x2(acc[i + FW / 2][j][2], acc[i + FW / 2][j][3]);
+            if (col_ok && m < t.rows) {
+              *reinterpret_cast<uint2 *>(pre) = p;
+              *reinterpret_cast<uint2 *>(pre + a.n_out) = u;
+            }
+          } else {
+            p.x = pack_bf16x2(acc[i][j][0] + bias[0], acc[i][j][1] + bias[1]);
+            p.y = pack_bf16x2(acc[i][j][2] + bias[2], acc[i][j][3] + bias[3]);
+            if (col_ok && m < t.rows) *reinterpret_cast<uint2 *>(pre) = p;
+          }
+        }
         // one output fragment at a time: keeps the scheduler from pulling
         // every accumulator into VGPRs at once
         __builtin_amdgcn_sched_barrier(0);
@@ -971,7 +997,7 @@ static hipError_t launch_persistent(const void *kernel, int &per_cu, GemmArgs a,
 template <int BM, int BNW, int WM, int WN, int BK, int PFD, int MODE>
 static hipError_t launch_bm(const GemmArgs &a, hipStream_t s) {
   static int per_cu = 0;
-  return launch_persistent<BM, MODE == kUpSwiglu ? BNW / 2 : BNW, WM * WN * 64>(
+  return launch_persistent<BM, mode_swiglu(MODE) ? BNW / 2 : BNW, WM * WN * 64>(
       reinterpret_cast<const void *>(&gemm_bf16_kernel<BM, BNW, WM, WN, BK, PFD, MODE>),
       per_cu, a, s);
 }
@@ -979,14 +1005,14 @@ static hipError_t launch_bm(const GemmArgs &a, hipStream_t s) {
 template <int BM, int MODE>
 static hipError_t launch_pp(const GemmArgs &a, hipStream_t s) {
   static int per_cu = 0;
-  return launch_persistent<BM, MODE == kUpSwiglu ? 128 : 256, 512>(
+  return launch_persistent<BM, mode_swiglu(MODE) ? 128 : 256, 512>(
       reinterpret_cast<const void *>(&gemm_pp_kernel<BM, MODE>), per_cu, a, s);
 }
 
 template <int BM, int BNW, int WM, int WN, int MODE>
 static hipError_t launch_dma(const GemmArgs &a, hipStream_t s) {
   static int per_cu = 0;
-  return launch_persistent<BM, MODE == kUpSwiglu ? BNW / 2 : BNW, WM * WN * 64>(
+  return launch_persistent<BM, mode_swiglu(MODE) ? BNW / 2 : BNW, WM * WN * 64>(
       reinterpret_cast<const void *>(&gemm_dma_kernel<BM, BNW, WM, WN, MODE>), per_cu, a, s);
 }
 
@@ -1000,7 +1026,7 @@ static hipError_t launch_dma(const GemmArgs &a, hipStream_t s) {
 template <int MODE>
 static hipError_t launch_big(const GemmArgs &a, hipStream_t s) {
   const double nblk = num_cus();
-  const int bn_out = MODE == kUpSwiglu ? 128 : 256;
+  const int bn_out = mode_swiglu(MODE) ? 128 : 256;
   const double n_tiles = (a.n_out + bn_out - 1) / bn_out;
   const double rows = (double)a.routed_rows + (double)a.S * a.T;
   const double groups = a.E + a.S;
@@ -1118,6 +1144,33 @@ hipError_t launch_expert_up_bf16(bool swiglu, const int32_t *offsets, int E, int
   a.c = static_cast<uint16_t *>(hidden);
   a.n_out = h;
   return swiglu ? launch_classes<kUpSwiglu>(a, s) : launch_classes<kUpGelu>(a, s);
+}
+
+// The up projection of a training step: hidden as above, and the
+// pre-activations [rows, w_rows] (SwiGLU gate rows then up rows; GELU with
+// the bias) that the backward pass differentiates through.
+hipError_t launch_expert_up_train_bf16(bool swiglu, const int32_t *offsets, int E, int S,
+                                       int T, int k, int d, int h, const void *x_perm,
+                                       const void *x, const void *w_up,
+                                       const void *w_up_shared, const void *b_up,
+                                       void *hidden, void *preact, hipStream_t s) {
+  GemmArgs a{};
+  a.offsets = offsets;
+  a.E = E;
+  a.S = S;
+  a.T = T;
+  a.routed_rows = T * k;
+  a.a_routed = static_cast<const uint16_t *>(x_perm);
+  a.a_shared = static_cast<const uint16_t *>(x);
+  a.K = d;
+  a.w = static_cast<const uint16_t *>(w_up);
+  a.w_shared = static_cast<const uint16_t *>(w_up_shared);
+  a.w_rows = swiglu ? 2 * h : h;
+  a.bias = static_cast<const uint16_t *>(b_up);
+  a.c = static_cast<uint16_t *>(hidden);
+  a.n_out = h;
+  a.c_pre = static_cast<uint16_t *>(preact);
+  return swiglu ? launch_classes<kUpSwigluPre>(a, s) : launch_classes<kUpGeluPre>(a, s);
 }
 
 hipError_t launch_expert_down_bf16(const int32_t *offsets, int E, int S, int T,

@@ -27,7 +27,7 @@ def test_library_exports_every_declared_entry_point():
     assert set(B.EXPORTS) == set(names), names
     for n in names:
         assert hasattr(lib, n), f"libmoe.so does not export {n}"
-    assert B.moe_abi_version() == 3
+    assert B.moe_abi_version() == 4
 
 
 def test_status_strings():
@@ -113,9 +113,10 @@ def test_every_entry_point_rejects_bad_config(name):
         L.moe_route_noisy(r, FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
                           FAKE, FAKE, None, FAKE, 1 << 40, None),
         L.moe_backward_workspace_bytes(r, C.byref(C.c_size_t())),
-        L.moe_backward(r, C.byref(w), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None,
-                       C.c_float(0.0), C.byref(B.grads(None, None, None, None)), FAKE,
+        L.moe_backward(r, C.byref(w), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, None,
+                       None, C.c_float(0.0), C.byref(B.grads(None, None, None, None)), FAKE,
                        1 << 40, None),
+        L.moe_expert_up_train(r, C.byref(w), FAKE, FAKE, FAKE, FAKE, FAKE, None),
     ]
     assert calls == [status] * len(calls)
 
@@ -189,7 +190,7 @@ def test_backward_checks():
     inv, uns = B.MOE_ERR_INVALID_ARGUMENT, B.MOE_ERR_UNSUPPORTED
     w = B.MoeWeights(FAKE, None, FAKE, None, FAKE, None, None, None)
     g = B.MoeGrads(FAKE, FAKE, None, FAKE, FAKE, None, None, None, None)
-    args = [FAKE] * 8 + [None, C.c_float(0.0), C.byref(g), FAKE, 1 << 40, None]
+    args = [FAKE] * 8 + [None, None, None, C.c_float(0.0), C.byref(g), FAKE, 1 << 40, None]
     bf = _cfg(dtype=1)
     # fp32 layers and the other gate modes have no backward pass here
     for cfg in (_cfg(dtype=0), _cfg(dtype=1, gate=1), _cfg(dtype=1, gate=2)):
@@ -197,15 +198,15 @@ def test_backward_checks():
         assert L.moe_backward_workspace_bytes(C.byref(cfg), C.byref(C.c_size_t())) == uns
     # required gradient outputs; shared-expert gradients iff S = 1
     g0 = B.MoeGrads(FAKE, None, None, FAKE, FAKE, None, None, None, None)
-    args0 = [FAKE] * 8 + [None, C.c_float(0.0), C.byref(g0), FAKE, 1 << 40, None]
+    args0 = [FAKE] * 8 + [None, None, None, C.c_float(0.0), C.byref(g0), FAKE, 1 << 40, None]
     assert L.moe_backward(C.byref(bf), C.byref(w), *args0) == inv
     gs = B.MoeGrads(FAKE, FAKE, None, FAKE, FAKE, None, None, FAKE, FAKE)
-    argss = [FAKE] * 8 + [None, C.c_float(0.0), C.byref(gs), FAKE, 1 << 40, None]
+    argss = [FAKE] * 8 + [None, None, None, C.c_float(0.0), C.byref(gs), FAKE, 1 << 40, None]
     assert L.moe_backward(C.byref(bf), C.byref(w), *argss) == inv
     # workspace
     n = C.c_size_t()
     assert L.moe_backward_workspace_bytes(C.byref(bf), C.byref(n)) == 0
-    small = [FAKE] * 8 + [None, C.c_float(0.0), C.byref(g), FAKE, n.value - 1, None]
+    small = [FAKE] * 8 + [None, None, None, C.c_float(0.0), C.byref(g), FAKE, n.value - 1, None]
     assert L.moe_backward(C.byref(bf), C.byref(w), *small) == B.MOE_ERR_WORKSPACE_TOO_SMALL
-    nan = [FAKE] * 8 + [None, C.c_float(float("nan")), C.byref(g), FAKE, 1 << 40, None]
+    nan = [FAKE] * 8 + [None, None, None, C.c_float(float("nan")), C.byref(g), FAKE, 1 << 40, None]
     assert L.moe_backward(C.byref(bf), C.byref(w), *nan) == inv

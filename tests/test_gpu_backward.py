@@ -24,8 +24,9 @@ def _gpu():
     require_gpu()
 
 
-def forward_saved(L, capacity=0):
-    """The stage entry points; every tensor the backward pass takes."""
+def forward_saved(L, capacity=0, train=False):
+    """The stage entry points; every tensor the backward pass takes (train:
+    the up projection that also stores the pre-activations)."""
     dl = DeviceLayer.upload(L, capacity=capacity)
     c, dev = dl.cfg, dl.x.device
     T, k, E, d = L.cfg.T, L.cfg.k, L.cfg.E, L.cfg.d
@@ -44,13 +45,21 @@ def forward_saved(L, capacity=0):
     B.moe_route(c, dl.x, dl.w_gate, dl.b_gate, s["idx"], s["w"], s["counts"])
     B.moe_permute(c, s["idx"], s["w"], dl.x, s["offsets"], s["perm_src"], s["pos"], s["imp"],
                   None, s["x_perm"], ws)
-    B.moe_expert_ffn(c, dl.weights(), s["x_perm"], dl.x, s["offsets"], s["y_perm"], ws)
+    if train:
+        nup = 2 * L.cfg.h if L.cfg.act == SWIGLU else L.cfg.h
+        s["hidden"] = torch.empty((R, L.cfg.h), dtype=torch.bfloat16, device=dev)
+        s["preact"] = torch.empty((R, nup), dtype=torch.bfloat16, device=dev)
+        B.moe_expert_up_train(c, dl.weights(), s["x_perm"], dl.x, s["offsets"], s["hidden"],
+                              s["preact"])
+        B.moe_expert_down(c, dl.weights(), s["hidden"], s["offsets"], s["y_perm"])
+    else:
+        B.moe_expert_ffn(c, dl.weights(), s["x_perm"], dl.x, s["offsets"], s["y_perm"], ws)
     B.moe_combine(c, s["y_perm"], s["pos"], s["w"], s["y"])
     return dl, s
 
 
-def run_backward(L, dy_bits, capacity=0, imp_w=0.0):
-    dl, s = forward_saved(L, capacity)
+def run_backward(L, dy_bits, capacity=0, imp_w=0.0, train=False):
+    dl, s = forward_saved(L, capacity, train)
     c, dev = dl.cfg, dl.x.device
     cfg = L.cfg
     E, d, h, S = cfg.E, cfg.d, cfg.h, cfg.S
@@ -70,16 +79,17 @@ def run_backward(L, dy_bits, capacity=0, imp_w=0.0):
     ws = torch.empty(max(B.moe_backward_workspace_bytes(c), 256), dtype=torch.uint8, device=dev)
     dy = to_device(dy_bits, dev)
     B.moe_backward(c, dl.weights(), dl.x, dy, s["idx"], s["w"], s["offsets"], s["pos"],
-                   s["x_perm"], s["y_perm"], s["imp"] if imp_w else None, imp_w, mg, ws)
+                   s["x_perm"], s["y_perm"], s["imp"] if imp_w else None, imp_w, mg, ws,
+                   hidden=s.get("hidden"), preact=s.get("preact"))
     torch.cuda.synchronize()
     out = {("x" if n == "dx" else n): (to_f64(t) if t is not None else None) for n, t in g.items()}
     return out, s, (dl, mg, ws, dy)
 
 
-def check_backward(L, capacity=0, imp_w=0.0, seed=0):
+def check_backward(L, capacity=0, imp_w=0.0, seed=0, train=False):
     rng = np.random.default_rng(seed)
     dy_bits = f32_to_bf16_bits(rng.standard_normal((L.cfg.T, L.cfg.d)).astype(np.float32))
-    got, s, _ = run_backward(L, dy_bits, capacity, imp_w)
+    got, s, _ = run_backward(L, dy_bits, capacity, imp_w, train)
     ridx, _, _ = oracle.route(L)
     assert np.array_equal(s["idx"].cpu().numpy(), ridx)
     keep = oracle.capacity_keep(L.cfg, ridx, capacity) if capacity else None
@@ -117,6 +127,49 @@ def test_backward_against_autograd(name):
         assert oracle.capacity_keep(cfg, idx, cap).sum() < cfg.T * cfg.k
     errs = check_backward(L, cap, imp_w)
     print(name, {n: f"{e:.2e}" for n, e in errs.items()})
+
+
+@pytest.mark.parametrize("name", ["swiglu-bias", "gelu-expert-bias", "shared-swiglu",
+                                  "capacity-drops", "e64-small-groups", "long-k-gelu"])
+def test_backward_with_stored_preactivations(name):
+    """The training forward (moe_expert_up_train) stores the pre-activations
+    and the backward takes them with the forward's hidden rows instead of
+    recomputing: the same gradients against the oracle."""
+    kw, cap, imp_w = CASES[name]
+    L = random_layer(61, wstd=0.15, **kw)
+    errs = check_backward(L, cap, imp_w, train=True)
+    print(name, {n: f"{e:.2e}" for n, e in errs.items()})
+
+
+def test_training_up_projection():
+    """moe_expert_up_train: hidden bitwise that of moe_expert_up; every
+    group's pre-activation rows against the oracle's (one bf16 rounding)."""
+    for kw in (dict(T=300, d=128, h=256, E=8, k=2, act=SWIGLU, dtype=BF16, S=1),
+               dict(T=200, d=64, h=192, E=6, k=2, act=GELU, dtype=BF16, expert_bias=True),
+               dict(T=100, d=64, h=64, E=64, k=6, act=SWIGLU, dtype=BF16)):
+        L = random_layer(64, wstd=0.15, **kw)
+        dl, s = forward_saved(L, train=True)
+        c, dev = dl.cfg, dl.x.device
+        ref_h = torch.empty_like(s["hidden"])
+        B.moe_expert_up(c, dl.weights(), s["x_perm"], dl.x, s["offsets"], ref_h)
+        torch.cuda.synchronize()
+        assert torch.equal(ref_h.view(torch.int16), s["hidden"].view(torch.int16))
+        cfg = L.cfg
+        off = s["offsets"].cpu().numpy()
+        src = s["perm_src"].cpu().numpy()
+        pre = to_f64(s["preact"])
+        xs = bf16_bits_to_f32(L.x).astype(np.float64)
+        for e in range(cfg.E + cfg.S):
+            if e < cfg.E:
+                rows = np.arange(off[e], off[e + 1])
+                xr = xs[src[rows]]
+            else:
+                rows = np.arange(cfg.T * cfg.k, cfg.T * cfg.k + cfg.T)
+                xr = xs
+            if rows.size == 0:
+                continue
+            ref = oracle.backward.preactivations(L, e, xr)
+            assert max_rel(pre[rows], ref) <= 1e-2, e
 
 
 def test_backward_is_deterministic():
