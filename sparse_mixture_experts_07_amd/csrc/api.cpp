@@ -155,7 +155,7 @@ void clear_pending_error() { (void)hipGetLastError(); }
 struct BwdLayout {
   size_t gimp, ds, dsp, ds_cols, poff, colsrc;
   size_t off_all, src_all, pos_all, hist, full_off, perm_w, imp_all;
-  size_t w1t, w2t, w1ts, w2ts, A, H, dyp, dH, dA, dxp, dypT, HT, dAT, xpT, total;
+  size_t A, H, dyp, dH, dA, dxp, dypT, HT, dAT, xpT, total;
 };
 
 BwdLayout bwd_layout(const moe_config_t *c) {
@@ -184,10 +184,6 @@ BwdLayout bwd_layout(const moe_config_t *c) {
   take(L.full_off, cap ? 4 * (E + 1) : 0);
   take(L.perm_w, cap ? 4 * T * k : 0);
   take(L.imp_all, cap ? 4 * E : 0);
-  take(L.w1t, 2 * E * nup * d);
-  take(L.w2t, 2 * E * h * d);
-  take(L.w1ts, 2 * S * nup * d);
-  take(L.w2ts, 2 * S * h * d);
   take(L.A, 2 * R * nup);
   take(L.H, 2 * R * h);
   take(L.dyp, 2 * R * d);
@@ -565,10 +561,6 @@ moe_status_t moe_backward(const moe_config_t *cfg, const moe_weights_t *w, const
     b.perm_w = at<float>(ws, L.perm_w);
     b.imp_all = at<float>(ws, L.imp_all);
   }
-  b.w1t = at<uint16_t>(ws, L.w1t);
-  b.w2t = at<uint16_t>(ws, L.w2t);
-  b.w1ts = S ? at<uint16_t>(ws, L.w1ts) : nullptr;
-  b.w2ts = S ? at<uint16_t>(ws, L.w2ts) : nullptr;
   b.A = at<uint16_t>(ws, L.A);
   b.H = at<uint16_t>(ws, L.H);
   b.dyp = at<uint16_t>(ws, L.dyp);

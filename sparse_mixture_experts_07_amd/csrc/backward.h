@@ -16,7 +16,6 @@ struct BwdBuffers {
   // regrouping of every assignment (router gradient under a capacity)
   int32_t *off_all, *src_all, *pos_all, *hist, *full_off;
   float *perm_w, *imp_all;
-  uint16_t *w1t, *w2t, *w1ts, *w2ts;
   uint16_t *A, *H, *dyp, *dH, *dA, *dxp;
   uint16_t *dypT, *HT, *dAT, *xpT;
 };

@@ -5,7 +5,7 @@
 // trainable"; Importance and CV^2: Qiita summary, "Load-balancing losses").
 //
 // The grouped GEMMs of the backward pass run in gemm_bf16.hip (dH = dY W2,
-// dX = dA W1 on transposed weight copies, the weight gradients over each
+// dX = dA W1 on the weights as stored, the weight gradients over each
 // group's rows); this file holds the rest, all bf16 storage with fp32
 // arithmetic:
 //   gate     per token: dw_j = <dy, Y_j> (Y_j the expert's output row),
@@ -15,8 +15,7 @@
 //   act      H = act(A) from the recomputed pre-activations A; dA = act'(A) dH
 //   layout   group columns padded to 64 for the transposed copies, and the
 //            grouped row behind every column
-//   transpose activations [R, C] -> [C, Rp] (group columns, zero padding),
-//            weights [B, R, C] -> [B, C, R]
+//   transpose activations [R, C] -> [C, Rp] (group columns, zero padding)
 //   sums     per-group weighted row sums (bias and router gradients)
 //   dx       dx = sum_j dX[pos_j] + dX_shared + sum_j ds_j W_g[i_j]
 // Every sum runs in a fixed order: results are deterministic.
@@ -312,41 +311,6 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_transpose_cols_kernel(
   }
 }
 
-// Batched transpose of [B][R][C] to [B][C][R]; R, C multiples of 64.
-__global__ __launch_bounds__(kBwdThreads) void bwd_transpose_kernel(
-    const uint16_t *__restrict__ src, int R, int C, uint16_t *__restrict__ dst) {
-  __shared__ uint16_t tile[64][64 + 2];
-  const int r0 = blockIdx.x * 64, c0 = blockIdx.y * 64;
-  const int64_t b = blockIdx.z;
-  const uint16_t *s = src + b * R * (int64_t)C;
-  uint16_t *o = dst + b * R * (int64_t)C;
-  const int tid = threadIdx.x;
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int q = tid + i * kBwdThreads;
-    const int rr = q / 8, v = q % 8;
-    const uint4 val = *reinterpret_cast<const uint4 *>(s + (int64_t)(r0 + rr) * C + c0 + 8 * v);
-    const uint32_t w4[4] = {val.x, val.y, val.z, val.w};
-#pragma unroll
-    for (int z = 0; z < 4; ++z) {
-      tile[rr][8 * v + 2 * z] = (uint16_t)(w4[z] & 0xffffu);
-      tile[rr][8 * v + 2 * z + 1] = (uint16_t)(w4[z] >> 16);
-    }
-  }
-  __syncthreads();
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int q = tid + i * kBwdThreads;
-    const int cc = q / 8, v = q % 8;
-    uint32_t w4[4];
-#pragma unroll
-    for (int z = 0; z < 4; ++z)
-      w4[z] = (uint32_t)tile[8 * v + 2 * z][cc] | ((uint32_t)tile[8 * v + 2 * z + 1][cc] << 16);
-    *reinterpret_cast<uint4 *>(o + (int64_t)(c0 + cc) * R + r0 + 8 * v) =
-        make_uint4(w4[0], w4[1], w4[2], w4[3]);
-  }
-}
-
 // dsp[pos[f]] = ds[f] (grouped-row order), then ds_cols[j] = dsp[colsrc[j]]
 // for routed rows, 0 otherwise.
 __global__ void bwd_scatter_ds_kernel(const float *__restrict__ ds, const int32_t *__restrict__ pos,
@@ -471,7 +435,7 @@ hipError_t launch_grouped_linear_bf16(const int32_t *offsets, int E, int S, int 
                                       int K, int n_out, const void *a_routed,
                                       const void *a_shared, const void *w,
                                       const void *w_shared, const void *bias, void *c,
-                                      hipStream_t s);
+                                      bool w_kn, hipStream_t s);
 hipError_t launch_permute(const int32_t *idx, const float *w, const void *x, int T, int k,
                           int E, int capacity, int row_bytes, int32_t *offsets,
                           int32_t *perm_src, int32_t *pos, float *importance, double *stats,
@@ -528,13 +492,6 @@ hipError_t launch_backward(const BwdArgs &a, const BwdBuffers &b, hipStream_t s)
   bwd_layout_kernel<<<1, kBwdThreads, 0, s>>>(a.offsets, E, S, T, routed, b.poff);
   bwd_colsrc_kernel<<<grid_for(Rp, kBwdThreads), kBwdThreads, 0, s>>>(a.offsets, b.poff, E, S, T,
                                                                        routed, Rp, b.colsrc);
-  // transposed weights: W1^T [E, d, nup], W2^T [E, h, d]
-  bwd_transpose_kernel<<<dim3(nup / 64, d / 64, E), kBwdThreads, 0, s>>>(a.w_up, nup, d, b.w1t);
-  bwd_transpose_kernel<<<dim3(d / 64, h / 64, E), kBwdThreads, 0, s>>>(a.w_down, d, h, b.w2t);
-  if (S) {
-    bwd_transpose_kernel<<<dim3(nup / 64, d / 64, 1), kBwdThreads, 0, s>>>(a.w_up_s, nup, d, b.w1ts);
-    bwd_transpose_kernel<<<dim3(d / 64, h / 64, 1), kBwdThreads, 0, s>>>(a.w_down_s, d, h, b.w2ts);
-  }
   MOE_TRY(hipGetLastError());
 
   // pre-activations (the training forward's, else recomputed), activations,
@@ -543,18 +500,20 @@ hipError_t launch_backward(const BwdArgs &a, const BwdBuffers &b, hipStream_t s)
   const uint16_t *H = a.hidden ? a.hidden : b.H;
   if (!a.preact)
     MOE_TRY(launch_grouped_linear_bf16(a.offsets, E, S, T, k, d, nup, a.x_perm, a.x, a.w_up,
-                                       a.w_up_s, a.swiglu ? nullptr : a.b_up, b.A, s));
+                                       a.w_up_s, a.swiglu ? nullptr : a.b_up, b.A, false, s));
   if (!a.hidden)
     bwd_act_kernel<<<grid_for((int64_t)R * (h / 8), kBwdThreads), kBwdThreads, 0, s>>>(
         A, R, h, a.swiglu, b.H);
+  // dH = dY W2 and dX = dA W1 read W2 [d][h] and W1 [nup][d] as stored
+  // (k-row weights), no transposed copies
   MOE_TRY(launch_grouped_linear_bf16(a.offsets, E, S, T, k, d, h, b.dyp,
-                                     b.dyp + (int64_t)routed * d, b.w2t, b.w2ts, nullptr, b.dH,
-                                     s));
+                                     b.dyp + (int64_t)routed * d, a.w_down, a.w_down_s, nullptr,
+                                     b.dH, true, s));
   bwd_act_grad_kernel<<<grid_for((int64_t)R * (h / 8), kBwdThreads), kBwdThreads, 0, s>>>(
       A, b.dH, R, h, a.swiglu, b.dA);
   MOE_TRY(launch_grouped_linear_bf16(a.offsets, E, S, T, k, nup, d, b.dA,
-                                     b.dA + (int64_t)routed * nup, b.w1t, b.w1ts, nullptr,
-                                     b.dxp, s));
+                                     b.dA + (int64_t)routed * nup, a.w_up, a.w_up_s, nullptr,
+                                     b.dxp, true, s));
   bwd_dx_kernel<<<T, kBwdThreads, 0, s>>>(b.dxp, a.pos, b.ds, a.idx, a.w_gate, T, k, d, E, S, R,
                                          a.dx);
   MOE_TRY(hipGetLastError());

@@ -41,8 +41,14 @@ namespace moe {
 
 // Up modes with Pre also store the pre-activations (SwiGLU: gate and up
 // rows; GELU: x W1^T + b1) for the backward pass of a training step.
-enum GemmMode { kUpGelu = 0, kUpSwiglu = 1, kDown = 2, kUpGeluPre = 3, kUpSwigluPre = 4 };
+// kDownKN: the plain map of kDown with each group's weight matrix stored
+// [K][N] (N contiguous), as the backward pass finds W2 and W1 for dH = dY W2
+// and dX = dA W1; its MFMA fragments come from LDS through transposing
+// reads.
+enum GemmMode { kUpGelu = 0, kUpSwiglu = 1, kDown = 2, kUpGeluPre = 3, kUpSwigluPre = 4,
+                kDownKN = 5 };
 constexpr bool mode_swiglu(int m) { return m == kUpSwiglu || m == kUpSwigluPre; }
+constexpr bool mode_kn(int m) { return m == kDownKN; }
 constexpr bool mode_gelu(int m) { return m == kUpGelu || m == kUpGeluPre; }
 constexpr bool mode_pre(int m) { return m == kUpGeluPre || m == kUpSwigluPre; }
 
@@ -124,11 +130,12 @@ __device__ __forceinline__ void tile_prefix(const GemmArgs &a, int *tprefix, int
 struct Tile {
   int g, grow0, rows, m0, n0;
   __amdgpu_buffer_rsrc_t rs_a, rs_w0, rs_w1;
+  uint32_t w_stride;   // kDownKN: bytes per k row of the weights
 };
 
 // Tile L of the launch's ragged tile space: group g owns tiles
 // [tprefix[g] * n_tiles, tprefix[g+1] * n_tiles), m-tile fastest.
-template <int BM, int BNW, bool SWI>
+template <int BM, int BNW, bool SWI, bool KN = false>
 __device__ __forceinline__ Tile decode_tile(const GemmArgs &a, const int *tprefix, int L) {
   const int G = a.E + a.S;
   int lo = 0, hi = G - 1;
@@ -166,7 +173,15 @@ __device__ __forceinline__ Tile decode_tile(const GemmArgs &a, const int *tprefi
   const int arows = min(BM, t.rows - t.m0);
   t.rs_a = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint16_t *>(abase + (int64_t)t.m0 * a.K), 0, arows * row_bytes, kBufferWord3);
-  if constexpr (SWI) {
+  if constexpr (KN) {
+    // [K][w_rows] weights: columns n0.. of every k row; the range ends with
+    // the group's matrix, so stages past K read zeros
+    t.w_stride = (uint32_t)a.w_rows * 2u;
+    t.rs_w0 = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t *>(wbase + t.n0), 0,
+        (uint32_t)(((int64_t)a.K * a.w_rows - t.n0) * 2), kBufferWord3);
+    t.rs_w1 = t.rs_w0;
+  } else if constexpr (SWI) {
     const int h = a.n_out;
     const int wv = min(BNW / 2, h - t.n0);
     t.rs_w0 = __builtin_amdgcn_make_buffer_rsrc(
@@ -198,6 +213,13 @@ struct TileMath {
   static constexpr int FW = WTW / 16;
   static constexpr bool SWI = mode_swiglu(MODE);
   static constexpr int BN_OUT = SWI ? BNW / 2 : BNW;
+  // kDownKN: a weight stage is BK rows of k, each BNW values of n (WCH
+  // 16-byte chunks); chunk c of row k sits at c ^ (k & 7), so the four k
+  // rows a transposing read touches fall in different banks
+  static constexpr bool KN = mode_kn(MODE);
+  static constexpr int WCH = BNW / 8;
+  static_assert(!KN || (WCH >= 8 && !PLANES), "k-row weight stage");
+  static __device__ __forceinline__ int kn_slot(int k, int c) { return k * WCH + (c ^ (k & 7)); }
   static constexpr int A_LD = BM * CH / NT;    // 16-byte loads per thread per stage
   static constexpr int W_LD = BNW * CH / NT;
   static_assert(BK == 32 || BK == 64, "stage depth");
@@ -224,6 +246,17 @@ struct TileMath {
 #pragma unroll
     for (int i = 0; i < A_LD; ++i)
       ra[i] = __builtin_amdgcn_raw_buffer_load_b128(t.rs_a, v0 + i * istride, ko, 0);
+    if constexpr (KN) {
+      // chunk q: k row q / WCH of the stage, 16-byte chunk q % WCH
+#pragma unroll
+      for (int i = 0; i < W_LD; ++i) {
+        const int q = (int)threadIdx.x + i * NT;
+        rw[i] = __builtin_amdgcn_raw_buffer_load_b128(
+            t.rs_w0, (uint32_t)(q / WCH) * t.w_stride + (uint32_t)(q % WCH) * 16u,
+            (int)((uint32_t)(kt * BK) * t.w_stride), 0);
+      }
+      return;
+    }
 #pragma unroll
     for (int i = 0; i < W_LD; ++i) {
       if (!SWI || i < W_LD / 2) {
@@ -247,7 +280,10 @@ struct TileMath {
 #pragma unroll
     for (int i = 0; i < W_LD; ++i) {
       const int q = tid + i * NT;
-      Ws[(q / CH) * CH + swz<BK>(q % CH, q / CH)] = rw[i];
+      if constexpr (KN)
+        Ws[kn_slot(q / WCH, q % WCH)] = rw[i];
+      else
+        Ws[(q / CH) * CH + swz<BK>(q % CH, q / CH)] = rw[i];
     }
   }
 
@@ -291,6 +327,27 @@ struct TileMath {
   }
   static __device__ __forceinline__ bf16x8_t read_w(const u32x4_t *Ws, int n, int wn) {
     const int lane = threadIdx.x % 64;
+    if constexpr (KN) {
+      // Two transposing reads (ds_read_b64_tr_b16).  In each 16-lane group
+      // the result lane i, element j is element i % 4 of the 4-value row
+      // whose address lane i / 4 + 4 j gave.  Lane 4 j + a of group g gives
+      // k row 8 g + 4 h + j (read h = 0, 1), n values nb + 4 a .. + 3; lane
+      // i then holds W[k0 + 8 g .. + 7][nb + i]: the fragment of n row i.
+      typedef short v4s __attribute__((ext_vector_type(4)));
+      const int g = lane / 16, sl = lane % 16;
+      const int nn = wrow(wn, n % FW, 0) + 4 * (sl & 3);
+      const int k0 = 32 * (n / FW) + 8 * g + (sl >> 2);
+      const char *base = reinterpret_cast<const char *>(Ws);
+      const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) v4s *)(base + kn_slot(k0, nn >> 3) * 16 +
+                                                    (nn & 7) * 2));
+      const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) v4s *)(base + kn_slot(k0 + 4, nn >> 3) * 16 +
+                                                    (nn & 7) * 2));
+      typedef short v8s __attribute__((ext_vector_type(8)));
+      const v8s both = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      return __builtin_bit_cast(bf16x8_t, both);
+    }
     const int ch = 4 * (n / FW) + lane / 16;
     const int r = wrow(wn, n % FW, lane % 16);
     return __builtin_bit_cast(bf16x8_t, Ws[w_idx(r, ch)]);
@@ -444,7 +501,7 @@ void gemm_bf16_kernel(GemmArgs a) {
   for (int it = 0;; ++it) {
     const int L = slice_tile(it);
     if (L >= total_tiles) break;
-    const Tile t = decode_tile<BM, BNW, TM::SWI>(a, tprefix, L);
+    const Tile t = decode_tile<BM, BNW, TM::SWI, TM::KN>(a, tprefix, L);
 
     f32x4_t acc[FW][FM];
 #pragma unroll
@@ -539,7 +596,7 @@ void gemm_pp_kernel(GemmArgs a) {
   for (int it = 0;; ++it) {
     const int L = slice_tile(it);
     if (L >= total_tiles) break;
-    const Tile t = decode_tile<BM, BNW, TM::SWI>(a, tprefix, L);
+    const Tile t = decode_tile<BM, BNW, TM::SWI, TM::KN>(a, tprefix, L);
 
     f32x4_t acc[FW][FM];
 #pragma unroll
@@ -630,7 +687,7 @@ void gemm_dma_kernel(GemmArgs a) {
   for (int it = 0;; ++it) {
     const int L = slice_tile(it);
     if (L >= total_tiles) break;
-    const Tile t = decode_tile<BM, BNW, TM::SWI>(a, tprefix, L);
+    const Tile t = decode_tile<BM, BNW, TM::SWI, TM::KN>(a, tprefix, L);
 
     // wave w moves blocks BPW w .. BPW w + BPW - 1 of the stage: token
     // blocks first, then weight blocks (SwiGLU: gate rows from one
@@ -649,6 +706,17 @@ void gemm_dma_kernel(GemmArgs a) {
         } else {
           const int wb = blk - ABLK;
           dst = Ws[s % NB] + wb * 64;
+          if constexpr (TM::KN) {
+            // 64 / WCH k rows per block; lane -> physical chunk lane % WCH
+            // of row kr, holding logical chunk (lane % WCH) ^ (kr & 7)
+            constexpr int RPB = 64 / TM::WCH;
+            const int kr = wb * RPB + lane / TM::WCH;
+            const uint32_t vw = (uint32_t)(lane / TM::WCH) * t.w_stride +
+                                (uint32_t)((lane % TM::WCH) ^ (kr & 7)) * 16u;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                t.rs_w0, dst, 16, vw, (int)((uint32_t)(s * BK + wb * RPB) * t.w_stride), 0, 0);
+            continue;
+          }
           if (TM::SWI && wb >= WBLK / 2) {
             rs = t.rs_w1;
             row = (wb - WBLK / 2) * 16;
@@ -1035,9 +1103,11 @@ static hipError_t launch_big(const GemmArgs &a, hipStream_t s) {
     return std::ceil(mt * n_tiles / nblk) * bm * per_row;
   };
   const bool bm192 = cost(192, 1.12) < cost(256, 1.0);
-  if (a.K <= 8192)
+  if (mode_kn(MODE) || a.K <= 8192)
     return bm192 ? launch_dma<192, 256, 4, 2, MODE>(a, s) : launch_dma<256, 256, 4, 2, MODE>(a, s);
-  return bm192 ? launch_pp<192, MODE>(a, s) : launch_pp<256, MODE>(a, s);
+  if constexpr (!mode_kn(MODE))
+    return bm192 ? launch_pp<192, MODE>(a, s) : launch_pp<256, MODE>(a, s);
+  return hipErrorInvalidValue;
 }
 
 // Groups are split by row count into two tile classes, one launch each:
@@ -1067,13 +1137,14 @@ static hipError_t launch_classes(GemmArgs a, hipStream_t s) {
 
 // Plain grouped linear map c[r] = a[r] W[g]^T (+ bias[g]) over the groups of
 // `offsets` and the shared group (rows T*k.., operand a_shared, weights
-// w_shared): the backward pass's dH = dY W2 and dX = dA W1 on transposed
-// weight copies, and the pre-activation recomputation A = X W1^T.
+// w_shared), each W[g] stored [n_out][K] or (w_kn) [K][n_out]: the backward
+// pass's dH = dY W2 and dX = dA W1 (k-row weights as stored) and the
+// pre-activation recomputation A = X W1^T.
 hipError_t launch_grouped_linear_bf16(const int32_t *offsets, int E, int S, int T, int k,
                                       int K, int n_out, const void *a_routed,
                                       const void *a_shared, const void *w,
                                       const void *w_shared, const void *bias, void *c,
-                                      hipStream_t s) {
+                                      bool w_kn, hipStream_t s) {
   GemmArgs a{};
   a.offsets = offsets;
   a.E = E;
@@ -1089,7 +1160,7 @@ hipError_t launch_grouped_linear_bf16(const int32_t *offsets, int E, int S, int 
   a.bias = static_cast<const uint16_t *>(bias);
   a.c = static_cast<uint16_t *>(c);
   a.n_out = n_out;
-  return launch_classes<kDown>(a, s);
+  return w_kn ? launch_classes<kDownKN>(a, s) : launch_classes<kDown>(a, s);
 }
 
 hipError_t launch_wgrad_bf16(const int32_t *poff, int G, int Rp, int M, int N, const void *at,
