@@ -1103,11 +1103,16 @@ static hipError_t launch_big(const GemmArgs &a, hipStream_t s) {
     return std::ceil(mt * n_tiles / nblk) * bm * per_row;
   };
   const bool bm192 = cost(192, 1.12) < cost(256, 1.0);
-  if (mode_kn(MODE) || a.K <= 8192)
-    return bm192 ? launch_dma<192, 256, 4, 2, MODE>(a, s) : launch_dma<256, 256, 4, 2, MODE>(a, s);
-  if constexpr (!mode_kn(MODE))
+  // k-row weights: waves of 128 (96) token rows x 64 weight rows, so that
+  // each wave makes fewer of the (twice as many) transposing weight reads
+  if constexpr (mode_kn(MODE)) {
+    return bm192 ? launch_dma<192, 256, 2, 4, MODE>(a, s) : launch_dma<256, 256, 2, 4, MODE>(a, s);
+  } else {
+    if (a.K <= 8192)
+      return bm192 ? launch_dma<192, 256, 4, 2, MODE>(a, s)
+                   : launch_dma<256, 256, 4, 2, MODE>(a, s);
     return bm192 ? launch_pp<192, MODE>(a, s) : launch_pp<256, MODE>(a, s);
-  return hipErrorInvalidValue;
+  }
 }
 
 // Groups are split by row count into two tile classes, one launch each:
