@@ -260,8 +260,9 @@ moe_status_t moe_forward(const moe_config_t *cfg, const moe_weights_t *w,
  * with the top-k selection of the forward held fixed (the selection has no
  * derivative, so the router learns through the softmax weights only:
  * techfeed summary, "The hardest part: making the router trainable";
- * Importance and its CV^2: Qiita summary, "Load-balancing losses").  bf16 layers and MOE_GATE_TOPK_SOFTMAX only (else
- * MOE_ERR_UNSUPPORTED); an expert capacity is honoured through pos (a
+ * Importance and its CV^2: Qiita summary, "Load-balancing losses").  bf16 layers
+ * with MOE_GATE_TOPK_SOFTMAX or MOE_GATE_BIAS_SELECTS (the bias then gets a
+ * zero gradient; MOE_GATE_SOFTMAX_ALL: MOE_ERR_UNSUPPORTED); an expert capacity is honoured through pos (a
  * dropped slot passes no gradient to its expert; its gate still counts in
  * Importance).  Every gradient has the dtype of its parameter: dx and the
  * expert weight and bias gradients bf16, the router's fp32 (accumulation is

@@ -9,7 +9,9 @@ summary, section "Sparsely-Gated MoE layer formula", with the gate of
 "Gating: Noisy Top-k Softmax" in its noise-free form):
 
     y(x) = sum_j G_j(x) E_{i_j}(x)  (+ the shared expert with weight 1)
-    G    = softmax over the kept k of s = x W_g^T + b
+    G    = softmax over the kept k of s = x W_g^T + b (the default gate; the
+           bias-selects gate takes the softmax of x W_g^T over the kept k,
+           the softmax-all gate the softmax over all E read at the kept k)
     loss = <dy, y> + w_imp * CV(Importance)^2
 
 where the kept experts i_j are the oracle's float32 top-k selection, held
@@ -99,11 +101,16 @@ def forward(layer, p: dict, idx: np.ndarray, keep: Optional[np.ndarray] = None):
     cfg = layer.cfg
     T, k, E = cfg.T, cfg.k, cfg.E
     x = p["x"]
-    s = x @ p["w_gate"].T
-    if "b_gate" in p:
-        s = s + p["b_gate"]
+    raw = x @ p["w_gate"].T
+    s = raw + p["b_gate"] if "b_gate" in p else raw
     it = torch.from_numpy(np.ascontiguousarray(idx, np.int64))
-    g = torch.softmax(torch.gather(s, 1, it), dim=1)
+    gate = getattr(cfg, "gate", 0)
+    if gate == 1:     # the bias steers the selection only
+        g = torch.softmax(torch.gather(raw, 1, it), dim=1)
+    elif gate == 2:   # softmax over all E, read at the kept experts
+        g = torch.gather(torch.softmax(s, dim=1), 1, it)
+    else:             # softmax over the kept k
+        g = torch.softmax(torch.gather(s, 1, it), dim=1)
     gk = g
     if keep is not None:
         gk = g * torch.from_numpy(np.asarray(keep, np.float64).reshape(T, k))

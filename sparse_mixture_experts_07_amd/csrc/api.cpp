@@ -201,7 +201,7 @@ BwdLayout bwd_layout(const moe_config_t *c) {
 moe_status_t check_bwd_cfg(const moe_config_t *cfg) {
   moe_status_t st = check_cfg(cfg);
   if (st != MOE_OK) return st;
-  if (cfg->dtype != MOE_DTYPE_BF16 || cfg->gate != MOE_GATE_TOPK_SOFTMAX)
+  if (cfg->dtype != MOE_DTYPE_BF16 || cfg->gate == MOE_GATE_SOFTMAX_ALL)
     return MOE_ERR_UNSUPPORTED;
   const int64_t Rp = moe::bwd_padded_cols(cfg->num_tokens, cfg->top_k, cfg->num_experts,
                                           cfg->num_shared);
@@ -518,6 +518,7 @@ moe_status_t moe_backward(const moe_config_t *cfg, const moe_weights_t *w, const
   a.h = (int)h;
   a.swiglu = swi;
   a.capacity = cfg->capacity;
+  a.bias_selects = cfg->gate == MOE_GATE_BIAS_SELECTS;
   a.x = static_cast<const uint16_t *>(x);
   a.dy = static_cast<const uint16_t *>(dy);
   a.w_up = static_cast<const uint16_t *>(w->w_up);

@@ -22,6 +22,7 @@ struct BwdBuffers {
 
 struct BwdArgs {
   int T, k, E, S, d, h, swiglu, capacity;
+  int bias_selects;   // the bias steers the selection only: it gets no gradient
   const uint16_t *x, *dy, *w_up, *w_down, *b_up, *w_up_s, *w_down_s;
   const float *w_gate;
   const int32_t *idx, *offsets, *pos;

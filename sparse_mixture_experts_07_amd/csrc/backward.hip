@@ -565,7 +565,15 @@ hipError_t launch_backward(const BwdArgs &a, const BwdBuffers &b, hipStream_t s)
   bwd_scatter_ds_kernel<<<grid_for(routed, 256), 256, 0, s>>>(b.ds, pos_r, routed, routed, b.dsp);
   bwd_ds_cols_kernel<<<grid_for(Rp, 256), 256, 0, s>>>(b.dsp, colsrc_r, Rp, routed, b.ds_cols);
   bwd_rowsum_kernel<float><<<dim3(d, E), kWave, 0, s>>>(xT, d, Rp, poff_r, b.ds_cols, a.dw_gate);
-  if (a.db_gate) bwd_group_sum_kernel<<<E, kWave, 0, s>>>(b.ds_cols, poff_r, a.db_gate);
+  // the gate values depend on the unbiased scores under the bias-selects
+  // gate (the same ds: w is the softmax of x W_g^T over the kept experts),
+  // so the bias has no gradient there
+  if (a.db_gate) {
+    if (a.bias_selects)
+      MOE_TRY(launch_fill_f32(a.db_gate, E, s));
+    else
+      bwd_group_sum_kernel<<<E, kWave, 0, s>>>(b.ds_cols, poff_r, a.db_gate);
+  }
   return hipGetLastError();
 #undef MOE_TRY
 }

@@ -192,8 +192,8 @@ def test_backward_checks():
     g = B.MoeGrads(FAKE, FAKE, None, FAKE, FAKE, None, None, None, None)
     args = [FAKE] * 8 + [None, None, None, C.c_float(0.0), C.byref(g), FAKE, 1 << 40, None]
     bf = _cfg(dtype=1)
-    # fp32 layers and the other gate modes have no backward pass here
-    for cfg in (_cfg(dtype=0), _cfg(dtype=1, gate=1), _cfg(dtype=1, gate=2)):
+    # fp32 layers and the softmax-all gate have no backward pass here
+    for cfg in (_cfg(dtype=0), _cfg(dtype=1, gate=2)):
         assert L.moe_backward(C.byref(cfg), C.byref(w), *args) == uns
         assert L.moe_backward_workspace_bytes(C.byref(cfg), C.byref(C.c_size_t())) == uns
     # required gradient outputs; shared-expert gradients iff S = 1

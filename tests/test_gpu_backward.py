@@ -8,6 +8,7 @@ import pytest
 import torch
 
 import oracle
+import synthetic
 from gpu_common import max_rel, require_gpu, to_f64
 from helpers import BF16, GELU, SWIGLU, random_layer
 from sparse_mixture_experts_07_amd import binding as B
@@ -170,6 +171,17 @@ def test_training_up_projection():
                 continue
             ref = oracle.backward.preactivations(L, e, xr)
             assert max_rel(pre[rows], ref) <= 1e-2, e
+
+
+@pytest.mark.parametrize("train", [False, True])
+def test_backward_bias_selects_gate(train):
+    """The bias-selects gate (the bias steers the selection only): the same
+    gradient path with the softmax of the unbiased kept scores; the bias
+    gets a zero gradient."""
+    L = random_layer(65, wstd=0.15, T=300, d=128, h=256, E=8, k=2, act=SWIGLU, dtype=BF16,
+                     bias=True, S=1, gate=synthetic.GATE_BIAS_SELECTS)
+    errs = check_backward(L, 0, 0.4, train=train)
+    print({n: f"{e:.2e}" for n, e in errs.items()})
 
 
 def test_backward_is_deterministic():

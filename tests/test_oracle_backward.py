@@ -92,3 +92,28 @@ def test_gradients_are_linear_in_dy_and_dropped_slots_get_none():
     gk = B.backward(L, d1, keep=keep, idx=idx)
     assert np.all(gk["w_up"][1] == 0) and np.all(gk["w_down"][1] == 0)
     assert np.abs(gk["w_up"][0]).max() > 0
+
+
+@pytest.mark.parametrize("gate", [1, 2], ids=["bias-selects", "softmax-all"])
+def test_gate_modes_forward_and_gradients(gate):
+    """The other gate modes: the torch forward equals the C oracle's, and
+    gradcheck holds; the bias-selects gate gives the bias no gradient."""
+    L = random_layer(9, T=7, d=6, h=5, E=5, k=2, act=SWIGLU, bias=True, gate=gate)
+    idx, _, _ = oracle.route(L)
+    p = B.params(L)
+    y, g, _ = B.forward(L, p, idx)
+    yc, _, wc = oracle.forward_tokens(L, range(7))
+    np.testing.assert_allclose(y.detach().numpy(), yc, rtol=1e-6, atol=1e-7 * np.abs(yc).max())
+    np.testing.assert_allclose(g.detach().numpy(), wc, rtol=1e-6)
+    dy = torch.from_numpy(np.random.default_rng(10).standard_normal((7, 6)))
+    names = list(p)
+
+    def f(*ts):
+        return B.loss(L, dict(zip(names, ts)), idx, dy, None, 0.3)
+
+    assert torch.autograd.gradcheck(f, tuple(p[n] for n in names), eps=1e-6, atol=1e-6, rtol=1e-5)
+    gr = B.backward(L, dy.numpy(), importance_weight=0.3, idx=idx)
+    if gate == 1:
+        assert np.all(gr["b_gate"] == 0)
+    else:
+        assert np.abs(gr["b_gate"]).max() > 0
