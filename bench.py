@@ -91,6 +91,8 @@ def main():
     cfg = synthetic.BY_NAME[args.workload].with_(gate=GATES[args.gate])
     if args.noisy and cfg.gate != 0:
         sys.exit("--noisy takes the default gate only")
+    if args.noisy and args.backward:
+        sys.exit("--noisy --backward: the noisy gate has no backward pass here")
     t_gen = time.time()
     L = synthetic.make_inputs(cfg)
     if args.noisy:
@@ -119,6 +121,9 @@ def main():
     y_perm = torch.empty((R, d), dtype=dt, device=dev)
     y = torch.empty((T, d), dtype=dt, device=dev)
     ws = torch.empty(B.moe_workspace_bytes(c), dtype=torch.uint8, device=dev)
+    # the softmax-all gate's backward reads the forward's router scores
+    logits = (torch.empty((T, E), dtype=torch.float32, device=dev)
+              if args.backward and cfg.gate == synthetic.GATE_SOFTMAX_ALL else None)
     if args.noisy:
         from sparse_mixture_experts_07_amd.device import to_device
         w_noise, noise = to_device(L.w_noise, dev), to_device(noise_np, dev)
@@ -133,7 +138,7 @@ def main():
             B.moe_route_noisy(c, dl.x, dl.w_gate, dl.b_gate, w_noise, noise, clean, nscale,
                               idx, tw, counts, nimp, nload, ncv2, ws)
         else:
-            B.moe_route(c, dl.x, dl.w_gate, dl.b_gate, idx, tw, counts)
+            B.moe_route(c, dl.x, dl.w_gate, dl.b_gate, idx, tw, counts, logits)
 
     if args.backward:
         if cfg.dtype != synthetic.BF16:
@@ -174,7 +179,7 @@ def main():
                                 torch.cuda.Event(enable_timing=True)))
                 bwd_evs[-1][0].record()
             B.moe_backward(c, W, dl.x, dy, idx, tw, offsets, pos, x_perm, y_perm, imp, 0.01,
-                           grads, ws_b, hidden=hidden, preact=preact)
+                           grads, ws_b, hidden=hidden, preact=preact, logits=logits)
             if ev is not None:
                 bwd_evs[-1][1].record()
 

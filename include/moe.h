@@ -42,7 +42,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 4
+#define MOE_ABI_VERSION 5
 
 typedef enum {
   MOE_OK = 0,
@@ -261,8 +261,11 @@ moe_status_t moe_forward(const moe_config_t *cfg, const moe_weights_t *w,
  * derivative, so the router learns through the softmax weights only:
  * techfeed summary, "The hardest part: making the router trainable";
  * Importance and its CV^2: Qiita summary, "Load-balancing losses").  bf16 layers
- * with MOE_GATE_TOPK_SOFTMAX or MOE_GATE_BIAS_SELECTS (the bias then gets a
- * zero gradient; MOE_GATE_SOFTMAX_ALL: MOE_ERR_UNSUPPORTED); an expert capacity is honoured through pos (a
+ * in every gate mode: under MOE_GATE_BIAS_SELECTS the bias gets a zero
+ * gradient; under MOE_GATE_SOFTMAX_ALL every score has a gradient (the gate
+ * value of a kept expert is its share of the softmax over all E), so the
+ * router gradients are dense and the backward reads the forward's scores.
+ * An expert capacity is honoured through pos (a
  * dropped slot passes no gradient to its expert; its gate still counts in
  * Importance).  Every gradient has the dtype of its parameter: dx and the
  * expert weight and bias gradients bf16, the router's fp32 (accumulation is
@@ -274,6 +277,8 @@ moe_status_t moe_forward(const moe_config_t *cfg, const moe_weights_t *w,
  *   hidden [R, h], preact [R, N_up] bf16 or NULL (moe_expert_up_train's):
  *     when preact is NULL the pre-activations are recomputed (one more up
  *     projection); when hidden is NULL it is formed from the pre-activations
+ *   logits [T, E] fp32 (moe_route's scores) under MOE_GATE_SOFTMAX_ALL,
+ *     else ignored (may be NULL)
  *   importance [E] fp32 or NULL (moe_permute's), importance_weight: the
  *     weight of the CV^2(Importance) term (ignored when importance is NULL)
  *   grads: every pointer device memory, written in full:
@@ -301,7 +306,7 @@ moe_status_t moe_backward(const moe_config_t *cfg, const moe_weights_t *w,
                           const void *x, const void *dy, const int32_t *topk_idx,
                           const float *topk_w, const int32_t *offsets,
                           const int32_t *pos, const void *x_perm, const void *y_perm,
-                          const void *hidden, const void *preact,
+                          const void *hidden, const void *preact, const float *logits,
                           const float *importance, float importance_weight,
                           const moe_grads_t *grads, void *ws, size_t ws_bytes,
                           hipStream_t stream);

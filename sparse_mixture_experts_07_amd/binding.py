@@ -81,7 +81,7 @@ def lib():
             "moe_grouped_rows": [P, P],
             "moe_route": [P, P, P, P, P, P, P, P, P],
             "moe_backward_workspace_bytes": [P, P],
-            "moe_backward": [P, P, P, P, P, P, P, P, P, P, P, P, P, C.c_float, P, P,
+            "moe_backward": [P, P, P, P, P, P, P, P, P, P, P, P, P, P, C.c_float, P, P,
                              C.c_size_t, P],
             "moe_expert_up_train": [P, P, P, P, P, P, P, P],
             "moe_route_noisy": [P, P, P, P, P, P, P, P, P, P, P, P, P, P, P,
@@ -213,12 +213,12 @@ def moe_backward_workspace_bytes(cfg: MoeConfig) -> int:
 
 def moe_backward(cfg, w: MoeWeights, x, dy, topk_idx, topk_w, offsets, pos, x_perm, y_perm,
                  importance, importance_weight: float, g: MoeGrads, ws, ws_bytes=None,
-                 stream=None, hidden=None, preact=None) -> None:
+                 stream=None, hidden=None, preact=None, logits=None) -> None:
     nb = _nbytes(ws) if ws_bytes is None and ws is not None else (ws_bytes or 0)
     _check("moe_backward", lib().moe_backward(
         C.byref(cfg), C.byref(w), _ptr(x), _ptr(dy), _ptr(topk_idx), _ptr(topk_w),
         _ptr(offsets), _ptr(pos), _ptr(x_perm), _ptr(y_perm), _ptr(hidden), _ptr(preact),
-        _ptr(importance), float(importance_weight), C.byref(g), _ptr(ws), nb,
+        _ptr(logits), _ptr(importance), float(importance_weight), C.byref(g), _ptr(ws), nb,
         _stream(stream)))
 
 

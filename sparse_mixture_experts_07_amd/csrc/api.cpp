@@ -155,7 +155,8 @@ void clear_pending_error() { (void)hipGetLastError(); }
 struct BwdLayout {
   size_t gimp, ds, dsp, ds_cols, poff, colsrc;
   size_t off_all, src_all, pos_all, hist, full_off, perm_w, imp_all;
-  size_t A, H, dyp, dH, dA, dxp, dypT, HT, dAT, xpT, total;
+  size_t A, H, dyp, dH, dA, dxp, dypT, HT, dAT, xpT;
+  size_t tm, dS, dxr, dpart, total;
 };
 
 BwdLayout bwd_layout(const moe_config_t *c) {
@@ -194,6 +195,13 @@ BwdLayout bwd_layout(const moe_config_t *c) {
   take(L.HT, 2 * h * Rp);
   take(L.dAT, 2 * nup * Rp);
   take(L.xpT, 2 * d * Rp);
+  const bool dense = c->gate == MOE_GATE_SOFTMAX_ALL;   // dense router gradients
+  take(L.tm, dense ? 4 * T : 0);
+  take(L.dS, dense ? 4 * T * E : 0);
+  take(L.dxr, dense ? 4 * T * d : 0);
+  int splits = 1, kchunk = 0;
+  if (dense && T > 0) moe::bwd_dense_plan(T, (int)E, (int)d, &splits, &kchunk);
+  take(L.dpart, splits > 1 ? 4 * (int64_t)splits * E * d : 0);
   L.total = o;
   return L;
 }
@@ -201,8 +209,7 @@ BwdLayout bwd_layout(const moe_config_t *c) {
 moe_status_t check_bwd_cfg(const moe_config_t *cfg) {
   moe_status_t st = check_cfg(cfg);
   if (st != MOE_OK) return st;
-  if (cfg->dtype != MOE_DTYPE_BF16 || cfg->gate == MOE_GATE_SOFTMAX_ALL)
-    return MOE_ERR_UNSUPPORTED;
+  if (cfg->dtype != MOE_DTYPE_BF16) return MOE_ERR_UNSUPPORTED;
   const int64_t Rp = moe::bwd_padded_cols(cfg->num_tokens, cfg->top_k, cfg->num_experts,
                                           cfg->num_shared);
   if (Rp >= (int64_t(1) << 31) / 512) return MOE_ERR_UNSUPPORTED;   // 32-bit tile offsets
@@ -468,7 +475,7 @@ moe_status_t moe_backward(const moe_config_t *cfg, const moe_weights_t *w, const
                           const void *dy, const int32_t *topk_idx, const float *topk_w,
                           const int32_t *offsets, const int32_t *pos, const void *x_perm,
                           const void *y_perm, const void *hidden, const void *preact,
-                          const float *importance,
+                          const float *logits, const float *importance,
                           float importance_weight, const moe_grads_t *g, void *ws,
                           size_t ws_bytes, hipStream_t stream) {
   moe_status_t st = check_bwd_cfg(cfg);
@@ -476,9 +483,10 @@ moe_status_t moe_backward(const moe_config_t *cfg, const moe_weights_t *w, const
   if ((st = check_weights(cfg, w, true, true, true)) != MOE_OK) return st;
   if (!g || !dev_ok(g->dw_gate) || !dev_ok(g->dw_up) || !dev_ok(g->dw_down) ||
       !opt_ok(g->db_gate) || !opt_ok(g->db_up) || !opt_ok(g->db_down) ||
-      !opt_ok(importance) || !opt_ok(hidden) || !opt_ok(preact) ||
+      !opt_ok(importance) || !opt_ok(hidden) || !opt_ok(preact) || !opt_ok(logits) ||
       !std::isfinite(importance_weight))
     return MOE_ERR_INVALID_ARGUMENT;
+  const bool softmax_all = cfg->gate == MOE_GATE_SOFTMAX_ALL;
   const bool swi = cfg->act == MOE_ACT_SWIGLU;
   if (swi && (g->db_up || g->db_down)) return MOE_ERR_INVALID_ARGUMENT;
   if (cfg->num_shared ? (!dev_ok(g->dw_up_shared) || !dev_ok(g->dw_down_shared))
@@ -504,7 +512,8 @@ moe_status_t moe_backward(const moe_config_t *cfg, const moe_weights_t *w, const
     return hip_status(e);
   }
   if (!dev_ok(x) || !dev_ok(dy) || !dev_ok(topk_idx) || !dev_ok(topk_w) || !dev_ok(offsets) ||
-      !dev_ok(pos) || !dev_ok(x_perm) || !dev_ok(y_perm) || !dev_ok(g->dx))
+      !dev_ok(pos) || !dev_ok(x_perm) || !dev_ok(y_perm) || !dev_ok(g->dx) ||
+      (softmax_all && !dev_ok(logits)))
     return MOE_ERR_INVALID_ARGUMENT;
   const BwdLayout L = bwd_layout(cfg);
   if (!dev_ok(ws)) return MOE_ERR_INVALID_ARGUMENT;
@@ -537,6 +546,7 @@ moe_status_t moe_backward(const moe_config_t *cfg, const moe_weights_t *w, const
   a.y_perm = static_cast<const uint16_t *>(y_perm);
   a.hidden = static_cast<const uint16_t *>(hidden);
   a.preact = static_cast<const uint16_t *>(preact);
+  a.logits = softmax_all ? logits : nullptr;
   a.dx = static_cast<uint16_t *>(g->dx);
   a.dw_gate = g->dw_gate;
   a.db_gate = g->db_gate;
@@ -572,6 +582,12 @@ moe_status_t moe_backward(const moe_config_t *cfg, const moe_weights_t *w, const
   b.HT = at<uint16_t>(ws, L.HT);
   b.dAT = at<uint16_t>(ws, L.dAT);
   b.xpT = at<uint16_t>(ws, L.xpT);
+  if (softmax_all) {
+    b.tm = at<float>(ws, L.tm);
+    b.dS = at<float>(ws, L.dS);
+    b.dxr = at<float>(ws, L.dxr);
+    b.dpart = at<float>(ws, L.dpart);
+  }
   return hip_status(moe::launch_backward(a, b, stream));
 }
 

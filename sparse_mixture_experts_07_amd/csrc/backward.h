@@ -18,7 +18,15 @@ struct BwdBuffers {
   float *perm_w, *imp_all;
   uint16_t *A, *H, *dyp, *dH, *dA, *dxp;
   uint16_t *dypT, *HT, *dAT, *xpT;
+  // softmax-all gate: per-token m [T], dense score gradients [T, E], the
+  // router's share of dx [T, d] (fp32)
+  float *tm, *dS, *dxr;
+  float *dpart;   // [splits, E, d] partial dW_g when the plan has several splits
 };
+
+// Token splits of the softmax-all gate's dense router weight gradient
+// (its partial sums take splits * E * d floats when splits > 1).
+void bwd_dense_plan(int64_t T, int E, int d, int *splits, int *kchunk);
 
 struct BwdArgs {
   int T, k, E, S, d, h, swiglu, capacity;
@@ -30,6 +38,7 @@ struct BwdArgs {
   float w_imp;
   const uint16_t *x_perm, *y_perm;
   const uint16_t *hidden, *preact;   // from the training forward, or NULL
+  const float *logits;   // the forward's router scores [T, E] (softmax-all gate), else NULL
   uint16_t *dx;
   float *dw_gate, *db_gate;   // fp32, the router's dtype
   uint16_t *dw_up, *dw_down, *db_up, *db_down, *dw_up_s, *dw_down_s;   // bf16

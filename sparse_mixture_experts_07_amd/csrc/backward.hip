@@ -75,7 +75,8 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_gate_kernel(
     const uint16_t *__restrict__ dy, const uint16_t *__restrict__ y_perm,
     const int32_t *__restrict__ pos, const int32_t *__restrict__ idx,
     const float *__restrict__ w, const float *__restrict__ gimp, int T, int k, int d, int E,
-    int S, int rows, uint16_t *__restrict__ dyp, float *__restrict__ ds) {
+    int S, int rows, uint16_t *__restrict__ dyp, float *__restrict__ ds,
+    float *__restrict__ tm) {
   __shared__ float red[kBwdThreads / kWave];
   __shared__ float dwp[kMaxExperts];
   const int t = blockIdx.x;
@@ -119,6 +120,7 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_gate_kernel(
       const float wj = w[(int64_t)t * k + j];
       ds[(int64_t)t * k + j] = wj * (dwp[j] - m);
     }
+    if (tm) tm[t] = m;
   }
 }
 
@@ -375,8 +377,8 @@ __global__ __launch_bounds__(kWave) void bwd_group_sum_kernel(
 __global__ __launch_bounds__(kBwdThreads) void bwd_dx_kernel(
     const uint16_t *__restrict__ dxp, const int32_t *__restrict__ pos,
     const float *__restrict__ ds, const int32_t *__restrict__ idx,
-    const float *__restrict__ wg, int T, int k, int d, int E, int S, int rows,
-    uint16_t *__restrict__ dx) {
+    const float *__restrict__ wg, const float *__restrict__ dxr, int T, int k, int d, int E,
+    int S, int rows, uint16_t *__restrict__ dx) {
   const int t = blockIdx.x;
   for (int c = 4 * threadIdx.x; c < d; c += 4 * kBwdThreads) {
     float acc[4] = {0.f, 0.f, 0.f, 0.f};
@@ -396,14 +398,22 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dx_kernel(
       acc[2] += bf16_lo(v.y);
       acc[3] += bf16_hi(v.y);
     }
-    for (int j = 0; j < k; ++j) {
-      const int e = min(max(idx[(int64_t)t * k + j], 0), E - 1);
-      const float sj = ds[(int64_t)t * k + j];
-      const float4 wv = *reinterpret_cast<const float4 *>(wg + (int64_t)e * d + c);
-      acc[0] += sj * wv.x;
-      acc[1] += sj * wv.y;
-      acc[2] += sj * wv.z;
-      acc[3] += sj * wv.w;
+    if (dxr) {   // dense router term (softmax-all gate)
+      const float4 r = *reinterpret_cast<const float4 *>(dxr + (int64_t)t * d + c);
+      acc[0] += r.x;
+      acc[1] += r.y;
+      acc[2] += r.z;
+      acc[3] += r.w;
+    } else {
+      for (int j = 0; j < k; ++j) {
+        const int e = min(max(idx[(int64_t)t * k + j], 0), E - 1);
+        const float sj = ds[(int64_t)t * k + j];
+        const float4 wv = *reinterpret_cast<const float4 *>(wg + (int64_t)e * d + c);
+        acc[0] += sj * wv.x;
+        acc[1] += sj * wv.y;
+        acc[2] += sj * wv.z;
+        acc[3] += sj * wv.w;
+      }
     }
     uint2 o;
     o.x = pack_bf16x2(acc[0], acc[1]);
@@ -421,6 +431,205 @@ __global__ void bwd_col_token_kernel(const int32_t *__restrict__ colsrc,
     const int r = colsrc[j];
     colsrc_tok[j] = (r >= 0 && r < n) ? min(max(perm_src[r], 0), T - 1) : -1;
   }
+}
+
+// Softmax-all gate: the gate values are w_j = p_{i_j} with p the softmax of
+// all E scores, so every score has a gradient: ds_e = p_e (dw'_e [e kept] -
+// m) with m = sum_j w_j dw'_j; for a kept expert this is the ds of the gate
+// kernel.  One wavefront per token writes the dense row dS[t][0..E).
+__global__ __launch_bounds__(kWave) void bwd_dense_ds_kernel(
+    const float *__restrict__ logits, const int32_t *__restrict__ idx,
+    const float *__restrict__ ds, const float *__restrict__ tm, int T, int E, int k,
+    float *__restrict__ dS) {
+  const int t = blockIdx.x;
+  const int lane = threadIdx.x;
+  const float *s = logits + (int64_t)t * E;
+  float mx = -INFINITY;
+  for (int e = lane; e < E; e += kWave) mx = fmaxf(mx, s[e]);
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+  float z = 0.0f;
+  for (int e = lane; e < E; e += kWave) z += expf(s[e] - mx);
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) z += __shfl_xor(z, off);
+  const float m = tm[t];
+  const int32_t *it = idx + (int64_t)t * k;
+  float *row = dS + (int64_t)t * E;
+  for (int e = lane; e < E; e += kWave) {
+    int j = 0;
+    while (j < k && it[j] != e) ++j;
+    row[e] = j < k ? ds[(int64_t)t * k + j] : -(expf(s[e] - mx) / z) * m;
+  }
+}
+
+// Dense fp32 products of the softmax-all gate's router gradients on the
+// fp32 matrix cores (v_mfma_f32_16x16x4_f32: lane l supplies A[l%16][l/16]
+// and B[l/16][l%16], and holds D[4(l/16)+r][l%16] in r = 0..3):
+//   C_z[m][n] = sum over k in split z of A(m, k) B[k][n]
+// with B [K][N] row-major (bf16 or fp32) and A [K][M] (AT) or [M][K].
+// Workgroup of 4 wavefronts (WM x WN), each a (16 MT) x (16 NT) block of
+// C; k in stages of 16 through LDS (rows padded by 16 floats so that the 4
+// k-rows of one MFMA operand fall in different banks), the next stage
+// loaded into registers while the current one is multiplied.
+template <bool AT>
+__device__ inline void dense_ld_a(const float *__restrict__ A, int M, int K, int m, int k,
+                                  float (&v)[4]) {
+  // AT: 4 consecutive m of row k; else 4 consecutive k of row m
+  const int64_t off = AT ? (int64_t)k * M + m : (int64_t)m * K + k;
+  const int n_ok = AT ? (k < K ? min(4, M - m) : 0) : (m < M ? min(4, K - k) : 0);
+  if (n_ok == 4 && (AT ? M % 4 == 0 : K % 4 == 0)) {
+    const float4 q = *reinterpret_cast<const float4 *>(A + off);
+    v[0] = q.x, v[1] = q.y, v[2] = q.z, v[3] = q.w;
+  } else {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) v[j] = j < n_ok ? A[off + j] : 0.0f;
+  }
+}
+
+__device__ inline void dense_ld_b(const float *__restrict__ B, int64_t off, bool ok,
+                                  float (&v)[4]) {
+  const float4 q = ok ? *reinterpret_cast<const float4 *>(B + off) : make_float4(0, 0, 0, 0);
+  v[0] = q.x, v[1] = q.y, v[2] = q.z, v[3] = q.w;
+}
+
+__device__ inline void dense_ld_b(const uint16_t *__restrict__ B, int64_t off, bool ok,
+                                  float (&v)[4]) {
+  const uint2 q = ok ? *reinterpret_cast<const uint2 *>(B + off) : make_uint2(0, 0);
+  v[0] = __uint_as_float(q.x << 16), v[1] = __uint_as_float(q.x & 0xffff0000u);
+  v[2] = __uint_as_float(q.y << 16), v[3] = __uint_as_float(q.y & 0xffff0000u);
+}
+
+template <int WM, int WN, int MT, int NT, bool AT, typename BT>
+__global__ __launch_bounds__(256) void bwd_dense_gemm_kernel(
+    const float *__restrict__ A, const BT *__restrict__ B, int M, int N, int K, int kchunk,
+    float *__restrict__ C) {
+  static_assert(WM * WN == 4, "four wavefronts");
+  constexpr int BM = WM * MT * 16, BN = WN * NT * 16, BK = 16;
+  constexpr int PA = BM + 16, PB = BN + 16;
+  constexpr int CA = BK * BM / 4, CB = BK * BN / 4;   // float4 chunks per stage
+  constexpr int NA = (CA + 255) / 256, NB = (CB + 255) / 256;
+  __shared__ float As[BK][PA];
+  __shared__ float Bs[BK][PB];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave / WN, wn = wave % WN;
+  const int m0 = blockIdx.y * BM, n0 = blockIdx.x * BN;
+  const int kb = blockIdx.z * kchunk, ke = min(K, kb + kchunk);
+  float ra[NA][4], rb[NB][4];
+  auto load = [&](int k0) {
+#pragma unroll
+    for (int q = 0; q < NA; ++q) {
+      const int i = tid + 256 * q;
+      if (i >= CA) break;
+      const int mm = AT ? (i % (BM / 4)) * 4 : i / (BK / 4);
+      const int kk = AT ? i / (BM / 4) : (i % (BK / 4)) * 4;
+      if (AT) {
+        dense_ld_a<true>(A, M, k0 + kk < ke ? K : 0, m0 + mm, k0 + kk, ra[q]);
+      } else {
+        // the k-range of this split bounds the row
+        dense_ld_a<false>(A, M, K, m0 + mm, k0 + kk, ra[q]);
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          if (k0 + kk + j >= ke) ra[q][j] = 0.0f;
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < NB; ++q) {
+      const int i = tid + 256 * q;
+      if (i >= CB) break;
+      const int kk = i / (BN / 4), nn = (i % (BN / 4)) * 4;
+      const int k = k0 + kk, n = n0 + nn;
+      dense_ld_b(B, (int64_t)k * N + n, k < ke && n < N, rb[q]);
+    }
+  };
+  auto store = [&]() {
+#pragma unroll
+    for (int q = 0; q < NA; ++q) {
+      const int i = tid + 256 * q;
+      if (i >= CA) break;
+      if (AT) {
+        const int kk = i / (BM / 4), mm = (i % (BM / 4)) * 4;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) As[kk][mm + j] = ra[q][j];
+      } else {
+        const int mm = i / (BK / 4), kk = (i % (BK / 4)) * 4;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) As[kk + j][mm] = ra[q][j];
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < NB; ++q) {
+      const int i = tid + 256 * q;
+      if (i >= CB) break;
+      const int kk = i / (BN / 4), nn = (i % (BN / 4)) * 4;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) Bs[kk][nn + j] = rb[q][j];
+    }
+  };
+  f32x4_t acc[MT][NT];
+#pragma unroll
+  for (int a = 0; a < MT; ++a)
+#pragma unroll
+    for (int b = 0; b < NT; ++b) acc[a][b] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+  if (kb < ke) load(kb);
+  for (int k0 = kb; k0 < ke; k0 += BK) {
+    __syncthreads();
+    store();
+    __syncthreads();
+    if (k0 + BK < ke) load(k0 + BK);
+    const int r = lane >> 4, c = lane & 15;
+#pragma unroll
+    for (int ks = 0; ks < BK; ks += 4) {
+      float av[MT], bv[NT];
+#pragma unroll
+      for (int a = 0; a < MT; ++a) av[a] = As[ks + r][(wm * MT + a) * 16 + c];
+#pragma unroll
+      for (int b = 0; b < NT; ++b) bv[b] = Bs[ks + r][(wn * NT + b) * 16 + c];
+#pragma unroll
+      for (int a = 0; a < MT; ++a)
+#pragma unroll
+        for (int b = 0; b < NT; ++b)
+          acc[a][b] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[a], bv[b], acc[a][b], 0, 0, 0);
+    }
+  }
+  float *Cz = C + (int64_t)blockIdx.z * M * N;
+  const int r = lane >> 4, c = lane & 15;
+#pragma unroll
+  for (int a = 0; a < MT; ++a)
+#pragma unroll
+    for (int b = 0; b < NT; ++b) {
+      const int n = n0 + (wn * NT + b) * 16 + c;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int m = m0 + (wm * MT + a) * 16 + 4 * r + q;
+        if (m < M && n < N) Cz[(int64_t)m * N + n] = acc[a][b][q];
+      }
+    }
+}
+
+// out[i] = sum over the splits z (ascending) of part[z][i], float4 lanes.
+__global__ void bwd_split_sum_kernel(const float *__restrict__ part, int splits, int64_t n4,
+                                     float *__restrict__ out) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n4) return;
+  const float4 *p = reinterpret_cast<const float4 *>(part) + i;
+  float4 s = p[0];
+  for (int z = 1; z < splits; ++z) {
+    const float4 v = p[(int64_t)z * n4];
+    s.x += v.x, s.y += v.y, s.z += v.z, s.w += v.w;
+  }
+  reinterpret_cast<float4 *>(out)[i] = s;
+}
+
+// db[e] = sum_t dS[t][e]: one wavefront per expert, lanes take t = lane,
+// lane + 64, ... in order, then a fixed butterfly.
+__global__ __launch_bounds__(kWave) void bwd_dense_bias_kernel(
+    const float *__restrict__ dS, int T, int E, float *__restrict__ db) {
+  const int e = blockIdx.x;
+  float s = 0.0f;
+  for (int t = threadIdx.x; t < T; t += kWave) s += dS[(int64_t)t * E + e];
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) s += __shfl_xor(s, off);
+  if (threadIdx.x == 0) db[e] = s;
 }
 
 __global__ void bwd_fill_f32_kernel(float *p, int64_t n, float v) {
@@ -465,6 +674,18 @@ int64_t bwd_padded_cols(int64_t T, int k, int E, int S) {
   return 64 * (n64 | 1);
 }
 
+// Token splits of the dense router weight gradient: enough workgroups to
+// fill the chip (about 1024), at least 128 tokens a split.
+void bwd_dense_plan(int64_t T, int E, int d, int *splits, int *kchunk) {
+  const int64_t tiles = E <= 32 ? (int64_t)((E + 15) / 16) * ((d + 255) / 256)
+                                : (int64_t)((E + 127) / 128) * ((d + 127) / 128);
+  int64_t z = std::max<int64_t>(1, std::min<int64_t>((1024 + tiles - 1) / tiles,
+                                                     (T + 127) / 128));
+  int64_t kc = ((T + z - 1) / z + 15) / 16 * 16;
+  *kchunk = (int)std::max<int64_t>(kc, 16);
+  *splits = (int)std::max<int64_t>(1, (T + *kchunk - 1) / *kchunk);
+}
+
 hipError_t launch_backward(const BwdArgs &a, const BwdBuffers &b, hipStream_t s) {
   const int T = a.T, k = a.k, E = a.E, S = a.S, d = a.d, h = a.h;
   const int G = E + S;
@@ -484,9 +705,18 @@ hipError_t launch_backward(const BwdArgs &a, const BwdBuffers &b, hipStream_t s)
     bwd_importance_grad_kernel<<<1, kBwdThreads, 0, s>>>(a.importance, E, a.w_imp, b.gimp);
     gimp = b.gimp;
   }
+  const bool dense = a.logits != nullptr;   // softmax-all gate: every score has a gradient
   bwd_gate_kernel<<<T, kBwdThreads, 0, s>>>(a.dy, a.y_perm, a.pos, a.idx, a.topk_w, gimp, T,
-                                            k, d, E, S, R, b.dyp, b.ds);
+                                            k, d, E, S, R, b.dyp, b.ds, dense ? b.tm : nullptr);
   MOE_TRY(hipGetLastError());
+  if (dense) {
+    bwd_dense_ds_kernel<<<T, kWave, 0, s>>>(a.logits, a.idx, b.ds, b.tm, T, E, k, b.dS);
+    // the router's share of dx: dS [T, E] times W_g [E, d]
+    bwd_dense_gemm_kernel<2, 2, 4, 4, false, float>
+        <<<dim3((d + 127) / 128, (T + 127) / 128, 1), 256, 0, s>>>(b.dS, a.w_gate, T, d, E, E,
+                                                                b.dxr);
+    MOE_TRY(hipGetLastError());
+  }
 
   // padded group columns
   bwd_layout_kernel<<<1, kBwdThreads, 0, s>>>(a.offsets, E, S, T, routed, b.poff);
@@ -514,8 +744,8 @@ hipError_t launch_backward(const BwdArgs &a, const BwdBuffers &b, hipStream_t s)
   MOE_TRY(launch_grouped_linear_bf16(a.offsets, E, S, T, k, nup, d, b.dA,
                                      b.dA + (int64_t)routed * nup, a.w_up, a.w_up_s, nullptr,
                                      b.dxp, true, s));
-  bwd_dx_kernel<<<T, kBwdThreads, 0, s>>>(b.dxp, a.pos, b.ds, a.idx, a.w_gate, T, k, d, E, S, R,
-                                         a.dx);
+  bwd_dx_kernel<<<T, kBwdThreads, 0, s>>>(b.dxp, a.pos, b.ds, a.idx, a.w_gate,
+                                         dense ? b.dxr : nullptr, T, k, d, E, S, R, a.dx);
   MOE_TRY(hipGetLastError());
 
   // weight gradients over each group's rows
@@ -538,6 +768,26 @@ hipError_t launch_backward(const BwdArgs &a, const BwdBuffers &b, hipStream_t s)
   if (a.db_up)
     bwd_rowsum_kernel<uint16_t><<<dim3(h, E), kWave, 0, s>>>(b.dAT, h, Rp, b.poff, nullptr,
                                                              a.db_up);
+  if (dense) {   // router gradients from the dense score gradients
+    // dW_g = dS^T X over token splits, then the splits summed in order
+    int splits, kchunk;
+    bwd_dense_plan(T, E, d, &splits, &kchunk);
+    float *dst = splits > 1 ? b.dpart : a.dw_gate;
+    if (E <= 32)
+      bwd_dense_gemm_kernel<1, 4, 1, 4, true, uint16_t>
+          <<<dim3((d + 255) / 256, (E + 15) / 16, splits), 256, 0, s>>>(b.dS, a.x, E, d, T,
+                                                                        kchunk, dst);
+    else
+      bwd_dense_gemm_kernel<2, 2, 4, 4, true, uint16_t>
+          <<<dim3((d + 127) / 128, (E + 127) / 128, splits), 256, 0, s>>>(b.dS, a.x, E, d, T,
+                                                                          kchunk, dst);
+    if (splits > 1) {
+      const int64_t n4 = (int64_t)E * d / 4;
+      bwd_split_sum_kernel<<<grid_for(n4, 256), 256, 0, s>>>(b.dpart, splits, n4, a.dw_gate);
+    }
+    if (a.db_gate) bwd_dense_bias_kernel<<<E, kWave, 0, s>>>(b.dS, T, E, a.db_gate);
+    return hipGetLastError();
+  }
   // router: dW_g[e] = sum over every assignment to e of ds * x, db_g[e] =
   // sum of ds.  A dropped slot has a score gradient too (its gate shapes the
   // kept softmax and Importance), so under a capacity every assignment is

@@ -43,7 +43,10 @@ def forward_saved(L, capacity=0, train=False):
              y_perm=torch.empty((R, d), dtype=torch.bfloat16, device=dev),
              y=torch.empty((T, d), dtype=torch.bfloat16, device=dev))
     ws = torch.empty(max(B.moe_workspace_bytes(c), 256), dtype=torch.uint8, device=dev)
-    B.moe_route(c, dl.x, dl.w_gate, dl.b_gate, s["idx"], s["w"], s["counts"])
+    # the softmax-all gate's backward reads the router scores
+    if L.cfg.gate == synthetic.GATE_SOFTMAX_ALL:
+        s["logits"] = torch.empty((T, E), dtype=torch.float32, device=dev)
+    B.moe_route(c, dl.x, dl.w_gate, dl.b_gate, s["idx"], s["w"], s["counts"], s.get("logits"))
     B.moe_permute(c, s["idx"], s["w"], dl.x, s["offsets"], s["perm_src"], s["pos"], s["imp"],
                   None, s["x_perm"], ws)
     if train:
@@ -81,7 +84,7 @@ def run_backward(L, dy_bits, capacity=0, imp_w=0.0, train=False):
     dy = to_device(dy_bits, dev)
     B.moe_backward(c, dl.weights(), dl.x, dy, s["idx"], s["w"], s["offsets"], s["pos"],
                    s["x_perm"], s["y_perm"], s["imp"] if imp_w else None, imp_w, mg, ws,
-                   hidden=s.get("hidden"), preact=s.get("preact"))
+                   hidden=s.get("hidden"), preact=s.get("preact"), logits=s.get("logits"))
     torch.cuda.synchronize()
     out = {("x" if n == "dx" else n): (to_f64(t) if t is not None else None) for n, t in g.items()}
     return out, s, (dl, mg, ws, dy)
@@ -182,6 +185,40 @@ def test_backward_bias_selects_gate(train):
                      bias=True, S=1, gate=synthetic.GATE_BIAS_SELECTS)
     errs = check_backward(L, 0, 0.4, train=train)
     print({n: f"{e:.2e}" for n, e in errs.items()})
+
+
+@pytest.mark.parametrize("case", [
+    (dict(T=300, d=128, h=256, E=8, k=2, act=SWIGLU, dtype=BF16, bias=True, S=1), 0, 0.4, False),
+    (dict(T=257, d=64, h=128, E=64, k=6, act=SWIGLU, dtype=BF16, bias=True), 0, 0.0, True),
+    (dict(T=400, d=64, h=128, E=6, k=2, act=GELU, dtype=BF16, bias=True, expert_bias=True),
+     150, 0.2, False),
+], ids=["shared-importance", "e64-train", "gelu-capacity"])
+def test_backward_softmax_all_gate(case):
+    """The softmax-all gate (the softmax over all E scores, read at the kept
+    experts): every score has a gradient, the unkept ones through the
+    normaliser, so the router gradients are dense."""
+    kw, cap, imp_w, train = case
+    L = random_layer(66, wstd=0.15, gate=synthetic.GATE_SOFTMAX_ALL, **kw)
+    errs = check_backward(L, cap, imp_w, train=train)
+    print({n: f"{e:.2e}" for n, e in errs.items()})
+
+
+def test_backward_softmax_all_needs_logits():
+    L = random_layer(66, T=64, d=64, h=64, E=4, k=2, act=SWIGLU, dtype=BF16, bias=True,
+                     gate=synthetic.GATE_SOFTMAX_ALL)
+    dy = f32_to_bf16_bits(np.random.default_rng(2).standard_normal((64, 64)).astype(np.float32))
+    dl, s = forward_saved(L)
+    s.pop("logits")
+    c, dev = dl.cfg, dl.x.device
+    f32 = dict(dtype=torch.float32, device=dev)
+    b16 = dict(dtype=torch.bfloat16, device=dev)
+    mg = B.grads(torch.empty((64, 64), **b16), torch.empty((4, 64), **f32),
+                 torch.empty((4, 128, 64), **b16), torch.empty((4, 64, 64), **b16),
+                 torch.empty(4, **f32))
+    ws = torch.empty(B.moe_backward_workspace_bytes(c), dtype=torch.uint8, device=dev)
+    with pytest.raises(RuntimeError, match="invalid"):
+        B.moe_backward(c, dl.weights(), dl.x, to_device(dy, dev), s["idx"], s["w"],
+                       s["offsets"], s["pos"], s["x_perm"], s["y_perm"], None, 0.0, mg, ws)
 
 
 def test_backward_is_deterministic():
