@@ -69,6 +69,9 @@ def lib():
         L.oracle_forward_tokens_keep.argtypes = [P, P, P, P, C.c_int64, P, P, P, P]
         L.oracle_capacity_keep.argtypes = [P, P, C.c_int32, P]
         L.oracle_permute_keep.argtypes = [P, P, P, P, P, P]
+        L.oracle_capacity_reroute.argtypes = [P, P, P, C.c_int32, P]
+        L.oracle_permute_assign.argtypes = [P, P, P, P, P]
+        L.oracle_forward_tokens_assign.argtypes = [P, P, P, P, C.c_int64, P, P, P, P]
         L.oracle_load_stats.argtypes = [P, P, C.c_int, P]
         L.oracle_param_counts.argtypes = [P, P, P]
         L.oracle_set_threads.argtypes = [C.c_int]
@@ -79,7 +82,9 @@ def lib():
                   "oracle_expert", "oracle_forward_tokens", "oracle_load_stats",
                   "oracle_param_counts", "oracle_max_threads",
                   "oracle_forward_tokens_keep", "oracle_capacity_keep",
-                  "oracle_permute_keep", "oracle_route_noisy", "oracle_cv2"):
+                  "oracle_permute_keep", "oracle_route_noisy", "oracle_cv2",
+                  "oracle_capacity_reroute", "oracle_permute_assign",
+                  "oracle_forward_tokens_assign"):
             getattr(L, f).restype = C.c_int
         _lib = L
     return _lib
@@ -205,6 +210,33 @@ def permute_keep(c, idx: np.ndarray, keep: np.ndarray):
     return off, src[: off[-1]], pos
 
 
+def capacity_reroute(c, idx: np.ndarray, scores: np.ndarray, capacity: int) -> np.ndarray:
+    """int32 [T*k]: the expert that computes each slot under a capacity with
+    one-hop next-choice re-routing of the overflow, -1 where it is dropped.
+    scores: float32 [T, E], the router scores the top k was taken on."""
+    idx = np.ascontiguousarray(idx, np.int32)
+    sc = np.ascontiguousarray(scores, np.float32)
+    assert sc.shape == (c.T, c.E)
+    assign = np.empty(c.T * c.k, np.int32)
+    cfg = _cfg(c)
+    _check(lib().oracle_capacity_reroute(C.byref(cfg), _ptr(idx), _ptr(sc), int(capacity),
+                                         _ptr(assign)), "oracle_capacity_reroute")
+    return assign
+
+
+def permute_assign(c, assign: np.ndarray):
+    """(offsets [E+1], perm_src [offsets[E]], pos [T*k] with -1 = dropped)
+    of the grouping by computing expert."""
+    assign = np.ascontiguousarray(assign, np.int32).reshape(-1)
+    off = np.empty(c.E + 1, np.int32)
+    src = np.empty(c.T * c.k, np.int32)
+    pos = np.empty(c.T * c.k, np.int32)
+    cfg = _cfg(c)
+    _check(lib().oracle_permute_assign(C.byref(cfg), _ptr(assign), _ptr(off), _ptr(src),
+                                       _ptr(pos)), "oracle_permute_assign")
+    return off, src[: off[-1]], pos
+
+
 def expert(layer, e: int, xrow: np.ndarray) -> np.ndarray:
     """Expert e (e == E: the shared expert) on one row, float64 [d]."""
     c = layer.cfg
@@ -217,9 +249,12 @@ def expert(layer, e: int, xrow: np.ndarray) -> np.ndarray:
     return y
 
 
-def forward_tokens(layer, tokens: Sequence[int], keep: Optional[np.ndarray] = None):
+def forward_tokens(layer, tokens: Sequence[int], keep: Optional[np.ndarray] = None,
+                   assign: Optional[np.ndarray] = None):
     """The layer on the listed tokens: (y float64 [n,d], idx [n,k], w [n,k]).
-    keep: uint8 [T*k] from capacity_keep (dropped slots add nothing)."""
+    keep: uint8 [T*k] from capacity_keep (dropped slots add nothing);
+    assign: int32 [T*k] from capacity_reroute (the computing expert of each
+    slot, -1 dropped)."""
     c = layer.cfg
     tok = np.ascontiguousarray(np.asarray(tokens, np.int64))
     n = tok.size
@@ -228,7 +263,13 @@ def forward_tokens(layer, tokens: Sequence[int], keep: Optional[np.ndarray] = No
     w = np.empty((n, c.k), np.float64)
     cfg = _cfg(c)
     W = _weights(layer)
-    if keep is None:
+    if assign is not None:
+        assign = np.ascontiguousarray(assign, np.int32).reshape(-1)
+        assert keep is None and assign.size == c.T * c.k
+        rc = lib().oracle_forward_tokens_assign(C.byref(cfg), C.byref(W), _ptr(layer.x),
+                                                _ptr(tok), n, _ptr(assign), _ptr(y),
+                                                _ptr(idx), _ptr(w))
+    elif keep is None:
         rc = lib().oracle_forward_tokens(C.byref(cfg), C.byref(W), _ptr(layer.x),
                                          _ptr(tok), n, _ptr(y), _ptr(idx), _ptr(w))
     else:

@@ -95,9 +95,12 @@ def preactivations(layer, e: int, xrows: np.ndarray) -> np.ndarray:
     return a.numpy()
 
 
-def forward(layer, p: dict, idx: np.ndarray, keep: Optional[np.ndarray] = None):
+def forward(layer, p: dict, idx: np.ndarray, keep: Optional[np.ndarray] = None,
+            assign: Optional[np.ndarray] = None):
     """(y [T, d], gate values [T, k], Importance [E]) as float64 tensors for
-    the fixed selection idx [T, k]."""
+    the fixed selection idx [T, k]; assign [T*k] (next-choice re-routing):
+    the expert that computes each slot, -1 dropped, the gate values still
+    those of idx."""
     cfg = layer.cfg
     T, k, E = cfg.T, cfg.k, cfg.E
     x = p["x"]
@@ -115,8 +118,9 @@ def forward(layer, p: dict, idx: np.ndarray, keep: Optional[np.ndarray] = None):
     if keep is not None:
         gk = g * torch.from_numpy(np.asarray(keep, np.float64).reshape(T, k))
     y = torch.zeros((T, cfg.d), dtype=torch.float64)
+    by = idx if assign is None else np.asarray(assign).reshape(T, k)
     for e in range(E):
-        t_sel, j_sel = np.nonzero(idx == e)
+        t_sel, j_sel = np.nonzero(by == e)
         if t_sel.size == 0:
             continue
         ts = torch.from_numpy(t_sel)
@@ -135,8 +139,9 @@ def cv2(v: torch.Tensor) -> torch.Tensor:
     return ((v - m) ** 2).mean() / (m * m)
 
 
-def loss(layer, p: dict, idx, dy: torch.Tensor, keep=None, importance_weight: float = 0.0):
-    y, _, imp = forward(layer, p, idx, keep)
+def loss(layer, p: dict, idx, dy: torch.Tensor, keep=None, importance_weight: float = 0.0,
+         assign=None):
+    y, _, imp = forward(layer, p, idx, keep, assign)
     L = (dy * y).sum()
     if importance_weight:
         L = L + importance_weight * cv2(imp)
@@ -144,14 +149,16 @@ def loss(layer, p: dict, idx, dy: torch.Tensor, keep=None, importance_weight: fl
 
 
 def backward(layer, dy: np.ndarray, keep: Optional[np.ndarray] = None,
-             importance_weight: float = 0.0, idx: Optional[np.ndarray] = None) -> dict:
+             importance_weight: float = 0.0, idx: Optional[np.ndarray] = None,
+             assign: Optional[np.ndarray] = None) -> dict:
     """Gradients (float64 numpy, keyed by the array names, 'x' included) of
     <dy, y> + importance_weight * CV^2(Importance) with the oracle's routing
-    (or the given selection idx)."""
+    (or the given selection idx; assign: the computing expert of each slot
+    under next-choice re-routing)."""
     if idx is None:
         idx, _, _ = _route(layer)
     p = params(layer)
-    L = loss(layer, p, idx, _f64(dy), keep, importance_weight)
+    L = loss(layer, p, idx, _f64(dy), keep, importance_weight, assign)
     names = list(p)
     grads = torch.autograd.grad(L, [p[n] for n in names], allow_unused=True)
     return {n: (np.zeros(tuple(p[n].shape)) if g is None else g.numpy())

@@ -51,6 +51,13 @@
  *   - expert capacity: an expert accepts its first C assignments in that
  *     flat order, the rest are dropped, the surviving weights are not
  *     renormalised (Go chapter, "What was simplified");
+ *   - next-choice re-routing of the overflow (Go chapter, "Design
+ *     viewpoints", capacity factor): one hop.  The o-th overflowing slot of
+ *     a token (slot order) is offered to the token's o-th best expert
+ *     outside its top k (score descending, ties to the lower index); each
+ *     expert accepts offers in flat order while it has room left after the
+ *     first round; an offer that finds no room is dropped.  The slot keeps
+ *     its gate value;
  *   - gate modes other than the default (cfg.gate):
  *     bias-selects: the router bias steers the selection only, the kept
  *     weights are the softmax of the unbiased kept scores (Go chapter,
@@ -361,6 +368,114 @@ int oracle_permute_keep(const oracle_cfg *c, const int32_t *idx,
   return 0;
 }
 
+/* Next-choice re-routing under a capacity (Go chapter, "Design viewpoints":
+ * an overflowing token is dropped or handed to its next candidate).  One hop:
+ *   1. expert e accepts its first C assignments in flat order f = t*k + j
+ *      (the drop rule above);
+ *   2. the o-th overflowing slot of token t (o counted in slot order) is
+ *      offered to the o-th best expert among those not in t's top k, best
+ *      meaning the higher score, ties to the lower index (no offer if there
+ *      are fewer than o + 1 such experts);
+ *   3. each expert accepts the offers in flat order while it has fewer than
+ *      C assignments; the rest are dropped.
+ * scores [T, E] float32 (the router scores the selection was taken on);
+ * assign[f] = the expert that computes slot f, or -1 if it is dropped.  The
+ * gate value of a slot is not changed by where it is computed. */
+static const float *rank_scores;   /* comparator context (single-threaded use) */
+static int by_score_then_index(const void *a, const void *b) {
+  const int ea = *(const int *)a, eb = *(const int *)b;
+  const float sa = rank_scores[ea], sb = rank_scores[eb];
+  if (sa > sb) return -1;
+  if (sa < sb) return 1;
+  return ea < eb ? -1 : (ea > eb);
+}
+
+int oracle_capacity_reroute(const oracle_cfg *c, const int32_t *idx, const float *scores,
+                            int32_t capacity, int32_t *assign) {
+  if (!cfg_ok(c) || !idx || !scores || !assign || capacity < 0) return -1;
+  const int64_t n = c->T * c->k;
+  const int E = c->E, k = c->k;
+  for (int64_t i = 0; i < c->T * E; ++i)
+    if (!isfinite(scores[i])) return -2;
+  int64_t *taken = (int64_t *)calloc((size_t)E, sizeof(int64_t));
+  int *cand = (int *)malloc(sizeof(int) * (size_t)E);
+  unsigned char *in_top = (unsigned char *)malloc((size_t)E);
+  int rc = 0;
+  /* 1. first round: the drop rule; -2 marks an overflowing slot */
+  for (int64_t f = 0; f < n && rc == 0; ++f) {
+    const int e = idx[f];
+    if (e < 0 || e >= E) {
+      rc = -1;
+      break;
+    }
+    if (capacity == 0 || taken[e] < capacity) {
+      assign[f] = e;
+      taken[e] += 1;
+    } else {
+      assign[f] = -2;
+    }
+  }
+  /* 2. offers: the token's ranked experts outside its top k */
+  int32_t *offer = (int32_t *)malloc(sizeof(int32_t) * (size_t)(n > 0 ? n : 1));
+  for (int64_t t = 0; t < c->T && rc == 0; ++t) {
+    for (int e = 0; e < E; ++e) in_top[e] = 0;
+    for (int j = 0; j < k; ++j) in_top[idx[t * k + j]] = 1;
+    int nc = 0;
+    for (int e = 0; e < E; ++e)
+      if (!in_top[e]) cand[nc++] = e;
+    rank_scores = scores + t * E;
+    qsort(cand, (size_t)nc, sizeof(int), by_score_then_index);
+    int o = 0;
+    for (int j = 0; j < k; ++j) {
+      const int64_t f = t * k + j;
+      offer[f] = -1;
+      if (assign[f] != -2) continue;
+      if (o < nc) offer[f] = cand[o];
+      ++o;
+    }
+  }
+  /* 3. second round: offers accepted in flat order while there is room */
+  for (int64_t f = 0; f < n && rc == 0; ++f) {
+    if (assign[f] != -2) continue;
+    const int e = offer[f];
+    if (e >= 0 && taken[e] < capacity) {
+      assign[f] = e;
+      taken[e] += 1;
+    } else {
+      assign[f] = -1;
+    }
+  }
+  free(offer);
+  free(taken);
+  free(cand);
+  free(in_top);
+  return rc;
+}
+
+/* Grouping by the computing expert of each slot (assign[f], -1 = dropped):
+ * offsets[E+1] over the computed rows, perm_src[p] for p < offsets[E],
+ * pos[f] = -1 for a dropped slot; rows in flat order within a group. */
+int oracle_permute_assign(const oracle_cfg *c, const int32_t *assign, int32_t *offsets,
+                          int32_t *perm_src, int32_t *pos) {
+  if (!cfg_ok(c) || !assign || !offsets || !perm_src || !pos) return -1;
+  const int64_t n = c->T * c->k;
+  for (int64_t f = 0; f < n; ++f)
+    if (assign[f] < -1 || assign[f] >= c->E) return -1;
+  int64_t p = 0;
+  for (int64_t f = 0; f < n; ++f) pos[f] = -1;
+  for (int e = 0; e < c->E; ++e) {
+    offsets[e] = (int32_t)p;
+    for (int64_t f = 0; f < n; ++f) {
+      if (assign[f] != e) continue;
+      perm_src[p] = (int32_t)(f / c->k);
+      pos[f] = (int32_t)p;
+      ++p;
+    }
+  }
+  offsets[c->E] = (int32_t)p;
+  return 0;
+}
+
 /* One expert (e < E routed, e == E shared) applied to one row, in double. */
 int oracle_expert(const oracle_cfg *c, const oracle_weights *W, int e,
                   const double *xr, double *yr) {
@@ -372,17 +487,17 @@ int oracle_expert(const oracle_cfg *c, const oracle_weights *W, int e,
   return 0;
 }
 
-/* The whole layer on the listed tokens: y[r] = sum_j w_j * E_{idx_j}(x_t)
- * (+ the shared expert with weight 1), accumulated in slot order.  keep
- * (T*k flags from oracle_capacity_keep, or NULL = keep all): a dropped slot
- * adds nothing and the other weights are not renormalised. */
-int oracle_forward_tokens_keep(const oracle_cfg *c, const oracle_weights *W,
+/* The whole layer on the listed tokens (the two entry points below). */
+static int forward_tokens_impl(const oracle_cfg *c, const oracle_weights *W,
                                const void *x, const int64_t *tokens, int64_t nt,
-                               const unsigned char *keep, double *y, int32_t *idx,
-                               double *w) {
+                               const unsigned char *keep, const int32_t *assign,
+                               double *y, int32_t *idx, double *w) {
   if (!cfg_ok(c) || !W || !W->w_gate || !x || !tokens || !y || !idx || !w ||
       nt < 0)
     return -1;
+  if (assign)
+    for (int64_t f = 0; f < c->T * c->k; ++f)
+      if (assign[f] < -1 || assign[f] >= c->E) return -1;
   if (c->S && (!W->w_up_shared || !W->w_down_shared)) return -1;
   for (int64_t r = 0; r < nt; ++r)
     if (tokens[r] < 0 || tokens[r] >= c->T) return -1;
@@ -411,7 +526,9 @@ int oracle_forward_tokens_keep(const oracle_cfg *c, const oracle_weights *W,
       for (int64_t i = 0; i < d; ++i) yo[i] = 0.0;
       for (int j = 0; j < c->k; ++j) {
         if (keep && !keep[t * c->k + j]) continue;
-        expert_ffn(c, W, ix[j], xr, hid, ye);
+        const int e = assign ? assign[t * c->k + j] : ix[j];   /* computing expert */
+        if (e < 0) continue;                                   /* dropped */
+        expert_ffn(c, W, e, xr, hid, ye);
         for (int64_t i = 0; i < d; ++i) yo[i] += wr[j] * ye[i];
       }
       if (c->S) {
@@ -427,6 +544,28 @@ int oracle_forward_tokens_keep(const oracle_cfg *c, const oracle_weights *W,
     free(hid);
   }
   return bad ? -2 : 0;
+}
+
+/* The whole layer on the listed tokens: y[r] = sum_j w_j * E_{idx_j}(x_t)
+ * (+ the shared expert with weight 1), accumulated in slot order.  keep
+ * (T*k flags from oracle_capacity_keep, or NULL = keep all): a dropped slot
+ * adds nothing and the other weights are not renormalised. */
+int oracle_forward_tokens_keep(const oracle_cfg *c, const oracle_weights *W,
+                               const void *x, const int64_t *tokens, int64_t nt,
+                               const unsigned char *keep, double *y, int32_t *idx,
+                               double *w) {
+  return forward_tokens_impl(c, W, x, tokens, nt, keep, NULL, y, idx, w);
+}
+
+/* The same with the computing expert of every slot given (T*k entries from
+ * oracle_capacity_reroute, -1 = dropped): y[r] = sum_j w_j *
+ * E_{assign_j}(x_t), the gate values w_j those of the top-k selection. */
+int oracle_forward_tokens_assign(const oracle_cfg *c, const oracle_weights *W,
+                                 const void *x, const int64_t *tokens, int64_t nt,
+                                 const int32_t *assign, double *y, int32_t *idx,
+                                 double *w) {
+  if (!assign) return -1;
+  return forward_tokens_impl(c, W, x, tokens, nt, NULL, assign, y, idx, w);
 }
 
 /* Side statistics: out[0] = CV^2(Importance), out[1] = CV^2(Load = counts),

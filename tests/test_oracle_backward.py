@@ -117,3 +117,31 @@ def test_gate_modes_forward_and_gradients(gate):
         assert np.all(gr["b_gate"] == 0)
     else:
         assert np.abs(gr["b_gate"]).max() > 0
+
+
+def test_rerouted_forward_and_gradients():
+    """Next-choice re-routing: the torch forward over the computing experts
+    equals the C oracle's, gradcheck holds, and an expert that computes no
+    slot gets no gradient while the router still does through the gates."""
+    L = random_layer(11, T=12, d=6, h=5, E=5, k=2, act=SWIGLU, bias=True)
+    L.b_gate = np.asarray([1.5, 1.0, 0, 0, 0], np.float32)
+    idx, _, sc = oracle.route(L, want_scores=True)
+    assign = oracle.capacity_reroute(L.cfg, idx, sc, 4)
+    keep = oracle.capacity_keep(L.cfg, idx, 4)
+    assert ((keep == 0) & (assign >= 0)).any()
+    p = B.params(L)
+    y, _, _ = B.forward(L, p, idx, assign=assign)
+    yc, _, _ = oracle.forward_tokens(L, range(12), assign=assign)
+    np.testing.assert_allclose(y.detach().numpy(), yc, rtol=1e-6, atol=1e-7 * np.abs(yc).max())
+    dy = torch.from_numpy(np.random.default_rng(12).standard_normal((12, 6)))
+    names = list(p)
+
+    def f(*ts):
+        return B.loss(L, dict(zip(names, ts)), idx, dy, None, 0.2, assign)
+
+    assert torch.autograd.gradcheck(f, tuple(p[n] for n in names), eps=1e-6, atol=1e-6, rtol=1e-5)
+    g = B.backward(L, dy.numpy(), importance_weight=0.2, idx=idx, assign=assign)
+    for e in range(5):
+        if not (assign == e).any():
+            assert np.all(g["w_up"][e] == 0) and np.all(g["w_down"][e] == 0)
+    assert np.abs(g["w_gate"]).max() > 0

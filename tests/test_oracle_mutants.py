@@ -67,6 +67,19 @@ MUTANTS = {
     "noisy_threshold_not_excluding": ("order[tk[e] ? k : k - 1]", "order[k - 1]"),
     "smooth_load_uses_noisy_score": ("const double diff = (double)cs[e] - thr;",
                                      "const double diff = (double)hs[e] - thr;"),
+    "reroute_always_first_candidate": ("if (o < nc) offer[f] = cand[o];",
+                                       "if (o < nc) offer[f] = cand[0];"),
+    "reroute_ties_to_higher_index": ("return ea < eb ? -1 : (ea > eb);",
+                                     "return ea > eb ? -1 : (ea < eb);"),
+    "reroute_candidates_ascending": ("if (sa > sb) return -1;\n  if (sa < sb) return 1;",
+                                     "if (sa < sb) return -1;\n  if (sa > sb) return 1;"),
+    "reroute_room_off_by_one": ("if (e >= 0 && taken[e] < capacity) {",
+                                "if (e >= 0 && taken[e] <= capacity) {"),
+    "reroute_forward_ignores_assignment": (
+        "const int e = assign ? assign[t * c->k + j] : ix[j];", "const int e = ix[j];"),
+    "assign_grouping_perm_src_modulo": (
+        "if (assign[f] != e) continue;\n      perm_src[p] = (int32_t)(f / c->k);",
+        "if (assign[f] != e) continue;\n      perm_src[p] = (int32_t)(f % c->k);"),
     "smooth_load_cdf_sign": ("return 0.5 * erfc(-z * M_SQRT1_2);",
                              "return 0.5 * erfc(z * M_SQRT1_2);"),
 }

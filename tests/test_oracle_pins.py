@@ -473,6 +473,143 @@ def test_token_with_every_slot_dropped(oracle_lib):
             np.testing.assert_array_equal(y[0], np.zeros(c.d))
 
 
+# ---- next-choice re-routing of the overflow (Go chapter, "Design
+# viewpoints", capacity factor: an overflowing token is dropped or handed to
+# its next candidate).  Reading: one hop; the o-th overflowing slot of a token
+# is offered to its o-th best expert outside its top k; experts take offers
+# in flat order into the room the first round left ----
+
+def _reroute(oracle_lib, scores, idx, C):
+    s = np.asarray(scores, np.float32)
+    idx = np.asarray(idx, np.int32).reshape(s.shape[0], -1)
+    c = synthetic.TINY.with_(T=s.shape[0], E=s.shape[1], k=idx.shape[1])
+    return oracle_lib.capacity_reroute(c, idx, s, C).tolist()
+
+
+def test_reroute_worked_examples(oracle_lib):
+    # every token prefers expert 0 (C = 1): token 1 moves to its second
+    # choice 2, token 2 to its second choice 1
+    assert _reroute(oracle_lib, [[3, 2, 1], [3, 1, 2], [3, 2, 1]], [0, 0, 0], 1) == [0, 2, 1]
+    # two offers to the same expert: the earlier token takes the one place
+    assert _reroute(oracle_lib, [[3, 2, 1]] * 3, [0, 0, 0], 1) == [0, 1, -1]
+    # a token with both slots overflowing: slot 0 gets its best expert
+    # outside the top 2 (expert 3, score 2), slot 1 the next one (expert 2)
+    assert _reroute(oracle_lib, [[4, 3, 2, 1], [4, 3, 1, 2]], [[0, 1], [0, 1]], 1) == [0, 1, 3, 2]
+    # equal candidate scores: the lower index first
+    assert _reroute(oracle_lib, [[5, 1, 1, 1]] * 2, [0, 0], 1) == [0, 1]
+    # the first round fills every expert before any offer: token 2's own
+    # choice of expert 1 outranks token 1's offer to it, and the offer is
+    # dropped (one hop: no third try)
+    assert _reroute(oracle_lib, [[3, 1, 2], [3, 2, 1], [1, 3, 2]], [0, 0, 1], 1) == [0, -1, 1]
+
+
+def _ranked_outside(scores_t, top):
+    rest = [e for e in range(len(scores_t)) if e not in set(top)]
+    return sorted(rest, key=lambda e: (-float(scores_t[e]), e))
+
+
+@pytest.mark.parametrize("C", [12, 17, 25])
+def test_reroute_against_brute_force(oracle_lib, C):
+    """Re-implementation by rounds over Python lists of the reading, on
+    skewed routings: kept slots unchanged, offers by ordinal, room left."""
+    T, E, k = 40, 7, 3
+    L = random_layer(20 + C, T=T, d=8, h=8, E=E, k=k, bias=True)
+    L.b_gate = np.asarray([2.0, 1.5, 1.0, 0, 0, 0, 0], np.float32)   # skew to low experts
+    c = L.cfg
+    idx, _, sc = oracle_lib.route(L, want_scores=True)
+    assign = oracle_lib.capacity_reroute(c, idx, sc, C)
+    keep = oracle_lib.capacity_keep(c, idx, C)
+    flat = idx.ravel()
+    taken = np.minimum(np.bincount(flat, minlength=E), C)
+    ref = np.where(keep == 1, flat, -1)
+    offers = {}
+    for t in range(T):
+        cand = _ranked_outside(sc[t], idx[t])
+        o = 0
+        for j in range(k):
+            f = t * k + j
+            if keep[f]:
+                continue
+            offers[f] = cand[o] if o < len(cand) else -1
+            o += 1
+    for f in sorted(offers):
+        e = offers[f]
+        if e >= 0 and taken[e] < C:
+            ref[f] = e
+            taken[e] += 1
+    np.testing.assert_array_equal(assign, ref)
+    assert (keep == 0).any() and (assign[keep == 0] >= 0).any()
+    # invariants: capacity honoured, re-routed experts outside the top k
+    assert (np.bincount(assign[assign >= 0], minlength=E) <= C).all()
+    for f in np.flatnonzero((keep == 0) & (assign >= 0)):
+        assert assign[f] not in idx[f // k]
+
+
+def test_reroute_degenerate_cases(oracle_lib):
+    L = random_layer(21, T=30, d=8, h=8, E=4, k=2)
+    c = L.cfg
+    idx, _, sc = oracle_lib.route(L, want_scores=True)
+    # no limit, or room for everything: every slot computed where it was routed
+    for C in (0, c.T * c.k):
+        np.testing.assert_array_equal(oracle_lib.capacity_reroute(c, idx, sc, C), idx.ravel())
+    # E = k: no expert outside the top k, so re-routing is the drop rule
+    L2 = random_layer(22, T=30, d=8, h=8, E=2, k=2)
+    idx2, _, sc2 = oracle_lib.route(L2, want_scores=True)
+    keep = oracle_lib.capacity_keep(L2.cfg, idx2, 7)
+    np.testing.assert_array_equal(oracle_lib.capacity_reroute(L2.cfg, idx2, sc2, 7),
+                                  np.where(keep == 1, idx2.ravel(), -1))
+
+
+def test_assign_grouping(oracle_lib):
+    """Rows grouped by computing expert in flat order (numpy lexsort); with
+    the drop rule's assignment it is the kept grouping."""
+    T, E, k, C = 50, 5, 3, 9
+    idx = _routing(7, T, E, k)
+    c = synthetic.TINY.with_(T=T, E=E, k=k)
+    keep = oracle_lib.capacity_keep(c, idx, C)
+    drop_assign = np.where(keep == 1, idx.ravel(), -1).astype(np.int32)
+    for a, b in zip(oracle_lib.permute_assign(c, drop_assign),
+                    oracle_lib.permute_keep(c, idx, keep)):
+        np.testing.assert_array_equal(a, b)
+    rng = np.random.default_rng(3)
+    assign = rng.integers(-1, E, size=T * k).astype(np.int32)
+    off, src, pos = oracle_lib.permute_assign(c, assign)
+    live = np.flatnonzero(assign >= 0)
+    order = live[np.lexsort((live, assign[live]))]
+    np.testing.assert_array_equal(off, np.concatenate(
+        [[0], np.cumsum(np.bincount(assign[live], minlength=E))]))
+    np.testing.assert_array_equal(src, order // k)
+    ref_pos = np.full(T * k, -1, np.int32)
+    ref_pos[order] = np.arange(order.size)
+    np.testing.assert_array_equal(pos, ref_pos)
+
+
+@pytest.mark.parametrize("S", [0, 1])
+def test_rerouted_forward_is_gated_sum_over_computing_experts(oracle_lib, S):
+    """y_t = sum_j G_j E_{a_j}(x_t) (+ shared): the kept-k softmax values
+    (scipy) applied to the expert that computes each slot."""
+    L = random_layer(23, T=24, d=10, h=14, E=5, k=2, act=SWIGLU, S=S, bias=True)
+    L.b_gate = np.asarray([1.5, 1.0, 0, 0, 0], np.float32)
+    c = L.cfg
+    idx, _, sc = oracle_lib.route(L, want_scores=True)
+    assign = oracle_lib.capacity_reroute(c, idx, sc, 6)
+    keep = oracle_lib.capacity_keep(c, idx, 6)
+    assert ((keep == 0) & (assign >= 0)).any() and (assign < 0).any()
+    y, _, _ = oracle_lib.forward_tokens(L, range(c.T), assign=assign)
+    for t in range(c.T):
+        top = np.argsort(-sc[t].astype(np.float64), kind="stable")[:c.k]
+        G = scipy.special.softmax(sc[t, top].astype(np.float64))
+        xr = L.x[t].astype(np.float64)
+        ref = np.zeros(c.d)
+        for j in range(c.k):
+            e = assign[t * c.k + j]
+            if e >= 0:
+                ref = ref + G[j] * oracle_lib.expert(L, int(e), xr)
+        if S:
+            ref = ref + oracle_lib.expert(L, c.E, xr)
+        np.testing.assert_allclose(y[t], ref, rtol=1e-12, atol=1e-14)
+
+
 # ---- gate modes.  bias-selects: the bias steers the selection only (Go
 # chapter, section 3 and "Pros, cons and real examples": DeepSeek-V3 balances
 # load through a bias instead of a loss); softmax-all: the softmax over all E
