@@ -47,6 +47,9 @@ def parse():
                    help="training step: the forward stages, then moe_backward")
     p.add_argument("--capacity-factor", type=float, default=0.0,
                    help="per-expert capacity ceil(f*T*k/E) with drops (0: none)")
+    p.add_argument("--overflow", choices=["drop", "next-choice"], default="drop",
+                   help="beyond the capacity: drop, or hand the slot on once to the "
+                        "token's next choice")
     p.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "traffic.txt"),
                    help="measured HBM bytes of the dominant kernel per workload (JSON text)")
     p.add_argument("--copy-calibration", action="store_true",
@@ -100,7 +103,10 @@ def main():
     cap = 0
     if args.capacity_factor > 0:
         cap = B.moe_expert_capacity(cfg.T, cfg.k, cfg.E, args.capacity_factor)
-    dl = DeviceLayer.upload(L, capacity=cap)
+    overflow = B.MOE_OVERFLOW_NEXT_CHOICE if args.overflow == "next-choice" else 0
+    if overflow and not cap:
+        sys.exit("--overflow next-choice needs --capacity-factor")
+    dl = DeviceLayer.upload(L, capacity=cap, overflow=overflow)
     gen_s = time.time() - t_gen
     c, W = dl.cfg, dl.weights()
     T, k, E, d, h = cfg.T, cfg.k, cfg.E, cfg.d, cfg.h
@@ -121,9 +127,11 @@ def main():
     y_perm = torch.empty((R, d), dtype=dt, device=dev)
     y = torch.empty((T, d), dtype=dt, device=dev)
     ws = torch.empty(B.moe_workspace_bytes(c), dtype=torch.uint8, device=dev)
-    # the softmax-all gate's backward reads the forward's router scores
+    # the softmax-all gate's backward and next-choice re-routing read the
+    # forward's router scores
     logits = (torch.empty((T, E), dtype=torch.float32, device=dev)
-              if args.backward and cfg.gate == synthetic.GATE_SOFTMAX_ALL else None)
+              if (args.backward and cfg.gate == synthetic.GATE_SOFTMAX_ALL) or overflow
+              else None)
     if args.noisy:
         from sparse_mixture_experts_07_amd.device import to_device
         w_noise, noise = to_device(L.w_noise, dev), to_device(noise_np, dev)
@@ -162,7 +170,8 @@ def main():
 
     def step(ev=None):
         route()
-        B.moe_permute(c, idx, tw, dl.x, offsets, perm_src, pos, imp, stats, x_perm, ws)
+        B.moe_permute(c, idx, tw, dl.x, offsets, perm_src, pos, imp, stats, x_perm, ws,
+                      logits=logits)
         if ev is not None:
             ev[0].record()
         if args.backward:   # the training forward keeps the pre-activations
@@ -258,12 +267,15 @@ def main():
         per_tok = (time.perf_counter() - t1) / len(probe)
         n = int(min(T, max(len(probe), args.cpu_seconds / max(per_tok, 1e-9))))
         sample = np.linspace(0, T - 1, n).astype(np.int64)
-        keep = None
-        if cap:
-            ridx, _, _ = oracle.route(L)
-            keep = oracle.capacity_keep(cfg, ridx, cap)
+        keep = assign = None
+        if cap:   # the capacity decision is over the whole batch (not timed)
+            ridx, _, rsc = oracle.route(L, want_scores=overflow != 0)
+            if overflow:
+                assign = oracle.capacity_reroute(cfg, ridx, rsc, cap)
+            else:
+                keep = oracle.capacity_keep(cfg, ridx, cap)
         t1 = time.perf_counter()
-        oracle.forward_tokens(L, sample, keep=keep)
+        oracle.forward_tokens(L, sample, keep=keep, assign=assign)
         el = time.perf_counter() - t1
         cpu = {"value": n / el, "unit": "tokens/s", "cores": nthr, "kind": "oracle",
                "sample": f"{n} of {T} tokens (evenly spaced), full routing + "
@@ -288,8 +300,8 @@ def main():
                    "router_bias": cfg.router_bias,
                    **({"gate": args.gate} if cfg.gate else {}),
                    **({"noisy_gate": True} if args.noisy else {}),
-                   **({"capacity_factor": args.capacity_factor, "capacity": cap}
-                      if cap else {})},
+                   **({"capacity_factor": args.capacity_factor, "capacity": cap,
+                       "overflow": args.overflow} if cap else {})},
         "roofline": roof,
         "cpu_baseline": cpu,
         "layer_tflops": layer_flops / (ms_step / 1e3) / 1e12,

@@ -42,7 +42,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 5
+#define MOE_ABI_VERSION 6
 
 typedef enum {
   MOE_OK = 0,
@@ -79,6 +79,19 @@ typedef enum {
   MOE_GATE_SOFTMAX_ALL = 2
 } moe_gate_t;
 
+/* What happens to an assignment beyond an expert's capacity.
+ *   MOE_OVERFLOW_DROP: it is dropped (see moe_config_t.capacity).
+ *   MOE_OVERFLOW_NEXT_CHOICE: it is handed on once (Go chapter, "Design
+ *     viewpoints": an overflowing token is dropped or passed to its next
+ *     candidate).  After the first round (the drop rule), the o-th
+ *     overflowing slot of a token (slot order) is offered to the token's
+ *     o-th best expert outside its top k (higher score first, ties to the
+ *     lower index); every expert accepts offers in flat order t*k + j while
+ *     it holds fewer than C assignments; an offer that finds no room is
+ *     dropped.  A re-routed slot keeps its gate value (the router's output
+ *     for that slot) and is computed by the expert it was handed to. */
+typedef enum { MOE_OVERFLOW_DROP = 0, MOE_OVERFLOW_NEXT_CHOICE = 1 } moe_overflow_t;
+
 typedef struct {
   int64_t num_tokens;  /* T */
   int32_t d_model;     /* d */
@@ -97,6 +110,7 @@ typedef struct {
                           what an expert accepts and drop the overflow).
                           See moe_expert_capacity for C from a factor. */
   int32_t gate;        /* moe_gate_t (0 = softmax over the kept k) */
+  int32_t overflow;    /* moe_overflow_t (0 = drop); used when capacity > 0 */
 } moe_config_t;
 
 /* Expert weights, all packed over experts into single tensors ("Weight
@@ -180,13 +194,19 @@ moe_status_t moe_route_noisy(const moe_config_t *cfg, const void *x,
  * flat index t*k + j) and the row move x -> x_perm ("Expert Backend":
  * sort and group tokens by expert id before the grouped GEMM).
  *   topk_idx, topk_w [T, k]   (device, in) as written by moe_route
+ *   logits     [T, E] fp32    (device, in) moe_route's scores; read only
+ *              under a capacity with MOE_OVERFLOW_NEXT_CHOICE (the next
+ *              choices), else ignored (may be NULL)
  *   x          [T, d] dtype   (device, in)
  *   offsets    [E + 1] int32  (out) group starts of the kept assignments;
- *              offsets[E] = T*k without a capacity, else sum_e min(n_e, C)
+ *              offsets[E] = T*k without a capacity, else the number of
+ *              computed assignments (sum_e min(n_e, C) under the drop rule)
  *   perm_src   [T*k] int32    (out) source token of grouped row p, for
  *              p < offsets[E]
  *   pos        [T*k] int32    (out) grouped row of assignment (t, j), or -1
- *              if the expert capacity dropped it
+ *              if the expert capacity dropped it; under next-choice
+ *              re-routing the row lies in the group of the expert that
+ *              computes the slot (rows in flat order within a group)
  *   importance [E] fp32       (out) Importance(X)_e = sum of the router
  *              weights routed to e (Qiita summary, "Load-balancing losses"),
  *              summed in group order; dropped assignments included (they
@@ -198,7 +218,8 @@ moe_status_t moe_route_noisy(const moe_config_t *cfg, const void *x,
  *              p < offsets[E]
  *   ws         workspace >= moe_workspace_bytes() */
 moe_status_t moe_permute(const moe_config_t *cfg, const int32_t *topk_idx,
-                         const float *topk_w, const void *x, int32_t *offsets,
+                         const float *topk_w, const float *logits, const void *x,
+                         int32_t *offsets,
                          int32_t *perm_src, int32_t *pos, float *importance,
                          double *stats, void *x_perm, void *ws,
                          size_t ws_bytes, hipStream_t stream);

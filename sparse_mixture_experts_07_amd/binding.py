@@ -28,6 +28,8 @@ MOE_ACT_SWIGLU = 1
 MOE_GATE_TOPK_SOFTMAX = 0
 MOE_GATE_BIAS_SELECTS = 1
 MOE_GATE_SOFTMAX_ALL = 2
+MOE_OVERFLOW_DROP = 0
+MOE_OVERFLOW_NEXT_CHOICE = 1
 
 EXPORTS = (
     "moe_abi_version", "moe_status_string", "moe_workspace_bytes",
@@ -50,7 +52,8 @@ class MoeConfig(C.Structure):
                 ("d_hidden", C.c_int32), ("num_experts", C.c_int32),
                 ("top_k", C.c_int32), ("num_shared", C.c_int32),
                 ("act", C.c_int32), ("dtype", C.c_int32),
-                ("capacity", C.c_int32), ("gate", C.c_int32)]
+                ("capacity", C.c_int32), ("gate", C.c_int32),
+                ("overflow", C.c_int32)]
 
 
 class MoeWeights(C.Structure):
@@ -86,7 +89,7 @@ def lib():
             "moe_expert_up_train": [P, P, P, P, P, P, P, P],
             "moe_route_noisy": [P, P, P, P, P, P, P, P, P, P, P, P, P, P, P,
                                 C.c_size_t, P],
-            "moe_permute": [P, P, P, P, P, P, P, P, P, P, P, C.c_size_t, P],
+            "moe_permute": [P, P, P, P, P, P, P, P, P, P, P, P, C.c_size_t, P],
             "moe_expert_up": [P, P, P, P, P, P, P],
             "moe_expert_down": [P, P, P, P, P, P],
             "moe_expert_ffn": [P, P, P, P, P, P, P, C.c_size_t, P],
@@ -150,16 +153,16 @@ def _check(fn: str, st: int) -> None:
 
 
 def config(T: int, d: int, h: int, E: int, k: int, act: int, dtype: int,
-           S: int = 0, capacity: int = 0, gate: int = 0) -> MoeConfig:
+           S: int = 0, capacity: int = 0, gate: int = 0, overflow: int = 0) -> MoeConfig:
     return MoeConfig(int(T), int(d), int(h), int(E), int(k), int(S), int(act),
-                     int(dtype), int(capacity), int(gate))
+                     int(dtype), int(capacity), int(gate), int(overflow))
 
 
-def config_of(c, capacity: int = 0) -> MoeConfig:
+def config_of(c, capacity: int = 0, overflow: int = 0) -> MoeConfig:
     """From any object with T, d, h, E, k, S, act, dtype (and optionally
     gate) attributes."""
     return config(c.T, c.d, c.h, c.E, c.k, c.act, c.dtype, c.S, capacity,
-                  getattr(c, "gate", 0))
+                  getattr(c, "gate", 0), overflow)
 
 
 def weights(w_gate, w_up, w_down, b_gate=None, b_up=None, b_down=None,
@@ -241,10 +244,10 @@ def moe_route_noisy(cfg, x, w_gate, b_gate, w_noise, noise, clean_logits, noise_
 
 
 def moe_permute(cfg, topk_idx, topk_w, x, offsets, perm_src, pos, importance,
-                stats, x_perm, ws, ws_bytes=None, stream=None) -> None:
+                stats, x_perm, ws, ws_bytes=None, stream=None, logits=None) -> None:
     nb = _nbytes(ws) if ws_bytes is None and ws is not None else (ws_bytes or 0)
     _check("moe_permute", lib().moe_permute(
-        C.byref(cfg), _ptr(topk_idx), _ptr(topk_w), _ptr(x), _ptr(offsets),
+        C.byref(cfg), _ptr(topk_idx), _ptr(topk_w), _ptr(logits), _ptr(x), _ptr(offsets),
         _ptr(perm_src), _ptr(pos), _ptr(importance), _ptr(stats), _ptr(x_perm),
         _ptr(ws), nb, _stream(stream)))
 

@@ -8,23 +8,18 @@
 
 #include "moe.h"
 #include "backward.h"
+#include "permute.h"
 
 namespace moe {
 hipError_t launch_fill_i32(int32_t *p, int n, int32_t v, hipStream_t s);
 hipError_t launch_route(bool bf16, int gate, const void *x, const float *wg, const float *bg,
                         int T, int d, int E, int k, int32_t *idx, float *w,
                         int32_t *counts, float *logits, hipStream_t s);
-int perm_num_segments(int64_t n);
 int64_t noisy_workspace_bytes(int64_t T, int E);
 hipError_t launch_noisy_gate(const float *noise, int T, int E, int k, const float *clean,
                              float *scale, int32_t *idx, float *w, int32_t *counts,
                              float *importance, float *load, double *cv2, void *ws,
                              hipStream_t s);
-hipError_t launch_permute(const int32_t *idx, const float *w, const void *x, int T,
-                          int k, int E, int capacity, int row_bytes, int32_t *offsets,
-                          int32_t *perm_src, int32_t *pos, float *importance,
-                          double *stats, void *x_perm, int32_t *hist, int32_t *full_off,
-                          float *perm_w, hipStream_t s);
 hipError_t launch_expert_up_bf16(bool swiglu, const int32_t *offsets, int E, int S,
                                  int T, int k, int d, int h, const void *x_perm,
                                  const void *x, const void *w_up,
@@ -69,7 +64,8 @@ moe_status_t check_cfg(const moe_config_t *c) {
   if (c->num_tokens < 0 || c->d_model <= 0 || c->d_hidden <= 0 ||
       c->num_experts < 1 || c->top_k < 1 || c->top_k > c->num_experts ||
       c->num_shared < 0 || c->capacity < 0 || c->gate < MOE_GATE_TOPK_SOFTMAX ||
-      c->gate > MOE_GATE_SOFTMAX_ALL)
+      c->gate > MOE_GATE_SOFTMAX_ALL || c->overflow < MOE_OVERFLOW_DROP ||
+      c->overflow > MOE_OVERFLOW_NEXT_CHOICE)
     return MOE_ERR_INVALID_ARGUMENT;
   if ((c->act != MOE_ACT_GELU && c->act != MOE_ACT_SWIGLU) ||
       (c->dtype != MOE_DTYPE_F32 && c->dtype != MOE_DTYPE_BF16))
@@ -107,9 +103,14 @@ size_t elem_bytes(const moe_config_t *c) { return c->dtype == MOE_DTYPE_BF16 ? 2
 
 // Workspace regions, each 256-byte aligned, in this order.
 struct Layout {
-  size_t hist, full_off, perm_w, permute_end;   // moe_permute scratch
-  size_t offsets, perm_src, pos, x_perm, hidden, y_perm, total;  // moe_forward
+  size_t hist, full_off, perm_w;                        // moe_permute scratch
+  size_t pos_a, cand, pos_b, fin, off_b, full_off_b, imp_s, permute_end;  // re-routing
+  size_t offsets, perm_src, pos, logits, x_perm, hidden, y_perm, total;  // moe_forward
 };
+
+bool reroutes(const moe_config_t *c) {
+  return c->capacity > 0 && c->overflow == MOE_OVERFLOW_NEXT_CHOICE;
+}
 
 Layout layout(const moe_config_t *c) {
   const int64_t T = c->num_tokens, n = T * c->top_k;
@@ -121,10 +122,19 @@ Layout layout(const moe_config_t *c) {
   L.hist = o;      o += align_up(sizeof(int32_t) * (size_t)moe::perm_num_segments(n) * E);
   L.full_off = o;  o += align_up(sizeof(int32_t) * (size_t)(E + 1));
   L.perm_w = o;    o += align_up(sizeof(float) * (size_t)n);
+  const size_t rn = reroutes(c) ? (size_t)n : 0, re = reroutes(c) ? (size_t)E : 0;
+  L.pos_a = o;       o += align_up(sizeof(int32_t) * rn);
+  L.cand = o;        o += align_up(sizeof(int32_t) * rn);
+  L.pos_b = o;       o += align_up(sizeof(int32_t) * rn);
+  L.fin = o;         o += align_up(sizeof(int32_t) * rn);
+  L.off_b = o;       o += align_up(sizeof(int32_t) * (re ? re + 1 : 0));
+  L.full_off_b = o;  o += align_up(sizeof(int32_t) * (re ? re + 1 : 0));
+  L.imp_s = o;       o += align_up(sizeof(float) * re);
   L.permute_end = o;
   L.offsets = o;   o += align_up(sizeof(int32_t) * (size_t)(E + 1));
   L.perm_src = o;  o += align_up(sizeof(int32_t) * (size_t)n);
   L.pos = o;       o += align_up(sizeof(int32_t) * (size_t)n);
+  L.logits = o;    o += align_up(sizeof(float) * (reroutes(c) ? (size_t)T * E : 0));
   L.x_perm = o;    o += align_up(es * (size_t)n * c->d_model);
   L.hidden = o;    o += align_up(es * (size_t)R * c->d_hidden);
   L.y_perm = o;    o += align_up(es * (size_t)R * c->d_model);
@@ -307,7 +317,8 @@ moe_status_t moe_route_noisy(const moe_config_t *cfg, const void *x, const float
 }
 
 moe_status_t moe_permute(const moe_config_t *cfg, const int32_t *topk_idx,
-                         const float *topk_w, const void *x, int32_t *offsets,
+                         const float *topk_w, const float *logits, const void *x,
+                         int32_t *offsets,
                          int32_t *perm_src, int32_t *pos, float *importance,
                          double *stats, void *x_perm, void *ws, size_t ws_bytes,
                          hipStream_t stream) {
@@ -317,7 +328,8 @@ moe_status_t moe_permute(const moe_config_t *cfg, const int32_t *topk_idx,
   if (!dev_ok(offsets) || !dev_ok(importance) || !opt_ok(stats))
     return MOE_ERR_INVALID_ARGUMENT;
   if (T > 0 && (!dev_ok(topk_idx) || !dev_ok(topk_w) || !dev_ok(x) ||
-                !dev_ok(perm_src) || !dev_ok(pos) || !dev_ok(x_perm) || !dev_ok(ws)))
+                !dev_ok(perm_src) || !dev_ok(pos) || !dev_ok(x_perm) || !dev_ok(ws) ||
+                (reroutes(cfg) && !dev_ok(logits))))
     return MOE_ERR_INVALID_ARGUMENT;
   const Layout L = layout(cfg);
   if (T > 0 && ws_bytes < L.permute_end) return MOE_ERR_WORKSPACE_TOO_SMALL;
@@ -325,6 +337,17 @@ moe_status_t moe_permute(const moe_config_t *cfg, const int32_t *topk_idx,
   if (T == 0) {
     hipError_t e = moe::launch_fill_i32(offsets, cfg->num_experts + 1, 0, stream);
     if (e != hipSuccess) return MOE_ERR_HIP;
+  }
+  if (T > 0 && reroutes(cfg)) {
+    moe::RerouteScratch r{at<int32_t>(ws, L.pos_a),  at<int32_t>(ws, L.cand),
+                          at<int32_t>(ws, L.pos_b),  at<int32_t>(ws, L.fin),
+                          at<int32_t>(ws, L.off_b),  at<int32_t>(ws, L.full_off_b),
+                          at<float>(ws, L.imp_s)};
+    return hip_status(moe::launch_permute_reroute(
+        topk_idx, topk_w, logits, x, T, cfg->top_k, cfg->num_experts, cfg->capacity,
+        (int)(cfg->d_model * elem_bytes(cfg)), offsets, perm_src, pos, importance, stats,
+        x_perm, at<int32_t>(ws, L.hist), at<int32_t>(ws, L.full_off), at<float>(ws, L.perm_w),
+        r, stream));
   }
   return hip_status(moe::launch_permute(
       topk_idx, topk_w, x, T, cfg->top_k, cfg->num_experts, cfg->capacity,
@@ -452,11 +475,12 @@ moe_status_t moe_forward(const moe_config_t *cfg, const moe_weights_t *w, const 
   void *x_perm = at<char>(ws, L.x_perm);
   void *hidden = at<char>(ws, L.hidden);
   void *y_perm = at<char>(ws, L.y_perm);
-  if ((st = moe_route(cfg, x, w->w_gate, w->b_gate, topk_idx, topk_w, counts, nullptr,
+  float *logits = reroutes(cfg) ? at<float>(ws, L.logits) : nullptr;   // next choices
+  if ((st = moe_route(cfg, x, w->w_gate, w->b_gate, topk_idx, topk_w, counts, logits,
                       stream)) != MOE_OK)
     return st;
-  if ((st = moe_permute(cfg, topk_idx, topk_w, x, offsets, perm_src, pos, importance, stats,
-                        x_perm, ws, L.permute_end, stream)) != MOE_OK)
+  if ((st = moe_permute(cfg, topk_idx, topk_w, logits, x, offsets, perm_src, pos, importance,
+                        stats, x_perm, ws, L.permute_end, stream)) != MOE_OK)
     return st;
   if ((st = moe_expert_up(cfg, w, x_perm, x, offsets, hidden, stream)) != MOE_OK) return st;
   if ((st = moe_expert_down(cfg, w, hidden, offsets, y_perm, stream)) != MOE_OK) return st;

@@ -21,6 +21,7 @@
 // Every sum runs in a fixed order: results are deterministic.
 #include "common.h"
 #include "backward.h"
+#include "permute.h"
 
 #pragma clang fp contract(off)
 
@@ -645,11 +646,6 @@ hipError_t launch_grouped_linear_bf16(const int32_t *offsets, int E, int S, int 
                                       const void *a_shared, const void *w,
                                       const void *w_shared, const void *bias, void *c,
                                       bool w_kn, hipStream_t s);
-hipError_t launch_permute(const int32_t *idx, const float *w, const void *x, int T, int k,
-                          int E, int capacity, int row_bytes, int32_t *offsets,
-                          int32_t *perm_src, int32_t *pos, float *importance, double *stats,
-                          void *x_perm, int32_t *hist, int32_t *full_off, float *perm_w,
-                          hipStream_t s);
 hipError_t launch_wgrad_bf16(const int32_t *poff, int G, int Rp, int M, int N, const void *at,
                              const void *bt, void *out, void *out_last, hipStream_t s);
 

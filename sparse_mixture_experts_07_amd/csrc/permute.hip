@@ -28,6 +28,7 @@
 // rows, pos = -1 for a dropped one); Importance and the statistics keep the
 // router's view (every assignment), through the full group starts.
 #include "common.h"
+#include "permute.h"
 
 namespace moe {
 
@@ -367,6 +368,100 @@ __global__ __launch_bounds__(kFusedThreads) void perm_fused_kernel(
   }
 }
 
+// Next-choice re-routing of the capacity overflow (Go chapter, "Design
+// viewpoints": an overflowing token is dropped or handed to its next
+// candidate), one hop: the o-th overflowing slot of a token (slot order) is
+// offered to its o-th best expert outside its top k (higher score first,
+// ties to the lower index), and each expert accepts offers in flat order
+// into the room the first round left.  Three groupings run in stream order:
+// the drop rule on the top k (which also gives Importance and the
+// statistics, the router's view), the offers (ranks among the offers to each
+// expert), and the final one over the computing expert of every slot.
+
+// One wavefront per token: cand[f] = the expert offered to overflowing slot
+// f, -1 for a kept slot or when the token has no expert left to offer.
+__global__ __launch_bounds__(kWave) void reroute_offer_kernel(
+    const int32_t *__restrict__ idx, const int32_t *__restrict__ pos_a,
+    const float *__restrict__ logits, int k, int E, int32_t *__restrict__ cand) {
+  constexpr int Q = kMaxExperts / kWave;
+  const int t = blockIdx.x;
+  const int lane = threadIdx.x;
+  const int32_t *it = idx + (int64_t)t * k;
+  const int32_t *pa = pos_a + (int64_t)t * k;
+  int32_t *ct = cand + (int64_t)t * k;
+  int nover = 0;
+  for (int j = 0; j < k; ++j) nover += pa[j] < 0;
+  if (nover == 0) {
+    for (int j = lane; j < k; j += kWave) ct[j] = -1;
+    return;
+  }
+  float sc[Q];
+  bool avail[Q];
+#pragma unroll
+  for (int q = 0; q < Q; ++q) {
+    const int e = lane + kWave * q;
+    bool a = e < E;
+    for (int j = 0; j < k && a; ++j) a = it[j] != e;
+    avail[q] = a;
+    sc[q] = a ? logits[(int64_t)t * E + e] : 0.0f;
+  }
+  for (int j = 0; j < k; ++j) {   // uniform over the wavefront
+    if (pa[j] >= 0) {
+      if (lane == 0) ct[j] = -1;
+      continue;
+    }
+    // best available (score descending, index ascending)
+    bool ba = false;
+    float bs = 0.0f;
+    int be = 0x7fffffff;
+#pragma unroll
+    for (int q = 0; q < Q; ++q) {
+      const int e = lane + kWave * q;
+      if (avail[q] && (!ba || sc[q] > bs || (sc[q] == bs && e < be))) {
+        ba = true;
+        bs = sc[q];
+        be = e;
+      }
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+      const bool oa = __shfl_xor((int)ba, off) != 0;
+      const float os = __shfl_xor(bs, off);
+      const int oe = __shfl_xor(be, off);
+      if (oa && (!ba || os > bs || (os == bs && oe < be))) {
+        ba = true;
+        bs = os;
+        be = oe;
+      }
+    }
+    if (lane == 0) ct[j] = ba ? be : -1;
+    if (ba && (be % kWave) == lane) avail[be / kWave] = false;
+  }
+}
+
+// fin[f]: the expert that computes slot f after both rounds, -1 if dropped;
+// pos[f] = -1 (the final grouping writes the computed slots' rows).
+__global__ void reroute_accept_kernel(
+    const int32_t *__restrict__ idx, const int32_t *__restrict__ pos_a,
+    const int32_t *__restrict__ cand, const int32_t *__restrict__ pos_b,
+    const int32_t *__restrict__ kept_a, const int32_t *__restrict__ off_b, int n, int E,
+    int cap, int32_t *__restrict__ fin, int32_t *__restrict__ pos) {
+  const int f = blockIdx.x * blockDim.x + threadIdx.x;
+  if (f >= n) return;
+  int out = -1;
+  if (pos_a[f] >= 0) {
+    out = idx[f];
+  } else {
+    const int e = cand[f];
+    if (static_cast<unsigned>(e) < static_cast<unsigned>(E)) {
+      const int room = cap - (kept_a[e + 1] - kept_a[e]);   // first-round starts
+      if (pos_b[f] - off_b[e] < room) out = e;
+    }
+  }
+  fin[f] = out;
+  pos[f] = -1;
+}
+
 __global__ void zero_f32_kernel(float *p, int n) {
   for (int i = threadIdx.x; i < n; i += blockDim.x) p[i] = 0.0f;
 }
@@ -411,6 +506,34 @@ hipError_t launch_permute(const int32_t *idx, const float *w, const void *x,
         static_cast<const uint4 *>(x), perm_src, offsets + E, n, T, row_bytes / 16,
         static_cast<uint4 *>(x_perm));
   return hipGetLastError();
+}
+
+hipError_t launch_permute_reroute(const int32_t *idx, const float *w, const float *logits,
+                                  const void *x, int T, int k, int E, int capacity,
+                                  int row_bytes, int32_t *offsets, int32_t *perm_src,
+                                  int32_t *pos, float *importance, double *stats,
+                                  void *x_perm, int32_t *hist, int32_t *full_off,
+                                  float *perm_w, const RerouteScratch &r, hipStream_t s) {
+  const int n = T * k;
+  if (n == 0) return launch_zero_stats(importance, E, stats, s);
+  hipError_t err;
+  // 1. the drop rule on the top k: kept slots, Importance, statistics
+  if ((err = launch_permute(idx, w, nullptr, T, k, E, capacity, row_bytes, offsets, perm_src,
+                            r.pos_a, importance, stats, nullptr, hist, full_off, perm_w, s)) !=
+      hipSuccess)
+    return err;
+  // 2. offers, and their ranks within each expert's offers (flat order)
+  reroute_offer_kernel<<<T, kWave, 0, s>>>(idx, r.pos_a, logits, k, E, r.cand);
+  if ((err = launch_permute(r.cand, w, nullptr, T, k, E, 0, row_bytes, r.off_b, perm_src,
+                            r.pos_b, r.imp_s, nullptr, nullptr, hist, r.full_off_b, perm_w,
+                            s)) != hipSuccess)
+    return err;
+  // (offsets still holds the first round's kept group starts here)
+  reroute_accept_kernel<<<(n + 255) / 256, 256, 0, s>>>(idx, r.pos_a, r.cand, r.pos_b, offsets,
+                                                        r.off_b, n, E, capacity, r.fin, pos);
+  // 3. the grouping by computing expert, with the row move
+  return launch_permute(r.fin, w, x, T, k, E, 0, row_bytes, offsets, perm_src, pos, r.imp_s,
+                        nullptr, x_perm, hist, r.full_off_b, perm_w, s);
 }
 
 }  // namespace moe

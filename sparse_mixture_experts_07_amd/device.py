@@ -45,9 +45,11 @@ class DeviceLayer:
     w_down_shared: Optional[torch.Tensor]
 
     @classmethod
-    def upload(cls, layer, device="cuda", capacity: int = 0) -> "DeviceLayer":
-        """capacity: per-expert limit on kept assignments (0: no limit)."""
-        return cls(B.config_of(layer.cfg, capacity), to_device(layer.x, device),
+    def upload(cls, layer, device="cuda", capacity: int = 0,
+               overflow: int = 0) -> "DeviceLayer":
+        """capacity: per-expert limit on kept assignments (0: no limit);
+        overflow: what happens beyond it (0 drop, 1 next choice)."""
+        return cls(B.config_of(layer.cfg, capacity, overflow), to_device(layer.x, device),
                    to_device(layer.w_gate, device), to_device(layer.b_gate, device),
                    to_device(layer.w_up, device), to_device(layer.w_down, device),
                    to_device(layer.b_up, device), to_device(layer.b_down, device),

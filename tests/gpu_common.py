@@ -28,9 +28,9 @@ def to_f64(t: torch.Tensor) -> np.ndarray:
     return t.detach().cpu().numpy().astype(np.float64)
 
 
-def run_forward(layer, capacity: int = 0):
+def run_forward(layer, capacity: int = 0, overflow: int = 0):
     """moe_forward on the layer; host copies of every output."""
-    dl = DeviceLayer.upload(layer, capacity=capacity)
+    dl = DeviceLayer.upload(layer, capacity=capacity, overflow=overflow)
     fw = Forward(dl)
     fw()
     torch.cuda.synchronize()
@@ -57,10 +57,11 @@ def check_routing(layer, idx, w, counts, t0=0):
     return ridx, rw
 
 
-def check_outputs(layer, y, tokens, tol=None, keep=None):
-    """keep: the oracle's capacity mask (dropped slots add nothing)."""
+def check_outputs(layer, y, tokens, tol=None, keep=None, assign=None):
+    """keep: the oracle's capacity mask (dropped slots add nothing); assign:
+    the oracle's computing expert of every slot (next-choice re-routing)."""
     tokens = np.asarray(tokens, np.int64)
-    ref, _, _ = oracle.forward_tokens(layer, tokens, keep=keep)
+    ref, _, _ = oracle.forward_tokens(layer, tokens, keep=keep, assign=assign)
     got = y[tokens]
     assert np.all(np.isfinite(got))
     tol = tol or (BF16_TOL if layer.cfg.dtype == 1 else F32_TOL)

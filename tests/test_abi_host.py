@@ -27,7 +27,7 @@ def test_library_exports_every_declared_entry_point():
     assert set(B.EXPORTS) == set(names), names
     for n in names:
         assert hasattr(lib, n), f"libmoe.so does not export {n}"
-    assert B.moe_abi_version() == 5
+    assert B.moe_abi_version() == 6
 
 
 def test_status_strings():
@@ -80,17 +80,20 @@ BAD_CFGS = {
     "capacity_negative": (dict(capacity=-1), B.MOE_ERR_INVALID_ARGUMENT),
     "gate_negative": (dict(gate=-1), B.MOE_ERR_INVALID_ARGUMENT),
     "gate_3": (dict(gate=3), B.MOE_ERR_INVALID_ARGUMENT),
+    "overflow_negative": (dict(overflow=-1), B.MOE_ERR_INVALID_ARGUMENT),
+    "overflow_2": (dict(overflow=2), B.MOE_ERR_INVALID_ARGUMENT),
 }
 
 FAKE = 1 << 20   # aligned non-null stand-in pointer; never dereferenced
 
 
 def _cfg(**kw):
-    base = dict(T=64, d=64, h=256, E=8, k=2, act=0, dtype=0, S=0, capacity=0, gate=0)
+    base = dict(T=64, d=64, h=256, E=8, k=2, act=0, dtype=0, S=0, capacity=0, gate=0,
+                overflow=0)
     base.update(kw)
     return B.config(base["T"], base["d"], base["h"], base["E"], base["k"],
                     base["act"], base["dtype"], base["S"], base["capacity"],
-                    base["gate"])
+                    base["gate"], base["overflow"])
 
 
 @pytest.mark.parametrize("name", list(BAD_CFGS))
@@ -103,7 +106,8 @@ def test_every_entry_point_rejects_bad_config(name):
     calls = [
         L.moe_workspace_bytes(r, C.byref(C.c_size_t())),
         L.moe_route(r, FAKE, FAKE, None, FAKE, FAKE, FAKE, None, None),
-        L.moe_permute(r, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, 1 << 40, None),
+        L.moe_permute(r, FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, 1 << 40,
+                      None),
         L.moe_expert_up(r, C.byref(w), FAKE, FAKE, FAKE, FAKE, None),
         L.moe_expert_down(r, C.byref(w), FAKE, FAKE, FAKE, None),
         L.moe_expert_ffn(r, C.byref(w), FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 40, None),
@@ -141,7 +145,15 @@ def test_pointer_and_workspace_checks():
     small = B.MOE_ERR_WORKSPACE_TOO_SMALL
     w = B.MoeWeights(FAKE, None, FAKE, None, FAKE, None, None, None)
     assert L.moe_forward(r, C.byref(w), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, 1024, None) == small
-    assert L.moe_permute(r, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, 16, None) == small
+    assert L.moe_permute(r, FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, 16,
+                         None) == small
+    # next-choice re-routing reads the router scores, and needs more scratch
+    rr = _cfg(capacity=20, overflow=1)
+    assert L.moe_permute(C.byref(rr), FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE,
+                         FAKE, 1 << 40, None) == inv
+    n_drop = B.moe_workspace_bytes(_cfg(capacity=20))
+    assert B.moe_workspace_bytes(rr) > n_drop
+    assert B.moe_workspace_bytes(_cfg(overflow=1)) == B.moe_workspace_bytes(_cfg())
     assert L.moe_expert_ffn(r, C.byref(w), FAKE, FAKE, FAKE, FAKE, FAKE, 16, None) == small
     assert L.moe_load_stats(None, None, 4, None, None, None) == inv
 

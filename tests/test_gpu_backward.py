@@ -25,10 +25,10 @@ def _gpu():
     require_gpu()
 
 
-def forward_saved(L, capacity=0, train=False):
+def forward_saved(L, capacity=0, train=False, overflow=0):
     """The stage entry points; every tensor the backward pass takes (train:
     the up projection that also stores the pre-activations)."""
-    dl = DeviceLayer.upload(L, capacity=capacity)
+    dl = DeviceLayer.upload(L, capacity=capacity, overflow=overflow)
     c, dev = dl.cfg, dl.x.device
     T, k, E, d = L.cfg.T, L.cfg.k, L.cfg.E, L.cfg.d
     R = B.moe_grouped_rows(c)
@@ -43,12 +43,13 @@ def forward_saved(L, capacity=0, train=False):
              y_perm=torch.empty((R, d), dtype=torch.bfloat16, device=dev),
              y=torch.empty((T, d), dtype=torch.bfloat16, device=dev))
     ws = torch.empty(max(B.moe_workspace_bytes(c), 256), dtype=torch.uint8, device=dev)
-    # the softmax-all gate's backward reads the router scores
-    if L.cfg.gate == synthetic.GATE_SOFTMAX_ALL:
+    # the softmax-all gate's backward and next-choice re-routing read the
+    # router scores
+    if L.cfg.gate == synthetic.GATE_SOFTMAX_ALL or (capacity and overflow):
         s["logits"] = torch.empty((T, E), dtype=torch.float32, device=dev)
     B.moe_route(c, dl.x, dl.w_gate, dl.b_gate, s["idx"], s["w"], s["counts"], s.get("logits"))
     B.moe_permute(c, s["idx"], s["w"], dl.x, s["offsets"], s["perm_src"], s["pos"], s["imp"],
-                  None, s["x_perm"], ws)
+                  None, s["x_perm"], ws, logits=s.get("logits"))
     if train:
         nup = 2 * L.cfg.h if L.cfg.act == SWIGLU else L.cfg.h
         s["hidden"] = torch.empty((R, L.cfg.h), dtype=torch.bfloat16, device=dev)
@@ -62,8 +63,8 @@ def forward_saved(L, capacity=0, train=False):
     return dl, s
 
 
-def run_backward(L, dy_bits, capacity=0, imp_w=0.0, train=False):
-    dl, s = forward_saved(L, capacity, train)
+def run_backward(L, dy_bits, capacity=0, imp_w=0.0, train=False, overflow=0):
+    dl, s = forward_saved(L, capacity, train, overflow)
     c, dev = dl.cfg, dl.x.device
     cfg = L.cfg
     E, d, h, S = cfg.E, cfg.d, cfg.h, cfg.S
@@ -90,14 +91,19 @@ def run_backward(L, dy_bits, capacity=0, imp_w=0.0, train=False):
     return out, s, (dl, mg, ws, dy)
 
 
-def check_backward(L, capacity=0, imp_w=0.0, seed=0, train=False):
+def check_backward(L, capacity=0, imp_w=0.0, seed=0, train=False, overflow=0):
     rng = np.random.default_rng(seed)
     dy_bits = f32_to_bf16_bits(rng.standard_normal((L.cfg.T, L.cfg.d)).astype(np.float32))
-    got, s, _ = run_backward(L, dy_bits, capacity, imp_w, train)
-    ridx, _, _ = oracle.route(L)
+    got, s, _ = run_backward(L, dy_bits, capacity, imp_w, train, overflow)
+    ridx, _, sc = oracle.route(L, want_scores=True)
     assert np.array_equal(s["idx"].cpu().numpy(), ridx)
-    keep = oracle.capacity_keep(L.cfg, ridx, capacity) if capacity else None
-    ref = oracle.backward.backward(L, bf16_bits_to_f32(dy_bits), keep, imp_w, idx=ridx)
+    keep = assign = None
+    if capacity and overflow:
+        assign = oracle.capacity_reroute(L.cfg, ridx, sc, capacity)
+    elif capacity:
+        keep = oracle.capacity_keep(L.cfg, ridx, capacity)
+    ref = oracle.backward.backward(L, bf16_bits_to_f32(dy_bits), keep, imp_w, idx=ridx,
+                                   assign=assign)
     errs = {}
     for n, r in ref.items():
         gv = got.get(n)
@@ -219,6 +225,18 @@ def test_backward_softmax_all_needs_logits():
     with pytest.raises(RuntimeError, match="invalid"):
         B.moe_backward(c, dl.weights(), dl.x, to_device(dy, dev), s["idx"], s["w"],
                        s["offsets"], s["pos"], s["x_perm"], s["y_perm"], None, 0.0, mg, ws)
+
+
+@pytest.mark.parametrize("train", [False, True])
+def test_backward_with_rerouting(train):
+    """Next-choice re-routing: a re-routed slot's gradient reaches the expert
+    that computed it; the router's gradient still flows through the top-k
+    gate values."""
+    L = random_layer(67, wstd=0.15, T=400, d=64, h=128, E=6, k=2, act=SWIGLU, dtype=BF16,
+                     bias=True, S=1)
+    L.b_gate = np.linspace(1.5, 0.0, 6).astype(np.float32)
+    errs = check_backward(L, 140, 0.2, train=train, overflow=B.MOE_OVERFLOW_NEXT_CHOICE)
+    print({n: f"{e:.2e}" for n, e in errs.items()})
 
 
 def test_backward_is_deterministic():
