@@ -104,7 +104,7 @@ size_t elem_bytes(const moe_config_t *c) { return c->dtype == MOE_DTYPE_BF16 ? 2
 // Workspace regions, each 256-byte aligned, in this order.
 struct Layout {
   size_t hist, full_off, perm_w;                        // moe_permute scratch
-  size_t pos_a, cand, pos_b, fin, off_b, full_off_b, imp_s, permute_end;  // re-routing
+  size_t pos_a, cand, pos_b, fin, off_b, full_off_b, permute_end;  // re-routing
   size_t offsets, perm_src, pos, logits, x_perm, hidden, y_perm, total;  // moe_forward
 };
 
@@ -129,7 +129,6 @@ Layout layout(const moe_config_t *c) {
   L.fin = o;         o += align_up(sizeof(int32_t) * rn);
   L.off_b = o;       o += align_up(sizeof(int32_t) * (re ? re + 1 : 0));
   L.full_off_b = o;  o += align_up(sizeof(int32_t) * (re ? re + 1 : 0));
-  L.imp_s = o;       o += align_up(sizeof(float) * re);
   L.permute_end = o;
   L.offsets = o;   o += align_up(sizeof(int32_t) * (size_t)(E + 1));
   L.perm_src = o;  o += align_up(sizeof(int32_t) * (size_t)n);
@@ -164,7 +163,7 @@ void clear_pending_error() { (void)hipGetLastError(); }
 // Backward workspace regions, each 256-byte aligned, in this order.
 struct BwdLayout {
   size_t gimp, ds, dsp, ds_cols, poff, colsrc;
-  size_t off_all, src_all, pos_all, hist, full_off, perm_w, imp_all;
+  size_t off_all, src_all, pos_all, hist, full_off, perm_w;
   size_t A, H, dyp, dH, dA, dxp, dypT, HT, dAT, xpT;
   size_t tm, dS, dxr, dpart, total;
 };
@@ -194,7 +193,6 @@ BwdLayout bwd_layout(const moe_config_t *c) {
   take(L.hist, cap ? 4 * (int64_t)moe::perm_num_segments(T * k) * E : 0);
   take(L.full_off, cap ? 4 * (E + 1) : 0);
   take(L.perm_w, cap ? 4 * T * k : 0);
-  take(L.imp_all, cap ? 4 * E : 0);
   take(L.A, 2 * R * nup);
   take(L.H, 2 * R * h);
   take(L.dyp, 2 * R * d);
@@ -341,8 +339,7 @@ moe_status_t moe_permute(const moe_config_t *cfg, const int32_t *topk_idx,
   if (T > 0 && reroutes(cfg)) {
     moe::RerouteScratch r{at<int32_t>(ws, L.pos_a),  at<int32_t>(ws, L.cand),
                           at<int32_t>(ws, L.pos_b),  at<int32_t>(ws, L.fin),
-                          at<int32_t>(ws, L.off_b),  at<int32_t>(ws, L.full_off_b),
-                          at<float>(ws, L.imp_s)};
+                          at<int32_t>(ws, L.off_b),  at<int32_t>(ws, L.full_off_b)};
     return hip_status(moe::launch_permute_reroute(
         topk_idx, topk_w, logits, x, T, cfg->top_k, cfg->num_experts, cfg->capacity,
         (int)(cfg->d_model * elem_bytes(cfg)), offsets, perm_src, pos, importance, stats,
@@ -594,7 +591,6 @@ moe_status_t moe_backward(const moe_config_t *cfg, const moe_weights_t *w, const
     b.hist = at<int32_t>(ws, L.hist);
     b.full_off = at<int32_t>(ws, L.full_off);
     b.perm_w = at<float>(ws, L.perm_w);
-    b.imp_all = at<float>(ws, L.imp_all);
   }
   b.A = at<uint16_t>(ws, L.A);
   b.H = at<uint16_t>(ws, L.H);

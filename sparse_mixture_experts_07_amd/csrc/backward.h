@@ -15,7 +15,7 @@ struct BwdBuffers {
   int32_t *poff, *colsrc;
   // regrouping of every assignment (router gradient under a capacity)
   int32_t *off_all, *src_all, *pos_all, *hist, *full_off;
-  float *perm_w, *imp_all;
+  float *perm_w;
   uint16_t *A, *H, *dyp, *dH, *dA, *dxp;
   uint16_t *dypT, *HT, *dAT, *xpT;
   // softmax-all gate: per-token m [T], dense score gradients [T, E], the

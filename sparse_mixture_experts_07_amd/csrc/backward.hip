@@ -794,7 +794,7 @@ hipError_t launch_backward(const BwdArgs &a, const BwdBuffers &b, hipStream_t s)
   const int32_t *pos_r = a.pos, *poff_r = b.poff, *colsrc_r = b.colsrc;
   if (a.capacity > 0) {
     MOE_TRY(launch_permute(a.idx, a.topk_w, a.x, T, k, E, 0, d * 2, b.off_all, b.src_all,
-                           b.pos_all, b.imp_all, nullptr, nullptr, b.hist, b.full_off,
+                           b.pos_all, nullptr, nullptr, nullptr, b.hist, b.full_off,
                            b.perm_w, s));
     bwd_layout_kernel<<<1, kBwdThreads, 0, s>>>(b.off_all, E, 0, T, routed, b.poff);
     bwd_colsrc_kernel<<<grid_for(Rp, kBwdThreads), kBwdThreads, 0, s>>>(

@@ -11,7 +11,8 @@ int perm_num_segments(int64_t n);
 
 // Stable grouping of the T*k assignments idx (ids outside [0, E) are left
 // out), an expert keeping its first `capacity` (0: all) in flat order; then
-// the row move into x_perm (skipped when x_perm is NULL).  hist [nseg * E],
+// the row move into x_perm (skipped when x_perm is NULL).  importance NULL:
+// no Importance and no statistics.  hist [nseg * E],
 // full_off [E + 1] and perm_w [T*k] are scratch.
 hipError_t launch_permute(const int32_t *idx, const float *w, const void *x, int T, int k,
                           int E, int capacity, int row_bytes, int32_t *offsets,
@@ -20,10 +21,9 @@ hipError_t launch_permute(const int32_t *idx, const float *w, const void *x, int
                           hipStream_t s);
 
 // Scratch of the next-choice re-routing: T*k int32 each for pos_a, cand,
-// pos_b and fin; E + 1 int32 each for off_b and full_off_b; E fp32 imp_s.
+// pos_b and fin; E + 1 int32 each for off_b and full_off_b.
 struct RerouteScratch {
   int32_t *pos_a, *cand, *pos_b, *fin, *off_b, *full_off_b;
-  float *imp_s;
 };
 
 // launch_permute under a capacity with the overflow re-routed one hop to the

@@ -329,7 +329,7 @@ __global__ __launch_bounds__(kFusedThreads) void perm_fused_kernel(
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) sum += __shfl_xor(sum, o);
     if (lane == 0) {
-      importance[x] = sum;
+      if (importance) importance[x] = sum;
       imp[x] = sum;
     }
   }
@@ -470,7 +470,7 @@ __global__ void zero_stats_kernel(double *p) {
 }
 
 hipError_t launch_zero_stats(float *importance, int E, double *stats, hipStream_t s) {
-  zero_f32_kernel<<<1, 256, 0, s>>>(importance, E);
+  if (importance) zero_f32_kernel<<<1, 256, 0, s>>>(importance, E);
   if (stats) zero_stats_kernel<<<1, 64, 0, s>>>(stats);
   return hipGetLastError();
 }
@@ -497,9 +497,11 @@ hipError_t launch_permute(const int32_t *idx, const float *w, const void *x,
     perm_scan_kernel<<<1, kPermThreads, 0, s>>>(hist, nseg, E, n, cap, full_off, offsets);
     perm_scatter_kernel<<<nseg, kPermThreads, 0, s>>>(idx, w, n, k, E, cap, hist, full_off,
                                                       offsets, pos, perm_src, perm_w);
-    perm_importance_kernel<<<(E + 3) / 4, kPermThreads, 0, s>>>(full_off, perm_w, E,
-                                                                importance);
-    if (stats) perm_stats_kernel<<<1, kWave, 0, s>>>(full_off, importance, E, stats);
+    if (importance) {   // NULL: grouping only
+      perm_importance_kernel<<<(E + 3) / 4, kPermThreads, 0, s>>>(full_off, perm_w, E,
+                                                                  importance);
+      if (stats) perm_stats_kernel<<<1, kWave, 0, s>>>(full_off, importance, E, stats);
+    }
   }
   if (x_perm)   // NULL: grouping only (the backward pass regroups every assignment)
     perm_move_kernel<<<blocks, kPermThreads, 0, s>>>(
@@ -525,14 +527,14 @@ hipError_t launch_permute_reroute(const int32_t *idx, const float *w, const floa
   // 2. offers, and their ranks within each expert's offers (flat order)
   reroute_offer_kernel<<<T, kWave, 0, s>>>(idx, r.pos_a, logits, k, E, r.cand);
   if ((err = launch_permute(r.cand, w, nullptr, T, k, E, 0, row_bytes, r.off_b, perm_src,
-                            r.pos_b, r.imp_s, nullptr, nullptr, hist, r.full_off_b, perm_w,
+                            r.pos_b, nullptr, nullptr, nullptr, hist, r.full_off_b, perm_w,
                             s)) != hipSuccess)
     return err;
   // (offsets still holds the first round's kept group starts here)
   reroute_accept_kernel<<<(n + 255) / 256, 256, 0, s>>>(idx, r.pos_a, r.cand, r.pos_b, offsets,
                                                         r.off_b, n, E, capacity, r.fin, pos);
   // 3. the grouping by computing expert, with the row move
-  return launch_permute(r.fin, w, x, T, k, E, 0, row_bytes, offsets, perm_src, pos, r.imp_s,
+  return launch_permute(r.fin, w, x, T, k, E, 0, row_bytes, offsets, perm_src, pos, nullptr,
                         nullptr, x_perm, hist, r.full_off_b, perm_w, s);
 }
 
