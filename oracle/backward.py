@@ -12,7 +12,7 @@ summary, section "Sparsely-Gated MoE layer formula", with the gate of
     G    = softmax over the kept k of s = x W_g^T + b (the default gate; the
            bias-selects gate takes the softmax of x W_g^T over the kept k,
            the softmax-all gate the softmax over all E read at the kept k)
-    loss = <dy, y> + w_imp * CV(Importance)^2
+    loss = <dy, y> + w_imp * CV(Importance)^2 (+ w_load * CV(Load)^2)
 
 where the kept experts i_j are the oracle's float32 top-k selection, held
 fixed (the selection is a step function: its derivative is zero wherever it
@@ -25,6 +25,14 @@ slots contribute nothing to y (their gate still counts in Importance, the
 router's view).  Expert FFNs: Linear -> exact GELU -> Linear with biases,
 or SwiGLU silu(x W1^T) * (x W3^T) -> W2 with W1 and W3 packed as [2h, d]
 ("Understanding MoE in Transformers", "Weight Loading Refactor").
+
+The noisy gate (Qiita summary, "Gating: Noisy Top-k Softmax", training
+form): H = s + n * Softplus(x W_noise^T) with the draws n given; G = the
+softmax of H over the kept k; the smooth Load_i = sum over tokens of
+Phi((s_i - kth_i) / Softplus_i), kth_i the k-th largest H without entry i
+(Shazeer et al.'s estimator, "Load-balancing losses").  The kept experts
+and the entry behind each kth_i come from the C oracle's float32 order of
+H and are held fixed, like the selection.
 Everything is evaluated in float64 from the exact values of the stored
 float32 / bfloat16 numbers; torch.autograd does the differentiation.
 """
@@ -36,9 +44,10 @@ import numpy as np
 import torch
 
 from . import route as _route
+from . import route_noisy as _route_noisy
 
 NAMES = ("x", "w_gate", "b_gate", "w_up", "w_down", "b_up", "b_down",
-         "w_up_shared", "w_down_shared")
+         "w_up_shared", "w_down_shared", "w_noise")
 
 
 def _f64(a) -> Optional[torch.Tensor]:
@@ -95,12 +104,36 @@ def preactivations(layer, e: int, xrows: np.ndarray) -> np.ndarray:
     return a.numpy()
 
 
+def noisy_selection(layer, noise: np.ndarray):
+    """The C oracle's float32 noisy selection: (idx [T, k], kth [T, E] or
+    None when k = E), kth[t, e] the entry of H behind the threshold of e: the
+    (k+1)-th of the stable descending order when e is kept, else the k-th."""
+    cfg = layer.cfg
+    r = _route_noisy(layer, noise)
+    order = np.argsort(-r["h"].astype(np.float64), axis=1, kind="stable")
+    assert np.array_equal(order[:, : cfg.k], r["idx"])
+    if cfg.k == cfg.E:
+        return r["idx"], None
+    kept = np.zeros((cfg.T, cfg.E), bool)
+    np.put_along_axis(kept, r["idx"].astype(np.int64), True, axis=1)
+    kth = np.where(kept, order[:, cfg.k : cfg.k + 1], order[:, cfg.k - 1 : cfg.k])
+    return r["idx"], kth
+
+
+def _noisy_scores(p: dict, s: torch.Tensor, noise: torch.Tensor):
+    """(H, Softplus of the noise scores) in float64."""
+    u = p["x"] @ p["w_noise"].T
+    sig = torch.nn.functional.softplus(u, beta=1.0, threshold=50.0)
+    return s + noise * sig, sig
+
+
 def forward(layer, p: dict, idx: np.ndarray, keep: Optional[np.ndarray] = None,
-            assign: Optional[np.ndarray] = None):
-    """(y [T, d], gate values [T, k], Importance [E]) as float64 tensors for
-    the fixed selection idx [T, k]; assign [T*k] (next-choice re-routing):
-    the expert that computes each slot, -1 dropped, the gate values still
-    those of idx."""
+            assign: Optional[np.ndarray] = None, noisy: Optional[dict] = None):
+    """(y [T, d], gate values [T, k], Importance [E], Load [E] or None) as
+    float64 tensors for the fixed selection idx [T, k]; assign [T*k]
+    (next-choice re-routing): the expert that computes each slot, -1
+    dropped, the gate values still those of idx; noisy: dict(noise [T, E],
+    kth [T, E] or None) for the noisy gate."""
     cfg = layer.cfg
     T, k, E = cfg.T, cfg.k, cfg.E
     x = p["x"]
@@ -108,7 +141,18 @@ def forward(layer, p: dict, idx: np.ndarray, keep: Optional[np.ndarray] = None,
     s = raw + p["b_gate"] if "b_gate" in p else raw
     it = torch.from_numpy(np.ascontiguousarray(idx, np.int64))
     gate = getattr(cfg, "gate", 0)
-    if gate == 1:     # the bias steers the selection only
+    load = None
+    if noisy is not None:   # softmax over the kept noisy scores; smooth Load
+        H, sig = _noisy_scores(p, s, _f64(noisy["noise"]))
+        g = torch.softmax(torch.gather(H, 1, it), dim=1)
+        if noisy["kth"] is None:   # k = E: every P is 1
+            load = torch.full((E,), float(T), dtype=torch.float64)
+        else:
+            thr = torch.gather(H, 1, torch.from_numpy(np.ascontiguousarray(noisy["kth"],
+                                                                           np.int64)))
+            z = (s - thr) / sig
+            load = (0.5 * torch.special.erfc(-z / np.sqrt(2.0))).sum(0)
+    elif gate == 1:   # the bias steers the selection only
         g = torch.softmax(torch.gather(raw, 1, it), dim=1)
     elif gate == 2:   # softmax over all E, read at the kept experts
         g = torch.gather(torch.softmax(s, dim=1), 1, it)
@@ -129,7 +173,7 @@ def forward(layer, p: dict, idx: np.ndarray, keep: Optional[np.ndarray] = None,
     if cfg.S:
         y = y + _ffn(cfg, p, E, x)
     imp = torch.zeros(E, dtype=torch.float64).index_add(0, it.reshape(-1), g.reshape(-1))
-    return y, g, imp
+    return y, g, imp, load
 
 
 def cv2(v: torch.Tensor) -> torch.Tensor:
@@ -140,25 +184,33 @@ def cv2(v: torch.Tensor) -> torch.Tensor:
 
 
 def loss(layer, p: dict, idx, dy: torch.Tensor, keep=None, importance_weight: float = 0.0,
-         assign=None):
-    y, _, imp = forward(layer, p, idx, keep, assign)
+         assign=None, noisy=None, load_weight: float = 0.0):
+    y, _, imp, load = forward(layer, p, idx, keep, assign, noisy)
     L = (dy * y).sum()
     if importance_weight:
         L = L + importance_weight * cv2(imp)
+    if load_weight and load is not None:
+        L = L + load_weight * cv2(load)
     return L
 
 
 def backward(layer, dy: np.ndarray, keep: Optional[np.ndarray] = None,
              importance_weight: float = 0.0, idx: Optional[np.ndarray] = None,
-             assign: Optional[np.ndarray] = None) -> dict:
+             assign: Optional[np.ndarray] = None, noise: Optional[np.ndarray] = None,
+             load_weight: float = 0.0) -> dict:
     """Gradients (float64 numpy, keyed by the array names, 'x' included) of
     <dy, y> + importance_weight * CV^2(Importance) with the oracle's routing
     (or the given selection idx; assign: the computing expert of each slot
-    under next-choice re-routing)."""
-    if idx is None:
+    under next-choice re-routing).  noise [T, E]: the noisy gate with these
+    draws (its selection from the C oracle), plus load_weight * CV^2(Load)."""
+    noisy = None
+    if noise is not None:
+        idx, kth = noisy_selection(layer, noise)
+        noisy = dict(noise=np.asarray(noise, np.float32), kth=kth)
+    elif idx is None:
         idx, _, _ = _route(layer)
     p = params(layer)
-    L = loss(layer, p, idx, _f64(dy), keep, importance_weight, assign)
+    L = loss(layer, p, idx, _f64(dy), keep, importance_weight, assign, noisy, load_weight)
     names = list(p)
     grads = torch.autograd.grad(L, [p[n] for n in names], allow_unused=True)
     return {n: (np.zeros(tuple(p[n].shape)) if g is None else g.numpy())

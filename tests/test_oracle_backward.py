@@ -26,7 +26,7 @@ def test_forward_matches_the_c_oracle(act, S, eb):
     L = _layer(1, act, S, expert_bias=eb, T=30, d=16, h=12, E=5, k=2)
     idx, _, _ = oracle.route(L)
     p = B.params(L)
-    y, g, imp = B.forward(L, p, idx)
+    y, g, imp, _ = B.forward(L, p, idx)
     yc, _, wc = oracle.forward_tokens(L, range(30))
     np.testing.assert_allclose(y.detach().numpy(), yc, rtol=1e-6, atol=1e-7 * np.abs(yc).max())
     np.testing.assert_allclose(g.detach().numpy(), wc, rtol=1e-6)
@@ -34,7 +34,7 @@ def test_forward_matches_the_c_oracle(act, S, eb):
     np.testing.assert_allclose(imp.detach().numpy(), rimp, rtol=1e-6)
     keep = oracle.capacity_keep(L.cfg, idx, 8)
     assert 0 < keep.sum() < keep.size
-    yk, _, _ = B.forward(L, p, idx, keep)
+    yk, _, _, _ = B.forward(L, p, idx, keep)
     yck, _, _ = oracle.forward_tokens(L, range(30), keep=keep)
     np.testing.assert_allclose(yk.detach().numpy(), yck, rtol=1e-6, atol=1e-7 * np.abs(yck).max())
 
@@ -101,7 +101,7 @@ def test_gate_modes_forward_and_gradients(gate):
     L = random_layer(9, T=7, d=6, h=5, E=5, k=2, act=SWIGLU, bias=True, gate=gate)
     idx, _, _ = oracle.route(L)
     p = B.params(L)
-    y, g, _ = B.forward(L, p, idx)
+    y, g, _, _ = B.forward(L, p, idx)
     yc, _, wc = oracle.forward_tokens(L, range(7))
     np.testing.assert_allclose(y.detach().numpy(), yc, rtol=1e-6, atol=1e-7 * np.abs(yc).max())
     np.testing.assert_allclose(g.detach().numpy(), wc, rtol=1e-6)
@@ -130,7 +130,7 @@ def test_rerouted_forward_and_gradients():
     keep = oracle.capacity_keep(L.cfg, idx, 4)
     assert ((keep == 0) & (assign >= 0)).any()
     p = B.params(L)
-    y, _, _ = B.forward(L, p, idx, assign=assign)
+    y, _, _, _ = B.forward(L, p, idx, assign=assign)
     yc, _, _ = oracle.forward_tokens(L, range(12), assign=assign)
     np.testing.assert_allclose(y.detach().numpy(), yc, rtol=1e-6, atol=1e-7 * np.abs(yc).max())
     dy = torch.from_numpy(np.random.default_rng(12).standard_normal((12, 6)))
@@ -145,3 +145,59 @@ def test_rerouted_forward_and_gradients():
         if not (assign == e).any():
             assert np.all(g["w_up"][e] == 0) and np.all(g["w_down"][e] == 0)
     assert np.abs(g["w_gate"]).max() > 0
+
+
+def _noisy_layer(seed, T=9, d=6, h=5, E=5, k=2, S=0):
+    L = random_layer(seed, T=T, d=d, h=h, E=E, k=k, act=SWIGLU, bias=True, S=S)
+    rng = np.random.default_rng(seed + 100)
+    L.w_noise = (rng.standard_normal((E, d)) * 0.4).astype(np.float32)
+    noise = rng.standard_normal((T, E)).astype(np.float32)
+    return L, noise
+
+
+def test_noisy_forward_matches_the_c_oracle():
+    """The torch noisy forward: gate values, and the smooth Load equal to
+    the sum over tokens of the C oracle's P(x, i)."""
+    L, noise = _noisy_layer(40, T=30, E=6, k=2)
+    idx, kth = B.noisy_selection(L, noise)
+    r = oracle.route_noisy(L, noise)
+    p = B.params(L)
+    _, g, _, load = B.forward(L, p, idx, noisy=dict(noise=noise, kth=kth))
+    np.testing.assert_allclose(g.detach().numpy(), r["w"], rtol=1e-6)
+    np.testing.assert_allclose(load.detach().numpy(), r["p"].sum(0), rtol=1e-6)
+
+
+@pytest.mark.parametrize("k,E,S,imp_w,load_w", [(2, 5, 0, 0.0, 0.6), (2, 5, 1, 0.3, 0.4),
+                                                (1, 4, 0, 0.2, 1.0), (3, 3, 0, 0.0, 0.5)])
+def test_noisy_gradients_match_finite_differences(k, E, S, imp_w, load_w):
+    """gradcheck of <dy, y> + w_imp CV^2(Importance) + w_load CV^2(Load)
+    for the noisy gate, every input including W_noise (k = E: the Load is
+    constant)."""
+    L, noise = _noisy_layer(41 + k + E, E=E, k=k, S=S)
+    idx, kth = B.noisy_selection(L, noise)
+    noisy = dict(noise=noise, kth=kth)
+    dy = torch.from_numpy(np.random.default_rng(5).standard_normal((L.cfg.T, L.cfg.d)))
+    p = B.params(L)
+    names = list(p)
+
+    def f(*ts):
+        return B.loss(L, dict(zip(names, ts)), idx, dy, None, imp_w, None, noisy, load_w)
+
+    assert torch.autograd.gradcheck(f, tuple(p[n] for n in names), eps=1e-6, atol=1e-6, rtol=1e-5)
+
+
+def test_noise_free_noisy_gate_is_the_clean_gate():
+    """Zero draws: H = s, so the selection, the output gradients and the
+    router's are the clean gate's, and W_noise gets no gradient from y (only
+    the Load term reaches it, through the Softplus scales)."""
+    L, noise = _noisy_layer(45, T=12, E=5, k=2)
+    zero = np.zeros_like(noise)
+    dy = np.random.default_rng(6).standard_normal((12, 6))
+    gn = B.backward(L, dy, importance_weight=0.3, noise=zero, load_weight=0.0)
+    gc = B.backward(L, dy, importance_weight=0.3)
+    for n in gc:
+        if n != "w_noise":
+            np.testing.assert_allclose(gn[n], gc[n], rtol=1e-12, atol=1e-14)
+    assert np.all(gn["w_noise"] == 0) and np.all(gc["w_noise"] == 0)
+    gl = B.backward(L, dy, importance_weight=0.3, noise=zero, load_weight=0.5)
+    assert np.abs(gl["w_noise"]).max() > 0
