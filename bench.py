@@ -23,6 +23,8 @@ if ROOT not in sys.path:
 
 PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+IMPORTANCE_LOSS_WEIGHT = 0.01   # training step: w * CV^2(Importance)
+LOAD_LOSS_WEIGHT = 0.01         # training step with the noisy gate: w * CV^2(smooth Load)
 METRIC = "MoE layer tokens/s + grouped-GEMM TFLOP/s (% MFMA peak); decode HBM GB/s"
 
 
@@ -94,8 +96,6 @@ def main():
     cfg = synthetic.BY_NAME[args.workload].with_(gate=GATES[args.gate])
     if args.noisy and cfg.gate != 0:
         sys.exit("--noisy takes the default gate only")
-    if args.noisy and args.backward:
-        sys.exit("--noisy --backward: the noisy gate has no backward pass here")
     t_gen = time.time()
     L = synthetic.make_inputs(cfg)
     if args.noisy:
@@ -167,6 +167,11 @@ def main():
             device=dev, dtype=dt)
         preact = torch.empty((R, cfg.n_up), dtype=dt, device=dev)
         bwd_evs = []
+        nz = None
+        if args.noisy:   # the noisy gate's share: W_noise and the smooth-Load loss
+            g_t["w_noise"] = torch.empty((E, d), **f32)
+            nz = B.noisy_grad(w_noise, noise, clean, nscale, g_t["w_noise"], nload,
+                              LOAD_LOSS_WEIGHT)
 
     def step(ev=None):
         route()
@@ -187,8 +192,9 @@ def main():
                 bwd_evs.append((torch.cuda.Event(enable_timing=True),
                                 torch.cuda.Event(enable_timing=True)))
                 bwd_evs[-1][0].record()
-            B.moe_backward(c, W, dl.x, dy, idx, tw, offsets, pos, x_perm, y_perm, imp, 0.01,
-                           grads, ws_b, hidden=hidden, preact=preact, logits=logits)
+            B.moe_backward(c, W, dl.x, dy, idx, tw, offsets, pos, x_perm, y_perm, imp,
+                           IMPORTANCE_LOSS_WEIGHT, grads, ws_b, hidden=hidden, preact=preact,
+                           logits=logits, noisy=nz)
             if ev is not None:
                 bwd_evs[-1][1].record()
 
@@ -322,7 +328,8 @@ def main():
         out["config"]["training_step"] = True
         out["backward"] = {"ms": bwd_ms, "tflops": bflops / (bwd_ms / 1e3) / 1e12,
                            "frac_mfma_peak": bflops / (bwd_ms / 1e3) / 1e12 / PEAK_BF16_TFLOPS,
-                           "importance_loss_weight": 0.01}
+                           "importance_loss_weight": IMPORTANCE_LOSS_WEIGHT,
+                           **({"load_loss_weight": LOAD_LOSS_WEIGHT} if args.noisy else {})}
     print(json.dumps(out))
 
 

@@ -42,7 +42,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 6
+#define MOE_ABI_VERSION 7
 
 typedef enum {
   MOE_OK = 0,
@@ -300,6 +300,8 @@ moe_status_t moe_forward(const moe_config_t *cfg, const moe_weights_t *w,
  *     projection); when hidden is NULL it is formed from the pre-activations
  *   logits [T, E] fp32 (moe_route's scores) under MOE_GATE_SOFTMAX_ALL,
  *     else ignored (may be NULL)
+ *   noisy: NULL for the clean gate, else the noisy gate's values and the
+ *     W_noise gradient (moe_noisy_grad_t above; MOE_GATE_TOPK_SOFTMAX only)
  *   importance [E] fp32 or NULL (moe_permute's), importance_weight: the
  *     weight of the CV^2(Importance) term (ignored when importance is NULL)
  *   grads: every pointer device memory, written in full:
@@ -321,6 +323,28 @@ typedef struct {
   void *dw_down_shared;
 } moe_grads_t;
 
+/* The noisy gate's share of the backward pass (the forward ran
+ * moe_route_noisy): its gate values are the softmax of the kept noisy
+ * scores H = s + n * Softplus(x W_noise^T), so the gradient reaches W_noise
+ * too; with a load weight the loss also holds load_weight * CV^2(Load) of
+ * the smooth Load (Qiita summary, "Load-balancing losses"), whose
+ * thresholds are the forward's entries of H (the k-th, or for a kept
+ * expert the (k+1)-th, of the stable descending order).
+ *   w_noise [E, d] fp32, noise [T, E] fp32 (the draws), clean_logits and
+ *   noise_scale [T, E] fp32, load [E] fp32 or NULL: moe_route_noisy's
+ *   inputs and outputs (device, in)
+ *   load_weight: the weight of CV^2(Load) (ignored when load is NULL)
+ *   dw_noise [E, d] fp32 (device, out, written in full) */
+typedef struct {
+  const float *w_noise;
+  const float *noise;
+  const float *clean_logits;
+  const float *noise_scale;
+  const float *load;
+  float load_weight;
+  float *dw_noise;
+} moe_noisy_grad_t;
+
 moe_status_t moe_backward_workspace_bytes(const moe_config_t *cfg, size_t *bytes);
 
 moe_status_t moe_backward(const moe_config_t *cfg, const moe_weights_t *w,
@@ -328,6 +352,7 @@ moe_status_t moe_backward(const moe_config_t *cfg, const moe_weights_t *w,
                           const float *topk_w, const int32_t *offsets,
                           const int32_t *pos, const void *x_perm, const void *y_perm,
                           const void *hidden, const void *preact, const float *logits,
+                          const moe_noisy_grad_t *noisy,
                           const float *importance, float importance_weight,
                           const moe_grads_t *grads, void *ws, size_t ws_bytes,
                           hipStream_t stream);

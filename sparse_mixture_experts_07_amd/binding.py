@@ -84,7 +84,7 @@ def lib():
             "moe_grouped_rows": [P, P],
             "moe_route": [P, P, P, P, P, P, P, P, P],
             "moe_backward_workspace_bytes": [P, P],
-            "moe_backward": [P, P, P, P, P, P, P, P, P, P, P, P, P, P, C.c_float, P, P,
+            "moe_backward": [P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, C.c_float, P, P,
                              C.c_size_t, P],
             "moe_expert_up_train": [P, P, P, P, P, P, P, P],
             "moe_route_noisy": [P, P, P, P, P, P, P, P, P, P, P, P, P, P, P,
@@ -207,6 +207,20 @@ def grads(dx, dw_gate, dw_up, dw_down, db_gate=None, db_up=None, db_down=None,
                     _ptr(db_up), _ptr(db_down), _ptr(dw_up_shared), _ptr(dw_down_shared))
 
 
+class MoeNoisyGrad(C.Structure):
+    _fields_ = [("w_noise", C.c_void_p), ("noise", C.c_void_p),
+                ("clean_logits", C.c_void_p), ("noise_scale", C.c_void_p),
+                ("load", C.c_void_p), ("load_weight", C.c_float),
+                ("dw_noise", C.c_void_p)]
+
+
+def noisy_grad(w_noise, noise, clean_logits, noise_scale, dw_noise, load=None,
+               load_weight: float = 0.0) -> MoeNoisyGrad:
+    """Pointer struct of the noisy gate's backward inputs and W_noise output."""
+    return MoeNoisyGrad(_ptr(w_noise), _ptr(noise), _ptr(clean_logits), _ptr(noise_scale),
+                        _ptr(load), float(load_weight), _ptr(dw_noise))
+
+
 def moe_backward_workspace_bytes(cfg: MoeConfig) -> int:
     n = C.c_size_t()
     _check("moe_backward_workspace_bytes",
@@ -216,12 +230,14 @@ def moe_backward_workspace_bytes(cfg: MoeConfig) -> int:
 
 def moe_backward(cfg, w: MoeWeights, x, dy, topk_idx, topk_w, offsets, pos, x_perm, y_perm,
                  importance, importance_weight: float, g: MoeGrads, ws, ws_bytes=None,
-                 stream=None, hidden=None, preact=None, logits=None) -> None:
+                 stream=None, hidden=None, preact=None, logits=None,
+                 noisy: MoeNoisyGrad = None) -> None:
     nb = _nbytes(ws) if ws_bytes is None and ws is not None else (ws_bytes or 0)
     _check("moe_backward", lib().moe_backward(
         C.byref(cfg), C.byref(w), _ptr(x), _ptr(dy), _ptr(topk_idx), _ptr(topk_w),
         _ptr(offsets), _ptr(pos), _ptr(x_perm), _ptr(y_perm), _ptr(hidden), _ptr(preact),
-        _ptr(logits), _ptr(importance), float(importance_weight), C.byref(g), _ptr(ws), nb,
+        _ptr(logits), C.byref(noisy) if noisy is not None else None, _ptr(importance),
+        float(importance_weight), C.byref(g), _ptr(ws), nb,
         _stream(stream)))
 
 

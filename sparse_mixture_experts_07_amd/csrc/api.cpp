@@ -165,7 +165,7 @@ struct BwdLayout {
   size_t gimp, ds, dsp, ds_cols, poff, colsrc;
   size_t off_all, src_all, pos_all, hist, full_off, perm_w;
   size_t A, H, dyp, dH, dA, dxp, dypT, HT, dAT, xpT;
-  size_t tm, dS, dxr, dpart, total;
+  size_t tm, dS, dU, gload, dxr, dpart, total;
 };
 
 BwdLayout bwd_layout(const moe_config_t *c) {
@@ -203,12 +203,15 @@ BwdLayout bwd_layout(const moe_config_t *c) {
   take(L.HT, 2 * h * Rp);
   take(L.dAT, 2 * nup * Rp);
   take(L.xpT, 2 * d * Rp);
-  const bool dense = c->gate == MOE_GATE_SOFTMAX_ALL;   // dense router gradients
-  take(L.tm, dense ? 4 * T : 0);
-  take(L.dS, dense ? 4 * T * E : 0);
-  take(L.dxr, dense ? 4 * T * d : 0);
+  // dense router gradients: the softmax-all gate, and the noisy gate (which
+  // the configuration does not name, so the space is always there)
+  take(L.tm, 4 * T);
+  take(L.dS, 4 * T * E);
+  take(L.dU, 4 * T * E);
+  take(L.gload, 4 * E);
+  take(L.dxr, 4 * T * d);
   int splits = 1, kchunk = 0;
-  if (dense && T > 0) moe::bwd_dense_plan(T, (int)E, (int)d, &splits, &kchunk);
+  if (T > 0) moe::bwd_dense_plan(T, (int)E, (int)d, &splits, &kchunk);
   take(L.dpart, splits > 1 ? 4 * (int64_t)splits * E * d : 0);
   L.total = o;
   return L;
@@ -496,7 +499,8 @@ moe_status_t moe_backward(const moe_config_t *cfg, const moe_weights_t *w, const
                           const void *dy, const int32_t *topk_idx, const float *topk_w,
                           const int32_t *offsets, const int32_t *pos, const void *x_perm,
                           const void *y_perm, const void *hidden, const void *preact,
-                          const float *logits, const float *importance,
+                          const float *logits, const moe_noisy_grad_t *noisy,
+                          const float *importance,
                           float importance_weight, const moe_grads_t *g, void *ws,
                           size_t ws_bytes, hipStream_t stream) {
   moe_status_t st = check_bwd_cfg(cfg);
@@ -508,6 +512,10 @@ moe_status_t moe_backward(const moe_config_t *cfg, const moe_weights_t *w, const
       !std::isfinite(importance_weight))
     return MOE_ERR_INVALID_ARGUMENT;
   const bool softmax_all = cfg->gate == MOE_GATE_SOFTMAX_ALL;
+  if (noisy && (cfg->gate != MOE_GATE_TOPK_SOFTMAX || !dev_ok(noisy->w_noise) ||
+                !dev_ok(noisy->dw_noise) || !opt_ok(noisy->load) ||
+                !std::isfinite(noisy->load_weight)))
+    return MOE_ERR_INVALID_ARGUMENT;
   const bool swi = cfg->act == MOE_ACT_SWIGLU;
   if (swi && (g->db_up || g->db_down)) return MOE_ERR_INVALID_ARGUMENT;
   if (cfg->num_shared ? (!dev_ok(g->dw_up_shared) || !dev_ok(g->dw_down_shared))
@@ -519,6 +527,7 @@ moe_status_t moe_backward(const moe_config_t *cfg, const moe_weights_t *w, const
   clear_pending_error();
   if (T == 0) {
     hipError_t e = moe::launch_fill_f32(g->dw_gate, E * d, stream);
+    if (e == hipSuccess && noisy) e = moe::launch_fill_f32(noisy->dw_noise, E * d, stream);
     if (e == hipSuccess) e = moe::launch_fill_f32(g->db_gate, E, stream);
     // bf16 gradients: a zero bf16 is two zero bytes; every count is even
     auto zero16 = [&](void *p, int64_t n) {
@@ -534,7 +543,9 @@ moe_status_t moe_backward(const moe_config_t *cfg, const moe_weights_t *w, const
   }
   if (!dev_ok(x) || !dev_ok(dy) || !dev_ok(topk_idx) || !dev_ok(topk_w) || !dev_ok(offsets) ||
       !dev_ok(pos) || !dev_ok(x_perm) || !dev_ok(y_perm) || !dev_ok(g->dx) ||
-      (softmax_all && !dev_ok(logits)))
+      (softmax_all && !dev_ok(logits)) ||
+      (noisy && (!dev_ok(noisy->noise) || !dev_ok(noisy->clean_logits) ||
+                 !dev_ok(noisy->noise_scale))))
     return MOE_ERR_INVALID_ARGUMENT;
   const BwdLayout L = bwd_layout(cfg);
   if (!dev_ok(ws)) return MOE_ERR_INVALID_ARGUMENT;
@@ -568,6 +579,15 @@ moe_status_t moe_backward(const moe_config_t *cfg, const moe_weights_t *w, const
   a.hidden = static_cast<const uint16_t *>(hidden);
   a.preact = static_cast<const uint16_t *>(preact);
   a.logits = softmax_all ? logits : nullptr;
+  if (noisy) {
+    a.clean = noisy->clean_logits;
+    a.scale = noisy->noise_scale;
+    a.noise = noisy->noise;
+    a.load = noisy->load;
+    a.w_load = noisy->load_weight;
+    a.w_noise = noisy->w_noise;
+    a.dw_noise = noisy->dw_noise;
+  }
   a.dx = static_cast<uint16_t *>(g->dx);
   a.dw_gate = g->dw_gate;
   a.db_gate = g->db_gate;
@@ -602,12 +622,12 @@ moe_status_t moe_backward(const moe_config_t *cfg, const moe_weights_t *w, const
   b.HT = at<uint16_t>(ws, L.HT);
   b.dAT = at<uint16_t>(ws, L.dAT);
   b.xpT = at<uint16_t>(ws, L.xpT);
-  if (softmax_all) {
-    b.tm = at<float>(ws, L.tm);
-    b.dS = at<float>(ws, L.dS);
-    b.dxr = at<float>(ws, L.dxr);
-    b.dpart = at<float>(ws, L.dpart);
-  }
+  b.tm = at<float>(ws, L.tm);
+  b.dS = at<float>(ws, L.dS);
+  b.dU = at<float>(ws, L.dU);
+  b.gload = at<float>(ws, L.gload);
+  b.dxr = at<float>(ws, L.dxr);
+  b.dpart = at<float>(ws, L.dpart);
   return hip_status(moe::launch_backward(a, b, stream));
 }
 

@@ -22,6 +22,7 @@ struct BwdBuffers {
   // router's share of dx [T, d] (fp32)
   float *tm, *dS, *dxr;
   float *dpart;   // [splits, E, d] partial dW_g when the plan has several splits
+  float *dU, *gload;   // noisy gate: noise-score gradients [T, E], Load term [E]
 };
 
 // Token splits of the softmax-all gate's dense router weight gradient
@@ -39,6 +40,11 @@ struct BwdArgs {
   const uint16_t *x_perm, *y_perm;
   const uint16_t *hidden, *preact;   // from the training forward, or NULL
   const float *logits;   // the forward's router scores [T, E] (softmax-all gate), else NULL
+  // noisy gate (clean != NULL): the forward's clean scores, Softplus scales,
+  // draws, smooth Load and its loss weight; W_noise and its gradient
+  const float *clean, *scale, *noise, *load, *w_noise;
+  float w_load;
+  float *dw_noise;
   uint16_t *dx;
   float *dw_gate, *db_gate;   // fp32, the router's dtype
   uint16_t *dw_up, *dw_down, *db_up, *db_down, *dw_up_s, *dw_down_s;   // bf16

@@ -463,6 +463,114 @@ __global__ __launch_bounds__(kWave) void bwd_dense_ds_kernel(
   }
 }
 
+// Noisy gate (H = s + n * Softplus(u), u = x W_noise^T; the kept weights are
+// the softmax of the kept H) with the smooth Load P(x, i) = Phi(z_i), z_i =
+// (s_i - H_{j(i)}) / Softplus_i, j(i) the k-th ranked entry of H when i is
+// not kept and the (k+1)-th when it is.  One wavefront per token writes the
+// dense gradients of the clean scores s and of the noise scores u:
+//   a_i    = gload_i phi(z_i) / Softplus_i       (gload: d w_load CV^2 / d Load)
+//   dH_i   = ds_j [i kept as slot j] - [i = k-th] sum_{unkept} a - [i = (k+1)-th]
+//            sum_{kept} a
+//   dS_i   = dH_i + a_i
+//   dU_i   = sigmoid(u_i) (n_i dH_i - a_i z_i),  sigmoid(u) = 1 - exp(-Softplus(u))
+// H is recomputed with the forward's one fused multiply-add, so the ranks
+// are the forward's.
+__global__ __launch_bounds__(kWave) void bwd_noisy_ds_kernel(
+    const float *__restrict__ clean, const float *__restrict__ scale,
+    const float *__restrict__ noise, const int32_t *__restrict__ idx,
+    const float *__restrict__ ds, const float *__restrict__ gload, int E, int k,
+    float *__restrict__ dS, float *__restrict__ dU) {
+  constexpr int Q = kMaxExperts / kWave;
+  const int t = blockIdx.x;
+  const int lane = threadIdx.x;
+  const int64_t row = (int64_t)t * E;
+  const int32_t *it = idx + (int64_t)t * k;
+  float sv[Q], sg[Q], nv[Q], hv[Q], dh[Q];
+  int slot[Q];
+#pragma unroll
+  for (int q = 0; q < Q; ++q) {
+    const int e = lane + kWave * q;
+    const bool ok = e < E;
+    sv[q] = ok ? clean[row + e] : 0.0f;
+    sg[q] = ok ? scale[row + e] : 0.0f;
+    nv[q] = ok ? noise[row + e] : 0.0f;
+    hv[q] = fmaf(nv[q], sg[q], sv[q]);
+    int j = -1;
+    for (int i = 0; i < k && ok; ++i)
+      if (it[i] == e) j = i;
+    slot[q] = j;
+    dh[q] = j >= 0 ? ds[(int64_t)t * k + j] : 0.0f;
+  }
+  float a[Q], z[Q];
+#pragma unroll
+  for (int q = 0; q < Q; ++q) a[q] = z[q] = 0.0f;
+  int jk = -1, jk1 = -1;
+  if (gload && k < E) {
+    jk = it[k - 1];
+    // the (k+1)-th: the best entry outside the kept k (H descending, index
+    // ascending), a wavefront arg-max
+    bool ba = false;
+    float bh = 0.0f;
+    int be = 0x7fffffff;
+#pragma unroll
+    for (int q = 0; q < Q; ++q) {
+      const int e = lane + kWave * q;
+      if (e < E && slot[q] < 0 && (!ba || hv[q] > bh || (hv[q] == bh && e < be))) {
+        ba = true;
+        bh = hv[q];
+        be = e;
+      }
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+      const bool oa = __shfl_xor((int)ba, off) != 0;
+      const float oh = __shfl_xor(bh, off);
+      const int oe = __shfl_xor(be, off);
+      if (oa && (!ba || oh > bh || (oh == bh && oe < be))) {
+        ba = true;
+        bh = oh;
+        be = oe;
+      }
+    }
+    jk1 = be;
+    const float hk = fmaf(noise[row + jk], scale[row + jk], clean[row + jk]);
+    const float hk1 = fmaf(noise[row + jk1], scale[row + jk1], clean[row + jk1]);
+    constexpr float kInvSqrt2Pi = 0.3989422804014327f;
+#pragma unroll
+    for (int q = 0; q < Q; ++q) {
+      const int e = lane + kWave * q;
+      if (e < E && sg[q] > 0.0f) {
+        z[q] = (sv[q] - (slot[q] >= 0 ? hk1 : hk)) / sg[q];
+        a[q] = gload[e] * kInvSqrt2Pi * expf(-0.5f * z[q] * z[q]) / sg[q];
+      }
+    }
+  }
+  float ak = 0.0f, au = 0.0f;   // sums of a over the kept and the other entries
+#pragma unroll
+  for (int q = 0; q < Q; ++q) {
+    if (slot[q] >= 0)
+      ak += a[q];
+    else
+      au += a[q];
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    ak += __shfl_xor(ak, off);
+    au += __shfl_xor(au, off);
+  }
+#pragma unroll
+  for (int q = 0; q < Q; ++q) {
+    const int e = lane + kWave * q;
+    if (e >= E) continue;
+    float dht = dh[q];
+    if (e == jk) dht -= au;
+    if (e == jk1) dht -= ak;
+    dS[row + e] = dht + a[q];
+    const float sigm = -expm1f(-sg[q]);
+    dU[row + e] = sigm * (nv[q] * dht - a[q] * z[q]);
+  }
+}
+
 // Dense fp32 products of the softmax-all gate's router gradients on the
 // fp32 matrix cores (v_mfma_f32_16x16x4_f32: lane l supplies A[l%16][l/16]
 // and B[l/16][l%16], and holds D[4(l/16)+r][l%16] in r = 0..3):
@@ -503,7 +611,7 @@ __device__ inline void dense_ld_b(const uint16_t *__restrict__ B, int64_t off, b
 template <int WM, int WN, int MT, int NT, bool AT, typename BT>
 __global__ __launch_bounds__(256) void bwd_dense_gemm_kernel(
     const float *__restrict__ A, const BT *__restrict__ B, int M, int N, int K, int kchunk,
-    float *__restrict__ C) {
+    int accumulate, float *__restrict__ C) {
   static_assert(WM * WN == 4, "four wavefronts");
   constexpr int BM = WM * MT * 16, BN = WN * NT * 16, BK = 16;
   constexpr int PA = BM + 16, PB = BN + 16;
@@ -602,7 +710,10 @@ __global__ __launch_bounds__(256) void bwd_dense_gemm_kernel(
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int m = m0 + (wm * MT + a) * 16 + 4 * r + q;
-        if (m < M && n < N) Cz[(int64_t)m * N + n] = acc[a][b][q];
+        if (m < M && n < N) {
+          float *c = Cz + (int64_t)m * N + n;
+          *c = accumulate ? *c + acc[a][b][q] : acc[a][b][q];
+        }
       }
     }
 }
@@ -701,16 +812,32 @@ hipError_t launch_backward(const BwdArgs &a, const BwdBuffers &b, hipStream_t s)
     bwd_importance_grad_kernel<<<1, kBwdThreads, 0, s>>>(a.importance, E, a.w_imp, b.gimp);
     gimp = b.gimp;
   }
-  const bool dense = a.logits != nullptr;   // softmax-all gate: every score has a gradient
+  // softmax-all and noisy gates: every score has a gradient (dense router
+  // gradients); the noisy gate's noise scores too
+  const bool noisy = a.clean != nullptr;
+  const bool dense = a.logits != nullptr || noisy;
   bwd_gate_kernel<<<T, kBwdThreads, 0, s>>>(a.dy, a.y_perm, a.pos, a.idx, a.topk_w, gimp, T,
-                                            k, d, E, S, R, b.dyp, b.ds, dense ? b.tm : nullptr);
+                                            k, d, E, S, R, b.dyp, b.ds, a.logits ? b.tm : nullptr);
   MOE_TRY(hipGetLastError());
   if (dense) {
-    bwd_dense_ds_kernel<<<T, kWave, 0, s>>>(a.logits, a.idx, b.ds, b.tm, T, E, k, b.dS);
-    // the router's share of dx: dS [T, E] times W_g [E, d]
+    if (noisy) {
+      const float *gload = nullptr;
+      if (a.load && a.w_load != 0.0f) {
+        bwd_importance_grad_kernel<<<1, kBwdThreads, 0, s>>>(a.load, E, a.w_load, b.gload);
+        gload = b.gload;
+      }
+      bwd_noisy_ds_kernel<<<T, kWave, 0, s>>>(a.clean, a.scale, a.noise, a.idx, b.ds, gload, E,
+                                              k, b.dS, b.dU);
+    } else {
+      bwd_dense_ds_kernel<<<T, kWave, 0, s>>>(a.logits, a.idx, b.ds, b.tm, T, E, k, b.dS);
+    }
+    // the router's share of dx: dS [T, E] times W_g [E, d] (+ dU W_noise)
+    const dim3 grid((d + 127) / 128, (T + 127) / 128, 1);
     bwd_dense_gemm_kernel<2, 2, 4, 4, false, float>
-        <<<dim3((d + 127) / 128, (T + 127) / 128, 1), 256, 0, s>>>(b.dS, a.w_gate, T, d, E, E,
-                                                                b.dxr);
+        <<<grid, 256, 0, s>>>(b.dS, a.w_gate, T, d, E, E, 0, b.dxr);
+    if (noisy)
+      bwd_dense_gemm_kernel<2, 2, 4, 4, false, float>
+          <<<grid, 256, 0, s>>>(b.dU, a.w_noise, T, d, E, E, 1, b.dxr);
     MOE_TRY(hipGetLastError());
   }
 
@@ -765,22 +892,26 @@ hipError_t launch_backward(const BwdArgs &a, const BwdBuffers &b, hipStream_t s)
     bwd_rowsum_kernel<uint16_t><<<dim3(h, E), kWave, 0, s>>>(b.dAT, h, Rp, b.poff, nullptr,
                                                              a.db_up);
   if (dense) {   // router gradients from the dense score gradients
-    // dW_g = dS^T X over token splits, then the splits summed in order
+    // dW = dS^T X over token splits, then the splits summed in order
     int splits, kchunk;
     bwd_dense_plan(T, E, d, &splits, &kchunk);
-    float *dst = splits > 1 ? b.dpart : a.dw_gate;
-    if (E <= 32)
-      bwd_dense_gemm_kernel<1, 4, 1, 4, true, uint16_t>
-          <<<dim3((d + 255) / 256, (E + 15) / 16, splits), 256, 0, s>>>(b.dS, a.x, E, d, T,
-                                                                        kchunk, dst);
-    else
-      bwd_dense_gemm_kernel<2, 2, 4, 4, true, uint16_t>
-          <<<dim3((d + 127) / 128, (E + 127) / 128, splits), 256, 0, s>>>(b.dS, a.x, E, d, T,
-                                                                          kchunk, dst);
-    if (splits > 1) {
-      const int64_t n4 = (int64_t)E * d / 4;
-      bwd_split_sum_kernel<<<grid_for(n4, 256), 256, 0, s>>>(b.dpart, splits, n4, a.dw_gate);
-    }
+    auto wgrad = [&](const float *dsc, float *out) {
+      float *dst = splits > 1 ? b.dpart : out;
+      if (E <= 32)
+        bwd_dense_gemm_kernel<1, 4, 1, 4, true, uint16_t>
+            <<<dim3((d + 255) / 256, (E + 15) / 16, splits), 256, 0, s>>>(dsc, a.x, E, d, T,
+                                                                          kchunk, 0, dst);
+      else
+        bwd_dense_gemm_kernel<2, 2, 4, 4, true, uint16_t>
+            <<<dim3((d + 127) / 128, (E + 127) / 128, splits), 256, 0, s>>>(dsc, a.x, E, d, T,
+                                                                            kchunk, 0, dst);
+      if (splits > 1) {
+        const int64_t n4 = (int64_t)E * d / 4;
+        bwd_split_sum_kernel<<<grid_for(n4, 256), 256, 0, s>>>(b.dpart, splits, n4, out);
+      }
+    };
+    wgrad(b.dS, a.dw_gate);
+    if (noisy) wgrad(b.dU, a.dw_noise);
     if (a.db_gate) bwd_dense_bias_kernel<<<E, kWave, 0, s>>>(b.dS, T, E, a.db_gate);
     return hipGetLastError();
   }

@@ -27,7 +27,7 @@ def test_library_exports_every_declared_entry_point():
     assert set(B.EXPORTS) == set(names), names
     for n in names:
         assert hasattr(lib, n), f"libmoe.so does not export {n}"
-    assert B.moe_abi_version() == 6
+    assert B.moe_abi_version() == 7
 
 
 def test_status_strings():
@@ -118,7 +118,7 @@ def test_every_entry_point_rejects_bad_config(name):
                           FAKE, FAKE, None, FAKE, 1 << 40, None),
         L.moe_backward_workspace_bytes(r, C.byref(C.c_size_t())),
         L.moe_backward(r, C.byref(w), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, None,
-                       None, None, C.c_float(0.0), C.byref(B.grads(None, None, None, None)), FAKE,
+                       None, None, None, C.c_float(0.0), C.byref(B.grads(None, None, None, None)), FAKE,
                        1 << 40, None),
         L.moe_expert_up_train(r, C.byref(w), FAKE, FAKE, FAKE, FAKE, FAKE, None),
     ]
@@ -202,7 +202,7 @@ def test_backward_checks():
     inv, uns = B.MOE_ERR_INVALID_ARGUMENT, B.MOE_ERR_UNSUPPORTED
     w = B.MoeWeights(FAKE, None, FAKE, None, FAKE, None, None, None)
     g = B.MoeGrads(FAKE, FAKE, None, FAKE, FAKE, None, None, None, None)
-    args = [FAKE] * 8 + [None, None, None, None, C.c_float(0.0), C.byref(g), FAKE, 1 << 40, None]
+    args = [FAKE] * 8 + [None, None, None, None, None, C.c_float(0.0), C.byref(g), FAKE, 1 << 40, None]
     bf = _cfg(dtype=1)
     # fp32 layers have no backward pass here
     f32 = _cfg(dtype=0)
@@ -215,18 +215,31 @@ def test_backward_checks():
     n0, n2 = C.c_size_t(), C.c_size_t()
     assert L.moe_backward_workspace_bytes(C.byref(_cfg(dtype=1)), C.byref(n0)) == 0
     assert L.moe_backward_workspace_bytes(C.byref(sa), C.byref(n2)) == 0
-    assert n2.value > n0.value
+    assert n2.value == n0.value   # the dense gradients' space is always reserved
+    # the noisy gate's backward: default gate only, W_noise and its gradient
+    # required, then the forward's draws, scores and scales
+    nz = B.MoeNoisyGrad(FAKE, FAKE, FAKE, FAKE, None, 0.5, FAKE)
+    a_nz = [FAKE] * 8 + [None, None, None, C.byref(nz), None, C.c_float(0.0), C.byref(g), FAKE,
+                         1 << 40, None]
+    assert L.moe_backward(C.byref(_cfg(dtype=1, gate=1)), C.byref(w), *a_nz) == inv
+    for bad in (B.MoeNoisyGrad(None, FAKE, FAKE, FAKE, None, 0.5, FAKE),
+                B.MoeNoisyGrad(FAKE, FAKE, FAKE, FAKE, None, 0.5, None),
+                B.MoeNoisyGrad(FAKE, None, FAKE, FAKE, None, 0.5, FAKE),
+                B.MoeNoisyGrad(FAKE, FAKE, FAKE, FAKE, None, float("inf"), FAKE)):
+        a_bad = [FAKE] * 8 + [None, None, None, C.byref(bad), None, C.c_float(0.0), C.byref(g),
+                              FAKE, 1 << 40, None]
+        assert L.moe_backward(C.byref(bf), C.byref(w), *a_bad) == inv
     # required gradient outputs; shared-expert gradients iff S = 1
     g0 = B.MoeGrads(FAKE, None, None, FAKE, FAKE, None, None, None, None)
-    args0 = [FAKE] * 8 + [None, None, None, None, C.c_float(0.0), C.byref(g0), FAKE, 1 << 40, None]
+    args0 = [FAKE] * 8 + [None, None, None, None, None, C.c_float(0.0), C.byref(g0), FAKE, 1 << 40, None]
     assert L.moe_backward(C.byref(bf), C.byref(w), *args0) == inv
     gs = B.MoeGrads(FAKE, FAKE, None, FAKE, FAKE, None, None, FAKE, FAKE)
-    argss = [FAKE] * 8 + [None, None, None, None, C.c_float(0.0), C.byref(gs), FAKE, 1 << 40, None]
+    argss = [FAKE] * 8 + [None, None, None, None, None, C.c_float(0.0), C.byref(gs), FAKE, 1 << 40, None]
     assert L.moe_backward(C.byref(bf), C.byref(w), *argss) == inv
     # workspace
     n = C.c_size_t()
     assert L.moe_backward_workspace_bytes(C.byref(bf), C.byref(n)) == 0
-    small = [FAKE] * 8 + [None, None, None, None, C.c_float(0.0), C.byref(g), FAKE, n.value - 1, None]
+    small = [FAKE] * 8 + [None, None, None, None, None, C.c_float(0.0), C.byref(g), FAKE, n.value - 1, None]
     assert L.moe_backward(C.byref(bf), C.byref(w), *small) == B.MOE_ERR_WORKSPACE_TOO_SMALL
-    nan = [FAKE] * 8 + [None, None, None, None, C.c_float(float("nan")), C.byref(g), FAKE, 1 << 40, None]
+    nan = [FAKE] * 8 + [None, None, None, None, None, C.c_float(float("nan")), C.byref(g), FAKE, 1 << 40, None]
     assert L.moe_backward(C.byref(bf), C.byref(w), *nan) == inv

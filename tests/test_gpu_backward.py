@@ -25,9 +25,10 @@ def _gpu():
     require_gpu()
 
 
-def forward_saved(L, capacity=0, train=False, overflow=0):
+def forward_saved(L, capacity=0, train=False, overflow=0, noise=None):
     """The stage entry points; every tensor the backward pass takes (train:
-    the up projection that also stores the pre-activations)."""
+    the up projection that also stores the pre-activations; noise: the noisy
+    gate with these draws and the layer's w_noise)."""
     dl = DeviceLayer.upload(L, capacity=capacity, overflow=overflow)
     c, dev = dl.cfg, dl.x.device
     T, k, E, d = L.cfg.T, L.cfg.k, L.cfg.E, L.cfg.d
@@ -47,7 +48,17 @@ def forward_saved(L, capacity=0, train=False, overflow=0):
     # router scores
     if L.cfg.gate == synthetic.GATE_SOFTMAX_ALL or (capacity and overflow):
         s["logits"] = torch.empty((T, E), dtype=torch.float32, device=dev)
-    B.moe_route(c, dl.x, dl.w_gate, dl.b_gate, s["idx"], s["w"], s["counts"], s.get("logits"))
+    if noise is None:
+        B.moe_route(c, dl.x, dl.w_gate, dl.b_gate, s["idx"], s["w"], s["counts"],
+                    s.get("logits"))
+    else:
+        f32 = dict(dtype=torch.float32, device=dev)
+        s.update(w_noise=to_device(L.w_noise, dev), noise=to_device(noise, dev),
+                 clean=torch.empty((T, E), **f32), scale=torch.empty((T, E), **f32),
+                 load=torch.empty(E, **f32), cv2=torch.empty(2, dtype=torch.float64, device=dev))
+        B.moe_route_noisy(c, dl.x, dl.w_gate, dl.b_gate, s["w_noise"], s["noise"], s["clean"],
+                          s["scale"], s["idx"], s["w"], s["counts"], s["imp"], s["load"],
+                          s["cv2"], ws)
     B.moe_permute(c, s["idx"], s["w"], dl.x, s["offsets"], s["perm_src"], s["pos"], s["imp"],
                   None, s["x_perm"], ws, logits=s.get("logits"))
     if train:
@@ -63,8 +74,9 @@ def forward_saved(L, capacity=0, train=False, overflow=0):
     return dl, s
 
 
-def run_backward(L, dy_bits, capacity=0, imp_w=0.0, train=False, overflow=0):
-    dl, s = forward_saved(L, capacity, train, overflow)
+def run_backward(L, dy_bits, capacity=0, imp_w=0.0, train=False, overflow=0, noise=None,
+                 load_w=0.0):
+    dl, s = forward_saved(L, capacity, train, overflow, noise)
     c, dev = dl.cfg, dl.x.device
     cfg = L.cfg
     E, d, h, S = cfg.E, cfg.d, cfg.h, cfg.S
@@ -83,18 +95,35 @@ def run_backward(L, dy_bits, capacity=0, imp_w=0.0, train=False, overflow=0):
                  g["b_down"], g["w_up_shared"], g["w_down_shared"])
     ws = torch.empty(max(B.moe_backward_workspace_bytes(c), 256), dtype=torch.uint8, device=dev)
     dy = to_device(dy_bits, dev)
+    nz = None
+    if noise is not None:
+        g["w_noise"] = torch.full((E, d), 7.0, **f32)   # written in full
+        nz = B.noisy_grad(s["w_noise"], s["noise"], s["clean"], s["scale"], g["w_noise"],
+                          s["load"] if load_w else None, load_w)
     B.moe_backward(c, dl.weights(), dl.x, dy, s["idx"], s["w"], s["offsets"], s["pos"],
                    s["x_perm"], s["y_perm"], s["imp"] if imp_w else None, imp_w, mg, ws,
-                   hidden=s.get("hidden"), preact=s.get("preact"), logits=s.get("logits"))
+                   hidden=s.get("hidden"), preact=s.get("preact"), logits=s.get("logits"),
+                   noisy=nz)
     torch.cuda.synchronize()
     out = {("x" if n == "dx" else n): (to_f64(t) if t is not None else None) for n, t in g.items()}
     return out, s, (dl, mg, ws, dy)
 
 
-def check_backward(L, capacity=0, imp_w=0.0, seed=0, train=False, overflow=0):
+def check_backward(L, capacity=0, imp_w=0.0, seed=0, train=False, overflow=0, noise=None,
+                   load_w=0.0):
     rng = np.random.default_rng(seed)
     dy_bits = f32_to_bf16_bits(rng.standard_normal((L.cfg.T, L.cfg.d)).astype(np.float32))
-    got, s, _ = run_backward(L, dy_bits, capacity, imp_w, train, overflow)
+    got, s, _ = run_backward(L, dy_bits, capacity, imp_w, train, overflow, noise, load_w)
+    if noise is not None:
+        # same selection and the same fp32 Softplus scales (so the same
+        # ranks of H behind the smooth Load's thresholds)
+        rn = oracle.route_noisy(L, noise)
+        assert np.array_equal(s["scale"].cpu().numpy().view(np.uint32), rn["scale"].view(np.uint32))
+        assert np.array_equal(s["idx"].cpu().numpy(), rn["idx"])
+        keep = oracle.capacity_keep(L.cfg, rn["idx"], capacity) if capacity else None
+        ref = oracle.backward.backward(L, bf16_bits_to_f32(dy_bits), keep, imp_w, noise=noise,
+                                       load_weight=load_w)
+        return _compare(got, ref)
     ridx, _, sc = oracle.route(L, want_scores=True)
     assert np.array_equal(s["idx"].cpu().numpy(), ridx)
     keep = assign = None
@@ -104,6 +133,10 @@ def check_backward(L, capacity=0, imp_w=0.0, seed=0, train=False, overflow=0):
         keep = oracle.capacity_keep(L.cfg, ridx, capacity)
     ref = oracle.backward.backward(L, bf16_bits_to_f32(dy_bits), keep, imp_w, idx=ridx,
                                    assign=assign)
+    return _compare(got, ref)
+
+
+def _compare(got, ref):
     errs = {}
     for n, r in ref.items():
         gv = got.get(n)
@@ -237,6 +270,40 @@ def test_backward_with_rerouting(train):
     L.b_gate = np.linspace(1.5, 0.0, 6).astype(np.float32)
     errs = check_backward(L, 140, 0.2, train=train, overflow=B.MOE_OVERFLOW_NEXT_CHOICE)
     print({n: f"{e:.2e}" for n, e in errs.items()})
+
+
+def _noisy_layer(seed, **kw):
+    L = random_layer(seed, wstd=0.15, **kw)
+    rng = np.random.default_rng(seed + 1000)
+    L.w_noise = (rng.standard_normal((L.cfg.E, L.cfg.d)) * 0.3).astype(np.float32)
+    return L, rng.standard_normal((L.cfg.T, L.cfg.E)).astype(np.float32)
+
+
+NOISY_CASES = {
+    "e8-shared-load": (dict(T=300, d=128, h=256, E=8, k=2, act=SWIGLU, dtype=BF16, bias=True, S=1),
+                       0, 0.3, 0.5, False),
+    "e64-k6-train": (dict(T=257, d=64, h=128, E=64, k=6, act=SWIGLU, dtype=BF16, bias=True),
+                     0, 0.0, 0.8, True),
+    "e256-k8": (dict(T=200, d=64, h=64, E=256, k=8, act=SWIGLU, dtype=BF16, bias=True),
+                0, 0.2, 0.5, False),
+    "gelu-capacity": (dict(T=400, d=64, h=128, E=6, k=2, act=GELU, dtype=BF16, bias=True,
+                           expert_bias=True), 150, 0.2, 0.4, False),
+    "k-eq-E": (dict(T=100, d=64, h=64, E=4, k=4, act=SWIGLU, dtype=BF16), 0, 0.3, 0.5, False),
+    "no-load-term": (dict(T=300, d=128, h=128, E=8, k=2, act=SWIGLU, dtype=BF16, bias=True),
+                     0, 0.0, 0.0, True),
+}
+
+
+@pytest.mark.parametrize("name", list(NOISY_CASES))
+def test_backward_noisy_gate(name):
+    """The noisy gate (moe_route_noisy's forward): gradients of <dy, y> +
+    w_imp CV^2(Importance) + w_load CV^2(smooth Load) in every parameter,
+    W_noise included, against the float64 autograd oracle."""
+    kw, cap, imp_w, load_w, train = NOISY_CASES[name]
+    L, noise = _noisy_layer(68, **kw)
+    errs = check_backward(L, cap, imp_w, train=train, noise=noise, load_w=load_w)
+    assert "w_noise" in errs
+    print(name, {n: f"{e:.2e}" for n, e in errs.items()})
 
 
 def test_backward_is_deterministic():
