@@ -140,7 +140,6 @@ def forward(layer, p: dict, idx: np.ndarray, keep: Optional[np.ndarray] = None,
     raw = x @ p["w_gate"].T
     s = raw + p["b_gate"] if "b_gate" in p else raw
     it = torch.from_numpy(np.ascontiguousarray(idx, np.int64))
-    gate = getattr(cfg, "gate", 0)
     load = None
     if noisy is not None:   # softmax over the kept noisy scores; smooth Load
         H, sig = _noisy_scores(p, s, _f64(noisy["noise"]))
@@ -152,12 +151,8 @@ def forward(layer, p: dict, idx: np.ndarray, keep: Optional[np.ndarray] = None,
                                                                            np.int64)))
             z = (s - thr) / sig
             load = (0.5 * torch.special.erfc(-z / np.sqrt(2.0))).sum(0)
-    elif gate == 1:   # the bias steers the selection only
-        g = torch.softmax(torch.gather(raw, 1, it), dim=1)
-    elif gate == 2:   # softmax over all E, read at the kept experts
-        g = torch.gather(torch.softmax(s, dim=1), 1, it)
-    else:             # softmax over the kept k
-        g = torch.softmax(torch.gather(s, 1, it), dim=1)
+    else:
+        g, _ = forward_gates(layer, p, idx)
     gk = g
     if keep is not None:
         gk = g * torch.from_numpy(np.asarray(keep, np.float64).reshape(T, k))
@@ -215,3 +210,140 @@ def backward(layer, dy: np.ndarray, keep: Optional[np.ndarray] = None,
     grads = torch.autograd.grad(L, [p[n] for n in names], allow_unused=True)
     return {n: (np.zeros(tuple(p[n].shape)) if g is None else g.numpy())
             for n, g in zip(names, grads)}
+
+
+# ---- slices of the same gradient for layers too large for the whole graph.
+# Both follow from the loss by separability, and both are pinned to
+# backward() on small layers: a token's x enters the loss only through its
+# own output row and its own gate values in Importance (so with the
+# Importance term replaced by its linearisation at the whole batch, the
+# loss of a token subset has the same gradient in those tokens' x); and the
+# expert FFN is a sum over hidden units (so the loss restricted to some
+# hidden units of one expert has the same gradient in those units' weights).
+
+def _router_params(layer) -> dict:
+    """x, w_gate (and b_gate) as float64 tensors, no expert weights."""
+    p = {"x": _f64(layer.x), "w_gate": _f64(layer.w_gate)}
+    if getattr(layer, "b_gate", None) is not None:
+        p["b_gate"] = _f64(layer.b_gate)
+    return p
+
+
+def importance_gradient(layer, importance_weight: float, idx=None) -> np.ndarray:
+    """d (w * CV^2(Importance)) / d Importance at the whole batch, float64
+    [E] (the oracle's routing unless idx is given)."""
+    if idx is None:
+        idx, _, _ = _route(layer)
+    imp = forward_gates(layer, _router_params(layer), idx)[1].detach().requires_grad_(True)
+    (g,) = torch.autograd.grad(importance_weight * cv2(imp), [imp])
+    return g.numpy()
+
+
+def forward_gates(layer, p: dict, idx: np.ndarray):
+    """(gate values [T, k], Importance [E]) of the fixed selection idx."""
+    cfg = layer.cfg
+    raw = p["x"] @ p["w_gate"].T
+    s = raw + p["b_gate"] if "b_gate" in p else raw
+    it = torch.from_numpy(np.ascontiguousarray(idx, np.int64))
+    gate = getattr(cfg, "gate", 0)
+    if gate == 1:     # the bias steers the selection only
+        g = torch.softmax(torch.gather(raw, 1, it), dim=1)
+    elif gate == 2:   # softmax over all E, read at the kept experts
+        g = torch.gather(torch.softmax(s, dim=1), 1, it)
+    else:             # softmax over the kept k
+        g = torch.softmax(torch.gather(s, 1, it), dim=1)
+    imp = torch.zeros(cfg.E, dtype=torch.float64).index_add(0, it.reshape(-1), g.reshape(-1))
+    return g, imp
+
+
+class _TokenSubset:
+    """The layer restricted to some tokens (same weights, T = len(tokens))."""
+
+    def __init__(self, layer, tokens):
+        self.cfg = layer.cfg.with_(T=len(tokens))
+        self.x = np.ascontiguousarray(np.asarray(layer.x)[np.asarray(tokens)])
+
+
+def dx_rows(layer, dy: np.ndarray, tokens, importance_weight: float = 0.0,
+            idx: Optional[np.ndarray] = None) -> np.ndarray:
+    """Rows `tokens` of d loss / d x (loss of backward(), no capacity),
+    float64 [len(tokens), d].  Only the experts those tokens use are taken
+    to float64."""
+    if idx is None:
+        idx, _, _ = _route(layer)
+    tokens = np.asarray(tokens, np.int64)
+    gimp = torch.from_numpy(importance_gradient(layer, importance_weight, idx))
+    sub = _TokenSubset(layer, tokens)
+    p = _router_params(layer)
+    p["x"] = _f64(sub.x).requires_grad_(True)
+    used = sorted(set(np.asarray(idx)[tokens].ravel().tolist()))
+    for n in ("w_up", "w_down", "b_up", "b_down"):
+        a = getattr(layer, n, None)
+        if a is not None and np.asarray(a).size:
+            p[n] = {e: _f64(np.asarray(a)[e]) for e in used}
+    for n in ("w_up_shared", "w_down_shared"):
+        a = getattr(layer, n, None)
+        if a is not None and np.asarray(a).size:
+            p[n] = _f64(a)
+    y, _, imp, _ = forward(sub, p, idx[tokens])
+    L = (_f64(np.asarray(dy)[tokens]) * y).sum() + (gimp * imp).sum()
+    (gx,) = torch.autograd.grad(L, [p["x"]])
+    return gx.numpy()
+
+
+def expert_unit_grads(layer, dy: np.ndarray, e: int, units, idx: Optional[np.ndarray] = None,
+                      w: Optional[np.ndarray] = None) -> dict:
+    """Gradients of the loss of backward() (no capacity) in the weights of
+    hidden units `units` of expert e (e == E: the shared expert), float64:
+    'w_up' [len(units), d] (SwiGLU: [2, len(units), d], gate rows then up
+    rows), 'w_down' [d, len(units)], and 'b_up' [len(units)] for a GELU
+    expert with biases.  The expert's rows: every slot routed to it with its
+    gate value (the shared expert: every token, weight 1).  idx: the
+    selection (the oracle's routing if None); w: its gate values [T, k]
+    (those of forward()'s graph if None)."""
+    cfg = layer.cfg
+    units = np.asarray(units, np.int64)
+    xs = _f64(layer.x)
+    dyt = _f64(np.asarray(dy))
+    if e == cfg.E:
+        rows_t = np.arange(cfg.T)
+        gw = torch.ones(cfg.T, dtype=torch.float64)
+        w1 = _f64(layer.w_up_shared)[0]
+        w2 = _f64(layer.w_down_shared)[0]
+        b1 = None
+    else:
+        if idx is None:
+            idx, _, _ = _route(layer)
+        if w is None:   # the gate values of backward()'s graph
+            w = forward_gates(layer, _router_params(layer), idx)[0].numpy()
+        t_sel, j_sel = np.nonzero(idx == e)
+        rows_t = t_sel
+        gw = torch.from_numpy(np.asarray(w, np.float64)[t_sel, j_sel])
+        w1 = _f64(np.asarray(layer.w_up)[e])
+        w2 = _f64(np.asarray(layer.w_down)[e])
+        b1 = (_f64(np.asarray(layer.b_up)[e])
+              if getattr(layer, "b_up", None) is not None and np.asarray(layer.b_up).size
+              else None)
+    h = cfg.h
+    xr = xs[torch.from_numpy(rows_t)]
+    dyr = dyt[torch.from_numpy(rows_t)] * gw.unsqueeze(1)
+    if cfg.act == 0:   # GELU
+        w1u = w1[torch.from_numpy(units)].clone().requires_grad_(True)
+        b1u = b1[torch.from_numpy(units)].clone().requires_grad_(True) if b1 is not None else None
+        a = xr @ w1u.T + (b1u if b1u is not None else 0.0)
+        hid = 0.5 * a * (1.0 + torch.special.erf(a / np.sqrt(2.0)))
+        leaves = [w1u] + ([b1u] if b1u is not None else [])
+    else:
+        w1u = torch.stack([w1[torch.from_numpy(units)], w1[torch.from_numpy(units + h)]])
+        w1u = w1u.clone().requires_grad_(True)
+        g = xr @ w1u[0].T
+        u = xr @ w1u[1].T
+        hid = g * torch.sigmoid(g) * u
+        leaves = [w1u]
+    w2u = w2[:, torch.from_numpy(units)].clone().requires_grad_(True)
+    L = (dyr * (hid @ w2u.T)).sum()
+    grads = torch.autograd.grad(L, leaves + [w2u])
+    out = {"w_up": grads[0].numpy(), "w_down": grads[-1].numpy()}
+    if cfg.act == 0 and b1 is not None:
+        out["b_up"] = grads[1].numpy()
+    return out

@@ -201,3 +201,32 @@ def test_noise_free_noisy_gate_is_the_clean_gate():
     assert np.all(gn["w_noise"] == 0) and np.all(gc["w_noise"] == 0)
     gl = B.backward(L, dy, importance_weight=0.3, noise=zero, load_weight=0.5)
     assert np.abs(gl["w_noise"]).max() > 0
+
+
+@pytest.mark.parametrize("act,S,gate,imp_w", [(SWIGLU, 1, 0, 0.4), (GELU, 0, 0, 0.3),
+                                              (SWIGLU, 0, 1, 0.2), (SWIGLU, 0, 2, 0.5)])
+def test_gradient_slices_equal_the_whole_graph(act, S, gate, imp_w):
+    """The slices used at sizes too large for the whole graph: dx rows of a
+    token subset (Importance linearised at the whole batch) and the weight
+    gradients of some hidden units of one expert equal the corresponding
+    entries of backward()."""
+    L = random_layer(50 + gate, T=40, d=8, h=12, E=5, k=2, act=act, S=S, bias=True,
+                     expert_bias=(act == GELU), gate=gate)
+    dy = np.random.default_rng(51).standard_normal((40, 8))
+    full = B.backward(L, dy, importance_weight=imp_w)
+    toks = [0, 7, 19, 39]
+    np.testing.assert_allclose(B.dx_rows(L, dy, toks, imp_w), full["x"][toks],
+                               rtol=1e-10, atol=1e-12)
+    units = np.array([0, 5, 11])
+    for e in list(range(5)) + ([5] if S else []):
+        g = B.expert_unit_grads(L, dy, e, units)
+        up = full["w_up_shared"][0] if e == 5 else full["w_up"][e]
+        down = full["w_down_shared"][0] if e == 5 else full["w_down"][e]
+        if act == SWIGLU:
+            np.testing.assert_allclose(g["w_up"][0], up[units], rtol=1e-10, atol=1e-12)
+            np.testing.assert_allclose(g["w_up"][1], up[units + 12], rtol=1e-10, atol=1e-12)
+        else:
+            np.testing.assert_allclose(g["w_up"], up[units], rtol=1e-10, atol=1e-12)
+            np.testing.assert_allclose(g["b_up"], full["b_up"][e][units], rtol=1e-10,
+                                       atol=1e-12)
+        np.testing.assert_allclose(g["w_down"], down[:, units], rtol=1e-10, atol=1e-12)
