@@ -127,19 +127,15 @@ def _noisy_scores(p: dict, s: torch.Tensor, noise: torch.Tensor):
     return s + noise * sig, sig
 
 
-def forward(layer, p: dict, idx: np.ndarray, keep: Optional[np.ndarray] = None,
-            assign: Optional[np.ndarray] = None, noisy: Optional[dict] = None):
-    """(y [T, d], gate values [T, k], Importance [E], Load [E] or None) as
-    float64 tensors for the fixed selection idx [T, k]; assign [T*k]
-    (next-choice re-routing): the expert that computes each slot, -1
-    dropped, the gate values still those of idx; noisy: dict(noise [T, E],
-    kth [T, E] or None) for the noisy gate."""
+def _gates(layer, p: dict, idx: np.ndarray, noisy: Optional[dict] = None):
+    """(gate values [T, k], Importance [E], smooth Load [E] or None) of the
+    fixed selection idx, float64, from x and the router weights in p."""
     cfg = layer.cfg
-    T, k, E = cfg.T, cfg.k, cfg.E
-    x = p["x"]
-    raw = x @ p["w_gate"].T
+    T, E = p["x"].shape[0], cfg.E
+    raw = p["x"] @ p["w_gate"].T
     s = raw + p["b_gate"] if "b_gate" in p else raw
     it = torch.from_numpy(np.ascontiguousarray(idx, np.int64))
+    gate = getattr(cfg, "gate", 0)
     load = None
     if noisy is not None:   # softmax over the kept noisy scores; smooth Load
         H, sig = _noisy_scores(p, s, _f64(noisy["noise"]))
@@ -151,8 +147,27 @@ def forward(layer, p: dict, idx: np.ndarray, keep: Optional[np.ndarray] = None,
                                                                            np.int64)))
             z = (s - thr) / sig
             load = (0.5 * torch.special.erfc(-z / np.sqrt(2.0))).sum(0)
-    else:
-        g, _ = forward_gates(layer, p, idx)
+    elif gate == 1:   # the bias steers the selection only
+        g = torch.softmax(torch.gather(raw, 1, it), dim=1)
+    elif gate == 2:   # softmax over all E, read at the kept experts
+        g = torch.gather(torch.softmax(s, dim=1), 1, it)
+    else:             # softmax over the kept k
+        g = torch.softmax(torch.gather(s, 1, it), dim=1)
+    imp = torch.zeros(E, dtype=torch.float64).index_add(0, it.reshape(-1), g.reshape(-1))
+    return g, imp, load
+
+
+def forward(layer, p: dict, idx: np.ndarray, keep: Optional[np.ndarray] = None,
+            assign: Optional[np.ndarray] = None, noisy: Optional[dict] = None):
+    """(y [T, d], gate values [T, k], Importance [E], Load [E] or None) as
+    float64 tensors for the fixed selection idx [T, k]; assign [T*k]
+    (next-choice re-routing): the expert that computes each slot, -1
+    dropped, the gate values still those of idx; noisy: dict(noise [T, E],
+    kth [T, E] or None) for the noisy gate."""
+    cfg = layer.cfg
+    T, k, E = cfg.T, cfg.k, cfg.E
+    x = p["x"]
+    g, imp, load = _gates(layer, p, idx, noisy)
     gk = g
     if keep is not None:
         gk = g * torch.from_numpy(np.asarray(keep, np.float64).reshape(T, k))
@@ -167,7 +182,6 @@ def forward(layer, p: dict, idx: np.ndarray, keep: Optional[np.ndarray] = None,
         y = y.index_add(0, ts, gk[ts, torch.from_numpy(j_sel)].unsqueeze(1) * out)
     if cfg.S:
         y = y + _ffn(cfg, p, E, x)
-    imp = torch.zeros(E, dtype=torch.float64).index_add(0, it.reshape(-1), g.reshape(-1))
     return y, g, imp, load
 
 
@@ -222,38 +236,29 @@ def backward(layer, dy: np.ndarray, keep: Optional[np.ndarray] = None,
 # hidden units of one expert has the same gradient in those units' weights).
 
 def _router_params(layer) -> dict:
-    """x, w_gate (and b_gate) as float64 tensors, no expert weights."""
+    """x, w_gate (and b_gate, w_noise) as float64 tensors, no expert weights."""
     p = {"x": _f64(layer.x), "w_gate": _f64(layer.w_gate)}
-    if getattr(layer, "b_gate", None) is not None:
-        p["b_gate"] = _f64(layer.b_gate)
+    for n in ("b_gate", "w_noise"):
+        if getattr(layer, n, None) is not None:
+            p[n] = _f64(getattr(layer, n))
     return p
 
 
-def importance_gradient(layer, importance_weight: float, idx=None) -> np.ndarray:
-    """d (w * CV^2(Importance)) / d Importance at the whole batch, float64
-    [E] (the oracle's routing unless idx is given)."""
+def balance_gradients(layer, importance_weight: float, idx=None, noisy=None,
+                      load_weight: float = 0.0):
+    """d (w_imp CV^2(Importance) + w_load CV^2(Load)) / d (Importance, Load)
+    at the whole batch, float64 [E] each (the oracle's routing unless idx is
+    given; noisy: dict(noise, kth) of the noisy gate)."""
     if idx is None:
         idx, _, _ = _route(layer)
-    imp = forward_gates(layer, _router_params(layer), idx)[1].detach().requires_grad_(True)
-    (g,) = torch.autograd.grad(importance_weight * cv2(imp), [imp])
-    return g.numpy()
-
-
-def forward_gates(layer, p: dict, idx: np.ndarray):
-    """(gate values [T, k], Importance [E]) of the fixed selection idx."""
-    cfg = layer.cfg
-    raw = p["x"] @ p["w_gate"].T
-    s = raw + p["b_gate"] if "b_gate" in p else raw
-    it = torch.from_numpy(np.ascontiguousarray(idx, np.int64))
-    gate = getattr(cfg, "gate", 0)
-    if gate == 1:     # the bias steers the selection only
-        g = torch.softmax(torch.gather(raw, 1, it), dim=1)
-    elif gate == 2:   # softmax over all E, read at the kept experts
-        g = torch.gather(torch.softmax(s, dim=1), 1, it)
-    else:             # softmax over the kept k
-        g = torch.softmax(torch.gather(s, 1, it), dim=1)
-    imp = torch.zeros(cfg.E, dtype=torch.float64).index_add(0, it.reshape(-1), g.reshape(-1))
-    return g, imp
+    _, imp, load = _gates(layer, _router_params(layer), idx, noisy)
+    imp = imp.detach().requires_grad_(True)
+    (gi,) = torch.autograd.grad(importance_weight * cv2(imp), [imp])
+    gl = torch.zeros_like(imp)
+    if load is not None and load_weight:
+        load = load.detach().requires_grad_(True)
+        (gl,) = torch.autograd.grad(load_weight * cv2(load), [load])
+    return gi.numpy(), gl.numpy()
 
 
 class _TokenSubset:
@@ -265,14 +270,23 @@ class _TokenSubset:
 
 
 def dx_rows(layer, dy: np.ndarray, tokens, importance_weight: float = 0.0,
-            idx: Optional[np.ndarray] = None) -> np.ndarray:
+            idx: Optional[np.ndarray] = None, noise: Optional[np.ndarray] = None,
+            load_weight: float = 0.0, selection=None) -> np.ndarray:
     """Rows `tokens` of d loss / d x (loss of backward(), no capacity),
-    float64 [len(tokens), d].  Only the experts those tokens use are taken
-    to float64."""
-    if idx is None:
-        idx, _, _ = _route(layer)
+    float64 [len(tokens), d]; the balance terms are linearised at the whole
+    batch.  noise: the noisy gate with these draws (selection: its
+    noisy_selection(), computed if None).  Only the experts those tokens use
+    are taken to float64."""
     tokens = np.asarray(tokens, np.int64)
-    gimp = torch.from_numpy(importance_gradient(layer, importance_weight, idx))
+    noisy = noisy_sub = None
+    if noise is not None:
+        idx, kth = selection if selection is not None else noisy_selection(layer, noise)
+        noisy = dict(noise=np.asarray(noise, np.float32), kth=kth)
+        noisy_sub = dict(noise=noisy["noise"][tokens], kth=None if kth is None else kth[tokens])
+    elif idx is None:
+        idx, _, _ = _route(layer)
+    gi, gl = balance_gradients(layer, importance_weight, idx, noisy, load_weight)
+    gimp, gload = torch.from_numpy(gi), torch.from_numpy(gl)
     sub = _TokenSubset(layer, tokens)
     p = _router_params(layer)
     p["x"] = _f64(sub.x).requires_grad_(True)
@@ -285,14 +299,17 @@ def dx_rows(layer, dy: np.ndarray, tokens, importance_weight: float = 0.0,
         a = getattr(layer, n, None)
         if a is not None and np.asarray(a).size:
             p[n] = _f64(a)
-    y, _, imp, _ = forward(sub, p, idx[tokens])
+    y, _, imp, load = forward(sub, p, idx[tokens], noisy=noisy_sub)
     L = (_f64(np.asarray(dy)[tokens]) * y).sum() + (gimp * imp).sum()
+    if load is not None:
+        L = L + (gload * load).sum()
     (gx,) = torch.autograd.grad(L, [p["x"]])
     return gx.numpy()
 
 
 def expert_unit_grads(layer, dy: np.ndarray, e: int, units, idx: Optional[np.ndarray] = None,
-                      w: Optional[np.ndarray] = None) -> dict:
+                      w: Optional[np.ndarray] = None, noise: Optional[np.ndarray] = None,
+                      selection=None) -> dict:
     """Gradients of the loss of backward() (no capacity) in the weights of
     hidden units `units` of expert e (e == E: the shared expert), float64:
     'w_up' [len(units), d] (SwiGLU: [2, len(units), d], gate rows then up
@@ -300,7 +317,8 @@ def expert_unit_grads(layer, dy: np.ndarray, e: int, units, idx: Optional[np.nda
     expert with biases.  The expert's rows: every slot routed to it with its
     gate value (the shared expert: every token, weight 1).  idx: the
     selection (the oracle's routing if None); w: its gate values [T, k]
-    (those of forward()'s graph if None)."""
+    (those of forward()'s graph if None); noise: the noisy gate with these
+    draws (selection: its noisy_selection(), computed if None)."""
     cfg = layer.cfg
     units = np.asarray(units, np.int64)
     xs = _f64(layer.x)
@@ -312,10 +330,14 @@ def expert_unit_grads(layer, dy: np.ndarray, e: int, units, idx: Optional[np.nda
         w2 = _f64(layer.w_down_shared)[0]
         b1 = None
     else:
-        if idx is None:
+        noisy = None
+        if noise is not None:
+            idx, kth = selection if selection is not None else noisy_selection(layer, noise)
+            noisy = dict(noise=np.asarray(noise, np.float32), kth=kth)
+        elif idx is None:
             idx, _, _ = _route(layer)
         if w is None:   # the gate values of backward()'s graph
-            w = forward_gates(layer, _router_params(layer), idx)[0].numpy()
+            w = _gates(layer, _router_params(layer), idx, noisy)[0].numpy()
         t_sel, j_sel = np.nonzero(idx == e)
         rows_t = t_sel
         gw = torch.from_numpy(np.asarray(w, np.float64)[t_sel, j_sel])

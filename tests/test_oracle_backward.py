@@ -230,3 +230,24 @@ def test_gradient_slices_equal_the_whole_graph(act, S, gate, imp_w):
             np.testing.assert_allclose(g["b_up"], full["b_up"][e][units], rtol=1e-10,
                                        atol=1e-12)
         np.testing.assert_allclose(g["w_down"], down[:, units], rtol=1e-10, atol=1e-12)
+
+
+@pytest.mark.parametrize("k,E", [(2, 5), (3, 3)])
+def test_noisy_slices_equal_the_whole_graph(k, E):
+    """The slices with the noisy gate: Importance and the smooth Load
+    linearised at the whole batch give the whole graph's dx rows; the
+    hidden-unit slices its expert weight gradients."""
+    L, noise = _noisy_layer(60 + E, T=30, E=E, k=k)
+    dy = np.random.default_rng(61).standard_normal((30, 6))
+    full = B.backward(L, dy, importance_weight=0.3, noise=noise, load_weight=0.7)
+    toks = [0, 11, 29]
+    got = B.dx_rows(L, dy, toks, 0.3, noise=noise, load_weight=0.7)
+    np.testing.assert_allclose(got, full["x"][toks], rtol=1e-10, atol=1e-12)
+    units = np.array([0, 4])
+    for e in range(E):
+        g = B.expert_unit_grads(L, dy, e, units, noise=noise)
+        np.testing.assert_allclose(g["w_up"][0], full["w_up"][e][units], rtol=1e-10, atol=1e-12)
+        np.testing.assert_allclose(g["w_up"][1], full["w_up"][e][units + 5], rtol=1e-10,
+                                   atol=1e-12)
+        np.testing.assert_allclose(g["w_down"], full["w_down"][e][:, units], rtol=1e-10,
+                                   atol=1e-12)
