@@ -345,6 +345,9 @@ typedef struct {
   float *dw_noise;
 } moe_noisy_grad_t;
 
+/* Workspace bytes of moe_backward for cfg (bf16 layers), enough for every
+ * gate mode and for the noisy gate (whose use the configuration does not
+ * name).  Pure host; *bytes is 0 when T == 0. */
 moe_status_t moe_backward_workspace_bytes(const moe_config_t *cfg, size_t *bytes);
 
 moe_status_t moe_backward(const moe_config_t *cfg, const moe_weights_t *w,
