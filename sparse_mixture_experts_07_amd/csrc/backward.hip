@@ -506,7 +506,7 @@ __global__ __launch_bounds__(kWave) void bwd_noisy_ds_kernel(
   for (int q = 0; q < Q; ++q) a[q] = z[q] = 0.0f;
   int jk = -1, jk1 = -1;
   if (gload && k < E) {
-    jk = it[k - 1];
+    jk = min(max(it[k - 1], 0), E - 1);   // clamped: a corrupt index stays in the row
     // the (k+1)-th: the best entry outside the kept k (H descending, index
     // ascending), a wavefront arg-max
     bool ba = false;
@@ -532,9 +532,12 @@ __global__ __launch_bounds__(kWave) void bwd_noisy_ds_kernel(
         be = oe;
       }
     }
-    jk1 = be;
+    // none only if the kept slots name every expert (a corrupt selection):
+    // then no entry takes the kept experts' term, and the load stays in range
+    jk1 = ba ? be : -1;
+    const int j1 = ba ? be : jk;
     const float hk = fmaf(noise[row + jk], scale[row + jk], clean[row + jk]);
-    const float hk1 = fmaf(noise[row + jk1], scale[row + jk1], clean[row + jk1]);
+    const float hk1 = fmaf(noise[row + j1], scale[row + j1], clean[row + j1]);
     constexpr float kInvSqrt2Pi = 0.3989422804014327f;
 #pragma unroll
     for (int q = 0; q < Q; ++q) {
