@@ -256,7 +256,10 @@ def main():
     # WRITE_SIZE counters, scaled by the counters of a plain 1 GiB copy;
     # null when not measured for these kernel sources
     roof["traffic"] = None
-    if args.traffic and os.path.exists(args.traffic):
+    # measured for the default step of each workload (no capacity, default
+    # gate, clean gate, inference up projection)
+    default_step = not (cap or cfg.gate or args.noisy or args.backward)
+    if default_step and args.traffic and os.path.exists(args.traffic):
         rec = json.load(open(args.traffic)).get(args.workload)
         if rec and rec.get("gemm_source_sha256") == source_digest():
             roof["traffic"] = rec["traffic_bytes"]
