@@ -216,15 +216,19 @@ def main():
            for _ in range(args.steps)]
     loop0 = torch.cuda.Event(enable_timing=True)
     loop1 = torch.cuda.Event(enable_timing=True)
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]   # step ends
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     loop0.record()
     for i in range(args.steps):
         step(evs[i])
+        marks[i].record()
     loop1.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_step = loop0.elapsed_time(loop1) / args.steps
+    step_ms = [(loop0 if i == 0 else marks[i - 1]).elapsed_time(marks[i])
+               for i in range(args.steps)]
     up_ms = [a.elapsed_time(b) for a, b in evs]
     up_avg = float(np.mean(up_ms))
 
@@ -286,9 +290,17 @@ def main():
         t1 = time.perf_counter()
         oracle.forward_tokens(L, sample, keep=keep, assign=assign)
         el = time.perf_counter() - t1
+        model = "unknown CPU"
+        try:
+            with open("/proc/cpuinfo") as fh:
+                model = next((l.split(":", 1)[1].strip() for l in fh
+                              if l.startswith("model name")), model)
+        except OSError:
+            pass
         cpu = {"value": n / el, "unit": "tokens/s", "cores": nthr, "kind": "oracle",
                "sample": f"{n} of {T} tokens (evenly spaced), full routing + "
-                         f"expert FFNs + combine per token, {el:.1f} s"}
+                         f"expert FFNs + combine per token, {el:.1f} s on {nthr} "
+                         f"OpenMP threads of {model} ({os.cpu_count()} logical CPUs)"}
 
     out = {
         "metric": METRIC,
@@ -298,6 +310,8 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": ms_step,
+        "step_ms": {"median": float(np.median(step_ms)), "min": float(np.min(step_ms)),
+                    "p90": float(np.percentile(step_ms, 90))},
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
