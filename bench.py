@@ -146,7 +146,8 @@ def main():
             B.moe_route_noisy(c, dl.x, dl.w_gate, dl.b_gate, w_noise, noise, clean, nscale,
                               idx, tw, counts, nimp, nload, ncv2, ws)
         else:
-            B.moe_route(c, dl.x, dl.w_gate, dl.b_gate, idx, tw, counts, logits)
+            # counts come from the grouping, as in moe_forward
+            B.moe_route(c, dl.x, dl.w_gate, dl.b_gate, idx, tw, None, logits)
 
     if args.backward:
         if cfg.dtype != synthetic.BF16:
@@ -176,7 +177,7 @@ def main():
     def step(ev=None):
         route()
         B.moe_permute(c, idx, tw, dl.x, offsets, perm_src, pos, imp, stats, x_perm, ws,
-                      logits=logits)
+                      logits=logits, counts=None if args.noisy else counts)
         if ev is not None:
             ev[0].record()
         if args.backward:   # the training forward keeps the pre-activations

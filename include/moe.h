@@ -42,7 +42,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 7
+#define MOE_ABI_VERSION 8
 
 typedef enum {
   MOE_OK = 0,
@@ -148,7 +148,8 @@ moe_status_t moe_grouped_rows(const moe_config_t *cfg, int64_t *rows);
  *            equal scores keep the lower index first (a stable sort)
  *   topk_w   [T, k] fp32   (out) the gate values of cfg->gate; default
  *            exp(s_j - s_0) / sum_i exp(s_i - s_0) over the kept i
- *   counts   [E] int32     (out) tokens routed to each expert (Stats)
+ *   counts   [E] int32 or NULL (out) tokens routed to each expert (Stats);
+ *            NULL skips them (moe_permute can count them instead)
  *   logits   [T, E] fp32 or NULL (out) router scores: for each (t, e)
  *            s = +0; s = fma(x[t,i], W_g[e,i], s) for i = 0..d-1 in order;
  *            s = s + b_g[e]; all in fp32 (the biased score, in every
@@ -214,6 +215,9 @@ moe_status_t moe_route_noisy(const moe_config_t *cfg, const void *x,
  *   stats      [3] double or NULL (out) CV^2(Importance), CV^2(Load) with
  *              Load = counts, and the load-balance loss E*sum_e f_e^2 of the
  *              Go chapter's section 3 (population variance; 0 if empty)
+ *   counts     [E] int32 or NULL (out) assignments per expert (every one,
+ *              dropped or not: moe_route's counts), from the grouping's
+ *              histogram
  *   x_perm     [T*k, d] dtype (out) x_perm[p] = x[perm_src[p]] for
  *              p < offsets[E]
  *   ws         workspace >= moe_workspace_bytes() */
@@ -221,7 +225,7 @@ moe_status_t moe_permute(const moe_config_t *cfg, const int32_t *topk_idx,
                          const float *topk_w, const float *logits, const void *x,
                          int32_t *offsets,
                          int32_t *perm_src, int32_t *pos, float *importance,
-                         double *stats, void *x_perm, void *ws,
+                         double *stats, int32_t *counts, void *x_perm, void *ws,
                          size_t ws_bytes, hipStream_t stream);
 
 /* Up projection + activation of every expert group (grouped GEMM on bf16

@@ -89,7 +89,7 @@ def lib():
             "moe_expert_up_train": [P, P, P, P, P, P, P, P],
             "moe_route_noisy": [P, P, P, P, P, P, P, P, P, P, P, P, P, P, P,
                                 C.c_size_t, P],
-            "moe_permute": [P, P, P, P, P, P, P, P, P, P, P, P, C.c_size_t, P],
+            "moe_permute": [P, P, P, P, P, P, P, P, P, P, P, P, P, C.c_size_t, P],
             "moe_expert_up": [P, P, P, P, P, P, P],
             "moe_expert_down": [P, P, P, P, P, P],
             "moe_expert_ffn": [P, P, P, P, P, P, P, C.c_size_t, P],
@@ -260,11 +260,12 @@ def moe_route_noisy(cfg, x, w_gate, b_gate, w_noise, noise, clean_logits, noise_
 
 
 def moe_permute(cfg, topk_idx, topk_w, x, offsets, perm_src, pos, importance,
-                stats, x_perm, ws, ws_bytes=None, stream=None, logits=None) -> None:
+                stats, x_perm, ws, ws_bytes=None, stream=None, logits=None,
+                counts=None) -> None:
     nb = _nbytes(ws) if ws_bytes is None and ws is not None else (ws_bytes or 0)
     _check("moe_permute", lib().moe_permute(
         C.byref(cfg), _ptr(topk_idx), _ptr(topk_w), _ptr(logits), _ptr(x), _ptr(offsets),
-        _ptr(perm_src), _ptr(pos), _ptr(importance), _ptr(stats), _ptr(x_perm),
+        _ptr(perm_src), _ptr(pos), _ptr(importance), _ptr(stats), _ptr(counts), _ptr(x_perm),
         _ptr(ws), nb, _stream(stream)))
 
 

@@ -266,7 +266,7 @@ moe_status_t moe_route(const moe_config_t *cfg, const void *x, const float *w_ga
                        int32_t *counts, float *logits, hipStream_t stream) {
   moe_status_t st = check_cfg(cfg);
   if (st != MOE_OK) return st;
-  if (!dev_ok(counts)) return MOE_ERR_INVALID_ARGUMENT;
+  if (!opt_ok(counts)) return MOE_ERR_INVALID_ARGUMENT;
   const int T = (int)cfg->num_tokens;
   if (T > 0 && (!dev_ok(x) || !dev_ok(w_gate) || !opt_ok(b_gate) ||
                 !dev_ok(topk_idx) || !dev_ok(topk_w) || !opt_ok(logits)))
@@ -317,16 +317,22 @@ moe_status_t moe_route_noisy(const moe_config_t *cfg, const void *x, const float
   return hip_status(e);
 }
 
-moe_status_t moe_permute(const moe_config_t *cfg, const int32_t *topk_idx,
-                         const float *topk_w, const float *logits, const void *x,
-                         int32_t *offsets,
-                         int32_t *perm_src, int32_t *pos, float *importance,
-                         double *stats, void *x_perm, void *ws, size_t ws_bytes,
-                         hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+// moe_permute; counts_out (or NULL): the assignments per expert from the
+// grouping's histogram (moe_forward takes the counts from here instead of
+// zeroing and accumulating them in the router)
+moe_status_t permute_impl(const moe_config_t *cfg, const int32_t *topk_idx,
+                          const float *topk_w, const float *logits, const void *x,
+                          int32_t *offsets, int32_t *perm_src, int32_t *pos, float *importance,
+                          double *stats, void *x_perm, void *ws, size_t ws_bytes,
+                          hipStream_t stream, int32_t *counts_out) {
   moe_status_t st = check_cfg(cfg);
   if (st != MOE_OK) return st;
   const int T = (int)cfg->num_tokens;
-  if (!dev_ok(offsets) || !dev_ok(importance) || !opt_ok(stats))
+  if (!dev_ok(offsets) || !dev_ok(importance) || !opt_ok(stats) || !opt_ok(counts_out))
     return MOE_ERR_INVALID_ARGUMENT;
   if (T > 0 && (!dev_ok(topk_idx) || !dev_ok(topk_w) || !dev_ok(x) ||
                 !dev_ok(perm_src) || !dev_ok(pos) || !dev_ok(x_perm) || !dev_ok(ws) ||
@@ -337,6 +343,8 @@ moe_status_t moe_permute(const moe_config_t *cfg, const int32_t *topk_idx,
   clear_pending_error();
   if (T == 0) {
     hipError_t e = moe::launch_fill_i32(offsets, cfg->num_experts + 1, 0, stream);
+    if (e == hipSuccess && counts_out)
+      e = moe::launch_fill_i32(counts_out, cfg->num_experts, 0, stream);
     if (e != hipSuccess) return MOE_ERR_HIP;
   }
   if (T > 0 && reroutes(cfg)) {
@@ -347,13 +355,27 @@ moe_status_t moe_permute(const moe_config_t *cfg, const int32_t *topk_idx,
         topk_idx, topk_w, logits, x, T, cfg->top_k, cfg->num_experts, cfg->capacity,
         (int)(cfg->d_model * elem_bytes(cfg)), offsets, perm_src, pos, importance, stats,
         x_perm, at<int32_t>(ws, L.hist), at<int32_t>(ws, L.full_off), at<float>(ws, L.perm_w),
-        r, stream));
+        r, stream, counts_out));
   }
   return hip_status(moe::launch_permute(
       topk_idx, topk_w, x, T, cfg->top_k, cfg->num_experts, cfg->capacity,
       (int)(cfg->d_model * elem_bytes(cfg)), offsets, perm_src, pos, importance, stats,
       x_perm, T ? at<int32_t>(ws, L.hist) : nullptr, T ? at<int32_t>(ws, L.full_off) : nullptr,
-      T ? at<float>(ws, L.perm_w) : nullptr, stream));
+      T ? at<float>(ws, L.perm_w) : nullptr, stream, counts_out));
+}
+
+}  // namespace
+
+extern "C" {
+
+moe_status_t moe_permute(const moe_config_t *cfg, const int32_t *topk_idx,
+                         const float *topk_w, const float *logits, const void *x,
+                         int32_t *offsets,
+                         int32_t *perm_src, int32_t *pos, float *importance,
+                         double *stats, int32_t *counts, void *x_perm, void *ws,
+                         size_t ws_bytes, hipStream_t stream) {
+  return permute_impl(cfg, topk_idx, topk_w, logits, x, offsets, perm_src, pos, importance,
+                      stats, x_perm, ws, ws_bytes, stream, counts);
 }
 
 moe_status_t moe_expert_up(const moe_config_t *cfg, const moe_weights_t *w,
@@ -476,11 +498,12 @@ moe_status_t moe_forward(const moe_config_t *cfg, const moe_weights_t *w, const 
   void *hidden = at<char>(ws, L.hidden);
   void *y_perm = at<char>(ws, L.y_perm);
   float *logits = reroutes(cfg) ? at<float>(ws, L.logits) : nullptr;   // next choices
-  if ((st = moe_route(cfg, x, w->w_gate, w->b_gate, topk_idx, topk_w, counts, logits,
+  // the router without counts: the grouping's histogram gives them
+  if ((st = moe_route(cfg, x, w->w_gate, w->b_gate, topk_idx, topk_w, nullptr, logits,
                       stream)) != MOE_OK)
     return st;
-  if ((st = moe_permute(cfg, topk_idx, topk_w, logits, x, offsets, perm_src, pos, importance,
-                        stats, x_perm, ws, L.permute_end, stream)) != MOE_OK)
+  if ((st = permute_impl(cfg, topk_idx, topk_w, logits, x, offsets, perm_src, pos, importance,
+                         stats, x_perm, ws, L.permute_end, stream, counts)) != MOE_OK)
     return st;
   if ((st = moe_expert_up(cfg, w, x_perm, x, offsets, hidden, stream)) != MOE_OK) return st;
   if ((st = moe_expert_down(cfg, w, hidden, offsets, y_perm, stream)) != MOE_OK) return st;

@@ -55,7 +55,8 @@ __global__ __launch_bounds__(kPermThreads) void perm_hist_kernel(
 // starts over every assignment; offsets: over the kept ones (capacity cap).
 __global__ __launch_bounds__(kPermThreads) void perm_scan_kernel(
     int32_t *__restrict__ hist, int nseg, int E, int n, int cap,
-    int32_t *__restrict__ full_off, int32_t *__restrict__ offsets) {
+    int32_t *__restrict__ full_off, int32_t *__restrict__ offsets,
+    int32_t *__restrict__ counts_out) {
   __shared__ int sc[kPermThreads], kc[kPermThreads];
   const int e = threadIdx.x;
   int total = 0;
@@ -80,6 +81,7 @@ __global__ __launch_bounds__(kPermThreads) void perm_scan_kernel(
   }
   const int start = sc[e] - total;  // exclusive
   if (e < E) {
+    if (counts_out) counts_out[e] = total;
     full_off[e] = start;
     offsets[e] = kc[e] - min(total, cap);
     for (int s = 0; s < nseg; ++s) hist[(int64_t)s * E + e] += start;
@@ -240,7 +242,8 @@ __global__ __launch_bounds__(kFusedThreads) void perm_fused_kernel(
     const int32_t *__restrict__ idx, const float *__restrict__ w, int n, int k,
     int E, int cap, int32_t *__restrict__ offsets, int32_t *__restrict__ pos,
     int32_t *__restrict__ perm_src, float *__restrict__ perm_w,
-    float *__restrict__ importance, double *__restrict__ stats) {
+    float *__restrict__ importance, double *__restrict__ stats,
+    int32_t *__restrict__ counts_out) {
   constexpr int NW = kFusedThreads / kWave;
   __shared__ int h[kMaxExperts];
   __shared__ int off[kMaxExperts + 1];    // full group starts
@@ -267,6 +270,7 @@ __global__ __launch_bounds__(kFusedThreads) void perm_fused_kernel(
     const int ex = block_exclusive_scan<kFusedThreads>(c, scan_tmp, &total);
     const int kex = block_exclusive_scan<kFusedThreads>(min(c, cap), scan_tmp, &ktotal);
     if (tid < E) {
+      if (counts_out) counts_out[tid] = c;
       off[tid] = ex;
       koff[tid] = kex;
       offsets[tid] = kex;
@@ -483,18 +487,20 @@ hipError_t launch_permute(const int32_t *idx, const float *w, const void *x,
                           int32_t *offsets, int32_t *perm_src, int32_t *pos,
                           float *importance, double *stats, void *x_perm,
                           int32_t *hist, int32_t *full_off, float *perm_w,
-                          hipStream_t s) {
+                          hipStream_t s, int32_t *counts_out) {
   const int n = T * k;
   if (n == 0) return launch_zero_stats(importance, E, stats, s);
   const int cap = capacity > 0 ? capacity : n;
   const int blocks = n < 8192 ? n : 8192;
   if (n <= kFusedMax) {
     perm_fused_kernel<<<1, kFusedThreads, 0, s>>>(idx, w, n, k, E, cap, offsets, pos,
-                                                  perm_src, perm_w, importance, stats);
+                                                  perm_src, perm_w, importance, stats,
+                                                  counts_out);
   } else {
     const int nseg = perm_num_segments(n);
     perm_hist_kernel<<<nseg, kPermThreads, 0, s>>>(idx, n, E, hist);
-    perm_scan_kernel<<<1, kPermThreads, 0, s>>>(hist, nseg, E, n, cap, full_off, offsets);
+    perm_scan_kernel<<<1, kPermThreads, 0, s>>>(hist, nseg, E, n, cap, full_off, offsets,
+                                                counts_out);
     perm_scatter_kernel<<<nseg, kPermThreads, 0, s>>>(idx, w, n, k, E, cap, hist, full_off,
                                                       offsets, pos, perm_src, perm_w);
     if (importance) {   // NULL: grouping only
@@ -515,14 +521,15 @@ hipError_t launch_permute_reroute(const int32_t *idx, const float *w, const floa
                                   int row_bytes, int32_t *offsets, int32_t *perm_src,
                                   int32_t *pos, float *importance, double *stats,
                                   void *x_perm, int32_t *hist, int32_t *full_off,
-                                  float *perm_w, const RerouteScratch &r, hipStream_t s) {
+                                  float *perm_w, const RerouteScratch &r, hipStream_t s,
+                                  int32_t *counts_out) {
   const int n = T * k;
   if (n == 0) return launch_zero_stats(importance, E, stats, s);
   hipError_t err;
   // 1. the drop rule on the top k: kept slots, Importance, statistics
   if ((err = launch_permute(idx, w, nullptr, T, k, E, capacity, row_bytes, offsets, perm_src,
-                            r.pos_a, importance, stats, nullptr, hist, full_off, perm_w, s)) !=
-      hipSuccess)
+                            r.pos_a, importance, stats, nullptr, hist, full_off, perm_w, s,
+                            counts_out)) != hipSuccess)
     return err;
   // 2. offers, and their ranks within each expert's offers (flat order)
   reroute_offer_kernel<<<T, kWave, 0, s>>>(idx, r.pos_a, logits, k, E, r.cand);

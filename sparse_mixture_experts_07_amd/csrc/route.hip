@@ -349,7 +349,7 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(
   }
   __syncthreads();
   for (int e = tid; e < E; e += kRouteThreads)
-    if (cnt[e]) atomicAdd(counts + e, cnt[e]);
+    if (counts && cnt[e]) atomicAdd(counts + e, cnt[e]);
 }
 
 __global__ void fill_i32_kernel(int32_t *p, int n, int32_t v) {
@@ -496,7 +496,7 @@ __global__ __launch_bounds__(NTH) void route_direct_kernel(
   }
   __syncthreads();
   for (int i = threadIdx.x; i < E; i += NTH)
-    if (cnt[i]) atomicAdd(counts + i, cnt[i]);
+    if (counts && cnt[i]) atomicAdd(counts + i, cnt[i]);
 }
 
 // Workgroups of four wavefronts; one wavefront each when there are fewer
@@ -674,7 +674,7 @@ __global__ __launch_bounds__(NWV * kWave) void route_lane_kernel(
   }
   __syncthreads();
   for (int i = threadIdx.x; i < E; i += G::NTH)
-    if (cnt[i]) atomicAdd(counts + i, cnt[i]);
+    if (counts && cnt[i]) atomicAdd(counts + i, cnt[i]);
 }
 
 template <typename XT, int EP, int NWV>
@@ -779,12 +779,13 @@ hipError_t launch_fill_i32(int32_t *p, int n, int32_t v, hipStream_t s) {
   return hipGetLastError();
 }
 
-// counts are zeroed here, then accumulated by the route kernel
+// counts are zeroed here, then accumulated by the route kernel; counts
+// NULL: no counts (the caller takes them from the grouping)
 hipError_t launch_route(bool bf16, int gate, const void *x, const float *wg,
                         const float *bg, int T, int d, int E, int k,
                         int32_t *idx, float *w, int32_t *counts, float *logits,
                         hipStream_t s) {
-  hipError_t err = launch_fill_i32(counts, E, 0, s);
+  hipError_t err = counts ? launch_fill_i32(counts, E, 0, s) : hipSuccess;
   if (err != hipSuccess || T == 0) return err;
   return bf16 ? launch_route_dt<uint16_t>(x, wg, bg, T, d, E, k, gate, idx, w, counts, logits, s)
               : launch_route_dt<float>(x, wg, bg, T, d, E, k, gate, idx, w, counts, logits, s);

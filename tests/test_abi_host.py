@@ -27,7 +27,7 @@ def test_library_exports_every_declared_entry_point():
     assert set(B.EXPORTS) == set(names), names
     for n in names:
         assert hasattr(lib, n), f"libmoe.so does not export {n}"
-    assert B.moe_abi_version() == 7
+    assert B.moe_abi_version() == 8
 
 
 def test_status_strings():
@@ -106,8 +106,8 @@ def test_every_entry_point_rejects_bad_config(name):
     calls = [
         L.moe_workspace_bytes(r, C.byref(C.c_size_t())),
         L.moe_route(r, FAKE, FAKE, None, FAKE, FAKE, FAKE, None, None),
-        L.moe_permute(r, FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, 1 << 40,
-                      None),
+        L.moe_permute(r, FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE, None, None, FAKE, FAKE,
+                      1 << 40, None),
         L.moe_expert_up(r, C.byref(w), FAKE, FAKE, FAKE, FAKE, None),
         L.moe_expert_down(r, C.byref(w), FAKE, FAKE, FAKE, None),
         L.moe_expert_ffn(r, C.byref(w), FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 40, None),
@@ -145,12 +145,12 @@ def test_pointer_and_workspace_checks():
     small = B.MOE_ERR_WORKSPACE_TOO_SMALL
     w = B.MoeWeights(FAKE, None, FAKE, None, FAKE, None, None, None)
     assert L.moe_forward(r, C.byref(w), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, 1024, None) == small
-    assert L.moe_permute(r, FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, 16,
-                         None) == small
+    assert L.moe_permute(r, FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE, None, None, FAKE, FAKE,
+                         16, None) == small
     # next-choice re-routing reads the router scores, and needs more scratch
     rr = _cfg(capacity=20, overflow=1)
-    assert L.moe_permute(C.byref(rr), FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE,
-                         FAKE, 1 << 40, None) == inv
+    assert L.moe_permute(C.byref(rr), FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE, None, None,
+                         FAKE, FAKE, 1 << 40, None) == inv
     n_drop = B.moe_workspace_bytes(_cfg(capacity=20))
     assert B.moe_workspace_bytes(rr) > n_drop
     assert B.moe_workspace_bytes(_cfg(overflow=1)) == B.moe_workspace_bytes(_cfg())

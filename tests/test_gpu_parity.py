@@ -239,8 +239,11 @@ def test_full_size_routing_and_permutation(name):
     imp = torch.empty(E, dtype=torch.float32, device=dev)
     stats = torch.empty(3, dtype=torch.float64, device=dev)
     x_perm = torch.empty((T * k, d), dtype=dl.x.dtype, device=dev)
-    B.moe_permute(c, gidx, gw, dl.x, offsets, perm_src, pos, imp, stats, x_perm, ws)
+    pcounts = torch.full((E,), -1, dtype=torch.int32, device=dev)
+    B.moe_permute(c, gidx, gw, dl.x, offsets, perm_src, pos, imp, stats, x_perm, ws,
+                  counts=pcounts)
     torch.cuda.synchronize()
+    assert np.array_equal(pcounts.cpu().numpy(), rc)   # the grouping's counts
     roff, rsrc, rpos = oracle.permute(cfg, ridx)
     assert np.array_equal(offsets.cpu().numpy(), roff)
     assert np.array_equal(perm_src.cpu().numpy(), rsrc)

@@ -95,9 +95,12 @@ def test_grouping_with_rerouting_bit_exact(name):
     gidx = torch.from_numpy(ridx).to(dev)
     gw = torch.from_numpy(rw.astype(np.float32)).to(dev)
     logits = torch.from_numpy(sc).to(dev)
+    pcounts = torch.full((E,), -1, dtype=torch.int32, device=dev)
     B.moe_permute(dl.cfg, gidx, gw, dl.x, offsets, perm_src, pos, imp, stats, x_perm, ws,
-                  logits=logits)
+                  logits=logits, counts=pcounts)
     torch.cuda.synchronize()
+    # the counts are the router's (every assignment, before any drop)
+    assert np.array_equal(pcounts.cpu().numpy(), oracle.counts(cfg, ridx, rw)[0])
     n = int(roff[-1])
     keep = oracle.capacity_keep(cfg, ridx, cap)
     assert int(keep.sum()) < n < T * k
