@@ -162,8 +162,7 @@ void clear_pending_error() { (void)hipGetLastError(); }
 
 // Backward workspace regions, each 256-byte aligned, in this order.
 struct BwdLayout {
-  size_t gimp, ds, dsp, ds_cols, poff, colsrc;
-  size_t off_all, src_all, pos_all, hist, full_off, perm_w;
+  size_t gimp, ds, poff, colsrc;
   size_t A, H, dyp, dH, dA, dxp, dypT, HT, dAT, xpT;
   size_t tm, dS, dU, gload, dxr, dpart, total;
 };
@@ -182,17 +181,8 @@ BwdLayout bwd_layout(const moe_config_t *c) {
   };
   take(L.gimp, 4 * E);
   take(L.ds, 4 * T * k);
-  take(L.dsp, 4 * T * k);
-  take(L.ds_cols, 4 * Rp);
   take(L.poff, 4 * (E + S + 1));
   take(L.colsrc, 4 * Rp);
-  const bool cap = c->capacity > 0;   // every assignment regrouped
-  take(L.off_all, cap ? 4 * (E + 1) : 0);
-  take(L.src_all, cap ? 4 * T * k : 0);
-  take(L.pos_all, cap ? 4 * T * k : 0);
-  take(L.hist, cap ? 4 * (int64_t)moe::perm_num_segments(T * k) * E : 0);
-  take(L.full_off, cap ? 4 * (E + 1) : 0);
-  take(L.perm_w, cap ? 4 * T * k : 0);
   take(L.A, 2 * R * nup);
   take(L.H, 2 * R * h);
   take(L.dyp, 2 * R * d);
@@ -203,8 +193,10 @@ BwdLayout bwd_layout(const moe_config_t *c) {
   take(L.HT, 2 * h * Rp);
   take(L.dAT, 2 * nup * Rp);
   take(L.xpT, 2 * d * Rp);
-  // dense router gradients: the softmax-all gate, and the noisy gate (which
-  // the configuration does not name, so the space is always there)
+  // router gradients: the dense score gradients of every gate; the dense
+  // share of dx and the noise-score gradients of the softmax-all and noisy
+  // gates (the configuration does not name the noisy gate, so the space is
+  // always there)
   take(L.tm, 4 * T);
   take(L.dS, 4 * T * E);
   take(L.dU, 4 * T * E);
@@ -623,18 +615,8 @@ moe_status_t moe_backward(const moe_config_t *cfg, const moe_weights_t *w, const
   moe::BwdBuffers b{};
   b.gimp = at<float>(ws, L.gimp);
   b.ds = at<float>(ws, L.ds);
-  b.dsp = at<float>(ws, L.dsp);
-  b.ds_cols = at<float>(ws, L.ds_cols);
   b.poff = at<int32_t>(ws, L.poff);
   b.colsrc = at<int32_t>(ws, L.colsrc);
-  if (cfg->capacity > 0) {
-    b.off_all = at<int32_t>(ws, L.off_all);
-    b.src_all = at<int32_t>(ws, L.src_all);
-    b.pos_all = at<int32_t>(ws, L.pos_all);
-    b.hist = at<int32_t>(ws, L.hist);
-    b.full_off = at<int32_t>(ws, L.full_off);
-    b.perm_w = at<float>(ws, L.perm_w);
-  }
   b.A = at<uint16_t>(ws, L.A);
   b.H = at<uint16_t>(ws, L.H);
   b.dyp = at<uint16_t>(ws, L.dyp);

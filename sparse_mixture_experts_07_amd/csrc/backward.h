@@ -11,22 +11,19 @@ int64_t bwd_padded_cols(int64_t T, int k, int E, int S);
 hipError_t launch_fill_f32(float *p, int64_t n, hipStream_t s);
 
 struct BwdBuffers {
-  float *gimp, *ds, *dsp, *ds_cols;
+  float *gimp, *ds;
   int32_t *poff, *colsrc;
-  // regrouping of every assignment (router gradient under a capacity)
-  int32_t *off_all, *src_all, *pos_all, *hist, *full_off;
-  float *perm_w;
   uint16_t *A, *H, *dyp, *dH, *dA, *dxp;
   uint16_t *dypT, *HT, *dAT, *xpT;
-  // softmax-all gate: per-token m [T], dense score gradients [T, E], the
-  // router's share of dx [T, d] (fp32)
+  // per-token m [T] and dense score gradients [T, E] (every gate); the
+  // router's share of dx [T, d] (fp32; softmax-all and noisy gates)
   float *tm, *dS, *dxr;
   float *dpart;   // [splits, E, d] partial dW_g when the plan has several splits
   float *dU, *gload;   // noisy gate: noise-score gradients [T, E], Load term [E]
 };
 
-// Token splits of the softmax-all gate's dense router weight gradient
-// (its partial sums take splits * E * d floats when splits > 1).
+// Token splits of the dense router weight gradient dS^T x (its partial sums
+// take splits * E * d floats when splits > 1).
 void bwd_dense_plan(int64_t T, int E, int d, int *splits, int *kchunk);
 
 struct BwdArgs {

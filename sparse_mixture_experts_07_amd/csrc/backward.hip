@@ -21,7 +21,6 @@
 // Every sum runs in a fixed order: results are deterministic.
 #include "common.h"
 #include "backward.h"
-#include "permute.h"
 
 #pragma clang fp contract(off)
 
@@ -314,62 +313,22 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_transpose_cols_kernel(
   }
 }
 
-// dsp[pos[f]] = ds[f] (grouped-row order), then ds_cols[j] = dsp[colsrc[j]]
-// for routed rows, 0 otherwise.
-__global__ void bwd_scatter_ds_kernel(const float *__restrict__ ds, const int32_t *__restrict__ pos,
-                                      int n, int routed, float *__restrict__ dsp) {
-  for (int f = blockIdx.x * blockDim.x + threadIdx.x; f < n; f += gridDim.x * blockDim.x) {
-    const int p = pos[f];
-    if (p >= 0 && p < routed) dsp[p] = ds[f];
-  }
-}
-
-__global__ void bwd_ds_cols_kernel(const float *__restrict__ dsp, const int32_t *__restrict__ colsrc,
-                                   int Rp, int routed, float *__restrict__ ds_cols) {
-  for (int j = blockIdx.x * blockDim.x + threadIdx.x; j < Rp; j += gridDim.x * blockDim.x) {
-    const int r = colsrc[j];
-    ds_cols[j] = (r >= 0 && r < routed) ? dsp[r] : 0.0f;
-  }
-}
-
-// out[g][c] = sum over group g's columns j of wcol[j] * at[c][j] (wcol NULL:
-// 1), for groups g < G; one wavefront per (g, c): lanes take columns
-// j = lane, lane + 64, ... in order, then a fixed butterfly.  OUT: float
-// (router gradients) or uint16_t (bf16 bias gradients).
-template <typename OUT>
+// out[g][c] = sum over group g's columns j of at[c][j] (bf16 bias
+// gradients), for groups g < G; one wavefront per (g, c): lanes take
+// columns j = lane, lane + 64, ... in order, then a fixed butterfly.
 __global__ __launch_bounds__(kWave) void bwd_rowsum_kernel(
     const uint16_t *__restrict__ at, int C, int Rp, const int32_t *__restrict__ poff,
-    const float *__restrict__ wcol, OUT *__restrict__ out) {
+    uint16_t *__restrict__ out) {
   const int c = blockIdx.x;
   const int g = blockIdx.y;
   const int lane = threadIdx.x;
   const int j0 = poff[g], j1 = poff[g + 1];
   const uint16_t *row = at + (int64_t)c * Rp;
   float s = 0.0f;
-  for (int j = j0 + lane; j < j1; j += kWave) {
-    const float v = __uint_as_float((uint32_t)row[j] << 16);
-    s += wcol ? wcol[j] * v : v;
-  }
+  for (int j = j0 + lane; j < j1; j += kWave) s += __uint_as_float((uint32_t)row[j] << 16);
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) s += __shfl_xor(s, off);
-  if (lane == 0) {
-    if constexpr (sizeof(OUT) == 2)
-      out[(int64_t)g * C + c] = (OUT)(pack_bf16x2(s, 0.0f) & 0xffffu);
-    else
-      out[(int64_t)g * C + c] = s;
-  }
-}
-
-// out[g] = sum over group g's columns of vals[j]; one wavefront per group.
-__global__ __launch_bounds__(kWave) void bwd_group_sum_kernel(
-    const float *__restrict__ vals, const int32_t *__restrict__ poff, float *__restrict__ out) {
-  const int g = blockIdx.x;
-  const int lane = threadIdx.x;
-  float s = 0.0f;
-  for (int j = poff[g] + lane; j < poff[g + 1]; j += kWave) s += vals[j];
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) s += __shfl_xor(s, off);
-  if (lane == 0) out[g] = s;
+  if (lane == 0) out[(int64_t)g * C + c] = (uint16_t)(pack_bf16x2(s, 0.0f) & 0xffffu);
 }
 
 // dx[t] = sum_j dX[pos_j] + dX[T*k + t] (shared) + sum_j ds_j W_g[i_j], fp32
@@ -399,7 +358,7 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dx_kernel(
       acc[2] += bf16_lo(v.y);
       acc[3] += bf16_hi(v.y);
     }
-    if (dxr) {   // dense router term (softmax-all gate)
+    if (dxr) {   // dense router term (softmax-all and noisy gates)
       const float4 r = *reinterpret_cast<const float4 *>(dxr + (int64_t)t * d + c);
       acc[0] += r.x;
       acc[1] += r.y;
@@ -423,43 +382,35 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dx_kernel(
   }
 }
 
-// colsrc_tok[j]: the token behind column j of a grouping (perm_src of the
-// grouped row colsrc[j]), or -1.
-__global__ void bwd_col_token_kernel(const int32_t *__restrict__ colsrc,
-                                     const int32_t *__restrict__ perm_src, int Rp, int n, int T,
-                                     int32_t *__restrict__ colsrc_tok) {
-  for (int j = blockIdx.x * blockDim.x + threadIdx.x; j < Rp; j += gridDim.x * blockDim.x) {
-    const int r = colsrc[j];
-    colsrc_tok[j] = (r >= 0 && r < n) ? min(max(perm_src[r], 0), T - 1) : -1;
-  }
-}
-
-// Softmax-all gate: the gate values are w_j = p_{i_j} with p the softmax of
-// all E scores, so every score has a gradient: ds_e = p_e (dw'_e [e kept] -
-// m) with m = sum_j w_j dw'_j; for a kept expert this is the ds of the gate
-// kernel.  One wavefront per token writes the dense row dS[t][0..E).
+// Dense score gradients dS [T, E], one wavefront per token.  A kept expert
+// takes the ds of the gate kernel.  Softmax-all gate (logits given): the gate
+// values are w_j = p_{i_j} with p the softmax of all E scores, so every
+// score has a gradient: ds_e = p_e (dw'_e [e kept] - m) with m = sum_j w_j
+// dw'_j, which for a kept expert is that ds.  Otherwise (logits NULL) an
+// unkept score has none: zero.
 __global__ __launch_bounds__(kWave) void bwd_dense_ds_kernel(
     const float *__restrict__ logits, const int32_t *__restrict__ idx,
     const float *__restrict__ ds, const float *__restrict__ tm, int T, int E, int k,
     float *__restrict__ dS) {
   const int t = blockIdx.x;
   const int lane = threadIdx.x;
-  const float *s = logits + (int64_t)t * E;
-  float mx = -INFINITY;
-  for (int e = lane; e < E; e += kWave) mx = fmaxf(mx, s[e]);
+  const float *s = logits ? logits + (int64_t)t * E : nullptr;
+  float mx = -INFINITY, z = 0.0f, m = 0.0f;
+  if (s) {
+    for (int e = lane; e < E; e += kWave) mx = fmaxf(mx, s[e]);
 #pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
-  float z = 0.0f;
-  for (int e = lane; e < E; e += kWave) z += expf(s[e] - mx);
+    for (int off = 32; off >= 1; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+    for (int e = lane; e < E; e += kWave) z += expf(s[e] - mx);
 #pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) z += __shfl_xor(z, off);
-  const float m = tm[t];
+    for (int off = 32; off >= 1; off >>= 1) z += __shfl_xor(z, off);
+    m = tm[t];
+  }
   const int32_t *it = idx + (int64_t)t * k;
   float *row = dS + (int64_t)t * E;
   for (int e = lane; e < E; e += kWave) {
     int j = 0;
     while (j < k && it[j] != e) ++j;
-    row[e] = j < k ? ds[(int64_t)t * k + j] : -(expf(s[e] - mx) / z) * m;
+    row[e] = j < k ? ds[(int64_t)t * k + j] : (s ? -(expf(s[e] - mx) / z) * m : 0.0f);
   }
 }
 
@@ -574,7 +525,7 @@ __global__ __launch_bounds__(kWave) void bwd_noisy_ds_kernel(
   }
 }
 
-// Dense fp32 products of the softmax-all gate's router gradients on the
+// Dense fp32 products of the router gradients on the
 // fp32 matrix cores (v_mfma_f32_16x16x4_f32: lane l supplies A[l%16][l/16]
 // and B[l/16][l%16], and holds D[4(l/16)+r][l%16] in r = 0..3):
 //   C_z[m][n] = sum over k in split z of A(m, k) B[k][n]
@@ -815,26 +766,32 @@ hipError_t launch_backward(const BwdArgs &a, const BwdBuffers &b, hipStream_t s)
     bwd_importance_grad_kernel<<<1, kBwdThreads, 0, s>>>(a.importance, E, a.w_imp, b.gimp);
     gimp = b.gimp;
   }
-  // softmax-all and noisy gates: every score has a gradient (dense router
-  // gradients); the noisy gate's noise scores too
+  // The score gradients as a dense [T, E] matrix for every gate (zero where
+  // a score has none), so that the router's weight gradient is one GEMM
+  // dS^T X whatever the selection and the drops (a dropped slot still has a
+  // score gradient: its gate shapes the kept softmax and Importance).  The
+  // softmax-all and noisy gates give every score a gradient, and then the
+  // router's share of dx is dense too (the noisy gate's noise scores also).
   const bool noisy = a.clean != nullptr;
   const bool dense = a.logits != nullptr || noisy;
   bwd_gate_kernel<<<T, kBwdThreads, 0, s>>>(a.dy, a.y_perm, a.pos, a.idx, a.topk_w, gimp, T,
                                             k, d, E, S, R, b.dyp, b.ds, a.logits ? b.tm : nullptr);
   MOE_TRY(hipGetLastError());
-  if (dense) {
-    if (noisy) {
-      const float *gload = nullptr;
-      if (a.load && a.w_load != 0.0f) {
-        bwd_importance_grad_kernel<<<1, kBwdThreads, 0, s>>>(a.load, E, a.w_load, b.gload);
-        gload = b.gload;
-      }
-      bwd_noisy_ds_kernel<<<T, kWave, 0, s>>>(a.clean, a.scale, a.noise, a.idx, b.ds, gload, E,
-                                              k, b.dS, b.dU);
-    } else {
-      bwd_dense_ds_kernel<<<T, kWave, 0, s>>>(a.logits, a.idx, b.ds, b.tm, T, E, k, b.dS);
+  if (noisy) {
+    const float *gload = nullptr;
+    if (a.load && a.w_load != 0.0f) {
+      bwd_importance_grad_kernel<<<1, kBwdThreads, 0, s>>>(a.load, E, a.w_load, b.gload);
+      gload = b.gload;
     }
-    // the router's share of dx: dS [T, E] times W_g [E, d] (+ dU W_noise)
+    bwd_noisy_ds_kernel<<<T, kWave, 0, s>>>(a.clean, a.scale, a.noise, a.idx, b.ds, gload, E, k,
+                                            b.dS, b.dU);
+  } else {
+    bwd_dense_ds_kernel<<<T, kWave, 0, s>>>(a.logits, a.idx, b.ds, b.tm, T, E, k, b.dS);
+  }
+  MOE_TRY(hipGetLastError());
+  if (dense) {
+    // the router's share of dx: dS [T, E] times W_g [E, d] (+ dU W_noise);
+    // otherwise the gate kernel's k score gradients per token serve
     const dim3 grid((d + 127) / 128, (T + 127) / 128, 1);
     bwd_dense_gemm_kernel<2, 2, 4, 4, false, float>
         <<<grid, 256, 0, s>>>(b.dS, a.w_gate, T, d, E, E, 0, b.dxr);
@@ -889,70 +846,36 @@ hipError_t launch_backward(const BwdArgs &a, const BwdBuffers &b, hipStream_t s)
   MOE_TRY(launch_wgrad_bf16(b.poff, G, Rp, nup, d, b.dAT, b.xpT, a.dw_up,
                             S ? a.dw_up_s : nullptr, s));
   if (a.db_down)
-    bwd_rowsum_kernel<uint16_t><<<dim3(d, E), kWave, 0, s>>>(b.dypT, d, Rp, b.poff, nullptr,
-                                                             a.db_down);
+    bwd_rowsum_kernel<<<dim3(d, E), kWave, 0, s>>>(b.dypT, d, Rp, b.poff, a.db_down);
   if (a.db_up)
-    bwd_rowsum_kernel<uint16_t><<<dim3(h, E), kWave, 0, s>>>(b.dAT, h, Rp, b.poff, nullptr,
-                                                             a.db_up);
-  if (dense) {   // router gradients from the dense score gradients
-    // dW = dS^T X over token splits, then the splits summed in order
-    int splits, kchunk;
-    bwd_dense_plan(T, E, d, &splits, &kchunk);
-    auto wgrad = [&](const float *dsc, float *out) {
-      float *dst = splits > 1 ? b.dpart : out;
-      if (E <= 32)
-        bwd_dense_gemm_kernel<1, 4, 1, 4, true, uint16_t>
-            <<<dim3((d + 255) / 256, (E + 15) / 16, splits), 256, 0, s>>>(dsc, a.x, E, d, T,
+    bwd_rowsum_kernel<<<dim3(h, E), kWave, 0, s>>>(b.dAT, h, Rp, b.poff, a.db_up);
+  // router: dW = dS^T X over token splits, then the splits summed in order
+  // (and dW_noise = dU^T X for the noisy gate); db = the column sums of dS,
+  // zero under the bias-selects gate (the bias there only steers selection)
+  int splits, kchunk;
+  bwd_dense_plan(T, E, d, &splits, &kchunk);
+  auto wgrad = [&](const float *dsc, float *out) {
+    float *dst = splits > 1 ? b.dpart : out;
+    if (E <= 32)
+      bwd_dense_gemm_kernel<1, 4, 1, 4, true, uint16_t>
+          <<<dim3((d + 255) / 256, (E + 15) / 16, splits), 256, 0, s>>>(dsc, a.x, E, d, T,
+                                                                        kchunk, 0, dst);
+    else
+      bwd_dense_gemm_kernel<2, 2, 4, 4, true, uint16_t>
+          <<<dim3((d + 127) / 128, (E + 127) / 128, splits), 256, 0, s>>>(dsc, a.x, E, d, T,
                                                                           kchunk, 0, dst);
-      else
-        bwd_dense_gemm_kernel<2, 2, 4, 4, true, uint16_t>
-            <<<dim3((d + 127) / 128, (E + 127) / 128, splits), 256, 0, s>>>(dsc, a.x, E, d, T,
-                                                                            kchunk, 0, dst);
-      if (splits > 1) {
-        const int64_t n4 = (int64_t)E * d / 4;
-        bwd_split_sum_kernel<<<grid_for(n4, 256), 256, 0, s>>>(b.dpart, splits, n4, out);
-      }
-    };
-    wgrad(b.dS, a.dw_gate);
-    if (noisy) wgrad(b.dU, a.dw_noise);
-    if (a.db_gate) bwd_dense_bias_kernel<<<E, kWave, 0, s>>>(b.dS, T, E, a.db_gate);
-    return hipGetLastError();
-  }
-  // router: dW_g[e] = sum over every assignment to e of ds * x, db_g[e] =
-  // sum of ds.  A dropped slot has a score gradient too (its gate shapes the
-  // kept softmax and Importance), so under a capacity every assignment is
-  // grouped again (no row move) and x is transposed in that order into the
-  // space of dY^T, which is no longer needed; otherwise the kept grouping
-  // is the full one and X^T serves.
-  const uint16_t *xT = b.xpT;
-  const int32_t *pos_r = a.pos, *poff_r = b.poff, *colsrc_r = b.colsrc;
-  if (a.capacity > 0) {
-    MOE_TRY(launch_permute(a.idx, a.topk_w, a.x, T, k, E, 0, d * 2, b.off_all, b.src_all,
-                           b.pos_all, nullptr, nullptr, nullptr, b.hist, b.full_off,
-                           b.perm_w, s));
-    bwd_layout_kernel<<<1, kBwdThreads, 0, s>>>(b.off_all, E, 0, T, routed, b.poff);
-    bwd_colsrc_kernel<<<grid_for(Rp, kBwdThreads), kBwdThreads, 0, s>>>(
-        b.off_all, b.poff, E, 0, T, routed, Rp, b.colsrc);
-    // the token behind each column, into the (now free) column-source space
-    // of the kept grouping's gradient pass: reuse dsp's neighbour ds_cols
-    bwd_col_token_kernel<<<grid_for(Rp, 256), 256, 0, s>>>(b.colsrc, b.src_all, Rp, routed, T,
-                                                           reinterpret_cast<int32_t *>(b.ds_cols));
-    bwd_transpose_cols_kernel<<<dim3(Rp / 64, d / 64), kBwdThreads, 0, s>>>(
-        a.x, a.x, T, d, reinterpret_cast<const int32_t *>(b.ds_cols), Rp, b.dypT);
-    xT = b.dypT;
-    pos_r = b.pos_all;
-  }
-  bwd_scatter_ds_kernel<<<grid_for(routed, 256), 256, 0, s>>>(b.ds, pos_r, routed, routed, b.dsp);
-  bwd_ds_cols_kernel<<<grid_for(Rp, 256), 256, 0, s>>>(b.dsp, colsrc_r, Rp, routed, b.ds_cols);
-  bwd_rowsum_kernel<float><<<dim3(d, E), kWave, 0, s>>>(xT, d, Rp, poff_r, b.ds_cols, a.dw_gate);
-  // the gate values depend on the unbiased scores under the bias-selects
-  // gate (the same ds: w is the softmax of x W_g^T over the kept experts),
-  // so the bias has no gradient there
+    if (splits > 1) {
+      const int64_t n4 = (int64_t)E * d / 4;
+      bwd_split_sum_kernel<<<grid_for(n4, 256), 256, 0, s>>>(b.dpart, splits, n4, out);
+    }
+  };
+  wgrad(b.dS, a.dw_gate);
+  if (noisy) wgrad(b.dU, a.dw_noise);
   if (a.db_gate) {
     if (a.bias_selects)
       MOE_TRY(launch_fill_f32(a.db_gate, E, s));
     else
-      bwd_group_sum_kernel<<<E, kWave, 0, s>>>(b.ds_cols, poff_r, a.db_gate);
+      bwd_dense_bias_kernel<<<E, kWave, 0, s>>>(b.dS, T, E, a.db_gate);
   }
   return hipGetLastError();
 #undef MOE_TRY
