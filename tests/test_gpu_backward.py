@@ -226,6 +226,21 @@ def test_backward_bias_selects_gate(train):
     print({n: f"{e:.2e}" for n, e in errs.items()})
 
 
+@pytest.mark.parametrize("overflow", [0, B.MOE_OVERFLOW_NEXT_CHOICE], ids=["drop", "next-choice"])
+def test_backward_bias_selects_gate_with_capacity(overflow):
+    """The bias-selects gate under an expert capacity, the bias tilted so that
+    the first experts overflow: a dropped or re-routed slot's gate value still
+    shapes the kept softmax and Importance, so the router's weight gradient
+    covers it; the bias still gets a zero gradient."""
+    L = random_layer(68, wstd=0.15, T=300, d=128, h=256, E=8, k=2, act=SWIGLU, dtype=BF16,
+                     bias=True, S=1, gate=synthetic.GATE_BIAS_SELECTS)
+    L.b_gate = np.linspace(1.5, 0.0, 8).astype(np.float32)
+    idx, _, _ = oracle.route(L)
+    assert oracle.capacity_keep(L.cfg, idx, 60).sum() < L.cfg.T * L.cfg.k
+    errs = check_backward(L, 60, 0.4, overflow=overflow)
+    print({n: f"{e:.2e}" for n, e in errs.items()})
+
+
 @pytest.mark.parametrize("case", [
     (dict(T=300, d=128, h=256, E=8, k=2, act=SWIGLU, dtype=BF16, bias=True, S=1), 0, 0.4, False),
     (dict(T=257, d=64, h=128, E=64, k=6, act=SWIGLU, dtype=BF16, bias=True), 0, 0.0, True),
