@@ -197,7 +197,10 @@ moe_status_t moe_route_noisy(const moe_config_t *cfg, const void *x,
  *   topk_idx, topk_w [T, k]   (device, in) as written by moe_route
  *   logits     [T, E] fp32    (device, in) moe_route's scores; read only
  *              under a capacity with MOE_OVERFLOW_NEXT_CHOICE (the next
- *              choices), else ignored (may be NULL)
+ *              choices are ranked by them), else ignored (may be NULL).
+ *              Re-routing is defined for moe_route's selection only: the
+ *              noisy gate selects on H, which no call outputs, so a
+ *              selection of moe_route_noisy is not to be re-routed
  *   x          [T, d] dtype   (device, in)
  *   offsets    [E + 1] int32  (out) group starts of the kept assignments;
  *              offsets[E] = T*k without a capacity, else the number of
@@ -210,8 +213,9 @@ moe_status_t moe_route_noisy(const moe_config_t *cfg, const void *x,
  *              computes the slot (rows in flat order within a group)
  *   importance [E] fp32       (out) Importance(X)_e = sum of the router
  *              weights routed to e (Qiita summary, "Load-balancing losses"),
- *              summed in group order; dropped assignments included (they
- *              are the router's output)
+ *              fp32, in a fixed order (64 lane-strided partial sums over
+ *              the group's rows, then a fixed butterfly), so deterministic;
+ *              dropped assignments included (they are the router's output)
  *   stats      [3] double or NULL (out) CV^2(Importance), CV^2(Load) with
  *              Load = counts, and the load-balance loss E*sum_e f_e^2 of the
  *              Go chapter's section 3 (population variance; 0 if empty)
@@ -240,8 +244,6 @@ moe_status_t moe_expert_up(const moe_config_t *cfg, const moe_weights_t *w,
                            const int32_t *offsets, void *hidden,
                            hipStream_t stream);
 
-/* Down projection of every group: y_perm[r] = W2[e] hidden[r] (+ b2[e]).
- *   hidden [R, h] dtype (in), y_perm [R, d] dtype (out) */
 /* The up projection of a training step: moe_expert_up, and the expert
  * pre-activations that the backward pass differentiates through, so that
  * moe_backward need not recompute them.  bf16 layers only (else
@@ -253,6 +255,8 @@ moe_status_t moe_expert_up_train(const moe_config_t *cfg, const moe_weights_t *w
                                  const void *x_perm, const void *x, const int32_t *offsets,
                                  void *hidden, void *preact, hipStream_t stream);
 
+/* Down projection of every group: y_perm[r] = W2[e] hidden[r] (+ b2[e]).
+ *   hidden [R, h] dtype (in), y_perm [R, d] dtype (out) */
 moe_status_t moe_expert_down(const moe_config_t *cfg, const moe_weights_t *w,
                              const void *hidden, const int32_t *offsets,
                              void *y_perm, hipStream_t stream);
@@ -305,7 +309,8 @@ moe_status_t moe_forward(const moe_config_t *cfg, const moe_weights_t *w,
  *   logits [T, E] fp32 (moe_route's scores) under MOE_GATE_SOFTMAX_ALL,
  *     else ignored (may be NULL)
  *   noisy: NULL for the clean gate, else the noisy gate's values and the
- *     W_noise gradient (moe_noisy_grad_t above; MOE_GATE_TOPK_SOFTMAX only)
+ *     W_noise gradient (moe_noisy_grad_t, defined after moe_grads_t below;
+ *     MOE_GATE_TOPK_SOFTMAX only)
  *   importance [E] fp32 or NULL (moe_permute's), importance_weight: the
  *     weight of the CV^2(Importance) term (ignored when importance is NULL)
  *   grads: every pointer device memory, written in full:

@@ -65,6 +65,7 @@ def lib():
         L.oracle_counts.argtypes = [P, P, P, P, P]
         L.oracle_permute.argtypes = [P, P, P, P, P]
         L.oracle_expert.argtypes = [P, P, C.c_int, P, P]
+        L.oracle_slot_outputs.argtypes = [P, P, P, P, C.c_int64, P, P]
         L.oracle_forward_tokens.argtypes = [P, P, P, P, C.c_int64, P, P, P]
         L.oracle_forward_tokens_keep.argtypes = [P, P, P, P, C.c_int64, P, P, P, P]
         L.oracle_capacity_keep.argtypes = [P, P, C.c_int32, P]
@@ -84,7 +85,7 @@ def lib():
                   "oracle_forward_tokens_keep", "oracle_capacity_keep",
                   "oracle_permute_keep", "oracle_route_noisy", "oracle_cv2",
                   "oracle_capacity_reroute", "oracle_permute_assign",
-                  "oracle_forward_tokens_assign"):
+                  "oracle_forward_tokens_assign", "oracle_slot_outputs"):
             getattr(L, f).restype = C.c_int
         _lib = L
     return _lib
@@ -247,6 +248,23 @@ def expert(layer, e: int, xrow: np.ndarray) -> np.ndarray:
     _check(lib().oracle_expert(C.byref(cfg), C.byref(W), int(e), _ptr(xr),
                                _ptr(y)), "oracle_expert")
     return y
+
+
+def slot_outputs(layer, tokens: Sequence[int], experts: np.ndarray) -> np.ndarray:
+    """Expert output of every slot of the listed tokens, before the gate
+    weight: float64 [n, k, d], row [r, j] = E_e(x_t) with t = tokens[r] and
+    e = experts[t, j] (int32 [T, k] or [T*k]: the selection, or the
+    computing expert of each slot; -1 gives zeros)."""
+    c = layer.cfg
+    tok = np.ascontiguousarray(np.asarray(tokens, np.int64))
+    ex = np.ascontiguousarray(np.asarray(experts, np.int32)).reshape(-1)
+    assert ex.size == c.T * c.k
+    out = np.empty((tok.size, c.k, c.d), np.float64)
+    cfg = _cfg(c)
+    W = _weights(layer)
+    _check(lib().oracle_slot_outputs(C.byref(cfg), C.byref(W), _ptr(layer.x), _ptr(tok),
+                                     tok.size, _ptr(ex), _ptr(out)), "oracle_slot_outputs")
+    return out
 
 
 def forward_tokens(layer, tokens: Sequence[int], keep: Optional[np.ndarray] = None,

@@ -369,3 +369,57 @@ def expert_unit_grads(layer, dy: np.ndarray, e: int, units, idx: Optional[np.nda
     if cfg.act == 0 and b1 is not None:
         out["b_up"] = grads[1].numpy()
     return out
+
+
+# ---- the router's weight gradients at sizes too large for the whole graph.
+# The router parameters (W_g, b_g, W_noise) enter the loss only through the
+# gate values: the expert outputs and the shared expert do not depend on
+# them.  So with every slot's expert output E_{i_j}(x_t) held fixed, the
+# loss restricted to the router,
+#     sum_t sum_j G_tj <dy_t, E_{i_j}(x_t)> + w_imp CV^2(Importance)
+#                                          (+ w_load CV^2(Load)),
+# has the same gradient in those parameters as the whole loss of backward()
+# (pinned to it on small layers).
+
+def slot_dy_products(layer, dy: np.ndarray, experts: np.ndarray, chunk: int = 256) -> np.ndarray:
+    """c[t, j] = <dy_t, E_e(x_t)> with e = experts[t, j] (the computing
+    expert of the slot, -1 for a dropped one: 0), float64 [T, k], from the C
+    oracle's float64 expert outputs, a chunk of tokens at a time."""
+    from . import slot_outputs as _slot_outputs
+    cfg = layer.cfg
+    dyf = np.asarray(dy, np.float64)
+    out = np.empty((cfg.T, cfg.k), np.float64)
+    for t0 in range(0, cfg.T, chunk):
+        toks = np.arange(t0, min(cfg.T, t0 + chunk))
+        ys = _slot_outputs(layer, toks, experts)
+        out[toks] = np.einsum("tjd,td->tj", ys, dyf[toks])
+    return out
+
+
+def router_grads(layer, slot_dy: np.ndarray, importance_weight: float = 0.0,
+                 idx: Optional[np.ndarray] = None, noise: Optional[np.ndarray] = None,
+                 load_weight: float = 0.0, selection=None) -> dict:
+    """Gradients of the loss of backward() in w_gate, b_gate and w_noise
+    (those the layer has), float64, from slot_dy = slot_dy_products(...) for
+    the same selection: idx (the oracle's routing if None), or the noisy
+    gate with these draws (selection: its noisy_selection(), computed if
+    None)."""
+    noisy = None
+    if noise is not None:
+        idx, kth = selection if selection is not None else noisy_selection(layer, noise)
+        noisy = dict(noise=np.asarray(noise, np.float32), kth=kth)
+    elif idx is None:
+        idx, _, _ = _route(layer)
+    p = _router_params(layer)
+    leaves = [n for n in ("w_gate", "b_gate", "w_noise") if n in p]
+    for n in leaves:
+        p[n].requires_grad_(True)
+    g, imp, load = _gates(layer, p, idx, noisy)
+    L = (g * torch.from_numpy(np.asarray(slot_dy, np.float64))).sum()
+    if importance_weight:
+        L = L + importance_weight * cv2(imp)
+    if load_weight and load is not None:
+        L = L + load_weight * cv2(load)
+    grads = torch.autograd.grad(L, [p[n] for n in leaves], allow_unused=True)
+    return {n: (np.zeros(tuple(p[n].shape)) if gr is None else gr.numpy())
+            for n, gr in zip(leaves, grads)}

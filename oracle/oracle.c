@@ -487,6 +487,44 @@ int oracle_expert(const oracle_cfg *c, const oracle_weights *W, int e,
   return 0;
 }
 
+/* The expert output of every slot of the listed tokens, before the gate
+ * weight: yslot[r][j] = E_{experts[t*k+j]}(x_t) for t = tokens[r], in double
+ * (a slot whose expert is -1, a dropped one, gets zeros).  This is the
+ * term E_i(x) of y = sum_i G(x)_i E_i(x) for each kept i ("Sparsely-Gated
+ * MoE" summary, "Sparsely-Gated MoE layer formula"), one row per slot, so
+ * that a test can form the router's share of the gradient, which needs
+ * every slot's expert output.  OpenMP over (token, slot) pairs. */
+int oracle_slot_outputs(const oracle_cfg *c, const oracle_weights *W, const void *x,
+                        const int64_t *tokens, int64_t nt, const int32_t *experts,
+                        double *yslot) {
+  if (!cfg_ok(c) || !W || !x || !tokens || !experts || !yslot || nt < 0) return -1;
+  for (int64_t r = 0; r < nt; ++r)
+    if (tokens[r] < 0 || tokens[r] >= c->T) return -1;
+  for (int64_t f = 0; f < c->T * c->k; ++f)
+    if (experts[f] < -1 || experts[f] >= c->E) return -1;
+  const int64_t d = c->d, k = c->k;
+#pragma omp parallel
+  {
+    double *xr = (double *)malloc(sizeof(double) * (size_t)d);
+    double *hid = (double *)malloc(sizeof(double) * (size_t)c->h);
+#pragma omp for schedule(dynamic, 1)
+    for (int64_t q = 0; q < nt * k; ++q) {
+      const int64_t t = tokens[q / k];
+      const int e = experts[t * k + q % k];
+      double *yo = yslot + q * d;
+      if (e < 0) {
+        for (int64_t i = 0; i < d; ++i) yo[i] = 0.0;
+        continue;
+      }
+      for (int64_t i = 0; i < d; ++i) xr[i] = elem(x, c->dtype, t * d + i);
+      expert_ffn(c, W, e, xr, hid, yo);
+    }
+    free(xr);
+    free(hid);
+  }
+  return 0;
+}
+
 /* The whole layer on the listed tokens (the two entry points below). */
 static int forward_tokens_impl(const oracle_cfg *c, const oracle_weights *W,
                                const void *x, const int64_t *tokens, int64_t nt,

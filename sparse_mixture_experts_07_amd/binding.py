@@ -31,6 +31,10 @@ MOE_GATE_SOFTMAX_ALL = 2
 MOE_OVERFLOW_DROP = 0
 MOE_OVERFLOW_NEXT_CHOICE = 1
 
+# The ABI this binding marshals for (moe.h's MOE_ABI_VERSION): a library of
+# another version may take other argument lists, so lib() refuses it.
+ABI_VERSION = 8
+
 EXPORTS = (
     "moe_abi_version", "moe_status_string", "moe_workspace_bytes",
     "moe_grouped_rows", "moe_route", "moe_permute", "moe_expert_up",
@@ -103,6 +107,11 @@ def lib():
             fn = getattr(L, name)
             fn.argtypes = args
             fn.restype = C.c_int
+        got = L.moe_abi_version()
+        if got != ABI_VERSION:
+            raise RuntimeError(
+                f"{LIB_PATH} implements ABI version {got}, this binding version "
+                f"{ABI_VERSION}: rebuild it with __graft_entry__.build()")
         _lib = L
     return _lib
 

@@ -13,9 +13,11 @@
 //                it; inside a wavefront, lanes holding the same expert are
 //                matched with 8 ballots (expert ids < 256) and ranked by
 //                lane order, so rows keep flat-index order.
-//   4. stats   - Importance(X)_e = sum of the kept weights of group e in
-//                group order, one wavefront per expert (Qiita summary
-//                "Load-balancing losses"); then one wavefront computes
+//   4. stats   - Importance(X)_e = sum of the router weights of group e,
+//                one wavefront per expert: lane l adds rows l, l+64, ...
+//                of the group in order, then a fixed xor butterfly over the
+//                64 partial sums (a fixed order, so deterministic; Qiita
+//                summary "Load-balancing losses"); then one wavefront computes
 //                CV^2(Importance), CV^2(Load) and the load-balance loss of
 //                the Go chapter's section 3, in fp64.
 //   5. move    - x_perm[p] = x[perm_src[p]], 16-byte vectors, one row per

@@ -71,7 +71,34 @@ def check_outputs(layer, y, tokens, tol=None, keep=None, assign=None):
 
 
 def sample_tokens(T: int, n: int = 48, seed: int = 0):
+    """n distinct tokens (all of them when T <= n): first, second, middle and
+    last always, the rest drawn at random; sorted."""
+    if T <= n:
+        return list(range(T))
     rng = np.random.default_rng(seed)
-    base = {0, 1, T // 2, T - 1}
-    extra = rng.choice(T, size=min(T, n), replace=False).tolist()
-    return sorted(base.union(extra))[: max(n, 4)]
+    base = sorted({0, 1, T // 2, T - 1})[:n]
+    rest = np.setdiff1d(np.arange(T), base)
+    extra = rng.choice(rest, size=n - len(base), replace=False).tolist()
+    return sorted(base + extra)
+
+
+def covering_tokens(idx: np.ndarray, n: int, seed: int = 0):
+    """At least one token of every non-empty expert group of the selection
+    idx [T, k] (so every group size class and every group's tiles of the
+    grouped GEMM are compared), first, second, middle and last, filled up to
+    n tokens at random; sorted."""
+    T = idx.shape[0]
+    picked = {0, 1, T // 2, T - 1} & set(range(T))
+    covered = set(idx[sorted(picked)].ravel().tolist())
+    rng = np.random.default_rng(seed)
+    for t in rng.permutation(T):
+        new = set(idx[t].tolist()) - covered
+        if new:
+            picked.add(int(t))
+            covered |= new
+    assert covered == set(idx.ravel().tolist())
+    if len(picked) < n:
+        rest = np.setdiff1d(np.arange(T), sorted(picked))
+        picked |= set(rng.choice(rest, size=min(rest.size, n - len(picked)),
+                                 replace=False).tolist())
+    return sorted(picked)

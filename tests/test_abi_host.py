@@ -27,7 +27,7 @@ def test_library_exports_every_declared_entry_point():
     assert set(B.EXPORTS) == set(names), names
     for n in names:
         assert hasattr(lib, n), f"libmoe.so does not export {n}"
-    assert B.moe_abi_version() == 8
+    assert B.moe_abi_version() == B.ABI_VERSION == 8
 
 
 def test_status_strings():

@@ -157,6 +157,10 @@ CASES = {
     "e64-small-groups": (dict(T=100, d=64, h=64, E=64, k=6, act=SWIGLU, dtype=BF16, bias=True), 0, 0.0),
     "large-groups": (dict(T=1200, d=256, h=512, E=3, k=2, act=SWIGLU, dtype=BF16, S=1), 0, 0.1),
     "long-k-gelu": (dict(T=600, d=64, h=8256, E=2, k=1, act=GELU, dtype=BF16, expert_bias=True), 0, 0.0),
+    # 256 experts at a mid size: the router weight gradient dS^T X runs its
+    # 128 x 128 tiles (2 x 8 of them) over 16 token splits, summed in order
+    "e256-router-splits": (dict(T=2048, d=1024, h=64, E=256, k=8, act=SWIGLU, dtype=BF16,
+                                bias=True, S=1), 0, 0.1),
 }
 
 

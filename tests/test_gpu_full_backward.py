@@ -8,8 +8,10 @@ the smallest and (DeepSeek-V3) the shared expert, against the oracle's
 slices of the same gradient (pinned to the whole graph on small layers).
 The same with the noisy gate (its smooth-Load loss weight 0.01, as
 `bench.py --noisy --backward`), plus output rows.  The router's weight
-gradients (W_g, W_noise) at those two shapes need every token's expert
-outputs and are checked at the GPT-2 shape and on small layers."""
+gradients (W_g, b_g, and W_noise with the noisy gate) at those two shapes
+against the oracle's router slice: every slot's float64 expert output held
+fixed (pinned to the whole graph on small layers), which takes one full
+oracle forward of the batch on the CPU."""
 from __future__ import annotations
 
 import numpy as np
@@ -88,6 +90,8 @@ def training_step(L, dy_bits, noise=None):
     torch.cuda.synchronize()
     out = {("x" if n == "dx" else n): to_f64(t) for n, t in g.items() if t is not None}
     out["y"] = to_f64(y)
+    if noise is not None:
+        out["w_noise"] = to_f64(dw_noise)
     ridx = idx.cpu().numpy()
     del dl, ws_b, x_perm, hidden, preact, y_perm, g, mg
     torch.cuda.empty_cache()
@@ -116,11 +120,11 @@ def test_full_size_training_step_gpt2():
 
 
 @pytest.mark.timeout(1200)
-@pytest.mark.parametrize("name,ntok,noisy", [("mixtral-8x7b", 12, False),
-                                             ("deepseek-v3", 6, False),
-                                             ("mixtral-8x7b", 8, True),
-                                             ("deepseek-v3", 4, True)])
-def test_full_size_training_step_sampled(name, ntok, noisy):
+@pytest.mark.parametrize("name,ntok,noisy,router", [("mixtral-8x7b", 12, False, True),
+                                                    ("deepseek-v3", 6, False, True),
+                                                    ("mixtral-8x7b", 8, True, True),
+                                                    ("deepseek-v3", 4, True, False)])
+def test_full_size_training_step_sampled(name, ntok, noisy, router):
     cfg = synthetic.BY_NAME[name]
     L = synthetic.make_inputs(cfg)
     noise = sel = None
@@ -168,6 +172,12 @@ def test_full_size_training_step_sampled(name, ntok, noisy):
         gup = np.stack([up[units], up[units + cfg.h]])   # SwiGLU: gate rows, up rows
         errs[f"w_up[{e}]"] = max_rel(gup, ref["w_up"])
         errs[f"w_down[{e}]"] = max_rel(down[:, units], ref["w_down"])
+    if router:   # every router weight gradient, from every slot's expert output
+        sdy = oracle.backward.slot_dy_products(L, dyf, ridx)
+        ref = oracle.backward.router_grads(L, sdy, IMP_W, idx=ridx, noise=noise,
+                                           load_weight=LOAD_W, selection=sel)
+        for n, r in ref.items():
+            errs[n] = max_rel(got[n].reshape(r.shape), r)
     print(name, "noisy" if noisy else "", {n: f"{v:.2e}" for n, v in errs.items()})
     for n, v in errs.items():
         assert v <= GRAD_TOL, f"{n}: max-relative error {v:.3e}"

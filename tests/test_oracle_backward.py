@@ -251,3 +251,73 @@ def test_noisy_slices_equal_the_whole_graph(k, E):
                                    atol=1e-12)
         np.testing.assert_allclose(g["w_down"], full["w_down"][e][:, units], rtol=1e-10,
                                    atol=1e-12)
+
+
+def test_slot_outputs_are_the_expert_ffns():
+    """oracle.slot_outputs (C, float64) row by row against the torch float64
+    expert FFNs (written separately in oracle/backward.py), and the gated
+    sum of the slots against the C forward; a dropped slot (-1) is zero."""
+    for act, S, eb in ((SWIGLU, 1, False), (GELU, 0, True)):
+        L = _layer(70, act, S, expert_bias=eb, T=20, d=12, h=10, E=6, k=3)
+        idx, w, _ = oracle.route(L)
+        toks = [0, 5, 19]
+        ys = oracle.slot_outputs(L, toks, idx)
+        p = {n: t.detach() for n, t in B.params(L).items()}
+        for r, t in enumerate(toks):
+            for j in range(3):
+                ref = B._ffn(L.cfg, p, int(idx[t, j]), p["x"][t:t + 1])[0].numpy()
+                np.testing.assert_allclose(ys[r, j], ref, rtol=1e-12, atol=1e-14)
+        yc, _, _ = oracle.forward_tokens(L, toks)
+        comb = np.einsum("tj,tjd->td", w[toks], ys)
+        if S:
+            comb += np.stack([oracle.expert(L, 6, B._f64(L.x)[t].numpy()) for t in toks])
+        np.testing.assert_allclose(comb, yc, rtol=1e-12, atol=1e-14)
+        dropped = np.where(np.arange(20 * 3).reshape(20, 3) % 4 == 1, -1, idx)
+        yd = oracle.slot_outputs(L, toks, dropped)
+        for r, t in enumerate(toks):
+            for j in range(3):
+                if dropped[t, j] < 0:
+                    assert np.all(yd[r, j] == 0)
+                else:
+                    assert np.array_equal(yd[r, j], ys[r, j])
+
+
+@pytest.mark.parametrize("gate,imp_w,policy", [(0, 0.4, None), (1, 0.3, None), (2, 0.5, None),
+                                               (0, 0.2, "drop"), (0, 0.3, "next-choice")])
+def test_router_gradient_slice_equals_the_whole_graph(gate, imp_w, policy):
+    """The router's weight gradients from the slots' expert outputs held
+    fixed equal those of backward() (the whole graph, pinned by gradcheck),
+    for every gate mode and under a capacity with either overflow policy."""
+    L = random_layer(80 + gate, T=40, d=8, h=12, E=5, k=2, act=SWIGLU, S=1, bias=True,
+                     gate=gate)
+    dy = np.random.default_rng(81).standard_normal((40, 8))
+    idx, _, sc = oracle.route(L, want_scores=True)
+    keep = assign = None
+    experts = idx
+    if policy == "drop":
+        keep = oracle.capacity_keep(L.cfg, idx, 12)
+        assert 0 < keep.sum() < keep.size
+        experts = np.where(keep.reshape(40, 2) != 0, idx, -1)
+    elif policy == "next-choice":
+        assign = oracle.capacity_reroute(L.cfg, idx, sc, 12)
+        assert np.any(assign.reshape(40, 2) != idx)
+        experts = assign
+    full = B.backward(L, dy, keep, imp_w, idx=idx, assign=assign)
+    got = B.router_grads(L, B.slot_dy_products(L, dy, experts, chunk=16), imp_w, idx=idx)
+    assert set(got) == {"w_gate", "b_gate"}
+    for n in got:
+        np.testing.assert_allclose(got[n], full[n], rtol=1e-10, atol=1e-12)
+
+
+def test_noisy_router_gradient_slice_equals_the_whole_graph():
+    """The same with the noisy gate: W_noise, W_g and b_g through the kept
+    softmax of H and the smooth Load."""
+    L, noise = _noisy_layer(85, T=30, E=5, k=2, S=1)
+    dy = np.random.default_rng(86).standard_normal((30, 6))
+    full = B.backward(L, dy, importance_weight=0.3, noise=noise, load_weight=0.7)
+    sel = B.noisy_selection(L, noise)
+    got = B.router_grads(L, B.slot_dy_products(L, dy, sel[0]), 0.3, noise=noise,
+                         load_weight=0.7, selection=sel)
+    assert set(got) == {"w_gate", "b_gate", "w_noise"}
+    for n in got:
+        np.testing.assert_allclose(got[n], full[n], rtol=1e-10, atol=1e-12)
