@@ -9,7 +9,9 @@ entry points, so that the dominant kernel (the expert up projection) can
 be bracketed with HIP events on the stream it runs on.
 
 Prints one JSON line.  Default workload: the Mixtral-8x7B-shape layer
-(T=4096, d=4096, h=14336, 8 experts, top-2, SwiGLU, bf16).
+(T=4096, d=4096, h=14336, 8 experts, top-2, SwiGLU, bf16); the default line
+also carries the gpt-oss-20b-shape decode layer (T=64, d=h=2880, 32
+experts, top-4, SwiGLU, bf16) under "decode", timed in the same process.
 """
 import argparse
 import json
@@ -58,6 +60,12 @@ def parse():
                         "token's next choice")
     p.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "traffic.txt"),
                    help="measured HBM bytes of the dominant kernel per workload (JSON text)")
+    p.add_argument("--grouped-copy", action="store_true",
+                   help="the dispatch writes the grouped copy x_perm and the up projection "
+                        "reads it (default: the up projection reads the rows of x in place)")
+    p.add_argument("--no-decode", action="store_true",
+                   help="default workload only: skip the decode-shape layer that the line "
+                        "also reports")
     p.add_argument("--copy-calibration", action="store_true",
                    help="first copy 1 GiB device to device three times, so that a PMC "
                         "run sees a plain copy of known size beside the layer's kernels")
@@ -75,27 +83,15 @@ def source_digest() -> str:
     return h.hexdigest()
 
 
-def main():
-    args = parse()
-    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py runs on one GPU only: this build has no multi-GPU path "
-              "(expert parallelism is a design note, not code)", file=sys.stderr)
-        sys.exit(2)
-
+def run_one(args):
+    """Time args.steps steps of args.workload; the result object (the JSON
+    line's fields)."""
     import numpy as np
     import torch
 
     import synthetic
     from sparse_mixture_experts_07_amd import binding as B
     from sparse_mixture_experts_07_amd.device import DeviceLayer, Forward
-
-    if args.copy_calibration:
-        src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
 
     cfg = synthetic.BY_NAME[args.workload].with_(gate=GATES[args.gate])
     if args.noisy and cfg.gate != 0:
@@ -110,6 +106,10 @@ def main():
     overflow = B.MOE_OVERFLOW_NEXT_CHOICE if args.overflow == "next-choice" else 0
     if overflow and not cap:
         sys.exit("--overflow next-choice needs --capacity-factor")
+    if overflow and args.noisy:
+        # the next choices are ranked by moe_route's scores; the noisy gate
+        # selects on H = s + n * Softplus(...), which no call outputs
+        sys.exit("--noisy does not combine with --overflow next-choice")
     dl = DeviceLayer.upload(L, capacity=cap, overflow=overflow)
     # Steps rotate through copies of the layer: a layer whose weights fit in
     # the 256 MB memory-side cache would otherwise be read back from it,
@@ -139,6 +139,7 @@ def main():
     pos = torch.empty(T * k, dtype=torch.int32, device=dev)
     imp = torch.empty(E, dtype=torch.float32, device=dev)
     stats = torch.empty(3, dtype=torch.float64, device=dev)
+    gathers = T * d * (2 if dt == torch.bfloat16 else 4) < 2 ** 31 and not args.grouped_copy
     x_perm = torch.empty((T * k, d), dtype=dt, device=dev)
     hidden = torch.empty((R, h), dtype=dt, device=dev)
     y_perm = torch.empty((R, d), dtype=dt, device=dev)
@@ -196,14 +197,17 @@ def main():
         dl, W = copies[turn[0] % ncopy], copy_w[turn[0] % ncopy]
         turn[0] += 1
         route(dl)
-        B.moe_permute(c, idx, tw, dl.x, offsets, perm_src, pos, imp, stats, x_perm, ws,
+        # the up projection reads the token rows of x in place (as moe_forward
+        # does); the training step keeps the grouped copy for the backward
+        xp = x_perm if args.backward or not gathers else None
+        B.moe_permute(c, idx, tw, dl.x, offsets, perm_src, pos, imp, stats, xp, ws,
                       logits=logits, counts=None if args.noisy else counts)
         if ev is not None:
             ev[0].record()
         if args.backward:   # the training forward keeps the pre-activations
             B.moe_expert_up_train(c, W, x_perm, dl.x, offsets, hidden, preact)
         else:
-            B.moe_expert_up(c, W, x_perm, dl.x, offsets, hidden)
+            B.moe_expert_up(c, W, xp, dl.x, offsets, hidden, perm_src=perm_src)
         if ev is not None:
             ev[1].record()
         B.moe_expert_down(c, W, hidden, offsets, y_perm)
@@ -358,6 +362,10 @@ def main():
         "input_gen_upload_s": gen_s,
         "stage_sequence_equals_moe_forward": same,
     }
+    if roof["traffic"] is not None:
+        roof["traffic_source"] = ("rocprofv3 FETCH_SIZE and WRITE_SIZE of this kernel at this "
+                                  "workload, committed in " + os.path.relpath(args.traffic, ROOT) +
+                                  " for the same kernel sources (not measured in this run)")
     if args.backward:
         bwd_ms = float(np.mean([a.elapsed_time(b) for a, b in bwd_evs]))
         # algorithmic backward work: dX and dW of both projections, twice
@@ -369,6 +377,52 @@ def main():
                            "frac_mfma_peak": bflops / (bwd_ms / 1e3) / 1e12 / PEAK_BF16_TFLOPS,
                            "importance_loss_weight": IMPORTANCE_LOSS_WEIGHT,
                            **({"load_loss_weight": LOAD_LOSS_WEIGHT} if args.noisy else {})}
+    del copies, copy_w, dl, L
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return out
+
+
+DEFAULT_WORKLOAD = "mixtral-8x7b"
+DECODE_WORKLOAD = "gpt-oss-20b-decode"
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on one GPU only: this build has no multi-GPU path "
+              "(expert parallelism is a design note, not code)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    if args.copy_calibration:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+    out = run_one(args)
+    # The default line also times the decode-shape layer (the metric's
+    # "decode HBM GB/s"), in the same process, after the headline workload.
+    plain = not (args.capacity_factor or args.noisy or args.backward or args.gate != "topk-softmax")
+    if args.workload == DEFAULT_WORKLOAD and plain and not args.no_decode:
+        dargs = argparse.Namespace(**vars(args))
+        dargs.workload = DECODE_WORKLOAD
+        dargs.no_cpu_baseline = True
+        dargs.steps = max(args.steps, 50)
+        dargs.warmup = max(args.warmup, 20)
+        dec = run_one(dargs)
+        out["decode"] = {
+            "workload": DECODE_WORKLOAD, "config": dec["config"],
+            "steps": dargs.steps, "warmup": dargs.warmup,
+            "decode_ms_per_step": dec["ms_per_step"], "step_ms": dec["step_ms"],
+            "tokens_per_s": dec["value"],
+            "expert_weight_gbs": dec["expert_weight_gbs"],
+            "frac_hbm_peak": dec["expert_weight_gbs"] / PEAK_HBM_GBS,
+            "experts_touched": dec["experts_touched"],
+            "roofline": dec["roofline"],
+            "stage_sequence_equals_moe_forward": dec["stage_sequence_equals_moe_forward"],
+        }
     print(json.dumps(out))
 
 

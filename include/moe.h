@@ -42,7 +42,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 8
+#define MOE_ABI_VERSION 9
 
 typedef enum {
   MOE_OK = 0,
@@ -223,7 +223,8 @@ moe_status_t moe_route_noisy(const moe_config_t *cfg, const void *x,
  *              dropped or not: moe_route's counts), from the grouping's
  *              histogram
  *   x_perm     [T*k, d] dtype (out) x_perm[p] = x[perm_src[p]] for
- *              p < offsets[E]
+ *              p < offsets[E]; or NULL: no rows are moved (the grouping
+ *              only; moe_expert_up can read the rows of x in place)
  *   ws         workspace >= moe_workspace_bytes() */
 moe_status_t moe_permute(const moe_config_t *cfg, const int32_t *topk_idx,
                          const float *topk_w, const float *logits, const void *x,
@@ -236,23 +237,31 @@ moe_status_t moe_permute(const moe_config_t *cfg, const int32_t *topk_idx,
  * MFMA, fp32 accumulation; fp32 SIMT for dtype fp32).  Experts with no rows
  * are skipped (conditional computation: Qiita summary, "Sparsely-Gated MoE
  * layer formula").
- *   x_perm [T*k, d], x [T, d] (shared expert input; may be NULL if S = 0)
+ *   The token rows of the routed groups come from x_perm [T*k, d] (grouped
+ *   by moe_permute), or, when x_perm is NULL, straight from x: grouped row
+ *   p is x[perm_src[p]] (perm_src [T*k] int32 from moe_permute), so the
+ *   grouped copy is never written.  The gathered form needs T*d*bytes <
+ *   2^31 (else MOE_ERR_UNSUPPORTED).
+ *   x [T, d] (the shared expert's input, and the gathered rows' source; may
+ *   be NULL if S = 0 and x_perm is given); perm_src ignored if x_perm given
  *   offsets [E + 1] int32
  *   hidden [R, h] dtype (out) activation rows, R = T*k + S*T */
 moe_status_t moe_expert_up(const moe_config_t *cfg, const moe_weights_t *w,
-                           const void *x_perm, const void *x,
-                           const int32_t *offsets, void *hidden,
+                           const void *x_perm, const int32_t *perm_src,
+                           const void *x, const int32_t *offsets, void *hidden,
                            hipStream_t stream);
 
 /* The up projection of a training step: moe_expert_up, and the expert
  * pre-activations that the backward pass differentiates through, so that
  * moe_backward need not recompute them.  bf16 layers only (else
  * MOE_ERR_UNSUPPORTED).
+ *   x_perm, perm_src, x, offsets as for moe_expert_up
  *   hidden [R, h] bf16 (out) as for moe_expert_up
  *   preact [R, N_up] bf16 (out): SwiGLU x W1^T (gate rows, columns 0..h-1)
  *          and x W3^T (up rows, columns h..2h-1); GELU x W1^T + b1 */
 moe_status_t moe_expert_up_train(const moe_config_t *cfg, const moe_weights_t *w,
-                                 const void *x_perm, const void *x, const int32_t *offsets,
+                                 const void *x_perm, const int32_t *perm_src,
+                                 const void *x, const int32_t *offsets,
                                  void *hidden, void *preact, hipStream_t stream);
 
 /* Down projection of every group: y_perm[r] = W2[e] hidden[r] (+ b2[e]).
@@ -261,11 +270,12 @@ moe_status_t moe_expert_down(const moe_config_t *cfg, const moe_weights_t *w,
                              const void *hidden, const int32_t *offsets,
                              void *y_perm, hipStream_t stream);
 
-/* moe_expert_up then moe_expert_down, hidden rows in the workspace. */
+/* moe_expert_up then moe_expert_down, hidden rows in the workspace; the
+ * token rows as for moe_expert_up (x_perm, or perm_src and x). */
 moe_status_t moe_expert_ffn(const moe_config_t *cfg, const moe_weights_t *w,
-                            const void *x_perm, const void *x,
-                            const int32_t *offsets, void *y_perm, void *ws,
-                            size_t ws_bytes, hipStream_t stream);
+                            const void *x_perm, const int32_t *perm_src,
+                            const void *x, const int32_t *offsets, void *y_perm,
+                            void *ws, size_t ws_bytes, hipStream_t stream);
 
 /* Collect: y[t] = sum_{j<k} topk_w[t,j] * y_perm[pos[t*k+j]] (+ the shared
  * row y_perm[T*k + t] with weight 1), accumulated in fp32 in slot order and
@@ -276,7 +286,8 @@ moe_status_t moe_combine(const moe_config_t *cfg, const void *y_perm,
                          const int32_t *pos, const float *topk_w, void *y,
                          hipStream_t stream);
 
-/* The whole layer: route, permute, expert up/down, combine.
+/* The whole layer: route, permute, expert up/down, combine (the up
+ * projection reads the token rows of x in place when T*d*bytes < 2^31).
  *   x [T, d] (in); y [T, d] (out); topk_idx, topk_w, counts, importance as
  *   above (out, required); stats [3] double or NULL (out). */
 moe_status_t moe_forward(const moe_config_t *cfg, const moe_weights_t *w,

@@ -33,7 +33,7 @@ MOE_OVERFLOW_NEXT_CHOICE = 1
 
 # The ABI this binding marshals for (moe.h's MOE_ABI_VERSION): a library of
 # another version may take other argument lists, so lib() refuses it.
-ABI_VERSION = 8
+ABI_VERSION = 9
 
 EXPORTS = (
     "moe_abi_version", "moe_status_string", "moe_workspace_bytes",
@@ -90,13 +90,13 @@ def lib():
             "moe_backward_workspace_bytes": [P, P],
             "moe_backward": [P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, C.c_float, P, P,
                              C.c_size_t, P],
-            "moe_expert_up_train": [P, P, P, P, P, P, P, P],
+            "moe_expert_up_train": [P, P, P, P, P, P, P, P, P],
             "moe_route_noisy": [P, P, P, P, P, P, P, P, P, P, P, P, P, P, P,
                                 C.c_size_t, P],
             "moe_permute": [P, P, P, P, P, P, P, P, P, P, P, P, P, C.c_size_t, P],
-            "moe_expert_up": [P, P, P, P, P, P, P],
+            "moe_expert_up": [P, P, P, P, P, P, P, P],
             "moe_expert_down": [P, P, P, P, P, P],
-            "moe_expert_ffn": [P, P, P, P, P, P, P, C.c_size_t, P],
+            "moe_expert_ffn": [P, P, P, P, P, P, P, P, C.c_size_t, P],
             "moe_combine": [P, P, P, P, P, P],
             "moe_forward": [P, P, P, P, P, P, P, P, P, P, C.c_size_t, P],
             "moe_param_counts": [P, P, P],
@@ -251,10 +251,11 @@ def moe_backward(cfg, w: MoeWeights, x, dy, topk_idx, topk_w, offsets, pos, x_pe
 
 
 def moe_expert_up_train(cfg, w: MoeWeights, x_perm, x, offsets, hidden, preact,
-                        stream=None) -> None:
+                        stream=None, perm_src=None) -> None:
+    """x_perm None: the token rows are x[perm_src[p]], read in place."""
     _check("moe_expert_up_train", lib().moe_expert_up_train(
-        C.byref(cfg), C.byref(w), _ptr(x_perm), _ptr(x), _ptr(offsets), _ptr(hidden),
-        _ptr(preact), _stream(stream)))
+        C.byref(cfg), C.byref(w), _ptr(x_perm), _ptr(perm_src), _ptr(x), _ptr(offsets),
+        _ptr(hidden), _ptr(preact), _stream(stream)))
 
 
 def moe_route_noisy(cfg, x, w_gate, b_gate, w_noise, noise, clean_logits, noise_scale,
@@ -279,9 +280,10 @@ def moe_permute(cfg, topk_idx, topk_w, x, offsets, perm_src, pos, importance,
 
 
 def moe_expert_up(cfg, w: MoeWeights, x_perm, x, offsets, hidden,
-                  stream=None) -> None:
+                  stream=None, perm_src=None) -> None:
+    """x_perm None: the token rows are x[perm_src[p]], read in place."""
     _check("moe_expert_up", lib().moe_expert_up(
-        C.byref(cfg), C.byref(w), _ptr(x_perm), _ptr(x), _ptr(offsets),
+        C.byref(cfg), C.byref(w), _ptr(x_perm), _ptr(perm_src), _ptr(x), _ptr(offsets),
         _ptr(hidden), _stream(stream)))
 
 
@@ -293,10 +295,10 @@ def moe_expert_down(cfg, w: MoeWeights, hidden, offsets, y_perm,
 
 
 def moe_expert_ffn(cfg, w: MoeWeights, x_perm, x, offsets, y_perm, ws,
-                   ws_bytes=None, stream=None) -> None:
+                   ws_bytes=None, stream=None, perm_src=None) -> None:
     nb = _nbytes(ws) if ws_bytes is None and ws is not None else (ws_bytes or 0)
     _check("moe_expert_ffn", lib().moe_expert_ffn(
-        C.byref(cfg), C.byref(w), _ptr(x_perm), _ptr(x), _ptr(offsets),
+        C.byref(cfg), C.byref(w), _ptr(x_perm), _ptr(perm_src), _ptr(x), _ptr(offsets),
         _ptr(y_perm), _ptr(ws), nb, _stream(stream)))
 
 

@@ -22,21 +22,22 @@ hipError_t launch_noisy_gate(const float *noise, int T, int E, int k, const floa
                              hipStream_t s);
 hipError_t launch_expert_up_bf16(bool swiglu, const int32_t *offsets, int E, int S,
                                  int T, int k, int d, int h, const void *x_perm,
-                                 const void *x, const void *w_up,
+                                 const int32_t *perm_src, const void *x, const void *w_up,
                                  const void *w_up_shared, const void *b_up,
                                  void *hidden, hipStream_t s);
 hipError_t launch_expert_up_train_bf16(bool swiglu, const int32_t *offsets, int E, int S,
                                        int T, int k, int d, int h, const void *x_perm,
-                                       const void *x, const void *w_up,
-                                       const void *w_up_shared, const void *b_up,
-                                       void *hidden, void *preact, hipStream_t s);
+                                       const int32_t *perm_src, const void *x,
+                                       const void *w_up, const void *w_up_shared,
+                                       const void *b_up, void *hidden, void *preact,
+                                       hipStream_t s);
 hipError_t launch_expert_down_bf16(const int32_t *offsets, int E, int S, int T, int k,
                                    int d, int h, const void *hidden,
                                    const void *w_down, const void *w_down_shared,
                                    const void *b_down, void *y_perm, hipStream_t s);
 hipError_t launch_expert_up_f32(bool swiglu, const int32_t *offsets, int E, int S,
                                 int T, int k, int d, int h, const void *x_perm,
-                                const void *x, const void *w_up,
+                                const int32_t *perm_src, const void *x, const void *w_up,
                                 const void *w_up_shared, const void *b_up,
                                 void *hidden, hipStream_t s);
 hipError_t launch_expert_down_f32(const int32_t *offsets, int E, int S, int T, int k,
@@ -112,6 +113,13 @@ bool reroutes(const moe_config_t *c) {
   return c->capacity > 0 && c->overflow == MOE_OVERFLOW_NEXT_CHOICE;
 }
 
+// moe_forward reads the token rows of the up projection from x in place
+// (no grouped copy) whenever 32-bit byte offsets reach every row of x.
+bool gathers(const moe_config_t *c) {
+  return (uint64_t)c->num_tokens * c->d_model * (c->dtype == MOE_DTYPE_BF16 ? 2 : 4) <
+         (1ull << 31);
+}
+
 Layout layout(const moe_config_t *c) {
   const int64_t T = c->num_tokens, n = T * c->top_k;
   const int64_t R = n + (int64_t)c->num_shared * T;
@@ -134,7 +142,7 @@ Layout layout(const moe_config_t *c) {
   L.perm_src = o;  o += align_up(sizeof(int32_t) * (size_t)n);
   L.pos = o;       o += align_up(sizeof(int32_t) * (size_t)n);
   L.logits = o;    o += align_up(sizeof(float) * (reroutes(c) ? (size_t)T * E : 0));
-  L.x_perm = o;    o += align_up(es * (size_t)n * c->d_model);
+  L.x_perm = o;    o += align_up(gathers(c) ? 0 : es * (size_t)n * c->d_model);
   L.hidden = o;    o += align_up(es * (size_t)R * c->d_hidden);
   L.y_perm = o;    o += align_up(es * (size_t)R * c->d_model);
   L.total = o;
@@ -327,7 +335,7 @@ moe_status_t permute_impl(const moe_config_t *cfg, const int32_t *topk_idx,
   if (!dev_ok(offsets) || !dev_ok(importance) || !opt_ok(stats) || !opt_ok(counts_out))
     return MOE_ERR_INVALID_ARGUMENT;
   if (T > 0 && (!dev_ok(topk_idx) || !dev_ok(topk_w) || !dev_ok(x) ||
-                !dev_ok(perm_src) || !dev_ok(pos) || !dev_ok(x_perm) || !dev_ok(ws) ||
+                !dev_ok(perm_src) || !dev_ok(pos) || !opt_ok(x_perm) || !dev_ok(ws) ||
                 (reroutes(cfg) && !dev_ok(logits))))
     return MOE_ERR_INVALID_ARGUMENT;
   const Layout L = layout(cfg);
@@ -370,45 +378,58 @@ moe_status_t moe_permute(const moe_config_t *cfg, const int32_t *topk_idx,
                       stats, x_perm, ws, ws_bytes, stream, counts);
 }
 
+// The token rows of the up projection: x_perm (the grouped copy), or, when
+// x_perm is NULL, rows perm_src[p] of x read in place.  The gathered rows are
+// addressed with 32-bit byte offsets into x.
+moe_status_t check_up_rows(const moe_config_t *cfg, const void *x_perm,
+                           const int32_t *perm_src, const void *x) {
+  if (x_perm) return dev_ok(x_perm) && (!cfg->num_shared || dev_ok(x)) ? MOE_OK
+                                                                     : MOE_ERR_INVALID_ARGUMENT;
+  if (!dev_ok(perm_src) || !dev_ok(x)) return MOE_ERR_INVALID_ARGUMENT;
+  if ((uint64_t)cfg->num_tokens * cfg->d_model * elem_bytes(cfg) >= (1ull << 31))
+    return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
 moe_status_t moe_expert_up(const moe_config_t *cfg, const moe_weights_t *w,
-                           const void *x_perm, const void *x, const int32_t *offsets,
-                           void *hidden, hipStream_t stream) {
+                           const void *x_perm, const int32_t *perm_src, const void *x,
+                           const int32_t *offsets, void *hidden, hipStream_t stream) {
   moe_status_t st = check_cfg(cfg);
   if (st != MOE_OK) return st;
   if ((st = check_weights(cfg, w, true, false, false)) != MOE_OK) return st;
   const int T = (int)cfg->num_tokens;
   if (T == 0) return MOE_OK;
-  if (!dev_ok(x_perm) || !dev_ok(offsets) || !dev_ok(hidden) ||
-      (cfg->num_shared && !dev_ok(x)))
-    return MOE_ERR_INVALID_ARGUMENT;
+  if (!dev_ok(offsets) || !dev_ok(hidden)) return MOE_ERR_INVALID_ARGUMENT;
+  if ((st = check_up_rows(cfg, x_perm, perm_src, x)) != MOE_OK) return st;
   clear_pending_error();
   const bool swi = cfg->act == MOE_ACT_SWIGLU;
   if (cfg->dtype == MOE_DTYPE_BF16)
     return hip_status(moe::launch_expert_up_bf16(
         swi, offsets, cfg->num_experts, cfg->num_shared, T, cfg->top_k, cfg->d_model,
-        cfg->d_hidden, x_perm, x, w->w_up, w->w_up_shared, w->b_up, hidden, stream));
+        cfg->d_hidden, x_perm, perm_src, x, w->w_up, w->w_up_shared, w->b_up, hidden,
+        stream));
   return hip_status(moe::launch_expert_up_f32(
       swi, offsets, cfg->num_experts, cfg->num_shared, T, cfg->top_k, cfg->d_model,
-      cfg->d_hidden, x_perm, x, w->w_up, w->w_up_shared, w->b_up, hidden, stream));
+      cfg->d_hidden, x_perm, perm_src, x, w->w_up, w->w_up_shared, w->b_up, hidden, stream));
 }
 
 moe_status_t moe_expert_up_train(const moe_config_t *cfg, const moe_weights_t *w,
-                                 const void *x_perm, const void *x, const int32_t *offsets,
-                                 void *hidden, void *preact, hipStream_t stream) {
+                                 const void *x_perm, const int32_t *perm_src, const void *x,
+                                 const int32_t *offsets, void *hidden, void *preact,
+                                 hipStream_t stream) {
   moe_status_t st = check_cfg(cfg);
   if (st != MOE_OK) return st;
   if (cfg->dtype != MOE_DTYPE_BF16) return MOE_ERR_UNSUPPORTED;
   if ((st = check_weights(cfg, w, true, false, false)) != MOE_OK) return st;
   const int T = (int)cfg->num_tokens;
   if (T == 0) return MOE_OK;
-  if (!dev_ok(x_perm) || !dev_ok(offsets) || !dev_ok(hidden) || !dev_ok(preact) ||
-      (cfg->num_shared && !dev_ok(x)))
-    return MOE_ERR_INVALID_ARGUMENT;
+  if (!dev_ok(offsets) || !dev_ok(hidden) || !dev_ok(preact)) return MOE_ERR_INVALID_ARGUMENT;
+  if ((st = check_up_rows(cfg, x_perm, perm_src, x)) != MOE_OK) return st;
   clear_pending_error();
   return hip_status(moe::launch_expert_up_train_bf16(
       cfg->act == MOE_ACT_SWIGLU, offsets, cfg->num_experts, cfg->num_shared, T, cfg->top_k,
-      cfg->d_model, cfg->d_hidden, x_perm, x, w->w_up, w->w_up_shared, w->b_up, hidden,
-      preact, stream));
+      cfg->d_model, cfg->d_hidden, x_perm, perm_src, x, w->w_up, w->w_up_shared, w->b_up,
+      hidden, preact, stream));
 }
 
 moe_status_t moe_expert_down(const moe_config_t *cfg, const moe_weights_t *w,
@@ -432,18 +453,19 @@ moe_status_t moe_expert_down(const moe_config_t *cfg, const moe_weights_t *w,
 }
 
 moe_status_t moe_expert_ffn(const moe_config_t *cfg, const moe_weights_t *w,
-                            const void *x_perm, const void *x, const int32_t *offsets,
-                            void *y_perm, void *ws, size_t ws_bytes, hipStream_t stream) {
+                            const void *x_perm, const int32_t *perm_src, const void *x,
+                            const int32_t *offsets, void *y_perm, void *ws, size_t ws_bytes,
+                            hipStream_t stream) {
   moe_status_t st = check_cfg(cfg);
   if (st != MOE_OK) return st;
   if ((st = check_weights(cfg, w, true, true, false)) != MOE_OK) return st;
   if (cfg->num_tokens == 0) return MOE_OK;
   if (!dev_ok(ws)) return MOE_ERR_INVALID_ARGUMENT;
   if (ws_bytes < hidden_bytes(cfg)) return MOE_ERR_WORKSPACE_TOO_SMALL;
-  if (!dev_ok(x_perm) || !dev_ok(offsets) || !dev_ok(y_perm) ||
-      (cfg->num_shared && !dev_ok(x)))
-    return MOE_ERR_INVALID_ARGUMENT;
-  if ((st = moe_expert_up(cfg, w, x_perm, x, offsets, ws, stream)) != MOE_OK) return st;
+  if (!dev_ok(offsets) || !dev_ok(y_perm)) return MOE_ERR_INVALID_ARGUMENT;
+  if ((st = check_up_rows(cfg, x_perm, perm_src, x)) != MOE_OK) return st;
+  if ((st = moe_expert_up(cfg, w, x_perm, perm_src, x, offsets, ws, stream)) != MOE_OK)
+    return st;
   return moe_expert_down(cfg, w, ws, offsets, y_perm, stream);
 }
 
@@ -486,7 +508,7 @@ moe_status_t moe_forward(const moe_config_t *cfg, const moe_weights_t *w, const 
   int32_t *offsets = at<int32_t>(ws, L.offsets);
   int32_t *perm_src = at<int32_t>(ws, L.perm_src);
   int32_t *pos = at<int32_t>(ws, L.pos);
-  void *x_perm = at<char>(ws, L.x_perm);
+  void *x_perm = gathers(cfg) ? nullptr : at<char>(ws, L.x_perm);
   void *hidden = at<char>(ws, L.hidden);
   void *y_perm = at<char>(ws, L.y_perm);
   float *logits = reroutes(cfg) ? at<float>(ws, L.logits) : nullptr;   // next choices
@@ -497,7 +519,8 @@ moe_status_t moe_forward(const moe_config_t *cfg, const moe_weights_t *w, const 
   if ((st = permute_impl(cfg, topk_idx, topk_w, logits, x, offsets, perm_src, pos, importance,
                          stats, x_perm, ws, L.permute_end, stream, counts)) != MOE_OK)
     return st;
-  if ((st = moe_expert_up(cfg, w, x_perm, x, offsets, hidden, stream)) != MOE_OK) return st;
+  if ((st = moe_expert_up(cfg, w, x_perm, perm_src, x, offsets, hidden, stream)) != MOE_OK)
+    return st;
   if ((st = moe_expert_down(cfg, w, hidden, offsets, y_perm, stream)) != MOE_OK) return st;
   return moe_combine(cfg, y_perm, pos, topk_w, y, stream);
 }

@@ -69,6 +69,11 @@ struct GemmArgs {
   int min_rows, max_rows;   // this launch takes the groups whose row count
                             // lies in [min_rows, max_rows]
   uint16_t *c_pre;          // Pre modes: [routed_rows + S*T, w_rows] pre-activations
+  // Gathered token rows (up projection): when set, grouped row p of a routed
+  // group is row gather[p] of gather_x [T, K] (the dispatch's perm_src), so
+  // the grouped copy x_perm is never written; a_routed is then unused
+  const int32_t *gather;
+  const uint16_t *gather_x;
 };
 
 // Word 3 of a raw buffer resource on gfx9-family parts (32-bit data format,
@@ -130,9 +135,29 @@ __device__ __forceinline__ void tile_prefix(const GemmArgs &a, int *tprefix, int
 // 32-bit offset per thread addresses all of its 16-byte loads.
 struct Tile {
   int g, grow0, rows, m0, n0;
+  bool gather;         // token rows gathered from GemmArgs::gather_x
   __amdgpu_buffer_rsrc_t rs_a, rs_w0, rs_w1;
   uint32_t w_stride;   // kDownKN: bytes per k row of the weights
 };
+
+// Byte offset (from the tile's A descriptor) of the start of tile-local
+// token row r.  Gathered rows: row gather[p] of x, the descriptor covering
+// all of x; a row past the group's end gets offset T * row_bytes, out of the
+// descriptor's range, so it reads zeros (as does a corrupt index).
+// Otherwise the descriptor starts at the tile's first row and ends with the
+// group's last one.
+__device__ __forceinline__ uint32_t a_row_offset(const GemmArgs &a, const Tile &t, int r,
+                                                 uint32_t row_bytes) {
+  if (t.gather) {
+    int src = a.T;
+    if (t.m0 + r < t.rows) {
+      const int p = a.gather[t.grow0 + t.m0 + r];
+      if ((unsigned)p < (unsigned)a.T) src = p;
+    }
+    return (uint32_t)src * row_bytes;
+  }
+  return (uint32_t)r * row_bytes;
+}
 
 // Tile L of the launch's ragged tile space: group g owns tiles
 // [tprefix[g] * n_tiles, tprefix[g+1] * n_tiles), m-tile fastest.
@@ -160,7 +185,7 @@ __device__ __forceinline__ Tile decode_tile(const GemmArgs &a, const int *tprefi
     const int r1 = min(max(a.offsets[t.g + 1], r0), a.routed_rows);
     t.grow0 = r0;
     t.rows = r1 - r0;
-    abase = a.a_routed + (int64_t)r0 * a.K;
+    abase = a.a_routed + (int64_t)r0 * a.K;   // (unused for gathered rows)
     wbase = a.w + (int64_t)t.g * a.w_rows * a.K;
   } else {
     t.grow0 = a.routed_rows;
@@ -172,8 +197,13 @@ __device__ __forceinline__ Tile decode_tile(const GemmArgs &a, const int *tprefi
   t.n0 = nt * (SWI ? BNW / 2 : BNW);
   const uint32_t row_bytes = (uint32_t)a.K * 2u;
   const int arows = min(BM, t.rows - t.m0);
-  t.rs_a = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint16_t *>(abase + (int64_t)t.m0 * a.K), 0, arows * row_bytes, kBufferWord3);
+  t.gather = a.gather != nullptr && t.g < a.E;
+  if (t.gather)
+    t.rs_a = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>(a.gather_x), 0,
+                                               (uint32_t)a.T * row_bytes, kBufferWord3);
+  else
+    t.rs_a = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t *>(abase + (int64_t)t.m0 * a.K), 0, arows * row_bytes, kBufferWord3);
   if constexpr (KN) {
     // [K][w_rows] weights: columns n0.. of every k row; the range ends with
     // the group's matrix, so stages past K read zeros
@@ -231,6 +261,14 @@ struct TileMath {
   static __device__ __forceinline__ uint32_t voff0(uint32_t row_bytes) {
     return (uint32_t)(threadIdx.x / CH) * row_bytes + (uint32_t)(threadIdx.x % CH) * 16u;
   }
+  // per-thread offsets of the A loads of tile t (gathered or contiguous rows)
+  static __device__ __forceinline__ void a_offsets(const GemmArgs &a, const Tile &t,
+                                                   uint32_t row_bytes, uint32_t (&va)[A_LD]) {
+#pragma unroll
+    for (int i = 0; i < A_LD; ++i)
+      va[i] = a_row_offset(a, t, (int)(threadIdx.x / CH) + i * (NT / CH), row_bytes) +
+              (uint32_t)(threadIdx.x % CH) * 16u;
+  }
 
   // register-staged stage loads: every thread moves A_LD + W_LD chunks
   static constexpr void check_load_split() {
@@ -238,6 +276,7 @@ struct TileMath {
     static_assert(!SWI || (W_LD % 2 == 0), "gate and up rows split the loads evenly");
   }
   static __device__ __forceinline__ void gload(const Tile &t, uint32_t v0, uint32_t row_bytes,
+                                               const uint32_t (&va)[A_LD],
                                                u32x4_t (&ra)[A_LD], u32x4_t (&rw)[W_LD], int kt) {
     check_load_split();
     const uint32_t istride = (uint32_t)(NT / CH) * row_bytes;
@@ -246,7 +285,7 @@ struct TileMath {
     const int ko = kt * (BK * 2);
 #pragma unroll
     for (int i = 0; i < A_LD; ++i)
-      ra[i] = __builtin_amdgcn_raw_buffer_load_b128(t.rs_a, v0 + i * istride, ko, 0);
+      ra[i] = __builtin_amdgcn_raw_buffer_load_b128(t.rs_a, va[i], ko, 0);
     if constexpr (KN) {
       // chunk q: k row q / WCH of the stage, 16-byte chunk q % WCH
 #pragma unroll
@@ -503,6 +542,8 @@ void gemm_bf16_kernel(GemmArgs a) {
     const int L = slice_tile(it);
     if (L >= total_tiles) break;
     const Tile t = decode_tile<BM, BNW, TM::SWI, TM::KN>(a, tprefix, L);
+    uint32_t va[A_LD];
+    TM::a_offsets(a, t, row_bytes, va);
 
     f32x4_t acc[FW][FM];
 #pragma unroll
@@ -517,21 +558,21 @@ void gemm_bf16_kernel(GemmArgs a) {
     // (the compiler would otherwise sink them next to their LDS stores and
     // expose the whole load latency).
     if constexpr (PFD == 2) {
-      TM::gload(t, v0, row_bytes, ra0, rw0, 0);
+      TM::gload(t, v0, row_bytes, va, ra0, rw0, 0);
       TM::lstore(As[0], Ws[0], ra0, rw0);
-      TM::gload(t, v0, row_bytes, ra1, rw1, 1);
+      TM::gload(t, v0, row_bytes, va, ra1, rw1, 1);
       __syncthreads();
       int kt = 0;
       for (; kt + 2 <= nk; kt += 2) {
         // even step: LDS buffer 0 holds stage kt, registers 1 hold stage kt+1
-        TM::gload(t, v0, row_bytes, ra0, rw0, kt + 2);
+        TM::gload(t, v0, row_bytes, va, ra0, rw0, kt + 2);
         __builtin_amdgcn_sched_barrier(0);
         TM::compute(As[0], Ws[0], acc, wm, wn);
         __builtin_amdgcn_sched_barrier(0);
         TM::lstore(As[1], Ws[1], ra1, rw1);
         __syncthreads();
         // odd step: LDS buffer 1 holds stage kt+1, registers 0 hold stage kt+2
-        TM::gload(t, v0, row_bytes, ra1, rw1, kt + 3);
+        TM::gload(t, v0, row_bytes, va, ra1, rw1, kt + 3);
         __builtin_amdgcn_sched_barrier(0);
         TM::compute(As[1], Ws[1], acc, wm, wn);
         __builtin_amdgcn_sched_barrier(0);
@@ -540,12 +581,12 @@ void gemm_bf16_kernel(GemmArgs a) {
       }
       if (kt < nk) TM::compute(As[0], Ws[0], acc, wm, wn);   // odd stage count
     } else {
-      TM::gload(t, v0, row_bytes, ra0, rw0, 0);
+      TM::gload(t, v0, row_bytes, va, ra0, rw0, 0);
       TM::lstore(As[0], Ws[0], ra0, rw0);
       __syncthreads();
       for (int kt = 0; kt < nk; ++kt) {
         const int buf = kt & 1;
-        TM::gload(t, v0, row_bytes, ra0, rw0, kt + 1);
+        TM::gload(t, v0, row_bytes, va, ra0, rw0, kt + 1);
         __builtin_amdgcn_sched_barrier(0);
         TM::compute(As[buf], Ws[buf], acc, wm, wn);
         __builtin_amdgcn_sched_barrier(0);
@@ -590,14 +631,16 @@ void gemm_pp_kernel(GemmArgs a) {
   tile_prefix<NT, BM>(a, tprefix, scan_tmp);
   __syncthreads();
   const int total_tiles = tprefix[a.E + a.S] * a.n_tiles;
-  const int nk = a.K / BK;
   const uint32_t row_bytes = (uint32_t)a.K * 2u;
   const uint32_t v0 = TM::voff0(row_bytes);
+  const int nk = a.K / BK;
 
   for (int it = 0;; ++it) {
     const int L = slice_tile(it);
     if (L >= total_tiles) break;
     const Tile t = decode_tile<BM, BNW, TM::SWI, TM::KN>(a, tprefix, L);
+    uint32_t va[A_LD];
+    TM::a_offsets(a, t, row_bytes, va);
 
     f32x4_t acc[FW][FM];
 #pragma unroll
@@ -606,14 +649,14 @@ void gemm_pp_kernel(GemmArgs a) {
       for (int j = 0; j < FM; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
     u32x4_t ra[A_LD], rw[W_LD];
-    TM::gload(t, v0, row_bytes, ra, rw, 0);
+    TM::gload(t, v0, row_bytes, va, ra, rw, 0);
     TM::lstore(As[0], Ws[0], ra, rw);
-    if (nk > 1) TM::gload(t, v0, row_bytes, ra, rw, 1);
+    if (nk > 1) TM::gload(t, v0, row_bytes, va, ra, rw, 1);
     __syncthreads();
 
     auto memory_slot = [&](int kt) {
       if (kt + 1 < nk) TM::lstore(As[(kt + 1) & 1], Ws[(kt + 1) & 1], ra, rw);
-      if (kt + 2 < nk) TM::gload(t, v0, row_bytes, ra, rw, kt + 2);
+      if (kt + 2 < nk) TM::gload(t, v0, row_bytes, va, ra, rw, kt + 2);
     };
     // group 1 runs its memory slots one stage ahead; one call site each for
     // compute and memory keeps the register assignment identical for both
@@ -680,15 +723,25 @@ void gemm_dma_kernel(GemmArgs a) {
   tile_prefix<NT, BM>(a, tprefix, scan_tmp);
   __syncthreads();
   const int total_tiles = tprefix[a.E + a.S] * a.n_tiles;
-  const int nk = a.K / BK;
   const uint32_t row_bytes = (uint32_t)a.K * 2u;
   // lane -> row lane / 4, 16-byte chunk lane % 4 of a 16-row block
   const uint32_t voff = (uint32_t)(lane / 4) * row_bytes + (uint32_t)(lane % 4) * 16u;
+  const int nk = a.K / BK;
 
   for (int it = 0;; ++it) {
     const int L = slice_tile(it);
     if (L >= total_tiles) break;
     const Tile t = decode_tile<BM, BNW, TM::SWI, TM::KN>(a, tprefix, L);
+    // offsets of this lane's token-row loads (row lane / 4 of each 16-row
+    // token block the wave moves, gathered or contiguous)
+    uint32_t va[BPW];
+#pragma unroll
+    for (int i = 0; i < BPW; ++i) {
+      const int blk = min(wave * BPW + i, NBLK - 1);   // wave-uniform
+      va[i] = blk < ABLK ? a_row_offset(a, t, blk * 16 + lane / 4, row_bytes) +
+                               (uint32_t)(lane % 4) * 16u
+                         : 0u;
+    }
 
     // wave w moves blocks BPW w .. BPW w + BPW - 1 of the stage: token
     // blocks first, then weight blocks (SwiGLU: gate rows from one
@@ -699,11 +752,10 @@ void gemm_dma_kernel(GemmArgs a) {
         const int blk = min(wave * BPW + i, NBLK - 1);
         __amdgpu_buffer_rsrc_t rs;
         u32x4_t *dst;
-        int row;
+        int row = 0;
         if (blk < ABLK) {
           rs = t.rs_a;
           dst = As[s % NB] + blk * 64;
-          row = blk * 16;
         } else {
           const int wb = blk - ABLK;
           dst = Ws[s % NB] + wb * 64;
@@ -726,7 +778,10 @@ void gemm_dma_kernel(GemmArgs a) {
             row = wb * 16;
           }
         }
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, dst, 16, voff,
+        // token blocks: the lane's own row offset (gathered rows); weight
+        // blocks: the block's first row in the scalar offset
+        const uint32_t vo = blk < ABLK ? va[i] : voff;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, dst, 16, vo,
                                                  row * (int)row_bytes + s * (BK * 2), 0, 0);
       }
     };
@@ -997,6 +1052,7 @@ void gemm_wgrad_kernel(WgradArgs a) {
     const int local = L % per_g;
     Tile t;
     t.g = g;
+    t.gather = false;
     t.grow0 = 0;
     t.rows = a.M;
     t.m0 = (local % a.m_tiles) * BM;
@@ -1335,16 +1391,21 @@ hipError_t launch_wgrad_bf16(const int32_t *poff, int G, int Rp, int M, int N, c
 
 hipError_t launch_expert_up_bf16(bool swiglu, const int32_t *offsets, int E, int S,
                                  int T, int k, int d, int h, const void *x_perm,
-                                 const void *x, const void *w_up,
+                                 const int32_t *perm_src, const void *x, const void *w_up,
                                  const void *w_up_shared, const void *b_up,
                                  void *hidden, hipStream_t s) {
   GemmArgs a{};
+  if (!x_perm) {   // token rows gathered from x
+    a.gather = perm_src;
+    a.gather_x = static_cast<const uint16_t *>(x);
+  }
   a.offsets = offsets;
   a.E = E;
   a.S = S;
   a.T = T;
   a.routed_rows = T * k;
-  a.a_routed = static_cast<const uint16_t *>(x_perm);
+  // (gathered rows: a_routed only stands in for the unused grouped copy)
+  a.a_routed = static_cast<const uint16_t *>(x_perm ? x_perm : x);
   a.a_shared = static_cast<const uint16_t *>(x);
   a.K = d;
   a.w = static_cast<const uint16_t *>(w_up);
@@ -1361,16 +1422,21 @@ hipError_t launch_expert_up_bf16(bool swiglu, const int32_t *offsets, int E, int
 // the bias) that the backward pass differentiates through.
 hipError_t launch_expert_up_train_bf16(bool swiglu, const int32_t *offsets, int E, int S,
                                        int T, int k, int d, int h, const void *x_perm,
-                                       const void *x, const void *w_up,
-                                       const void *w_up_shared, const void *b_up,
-                                       void *hidden, void *preact, hipStream_t s) {
+                                       const int32_t *perm_src, const void *x,
+                                       const void *w_up, const void *w_up_shared,
+                                       const void *b_up, void *hidden, void *preact,
+                                       hipStream_t s) {
   GemmArgs a{};
+  if (!x_perm) {   // token rows gathered from x
+    a.gather = perm_src;
+    a.gather_x = static_cast<const uint16_t *>(x);
+  }
   a.offsets = offsets;
   a.E = E;
   a.S = S;
   a.T = T;
   a.routed_rows = T * k;
-  a.a_routed = static_cast<const uint16_t *>(x_perm);
+  a.a_routed = static_cast<const uint16_t *>(x_perm ? x_perm : x);
   a.a_shared = static_cast<const uint16_t *>(x);
   a.K = d;
   a.w = static_cast<const uint16_t *>(w_up);

@@ -21,6 +21,7 @@ struct F32Args {
   const float *bias;
   float *c;
   int n_out;
+  const int32_t *gather;   // or NULL: routed row p is row gather[p] of a_shared (x)
 };
 
 template <int MODE>
@@ -62,7 +63,12 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(F32Args a) {
     for (int q = tid; q < BM * BK / 4; q += 256) {
       const int r = q / (BK / 4), c = (q % (BK / 4)) * 4;
       const int row = min(m0 + r, rows - 1);
-      const float4 v = *reinterpret_cast<const float4 *>(A + (int64_t)row * a.K + k0 + c);
+      const float *arow = A + (int64_t)row * a.K;
+      if (a.gather && g < a.E) {   // the token's row of x (an index out of range reads row 0)
+        const int src = a.gather[r0 + row];
+        arow = a.a_shared + (int64_t)((unsigned)src < (unsigned)a.T ? src : 0) * a.K;
+      }
+      const float4 v = *reinterpret_cast<const float4 *>(arow + k0 + c);
       As[c + 0][r] = v.x; As[c + 1][r] = v.y; As[c + 2][r] = v.z; As[c + 3][r] = v.w;
     }
     for (int b = 0; b < NB; ++b)
@@ -122,12 +128,13 @@ static hipError_t launch_f32(const F32Args &a, hipStream_t s) {
 
 hipError_t launch_expert_up_f32(bool swiglu, const int32_t *offsets, int E, int S,
                                 int T, int k, int d, int h, const void *x_perm,
-                                const void *x, const void *w_up,
+                                const int32_t *perm_src, const void *x, const void *w_up,
                                 const void *w_up_shared, const void *b_up,
                                 void *hidden, hipStream_t s) {
   F32Args a{};
+  if (!x_perm) a.gather = perm_src;   // token rows gathered from x
   a.offsets = offsets; a.E = E; a.S = S; a.T = T; a.routed_rows = T * k;
-  a.a_routed = static_cast<const float *>(x_perm);
+  a.a_routed = static_cast<const float *>(x_perm ? x_perm : x);
   a.a_shared = static_cast<const float *>(x);
   a.K = d;
   a.w = static_cast<const float *>(w_up);

@@ -27,7 +27,7 @@ def test_library_exports_every_declared_entry_point():
     assert set(B.EXPORTS) == set(names), names
     for n in names:
         assert hasattr(lib, n), f"libmoe.so does not export {n}"
-    assert B.moe_abi_version() == B.ABI_VERSION == 8
+    assert B.moe_abi_version() == B.ABI_VERSION == 9
 
 
 def test_status_strings():
@@ -58,7 +58,11 @@ def test_workspace_covers_every_buffer():
         c = B.config_of(cfg)
         es = 2 if cfg.dtype == synthetic.BF16 else 4
         R = cfg.T * (cfg.k + cfg.S)
-        need = es * (cfg.T * cfg.k * cfg.d + R * cfg.h + R * cfg.d)
+        # hidden and expert-output rows; moe_forward reads the token rows of
+        # x in place (no grouped copy) while T * d * es < 2^31
+        need = es * (R * cfg.h + R * cfg.d)
+        if cfg.T * cfg.d * es >= 2 ** 31:
+            need += es * cfg.T * cfg.k * cfg.d
         assert B.moe_workspace_bytes(c) >= need
         assert B.moe_grouped_rows(c) == R
     assert B.moe_workspace_bytes(B.config_of(synthetic.TINY.with_(T=0))) == 0
@@ -108,9 +112,9 @@ def test_every_entry_point_rejects_bad_config(name):
         L.moe_route(r, FAKE, FAKE, None, FAKE, FAKE, FAKE, None, None),
         L.moe_permute(r, FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE, None, None, FAKE, FAKE,
                       1 << 40, None),
-        L.moe_expert_up(r, C.byref(w), FAKE, FAKE, FAKE, FAKE, None),
+        L.moe_expert_up(r, C.byref(w), FAKE, None, FAKE, FAKE, FAKE, None),
         L.moe_expert_down(r, C.byref(w), FAKE, FAKE, FAKE, None),
-        L.moe_expert_ffn(r, C.byref(w), FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 40, None),
+        L.moe_expert_ffn(r, C.byref(w), FAKE, None, FAKE, FAKE, FAKE, FAKE, 1 << 40, None),
         L.moe_combine(r, FAKE, FAKE, FAKE, FAKE, None),
         L.moe_forward(r, C.byref(w), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, 1 << 40, None),
         L.moe_param_counts(r, C.byref(C.c_int64()), C.byref(C.c_int64())),
@@ -120,7 +124,7 @@ def test_every_entry_point_rejects_bad_config(name):
         L.moe_backward(r, C.byref(w), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, None,
                        None, None, None, C.c_float(0.0), C.byref(B.grads(None, None, None, None)), FAKE,
                        1 << 40, None),
-        L.moe_expert_up_train(r, C.byref(w), FAKE, FAKE, FAKE, FAKE, FAKE, None),
+        L.moe_expert_up_train(r, C.byref(w), FAKE, None, FAKE, FAKE, FAKE, FAKE, None),
     ]
     assert calls == [status] * len(calls)
 
@@ -137,10 +141,21 @@ def test_pointer_and_workspace_checks():
     # SwiGLU experts take no biases; shared weights iff S = 1
     sw = _cfg(act=1)
     w_bias = B.MoeWeights(FAKE, None, FAKE, FAKE, FAKE, None, None, None)
-    assert L.moe_expert_up(C.byref(sw), C.byref(w_bias), FAKE, FAKE, FAKE, FAKE, None) == inv
+    assert L.moe_expert_up(C.byref(sw), C.byref(w_bias), FAKE, None, FAKE, FAKE, FAKE,
+                           None) == inv
     sh = _cfg(act=1, S=1)
     w_noshared = B.MoeWeights(FAKE, None, FAKE, None, FAKE, None, None, None)
-    assert L.moe_expert_up(C.byref(sh), C.byref(w_noshared), FAKE, FAKE, FAKE, FAKE, None) == inv
+    assert L.moe_expert_up(C.byref(sh), C.byref(w_noshared), FAKE, None, FAKE, FAKE, FAKE,
+                           None) == inv
+    # token rows: x_perm, or perm_src and x (gathered in place); neither is invalid
+    assert L.moe_expert_up(r, C.byref(w_base := B.MoeWeights(FAKE, None, FAKE, None, FAKE, None,
+                                                             None, None)),
+                           None, None, FAKE, FAKE, FAKE, None) == inv
+    assert L.moe_expert_up(r, C.byref(w_base), None, FAKE, None, FAKE, FAKE, None) == inv
+    # gathered rows are addressed with 32-bit byte offsets into x
+    big = _cfg(T=1 << 20, d=1024, h=64, E=8, k=2, act=1, dtype=1)
+    assert L.moe_expert_up(C.byref(big), C.byref(w_base), None, FAKE, FAKE, FAKE, FAKE,
+                           None) == B.MOE_ERR_UNSUPPORTED
     # workspace too small is reported before anything is enqueued
     small = B.MOE_ERR_WORKSPACE_TOO_SMALL
     w = B.MoeWeights(FAKE, None, FAKE, None, FAKE, None, None, None)
@@ -154,7 +169,7 @@ def test_pointer_and_workspace_checks():
     n_drop = B.moe_workspace_bytes(_cfg(capacity=20))
     assert B.moe_workspace_bytes(rr) > n_drop
     assert B.moe_workspace_bytes(_cfg(overflow=1)) == B.moe_workspace_bytes(_cfg())
-    assert L.moe_expert_ffn(r, C.byref(w), FAKE, FAKE, FAKE, FAKE, FAKE, 16, None) == small
+    assert L.moe_expert_ffn(r, C.byref(w), FAKE, None, FAKE, FAKE, FAKE, FAKE, 16, None) == small
     assert L.moe_load_stats(None, None, 4, None, None, None) == inv
 
 
@@ -243,3 +258,4 @@ def test_backward_checks():
     assert L.moe_backward(C.byref(bf), C.byref(w), *small) == B.MOE_ERR_WORKSPACE_TOO_SMALL
     nan = [FAKE] * 8 + [None, None, None, None, None, C.c_float(float("nan")), C.byref(g), FAKE, 1 << 40, None]
     assert L.moe_backward(C.byref(bf), C.byref(w), *nan) == inv
+

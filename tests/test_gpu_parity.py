@@ -281,3 +281,65 @@ def test_full_size_forward(name):
     toks = range(cfg.T) if n is None else covering_tokens(ridx, n)
     err = check_outputs(L, res["y"], toks)
     print(f"{name}: max-relative error {err:.3e} over {len(toks)} of {cfg.T} rows")
+
+
+GATHER_CASES = {
+    "small-groups": dict(T=100, d=128, h=128, E=16, k=2, act=SWIGLU, dtype=BF16),
+    "three-classes-shared": dict(T=1000, d=128, h=256, E=8, k=2, act=SWIGLU, dtype=BF16, S=1,
+                                 bias=True),
+    "dma-large-groups": dict(T=1200, d=256, h=512, E=3, k=2, act=SWIGLU, dtype=BF16),
+    "pp-long-k": dict(T=300, d=8256, h=128, E=4, k=2, act=SWIGLU, dtype=BF16),
+    "gelu-bias": dict(T=700, d=128, h=192, E=4, k=2, act=GELU, dtype=BF16, expert_bias=True),
+    "f32-gelu-bias": dict(T=200, d=128, h=256, E=6, k=2, act=GELU, dtype=F32, expert_bias=True),
+}
+
+
+@pytest.mark.parametrize("name", list(GATHER_CASES))
+@pytest.mark.parametrize("capacity", [0, 70])
+def test_gathered_rows_equal_grouped_copy(name, capacity):
+    """The up projection reading the token rows of x in place (perm_src)
+    gives bitwise the result of reading the grouped copy x_perm, for every
+    GEMM kernel and tile class, with and without dropped slots; so does the
+    training up projection (hidden and pre-activations)."""
+    kw = dict(GATHER_CASES[name])
+    L = random_layer(zlib.crc32(name.encode()) % 1000, wstd=0.1, **kw)
+    if name == "three-classes-shared":
+        L.b_gate = np.float32([4, 3, 2, 1, 0, -1, -2, -3]) * np.float32(0.6)
+    dl = DeviceLayer.upload(L, capacity=capacity)
+    c = dl.cfg
+    T, k, E, d, h = L.cfg.T, L.cfg.k, L.cfg.E, L.cfg.d, L.cfg.h
+    dev = dl.x.device
+    dt = dl.act_dtype
+    R = B.moe_grouped_rows(c)
+    idx = torch.empty((T, k), dtype=torch.int32, device=dev)
+    w = torch.empty((T, k), dtype=torch.float32, device=dev)
+    B.moe_route(c, dl.x, dl.w_gate, dl.b_gate, idx, w, None)
+    ws = torch.empty(B.moe_workspace_bytes(c), dtype=torch.uint8, device=dev)
+    offsets = torch.empty(E + 1, dtype=torch.int32, device=dev)
+    perm_src = torch.empty(T * k, dtype=torch.int32, device=dev)
+    pos = torch.empty(T * k, dtype=torch.int32, device=dev)
+    imp = torch.empty(E, dtype=torch.float32, device=dev)
+    x_perm = torch.empty((T * k, d), dtype=dt, device=dev)
+    B.moe_permute(c, idx, w, dl.x, offsets, perm_src, pos, imp, None, x_perm, ws)
+    h_copy = torch.full((R, h), 7, dtype=dt, device=dev)
+    h_gath = torch.full((R, h), 7, dtype=dt, device=dev)
+    B.moe_expert_up(c, dl.weights(), x_perm, dl.x, offsets, h_copy)
+    B.moe_expert_up(c, dl.weights(), None, dl.x, offsets, h_gath, perm_src=perm_src)
+    torch.cuda.synchronize()
+    n = int(offsets[E].item())
+    rows = list(range(n)) + list(range(T * k, R))   # computed rows (kept, then shared)
+    iv = torch.int16 if dt == torch.bfloat16 else torch.int32
+    assert torch.equal(h_copy.view(iv)[rows], h_gath.view(iv)[rows])
+    if dt == torch.bfloat16:
+        nup = 2 * h if L.cfg.act == SWIGLU else h
+        p_copy = torch.empty((R, nup), dtype=dt, device=dev)
+        p_gath = torch.empty((R, nup), dtype=dt, device=dev)
+        t_copy = torch.empty_like(h_copy)
+        t_gath = torch.empty_like(h_gath)
+        B.moe_expert_up_train(c, dl.weights(), x_perm, dl.x, offsets, t_copy, p_copy)
+        B.moe_expert_up_train(c, dl.weights(), None, dl.x, offsets, t_gath, p_gath,
+                              perm_src=perm_src)
+        torch.cuda.synchronize()
+        assert torch.equal(t_copy.view(iv)[rows], t_gath.view(iv)[rows])
+        assert torch.equal(p_copy.view(iv)[rows], p_gath.view(iv)[rows])
+        assert torch.equal(t_gath.view(iv)[rows], h_gath.view(iv)[rows])
