@@ -233,6 +233,25 @@ moe_status_t moe_permute(const moe_config_t *cfg, const int32_t *topk_idx,
                          double *stats, int32_t *counts, void *x_perm, void *ws,
                          size_t ws_bytes, hipStream_t stream);
 
+/* moe_permute without a workspace argument, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation.  The scratch is a static device array
+ * of MOE_NOALLOC_SCRATCH_BYTES per GPU inside the library (its address is
+ * looked up once per device, on the first call there; the array lives until
+ * the process ends).  Arguments and results as for moe_permute.  A
+ * configuration whose dispatch scratch exceeds the array (T*k beyond about
+ * 2^21 assignments with next-choice re-routing, more without) returns
+ * MOE_ERR_WORKSPACE_TOO_SMALL before anything is enqueued.  Every call on a
+ * GPU shares that GPU's array: calls that overlap on one GPU (other streams,
+ * other host threads) race and give undefined results; calls in one stream
+ * are ordered and safe.  No call leaves state that a later one relies on. */
+#define MOE_NOALLOC_SCRATCH_BYTES (64u << 20)
+moe_status_t moe_permute_noalloc(const moe_config_t *cfg, const int32_t *topk_idx,
+                                 const float *topk_w, const float *logits, const void *x,
+                                 int32_t *offsets, int32_t *perm_src, int32_t *pos,
+                                 float *importance, double *stats, int32_t *counts,
+                                 void *x_perm, hipStream_t stream);
+
 /* Up projection + activation of every expert group (grouped GEMM on bf16
  * MFMA, fp32 accumulation; fp32 SIMT for dtype fp32).  Experts with no rows
  * are skipped (conditional computation: Qiita summary, "Sparsely-Gated MoE

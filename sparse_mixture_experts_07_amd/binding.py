@@ -41,7 +41,7 @@ EXPORTS = (
     "moe_expert_down", "moe_expert_ffn", "moe_combine", "moe_forward",
     "moe_param_counts", "moe_load_stats", "moe_expert_capacity",
     "moe_route_noisy", "moe_backward_workspace_bytes", "moe_backward",
-    "moe_expert_up_train",
+    "moe_expert_up_train", "moe_permute_noalloc",
 )
 
 
@@ -94,6 +94,7 @@ def lib():
             "moe_route_noisy": [P, P, P, P, P, P, P, P, P, P, P, P, P, P, P,
                                 C.c_size_t, P],
             "moe_permute": [P, P, P, P, P, P, P, P, P, P, P, P, P, C.c_size_t, P],
+            "moe_permute_noalloc": [P, P, P, P, P, P, P, P, P, P, P, P, P],
             "moe_expert_up": [P, P, P, P, P, P, P, P],
             "moe_expert_down": [P, P, P, P, P, P],
             "moe_expert_ffn": [P, P, P, P, P, P, P, P, C.c_size_t, P],
@@ -277,6 +278,15 @@ def moe_permute(cfg, topk_idx, topk_w, x, offsets, perm_src, pos, importance,
         C.byref(cfg), _ptr(topk_idx), _ptr(topk_w), _ptr(logits), _ptr(x), _ptr(offsets),
         _ptr(perm_src), _ptr(pos), _ptr(importance), _ptr(stats), _ptr(counts), _ptr(x_perm),
         _ptr(ws), nb, _stream(stream)))
+
+
+def moe_permute_noalloc(cfg, topk_idx, topk_w, x, offsets, perm_src, pos, importance,
+                        stats, x_perm, stream=None, logits=None, counts=None) -> None:
+    """moe_permute with the library's static scratch (no workspace)."""
+    _check("moe_permute_noalloc", lib().moe_permute_noalloc(
+        C.byref(cfg), _ptr(topk_idx), _ptr(topk_w), _ptr(logits), _ptr(x), _ptr(offsets),
+        _ptr(perm_src), _ptr(pos), _ptr(importance), _ptr(stats), _ptr(counts), _ptr(x_perm),
+        _stream(stream)))
 
 
 def moe_expert_up(cfg, w: MoeWeights, x_perm, x, offsets, hidden,

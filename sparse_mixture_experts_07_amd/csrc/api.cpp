@@ -391,6 +391,29 @@ moe_status_t check_up_rows(const moe_config_t *cfg, const void *x_perm,
   return MOE_OK;
 }
 
+static_assert(MOE_NOALLOC_SCRATCH_BYTES == moe::kNoallocScratchBytes,
+              "the header states the static scratch size");
+
+moe_status_t moe_permute_noalloc(const moe_config_t *cfg, const int32_t *topk_idx,
+                                 const float *topk_w, const float *logits, const void *x,
+                                 int32_t *offsets, int32_t *perm_src, int32_t *pos,
+                                 float *importance, double *stats, int32_t *counts,
+                                 void *x_perm, hipStream_t stream) {
+  moe_status_t st = check_cfg(cfg);
+  if (st != MOE_OK) return st;
+  // the scratch this configuration needs must fit the static array (checked
+  // on the host, before any device call)
+  if (cfg->num_tokens > 0 && layout(cfg).permute_end > moe::kNoallocScratchBytes)
+    return MOE_ERR_WORKSPACE_TOO_SMALL;
+  void *ws = nullptr;
+  if (cfg->num_tokens > 0) {
+    clear_pending_error();
+    if (moe::noalloc_scratch(&ws) != hipSuccess) return MOE_ERR_HIP;
+  }
+  return permute_impl(cfg, topk_idx, topk_w, logits, x, offsets, perm_src, pos, importance,
+                      stats, x_perm, ws, ws ? moe::kNoallocScratchBytes : 0, stream, counts);
+}
+
 moe_status_t moe_expert_up(const moe_config_t *cfg, const moe_weights_t *w,
                            const void *x_perm, const int32_t *perm_src, const void *x,
                            const int32_t *offsets, void *hidden, hipStream_t stream) {

@@ -37,4 +37,10 @@ hipError_t launch_permute_reroute(const int32_t *idx, const float *w, const floa
                                   float *perm_w, const RerouteScratch &r, hipStream_t s,
                                   int32_t *counts_out = nullptr);
 
+// The allocation-free dispatch's scratch: a static device array of this
+// many bytes per GPU; noalloc_scratch() gives the current device's address
+// (taken with hipGetSymbolAddress on the first call on each device).
+constexpr size_t kNoallocScratchBytes = size_t(64) << 20;
+hipError_t noalloc_scratch(void **ptr);
+
 }  // namespace moe

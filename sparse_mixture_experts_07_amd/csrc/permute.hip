@@ -32,6 +32,8 @@
 #include "common.h"
 #include "permute.h"
 
+#include <mutex>
+
 namespace moe {
 
 constexpr int kSeg = 1024;          // assignments per segment
@@ -545,6 +547,31 @@ hipError_t launch_permute_reroute(const int32_t *idx, const float *w, const floa
   // 3. the grouping by computing expert, with the row move
   return launch_permute(r.fin, w, x, T, k, E, 0, row_bytes, offsets, perm_src, pos, nullptr,
                         nullptr, x_perm, hist, r.full_off_b, perm_w, s);
+}
+
+// Scratch of the allocation-free dispatch (moe_permute_noalloc): one array
+// per GPU in the code object, held until the process ends.  Host code never
+// uses the array's name as an address (it is a host-side stand-in): the
+// device address is taken once per device with hipGetSymbolAddress and kept.
+static __device__ __align__(256) unsigned char scratch[kNoallocScratchBytes];
+
+hipError_t noalloc_scratch(void **ptr) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void *addr[kMaxDevices] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void *p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    addr[dev] = p;
+  }
+  *ptr = addr[dev];
+  return hipSuccess;
 }
 
 }  // namespace moe

@@ -259,3 +259,14 @@ def test_backward_checks():
     nan = [FAKE] * 8 + [None, None, None, None, None, C.c_float(float("nan")), C.byref(g), FAKE, 1 << 40, None]
     assert L.moe_backward(C.byref(bf), C.byref(w), *nan) == inv
 
+
+def test_noalloc_dispatch_rejects_configs_beyond_its_scratch():
+    """moe_permute_noalloc refuses, on the host and before any device call,
+    a batch whose dispatch scratch exceeds the static array."""
+    L = B.lib()
+    big = _cfg(T=1 << 22, d=64, h=64, E=256, k=8, act=1, dtype=1)
+    assert L.moe_permute_noalloc(C.byref(big), FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                 None, None, FAKE, None) == B.MOE_ERR_WORKSPACE_TOO_SMALL
+    bad = _cfg(k=9)
+    assert L.moe_permute_noalloc(C.byref(bad), FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                 None, None, FAKE, None) == B.MOE_ERR_INVALID_ARGUMENT
