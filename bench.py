@@ -281,6 +281,7 @@ def run_one(args):
     roof["frac"] = roof["achieved"] / roof["peak"]
     roof["kernel"] = "expert up projection + activation (moe_expert_up: gemm_dma_kernel / gemm_pp_kernel / gemm_bf16_kernel by group size and K)"
     roof["avg_ms"] = up_avg
+    roof["algorithmic_bytes"] = up_bytes   # per step: W_up of touched experts + A read + H write
     # HBM bytes per launch of the dominant kernel from the FETCH_SIZE and
     # WRITE_SIZE counters, scaled by the counters of a plain 1 GiB copy;
     # null when not measured for these kernel sources

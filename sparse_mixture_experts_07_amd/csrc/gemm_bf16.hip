@@ -81,14 +81,27 @@ struct GemmArgs {
 constexpr int kBufferWord3 = 0x00020000;
 
 // LDS placement of 16-byte chunk `chunk` of tile row `row`.  With 32-wide
-// k stages a row is 64 B and a fragment read (16 rows x 4 chunks) is one
-// contiguous 1 KB block: no swizzle.  With 64-wide stages the 128-B rows are
-// XOR-swizzled (pattern chosen by measuring fragment-read throughput and
-// whole-kernel time against a k32-plane layout).
+// k stages a row is 64 B and 16 rows fill one 1 KB block; in a fragment read
+// 16 lanes read one chunk of 16 consecutive rows, which unswizzled fall on
+// only 4 distinct 16-byte slots of the 256-byte bank row.  XOR-ing the chunk
+// with bits 2-3 of the row spreads the 16 rows over 16 slots.  (Measured on
+// MI355X the k32 DMA kernel's bank-conflict counter is the same with and
+// without this swizzle, and so is its time: its conflicts come from another
+// access.)  With 64-wide stages the 128-B rows are XOR-swizzled (pattern
+// chosen by measuring fragment-read throughput and whole-kernel time against
+// a k32-plane layout).  The swizzle is an XOR, so it is its own inverse:
+// swz(swz(c, r), r) = c.
 template <int BK>
 __device__ __forceinline__ int swz(int chunk, int row) {
-  if constexpr (BK == 32) return chunk;
+  if constexpr (BK == 32) return chunk ^ ((row >> 2) & 3);
   return chunk ^ ((((row >> 2) & 3) << 1) ^ ((row >> 1) & 1));
+}
+
+// DMA lane map of a k32 stage: lane l of a 16-row block (first row a
+// multiple of 16) fills LDS slot l, i.e. row l / 4, physical chunk l % 4,
+// which holds logical chunk swz(l % 4, l / 4) = (l % 4) ^ (l / 16).
+__device__ __forceinline__ uint32_t dma32_chunk_bytes(int lane) {
+  return (uint32_t)swz<32>(lane % 4, lane / 4) * 16u;
 }
 
 // Workgroup barrier that orders LDS only: the wave waits for its own LDS
@@ -724,8 +737,8 @@ void gemm_dma_kernel(GemmArgs a) {
   __syncthreads();
   const int total_tiles = tprefix[a.E + a.S] * a.n_tiles;
   const uint32_t row_bytes = (uint32_t)a.K * 2u;
-  // lane -> row lane / 4, 16-byte chunk lane % 4 of a 16-row block
-  const uint32_t voff = (uint32_t)(lane / 4) * row_bytes + (uint32_t)(lane % 4) * 16u;
+  // lane -> row lane / 4 of a 16-row block, the chunk its LDS slot holds
+  const uint32_t voff = (uint32_t)(lane / 4) * row_bytes + dma32_chunk_bytes(lane);
   const int nk = a.K / BK;
 
   for (int it = 0;; ++it) {
@@ -739,7 +752,7 @@ void gemm_dma_kernel(GemmArgs a) {
     for (int i = 0; i < BPW; ++i) {
       const int blk = min(wave * BPW + i, NBLK - 1);   // wave-uniform
       va[i] = blk < ABLK ? a_row_offset(a, t, blk * 16 + lane / 4, row_bytes) +
-                               (uint32_t)(lane % 4) * 16u
+                               dma32_chunk_bytes(lane)
                          : 0u;
     }
 
@@ -839,6 +852,13 @@ void gemm_dma_kernel(GemmArgs a) {
     __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(2 * BPW));   // stages 0 and 1
     __syncthreads();
     read_stage(0, fa0, fw0);
+    // iteration 0 DMAs stage 4 into stage 0's buffer: every wave's reads of
+    // stage 0 must be done first (later stages are read before the barrier
+    // that ends the previous iteration)
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(63));
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
 
     // two stages per trip so the register sets are named statically (nk is
     // even: K is a multiple of 64)
@@ -880,8 +900,8 @@ struct DmaLoop {
                                              int wave, int wm, int wn,
                                              f32x4_t (&acc)[FW][FM]) {
     const int lane = threadIdx.x % 64;
-    // lane -> row lane / 4, 16-byte chunk lane % 4 of a 16-row block
-    const uint32_t voff = (uint32_t)(lane / 4) * row_bytes + (uint32_t)(lane % 4) * 16u;
+    // lane -> row lane / 4 of a 16-row block, the chunk its LDS slot holds
+    const uint32_t voff = (uint32_t)(lane / 4) * row_bytes + dma32_chunk_bytes(lane);
     // wave w moves blocks BPW w .. BPW w + BPW - 1 of the stage: token
     // blocks first, then weight blocks (SwiGLU: gate rows from one
     // descriptor, up rows from the other)
@@ -959,6 +979,12 @@ struct DmaLoop {
     __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(2 * BPW));   // stages 0 and 1
     __syncthreads();
     read_stage(0, fa0, fw0);
+    // iteration 0 DMAs stage 4 into stage 0's buffer: every wave's reads of
+    // stage 0 must be done first
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(63));
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
 
     // two stages per trip so the register sets are named statically (nk is
     // even)
