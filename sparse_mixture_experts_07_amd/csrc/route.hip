@@ -357,6 +357,60 @@ __global__ void fill_i32_kernel(int32_t *p, int n, int32_t v) {
     p[i] = v;
 }
 
+// The end of every chain layout with one (token, expert) chain per lane:
+// lane (t, e) holds the unbiased chain acc of its token and expert, the EP
+// lanes of token t form one group.  Biased score, logits, KeepTopK over the
+// group (lower index wins ties), gate weights, outputs, and the workgroup's
+// count histogram cnt[] (zeroed by the caller before this point; NTH
+// threads) merged into counts with one atomic per (workgroup, expert).
+template <int EP, int NTH>
+__device__ __forceinline__ void lane_select(float acc, int t, int e, int T, int E, int k,
+                                            int gate, const float *__restrict__ bg,
+                                            int32_t *__restrict__ topk_idx,
+                                            float *__restrict__ topk_w,
+                                            int32_t *__restrict__ counts,
+                                            float *__restrict__ logits, int *cnt) {
+  const bool valid = t < T && e < E;
+  float sc = acc;
+  if (bg && e < E) sc = acc + bg[e];
+  if (logits && valid) logits[(int64_t)t * E + e] = sc;
+
+  bool avail = e < E;
+  int my_e = 0;
+  float my_v = 0.0f, s0 = 0.0f;
+  for (int j = 0; j < k; ++j) {
+    float bv = sc;
+    int be = avail ? e : 0x7fffffff;
+#pragma unroll
+    for (int off = EP / 2; off >= 1; off >>= 1) {
+      const float ov = __shfl_xor(bv, off);
+      const int oe = __shfl_xor(be, off);
+      const bool take = oe != 0x7fffffff &&
+                        (be == 0x7fffffff || ov > bv || (ov == bv && oe < be));
+      if (take) {
+        bv = ov;
+        be = oe;
+      }
+    }
+    if (be == e) avail = false;
+    if (j == 0) s0 = bv;
+    if (e == j) {
+      my_e = be;
+      my_v = bv;
+    }
+  }
+  const float gw = group_gate<EP>(gate, e, E, k, sc, acc, my_e, my_v, s0);
+  __syncthreads();   // cnt[] zeroed
+  if (t < T && e < k) {
+    topk_idx[(int64_t)t * k + e] = my_e;
+    topk_w[(int64_t)t * k + e] = gw;
+    atomicAdd(&cnt[my_e], 1);
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < E; i += NTH)
+    if (counts && cnt[i]) atomicAdd(counts + i, cnt[i]);
+}
+
 // ---------------------------------------------------------------------------
 // Few experts (E <= 64): a wavefront owns 64/EP tokens x EP experts with one
 // (token, expert) chain per lane, and streams its x and W_g rows straight
@@ -409,7 +463,6 @@ __global__ __launch_bounds__(NTH) void route_direct_kernel(
   const int wave = threadIdx.x / kWave;
   const int e = lane % EP;
   const int t = (blockIdx.x * (NTH / kWave) + wave) * TPW + lane / EP;
-  const bool valid = t < T && e < E;
   for (int i = threadIdx.x; i < EP; i += NTH) cnt[i] = 0;
 
   const uint32_t xrec = (uint32_t)T * (uint32_t)d * RowLoad<XT>::kBytes;
@@ -458,45 +511,7 @@ __global__ __launch_bounds__(NTH) void route_direct_kernel(
   for (int u = 0; u < NS; ++u)
     if (c + u < nstep) consume(u);
 
-  float sc = acc;
-  if (bg && e < E) sc = acc + bg[e];
-  if (logits && valid) logits[(int64_t)t * E + e] = sc;
-
-  // ---- KeepTopK over the EP lanes of each token (lower index wins ties) ----
-  bool avail = e < E;
-  int my_e = 0;
-  float my_v = 0.0f, s0 = 0.0f;
-  for (int j = 0; j < k; ++j) {
-    float bv = sc;
-    int be = avail ? e : 0x7fffffff;
-#pragma unroll
-    for (int off = EP / 2; off >= 1; off >>= 1) {
-      const float ov = __shfl_xor(bv, off);
-      const int oe = __shfl_xor(be, off);
-      const bool take = oe != 0x7fffffff &&
-                        (be == 0x7fffffff || ov > bv || (ov == bv && oe < be));
-      if (take) {
-        bv = ov;
-        be = oe;
-      }
-    }
-    if (be == e) avail = false;
-    if (j == 0) s0 = bv;
-    if (e == j) {
-      my_e = be;
-      my_v = bv;
-    }
-  }
-  const float gw = group_gate<EP>(gate, e, E, k, sc, acc, my_e, my_v, s0);
-  __syncthreads();   // cnt[] zeroed
-  if (t < T && e < k) {
-    topk_idx[(int64_t)t * k + e] = my_e;
-    topk_w[(int64_t)t * k + e] = gw;
-    atomicAdd(&cnt[my_e], 1);
-  }
-  __syncthreads();
-  for (int i = threadIdx.x; i < E; i += NTH)
-    if (counts && cnt[i]) atomicAdd(counts + i, cnt[i]);
+  lane_select<EP, NTH>(acc, t, e, T, E, k, gate, bg, topk_idx, topk_w, counts, logits, cnt);
 }
 
 // Workgroups of four wavefronts; one wavefront each when there are fewer
@@ -552,7 +567,6 @@ __global__ __launch_bounds__(NWV * kWave) void route_lane_kernel(
   const int tl = wave * TPW + lane / EP;   // token within the workgroup
   const int tb = blockIdx.x * G::TPB;      // first token of the workgroup
   const int t = tb + tl;
-  const bool valid = t < T && e < E;
   for (int i = threadIdx.x; i < EP; i += G::NTH) cnt[i] = 0;
 
   // buffer descriptors: x rows of this workgroup's tokens, all of W_g; reads
@@ -636,45 +650,8 @@ __global__ __launch_bounds__(NWV * kWave) void route_lane_kernel(
     }
   }
 
-  float sc = acc;
-  if (bg && e < E) sc = acc + bg[e];
-  if (logits && valid) logits[(int64_t)t * E + e] = sc;
-
-  // ---- KeepTopK over the EP lanes of each token (lower index wins ties) ----
-  bool avail = e < E;
-  int my_e = 0;
-  float my_v = 0.0f, s0 = 0.0f;
-  for (int j = 0; j < k; ++j) {
-    float bv = sc;
-    int be = avail ? e : 0x7fffffff;
-#pragma unroll
-    for (int off = EP / 2; off >= 1; off >>= 1) {
-      const float ov = __shfl_xor(bv, off);
-      const int oe = __shfl_xor(be, off);
-      const bool take = oe != 0x7fffffff &&
-                        (be == 0x7fffffff || ov > bv || (ov == bv && oe < be));
-      if (take) {
-        bv = ov;
-        be = oe;
-      }
-    }
-    if (be == e) avail = false;
-    if (j == 0) s0 = bv;
-    if (e == j) {
-      my_e = be;
-      my_v = bv;
-    }
-  }
-  const float gw = group_gate<EP>(gate, e, E, k, sc, acc, my_e, my_v, s0);
-  __syncthreads();   // cnt[] zeroed
-  if (t < T && e < k) {
-    topk_idx[(int64_t)t * k + e] = my_e;
-    topk_w[(int64_t)t * k + e] = gw;
-    atomicAdd(&cnt[my_e], 1);
-  }
-  __syncthreads();
-  for (int i = threadIdx.x; i < E; i += G::NTH)
-    if (counts && cnt[i]) atomicAdd(counts + i, cnt[i]);
+  lane_select<EP, G::NTH>(acc, t, e, T, E, k, gate, bg, topk_idx, topk_w, counts, logits,
+                          cnt);
 }
 
 template <typename XT, int EP, int NWV>

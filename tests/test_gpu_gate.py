@@ -102,3 +102,41 @@ def test_gate_mode_with_capacity():
     keep = oracle.capacity_keep(L.cfg, ridx, cap)
     assert keep.sum() < keep.size
     check_outputs(L, res["y"], range(600), keep=keep)
+
+
+@pytest.mark.parametrize("dtype", [BF16, F32], ids=["bf16", "f32"])
+@pytest.mark.parametrize("E,k,d", [(6, 2, 64), (8, 2, 192), (16, 3, 128), (32, 4, 2880),
+                                   (64, 6, 320)])
+def test_logits_output_leaves_routing_unchanged(E, k, d, dtype):
+    """moe_route with and without the logits output (decode-sized batches,
+    the one-chain-per-lane kernel): indices, weights and counts bitwise
+    equal, and the logits bit-exact against the oracle's scores, for token
+    counts around a multiple of 64, every gate mode, with and without the
+    router bias."""
+    for T in (1, 63, 64, 65, 200):
+        for gate in (synthetic.GATE_TOPK_SOFTMAX, SEL, ALL):
+            for bias in (False, True):
+                if gate == SEL and not bias:
+                    continue
+                L = random_layer(35 + T + E, T=T, d=d, h=64, E=E, k=k, act=SWIGLU,
+                                 dtype=dtype, bias=bias, gate=gate)
+                dl = DeviceLayer.upload(L)
+                c, dev = dl.cfg, dl.x.device
+                out = []
+                for with_logits in (False, True):
+                    idx = torch.empty((T, k), dtype=torch.int32, device=dev)
+                    w = torch.empty((T, k), dtype=torch.float32, device=dev)
+                    cnt = torch.empty(E, dtype=torch.int32, device=dev)
+                    lg = torch.empty((T, E), dtype=torch.float32, device=dev) if with_logits else None
+                    B.moe_route(c, dl.x, dl.w_gate, dl.b_gate, idx, w, cnt, lg)
+                    torch.cuda.synchronize()
+                    out.append((idx.cpu().numpy(), w.cpu().numpy(), cnt.cpu().numpy(),
+                                None if lg is None else lg.cpu().numpy()))
+                (i0, w0, c0, _), (i1, w1, c1, lg1) = out
+                tag = f"T={T} gate={gate} bias={bias}"
+                assert np.array_equal(i0, i1), tag
+                assert np.array_equal(w0.view(np.uint32), w1.view(np.uint32)), tag
+                assert np.array_equal(c0, c1), tag
+                _, _, rsc = oracle.route(L, want_scores=True)
+                assert np.array_equal(lg1.view(np.uint32), rsc.view(np.uint32)), tag
+                check_routing(L, i1, w1, c1)
