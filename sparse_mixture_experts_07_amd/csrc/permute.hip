@@ -254,17 +254,28 @@ __global__ __launch_bounds__(kFusedThreads) void perm_fused_kernel(
   __shared__ int koff[kMaxExperts];       // kept group starts
   __shared__ int run[NW][kMaxExperts];
   __shared__ int scan_tmp[NW];
+  __shared__ float pw[kFusedMax];         // the weights in grouped order
+  constexpr int NC = kFusedMax / kFusedThreads;
   const int tid = threadIdx.x;
   const int lane = tid % kWave;
   const int wv = tid / kWave;
 
+  // every assignment's expert and weight, loaded once up front (thread tid
+  // holds assignments tid + c * kFusedThreads)
+  int ea[NC];
+  float wa[NC];
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    const int f = tid + c * kFusedThreads;
+    ea[c] = f < n ? idx[f] : -1;
+    wa[c] = f < n ? w[f] : 0.0f;
+  }
   // 1. histogram
   for (int e = tid; e < kMaxExperts; e += kFusedThreads) h[e] = 0;
   __syncthreads();
-  for (int f = tid; f < n; f += kFusedThreads) {
-    const int e = idx[f];
-    if (static_cast<unsigned>(e) < static_cast<unsigned>(E)) atomicAdd(&h[e], 1);
-  }
+#pragma unroll
+  for (int c = 0; c < NC; ++c)
+    if (static_cast<unsigned>(ea[c]) < static_cast<unsigned>(E)) atomicAdd(&h[ea[c]], 1);
   __syncthreads();
   // 2. group offsets: exclusive scans over the experts, of every assignment
   //    (full) and of the kept ones (capacity)
@@ -288,9 +299,12 @@ __global__ __launch_bounds__(kFusedThreads) void perm_fused_kernel(
   __syncthreads();
   // 3. stable scatter, one chunk of kFusedThreads assignments at a time
   const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  for (int c0 = 0; c0 < n; c0 += kFusedThreads) {
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    const int c0 = c * kFusedThreads;
+    if (c0 >= n) break;
     const int f = c0 + tid;
-    int e = f < n ? idx[f] : -1;
+    int e = ea[c];
     const bool valid = static_cast<unsigned>(e) < static_cast<unsigned>(E);
     if (!valid) e = 0;
     uint64_t peers = __ballot(valid);
@@ -318,7 +332,8 @@ __global__ __launch_bounds__(kFusedThreads) void perm_fused_kernel(
     if (valid) {
       const int p = run[wv][e] + rank;
       const int r = p - off[e];
-      perm_w[p] = w[f];
+      perm_w[p] = wa[c];
+      pw[p] = wa[c];
       if (r < cap) {
         const int q = koff[e] + r;
         pos[f] = q;
@@ -333,7 +348,7 @@ __global__ __launch_bounds__(kFusedThreads) void perm_fused_kernel(
   __shared__ float imp[kMaxExperts];
   for (int x = wv; x < E; x += NW) {
     float sum = 0.0f;
-    for (int r = off[x] + lane; r < off[x + 1]; r += kWave) sum += perm_w[r];
+    for (int r = off[x] + lane; r < off[x + 1]; r += kWave) sum += pw[r];
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) sum += __shfl_xor(sum, o);
     if (lane == 0) {
