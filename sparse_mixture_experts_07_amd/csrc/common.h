@@ -19,17 +19,17 @@ __device__ __forceinline__ float bf16_to_f32(uint16_t b) {
   return __uint_as_float(static_cast<uint32_t>(b) << 16);
 }
 
-// float32 -> bfloat16, round to nearest, ties to even; NaN stays NaN.
-__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((u >> 16) | 0x40u);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return static_cast<uint16_t>(u >> 16);
-}
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
+// float32 -> bfloat16, round to nearest, ties to even; NaN stays NaN: the
+// gfx950 conversion instruction (v_cvt_pk_bf16_f32), two values per
+// instruction.
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return static_cast<uint32_t>(f32_to_bf16(lo)) |
-         (static_cast<uint32_t>(f32_to_bf16(hi)) << 16);
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){lo, hi}, bf16x2_t));
+}
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  return static_cast<uint16_t>(pack_bf16x2(f, 0.0f));
 }
 
 // GELU x * Phi(x) = x (1 + erf(x / sqrt 2)) / 2 in fp32, erf from
@@ -54,9 +54,10 @@ __device__ __forceinline__ float gelu_f32(float a) {
   return a < 0.0f ? h : a - h;
 }
 
-// SiLU x * sigmoid(x) in fp32.
+// SiLU x * sigmoid(x) in fp32, the reciprocal from v_rcp_f32 (1 ulp) rather
+// than an IEEE division (about twice the instructions).
 __device__ __forceinline__ float silu_f32(float g) {
-  return g / (1.0f + __expf(-g));
+  return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g));
 }
 
 __device__ __forceinline__ int ceil_div(int a, int b) { return (a + b - 1) / b; }
