@@ -699,8 +699,12 @@ void gemm_pp_kernel(GemmArgs a) {
   constexpr int NT = TM::NT, CH = TM::CH, A_LD = TM::A_LD, W_LD = TM::W_LD;
   constexpr int FM = TM::FM, FW = TM::FW;
 
-  __shared__ u32x4_t As[2][BM * CH];
-  __shared__ u32x4_t Ws[2][BNW * CH];
+  // the two stage buffers (token, then weight); between tiles they also
+  // stage the output tile
+  __shared__ u32x4_t ring[2 * (BM + BNW) * CH];
+  static_assert(BM * TM::BN_OUT * 2 <= 2 * (BM + BNW) * CH * 16, "output tile fits the ring");
+  auto As = reinterpret_cast<u32x4_t(*)[BM * CH]>(ring);
+  auto Ws = reinterpret_cast<u32x4_t(*)[BNW * CH]>(ring + 2 * BM * CH);
   __shared__ int tprefix[2 * NT + 2];
   __shared__ int scan_tmp[NT / 64];
 
@@ -751,7 +755,13 @@ void gemm_pp_kernel(GemmArgs a) {
       memory_slot(kt + grp);
       if (kt + grp < nk) lds_barrier();
     }
-    TM::epilogue(a, t, acc, wm, wn);
+    // (every compute slot ended before the last barrier: the ring is free)
+    if constexpr (mode_pre(MODE) || mode_gelu(MODE)) {
+      TM::epilogue(a, t, acc, wm, wn);
+    } else {
+      TM::epilogue_staged(a, t, acc, wm, wn, ring);
+      __syncthreads();   // the staged rows are read before the next stores
+    }
   }
 }
 
