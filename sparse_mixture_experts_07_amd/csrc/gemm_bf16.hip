@@ -27,7 +27,7 @@
 //                     memory into four rotating LDS buffers, 8 waves
 //   gemm_pp_kernel    large groups, longer K: register-staged loads, two
 //                     wave groups alternating compute and memory slots
-//   gemm_bf16_kernel  small groups (<= 64 rows, e.g. decode): 32-row tiles
+//   gemm_bf16_kernel  small groups (<= 64 rows, e.g. decode): 32- or 64-row tiles
 //                     streaming the weights, registers -> LDS, lock-step
 //
 // Measured on MI355X the large-group kernels are bound by the L2 -> CU
@@ -1405,11 +1405,11 @@ static hipError_t launch_big(const GemmArgs &a, hipStream_t s) {
   }
 }
 
-// Groups are split by row count into two tile classes, one launch each:
-// small groups (<= 64 rows: decode batches, cold experts) stream their
-// weights through 32-row tiles; larger groups use 256- or 192-row tiles.  The
+// Groups are split by row count into tile classes, one launch each: small
+// groups (<= 64 rows: decode batches, cold experts) stream their weights
+// through 32- or 64-row tiles; larger groups use 256- or 192-row tiles.  The
 // large class is skipped when no group can exceed 64 rows (every group has
-// at most T rows); the small class when groups are large on average.
+// at most T rows); the small classes when groups are large on average.
 template <int MODE>
 static hipError_t launch_classes(GemmArgs a, hipStream_t s) {
   hipError_t err = hipSuccess;
@@ -1427,6 +1427,16 @@ static hipError_t launch_classes(GemmArgs a, hipStream_t s) {
   }
   a.min_rows = 1;
   a.max_rows = 64;
+  // Groups average 16 rows or more (cold experts of a large batch): those
+  // of 33-64 rows take one 64-row tile, so each weight tile crosses the
+  // load path once instead of twice (measured 1.2 % faster on a 256-expert
+  // batch of 8192 tokens); decode batches keep the single launch.
+  if ((int64_t)a.routed_rows >= 16ll * a.E) {
+    a.min_rows = 33;
+    if ((err = launch_bm<64, 128, 2, 2, 64, 2, MODE>(a, s)) != hipSuccess) return err;
+    a.min_rows = 1;
+    a.max_rows = 32;
+  }
   return launch_bm<32, 128, 2, 2, 64, 2, MODE>(a, s);
 }
 
