@@ -66,6 +66,11 @@ def parse():
     p.add_argument("--no-decode", action="store_true",
                    help="default workload only: skip the decode-shape layer that the line "
                         "also reports")
+    p.add_argument("--weight-layout", choices=["tiled", "row-major"], default=None,
+                   help="order of the expert matrices in HBM (default for bf16 forward "
+                        "steps: tiled, rewritten once by moe_tile_weights before timing, "
+                        "as at weight loading; otherwise row-major, the only order the "
+                        "backward pass and fp32 layers read)")
     p.add_argument("--copy-calibration", action="store_true",
                    help="first copy 1 GiB device to device three times, so that a PMC "
                         "run sees a plain copy of known size beside the layer's kernels")
@@ -122,6 +127,14 @@ def run_one(args):
     ncopy = args.weight_copies or min(32, max(1, -(-(1 << 30) // layer_bytes)))
     copies = [dl] + [DeviceLayer.upload(L, capacity=cap, overflow=overflow)
                      for _ in range(ncopy - 1)]
+    layout = args.weight_layout or ("tiled" if cfg.dtype == synthetic.BF16 and not args.backward
+                                    else "row-major")
+    if layout == "tiled":
+        if args.backward or cfg.dtype != synthetic.BF16:
+            sys.exit("--weight-layout tiled: bf16 forward steps only")
+        copies = [cp.tiled() for cp in copies]
+        dl = copies[0]
+        torch.cuda.synchronize()
     copy_w = [cp.weights() for cp in copies]
     turn = [0]
     gen_s = time.time() - t_gen
@@ -351,7 +364,7 @@ def run_one(args):
                    **({"noisy_gate": True} if args.noisy else {}),
                    **({"capacity_factor": args.capacity_factor, "capacity": cap,
                        "overflow": args.overflow} if cap else {}),
-                   "weight_copies": ncopy},
+                   "weight_copies": ncopy, "weight_layout": layout},
         "roofline": roof,
         "cpu_baseline": cpu,
         "layer_tflops": layer_flops / (ms_step / 1e3) / 1e12,

@@ -42,7 +42,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 9
+#define MOE_ABI_VERSION 10
 
 typedef enum {
   MOE_OK = 0,
@@ -113,9 +113,20 @@ typedef struct {
   int32_t overflow;    /* moe_overflow_t (0 = drop); used when capacity > 0 */
 } moe_config_t;
 
+/* Storage order of the expert matrices (w_up, w_down, w_up_shared,
+ * w_down_shared); the router and the biases are always row-major. */
+typedef enum {
+  MOE_LAYOUT_ROW_MAJOR = 0, /* [rows, cols], cols contiguous */
+  MOE_LAYOUT_TILED = 1      /* bf16 only: the blocked order of moe_tile_weights,
+                               which the expert GEMMs load as whole 1 KB blocks */
+} moe_layout_t;
+
 /* Expert weights, all packed over experts into single tensors ("Weight
  * Loading Refactor" section of "Understanding MoE in Transformers").
- * Every matrix is [out_features, in_features] with in_features contiguous. */
+ * Every matrix is [out_features, in_features] with in_features contiguous
+ * (layout MOE_LAYOUT_ROW_MAJOR, the zero value), or the same numbers in the
+ * tiled order (MOE_LAYOUT_TILED; forward calls only: moe_backward returns
+ * MOE_ERR_UNSUPPORTED for it, and so does any call of an fp32 layer). */
 typedef struct {
   const float *w_gate;   /* router W_g [E, d] fp32 (required) */
   const float *b_gate;   /* router bias [E] fp32, or NULL (added to the score) */
@@ -126,6 +137,7 @@ typedef struct {
   const void *b_down;    /* GELU only: [E, d] or NULL; must be NULL for SwiGLU */
   const void *w_up_shared;   /* S = 1: [1, 2h, d], else NULL */
   const void *w_down_shared; /* S = 1: [1, d, h], else NULL */
+  int32_t layout;            /* moe_layout_t of the four expert matrices */
 } moe_weights_t;
 
 int moe_abi_version(void);
@@ -314,6 +326,25 @@ moe_status_t moe_forward(const moe_config_t *cfg, const moe_weights_t *w,
                          float *topk_w, int32_t *counts, float *importance,
                          double *stats, void *ws, size_t ws_bytes,
                          hipStream_t stream);
+
+/* Rewrites `count` row-major bf16 matrices [rows, cols] (src) into the
+ * tiled order (dst, the same number of bytes) that moe_weights_t takes with
+ * layout MOE_LAYOUT_TILED: the same expert matrices ("Weight Loading
+ * Refactor" section of "Understanding MoE in Transformers"), stored so that
+ * each 16-row x 32-column block is 1 KB of contiguous memory.  The stack of
+ * count matrices is treated as one [count*rows, cols] matrix (rows is a
+ * multiple of 16, so no block straddles two matrices).
+ *   Block (rb, kb), rb < count*rows/16, kb < cols/32, is the 1 KB at byte
+ *   offset (rb * cols/32 + kb) * 1024 of dst; its 16-byte piece p (0..63)
+ *   holds row 16*rb + p/4, columns 32*kb + 8*c .. 32*kb + 8*c + 7, where
+ *   c = (p % 4) XOR (p / 16).
+ *   rows > 0, rows % 16 == 0, cols > 0, cols % 32 == 0, count >= 0 (0: no
+ *   work), else MOE_ERR_INVALID_ARGUMENT; src and dst are device pointers,
+ *   16-byte aligned, owned by the caller, and must not overlap
+ *   (MOE_ERR_INVALID_ARGUMENT).  One kernel on `stream`; run it once when
+ *   the weights are loaded, not per forward call. */
+moe_status_t moe_tile_weights(const void *src, void *dst, int64_t count, int32_t rows,
+                              int32_t cols, hipStream_t stream);
 
 /* Backward pass: gradients of <dy, y> + importance_weight * CV^2(Importance)
  * with the top-k selection of the forward held fixed (the selection has no

@@ -30,10 +30,12 @@ MOE_GATE_BIAS_SELECTS = 1
 MOE_GATE_SOFTMAX_ALL = 2
 MOE_OVERFLOW_DROP = 0
 MOE_OVERFLOW_NEXT_CHOICE = 1
+MOE_LAYOUT_ROW_MAJOR = 0
+MOE_LAYOUT_TILED = 1
 
 # The ABI this binding marshals for (moe.h's MOE_ABI_VERSION): a library of
 # another version may take other argument lists, so lib() refuses it.
-ABI_VERSION = 9
+ABI_VERSION = 10
 
 EXPORTS = (
     "moe_abi_version", "moe_status_string", "moe_workspace_bytes",
@@ -41,7 +43,7 @@ EXPORTS = (
     "moe_expert_down", "moe_expert_ffn", "moe_combine", "moe_forward",
     "moe_param_counts", "moe_load_stats", "moe_expert_capacity",
     "moe_route_noisy", "moe_backward_workspace_bytes", "moe_backward",
-    "moe_expert_up_train", "moe_permute_noalloc",
+    "moe_expert_up_train", "moe_permute_noalloc", "moe_tile_weights",
 )
 
 
@@ -64,7 +66,8 @@ class MoeWeights(C.Structure):
     _fields_ = [("w_gate", C.c_void_p), ("b_gate", C.c_void_p),
                 ("w_up", C.c_void_p), ("b_up", C.c_void_p),
                 ("w_down", C.c_void_p), ("b_down", C.c_void_p),
-                ("w_up_shared", C.c_void_p), ("w_down_shared", C.c_void_p)]
+                ("w_up_shared", C.c_void_p), ("w_down_shared", C.c_void_p),
+                ("layout", C.c_int32)]
 
 
 _lib = None
@@ -103,6 +106,7 @@ def lib():
             "moe_param_counts": [P, P, P],
             "moe_load_stats": [P, P, C.c_int32, P, P, P],
             "moe_expert_capacity": [C.c_int64, C.c_int32, C.c_int32, C.c_double, P],
+            "moe_tile_weights": [P, P, C.c_int64, C.c_int32, C.c_int32, P],
         }
         for name, args in sig.items():
             fn = getattr(L, name)
@@ -176,11 +180,21 @@ def config_of(c, capacity: int = 0, overflow: int = 0) -> MoeConfig:
 
 
 def weights(w_gate, w_up, w_down, b_gate=None, b_up=None, b_down=None,
-            w_up_shared=None, w_down_shared=None) -> MoeWeights:
-    """Pointer struct; the caller keeps the tensors alive while it is used."""
+            w_up_shared=None, w_down_shared=None,
+            layout: int = MOE_LAYOUT_ROW_MAJOR) -> MoeWeights:
+    """Pointer struct; the caller keeps the tensors alive while it is used.
+    layout: MOE_LAYOUT_TILED when the four expert matrices went through
+    moe_tile_weights."""
     return MoeWeights(_ptr(w_gate), _ptr(b_gate), _ptr(w_up), _ptr(b_up),
                       _ptr(w_down), _ptr(b_down), _ptr(w_up_shared),
-                      _ptr(w_down_shared))
+                      _ptr(w_down_shared), layout)
+
+
+def moe_tile_weights(src, dst, count: int, rows: int, cols: int, stream=None) -> None:
+    """dst (same size as src) = the count bf16 matrices [rows, cols] of src
+    in the tiled order of MOE_LAYOUT_TILED."""
+    _check("moe_tile_weights", lib().moe_tile_weights(
+        _ptr(src), _ptr(dst), count, rows, cols, _stream(stream)))
 
 
 # ------------------------------------------------------------ entry points --

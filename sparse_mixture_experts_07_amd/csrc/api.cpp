@@ -24,17 +24,20 @@ hipError_t launch_expert_up_bf16(bool swiglu, const int32_t *offsets, int E, int
                                  int T, int k, int d, int h, const void *x_perm,
                                  const int32_t *perm_src, const void *x, const void *w_up,
                                  const void *w_up_shared, const void *b_up,
-                                 void *hidden, hipStream_t s);
+                                 void *hidden, bool w_tiled, hipStream_t s);
 hipError_t launch_expert_up_train_bf16(bool swiglu, const int32_t *offsets, int E, int S,
                                        int T, int k, int d, int h, const void *x_perm,
                                        const int32_t *perm_src, const void *x,
                                        const void *w_up, const void *w_up_shared,
                                        const void *b_up, void *hidden, void *preact,
-                                       hipStream_t s);
+                                       bool w_tiled, hipStream_t s);
 hipError_t launch_expert_down_bf16(const int32_t *offsets, int E, int S, int T, int k,
                                    int d, int h, const void *hidden,
                                    const void *w_down, const void *w_down_shared,
-                                   const void *b_down, void *y_perm, hipStream_t s);
+                                   const void *b_down, void *y_perm, bool w_tiled,
+                                   hipStream_t s);
+hipError_t launch_tile_weights(const void *src, void *dst, int64_t rows, int cols,
+                               hipStream_t s);
 hipError_t launch_expert_up_f32(bool swiglu, const int32_t *offsets, int E, int S,
                                 int T, int k, int d, int h, const void *x_perm,
                                 const int32_t *perm_src, const void *x, const void *w_up,
@@ -82,6 +85,9 @@ moe_status_t check_cfg(const moe_config_t *c) {
 moe_status_t check_weights(const moe_config_t *c, const moe_weights_t *w, bool up,
                            bool down, bool router) {
   if (!w) return MOE_ERR_INVALID_ARGUMENT;
+  if (w->layout != MOE_LAYOUT_ROW_MAJOR && w->layout != MOE_LAYOUT_TILED)
+    return MOE_ERR_INVALID_ARGUMENT;
+  if (w->layout == MOE_LAYOUT_TILED && c->dtype != MOE_DTYPE_BF16) return MOE_ERR_UNSUPPORTED;
   if (router && !dev_ok(w->w_gate)) return MOE_ERR_INVALID_ARGUMENT;
   if (router && !opt_ok(w->b_gate)) return MOE_ERR_INVALID_ARGUMENT;
   const bool swi = c->act == MOE_ACT_SWIGLU;
@@ -430,7 +436,7 @@ moe_status_t moe_expert_up(const moe_config_t *cfg, const moe_weights_t *w,
     return hip_status(moe::launch_expert_up_bf16(
         swi, offsets, cfg->num_experts, cfg->num_shared, T, cfg->top_k, cfg->d_model,
         cfg->d_hidden, x_perm, perm_src, x, w->w_up, w->w_up_shared, w->b_up, hidden,
-        stream));
+        w->layout == MOE_LAYOUT_TILED, stream));
   return hip_status(moe::launch_expert_up_f32(
       swi, offsets, cfg->num_experts, cfg->num_shared, T, cfg->top_k, cfg->d_model,
       cfg->d_hidden, x_perm, perm_src, x, w->w_up, w->w_up_shared, w->b_up, hidden, stream));
@@ -452,7 +458,7 @@ moe_status_t moe_expert_up_train(const moe_config_t *cfg, const moe_weights_t *w
   return hip_status(moe::launch_expert_up_train_bf16(
       cfg->act == MOE_ACT_SWIGLU, offsets, cfg->num_experts, cfg->num_shared, T, cfg->top_k,
       cfg->d_model, cfg->d_hidden, x_perm, perm_src, x, w->w_up, w->w_up_shared, w->b_up,
-      hidden, preact, stream));
+      hidden, preact, w->layout == MOE_LAYOUT_TILED, stream));
 }
 
 moe_status_t moe_expert_down(const moe_config_t *cfg, const moe_weights_t *w,
@@ -469,7 +475,8 @@ moe_status_t moe_expert_down(const moe_config_t *cfg, const moe_weights_t *w,
   if (cfg->dtype == MOE_DTYPE_BF16)
     return hip_status(moe::launch_expert_down_bf16(
         offsets, cfg->num_experts, cfg->num_shared, T, cfg->top_k, cfg->d_model,
-        cfg->d_hidden, hidden, w->w_down, w->w_down_shared, w->b_down, y_perm, stream));
+        cfg->d_hidden, hidden, w->w_down, w->w_down_shared, w->b_down, y_perm,
+        w->layout == MOE_LAYOUT_TILED, stream));
   return hip_status(moe::launch_expert_down_f32(
       offsets, cfg->num_experts, cfg->num_shared, T, cfg->top_k, cfg->d_model,
       cfg->d_hidden, hidden, w->w_down, w->w_down_shared, w->b_down, y_perm, stream));
@@ -548,6 +555,20 @@ moe_status_t moe_forward(const moe_config_t *cfg, const moe_weights_t *w, const 
   return moe_combine(cfg, y_perm, pos, topk_w, y, stream);
 }
 
+moe_status_t moe_tile_weights(const void *src, void *dst, int64_t count, int32_t rows,
+                              int32_t cols, hipStream_t stream) {
+  if (count < 0 || rows <= 0 || rows % 16 != 0 || cols <= 0 || cols % 32 != 0)
+    return MOE_ERR_INVALID_ARGUMENT;
+  if (count == 0) return MOE_OK;
+  if (!dev_ok(src) || !dev_ok(dst)) return MOE_ERR_INVALID_ARGUMENT;
+  if (count > INT64_MAX / rows / cols / 2) return MOE_ERR_INVALID_ARGUMENT;
+  const uint64_t bytes = (uint64_t)count * rows * cols * 2;
+  const uintptr_t s0 = reinterpret_cast<uintptr_t>(src), d0 = reinterpret_cast<uintptr_t>(dst);
+  if (s0 < d0 + bytes && d0 < s0 + bytes) return MOE_ERR_INVALID_ARGUMENT;   // overlap
+  clear_pending_error();
+  return hip_status(moe::launch_tile_weights(src, dst, count * rows, cols, stream));
+}
+
 moe_status_t moe_backward_workspace_bytes(const moe_config_t *cfg, size_t *bytes) {
   moe_status_t st = check_bwd_cfg(cfg);
   if (st != MOE_OK) return st;
@@ -567,6 +588,8 @@ moe_status_t moe_backward(const moe_config_t *cfg, const moe_weights_t *w, const
   moe_status_t st = check_bwd_cfg(cfg);
   if (st != MOE_OK) return st;
   if ((st = check_weights(cfg, w, true, true, true)) != MOE_OK) return st;
+  // the backward's GEMMs read the expert matrices row-major only
+  if (w->layout != MOE_LAYOUT_ROW_MAJOR) return MOE_ERR_UNSUPPORTED;
   if (!g || !dev_ok(g->dw_gate) || !dev_ok(g->dw_up) || !dev_ok(g->dw_down) ||
       !opt_ok(g->db_gate) || !opt_ok(g->db_up) || !opt_ok(g->db_down) ||
       !opt_ok(importance) || !opt_ok(hidden) || !opt_ok(preact) || !opt_ok(logits) ||

@@ -74,6 +74,19 @@ struct GemmArgs {
   // the grouped copy x_perm is never written; a_routed is then unused
   const int32_t *gather;
   const uint16_t *gather_x;
+  // Weights (w, w_shared) in the tiled layout: each [w_rows, K] matrix is a
+  // grid of 1 KB blocks of 16 rows x 32 k, block (rb, kb) at byte
+  // (rb * K/32 + kb) * 1024, 16-byte piece p of a block holding row p / 4 and
+  // chunk (p % 4) ^ (p / 16) of the block (tile_weights_kernel writes it).
+  // The launch picks the kernels compiled for that order (template flag WT).
+  int w_tiled;
+};
+
+// Weight-load addressing of the register-staged kernels: load i of stage kt
+// reads byte v0 + i * istride + kt * kstep of the tile's weight descriptor.
+struct WAddr {
+  uint32_t v0, istride;
+  int kstep;
 };
 
 // Word 3 of a raw buffer resource on gfx9-family parts (32-bit data format,
@@ -283,16 +296,39 @@ struct TileMath {
               (uint32_t)(threadIdx.x % CH) * 16u;
   }
 
+  // The thread's weight loads: row tid / CH + i * (NT / CH), chunk tid % CH
+  // as for the token rows.  Row-major weights: from the tile's first row;
+  // tiled weights: the same row and chunk inside its 16 x 32 block, so that
+  // a wavefront's loads cover whole 1 KB blocks (whole 128-byte lines).
+  template <bool WT>
+  static __device__ __forceinline__ WAddr waddr(const GemmArgs &a, uint32_t row_bytes) {
+    WAddr w;
+    if constexpr (WT) {
+      static_assert((NT / CH) % 16 == 0, "a load's rows span whole blocks");
+      const uint32_t nkb = (uint32_t)a.K / 32u;
+      const int r = threadIdx.x / CH, c = threadIdx.x % CH;
+      const int rr = r % 16;
+      w.v0 = ((uint32_t)(r / 16) * nkb + (uint32_t)(c / 4)) * 1024u +
+             (uint32_t)(rr * 4 + ((c % 4) ^ (rr / 4))) * 16u;
+      w.istride = (uint32_t)(NT / CH / 16) * nkb * 1024u;
+      w.kstep = (BK / 32) * 1024;
+    } else {
+      w.v0 = voff0(row_bytes);
+      w.istride = (uint32_t)(NT / CH) * row_bytes;
+      w.kstep = BK * 2;
+    }
+    return w;
+  }
+
   // register-staged stage loads: every thread moves A_LD + W_LD chunks
   static constexpr void check_load_split() {
     static_assert(A_LD * NT == BM * CH && W_LD * NT == BNW * CH, "load split");
     static_assert(!SWI || (W_LD % 2 == 0), "gate and up rows split the loads evenly");
   }
-  static __device__ __forceinline__ void gload(const Tile &t, uint32_t v0, uint32_t row_bytes,
+  static __device__ __forceinline__ void gload(const Tile &t, const WAddr &wa,
                                                const uint32_t (&va)[A_LD],
                                                u32x4_t (&ra)[A_LD], u32x4_t (&rw)[W_LD], int kt) {
     check_load_split();
-    const uint32_t istride = (uint32_t)(NT / CH) * row_bytes;
     // the k offset is uniform: it goes in the scalar offset, so the vector
     // offsets stay loop-invariant (row validity is decided by them alone)
     const int ko = kt * (BK * 2);
@@ -313,10 +349,11 @@ struct TileMath {
 #pragma unroll
     for (int i = 0; i < W_LD; ++i) {
       if (!SWI || i < W_LD / 2) {
-        rw[i] = __builtin_amdgcn_raw_buffer_load_b128(t.rs_w0, v0 + i * istride, ko, 0);
+        rw[i] = __builtin_amdgcn_raw_buffer_load_b128(t.rs_w0, wa.v0 + i * wa.istride,
+                                                      kt * wa.kstep, 0);
       } else {
         rw[i] = __builtin_amdgcn_raw_buffer_load_b128(
-            t.rs_w1, v0 + (i - W_LD / 2) * istride, ko, 0);
+            t.rs_w1, wa.v0 + (i - W_LD / 2) * wa.istride, kt * wa.kstep, 0);
       }
     }
   }
@@ -596,7 +633,7 @@ __device__ __forceinline__ int slice_tile(int it) {
 // while stage k is computed.  At least two waves per SIMD: 8-wave tiles run
 // one workgroup per CU, 4-wave tiles two (their register budget is capped
 // at 256 per lane).
-template <int BM, int BNW, int WM, int WN, int BK, int PFD, int MODE>
+template <int BM, int BNW, int WM, int WN, int BK, int PFD, int MODE, bool WT>
 __global__ __launch_bounds__(WM *WN * 64) __attribute__((amdgpu_waves_per_eu(2)))
 void gemm_bf16_kernel(GemmArgs a) {
   using TM = TileMath<BM, BNW, WM, WN, BK, MODE>;
@@ -616,7 +653,7 @@ void gemm_bf16_kernel(GemmArgs a) {
   const int total_tiles = tprefix[a.E + a.S] * a.n_tiles;
   const int nk = a.K / BK;
   const uint32_t row_bytes = (uint32_t)a.K * 2u;
-  const uint32_t v0 = TM::voff0(row_bytes);
+  const WAddr wa = TM::template waddr<WT>(a, row_bytes);
 
   for (int it = 0;; ++it) {
     const int L = slice_tile(it);
@@ -638,21 +675,21 @@ void gemm_bf16_kernel(GemmArgs a) {
     // (the compiler would otherwise sink them next to their LDS stores and
     // expose the whole load latency).
     if constexpr (PFD == 2) {
-      TM::gload(t, v0, row_bytes, va, ra0, rw0, 0);
+      TM::gload(t, wa, va, ra0, rw0, 0);
       TM::lstore(As[0], Ws[0], ra0, rw0);
-      TM::gload(t, v0, row_bytes, va, ra1, rw1, 1);
+      TM::gload(t, wa, va, ra1, rw1, 1);
       __syncthreads();
       int kt = 0;
       for (; kt + 2 <= nk; kt += 2) {
         // even step: LDS buffer 0 holds stage kt, registers 1 hold stage kt+1
-        TM::gload(t, v0, row_bytes, va, ra0, rw0, kt + 2);
+        TM::gload(t, wa, va, ra0, rw0, kt + 2);
         __builtin_amdgcn_sched_barrier(0);
         TM::compute(As[0], Ws[0], acc, wm, wn);
         __builtin_amdgcn_sched_barrier(0);
         TM::lstore(As[1], Ws[1], ra1, rw1);
         __syncthreads();
         // odd step: LDS buffer 1 holds stage kt+1, registers 0 hold stage kt+2
-        TM::gload(t, v0, row_bytes, va, ra1, rw1, kt + 3);
+        TM::gload(t, wa, va, ra1, rw1, kt + 3);
         __builtin_amdgcn_sched_barrier(0);
         TM::compute(As[1], Ws[1], acc, wm, wn);
         __builtin_amdgcn_sched_barrier(0);
@@ -661,12 +698,12 @@ void gemm_bf16_kernel(GemmArgs a) {
       }
       if (kt < nk) TM::compute(As[0], Ws[0], acc, wm, wn);   // odd stage count
     } else {
-      TM::gload(t, v0, row_bytes, va, ra0, rw0, 0);
+      TM::gload(t, wa, va, ra0, rw0, 0);
       TM::lstore(As[0], Ws[0], ra0, rw0);
       __syncthreads();
       for (int kt = 0; kt < nk; ++kt) {
         const int buf = kt & 1;
-        TM::gload(t, v0, row_bytes, va, ra0, rw0, kt + 1);
+        TM::gload(t, wa, va, ra0, rw0, kt + 1);
         __builtin_amdgcn_sched_barrier(0);
         TM::compute(As[buf], Ws[buf], acc, wm, wn);
         __builtin_amdgcn_sched_barrier(0);
@@ -691,7 +728,7 @@ void gemm_bf16_kernel(GemmArgs a) {
 // 2k, group 0 in slot 2k+1, so stage k+1 is complete before slot 2k+2 and
 // two LDS buffers suffice: stage k+2 overwrites stage k only from slot
 // 2k+2 on, after both groups have finished it.
-template <int BM, int MODE>
+template <int BM, int MODE, bool WT>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2)))
 void gemm_pp_kernel(GemmArgs a) {
   constexpr int BNW = 256, WM = 4, WN = 2, BK = 64;
@@ -716,7 +753,7 @@ void gemm_pp_kernel(GemmArgs a) {
   __syncthreads();
   const int total_tiles = tprefix[a.E + a.S] * a.n_tiles;
   const uint32_t row_bytes = (uint32_t)a.K * 2u;
-  const uint32_t v0 = TM::voff0(row_bytes);
+  const WAddr wa = TM::template waddr<WT>(a, row_bytes);
   const int nk = a.K / BK;
 
   for (int it = 0;; ++it) {
@@ -733,14 +770,14 @@ void gemm_pp_kernel(GemmArgs a) {
       for (int j = 0; j < FM; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
     u32x4_t ra[A_LD], rw[W_LD];
-    TM::gload(t, v0, row_bytes, va, ra, rw, 0);
+    TM::gload(t, wa, va, ra, rw, 0);
     TM::lstore(As[0], Ws[0], ra, rw);
-    if (nk > 1) TM::gload(t, v0, row_bytes, va, ra, rw, 1);
+    if (nk > 1) TM::gload(t, wa, va, ra, rw, 1);
     __syncthreads();
 
     auto memory_slot = [&](int kt) {
       if (kt + 1 < nk) TM::lstore(As[(kt + 1) & 1], Ws[(kt + 1) & 1], ra, rw);
-      if (kt + 2 < nk) TM::gload(t, v0, row_bytes, va, ra, rw, kt + 2);
+      if (kt + 2 < nk) TM::gload(t, wa, va, ra, rw, kt + 2);
     };
     // group 1 runs its memory slots one stage ahead; one call site each for
     // compute and memory keeps the register assignment identical for both
@@ -782,7 +819,7 @@ void gemm_pp_kernel(GemmArgs a) {
 // the last stage stay in bounds (buffer descriptors; spare LDS buffers) and
 // are never used; rows past the group's end or the weight matrix only feed
 // outputs that the epilogue drops.
-template <int BM, int BNW, int WM, int WN, int MODE>
+template <int BM, int BNW, int WM, int WN, int MODE, bool WT>
 __global__ __launch_bounds__(WM *WN * 64) __attribute__((amdgpu_waves_per_eu(WM * WN / 4)))
 void gemm_dma_kernel(GemmArgs a) {
   constexpr int BK = 32, NB = 4, NW = WM * WN;
@@ -818,23 +855,33 @@ void gemm_dma_kernel(GemmArgs a) {
   __syncthreads();
   const int total_tiles = tprefix[a.E + a.S] * a.n_tiles;
   const uint32_t row_bytes = (uint32_t)a.K * 2u;
-  // lane -> row lane / 4 of a 16-row block, the chunk its LDS slot holds
+  // lane -> row lane / 4 of a 16-row block, the chunk its LDS slot holds;
+  // tiled weights hold each 16-row block of a stage as 1 KB in LDS order
   const uint32_t voff = (uint32_t)(lane / 4) * row_bytes + dma32_chunk_bytes(lane);
   const int nk = a.K / BK;
+  static_assert(!(WT && TM::KN), "k-row weights are row-major");
 
   for (int it = 0;; ++it) {
     const int L = slice_tile(it);
     if (L >= total_tiles) break;
     const Tile t = decode_tile<BM, BNW, TM::SWI, TM::KN>(a, tprefix, L);
     // offsets of this lane's token-row loads (row lane / 4 of each 16-row
-    // token block the wave moves, gathered or contiguous)
+    // token block the wave moves, gathered or contiguous); tiled weights:
+    // the lane's 16 bytes of the weight block's first stage, so that the
+    // scalar offset only steps through the stages
     uint32_t va[BPW];
 #pragma unroll
     for (int i = 0; i < BPW; ++i) {
       const int blk = min(wave * BPW + i, NBLK - 1);   // wave-uniform
-      va[i] = blk < ABLK ? a_row_offset(a, t, blk * 16 + lane / 4, row_bytes) +
-                               dma32_chunk_bytes(lane)
-                         : 0u;
+      if (blk < ABLK) {
+        va[i] = a_row_offset(a, t, blk * 16 + lane / 4, row_bytes) + dma32_chunk_bytes(lane);
+      } else if constexpr (WT) {
+        const int wb = blk - ABLK;
+        const int rb = TM::SWI && wb >= WBLK / 2 ? wb - WBLK / 2 : wb;   // block in its half
+        va[i] = (uint32_t)(rb * nk) * 1024u + (uint32_t)lane * 16u;
+      } else {
+        va[i] = 0u;
+      }
     }
 
     // wave w moves blocks BPW w .. BPW w + BPW - 1 of the stage: token
@@ -873,10 +920,11 @@ void gemm_dma_kernel(GemmArgs a) {
           }
         }
         // token blocks: the lane's own row offset (gathered rows); weight
-        // blocks: the block's first row in the scalar offset
-        const uint32_t vo = blk < ABLK ? va[i] : voff;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, dst, 16, vo,
-                                                 row * (int)row_bytes + s * (BK * 2), 0, 0);
+        // blocks: the block's first row in the scalar offset (row-major), or
+        // the block in the lane's offset and the stage's 1 KB step (tiled)
+        const uint32_t vo = blk < ABLK || WT ? va[i] : voff;
+        const int so = WT && blk >= ABLK ? s * 1024 : row * (int)row_bytes + s * (BK * 2);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, dst, 16, vo, so, 0, 0);
       }
     };
 
@@ -1352,26 +1400,27 @@ static hipError_t launch_persistent(const void *kernel, int &per_cu, GemmArgs a,
   return hipLaunchKernel(kernel, dim3((unsigned)grid), dim3(NT), args, 0, s);
 }
 
-template <int BM, int BNW, int WM, int WN, int BK, int PFD, int MODE>
+template <int BM, int BNW, int WM, int WN, int BK, int PFD, int MODE, bool WT>
 static hipError_t launch_bm(const GemmArgs &a, hipStream_t s) {
   static int per_cu = 0;
   return launch_persistent<BM, mode_swiglu(MODE) ? BNW / 2 : BNW, WM * WN * 64>(
-      reinterpret_cast<const void *>(&gemm_bf16_kernel<BM, BNW, WM, WN, BK, PFD, MODE>),
+      reinterpret_cast<const void *>(&gemm_bf16_kernel<BM, BNW, WM, WN, BK, PFD, MODE, WT>),
       per_cu, a, s);
 }
 
-template <int BM, int MODE>
+template <int BM, int MODE, bool WT>
 static hipError_t launch_pp(const GemmArgs &a, hipStream_t s) {
   static int per_cu = 0;
   return launch_persistent<BM, mode_swiglu(MODE) ? 128 : 256, 512>(
-      reinterpret_cast<const void *>(&gemm_pp_kernel<BM, MODE>), per_cu, a, s);
+      reinterpret_cast<const void *>(&gemm_pp_kernel<BM, MODE, WT>), per_cu, a, s);
 }
 
-template <int BM, int BNW, int WM, int WN, int MODE>
+template <int BM, int BNW, int WM, int WN, int MODE, bool WT>
 static hipError_t launch_dma(const GemmArgs &a, hipStream_t s) {
   static int per_cu = 0;
   return launch_persistent<BM, mode_swiglu(MODE) ? BNW / 2 : BNW, WM * WN * 64>(
-      reinterpret_cast<const void *>(&gemm_dma_kernel<BM, BNW, WM, WN, MODE>), per_cu, a, s);
+      reinterpret_cast<const void *>(&gemm_dma_kernel<BM, BNW, WM, WN, MODE, WT>), per_cu, a,
+      s);
 }
 
 // Large groups.  Row tile: 256 or 192 token rows, whichever needs fewer
@@ -1381,7 +1430,7 @@ static hipError_t launch_dma(const GemmArgs &a, hipStream_t s) {
 // is estimated as rows / BM plus half a tile per group.  Kernel: the
 // DMA-fed one up to K = 8192, the ping-pong one on longer K (measured on
 // MI355X).
-template <int MODE>
+template <int MODE, bool WT>
 static hipError_t launch_big(const GemmArgs &a, hipStream_t s) {
   const double nblk = num_cus();
   const int bn_out = mode_swiglu(MODE) ? 128 : 256;
@@ -1396,12 +1445,13 @@ static hipError_t launch_big(const GemmArgs &a, hipStream_t s) {
   // k-row weights: waves of 128 (96) token rows x 64 weight rows, so that
   // each wave makes fewer of the (twice as many) transposing weight reads
   if constexpr (mode_kn(MODE)) {
-    return bm192 ? launch_dma<192, 256, 2, 4, MODE>(a, s) : launch_dma<256, 256, 2, 4, MODE>(a, s);
+    return bm192 ? launch_dma<192, 256, 2, 4, MODE, WT>(a, s)
+                 : launch_dma<256, 256, 2, 4, MODE, WT>(a, s);
   } else {
     if (a.K <= 8192)
-      return bm192 ? launch_dma<192, 256, 4, 2, MODE>(a, s)
-                   : launch_dma<256, 256, 4, 2, MODE>(a, s);
-    return bm192 ? launch_pp<192, MODE>(a, s) : launch_pp<256, MODE>(a, s);
+      return bm192 ? launch_dma<192, 256, 4, 2, MODE, WT>(a, s)
+                   : launch_dma<256, 256, 4, 2, MODE, WT>(a, s);
+    return bm192 ? launch_pp<192, MODE, WT>(a, s) : launch_pp<256, MODE, WT>(a, s);
   }
 }
 
@@ -1410,20 +1460,20 @@ static hipError_t launch_big(const GemmArgs &a, hipStream_t s) {
 // through 32- or 64-row tiles; larger groups use 256- or 192-row tiles.  The
 // large class is skipped when no group can exceed 64 rows (every group has
 // at most T rows); the small classes when groups are large on average.
-template <int MODE>
-static hipError_t launch_classes(GemmArgs a, hipStream_t s) {
+template <int MODE, bool WT>
+static hipError_t launch_classes_t(GemmArgs a, hipStream_t s) {
   hipError_t err = hipSuccess;
   // Groups average 512 rows or more: small groups are rare enough that the
   // large-tile launch takes every group and the second launch is saved.
   if ((int64_t)a.routed_rows >= 512ll * a.E) {
     a.min_rows = 1;
     a.max_rows = 1 << 30;
-    return launch_big<MODE>(a, s);
+    return launch_big<MODE, WT>(a, s);
   }
   if (a.T > 64) {
     a.min_rows = 65;
     a.max_rows = 1 << 30;
-    if ((err = launch_big<MODE>(a, s)) != hipSuccess) return err;
+    if ((err = launch_big<MODE, WT>(a, s)) != hipSuccess) return err;
   }
   a.min_rows = 1;
   a.max_rows = 64;
@@ -1433,11 +1483,20 @@ static hipError_t launch_classes(GemmArgs a, hipStream_t s) {
   // batch of 8192 tokens); decode batches keep the single launch.
   if ((int64_t)a.routed_rows >= 16ll * a.E) {
     a.min_rows = 33;
-    if ((err = launch_bm<64, 128, 2, 2, 64, 2, MODE>(a, s)) != hipSuccess) return err;
+    if ((err = launch_bm<64, 128, 2, 2, 64, 2, MODE, WT>(a, s)) != hipSuccess) return err;
     a.min_rows = 1;
     a.max_rows = 32;
   }
-  return launch_bm<32, 128, 2, 2, 64, 2, MODE>(a, s);
+  return launch_bm<32, 128, 2, 2, 64, 2, MODE, WT>(a, s);
+}
+
+// The kernels compiled for the weights' order (k-row weights: row-major only).
+template <int MODE>
+static hipError_t launch_classes(const GemmArgs &a, hipStream_t s) {
+  if constexpr (!mode_kn(MODE)) {
+    if (a.w_tiled) return launch_classes_t<MODE, true>(a, s);
+  }
+  return launch_classes_t<MODE, false>(a, s);
 }
 
 // Plain grouped linear map c[r] = a[r] W[g]^T (+ bias[g]) over the groups of
@@ -1519,8 +1578,9 @@ hipError_t launch_expert_up_bf16(bool swiglu, const int32_t *offsets, int E, int
                                  int T, int k, int d, int h, const void *x_perm,
                                  const int32_t *perm_src, const void *x, const void *w_up,
                                  const void *w_up_shared, const void *b_up,
-                                 void *hidden, hipStream_t s) {
+                                 void *hidden, bool w_tiled, hipStream_t s) {
   GemmArgs a{};
+  a.w_tiled = w_tiled;
   if (!x_perm) {   // token rows gathered from x
     a.gather = perm_src;
     a.gather_x = static_cast<const uint16_t *>(x);
@@ -1551,8 +1611,9 @@ hipError_t launch_expert_up_train_bf16(bool swiglu, const int32_t *offsets, int 
                                        const int32_t *perm_src, const void *x,
                                        const void *w_up, const void *w_up_shared,
                                        const void *b_up, void *hidden, void *preact,
-                                       hipStream_t s) {
+                                       bool w_tiled, hipStream_t s) {
   GemmArgs a{};
+  a.w_tiled = w_tiled;
   if (!x_perm) {   // token rows gathered from x
     a.gather = perm_src;
     a.gather_x = static_cast<const uint16_t *>(x);
@@ -1579,8 +1640,9 @@ hipError_t launch_expert_down_bf16(const int32_t *offsets, int E, int S, int T,
                                    int k, int d, int h, const void *hidden,
                                    const void *w_down, const void *w_down_shared,
                                    const void *b_down, void *y_perm,
-                                   hipStream_t s) {
+                                   bool w_tiled, hipStream_t s) {
   GemmArgs a{};
+  a.w_tiled = w_tiled;
   a.offsets = offsets;
   a.E = E;
   a.S = S;
@@ -1596,6 +1658,35 @@ hipError_t launch_expert_down_bf16(const int32_t *offsets, int E, int S, int T,
   a.c = static_cast<uint16_t *>(y_perm);
   a.n_out = d;
   return launch_classes<kDown>(a, s);
+}
+
+// Tiled weight order (GemmArgs::w_tiled) of a [rows, cols] bf16 matrix
+// stack: 16-byte piece q of dst lies in block b = q / 64 = (rb, kb), rb =
+// b / (cols/32), kb = b % (cols/32), at p = q % 64, and holds row 16 rb +
+// p / 4, columns 32 kb + 8 c .. + 7 with c = (p % 4) ^ (p / 16): the LDS
+// order of a 16-row k32 block of the DMA-fed kernel.  One thread per piece,
+// consecutive threads writing consecutive pieces.
+__global__ __launch_bounds__(256) void tile_weights_kernel(const u32x4_t *__restrict__ src,
+                                                           u32x4_t *__restrict__ dst,
+                                                           int64_t pieces, int nkb) {
+  for (int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x; q < pieces;
+       q += (int64_t)gridDim.x * 256) {
+    const int64_t b = q / 64;
+    const int p = (int)(q % 64);
+    const int64_t row = (b / nkb) * 16 + p / 4;
+    const int c = (p % 4) ^ (p / 16);
+    dst[q] = src[row * (4 * nkb) + (b % nkb) * 4 + c];
+  }
+}
+
+hipError_t launch_tile_weights(const void *src, void *dst, int64_t rows, int cols,
+                               hipStream_t s) {
+  const int64_t pieces = rows * (cols / 8);
+  if (pieces == 0) return hipSuccess;
+  const int64_t blocks = std::min<int64_t>((pieces + 255) / 256, 8192);
+  tile_weights_kernel<<<dim3((unsigned)blocks), dim3(256), 0, s>>>(
+      static_cast<const u32x4_t *>(src), static_cast<u32x4_t *>(dst), pieces, cols / 32);
+  return hipGetLastError();
 }
 
 }  // namespace moe

@@ -4,7 +4,7 @@ points.  Torch only owns memory and streams here; all arithmetic of the
 layer runs in libmoe.so."""
 from __future__ import annotations
 
-from dataclasses import dataclass
+from dataclasses import dataclass, replace
 from typing import Optional
 
 import numpy as np
@@ -43,6 +43,7 @@ class DeviceLayer:
     b_down: Optional[torch.Tensor]
     w_up_shared: Optional[torch.Tensor]
     w_down_shared: Optional[torch.Tensor]
+    layout: int = B.MOE_LAYOUT_ROW_MAJOR
 
     @classmethod
     def upload(cls, layer, device="cuda", capacity: int = 0,
@@ -59,7 +60,24 @@ class DeviceLayer:
     def weights(self) -> B.MoeWeights:
         return B.weights(self.w_gate, self.w_up, self.w_down, self.b_gate,
                          self.b_up, self.b_down, self.w_up_shared,
-                         self.w_down_shared)
+                         self.w_down_shared, self.layout)
+
+    def tiled(self) -> "DeviceLayer":
+        """The same layer with its four expert matrices rewritten by
+        moe_tile_weights (bf16 layers; forward calls only)."""
+        if self.layout == B.MOE_LAYOUT_TILED:
+            return self
+
+        def tile(w):
+            if w is None:
+                return None
+            out = torch.empty_like(w)
+            B.moe_tile_weights(w, out, 1, w.numel() // w.shape[-1], w.shape[-1])
+            return out
+        return replace(self, w_up=tile(self.w_up), w_down=tile(self.w_down),
+                       w_up_shared=tile(self.w_up_shared),
+                       w_down_shared=tile(self.w_down_shared),
+                       layout=B.MOE_LAYOUT_TILED)
 
     @property
     def act_dtype(self):

@@ -27,7 +27,7 @@ def test_library_exports_every_declared_entry_point():
     assert set(B.EXPORTS) == set(names), names
     for n in names:
         assert hasattr(lib, n), f"libmoe.so does not export {n}"
-    assert B.moe_abi_version() == B.ABI_VERSION == 9
+    assert B.moe_abi_version() == B.ABI_VERSION == 10
 
 
 def test_status_strings():
@@ -270,3 +270,44 @@ def test_noalloc_dispatch_rejects_configs_beyond_its_scratch():
     bad = _cfg(k=9)
     assert L.moe_permute_noalloc(C.byref(bad), FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE,
                                  None, None, FAKE, None) == B.MOE_ERR_INVALID_ARGUMENT
+
+
+def test_tiled_layout_checks():
+    """The tiled weight order: moe_tile_weights validates its sizes and
+    pointers, the layout field takes two values, fp32 layers and the
+    backward pass refuse the tiled order, all before any launch."""
+    L = B.lib()
+    inv, uns = B.MOE_ERR_INVALID_ARGUMENT, B.MOE_ERR_UNSUPPORTED
+    far = FAKE + (1 << 30)
+    for count, rows, cols in ((-1, 16, 32), (1, 0, 32), (1, 8, 32), (1, 24, 32), (1, 16, 0),
+                              (1, 16, 48), (1, 16, -32)):
+        assert L.moe_tile_weights(FAKE, far, count, rows, cols, None) == inv, (count, rows, cols)
+    assert L.moe_tile_weights(FAKE, far, 0, 16, 32, None) == 0          # no work
+    assert L.moe_tile_weights(None, far, 1, 16, 32, None) == inv
+    assert L.moe_tile_weights(FAKE, None, 1, 16, 32, None) == inv
+    assert L.moe_tile_weights(FAKE + 8, far, 1, 16, 32, None) == inv   # misaligned
+    # overlapping source and destination (1 KB each)
+    assert L.moe_tile_weights(FAKE, FAKE + 1008, 1, 16, 32, None) == inv
+    assert L.moe_tile_weights(FAKE + 1008, FAKE, 1, 16, 32, None) == inv
+    assert L.moe_tile_weights(FAKE, FAKE, 1, 16, 32, None) == inv
+    # byte count beyond int64
+    assert L.moe_tile_weights(FAKE, far, 1 << 40, 1 << 14, 1 << 14, None) == inv
+
+    bf = _cfg(dtype=1)
+    f32 = _cfg(dtype=0)
+    tiled = B.MoeWeights(FAKE, None, FAKE, None, FAKE, None, None, None, B.MOE_LAYOUT_TILED)
+    bad = B.MoeWeights(FAKE, None, FAKE, None, FAKE, None, None, None, 2)
+    for cfg, w, want in ((f32, tiled, uns), (bf, bad, inv), (f32, bad, inv)):
+        r = C.byref(cfg)
+        calls = [
+            L.moe_expert_up(r, C.byref(w), FAKE, None, FAKE, FAKE, FAKE, None),
+            L.moe_expert_down(r, C.byref(w), FAKE, FAKE, FAKE, None),
+            L.moe_expert_ffn(r, C.byref(w), FAKE, None, FAKE, FAKE, FAKE, FAKE, 1 << 40, None),
+            L.moe_forward(r, C.byref(w), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE,
+                          1 << 40, None),
+        ]
+        assert calls == [want] * len(calls)
+    g = B.MoeGrads(FAKE, FAKE, None, FAKE, FAKE, None, None, None, None)
+    args = [FAKE] * 8 + [None, None, None, None, None, C.c_float(0.0), C.byref(g), FAKE,
+                         1 << 40, None]
+    assert L.moe_backward(C.byref(bf), C.byref(tiled), *args) == uns

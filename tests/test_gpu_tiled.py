@@ -1,0 +1,211 @@
+"""The tiled weight order (MOE_LAYOUT_TILED).
+
+moe_tile_weights must write exactly the block order include/moe.h documents
+(checked against that formula evaluated with numpy index arithmetic), and
+every forward entry point must give bitwise the same results from tiled and
+from row-major weights: the kernels and their arithmetic are the same, only
+the addresses of the weight loads differ.  The row-major path is the one
+pinned to the oracle by the other parity tests; the layers below also
+compare the tiled forward with the oracle directly, one per GEMM kernel
+(small groups in 32- and 64-row tiles, the DMA-fed large-group kernel, the
+ping-pong kernel for K > 8192), and the benchmarked shapes are checked for
+bitwise equality at full size.
+"""
+import zlib
+
+import numpy as np
+import pytest
+import torch
+
+import synthetic
+from gpu_common import check_outputs, check_routing, require_gpu, sample_tokens, to_f64
+from helpers import BF16, F32, GELU, SWIGLU, random_layer
+from sparse_mixture_experts_07_amd import binding as B
+from sparse_mixture_experts_07_amd.device import DeviceLayer, Forward
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    require_gpu()
+
+
+def tiled_order(w: np.ndarray) -> np.ndarray:
+    """The documented order of a [R, C] matrix of 16-bit values: 16-byte
+    piece q lies in block b = q // 64 = (rb, kb) with kb = b % (C/32),
+    rb = b // (C/32); at p = q % 64 it holds row 16 rb + p // 4, columns
+    32 kb + 8 c .. + 7 with c = (p % 4) ^ (p // 16)."""
+    R, C = w.shape
+    nkb = C // 32
+    pieces = w.reshape(R, C // 8, 8)
+    q = np.arange(R * C // 8)
+    b, p = q // 64, q % 64
+    row = (b // nkb) * 16 + p // 4
+    chunk = (b % nkb) * 4 + ((p % 4) ^ (p // 16))
+    return pieces[row, chunk].reshape(R, C)
+
+
+@pytest.mark.parametrize("count,rows,cols", [(1, 16, 32), (3, 64, 96), (2, 48, 4096),
+                                             (5, 32, 2880), (1, 8256, 128)])
+def test_tile_weights_writes_the_documented_order(count, rows, cols):
+    rng = np.random.default_rng(rows * 7 + cols)
+    host = rng.integers(0, 1 << 16, (count, rows, cols), dtype=np.uint16)
+    src = torch.from_numpy(host.view(np.int16)).cuda()
+    dst = torch.full_like(src, 0x5555)
+    B.moe_tile_weights(src, dst, count, rows, cols)
+    torch.cuda.synchronize()
+    got = dst.cpu().numpy().view(np.uint16).reshape(count * rows, cols)
+    assert np.array_equal(got, tiled_order(host.reshape(count * rows, cols)))
+    assert np.array_equal(src.cpu().numpy().view(np.uint16), host)   # source untouched
+    # the stack is one matrix: tiling matrix by matrix gives the same bytes
+    one = torch.empty_like(src)
+    for m in range(count):
+        B.moe_tile_weights(src[m], one[m], 1, rows, cols)
+    torch.cuda.synchronize()
+    assert torch.equal(one, dst)
+
+
+def _iv(t):
+    return t.view(torch.int16)
+
+
+# One layer per tile class and kernel of the grouped GEMM (the class follows
+# the group sizes: routed rows / E >= 512 puts every group in the large-tile
+# launch; otherwise groups of <= 32 rows take 32-row tiles, 33-64 rows
+# 64-row tiles when groups average 16 rows or more, larger ones the
+# large-tile kernel, which is the ping-pong one for K > 8192).
+LAYERS = {
+    "small32-gelu-bias": dict(T=37, d=64, h=128, E=5, k=2, act=GELU, dtype=BF16,
+                              expert_bias=True),
+    "small64-shared": dict(T=129, d=128, h=256, E=4, k=2, act=SWIGLU, dtype=BF16, S=1),
+    "e256-router-bias": dict(T=600, d=64, h=64, E=256, k=8, act=SWIGLU, dtype=BF16, bias=True),
+    "ntail-swiglu": dict(T=300, d=192, h=320, E=7, k=3, act=SWIGLU, dtype=BF16),
+    "dma-one-class-gelu": dict(T=1000, d=256, h=512, E=3, k=2, act=GELU, dtype=BF16,
+                               expert_bias=True),
+    "pp-long-k-down": dict(T=300, d=128, h=8256, E=4, k=2, act=SWIGLU, dtype=BF16),
+    "pp-long-k-up": dict(T=300, d=8256, h=128, E=4, k=2, act=SWIGLU, dtype=BF16),
+}
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("name", list(LAYERS))
+def test_tiled_forward_equals_row_major_and_oracle(name):
+    L = random_layer(zlib.crc32(name.encode()) % 1000, wstd=0.1, **LAYERS[name])
+    dl = DeviceLayer.upload(L)
+    dt = dl.tiled()
+    assert dt.layout == B.MOE_LAYOUT_TILED and dl.layout == B.MOE_LAYOUT_ROW_MAJOR
+    f_row, f_til = Forward(dl), Forward(dt)
+    f_row()
+    f_til()
+    torch.cuda.synchronize()
+    assert torch.equal(_iv(f_row.y), _iv(f_til.y))
+    assert torch.equal(f_row.topk_idx, f_til.topk_idx)
+    assert torch.equal(f_row.counts, f_til.counts)
+    # and the tiled result against the oracle itself
+    check_routing(L, f_til.topk_idx.cpu().numpy(), f_til.topk_w.cpu().numpy(),
+                  f_til.counts.cpu().numpy())
+    toks = range(L.cfg.T) if L.cfg.T <= 400 else sample_tokens(L.cfg.T, 64)
+    check_outputs(L, to_f64(f_til.y), toks)
+
+
+def test_stage_entry_points_take_tiled_weights():
+    """moe_expert_up, moe_expert_up_train (hidden and pre-activations),
+    moe_expert_down and moe_expert_ffn: bitwise equal for both orders."""
+    L = random_layer(71, T=1000, d=128, h=256, E=8, k=2, act=SWIGLU, dtype=BF16, S=1,
+                     bias=True, wstd=0.1)
+    L.b_gate = np.float32([4, 3, 2, 1, 0, -1, -2, -3]) * np.float32(0.6)
+    dl = DeviceLayer.upload(L)
+    dt = dl.tiled()
+    c = dl.cfg
+    T, k, E, d, h = L.cfg.T, L.cfg.k, L.cfg.E, L.cfg.d, L.cfg.h
+    dev = dl.x.device
+    R = B.moe_grouped_rows(c)
+    idx = torch.empty((T, k), dtype=torch.int32, device=dev)
+    w = torch.empty((T, k), dtype=torch.float32, device=dev)
+    B.moe_route(c, dl.x, dl.w_gate, dl.b_gate, idx, w, None)
+    ws = torch.empty(B.moe_workspace_bytes(c), dtype=torch.uint8, device=dev)
+    offsets = torch.empty(E + 1, dtype=torch.int32, device=dev)
+    perm_src = torch.empty(T * k, dtype=torch.int32, device=dev)
+    pos = torch.empty(T * k, dtype=torch.int32, device=dev)
+    imp = torch.empty(E, dtype=torch.float32, device=dev)
+    x_perm = torch.empty((T * k, d), dtype=torch.bfloat16, device=dev)
+    B.moe_permute(c, idx, w, dl.x, offsets, perm_src, pos, imp, None, x_perm, ws)
+    out = {}
+    for tag, layer in (("row", dl), ("tiled", dt)):
+        W = layer.weights()
+        hid = torch.empty((R, h), dtype=torch.bfloat16, device=dev)
+        B.moe_expert_up(c, W, None, dl.x, offsets, hid, perm_src=perm_src)
+        hid_t = torch.empty_like(hid)
+        pre = torch.empty((R, 2 * h), dtype=torch.bfloat16, device=dev)
+        B.moe_expert_up_train(c, W, x_perm, dl.x, offsets, hid_t, pre)
+        yp = torch.empty((R, d), dtype=torch.bfloat16, device=dev)
+        B.moe_expert_down(c, W, hid, offsets, yp)
+        yf = torch.empty_like(yp)
+        B.moe_expert_ffn(c, W, x_perm, dl.x, offsets, yf, ws)
+        out[tag] = (hid, hid_t, pre, yp, yf)
+    torch.cuda.synchronize()
+    for a, b in zip(out["row"], out["tiled"]):
+        assert torch.equal(_iv(a), _iv(b))
+
+
+def test_backward_and_fp32_refuse_tiled_weights():
+    L = random_layer(3, T=64, d=64, h=128, E=4, k=2, act=SWIGLU, dtype=BF16, wstd=0.1)
+    dt = DeviceLayer.upload(L).tiled()
+    c = dt.cfg
+    dev = dt.x.device
+    dy = torch.zeros_like(dt.x)
+    with pytest.raises(B.MoeError) as e:
+        B.moe_backward(c, dt.weights(), dt.x, dy, None, None, None, None, None, None, None,
+                       0.0, B.grads(dt.x, dt.w_gate, dt.w_up, dt.w_down),
+                       torch.empty(256, dtype=torch.uint8, device=dev))
+    assert e.value.status == B.MOE_ERR_UNSUPPORTED
+    Lf = random_layer(3, T=64, d=64, h=128, E=4, k=2, act=SWIGLU, dtype=F32, wstd=0.1)
+    df = DeviceLayer.upload(Lf)
+    W = B.weights(df.w_gate, df.w_up, df.w_down, layout=B.MOE_LAYOUT_TILED)
+    fw = Forward(df)
+    with pytest.raises(B.MoeError) as e:
+        B.moe_forward(df.cfg, W, df.x, fw.y, fw.topk_idx, fw.topk_w, fw.counts,
+                      fw.importance, fw.stats, fw.ws)
+    assert e.value.status == B.MOE_ERR_UNSUPPORTED
+
+
+def _device_layer(cfg, seed: int) -> DeviceLayer:
+    """A layer of the given shape drawn on the GPU (bit-equality of the two
+    weight orders needs no oracle, so no host copy): x and weights normal,
+    the router bias of the configuration's recipe."""
+    g = torch.Generator(device="cuda").manual_seed(seed)
+    bf = torch.bfloat16
+
+    def rnd(*shape, std=1.0, dtype=bf):
+        return (torch.randn(*shape, generator=g, device="cuda") * std).to(dtype)
+    d, h, E = cfg.d, cfg.h, cfg.E
+    nup = cfg.n_up
+    b_gate = None
+    if cfg.router_bias == "zipf1.1":
+        b_gate = torch.from_numpy(synthetic.generate.zipf_log_bias(E, 1.1)).cuda()
+    elif cfg.router_bias == "normal0.5":
+        b_gate = rnd(E, std=0.5, dtype=torch.float32)
+    S = cfg.S
+    return DeviceLayer(B.config_of(cfg), rnd(cfg.T, d), rnd(E, d, std=d ** -0.5, dtype=torch.float32),
+                       b_gate, rnd(E, nup, d, std=d ** -0.5), rnd(E, d, h, std=h ** -0.5),
+                       None, None, rnd(1, nup, d, std=d ** -0.5) if S else None,
+                       rnd(1, d, h, std=h ** -0.5) if S else None)
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("name", ["gpt2-moe", "mixtral-8x7b", "gpt-oss-20b-decode",
+                                  "deepseek-v3"])
+def test_full_size_tiled_equals_row_major(name):
+    cfg = synthetic.BY_NAME[name]
+    dl = _device_layer(cfg, zlib.crc32(name.encode()))
+    f_row = Forward(dl)
+    f_row()
+    y_row = f_row.y.clone()
+    del f_row
+    dt = dl.tiled()
+    dl.w_up = dl.w_down = dl.w_up_shared = dl.w_down_shared = None
+    f_til = Forward(dt)
+    f_til()
+    torch.cuda.synchronize()
+    assert torch.equal(_iv(y_row), _iv(f_til.y))
