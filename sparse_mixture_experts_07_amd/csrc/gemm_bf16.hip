@@ -23,10 +23,12 @@
 // a few neighbouring weight tiles, so weight tiles are fetched from HBM once
 // per XCD and reused from its L2.  Three kernels share the tile arithmetic:
 //
-//   gemm_dma_kernel   large groups, K <= 8192: operands DMA'd from global
-//                     memory into four rotating LDS buffers, 8 waves
-//   gemm_pp_kernel    large groups, longer K: register-staged loads, two
-//                     wave groups alternating compute and memory slots
+//   gemm_dma_kernel   large groups (row-major weights: K <= 8192): operands
+//                     DMA'd from global memory into four rotating LDS
+//                     buffers, 8 waves
+//   gemm_pp_kernel    large groups, row-major weights, longer K: register-
+//                     staged loads, two wave groups alternating compute and
+//                     memory slots
 //   gemm_bf16_kernel  small groups (<= 64 rows, e.g. decode): 32- or 64-row tiles
 //                     streaming the weights, registers -> LDS, lock-step
 //
@@ -728,7 +730,7 @@ void gemm_bf16_kernel(GemmArgs a) {
 // 2k, group 0 in slot 2k+1, so stage k+1 is complete before slot 2k+2 and
 // two LDS buffers suffice: stage k+2 overwrites stage k only from slot
 // 2k+2 on, after both groups have finished it.
-template <int BM, int MODE, bool WT>
+template <int BM, int MODE>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2)))
 void gemm_pp_kernel(GemmArgs a) {
   constexpr int BNW = 256, WM = 4, WN = 2, BK = 64;
@@ -753,7 +755,7 @@ void gemm_pp_kernel(GemmArgs a) {
   __syncthreads();
   const int total_tiles = tprefix[a.E + a.S] * a.n_tiles;
   const uint32_t row_bytes = (uint32_t)a.K * 2u;
-  const WAddr wa = TM::template waddr<WT>(a, row_bytes);
+  const WAddr wa = TM::template waddr<false>(a, row_bytes);
   const int nk = a.K / BK;
 
   for (int it = 0;; ++it) {
@@ -1408,11 +1410,11 @@ static hipError_t launch_bm(const GemmArgs &a, hipStream_t s) {
       per_cu, a, s);
 }
 
-template <int BM, int MODE, bool WT>
+template <int BM, int MODE>
 static hipError_t launch_pp(const GemmArgs &a, hipStream_t s) {
   static int per_cu = 0;
   return launch_persistent<BM, mode_swiglu(MODE) ? 128 : 256, 512>(
-      reinterpret_cast<const void *>(&gemm_pp_kernel<BM, MODE, WT>), per_cu, a, s);
+      reinterpret_cast<const void *>(&gemm_pp_kernel<BM, MODE>), per_cu, a, s);
 }
 
 template <int BM, int BNW, int WM, int WN, int MODE, bool WT>
@@ -1428,8 +1430,9 @@ static hipError_t launch_dma(const GemmArgs &a, hipStream_t s) {
 // smaller tile's lower operand reuse is priced in (measured: about 12 %
 // more time per row); group sizes are device-side, so the count of m-tiles
 // is estimated as rows / BM plus half a tile per group.  Kernel: the
-// DMA-fed one up to K = 8192, the ping-pong one on longer K (measured on
-// MI355X).
+// DMA-fed one, except row-major weights with K > 8192, which take the
+// ping-pong one (measured on MI355X: at K = 14336 the ping-pong kernel wins
+// over row-major weights, the DMA-fed one over tiled weights).
 template <int MODE, bool WT>
 static hipError_t launch_big(const GemmArgs &a, hipStream_t s) {
   const double nblk = num_cus();
@@ -1448,10 +1451,11 @@ static hipError_t launch_big(const GemmArgs &a, hipStream_t s) {
     return bm192 ? launch_dma<192, 256, 2, 4, MODE, WT>(a, s)
                  : launch_dma<256, 256, 2, 4, MODE, WT>(a, s);
   } else {
-    if (a.K <= 8192)
-      return bm192 ? launch_dma<192, 256, 4, 2, MODE, WT>(a, s)
-                   : launch_dma<256, 256, 4, 2, MODE, WT>(a, s);
-    return bm192 ? launch_pp<192, MODE, WT>(a, s) : launch_pp<256, MODE, WT>(a, s);
+    if constexpr (!WT) {
+      if (a.K > 8192) return bm192 ? launch_pp<192, MODE>(a, s) : launch_pp<256, MODE>(a, s);
+    }
+    return bm192 ? launch_dma<192, 256, 4, 2, MODE, WT>(a, s)
+                 : launch_dma<256, 256, 4, 2, MODE, WT>(a, s);
   }
 }
 

@@ -7,9 +7,10 @@ from row-major weights: the kernels and their arithmetic are the same, only
 the addresses of the weight loads differ.  The row-major path is the one
 pinned to the oracle by the other parity tests; the layers below also
 compare the tiled forward with the oracle directly, one per GEMM kernel
-(small groups in 32- and 64-row tiles, the DMA-fed large-group kernel, the
-ping-pong kernel for K > 8192), and the benchmarked shapes are checked for
-bitwise equality at full size.
+(small groups in 32- and 64-row tiles, the DMA-fed large-group kernel at
+short and long K; tiled weights never take the ping-pong kernel, which
+row-major weights use above K = 8192), and the benchmarked shapes are
+checked for bitwise equality at full size.
 """
 import zlib
 
@@ -74,7 +75,8 @@ def _iv(t):
 # the group sizes: routed rows / E >= 512 puts every group in the large-tile
 # launch; otherwise groups of <= 32 rows take 32-row tiles, 33-64 rows
 # 64-row tiles when groups average 16 rows or more, larger ones the
-# large-tile kernel, which is the ping-pong one for K > 8192).
+# large-tile kernel; K > 8192 below compares the DMA-fed kernel over tiled
+# weights with the ping-pong one over row-major weights).
 LAYERS = {
     "small32-gelu-bias": dict(T=37, d=64, h=128, E=5, k=2, act=GELU, dtype=BF16,
                               expert_bias=True),
@@ -83,8 +85,8 @@ LAYERS = {
     "ntail-swiglu": dict(T=300, d=192, h=320, E=7, k=3, act=SWIGLU, dtype=BF16),
     "dma-one-class-gelu": dict(T=1000, d=256, h=512, E=3, k=2, act=GELU, dtype=BF16,
                                expert_bias=True),
-    "pp-long-k-down": dict(T=300, d=128, h=8256, E=4, k=2, act=SWIGLU, dtype=BF16),
-    "pp-long-k-up": dict(T=300, d=8256, h=128, E=4, k=2, act=SWIGLU, dtype=BF16),
+    "long-k-down": dict(T=300, d=128, h=8256, E=4, k=2, act=SWIGLU, dtype=BF16),
+    "long-k-up": dict(T=300, d=8256, h=128, E=4, k=2, act=SWIGLU, dtype=BF16),
 }
 
 
