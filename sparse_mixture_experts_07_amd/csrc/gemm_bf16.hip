@@ -33,8 +33,12 @@
 //                     streaming the weights, registers -> LDS, lock-step
 //
 // Measured on MI355X the large-group kernels are bound by the L2 -> CU
-// operand stream (about 21-26 B/clk per CU in this access pattern, against
+// operand stream (about 21-26 B/clk per CU over row-major weights, against
 // 32 B/clk that full MFMA rate on 256 x 256 tiles would need), not by LDS.
+// The texture path's cost goes by the cache lines a load touches: a 16-row
+// x 64-byte block is 16 half lines, so weights in the tiled order (each
+// such block stored as 1 KB of contiguous memory) load at twice the bytes
+// per cycle; the token rows, gathered from any row, stay row-major.
 #include "common.h"
 
 #include <algorithm>
