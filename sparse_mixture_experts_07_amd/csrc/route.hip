@@ -97,13 +97,13 @@ struct XLoad<float> {  // fp32 rows: 4 values (16 B) per load
 // the global loads of super-chunk c+1 fly while super-chunk c is consumed,
 // so one load latency is paid per G x 32 columns.  Each thread walks k in
 // ascending order for every one of its TPT x EPT chains.
-template <typename XT, int TX, int EPT, int TPT, int GMAX>
-__global__ __launch_bounds__(kRouteThreads) void route_kernel(
+template <typename XT, int TX, int EPT, int TPT, int GMAX, int NTH>
+__global__ __launch_bounds__(NTH) void route_kernel(
     const XT *__restrict__ x, const float *__restrict__ wg,
     const float *__restrict__ bg, int T, int d, int E, int k, int gate, int G,
     int32_t *__restrict__ topk_idx, float *__restrict__ topk_w,
     int32_t *__restrict__ counts, float *__restrict__ logits) {
-  constexpr int TY = kRouteThreads / TX;
+  constexpr int TY = NTH / TX;
   constexpr int BT = TY * TPT;
   constexpr int EP = TX * EPT;      // padded expert count
   constexpr int EPS = EP + 1;       // score row stride
@@ -112,9 +112,9 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(
   constexpr int NQ = (EP + 63) / 64;  // score slots per lane in the top-k
   constexpr int VEC = XLoad<XT>::kVec;
   constexpr int XQ = BT * (BK / VEC);              // x vector loads per chunk
-  constexpr int XL = (XQ + kRouteThreads - 1) / kRouteThreads;
+  constexpr int XL = (XQ + NTH - 1) / NTH;
   constexpr int WQ = EP * (BK / 4);                // W_g float4 loads per chunk
-  constexpr int WL = (WQ + kRouteThreads - 1) / kRouteThreads;
+  constexpr int WL = (WQ + NTH - 1) / NTH;
   constexpr int CHUNK = (BT + EP) * KS;            // floats per staged chunk
 
   extern __shared__ float lds[];                   // 2 * G * CHUNK floats
@@ -126,7 +126,7 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(
   const int ty = tid / TX;
   const int t0 = blockIdx.x * BT;
 
-  for (int e = tid; e < EP; e += kRouteThreads) cnt[e] = 0;
+  for (int e = tid; e < EP; e += NTH) cnt[e] = 0;
 
   float acc[TPT][EPT];
 #pragma unroll
@@ -143,7 +143,7 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(
       const int kg = k0 + g * BK;
 #pragma unroll
       for (int i = 0; i < XL; ++i) {
-        const int q = tid + i * kRouteThreads;
+        const int q = tid + i * NTH;
         const int row = q / (BK / VEC);
         const int c = (q % (BK / VEC)) * VEC;
         if (q < XQ && t0 + row < T) {
@@ -155,7 +155,7 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(
       }
 #pragma unroll
       for (int i = 0; i < WL; ++i) {
-        const int q = tid + i * kRouteThreads;
+        const int q = tid + i * NTH;
         const int e = q / (BK / 4);
         const int c = (q % (BK / 4)) * 4;
         wr[g][i] = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -171,7 +171,7 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(
       float *ws = xs + BT * KS;
 #pragma unroll
       for (int i = 0; i < XL; ++i) {
-        const int q = tid + i * kRouteThreads;
+        const int q = tid + i * NTH;
         if (q < XQ) {
           const int row = q / (BK / VEC);
           const int c = (q % (BK / VEC)) * VEC;
@@ -183,7 +183,7 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(
       }
 #pragma unroll
       for (int i = 0; i < WL; ++i) {
-        const int q = tid + i * kRouteThreads;
+        const int q = tid + i * NTH;
         if (q < WQ) *reinterpret_cast<float4 *>(ws + (q / (BK / 4)) * KS + (q % (BK / 4)) * 4) = wr[g][i];
       }
     }
@@ -253,7 +253,7 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(
   // ---- KeepTopK + softmax: one wavefront per token ----
   const int lane = tid % kWave;
   const int wave = tid / kWave;
-  constexpr int NW = kRouteThreads / kWave;
+  constexpr int NW = NTH / kWave;
   for (int row = wave; row < BT; row += NW) {
     const int t = t0 + row;
     if (t >= T) break;
@@ -348,7 +348,7 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(
     }
   }
   __syncthreads();
-  for (int e = tid; e < E; e += kRouteThreads)
+  for (int e = tid; e < E; e += NTH)
     if (counts && cnt[e]) atomicAdd(counts + e, cnt[e]);
 }
 
@@ -685,12 +685,12 @@ static hipError_t launch_route_direct(const void *x, const float *wg, const floa
   return hipGetLastError();
 }
 
-template <typename XT, int TX, int EPT, int TPT, int GMAX>
+template <typename XT, int TX, int EPT, int TPT, int GMAX, int NTH = kRouteThreads>
 static hipError_t launch_route_t(const void *x, const float *wg, const float *bg,
                                  int T, int d, int E, int k, int gate, int32_t *idx,
                                  float *w, int32_t *counts, float *logits,
                                  hipStream_t s) {
-  constexpr int BT = (kRouteThreads / TX) * TPT;
+  constexpr int BT = (NTH / TX) * TPT;
   constexpr int CHUNK = (BT + TX * EPT) * (kRouteBK + 4);
   constexpr int EPS = TX * EPT + 1;
   // chunks per super-chunk: the most that divide d and keep the two LDS
@@ -705,12 +705,12 @@ static hipError_t launch_route_t(const void *x, const float *wg, const float *bg
   // scores (and the unbiased ones for the bias-selects gate) reuse the space
   const size_t score_lds = sizeof(float) * (size_t)BT * EPS * (gate == kGateBiasSelects ? 2 : 1);
   if (lds < score_lds) lds = score_lds;
-  auto kern = route_kernel<XT, TX, EPT, TPT, GMAX>;
+  auto kern = route_kernel<XT, TX, EPT, TPT, GMAX, NTH>;
   hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (err != hipSuccess) return err;
   const int blocks = (T + BT - 1) / BT;
-  kern<<<blocks, kRouteThreads, lds, s>>>(static_cast<const XT *>(x), wg, bg, T, d, E, k, gate, G,
+  kern<<<blocks, NTH, lds, s>>>(static_cast<const XT *>(x), wg, bg, T, d, E, k, gate, G,
                                           idx, w, counts, logits);
   return hipGetLastError();
 }
@@ -745,12 +745,17 @@ static hipError_t launch_route_dt(const void *x, const float *wg, const float *b
   if (E <= 32) MOE_LANE(32);
   if (E <= 64) MOE_LANE(64);
 #undef MOE_LANE
-#define MOE_ROUTE(TX, EPT, TPT, GM) \
-  return launch_route_t<XT, TX, EPT, TPT, GM>(x, wg, bg, T, d, E, k, gate, idx, w, counts, logits, s)
-  if (E <= 128) MOE_ROUTE(32, 4, 4, 1);
-  // 16 tokens per workgroup: two workgroups per CU at T = 8192 (measured on
-  // MI355X at E = 256, d = 7168: 559 us against 726 us for 32 tokens)
-  MOE_ROUTE(64, 4, 4, 1);
+#define MOE_ROUTE(TX, EPT, TPT, GM, NTH) \
+  return launch_route_t<XT, TX, EPT, TPT, GM, NTH>(x, wg, bg, T, d, E, k, gate, idx, w, counts, logits, s)
+  if (E <= 128) MOE_ROUTE(32, 4, 4, 1, kRouteThreads);
+  // Every workgroup streams all of W_g through LDS, so fewer, larger
+  // workgroups move less of it from L2: 32 tokens in 8 wavefronts (one
+  // workgroup per CU at T = 8192) once there are at least 256 of them
+  // (measured on MI355X at E = 256, d = 7168: 520 us against 571 us for
+  // 16 tokens in 4 wavefronts, two per CU; 32 tokens in 4 wavefronts,
+  // one wavefront per SIMD, measured 726 us against 559 us)
+  if (T >= 32 * 256) MOE_ROUTE(64, 4, 4, 1, 512);
+  MOE_ROUTE(64, 4, 4, 1, kRouteThreads);
 #undef MOE_ROUTE
 }
 
