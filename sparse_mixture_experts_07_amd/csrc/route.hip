@@ -627,26 +627,37 @@ __global__ __launch_bounds__(NWV * kWave) void route_lane_kernel(
     const u32x4_t *xb = lds[ch % G::NB];
     const u32x4_t *wb = xb + G::XBLK * 64;
     const int ncol = min(CC, d - ch * CC);
-    for (int c = 0; c < ncol; c += 32) {
+    // The chain's operands, 32 columns at a time, in two register sets: the
+    // LDS reads of the next 32 columns are issued before the FMAs of these,
+    // so their latency hides behind the chain.
+    constexpr int XR = sizeof(XT) == 2 ? 4 : 8;   // 16-byte x slots per 32 columns
+    u32x4_t xs[2][XR], ws[2][8];
+    auto rd = [&](int b, int c) {
+#pragma unroll
+      for (int i = 0; i < XR; ++i) xs[b][i] = xb[G::xslot(tl, c / (32 / XR) + i)];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) ws[b][i] = wb[G::wslot(e, c / 4 + i)];
+    };
+    auto fma = [&](int b) {
       float xv[32];
-      if constexpr (sizeof(XT) == 2) {
-        u32x4_t xs[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) xs[i] = xb[G::xslot(tl, c / 8 + i)];
-        RowLoad<uint16_t>::expand(xs, xv);
-      } else {
-        u32x4_t xs[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) xs[i] = xb[G::xslot(tl, c / 4 + i)];
-        RowLoad<float>::expand(xs, xv);
-      }
-      u32x4_t ws[8];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) ws[i] = wb[G::wslot(e, c / 4 + i)];
+      if constexpr (sizeof(XT) == 2)
+        RowLoad<uint16_t>::expand(xs[b], xv);
+      else
+        RowLoad<float>::expand(xs[b], xv);
 #pragma unroll
       for (int i = 0; i < 8; ++i)
 #pragma unroll
-        for (int q = 0; q < 4; ++q) acc = __builtin_fmaf(xv[4 * i + q], __uint_as_float(ws[i][q]), acc);
+        for (int q = 0; q < 4; ++q) acc = __builtin_fmaf(xv[4 * i + q], __uint_as_float(ws[b][i][q]), acc);
+    };
+    // (ncol is a multiple of 64; the last prefetch re-reads the chunk's
+    // last 32 columns and is not consumed, which keeps the loop branch-free)
+    static_assert(CC % 64 == 0, "chunks of whole 64-column steps");
+    rd(0, 0);
+    for (int c = 0; c < ncol; c += 64) {
+      rd(1, c + 32);
+      fma(0);
+      rd(0, min(c + 64, ncol - 32));
+      fma(1);
     }
   }
 
