@@ -403,8 +403,8 @@ DECODE_WORKLOAD = "gpt-oss-20b-decode"
 
 def main():
     args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on one GPU only: the library has no multi-GPU path "
-        print("bench.py runs on one GPU only: this build has no multi-GPU path "
               "(expert parallelism is a design note, not code)", file=sys.stderr)
         sys.exit(2)
     import torch
