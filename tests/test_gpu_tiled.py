@@ -111,6 +111,32 @@ def test_tiled_forward_equals_row_major_and_oracle(name):
     check_outputs(L, to_f64(f_til.y), toks)
 
 
+# The routing variants change which rows the grouped GEMMs see, not how
+# they read weights: capacity with drops or next-choice re-routing, the two
+# other gate modes.
+VARIANTS = {
+    "capacity-drop": dict(capacity=60, overflow=0, gate=0),
+    "capacity-next-choice": dict(capacity=60, overflow=1, gate=0),
+    "bias-selects": dict(capacity=0, overflow=0, gate=1),
+    "softmax-all": dict(capacity=0, overflow=0, gate=2),
+}
+
+
+@pytest.mark.parametrize("name", list(VARIANTS))
+def test_routing_variants_equal_over_both_orders(name):
+    v = VARIANTS[name]
+    L = random_layer(57, T=400, d=128, h=256, E=8, k=2, act=SWIGLU, dtype=BF16, S=1,
+                     bias=True, wstd=0.1, gate=v["gate"])
+    dl = DeviceLayer.upload(L, capacity=v["capacity"], overflow=v["overflow"])
+    f_row, f_til = Forward(dl), Forward(dl.tiled())
+    f_row()
+    f_til()
+    torch.cuda.synchronize()
+    assert torch.equal(_iv(f_row.y), _iv(f_til.y))
+    assert torch.equal(f_row.topk_idx, f_til.topk_idx)
+    assert torch.equal(f_row.topk_w, f_til.topk_w)
+
+
 def test_stage_entry_points_take_tiled_weights():
     """moe_expert_up, moe_expert_up_train (hidden and pre-activations),
     moe_expert_down and moe_expert_ffn: bitwise equal for both orders."""
