@@ -167,6 +167,7 @@ __device__ __forceinline__ void tile_prefix(const GemmArgs &a, int *tprefix, int
 // 32-bit offset per thread addresses all of its 16-byte loads.
 struct Tile {
   int g, grow0, rows, m0, n0;
+  int hv;              // token rows of the tile that it computes and stores
   bool gather;         // token rows gathered from GemmArgs::gather_x
   __amdgpu_buffer_rsrc_t rs_a, rs_w0, rs_w1;
   uint32_t w_stride;   // kDownKN: bytes per k row of the weights
@@ -174,15 +175,15 @@ struct Tile {
 
 // Byte offset (from the tile's A descriptor) of the start of tile-local
 // token row r.  Gathered rows: row gather[p] of x, the descriptor covering
-// all of x; a row past the group's end gets offset T * row_bytes, out of the
-// descriptor's range, so it reads zeros (as does a corrupt index).
-// Otherwise the descriptor starts at the tile's first row and ends with the
-// group's last one.
+// all of x; a row past the tile's rows (t.hv) gets offset T * row_bytes, out
+// of the descriptor's range, so it reads zeros (as does a corrupt index).
+// Otherwise the descriptor starts at the tile's first row and ends with its
+// last one.
 __device__ __forceinline__ uint32_t a_row_offset(const GemmArgs &a, const Tile &t, int r,
                                                  uint32_t row_bytes) {
   if (t.gather) {
     int src = a.T;
-    if (t.m0 + r < t.rows) {
+    if (r < t.hv) {
       const int p = a.gather[t.grow0 + t.m0 + r];
       if ((unsigned)p < (unsigned)a.T) src = p;
     }
@@ -192,7 +193,14 @@ __device__ __forceinline__ uint32_t a_row_offset(const GemmArgs &a, const Tile &
 }
 
 // Tile L of the launch's ragged tile space: group g owns tiles
-// [tprefix[g] * n_tiles, tprefix[g+1] * n_tiles), m-tile fastest.
+// [tprefix[g] * n_tiles, tprefix[g+1] * n_tiles), m-tile fastest.  A group
+// of `rows` rows has mt = ceil(rows / BM) m-tiles, and they split its rows
+// evenly: each takes hb = rows / mt rounded up to 16 rows (hb <= BM), the
+// last one the rest.  A group of 1100 rows thus runs as 5 tiles of 224 rows
+// rather than 4 full tiles and one of 76 rows padded to BM, and the rows
+// past hb in a tile are neither read nor computed (the large-group kernel
+// skips their MFMAs), so the padded work shrinks from up to BM - 1 rows per
+// group to under 16 rows per tile.
 template <int BM, int BNW, bool SWI, bool KN = false>
 __device__ __forceinline__ Tile decode_tile(const GemmArgs &a, const int *tprefix, int L) {
   const int G = a.E + a.S;
@@ -225,10 +233,12 @@ __device__ __forceinline__ Tile decode_tile(const GemmArgs &a, const int *tprefi
     abase = a.a_shared;
     wbase = a.w_shared;
   }
-  t.m0 = mt * BM;
+  const int hb = min(BM, ((t.rows + tg - 1) / tg + 15) & ~15);
+  t.m0 = mt * hb;
+  t.hv = min(hb, t.rows - t.m0);
   t.n0 = nt * (SWI ? BNW / 2 : BNW);
   const uint32_t row_bytes = (uint32_t)a.K * 2u;
-  const int arows = min(BM, t.rows - t.m0);
+  const int arows = t.hv;
   t.gather = a.gather != nullptr && t.g < a.E;
   if (t.gather)
     t.rs_a = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>(a.gather_x), 0,
@@ -283,6 +293,12 @@ struct TileMath {
   static constexpr int WCH = BNW / 8;
   static_assert(!KN || (WCH >= 8 && !PLANES), "k-row weight stage");
   static __device__ __forceinline__ int kn_slot(int k, int c) { return k * WCH + (c ^ (k & 7)); }
+  // Token rows of fragment j of wave row wm: the waves' fragments
+  // interleave (fragment j of the WM wave rows covers rows 16 (j WM + wm)
+  // .. + 15), so that when a tile computes only its first hv rows every
+  // wave row drops the same number of fragments, give or take one, and the
+  // SIMDs (two wave rows each) stay evenly loaded.
+  static __device__ __forceinline__ int frag_row(int wm, int j) { return (j * WM + wm) * 16; }
   static constexpr int A_LD = BM * CH / NT;    // 16-byte loads per thread per stage
   static constexpr int W_LD = BNW * CH / NT;
   static_assert(BK == 32 || BK == 64, "stage depth");
@@ -418,7 +434,7 @@ struct TileMath {
   static __device__ __forceinline__ bf16x8_t read_a(const u32x4_t *As, int s, int j, int wm) {
     const int lane = threadIdx.x % 64;
     const int ch = 4 * s + lane / 16;
-    const int r = wm * WTM + j * 16 + lane % 16;
+    const int r = frag_row(wm, j) + lane % 16;
     return __builtin_bit_cast(bf16x8_t, As[a_idx(r, ch)]);
   }
   static __device__ __forceinline__ bf16x8_t read_w(const u32x4_t *Ws, int n, int wn) {
@@ -515,7 +531,9 @@ struct TileMath {
       }
 #pragma unroll
       for (int j = 0; j < FM; ++j) {
-        const int m = t.m0 + wm * WTM + j * 16 + lrow;
+        const int lr = frag_row(wm, j) + lrow;   // tile-local row
+        const int m = t.grow0 + t.m0 + lr;
+        const bool row_ok = lr < t.hv;
         float v[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
@@ -530,11 +548,11 @@ struct TileMath {
         uint2 o;
         o.x = pack_bf16x2(v[0], v[1]);
         o.y = pack_bf16x2(v[2], v[3]);
-        if (col_ok && m < t.rows)
-          *reinterpret_cast<uint2 *>(a.c + (int64_t)(t.grow0 + m) * a.n_out + col) = o;
+        if (col_ok && row_ok)
+          *reinterpret_cast<uint2 *>(a.c + (int64_t)m * a.n_out + col) = o;
         if constexpr (mode_pre(MODE)) {
           // pre-activations: row stride w_rows (2h SwiGLU, h GELU)
-          uint16_t *pre = a.c_pre + (int64_t)(t.grow0 + m) * a.w_rows + col;
+          uint16_t *pre = a.c_pre + (int64_t)m * a.w_rows + col;
           uint2 p;
           if constexpr (mode_swiglu(MODE)) {
             p.x = pack_bf16x2(acc[i][j][0], acc[i][j][1]);
@@ -542,14 +560,14 @@ struct TileMath {
             uint2 u;
             u.x = pack_bf16x2(acc[i + FW / 2][j][0], acc[i + FW / 2][j][1]);
             u.y = pack_bf16x2(acc[i + FW / 2][j][2], acc[i + FW / 2][j][3]);
-            if (col_ok && m < t.rows) {
+            if (col_ok && row_ok) {
               *reinterpret_cast<uint2 *>(pre) = p;
               *reinterpret_cast<uint2 *>(pre + a.n_out) = u;
             }
           } else {
             p.x = pack_bf16x2(acc[i][j][0] + bias[0], acc[i][j][1] + bias[1]);
             p.y = pack_bf16x2(acc[i][j][2] + bias[2], acc[i][j][3] + bias[3]);
-            if (col_ok && m < t.rows) *reinterpret_cast<uint2 *>(pre) = p;
+            if (col_ok && row_ok) *reinterpret_cast<uint2 *>(pre) = p;
           }
         }
         // one output fragment at a time: keeps the scheduler from pulling
@@ -595,7 +613,7 @@ struct TileMath {
       }
 #pragma unroll
       for (int j = 0; j < FM; ++j) {
-        const int r = wm * WTM + j * 16 + lrow;   // tile-local row
+        const int r = frag_row(wm, j) + lrow;   // tile-local row
         float v[4];
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
@@ -616,7 +634,7 @@ struct TileMath {
       }
     }
     __syncthreads();
-    const int rows_valid = min(BM, t.rows - t.m0);
+    const int rows_valid = t.hv;
     const int cols_valid = min(BN_OUT, a.n_out - t.n0);
     for (int c = threadIdx.x; c < BM * NCH; c += NT) {
       const int r = c / NCH, q = c % NCH;
@@ -729,7 +747,7 @@ void gemm_bf16_kernel(GemmArgs a) {
 // the matrix core while the other moves data.  Slots end at LDS-only
 // barriers: global loads stay in flight for two slots.
 //
-// Group 0 (the first BM/2 token rows) computes stage k in slot 2k, group 1
+// Group 0 (wave rows 0 and 1) computes stage k in slot 2k, group 1
 // (the others) in slot 2k+1.  Group 1 stores its half of stage k+1 in slot
 // 2k, group 0 in slot 2k+1, so stage k+1 is complete before slot 2k+2 and
 // two LDS buffers suffice: stage k+2 overwrites stage k only from slot
@@ -805,6 +823,22 @@ void gemm_pp_kernel(GemmArgs a) {
       TM::epilogue_staged(a, t, acc, wm, wn, ring);
       __syncthreads();   // the staged rows are read before the next stores
     }
+  }
+}
+
+// A compile-time count, and the call f(IntC<c>) for c = clamp(n, 1, N)
+// (a wave-uniform count picks one of N unrolled code paths).
+template <int V>
+struct IntC {
+  static constexpr int value = V;
+};
+template <int N, typename F>
+__device__ __forceinline__ void with_count(int n, F &&f) {
+  if constexpr (N <= 1) {
+    f(IntC<1>{});
+  } else {
+    if (n >= N) f(IntC<N>{});
+    else with_count<N - 1>(n, f);
   }
 }
 
@@ -940,66 +974,88 @@ void gemm_dma_kernel(GemmArgs a) {
 #pragma unroll
       for (int j = 0; j < FM; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-    bf16x8_t fa0[FM], fw0[FW], fa1[FM], fw1[FW];
-    auto read_stage = [&](int buf, bf16x8_t(&fa)[FM], bf16x8_t(&fw)[FW]) {
+    // The main loop for FV token fragments per wave: fragments FV.. of the
+    // wave cover rows past the tile's hv (their LDS rows hold zeros) and
+    // are neither read nor multiplied.  Every wave issues the same DMAs and
+    // barriers whatever its FV.
+    auto main_loop = [&](auto fv_const) {
+      constexpr int FV = decltype(fv_const)::value;
+      constexpr int NMEMV = FV + FW + BPW;
+      constexpr int QMV = (FW * FV) / NMEMV >= 2 ? 2 : 1;
+      bf16x8_t fa0[FV], fw0[FW], fa1[FV], fw1[FW];
+      auto read_stage = [&](int buf, bf16x8_t(&fa)[FV], bf16x8_t(&fw)[FW]) {
 #pragma unroll
-      for (int j = 0; j < FM; ++j) fa[j] = TM::read_a(As[buf], 0, j, wm);
+        for (int j = 0; j < FV; ++j) fa[j] = TM::read_a(As[buf], 0, j, wm);
 #pragma unroll
-      for (int i = 0; i < FW; ++i) fw[i] = TM::read_w(Ws[buf], i, wn);
-    };
-    auto iteration = [&](int s, bf16x8_t(&fa_cur)[FM], bf16x8_t(&fw_cur)[FW],
-                         bf16x8_t(&fa_nxt)[FM], bf16x8_t(&fw_nxt)[FW]) {
-      read_stage((s + 1) % NB, fa_nxt, fw_nxt);
+        for (int i = 0; i < FW; ++i) fw[i] = TM::read_w(Ws[buf], i, wn);
+      };
+      auto iteration = [&](int s, bf16x8_t(&fa_cur)[FV], bf16x8_t(&fw_cur)[FW],
+                           bf16x8_t(&fa_nxt)[FV], bf16x8_t(&fw_nxt)[FW]) {
+        read_stage((s + 1) % NB, fa_nxt, fw_nxt);
 #pragma unroll
-      for (int i = 0; i < FW; ++i)
+        for (int i = 0; i < FW; ++i)
 #pragma unroll
-        for (int j = 0; j < FM; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fw_cur[i], fa_cur[j], acc[i][j],
-                                                               0, 0, 0);
-      dma(s + 4);
-      // operand reads one per QM MFMAs, then the DMAs one per QM MFMAs
+          for (int j = 0; j < FV; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fw_cur[i], fa_cur[j], acc[i][j],
+                                                                 0, 0, 0);
+        dma(s + 4);
+        // operand reads one per QMV MFMAs, then the DMAs one per QMV MFMAs
+        // (with too few MFMAs to spread them over, the compiler places them)
+        if constexpr (QMV * NMEMV <= FW * FV) {
 #pragma unroll
-      for (int q = 0; q < FM + FW; ++q) {
-        __builtin_amdgcn_sched_group_barrier(0x008, QM, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      }
+          for (int q = 0; q < FV + FW; ++q) {
+            __builtin_amdgcn_sched_group_barrier(0x008, QMV, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+          }
 #pragma unroll
-      for (int q = 0; q < BPW; ++q) {
-        __builtin_amdgcn_sched_group_barrier(0x008, QM, 0);
-        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
-      }
-      if constexpr (FW * FM > QM * NMEM)
-        __builtin_amdgcn_sched_group_barrier(0x008, FW * FM - QM * NMEM, 0);
-      // Stage s+2 has landed (stages s+3 and s+4 may still be in flight) and
-      // this wave's operand reads are done; then a plain barrier (a fence
-      // would also wait for the DMAs still in flight).  The empty asm
-      // statements keep the compiler from moving LDS accesses across it.
-      __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(2 * BPW));
+          for (int q = 0; q < BPW; ++q) {
+            __builtin_amdgcn_sched_group_barrier(0x008, QMV, 0);
+            __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+          }
+          if constexpr (FW * FV > QMV * NMEMV)
+            __builtin_amdgcn_sched_group_barrier(0x008, FW * FV - QMV * NMEMV, 0);
+        }
+        // Stage s+2 has landed (stages s+3 and s+4 may still be in flight) and
+        // this wave's operand reads are done; then a plain barrier (a fence
+        // would also wait for the DMAs still in flight).  The empty asm
+        // statements keep the compiler from moving LDS accesses across it.
+        __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(2 * BPW));
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+      };
+
+      dma(0);
+      dma(1);
+      dma(2);
+      dma(3);
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(2 * BPW));   // stages 0 and 1
+      __syncthreads();
+      read_stage(0, fa0, fw0);
+      // iteration 0 DMAs stage 4 into stage 0's buffer: every wave's reads of
+      // stage 0 must be done first (later stages are read before the barrier
+      // that ends the previous iteration)
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(63));
       asm volatile("" ::: "memory");
       __builtin_amdgcn_s_barrier();
       asm volatile("" ::: "memory");
+
+      // two stages per trip so the register sets are named statically (nk is
+      // even: K is a multiple of 64)
+      for (int s = 0; s < nk; s += 2) {
+        iteration(s, fa0, fw0, fa1, fw1);
+        iteration(s + 1, fa1, fw1, fa0, fw0);
+      }
     };
-
-    dma(0);
-    dma(1);
-    dma(2);
-    dma(3);
-    __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(2 * BPW));   // stages 0 and 1
-    __syncthreads();
-    read_stage(0, fa0, fw0);
-    // iteration 0 DMAs stage 4 into stage 0's buffer: every wave's reads of
-    // stage 0 must be done first (later stages are read before the barrier
-    // that ends the previous iteration)
-    __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(63));
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-
-    // two stages per trip so the register sets are named statically (nk is
-    // even: K is a multiple of 64)
-    for (int s = 0; s < nk; s += 2) {
-      iteration(s, fa0, fw0, fa1, fw1);
-      iteration(s + 1, fa1, fw1, fa0, fw0);
+    if constexpr (TM::KN) {
+      // k-row weights (2 x 4 waves, 8 fragments per wave): every fragment
+      // is computed, which keeps one copy of the loop
+      main_loop(IntC<FM>{});
+    } else {
+      // fragments j < fv of this wave hold rows below hv
+      const int nfr = (t.hv + 15) / 16;
+      const int fv = __builtin_amdgcn_readfirstlane(nfr > wm ? (nfr - wm + WM - 1) / WM : 0);
+      with_count<FM>(fv, main_loop);
     }
     // the next tile's first DMAs (and the staged output) go to buffers that
     // the last (unused) DMAs and reads above may still touch
@@ -1195,7 +1251,7 @@ void gemm_wgrad_kernel(WgradArgs a) {
   using DL = DmaLoop<BM, BNW, WM, WN, kDown>;
   using TM = typename DL::TM;
   constexpr int CH = TM::CH, NB = DL::NB, NT = TM::NT;
-  constexpr int FM = TM::FM, FW = TM::FW, WTM = TM::WTM, WTW = TM::WTW;
+  constexpr int FM = TM::FM, FW = TM::FW, WTW = TM::WTW;
   // the operand buffers, reused after the main loop to stage the output
   // tile (BM rows of BNW bf16) so that it leaves in whole 16-byte chunks
   constexpr int LDS_CHUNKS = NB * (BM + BNW) * CH;
@@ -1226,6 +1282,7 @@ void gemm_wgrad_kernel(WgradArgs a) {
     t.grow0 = 0;
     t.rows = a.M;
     t.m0 = (local % a.m_tiles) * BM;
+    t.hv = min(BM, a.M - t.m0);
     t.n0 = (local / a.m_tiles) * BNW;
     const int c0 = __builtin_amdgcn_readfirstlane(a.poff[g]);
     const int c1 = __builtin_amdgcn_readfirstlane(a.poff[g + 1]);
@@ -1255,7 +1312,7 @@ void gemm_wgrad_kernel(WgradArgs a) {
       const int col = wn * WTW + i * 16 + 4 * (lane / 16);
 #pragma unroll
       for (int j = 0; j < FM; ++j) {
-        const int r = wm * WTM + j * 16 + lane % 16;
+        const int r = TM::frag_row(wm, j) + lane % 16;
         uint2 v;
         v.x = pack_bf16x2(acc[i][j][0], acc[i][j][1]);
         v.y = pack_bf16x2(acc[i][j][2], acc[i][j][3]);
