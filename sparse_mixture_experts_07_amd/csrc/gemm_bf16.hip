@@ -868,9 +868,12 @@ void gemm_dma_kernel(GemmArgs a) {
   constexpr int FM = TM::FM, FW = TM::FW;
   constexpr int ABLK = BM / 16, WBLK = BNW / 16;        // 16-row DMA blocks
   constexpr int NBLK = ABLK + WBLK;
-  // blocks per wave; when they do not split evenly the last waves repeat
-  // the stage's last block (same data to the same place), so that every
-  // wave issues the same number of DMAs and one vmcnt fits all
+  // blocks per wave.  A wave whose first block is past the stage's last
+  // (the eighth wave of a 192-row tile: 28 blocks for 8 waves of 4) issues
+  // no DMAs: its vmcnt wait is then empty, and the barrier after it still
+  // waits for every other wave's.  Were a wave's blocks only partly past
+  // the end, it would repeat the stage's last block (same data to the same
+  // place), so that its vmcnt counts stages like everyone else's.
   constexpr int BPW = (NBLK + NW - 1) / NW;
   static_assert(CH == 4, "k32 stages");
   // interleave: QM MFMAs per operand read or DMA, then the rest
@@ -926,8 +929,14 @@ void gemm_dma_kernel(GemmArgs a) {
 
     // wave w moves blocks BPW w .. BPW w + BPW - 1 of the stage: token
     // blocks first, then weight blocks (SwiGLU: gate rows from one
-    // descriptor, up rows from the other)
+    // descriptor, up rows from the other).  A wave whose blocks are all
+    // token blocks past the tile's rows (or all past the stage's last
+    // block) issues no DMAs for this tile: no fragment of those rows is
+    // read, and as above its empty vmcnt wait is covered by the barrier.
+    const int nvb = (t.hv + 15) / 16;
+    const bool idle = wave * BPW >= NBLK || (wave * BPW + BPW <= ABLK && wave * BPW >= nvb);
     auto dma = [&](int s) {
+      if (idle) return;
 #pragma unroll
       for (int i = 0; i < BPW; ++i) {
         const int blk = min(wave * BPW + i, NBLK - 1);
@@ -1085,9 +1094,12 @@ struct DmaLoop {
   static constexpr int CH = TM::CH, FM = TM::FM, FW = TM::FW;
   static constexpr int ABLK = BM / 16, WBLK = BNW / 16;   // 16-row DMA blocks
   static constexpr int NBLK = ABLK + WBLK;
-  // blocks per wave; when they do not split evenly the last waves repeat
-  // the stage's last block (same data to the same place), so that every
-  // wave issues the same number of DMAs and one vmcnt fits all
+  // blocks per wave.  A wave whose first block is past the stage's last
+  // (the eighth wave of a 192-row tile: 28 blocks for 8 waves of 4) issues
+  // no DMAs: its vmcnt wait is then empty, and the barrier after it still
+  // waits for every other wave's.  Were a wave's blocks only partly past
+  // the end, it would repeat the stage's last block (same data to the same
+  // place), so that its vmcnt counts stages like everyone else's.
   static constexpr int BPW = (NBLK + NW - 1) / NW;
   static_assert(CH == 4, "k32 stages");
   // interleave: QM MFMAs per operand read or DMA, then the rest
@@ -1106,6 +1118,7 @@ struct DmaLoop {
     // blocks first, then weight blocks (SwiGLU: gate rows from one
     // descriptor, up rows from the other)
     auto dma = [&](int s) {
+      if (wave * BPW >= NBLK) return;
 #pragma unroll
       for (int i = 0; i < BPW; ++i) {
         const int blk = min(wave * BPW + i, NBLK - 1);
