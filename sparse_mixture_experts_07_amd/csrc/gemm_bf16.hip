@@ -832,6 +832,16 @@ template <int V>
 struct IntC {
   static constexpr int value = V;
 };
+// f(IntC<c>) for c = clamp(n, 0, N)
+template <int N, typename F>
+__device__ __forceinline__ void with_count0(int n, F &&f) {
+  if constexpr (N <= 0) {
+    f(IntC<0>{});
+  } else {
+    if (n >= N) f(IntC<N>{});
+    else with_count0<N - 1>(n, f);
+  }
+}
 template <int N, typename F>
 __device__ __forceinline__ void with_count(int n, F &&f) {
   if constexpr (N <= 1) {
@@ -929,52 +939,56 @@ void gemm_dma_kernel(GemmArgs a) {
 
     // wave w moves blocks BPW w .. BPW w + BPW - 1 of the stage: token
     // blocks first, then weight blocks (SwiGLU: gate rows from one
-    // descriptor, up rows from the other).  A wave whose blocks are all
-    // token blocks past the tile's rows (or all past the stage's last
-    // block) issues no DMAs for this tile: no fragment of those rows is
-    // read, and as above its empty vmcnt wait is covered by the barrier.
+    // descriptor, up rows from the other).  It moves only the first ndma
+    // of them: blocks past the stage's last one, and token blocks past the
+    // tile's rows (no fragment of those rows is read), are left out.  They
+    // are the last ones of the wave's run, since no run straddles the
+    // token/weight boundary.  Each wave waits on its own count of DMAs (two
+    // stages' worth stay in flight), and the stage barrier after the wait
+    // covers the other waves' DMAs; the main loop is compiled for each
+    // count, so the DMA issue and the waits stay branch-free.
+    static_assert(ABLK % BPW == 0, "no wave moves both token and weight blocks");
     const int nvb = (t.hv + 15) / 16;
-    const bool idle = wave * BPW >= NBLK || (wave * BPW + BPW <= ABLK && wave * BPW >= nvb);
-    auto dma = [&](int s) {
-      if (idle) return;
-#pragma unroll
-      for (int i = 0; i < BPW; ++i) {
-        const int blk = min(wave * BPW + i, NBLK - 1);
-        __amdgpu_buffer_rsrc_t rs;
-        u32x4_t *dst;
-        int row = 0;
-        if (blk < ABLK) {
-          rs = t.rs_a;
-          dst = As[s % NB] + blk * 64;
-        } else {
-          const int wb = blk - ABLK;
-          dst = Ws[s % NB] + wb * 64;
-          if constexpr (TM::KN) {
-            // 64 / WCH k rows per block; lane -> physical chunk lane % WCH
-            // of row kr, holding logical chunk (lane % WCH) ^ (kr & 7)
-            constexpr int RPB = 64 / TM::WCH;
-            const int kr = wb * RPB + lane / TM::WCH;
-            const uint32_t vw = (uint32_t)(lane / TM::WCH) * t.w_stride +
-                                (uint32_t)((lane % TM::WCH) ^ (kr & 7)) * 16u;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                t.rs_w0, dst, 16, vw, (int)((uint32_t)(s * BK + wb * RPB) * t.w_stride), 0, 0);
-            continue;
-          }
-          if (TM::SWI && wb >= WBLK / 2) {
-            rs = t.rs_w1;
-            row = (wb - WBLK / 2) * 16;
-          } else {
-            rs = t.rs_w0;
-            row = wb * 16;
-          }
+    int nd = min(BPW, max(0, NBLK - wave * BPW));
+    if (wave * BPW < ABLK) nd = min(nd, max(0, nvb - wave * BPW));
+    const int ndma = __builtin_amdgcn_readfirstlane(nd);
+    // the wave's block i of stage s
+    auto issue = [&](int i, int s) {
+      const int blk = min(wave * BPW + i, NBLK - 1);
+      __amdgpu_buffer_rsrc_t rs;
+      u32x4_t *dst;
+      int row = 0;
+      if (blk < ABLK) {
+        rs = t.rs_a;
+        dst = As[s % NB] + blk * 64;
+      } else {
+        const int wb = blk - ABLK;
+        dst = Ws[s % NB] + wb * 64;
+        if constexpr (TM::KN) {
+          // 64 / WCH k rows per block; lane -> physical chunk lane % WCH
+          // of row kr, holding logical chunk (lane % WCH) ^ (kr & 7)
+          constexpr int RPB = 64 / TM::WCH;
+          const int kr = wb * RPB + lane / TM::WCH;
+          const uint32_t vw = (uint32_t)(lane / TM::WCH) * t.w_stride +
+                              (uint32_t)((lane % TM::WCH) ^ (kr & 7)) * 16u;
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(
+              t.rs_w0, dst, 16, vw, (int)((uint32_t)(s * BK + wb * RPB) * t.w_stride), 0, 0);
+          return;
         }
-        // token blocks: the lane's own row offset (gathered rows); weight
-        // blocks: the block's first row in the scalar offset (row-major), or
-        // the block in the lane's offset and the stage's 1 KB step (tiled)
-        const uint32_t vo = blk < ABLK || WT ? va[i] : voff;
-        const int so = WT && blk >= ABLK ? s * 1024 : row * (int)row_bytes + s * (BK * 2);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, dst, 16, vo, so, 0, 0);
+        if (TM::SWI && wb >= WBLK / 2) {
+          rs = t.rs_w1;
+          row = (wb - WBLK / 2) * 16;
+        } else {
+          rs = t.rs_w0;
+          row = wb * 16;
+        }
       }
+      // token blocks: the lane's own row offset (gathered rows); weight
+      // blocks: the block's first row in the scalar offset (row-major), or
+      // the block in the lane's offset and the stage's 1 KB step (tiled)
+      const uint32_t vo = blk < ABLK || WT ? va[i] : voff;
+      const int so = WT && blk >= ABLK ? s * 1024 : row * (int)row_bytes + s * (BK * 2);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, dst, 16, vo, so, 0, 0);
     };
 
     f32x4_t acc[FW][FM];
@@ -983,13 +997,18 @@ void gemm_dma_kernel(GemmArgs a) {
 #pragma unroll
       for (int j = 0; j < FM; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-    // The main loop for FV token fragments per wave: fragments FV.. of the
-    // wave cover rows past the tile's hv (their LDS rows hold zeros) and
-    // are neither read nor multiplied.  Every wave issues the same DMAs and
-    // barriers whatever its FV.
-    auto main_loop = [&](auto fv_const) {
+    // The main loop for FV token fragments and ND DMAs per stage: fragments
+    // FV.. of the wave cover rows past the tile's hv and are neither read
+    // nor multiplied.  Every wave takes the same barriers whatever its FV
+    // and ND.
+    auto main_loop = [&](auto fv_const, auto nd_const) {
       constexpr int FV = decltype(fv_const)::value;
-      constexpr int NMEMV = FV + FW + BPW;
+      constexpr int ND = decltype(nd_const)::value;
+      auto dma = [&](int s) {
+#pragma unroll
+        for (int i = 0; i < ND; ++i) issue(i, s);
+      };
+      constexpr int NMEMV = FV + FW + ND;
       constexpr int QMV = (FW * FV) / NMEMV >= 2 ? 2 : 1;
       bf16x8_t fa0[FV], fw0[FW], fa1[FV], fw1[FW];
       auto read_stage = [&](int buf, bf16x8_t(&fa)[FV], bf16x8_t(&fw)[FW]) {
@@ -1017,7 +1036,7 @@ void gemm_dma_kernel(GemmArgs a) {
             __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
           }
 #pragma unroll
-          for (int q = 0; q < BPW; ++q) {
+          for (int q = 0; q < ND; ++q) {
             __builtin_amdgcn_sched_group_barrier(0x008, QMV, 0);
             __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
           }
@@ -1028,7 +1047,7 @@ void gemm_dma_kernel(GemmArgs a) {
         // this wave's operand reads are done; then a plain barrier (a fence
         // would also wait for the DMAs still in flight).  The empty asm
         // statements keep the compiler from moving LDS accesses across it.
-        __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(2 * BPW));
+        __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(2 * ND));
         asm volatile("" ::: "memory");
         __builtin_amdgcn_s_barrier();
         asm volatile("" ::: "memory");
@@ -1038,7 +1057,7 @@ void gemm_dma_kernel(GemmArgs a) {
       dma(1);
       dma(2);
       dma(3);
-      __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(2 * BPW));   // stages 0 and 1
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(2 * ND));   // stages 0 and 1
       __syncthreads();
       read_stage(0, fa0, fw0);
       // iteration 0 DMAs stage 4 into stage 0's buffer: every wave's reads of
@@ -1058,13 +1077,15 @@ void gemm_dma_kernel(GemmArgs a) {
     };
     if constexpr (TM::KN) {
       // k-row weights (2 x 4 waves, 8 fragments per wave): every fragment
-      // is computed, which keeps one copy of the loop
-      main_loop(IntC<FM>{});
+      // is computed, which keeps fewer copies of the loop
+      with_count0<BPW>(ndma, [&](auto ndc) { main_loop(IntC<FM>{}, ndc); });
     } else {
       // fragments j < fv of this wave hold rows below hv
       const int nfr = (t.hv + 15) / 16;
       const int fv = __builtin_amdgcn_readfirstlane(nfr > wm ? (nfr - wm + WM - 1) / WM : 0);
-      with_count<FM>(fv, main_loop);
+      with_count<FM>(fv, [&](auto fvc) {
+        with_count0<BPW>(ndma, [&](auto ndc) { main_loop(fvc, ndc); });
+      });
     }
     // the next tile's first DMAs (and the staged output) go to buffers that
     // the last (unused) DMAs and reads above may still touch
